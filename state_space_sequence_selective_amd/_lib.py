@@ -1,0 +1,214 @@
+"""ctypes binding of libmamba_scan.so (include/mamba_scan.h).
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+size, their device pointers are handed to the C entry points, and a non-zero
+status becomes MambaScanError.  There is no fallback: without the built HIP
+library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmamba_scan.so")
+
+MAMBA_F32, MAMBA_BF16, MAMBA_F16 = 0, 1, 2
+STATUS = {0: "MAMBA_OK", 1: "MAMBA_ERR_INVALID", 2: "MAMBA_ERR_UNSUPPORTED",
+          3: "MAMBA_ERR_CAPACITY", 4: "MAMBA_ERR_HIP"}
+ACT_CODES = {"f32": MAMBA_F32, "bf16": MAMBA_BF16, "f16": MAMBA_F16}
+TORCH_DTYPES = {MAMBA_F32: torch.float32, MAMBA_BF16: torch.bfloat16, MAMBA_F16: torch.float16}
+
+EXPORTED = ("mamba_abi_version", "mamba_last_error", "mamba_ckpt_bytes", "mamba_workspace_bytes",
+            "mamba_scan_fwd", "mamba_scan_bwd", "mamba_conv_scan_gate_fwd", "mamba_conv_scan_gate_bwd")
+
+
+class MambaScanError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, message))
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    """mamba_dims_t."""
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_inner", ctypes.c_int64),
+                ("d_state", ctypes.c_int64), ("dt_rank", ctypes.c_int64), ("d_conv", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("act", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    @classmethod
+    def make(cls, batch, seqlen, d_inner, d_state, dt_rank=0, d_conv=0, chunk=0, act="bf16"):
+        code = ACT_CODES[act] if isinstance(act, str) else int(act)
+        return cls(batch, seqlen, d_inner, d_state, dt_rank, d_conv, chunk, code, 0)
+
+    @property
+    def L(self) -> int:
+        return self.chunk if self.chunk else 32
+
+    @property
+    def xdbl_dim(self) -> int:
+        return self.dt_rank + 2 * self.d_state
+
+    @property
+    def act_dtype(self) -> torch.dtype:
+        return TORCH_DTYPES[self.act]
+
+    def __repr__(self):
+        return "Dims(%s)" % ", ".join("%s=%d" % (f, getattr(self, f)) for f, _ in self._fields_)
+
+
+_lib = None
+
+
+def load():
+    """Load the built library; raises if it is missing (no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmamba_scan.so is not built (expected at %s); run __graft_entry__.build() "
+                          "or state_space_sequence_selective_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, D = ctypes.c_void_p, ctypes.POINTER(Dims)
+    lib.mamba_abi_version.restype = ctypes.c_int
+    lib.mamba_abi_version.argtypes = []
+    lib.mamba_last_error.restype = ctypes.c_char_p
+    lib.mamba_last_error.argtypes = []
+    for name in ("mamba_ckpt_bytes", "mamba_workspace_bytes"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mamba_scan_fwd.restype = ctypes.c_int
+    lib.mamba_scan_fwd.argtypes = [D] + [P] * 12
+    lib.mamba_scan_bwd.restype = ctypes.c_int
+    lib.mamba_scan_bwd.argtypes = [D] + [P] * 16 + [ctypes.c_size_t, P]
+    lib.mamba_conv_scan_gate_fwd.restype = ctypes.c_int
+    lib.mamba_conv_scan_gate_fwd.argtypes = [D] + [P] * 17
+    lib.mamba_conv_scan_gate_bwd.restype = ctypes.c_int
+    lib.mamba_conv_scan_gate_bwd.argtypes = [D] + [P] * 22 + [ctypes.c_size_t, P]
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().mamba_last_error().decode()
+
+
+def abi_version() -> int:
+    return load().mamba_abi_version()
+
+
+def _check(status: int):
+    if status != 0:
+        raise MambaScanError(status, last_error())
+
+
+def ckpt_bytes(dims: Dims) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mamba_ckpt_bytes(ctypes.byref(dims), ctypes.byref(out)))
+    return out.value
+
+
+def workspace_bytes(dims: Dims) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mamba_workspace_bytes(ctypes.byref(dims), ctypes.byref(out)))
+    return out.value
+
+
+def ckpt_shape(dims: Dims):
+    return (dims.batch, -(-dims.seqlen // dims.L), dims.d_state, dims.d_inner)
+
+
+# ---------------------------------------------------------------- marshalling
+
+
+def _ptr(t, name, dtype, shape, required=False):
+    if t is None:
+        if required:
+            raise ValueError("%s is required" % name)
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor, got %s" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shapes(d: Dims):
+    act = (d.batch, d.seqlen, d.d_inner)
+    return dict(act=act, xdbl=(d.batch, d.seqlen, d.xdbl_dim), a_log=(d.d_inner, d.d_state),
+                vec=(d.d_inner,), state=(d.batch, d.d_inner, d.d_state), ckpt=ckpt_shape(d),
+                conv_w=(d.d_inner, d.d_conv), conv_state=(d.batch, d.d_inner, d.d_conv))
+
+
+def scan_fwd(d: Dims, u, delta_raw, a_log, xdbl, D=None, z=None, h0=None, *, out, y_save=None,
+             h_last=None, ckpt=None, stream=None):
+    s, at, f = _shapes(d), d.act_dtype, torch.float32
+    args = [ctypes.byref(d), _ptr(u, "u", at, s["act"], True), _ptr(delta_raw, "delta_raw", at, s["act"], True),
+            _ptr(a_log, "a_log", f, s["a_log"], True), _ptr(xdbl, "xdbl", at, s["xdbl"], True),
+            _ptr(D, "D", f, s["vec"]), _ptr(z, "z", at, s["act"]), _ptr(h0, "h0", f, s["state"]),
+            _ptr(out, "out", at, s["act"], True), _ptr(y_save, "y_save", at, s["act"]),
+            _ptr(h_last, "h_last", f, s["state"]), _ptr(ckpt, "ckpt", f, s["ckpt"]), _stream(stream)]
+    _check(load().mamba_scan_fwd(*args))
+
+
+def scan_bwd(d: Dims, u, delta_raw, a_log, xdbl, D, z, y_saved, ckpt, dout, *, d_u, d_delta_raw, d_z,
+             d_xdbl, d_a_log, d_D, workspace, stream=None):
+    s, at, f = _shapes(d), d.act_dtype, torch.float32
+    ws = _ptr(workspace, "workspace", torch.uint8, (workspace.numel(),), True) if workspace is not None else None
+    args = [ctypes.byref(d), _ptr(u, "u", at, s["act"], True), _ptr(delta_raw, "delta_raw", at, s["act"], True),
+            _ptr(a_log, "a_log", f, s["a_log"], True), _ptr(xdbl, "xdbl", at, s["xdbl"], True),
+            _ptr(D, "D", f, s["vec"]), _ptr(z, "z", at, s["act"]), _ptr(y_saved, "y_saved", at, s["act"]),
+            _ptr(ckpt, "ckpt", f, s["ckpt"], True), _ptr(dout, "dout", at, s["act"], True),
+            _ptr(d_u, "d_u", at, s["act"], True), _ptr(d_delta_raw, "d_delta_raw", at, s["act"], True),
+            _ptr(d_z, "d_z", at, s["act"]), _ptr(d_xdbl, "d_xdbl", f, s["xdbl"], True),
+            _ptr(d_a_log, "d_a_log", f, s["a_log"], True), _ptr(d_D, "d_D", f, s["vec"], True),
+            ws, ctypes.c_size_t(0 if workspace is None else workspace.numel()), _stream(stream)]
+    _check(load().mamba_scan_bwd(*args))
+
+
+def conv_scan_gate_fwd(d: Dims, x, conv_w, conv_b, conv_state0, delta_raw, a_log, xdbl, D=None, z=None,
+                       h0=None, *, out, u_out=None, y_save=None, h_last=None, conv_state_last=None, ckpt=None,
+                       stream=None):
+    s, at, f = _shapes(d), d.act_dtype, torch.float32
+    args = [ctypes.byref(d), _ptr(x, "x", at, s["act"], True), _ptr(conv_w, "conv_w", f, s["conv_w"], True),
+            _ptr(conv_b, "conv_b", f, s["vec"]), _ptr(conv_state0, "conv_state0", f, s["conv_state"]),
+            _ptr(delta_raw, "delta_raw", at, s["act"], True), _ptr(a_log, "a_log", f, s["a_log"], True),
+            _ptr(xdbl, "xdbl", at, s["xdbl"], True), _ptr(D, "D", f, s["vec"]), _ptr(z, "z", at, s["act"]),
+            _ptr(h0, "h0", f, s["state"]), _ptr(out, "out", at, s["act"], True),
+            _ptr(u_out, "u_out", at, s["act"]), _ptr(y_save, "y_save", at, s["act"]),
+            _ptr(h_last, "h_last", f, s["state"]), _ptr(conv_state_last, "conv_state_last", f, s["conv_state"]),
+            _ptr(ckpt, "ckpt", f, s["ckpt"]), _stream(stream)]
+    _check(load().mamba_conv_scan_gate_fwd(*args))
+
+
+def conv_scan_gate_bwd(d: Dims, x, conv_w, conv_b, conv_state0, delta_raw, a_log, xdbl, D, z, y_saved, ckpt,
+                       dout, d_u_extra=None, *, d_x, d_delta_raw, d_z, d_xdbl, d_a_log, d_D, d_conv_w, d_conv_b,
+                       workspace, stream=None):
+    s, at, f = _shapes(d), d.act_dtype, torch.float32
+    ws = _ptr(workspace, "workspace", torch.uint8, (workspace.numel(),), True) if workspace is not None else None
+    args = [ctypes.byref(d), _ptr(x, "x", at, s["act"], True), _ptr(conv_w, "conv_w", f, s["conv_w"], True),
+            _ptr(conv_b, "conv_b", f, s["vec"]), _ptr(conv_state0, "conv_state0", f, s["conv_state"]),
+            _ptr(delta_raw, "delta_raw", at, s["act"], True), _ptr(a_log, "a_log", f, s["a_log"], True),
+            _ptr(xdbl, "xdbl", at, s["xdbl"], True), _ptr(D, "D", f, s["vec"]), _ptr(z, "z", at, s["act"]),
+            _ptr(y_saved, "y_saved", at, s["act"]), _ptr(ckpt, "ckpt", f, s["ckpt"], True),
+            _ptr(dout, "dout", at, s["act"], True), _ptr(d_u_extra, "d_u_extra", at, s["act"]),
+            _ptr(d_x, "d_x", at, s["act"], True), _ptr(d_delta_raw, "d_delta_raw", at, s["act"], True),
+            _ptr(d_z, "d_z", at, s["act"]), _ptr(d_xdbl, "d_xdbl", f, s["xdbl"], True),
+            _ptr(d_a_log, "d_a_log", f, s["a_log"], True), _ptr(d_D, "d_D", f, s["vec"], True),
+            _ptr(d_conv_w, "d_conv_w", f, s["conv_w"], True), _ptr(d_conv_b, "d_conv_b", f, s["vec"], True),
+            ws, ctypes.c_size_t(0 if workspace is None else workspace.numel()), _stream(stream)]
+    _check(load().mamba_conv_scan_gate_bwd(*args))

@@ -1,0 +1,362 @@
+// C ABI of the selective-scan layer core: argument checks, workspace
+// layout and kernel dispatch.  Declared in include/mamba_scan.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "mamba_scan.h"
+#include "scan_common.h"
+
+namespace mscan {
+hipError_t launch_fwd_f32(const FwdArgs& p, int ds, int spl, hipStream_t st);
+hipError_t launch_fwd_bf16(const FwdArgs& p, int ds, int spl, hipStream_t st);
+hipError_t launch_fwd_f16(const FwdArgs& p, int ds, int spl, hipStream_t st);
+hipError_t launch_bwd_f32(const BwdArgs& p, int ds, int L, hipStream_t st);
+hipError_t launch_bwd_bf16(const BwdArgs& p, int ds, int L, hipStream_t st);
+hipError_t launch_bwd_f16(const BwdArgs& p, int ds, int L, hipStream_t st);
+hipError_t launch_reduce(const ReduceArgs& p, hipStream_t st);
+
+static hipError_t launch_fwd(const FwdArgs& p, Act act, int ds, int spl, hipStream_t st) {
+  switch (act) {
+    case Act::F32: return launch_fwd_f32(p, ds, spl, st);
+    case Act::BF16: return launch_fwd_bf16(p, ds, spl, st);
+    case Act::F16: return launch_fwd_f16(p, ds, spl, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_bwd(const BwdArgs& p, Act act, int ds, int L, hipStream_t st) {
+  switch (act) {
+    case Act::F32: return launch_bwd_f32(p, ds, L, st);
+    case Act::BF16: return launch_bwd_bf16(p, ds, L, st);
+    case Act::F16: return launch_bwd_f16(p, ds, L, st);
+  }
+  return hipErrorInvalidValue;
+}
+}  // namespace mscan
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fn, const std::string& msg) {
+  g_err = std::string(fn) + ": " + msg;
+  return code;
+}
+
+struct Plan {
+  int64_t B, T, Di, Ds, R, X, nC, nG;
+  int K;          // conv taps (0 for the scan entry points)
+  int L;          // checkpoint interval
+  int spl_fwd;    // states per lane in the forward kernel
+  mscan::Act act;
+  int esize;      // bytes per activation element
+};
+
+constexpr int64_t kMaxElems = int64_t(1) << 46;
+
+int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
+  if (!d) return fail(MAMBA_ERR_INVALID, fn, "dims is NULL");
+  if (d->reserved != 0) return fail(MAMBA_ERR_INVALID, fn, "dims.reserved must be 0");
+  if (d->act < 0 || d->act > 2) return fail(MAMBA_ERR_INVALID, fn, "dims.act is not a mamba_dtype_t");
+  if (d->batch < 1 || d->batch > 65535)
+    return fail(d->batch < 1 ? MAMBA_ERR_INVALID : MAMBA_ERR_CAPACITY, fn, "batch must be in [1, 65535]");
+  if (d->seqlen < 1) return fail(MAMBA_ERR_INVALID, fn, "seqlen must be >= 1");
+  if (d->d_inner < 4 || d->d_inner % 4 != 0)
+    return fail(MAMBA_ERR_INVALID, fn, "d_inner must be a positive multiple of 4");
+  if (d->dt_rank < 0) return fail(MAMBA_ERR_INVALID, fn, "dt_rank must be >= 0");
+  if (d->d_state < 1) return fail(MAMBA_ERR_INVALID, fn, "d_state must be >= 1");
+  if (d->d_state != 4 && d->d_state != 8 && d->d_state != 16 && d->d_state != 32)
+    return fail(MAMBA_ERR_UNSUPPORTED, fn, "d_state must be 4, 8, 16 or 32");
+  if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
+    return fail(d->chunk < 0 ? MAMBA_ERR_INVALID : MAMBA_ERR_UNSUPPORTED, fn,
+                "chunk must be 0 (default 32), 16, 32 or 64");
+  const int L = d->chunk ? d->chunk : 32;
+  // the backward keeps L steps of state in registers: supported pairs
+  const bool pair_ok = (d->d_state == 4) || (d->d_state <= 16 && L <= 32) || (d->d_state == 32 && L == 16);
+  if (!pair_ok)
+    return fail(MAMBA_ERR_UNSUPPORTED, fn,
+                "chunk must be <= 32 for d_state 8 or 16, and 16 for d_state 32");
+  int K = 0;
+  if (fused) {
+    if (d->d_conv < 1) return fail(MAMBA_ERR_INVALID, fn, "d_conv must be >= 1");
+    if (d->d_conv > 4) return fail(MAMBA_ERR_UNSUPPORTED, fn, "d_conv must be <= 4");
+    K = d->d_conv;
+  }
+  const int64_t X = d->dt_rank + 2 * d->d_state;
+  if (d->seqlen > kMaxElems / d->batch || d->batch * d->seqlen > kMaxElems / (d->d_inner > X ? d->d_inner : X))
+    return fail(MAMBA_ERR_CAPACITY, fn, "B * T * max(d_inner, xdbl row) exceeds 2^46 elements");
+  pl->B = d->batch;
+  pl->T = d->seqlen;
+  pl->Di = d->d_inner;
+  pl->Ds = d->d_state;
+  pl->R = d->dt_rank;
+  pl->X = X;
+  pl->L = L;
+  pl->nC = (d->seqlen + L - 1) / L;
+  pl->nG = (d->d_inner + 63) / 64;
+  pl->K = K;
+  pl->spl_fwd = d->d_state >= 8 ? 2 : 1;
+  pl->act = static_cast<mscan::Act>(d->act);
+  pl->esize = d->act == MAMBA_F32 ? 4 : 2;
+  return MAMBA_OK;
+}
+
+bool misaligned(const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+// Checks one pointer argument; `need` false allows NULL.
+int check_ptr(const char* fn, const char* name, const void* p, bool need, int align) {
+  if (!p) return need ? fail(MAMBA_ERR_INVALID, fn, std::string(name) + " is NULL") : MAMBA_OK;
+  if (misaligned(p, align))
+    return fail(MAMBA_ERR_INVALID, fn, std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+  return MAMBA_OK;
+}
+
+#define MSCAN_TRY(expr)               \
+  do {                                \
+    int rc_ = (expr);                 \
+    if (rc_ != MAMBA_OK) return rc_;  \
+  } while (0)
+
+int64_t param_width(const Plan& pl) { return pl.Ds + 1 + (pl.K > 0 ? pl.K + 1 : 0); }
+
+size_t bc_part_bytes(const Plan& pl) {
+  return static_cast<size_t>(pl.nG) * pl.B * pl.T * 2 * pl.Ds * sizeof(float);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t workspace_need(const Plan& pl) {
+  return align256(bc_part_bytes(pl)) + static_cast<size_t>(pl.B) * pl.Di * param_width(pl) * sizeof(float);
+}
+
+int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_w, const float* conv_b,
+               const float* conv_state0, const void* delta_raw, const float* a_log, const void* xdbl,
+               const float* D, const void* z, const float* h0, void* out, void* u_out, void* y_save,
+               float* h_last, float* conv_state_last, float* ckpt, void* stream) {
+  const int e = pl.esize;
+  MSCAN_TRY(check_ptr(fn, pl.K ? "x" : "u", x, true, e));
+  MSCAN_TRY(check_ptr(fn, "delta_raw", delta_raw, true, e));
+  MSCAN_TRY(check_ptr(fn, "a_log", a_log, true, 4));
+  MSCAN_TRY(check_ptr(fn, "xdbl", xdbl, true, e));
+  MSCAN_TRY(check_ptr(fn, "D", D, false, 4));
+  MSCAN_TRY(check_ptr(fn, "z", z, false, e));
+  MSCAN_TRY(check_ptr(fn, "h0", h0, false, 4));
+  MSCAN_TRY(check_ptr(fn, "out", out, true, e));
+  MSCAN_TRY(check_ptr(fn, "y_save", y_save, false, e));
+  MSCAN_TRY(check_ptr(fn, "h_last", h_last, false, 4));
+  MSCAN_TRY(check_ptr(fn, "ckpt", ckpt, false, 4));
+  if (pl.K > 0) {
+    MSCAN_TRY(check_ptr(fn, "conv_w", conv_w, true, 4));
+    MSCAN_TRY(check_ptr(fn, "conv_b", conv_b, false, 4));
+    MSCAN_TRY(check_ptr(fn, "conv_state0", conv_state0, false, 4));
+    MSCAN_TRY(check_ptr(fn, "u_out", u_out, false, e));
+    MSCAN_TRY(check_ptr(fn, "conv_state_last", conv_state_last, false, 4));
+  }
+  mscan::FwdArgs a{};
+  a.x = x;
+  a.delta_raw = delta_raw;
+  a.a_log = a_log;
+  a.xdbl = xdbl;
+  a.D = D;
+  a.z = z;
+  a.h0 = h0;
+  a.conv_w = conv_w;
+  a.conv_b = conv_b;
+  a.conv_state0 = conv_state0;
+  a.out = out;
+  a.u_out = u_out;
+  a.y_save = y_save;
+  a.h_last = h_last;
+  a.conv_state_last = conv_state_last;
+  a.ckpt = ckpt;
+  a.B = pl.B;
+  a.T = pl.T;
+  a.Di = pl.Di;
+  a.R = pl.R;
+  a.X = pl.X;
+  a.nC = pl.nC;
+  a.K = pl.K;
+  a.L = pl.L;
+  hipError_t err = mscan::launch_fwd(a, pl.act, static_cast<int>(pl.Ds), pl.spl_fwd,
+                                     static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("forward launch: ") + hipGetErrorString(err));
+  g_err.clear();
+  return MAMBA_OK;
+}
+
+int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv_w, const float* conv_b,
+                const float* conv_state0, const void* delta_raw, const float* a_log, const void* xdbl,
+                const float* D, const void* z, const void* y_saved, const float* ckpt, const void* dout,
+                const void* d_u_extra, void* d_x, void* d_delta_raw, void* d_z, float* d_xdbl,
+                float* d_a_log, float* d_D, float* d_conv_w, float* d_conv_b, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const int e = pl.esize;
+  MSCAN_TRY(check_ptr(fn, pl.K ? "x" : "u", x, true, e));
+  MSCAN_TRY(check_ptr(fn, "delta_raw", delta_raw, true, e));
+  MSCAN_TRY(check_ptr(fn, "a_log", a_log, true, 4));
+  MSCAN_TRY(check_ptr(fn, "xdbl", xdbl, true, e));
+  MSCAN_TRY(check_ptr(fn, "D", D, false, 4));
+  MSCAN_TRY(check_ptr(fn, "z", z, false, e));
+  MSCAN_TRY(check_ptr(fn, "y_saved", y_saved, z != nullptr, e));
+  MSCAN_TRY(check_ptr(fn, "ckpt", ckpt, true, 4));
+  MSCAN_TRY(check_ptr(fn, "dout", dout, true, e));
+  MSCAN_TRY(check_ptr(fn, pl.K ? "d_x" : "d_u", d_x, true, e));
+  MSCAN_TRY(check_ptr(fn, "d_delta_raw", d_delta_raw, true, e));
+  MSCAN_TRY(check_ptr(fn, "d_z", d_z, z != nullptr, e));
+  MSCAN_TRY(check_ptr(fn, "d_xdbl", d_xdbl, true, 4));
+  MSCAN_TRY(check_ptr(fn, "d_a_log", d_a_log, true, 4));
+  MSCAN_TRY(check_ptr(fn, "d_D", d_D, true, 4));
+  if (pl.K > 0) {
+    MSCAN_TRY(check_ptr(fn, "conv_w", conv_w, true, 4));
+    MSCAN_TRY(check_ptr(fn, "conv_b", conv_b, false, 4));
+    MSCAN_TRY(check_ptr(fn, "conv_state0", conv_state0, false, 4));
+    MSCAN_TRY(check_ptr(fn, "d_u_extra", d_u_extra, false, e));
+    MSCAN_TRY(check_ptr(fn, "d_conv_w", d_conv_w, true, 4));
+    MSCAN_TRY(check_ptr(fn, "d_conv_b", d_conv_b, true, 4));
+  }
+  MSCAN_TRY(check_ptr(fn, "workspace", workspace, true, 256));
+  const size_t need = workspace_need(pl);
+  if (workspace_bytes < need)
+    return fail(MAMBA_ERR_CAPACITY, fn,
+                "workspace_bytes " + std::to_string(workspace_bytes) + " < required " + std::to_string(need));
+  float* part_bc = static_cast<float*>(workspace);
+  float* part_par = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(bc_part_bytes(pl)));
+  const int PW = static_cast<int>(param_width(pl));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  mscan::BwdArgs a{};
+  a.x = x;
+  a.delta_raw = delta_raw;
+  a.a_log = a_log;
+  a.xdbl = xdbl;
+  a.D = D;
+  a.z = z;
+  a.y_saved = y_saved;
+  a.conv_w = conv_w;
+  a.conv_b = conv_b;
+  a.conv_state0 = conv_state0;
+  a.ckpt = ckpt;
+  a.dout = dout;
+  a.d_u_extra = d_u_extra;
+  a.d_x = d_x;
+  a.d_delta_raw = d_delta_raw;
+  a.d_z = d_z;
+  a.part_bc = part_bc;
+  a.part_par = part_par;
+  a.B = pl.B;
+  a.T = pl.T;
+  a.Di = pl.Di;
+  a.R = pl.R;
+  a.X = pl.X;
+  a.nC = pl.nC;
+  a.K = pl.K;
+  a.L = pl.L;
+  a.PW = PW;
+  hipError_t err = mscan::launch_bwd(a, pl.act, static_cast<int>(pl.Ds), pl.L, st);
+  if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("backward launch: ") + hipGetErrorString(err));
+
+  mscan::ReduceArgs r{};
+  r.part_bc = part_bc;
+  r.part_par = part_par;
+  r.d_xdbl = d_xdbl;
+  r.d_a_log = d_a_log;
+  r.d_D = d_D;
+  r.d_conv_w = d_conv_w;
+  r.d_conv_b = d_conv_b;
+  r.B = pl.B;
+  r.T = pl.T;
+  r.Di = pl.Di;
+  r.Ds = pl.Ds;
+  r.R = pl.R;
+  r.X = pl.X;
+  r.nG = pl.nG;
+  r.K = pl.K;
+  r.PW = PW;
+  err = mscan::launch_reduce(r, st);
+  if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("reduce launch: ") + hipGetErrorString(err));
+  g_err.clear();
+  return MAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mamba_abi_version(void) { return MAMBA_SCAN_ABI_VERSION; }
+
+const char* mamba_last_error(void) { return g_err.c_str(); }
+
+int mamba_ckpt_bytes(const mamba_dims_t* dims, size_t* bytes) {
+  const char* fn = "mamba_ckpt_bytes";
+  Plan pl;
+  MSCAN_TRY(plan_dims(dims, false, fn, &pl));
+  if (!bytes) return fail(MAMBA_ERR_INVALID, fn, "bytes is NULL");
+  *bytes = static_cast<size_t>(pl.B) * pl.nC * pl.Ds * pl.Di * sizeof(float);
+  g_err.clear();
+  return MAMBA_OK;
+}
+
+int mamba_workspace_bytes(const mamba_dims_t* dims, size_t* bytes) {
+  const char* fn = "mamba_workspace_bytes";
+  Plan pl;
+  const bool fused = dims && dims->d_conv > 0;
+  MSCAN_TRY(plan_dims(dims, fused, fn, &pl));
+  if (!bytes) return fail(MAMBA_ERR_INVALID, fn, "bytes is NULL");
+  *bytes = workspace_need(pl);
+  g_err.clear();
+  return MAMBA_OK;
+}
+
+int mamba_scan_fwd(const mamba_dims_t* dims, const void* u, const void* delta_raw, const float* a_log,
+                   const void* xdbl, const float* D, const void* z, const float* h0, void* out,
+                   void* y_save, float* h_last, float* ckpt, void* stream) {
+  const char* fn = "mamba_scan_fwd";
+  Plan pl;
+  MSCAN_TRY(plan_dims(dims, false, fn, &pl));
+  return do_forward(fn, pl, u, nullptr, nullptr, nullptr, delta_raw, a_log, xdbl, D, z, h0, out, nullptr,
+                    y_save, h_last, nullptr, ckpt, stream);
+}
+
+int mamba_scan_bwd(const mamba_dims_t* dims, const void* u, const void* delta_raw, const float* a_log,
+                   const void* xdbl, const float* D, const void* z, const void* y_saved, const float* ckpt,
+                   const void* dout, void* d_u, void* d_delta_raw, void* d_z, float* d_xdbl, float* d_a_log,
+                   float* d_D, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "mamba_scan_bwd";
+  Plan pl;
+  MSCAN_TRY(plan_dims(dims, false, fn, &pl));
+  return do_backward(fn, pl, u, nullptr, nullptr, nullptr, delta_raw, a_log, xdbl, D, z, y_saved, ckpt, dout,
+                     nullptr, d_u, d_delta_raw, d_z, d_xdbl, d_a_log, d_D, nullptr, nullptr, workspace,
+                     workspace_bytes, stream);
+}
+
+int mamba_conv_scan_gate_fwd(const mamba_dims_t* dims, const void* x, const float* conv_w, const float* conv_b,
+                             const float* conv_state0, const void* delta_raw, const float* a_log,
+                             const void* xdbl, const float* D, const void* z, const float* h0, void* out,
+                             void* u_out, void* y_save, float* h_last, float* conv_state_last, float* ckpt,
+                             void* stream) {
+  const char* fn = "mamba_conv_scan_gate_fwd";
+  Plan pl;
+  MSCAN_TRY(plan_dims(dims, true, fn, &pl));
+  return do_forward(fn, pl, x, conv_w, conv_b, conv_state0, delta_raw, a_log, xdbl, D, z, h0, out, u_out,
+                    y_save, h_last, conv_state_last, ckpt, stream);
+}
+
+int mamba_conv_scan_gate_bwd(const mamba_dims_t* dims, const void* x, const float* conv_w, const float* conv_b,
+                             const float* conv_state0, const void* delta_raw, const float* a_log,
+                             const void* xdbl, const float* D, const void* z, const void* y_saved,
+                             const float* ckpt, const void* dout, const void* d_u_extra, void* d_x,
+                             void* d_delta_raw, void* d_z, float* d_xdbl, float* d_a_log, float* d_D,
+                             float* d_conv_w, float* d_conv_b, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  const char* fn = "mamba_conv_scan_gate_bwd";
+  Plan pl;
+  MSCAN_TRY(plan_dims(dims, true, fn, &pl));
+  return do_backward(fn, pl, x, conv_w, conv_b, conv_state0, delta_raw, a_log, xdbl, D, z, y_saved, ckpt, dout,
+                     d_u_extra, d_x, d_delta_raw, d_z, d_xdbl, d_a_log, d_D, d_conv_w, d_conv_b, workspace,
+                     workspace_bytes, stream);
+}
+
+}  // extern "C"

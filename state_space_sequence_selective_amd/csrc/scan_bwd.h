@@ -1,0 +1,379 @@
+// Backward of the selective-scan layer core (gfx950): the reverse-time
+// adjoint of scan_fwd.hip.
+//
+// What it produces follows the backward scratch of the mamba-rs 0.3.1
+// forward_mixed.rs page (GpuMambaMixedTrainScratch): d_y from the gate,
+// d_gate (= d_z), d_delta -> d_delta_raw (softplus backward), d_u, d_B and
+// d_C reduced over channels, per-sample d_D and d_a_log, and the conv1d
+// weight / bias gradients.  Per step t (reverse time) and state n:
+//   dh      = dy_t C_t[n] + carry          (dL/dh_t)
+//   d_C     += dy_t h_t        d_B += dh delta_t u_t
+//   d_u_t   += dh delta_t B_t  d_delta_t += dh (B_t u_t + A dA h_{t-1})
+//   d_A     += dh delta_t dA h_{t-1}       carry = dh dA
+// with d_u_t += D dy_t, d_D += dy_t u_t and d_a_log = A d_A (A = -exp(a_log)).
+//
+// Mapping.  As in the forward: a workgroup owns 64 channels (lanes) of one
+// batch row; wave g owns states [g*SPL, (g+1)*SPL).  The sequence is walked
+// backwards in tiles of L steps, L being the checkpoint interval:
+//   stage     : per (t, channel) item, delta, delta*u and dy = dout*silu(z)
+//               go to LDS; d_z = dout * y * silu'(z) is written at once from
+//               the saved y; the rest of the item's scalars stay in the
+//               staging thread's registers for the epilogue.
+//   recompute : from ckpt, each wave re-runs its states over the tile and
+//               keeps h_t and dA_t for every step in registers (SPL*L = 64
+//               of each).  Every G steps the wave sums dy*h over its 64
+//               channels (d_C) in a wave-private LDS block.
+//   reverse   : G steps at a time, each wave runs the adjoint for its states,
+//               sums delta*u*dh over its channels (d_B) the same way, and
+//               leaves per-(t, channel) partials of sum_n dh B and
+//               sum_n dh A dA h_{t-1} in LDS; the epilogue threads add the
+//               partials of all waves and write d_u (or, fused, push d_u
+//               through SiLU and the conv) and d_delta_raw.
+// d_B / d_C per channel group, and d_a_log / d_D / conv grads per batch row,
+// go to a workspace; mscan_reduce_kernel adds them up in a fixed order.
+#pragma once
+#include "scan_common.h"
+
+namespace mscan {
+
+// wave-local ordering point for LDS traffic between lanes of one wave
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Sum a wave-private block red[c][o] (64 channels x NO outputs, row stride
+// NO + 1) over c.  Returns the total for output o = lane % NO on the lanes
+// with lane / NO == 0.
+template <int NO>
+__device__ __forceinline__ float wave_channel_sum(const float* red, int lane) {
+  static_assert(NO <= 64 && (64 % NO) == 0, "outputs per block");
+  constexpr int LPO = 64 / NO;     // lanes per output
+  constexpr int CPL = 64 / LPO;    // channels per lane
+  const int o = lane % NO, part = lane / NO;
+  float acc = 0.0f;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) acc += red[(part * CPL + m) * (NO + 1) + o];
+#pragma unroll
+  for (int off = NO; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  return acc;
+}
+
+template <Act A, int DS, int SPL, int L, bool FUSED>
+__global__ void __launch_bounds__(64 * (DS / SPL))
+scan_bwd_kernel(const BwdArgs p) {
+  constexpr int G = DS / SPL;          // waves
+  constexpr int NT = 64 * G;
+  constexpr int SUB = G;               // steps per reverse sub-tile
+  static_assert(L % SUB == 0, "sub-tiles must tile the chunk");
+  constexpr int NSUB = L / SUB;        // = stage items per thread
+  constexpr int NO = SUB * SPL;        // channel sums per wave per sub-tile
+  constexpr int KMAX = FUSED ? 4 : 1;   // conv taps supported: 1..4
+  using io = IO<A>;
+
+  __shared__ float s_dl[L][64];        // delta
+  __shared__ float s_du[L][64];        // delta * u
+  __shared__ float s_dy[L][64];        // dy = dout * silu(z)
+  __shared__ float s_bc[L][2 * DS];
+  __shared__ float s_su[G][SUB][64];   // per-wave sum_n dh B
+  __shared__ float s_sd[G][SUB][64];   // per-wave sum_n dh A dA h_{t-1}
+  __shared__ float s_red[G][64 * (NO + 1)];
+  __shared__ float s_dp[SUB + KMAX][64];
+
+  const int tid = threadIdx.x;
+  const int c = tid & 63;
+  const int g = tid >> 6;
+  const int64_t b = blockIdx.y;
+  const int64_t cg = blockIdx.x;
+  const int64_t i = cg * 64 + c;
+  const bool on = i < p.Di;
+  const int64_t T = p.T, Di = p.Di, BT = p.B * p.T;
+  const bool gate = p.z != nullptr;
+  const int K = FUSED ? p.K : 0;
+  float* red = s_red[g];
+
+  float a2[SPL], an[SPL], carry[SPL], dacc[SPL];
+#pragma unroll
+  for (int s = 0; s < SPL; ++s) {
+    const int n = g * SPL + s;
+    an[s] = on ? -expf(p.a_log[i * DS + n]) : 0.0f;
+    a2[s] = an[s] * kLog2e;
+    carry[s] = 0.0f;
+    dacc[s] = 0.0f;
+  }
+  const float Dv = (on && p.D) ? p.D[i] : 0.0f;
+  float cw[KMAX];
+  float cb = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) cw[k] = (FUSED && on && k < K) ? p.conv_w[i * K + k] : 0.0f;
+  if (FUSED) cb = (on && p.conv_b) ? p.conv_b[i] : 0.0f;
+  float acc_dD = 0.0f, acc_cb = 0.0f;
+  float acc_cw[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) acc_cw[k] = 0.0f;
+  if (FUSED)
+    for (int j = tid; j < (SUB + KMAX) * 64; j += NT) (&s_dp[0][0])[j] = 0.0f;
+
+  const int64_t ntiles = (T + L - 1) / L;
+  for (int64_t kt = ntiles - 1; kt >= 0; --kt) {
+    const int64_t t0 = kt * L;
+    const int len = static_cast<int>(T - t0 < L ? T - t0 : L);
+    float e_dl[NSUB], e_u[NSUB], e_sig[NSUB], e_dy[NSUB], e_dsp[NSUB];
+
+    // ---------------------------------------------------------------- stage
+#pragma unroll
+    for (int k = 0; k < NSUB; ++k) {
+      const int tt = g + G * k;
+      float dl = 0.0f, u = 0.0f, sig = 0.0f, dy = 0.0f, dsp = 0.0f;
+      if (tt < len && on) {
+        const int64_t row = b * T + t0 + tt;
+        const int64_t e = row * Di + i;
+        const float dr = io::ld(p.delta_raw, e);
+        dl = softplus(dr);
+        sig = sigmoid(dr);
+        if (FUSED) {
+          float pre = cb;
+#pragma unroll
+          for (int k2 = 0; k2 < KMAX; ++k2) {
+            if (k2 < K) {
+              const int64_t s = t0 + tt - (K - 1) + k2;
+              float xv;
+              if (s >= 0) xv = io::ld(p.x, (b * T + s) * Di + i);
+              else xv = p.conv_state0 ? p.conv_state0[(b * Di + i) * K + (K + s)] : 0.0f;
+              pre = fmaf(cw[k2], xv, pre);
+            }
+          }
+          const float sp = sigmoid(pre);
+          u = pre * sp;
+          dsp = sp * (1.0f + pre * (1.0f - sp));
+        } else {
+          u = io::ld(p.x, e);
+        }
+        const float go = io::ld(p.dout, e);
+        if (gate) {
+          const float zv = io::ld(p.z, e);
+          const float sz = sigmoid(zv);
+          dy = go * zv * sz;
+          const float yv = io::ld(p.y_saved, e);
+          io::st(p.d_z, e, go * yv * (sz * (1.0f + zv * (1.0f - sz))));
+        } else {
+          dy = go;
+        }
+      }
+      s_dl[tt][c] = dl;
+      s_du[tt][c] = dl * u;
+      s_dy[tt][c] = dy;
+      e_dl[k] = dl;
+      e_u[k] = u;
+      e_sig[k] = sig;
+      e_dy[k] = dy;
+      e_dsp[k] = dsp;
+    }
+    for (int j = tid; j < L * 2 * DS; j += NT) {
+      const int tt = j / (2 * DS), m = j % (2 * DS);
+      s_bc[tt][m] = tt < len ? io::ld(p.xdbl, (b * T + t0 + tt) * p.X + p.R + m) : 0.0f;
+    }
+    __syncthreads();
+
+    // ------------------------------------------------------------ recompute
+    float hs[L][SPL], das[L][SPL];
+    {
+      float h[SPL];
+#pragma unroll
+      for (int s = 0; s < SPL; ++s)
+        h[s] = on ? p.ckpt[((b * p.nC + kt) * DS + g * SPL + s) * Di + i] : 0.0f;
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) {
+#pragma unroll
+        for (int q = 0; q < SUB; ++q) {
+          const int tt = sb * SUB + q;
+          if (tt < len) {
+            const float dl = s_dl[tt][c];
+            const float du = s_du[tt][c];
+            const float dy = s_dy[tt][c];
+#pragma unroll
+            for (int s = 0; s < SPL; ++s) {
+              const int n = g * SPL + s;
+              const float dA = exp2_fast(dl * a2[s]);
+              h[s] = fmaf(dA, h[s], du * s_bc[tt][n]);
+              hs[tt][s] = h[s];
+              das[tt][s] = dA;
+              red[c * (NO + 1) + q * SPL + s] = dy * h[s];
+            }
+          } else {
+#pragma unroll
+            for (int s = 0; s < SPL; ++s) {
+              hs[tt][s] = 0.0f;
+              das[tt][s] = 0.0f;
+              red[c * (NO + 1) + q * SPL + s] = 0.0f;
+            }
+          }
+          // keep the scheduler from hoisting later steps' LDS reads (each
+          // would hold a register across the whole unrolled chunk)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        wave_lds_sync();
+        const float v = wave_channel_sum<NO>(red, c);
+        if (c < NO) {
+          const int q = c / SPL, s = c % SPL;
+          const int tt = sb * SUB + q;
+          if (tt < len)
+            p.part_bc[(cg * BT + b * T + t0 + tt) * (2 * DS) + DS + g * SPL + s] = v;
+        }
+        wave_lds_sync();
+      }
+    }
+
+    // -------------------------------------------------------------- reverse
+#pragma unroll
+    for (int sb = NSUB - 1; sb >= 0; --sb) {
+#pragma unroll
+      for (int q = SUB - 1; q >= 0; --q) {
+        const int tt = sb * SUB + q;
+        float su = 0.0f, sd = 0.0f;
+        if (tt < len) {
+          const float dl = s_dl[tt][c];
+          const float du = s_du[tt][c];
+          const float dy = s_dy[tt][c];
+#pragma unroll
+          for (int s = 0; s < SPL; ++s) {
+            const int n = g * SPL + s;
+            const float Bn = s_bc[tt][n];
+            const float Cn = s_bc[tt][DS + n];
+            const float dh = fmaf(dy, Cn, carry[s]);
+            const float dah = fmaf(-du, Bn, hs[tt][s]);   // dA h_{t-1} = h_t - delta u B
+            const float qv = dh * dah;
+            dacc[s] = fmaf(qv, dl, dacc[s]);
+            carry[s] = dh * das[tt][s];
+            su = fmaf(dh, Bn, su);
+            sd = fmaf(qv, an[s], sd);
+            red[c * (NO + 1) + q * SPL + s] = dh * du;
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < SPL; ++s) red[c * (NO + 1) + q * SPL + s] = 0.0f;
+        }
+        s_su[g][q][c] = su;
+        s_sd[g][q][c] = sd;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wave_lds_sync();
+      {
+        const float v = wave_channel_sum<NO>(red, c);
+        if (c < NO) {
+          const int q = c / SPL, s = c % SPL;
+          const int tt = sb * SUB + q;
+          if (tt < len)
+            p.part_bc[(cg * BT + b * T + t0 + tt) * (2 * DS) + g * SPL + s] = v;
+        }
+      }
+      __syncthreads();
+
+      // ---- epilogue: item (t0 + sb*SUB + g, channel c); stage slot k = sb
+      const int tt = sb * SUB + g;
+      const bool live = tt < len && on;
+      const int64_t e = (b * T + t0 + tt) * Di + i;
+      float dp = 0.0f;
+      if (live) {
+        float su = 0.0f, sd = 0.0f;
+#pragma unroll
+        for (int w = 0; w < G; ++w) {
+          su += s_su[w][g][c];
+          sd += s_sd[w][g][c];
+        }
+        float du = fmaf(e_dl[sb], su, Dv * e_dy[sb]);
+        const float ddl = fmaf(e_u[sb], su, sd);
+        io::st(p.d_delta_raw, e, ddl * e_sig[sb]);
+        acc_dD = fmaf(e_dy[sb], e_u[sb], acc_dD);
+        if (FUSED) {
+          if (p.d_u_extra) du += io::ld(p.d_u_extra, e);
+          dp = du * e_dsp[sb];
+          acc_cb += dp;
+#pragma unroll
+          for (int k2 = 0; k2 < KMAX; ++k2) {
+            if (k2 < K) {
+              const int64_t s = t0 + tt - (K - 1) + k2;
+              float xv;
+              if (s >= 0) xv = io::ld(p.x, (b * T + s) * Di + i);
+              else xv = p.conv_state0 ? p.conv_state0[(b * Di + i) * K + (K + s)] : 0.0f;
+              acc_cw[k2] = fmaf(dp, xv, acc_cw[k2]);
+            }
+          }
+        } else {
+          io::st(p.d_x, e, du);
+        }
+      }
+      if (FUSED) {
+        // d_x[s] = sum_k w_k dp[s + K-1-k]; rows >= SUB of s_dp hold the
+        // first K-1 dp of the later sub-tile (zero past the sequence end)
+        s_dp[g][c] = dp;
+        __syncthreads();
+        if (live) {
+          float gx = 0.0f;
+#pragma unroll
+          for (int k2 = 0; k2 < KMAX; ++k2)
+            if (k2 < K) gx = fmaf(cw[k2], s_dp[g + K - 1 - k2][c], gx);
+          io::st(p.d_x, e, gx);
+        }
+        __syncthreads();
+        // the K-1 steps after the next sub-tile: this sub-tile's first steps,
+        // then (when SUB < K-1) older entries; descending keeps reads ahead
+        // of writes
+        if (g == 0)
+          for (int j = K - 2; j >= 0; --j) s_dp[SUB + j][c] = s_dp[j][c];
+      }
+      __syncthreads();
+    }
+  }
+
+  // ------------------------------------------------ per batch-row partials
+  const int64_t pb = (b * Di + i) * p.PW;
+  if (on) {
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) p.part_par[pb + g * SPL + s] = an[s] * dacc[s];
+  }
+  const int nq = FUSED ? K + 2 : 1;
+  for (int qd = 0; qd < nq; ++qd) {
+    float v = qd == 0 ? acc_dD : (qd == 1 ? acc_cb : 0.0f);
+#pragma unroll
+    for (int k2 = 0; k2 < KMAX; ++k2)
+      if (qd == k2 + 2) v = acc_cw[k2];
+    s_su[g][0][c] = v;
+    __syncthreads();
+    if (g == 0 && on) {
+      float tot = 0.0f;
+      for (int w = 0; w < G; ++w) tot += s_su[w][0][c];
+      // layout within PW: [Ds a_log | 1 D | K conv_w | 1 conv_b]
+      const int slot = qd == 0 ? DS : (qd == 1 ? DS + 1 + K : DS + 1 + (qd - 2));
+      p.part_par[pb + slot] = tot;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ launch
+template <Act A, int DS, int SPL, int L>
+static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
+  constexpr int G = DS / SPL;
+  dim3 grid(static_cast<unsigned>((p.Di + 63) / 64), static_cast<unsigned>(p.B));
+  if (p.K > 0)
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true>), grid, dim3(64 * G), 0, st, p);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false>), grid, dim3(64 * G), 0, st, p);
+  return hipGetLastError();
+}
+
+template <Act A>
+hipError_t launch_bwd_a(const BwdArgs& p, int ds, int L, hipStream_t st) {
+#define MSCAN_CASE(DS_, L_) \
+  if (ds == DS_ && L == L_) return launch_bwd_t<A, DS_, (64 / L_), L_>(p, st);
+  MSCAN_CASE(4, 16) MSCAN_CASE(4, 32) MSCAN_CASE(4, 64)
+  MSCAN_CASE(8, 16) MSCAN_CASE(8, 32)
+  MSCAN_CASE(16, 16) MSCAN_CASE(16, 32)
+  MSCAN_CASE(32, 16)
+#undef MSCAN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mscan

@@ -1,0 +1,145 @@
+// Device helpers and kernel argument blocks shared by the selective-scan
+// kernels (gfx950).  Every kernel takes ONE argument struct, so no two
+// pointers can be swapped by argument order at a launch site.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mscan {
+
+enum class Act : int { F32 = 0, BF16 = 1, F16 = 2 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- dtype I/O
+template <Act A>
+struct IO;
+
+template <>
+struct IO<Act::F32> {
+  static __device__ __forceinline__ float ld(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  static __device__ __forceinline__ void st(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+};
+
+template <>
+struct IO<Act::BF16> {
+  static __device__ __forceinline__ float ld(const void* p, int64_t i) {
+    const uint32_t b = static_cast<const uint16_t*>(p)[i];
+    return __uint_as_float(b << 16);
+  }
+  // round to nearest even; NaN stays a (quiet) NaN
+  static __device__ __forceinline__ void st(void* p, int64_t i, float v) {
+    const uint32_t u = __float_as_uint(v);
+    uint16_t r;
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+      r = static_cast<uint16_t>((u >> 16) | 0x40u);
+    } else {
+      r = static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
+    static_cast<uint16_t*>(p)[i] = r;
+  }
+};
+
+template <>
+struct IO<Act::F16> {
+  static __device__ __forceinline__ float ld(const void* p, int64_t i) {
+    return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+  }
+  // the hardware conversion rounds to nearest even (default mode)
+  static __device__ __forceinline__ void st(void* p, int64_t i, float v) {
+    static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
+  }
+};
+
+// ---------------------------------------------------------------- math
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// log(1 + e) for e in [0, 1], with the correction that keeps the relative
+// error small when 1 + e rounds (Goldberg, "What every computer scientist
+// should know about floating-point arithmetic", Theorem 4).
+__device__ __forceinline__ float log1p_small(float e) {
+  const float w = 1.0f + e;
+  if (w == 1.0f) return e;
+  return __builtin_amdgcn_logf(w) * 0.6931471805599453f * (e / (w - 1.0f));
+}
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|)
+__device__ __forceinline__ float softplus(float x) {
+  return fmaxf(x, 0.0f) + log1p_small(exp2_fast(-fabsf(x) * kLog2e));
+}
+
+// logistic sigmoid; exp2 of a large positive argument gives +inf and the
+// reciprocal then gives 0, which is the right limit.
+__device__ __forceinline__ float sigmoid(float x) {
+  return rcp_fast(1.0f + exp2_fast(-x * kLog2e));
+}
+
+// ---------------------------------------------------------------- arguments
+struct FwdArgs {
+  const void* x;            // u (scan entry) or conv input (fused entry) [B,T,Di]
+  const void* delta_raw;    // [B,T,Di]
+  const float* a_log;       // [Di,Ds]
+  const void* xdbl;         // [B,T,X]
+  const float* D;           // [Di] or null
+  const void* z;            // [B,T,Di] or null
+  const float* h0;          // [B,Di,Ds] or null
+  const float* conv_w;      // [Di,K] (K > 0)
+  const float* conv_b;      // [Di] or null
+  const float* conv_state0; // [B,Di,K] or null
+  void* out;                // [B,T,Di]
+  void* u_out;              // [B,T,Di] or null
+  void* y_save;             // [B,T,Di] or null
+  float* h_last;            // [B,Di,Ds] or null
+  float* conv_state_last;   // [B,Di,K] or null
+  float* ckpt;              // [B,nC,Ds,Di] or null
+  int64_t B, T, Di, R, X, nC;
+  int K;                    // conv taps, 0 = no conv
+  int L;                    // checkpoint interval
+};
+
+struct BwdArgs {
+  const void* x;
+  const void* delta_raw;
+  const float* a_log;
+  const void* xdbl;
+  const float* D;
+  const void* z;
+  const void* y_saved;      // [B,T,Di] (gate only)
+  const float* conv_w;
+  const float* conv_b;
+  const float* conv_state0;
+  const float* ckpt;        // [B,nC,Ds,Di]
+  const void* dout;
+  const void* d_u_extra;    // [B,T,Di] or null (fused only)
+  void* d_x;                // d_u (scan) or d_x (fused) [B,T,Di]
+  void* d_delta_raw;        // [B,T,Di]
+  void* d_z;                // [B,T,Di] (gate only)
+  float* part_bc;           // [nG, B*T, 2*Ds]: per channel-group sums of d_B | d_C
+  float* part_par;          // [B, Di, PW]: per batch row d_a_log | d_D | d_conv_w | d_conv_b
+  int64_t B, T, Di, R, X, nC;
+  int K;
+  int L;
+  int PW;                   // Ds + 1 + K + 1 (conv terms only when K > 0)
+};
+
+struct ReduceArgs {
+  const float* part_bc;
+  const float* part_par;
+  float* d_xdbl;            // [B,T,X], B/C columns +=
+  float* d_a_log;           // [Di,Ds] +=
+  float* d_D;               // [Di] +=
+  float* d_conv_w;          // [Di,K] += or null
+  float* d_conv_b;          // [Di] += or null
+  int64_t B, T, Di, Ds, R, X, nG;
+  int K;
+  int PW;
+};
+
+}  // namespace mscan

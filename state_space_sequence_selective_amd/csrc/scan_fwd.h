@@ -1,0 +1,196 @@
+// Forward of the selective-scan layer core (gfx950).
+//
+// Steps (mamba-rs 0.3.1 src/mamba_ssm/gpu/forward_mixed.rs, per-layer
+// forward): F4a causal depthwise conv1d + SiLU (fused entry only), F4c
+// delta = softplus(delta_raw), F4d the f32 recurrence
+//   h_t = exp(delta_t A) h_{t-1} + delta_t B_t u_t,  y_t = C_t . h_t + D u_t
+// with A = -exp(a_log) (mamba-rs 0.7.3 trainer.rs, recompute_a_neg_all),
+// and F4e out = y * silu(z).
+//
+// Mapping.  A workgroup owns 64 channels of one batch row and walks the
+// whole sequence.  Lane c of every wave is channel c; wave g holds states
+// [g*SPL, (g+1)*SPL) of all 64 channels in registers, so B_t / C_t reads are
+// wave-uniform LDS broadcasts.  Time advances in tiles of TT steps:
+//   stage   : every thread turns a few (t, channel) items of the tile into
+//             delta and delta*u (one softplus per item, shared by all
+//             waves through LDS); B/C rows of the tile go to LDS as f32.
+//   scan    : each wave runs the recurrence for its states and leaves its
+//             partial C.h per (t, channel) in LDS.
+//   output  : the staging threads add the partials of all waves, add D*u,
+//             apply the gate and write out (and y, u when asked).
+// The state entering every L-th step is written to ckpt for the backward.
+#pragma once
+#include "scan_common.h"
+
+namespace mscan {
+
+template <Act A, int DS, int SPL, int TT>
+__global__ void __launch_bounds__(64 * (DS / SPL))
+scan_fwd_kernel(const FwdArgs p) {
+  constexpr int G = DS / SPL;          // waves per workgroup
+  constexpr int NT = 64 * G;           // threads
+  static_assert(TT % G == 0, "tile must hold a whole number of items per thread");
+  constexpr int IPT = TT / G;          // (t, channel) items per thread per tile
+  using io = IO<A>;
+
+  __shared__ float s_dl[TT][64];       // delta
+  __shared__ float s_du[TT][64];       // delta * u
+  __shared__ float s_bc[TT][2 * DS];   // B_t | C_t as f32
+  __shared__ float s_yp[G][TT][64];    // per-wave partial C.h
+
+  const int tid = threadIdx.x;
+  const int c = tid & 63;
+  const int g = tid >> 6;
+  const int64_t b = blockIdx.y;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + c;
+  const bool on = i < p.Di;
+  const int64_t T = p.T, Di = p.Di;
+  const bool gate = p.z != nullptr;
+  const int K = p.K;
+
+  float a2[SPL], h[SPL];
+#pragma unroll
+  for (int s = 0; s < SPL; ++s) {
+    const int n = g * SPL + s;
+    a2[s] = on ? -expf(p.a_log[i * DS + n]) * kLog2e : 0.0f;
+    h[s] = (on && p.h0) ? p.h0[(b * Di + i) * DS + n] : 0.0f;
+  }
+  const float Dv = (on && p.D) ? p.D[i] : 0.0f;
+  constexpr int KMAX = 4;   // conv taps supported: 1..4
+  float cw[KMAX];
+  float cb = 0.0f;
+  if (K > 0) {
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) cw[k] = (on && k < K) ? p.conv_w[i * K + k] : 0.0f;
+    cb = (on && p.conv_b) ? p.conv_b[i] : 0.0f;
+  }
+
+  for (int64_t t0 = 0; t0 < T; t0 += TT) {
+    const int len = static_cast<int>(T - t0 < TT ? T - t0 : TT);
+    float e_u[IPT], e_sz[IPT];
+
+    // ---- stage
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int tt = g + G * k;
+      float dl = 0.0f, du = 0.0f, u = 0.0f, sz = 1.0f;
+      if (tt < len && on) {
+        const int64_t row = b * T + t0 + tt;
+        const int64_t e = row * Di + i;
+        if (K > 0) {
+          float pre = cb;
+#pragma unroll
+          for (int k2 = 0; k2 < KMAX; ++k2) {
+            if (k2 < K) {
+              const int64_t s = t0 + tt - (K - 1) + k2;
+              float xv;
+              if (s >= 0) xv = io::ld(p.x, (b * T + s) * Di + i);
+              else xv = p.conv_state0 ? p.conv_state0[(b * Di + i) * K + (K + s)] : 0.0f;
+              pre = fmaf(cw[k2], xv, pre);
+            }
+          }
+          u = pre * sigmoid(pre);
+        } else {
+          u = io::ld(p.x, e);
+        }
+        dl = softplus(io::ld(p.delta_raw, e));
+        du = dl * u;
+        if (gate) {
+          const float zv = io::ld(p.z, e);
+          sz = zv * sigmoid(zv);
+        }
+      }
+      s_dl[tt][c] = dl;
+      s_du[tt][c] = du;
+      e_u[k] = u;
+      e_sz[k] = sz;
+    }
+    for (int j = tid; j < TT * 2 * DS; j += NT) {
+      const int tt = j / (2 * DS), m = j % (2 * DS);
+      s_bc[tt][m] = tt < len ? io::ld(p.xdbl, (b * T + t0 + tt) * p.X + p.R + m) : 0.0f;
+    }
+    __syncthreads();
+
+    // ---- checkpoint: the state entering step t0 (TT divides L)
+    if (p.ckpt && on && (t0 % p.L) == 0) {
+      const int64_t cidx = t0 / p.L;
+#pragma unroll
+      for (int s = 0; s < SPL; ++s)
+        p.ckpt[((b * p.nC + cidx) * DS + g * SPL + s) * Di + i] = h[s];
+    }
+
+    // ---- scan
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if (tt < len) {
+        const float dl = s_dl[tt][c];
+        const float du = s_du[tt][c];
+        float yp = 0.0f;
+#pragma unroll
+        for (int s = 0; s < SPL; ++s) {
+          const int n = g * SPL + s;
+          const float dA = exp2_fast(dl * a2[s]);
+          h[s] = fmaf(dA, h[s], du * s_bc[tt][n]);
+          yp = fmaf(s_bc[tt][DS + n], h[s], yp);
+        }
+        s_yp[g][tt][c] = yp;
+      }
+    }
+    __syncthreads();
+
+    // ---- output
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int tt = g + G * k;
+      if (tt < len && on) {
+        float y = Dv * e_u[k];
+#pragma unroll
+        for (int w = 0; w < G; ++w) y += s_yp[w][tt][c];
+        const int64_t e = (b * T + t0 + tt) * Di + i;
+        io::st(p.out, e, gate ? y * e_sz[k] : y);
+        if (p.y_save) io::st(p.y_save, e, y);
+        if (p.u_out) io::st(p.u_out, e, e_u[k]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (p.h_last && on) {
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) p.h_last[(b * Di + i) * DS + g * SPL + s] = h[s];
+  }
+  if (p.conv_state_last && on && g == 0) {
+    for (int k = 0; k < K; ++k) {
+      const int64_t s = T - K + k;
+      float xv;
+      if (s >= 0) xv = io::ld(p.x, (b * T + s) * Di + i);
+      else xv = p.conv_state0 ? p.conv_state0[(b * Di + i) * K + (K + s)] : 0.0f;
+      p.conv_state_last[(b * Di + i) * K + k] = xv;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+template <Act A, int DS, int SPL>
+static hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t st) {
+  constexpr int G = DS / SPL;
+  constexpr int TT = G >= 16 ? G : 16;
+  dim3 grid(static_cast<unsigned>((p.Di + 63) / 64), static_cast<unsigned>(p.B));
+  hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT>), grid, dim3(64 * G), 0, st, p);
+  return hipGetLastError();
+}
+
+template <Act A>
+hipError_t launch_fwd_a(const FwdArgs& p, int ds, int spl, hipStream_t st) {
+#define MSCAN_CASE(DS_, SPL_) \
+  if (ds == DS_ && spl == SPL_) return launch_fwd_t<A, DS_, SPL_>(p, st);
+  MSCAN_CASE(4, 1) MSCAN_CASE(4, 2) MSCAN_CASE(4, 4)
+  MSCAN_CASE(8, 1) MSCAN_CASE(8, 2) MSCAN_CASE(8, 4)
+  MSCAN_CASE(16, 1) MSCAN_CASE(16, 2) MSCAN_CASE(16, 4)
+  MSCAN_CASE(32, 2) MSCAN_CASE(32, 4)
+  MSCAN_CASE(64, 4)
+#undef MSCAN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mscan

@@ -1,0 +1,148 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry
+point the header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba_scan.h")
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    import state_space_sequence_selective_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libmamba_scan.so not built")
+    m.load()
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_entry_points(pkg):
+    assert declared_functions() == sorted(pkg.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(pkg):
+    lib = ctypes.CDLL(pkg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen("nm -D --defined-only %s" % pkg.LIB_PATH).read()
+    for name in declared_functions():
+        assert re.search(r"\bT %s\b" % name, out), name
+
+
+def test_abi_version(pkg):
+    assert pkg.abi_version() == 1
+
+
+def _dims(pkg, **kw):
+    base = dict(batch=2, seqlen=100, d_inner=64, d_state=16, dt_rank=0, d_conv=0, chunk=32, act="bf16")
+    base.update(kw)
+    return pkg.Dims.make(**base)
+
+
+def test_sizes(pkg):
+    d = _dims(pkg)
+    assert pkg.ckpt_bytes(d) == 2 * 4 * 16 * 64 * 4            # ceil(100/32) = 4 checkpoints
+    # per-group d_B|d_C partials (1 group) padded to 256 B, then per-row param partials
+    bc = 1 * 2 * 100 * 32 * 4
+    assert pkg.workspace_bytes(d) == ((bc + 255) // 256) * 256 + 2 * 64 * 17 * 4
+    dc = _dims(pkg, d_conv=4, d_inner=128)
+    bc = 2 * 2 * 100 * 32 * 4
+    assert pkg.workspace_bytes(dc) == ((bc + 255) // 256) * 256 + 2 * 128 * 22 * 4
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(batch=0), 1, "batch"),
+    (dict(batch=70000), 3, "batch"),
+    (dict(seqlen=0), 1, "seqlen"),
+    (dict(d_inner=66), 1, "d_inner"),
+    (dict(d_inner=0), 1, "d_inner"),
+    (dict(d_state=12), 2, "d_state"),
+    (dict(d_state=64), 2, "d_state"),
+    (dict(chunk=48), 2, "chunk"),
+    (dict(chunk=-16), 1, "chunk"),
+    (dict(chunk=64), 2, "chunk"),                 # d_state 16 holds at most 32 steps
+    (dict(d_state=32, chunk=32), 2, "chunk"),
+    (dict(dt_rank=-1), 1, "dt_rank"),
+    (dict(act=5), 1, "act"),
+    (dict(seqlen=1 << 40), 3, "2^46"),
+])
+def test_bad_dims_rejected(pkg, kw, status, msg):
+    d = _dims(pkg, **kw)
+    with pytest.raises(pkg.MambaScanError) as ei:
+        pkg.ckpt_bytes(d)
+    assert ei.value.status == status
+    assert msg in str(ei.value) and "mamba_ckpt_bytes" in str(ei.value)
+
+
+def test_reserved_must_be_zero(pkg):
+    d = _dims(pkg)
+    d.reserved = 1
+    with pytest.raises(pkg.MambaScanError, match="reserved"):
+        pkg.ckpt_bytes(d)
+
+
+def _raw(pkg):
+    return pkg.load()
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch(pkg):
+    lib = _raw(pkg)
+    d = _dims(pkg)
+    P = ctypes.c_void_p
+    good = P(0x10000)           # never dereferenced: the call fails before any launch
+    # u NULL
+    rc = lib.mamba_scan_fwd(ctypes.byref(d), None, good, good, good, None, None, None, good, None, None, None, None)
+    assert rc == 1 and "mamba_scan_fwd: u is NULL" == pkg.last_error()
+    # out misaligned (bf16 needs 2-byte alignment)
+    rc = lib.mamba_scan_fwd(ctypes.byref(d), good, good, good, good, None, None, None, P(0x10001), None, None,
+                            None, None)
+    assert rc == 1 and "out is not 2-byte aligned" in pkg.last_error()
+    # a_log misaligned (f32)
+    rc = lib.mamba_scan_fwd(ctypes.byref(d), good, good, P(0x10002), good, None, None, None, good, None, None,
+                            None, None)
+    assert rc == 1 and "a_log" in pkg.last_error()
+    # backward: z given but y_saved missing
+    args = [ctypes.byref(d), good, good, good, good, None, good, None, good, good, good, good, good, good, good,
+            good, good, ctypes.c_size_t(1 << 30), None]
+    rc = lib.mamba_scan_bwd(*args)
+    assert rc == 1 and "y_saved is NULL" in pkg.last_error()
+    # backward: workspace too small
+    args = [ctypes.byref(d), good, good, good, good, None, None, None, good, good, good, good, None, good, good,
+            good, P(0x100000), ctypes.c_size_t(16), None]
+    rc = lib.mamba_scan_bwd(*args)
+    assert rc == 3 and "workspace_bytes" in pkg.last_error()
+    # fused: d_conv out of range
+    dc = _dims(pkg, d_conv=5)
+    rc = lib.mamba_conv_scan_gate_fwd(ctypes.byref(dc), *([good] * 17))
+    assert rc == 2 and "d_conv" in pkg.last_error()
+    dc = _dims(pkg, d_conv=0)
+    rc = lib.mamba_conv_scan_gate_bwd(ctypes.byref(dc), *([good] * 22), ctypes.c_size_t(1 << 30), None)
+    assert rc == 1 and "mamba_conv_scan_gate_bwd: d_conv" in pkg.last_error()
+
+
+def test_binding_rejects_host_tensors(pkg):
+    torch = pytest.importorskip("torch")
+    d = _dims(pkg, batch=1, seqlen=4)
+    t = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        pkg.scan_fwd(d, t, t, torch.zeros(64, 16), torch.zeros(1, 4, 32, dtype=torch.bfloat16), out=t)
+
+
+def test_product_does_not_touch_the_oracle():
+    """The product package never imports the oracle or the input generator."""
+    pkgdir = os.path.join(ROOT, "state_space_sequence_selective_amd")
+    for dirpath, _, files in os.walk(pkgdir):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.lower() or f == "__init__.py" and "oracle" not in src, f
+                assert "import workloads" not in src and "from workloads" not in src, f

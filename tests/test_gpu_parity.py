@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances (per output tensor):
+  f32 outputs (h_last, ckpt, d_xdbl, d_a_log, d_D, conv grads, and every
+  output of an f32 workload):  max|gpu - oracle| / max(1, max|oracle|) <= 1e-4
+  half-precision outputs (out, y, u, d_x, d_delta_raw, d_z of bf16/f16
+  workloads):                  max|gpu - oracle| / max|oracle|        <= 2e-2
+The oracle reads exactly the rounded arrays the GPU reads.
+"""
+import numpy as np
+import pytest
+
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_HALF = 2e-2
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def mscan():
+    _need_gpu()
+    import state_space_sequence_selective_amd as m
+    m.load()
+    return m
+
+
+def _dev(a, dtype):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda", dtype)
+
+
+def _device_inputs(w, inp):
+    at = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.act]
+    dev = {}
+    for k in ("x", "delta_raw", "z", "dout", "xdbl", "d_u_extra"):
+        if inp.get(k) is not None:
+            dev[k] = _dev(inp[k], at)
+    for k in ("a_log", "D", "conv_w", "conv_b", "h0", "conv_state0"):
+        if inp.get(k) is not None:
+            dev[k] = _dev(inp[k], torch.float32)
+    return dev
+
+
+def _dims(m, w, chunk):
+    return m.Dims.make(w.batch, w.seqlen, w.d_inner, w.d_state, w.dt_rank, w.d_conv, chunk, w.act)
+
+
+def _oracle(oracle_lib, w, inp, chunk, channels=None):
+    kw = dict(x=inp["x"], delta_raw=inp["delta_raw"], a_log=inp["a_log"], xdbl=inp["xdbl"], D=inp.get("D"),
+              z=inp.get("z"), h0=inp.get("h0"))
+    if w.d_conv:
+        kw.update(conv_w=inp["conv_w"], conv_b=inp.get("conv_b"), conv_state0=inp.get("conv_state0"))
+    dout, due = inp["dout"], inp.get("d_u_extra")
+    if channels is not None:
+        S = np.asarray(channels)
+        for k in ("x", "delta_raw", "z"):
+            if kw.get(k) is not None:
+                kw[k] = kw[k][..., S]
+        for k in ("a_log", "D", "conv_w", "conv_b"):
+            if kw.get(k) is not None:
+                kw[k] = kw[k][S]
+        for k in ("h0", "conv_state0"):
+            if kw.get(k) is not None:
+                kw[k] = kw[k][:, S]
+        dout = dout[..., S]
+        due = None if due is None else due[..., S]
+    L = chunk if chunk else 32
+    f = oracle_lib.forward(chunk=L, **kw)
+    g = oracle_lib.backward(dout=dout, d_u_extra=due, **kw)
+    return f, g
+
+
+def _err(gpu, ora, half):
+    g = gpu.detach().float().cpu().numpy().astype(np.float64) if isinstance(gpu, torch.Tensor) else gpu
+    o = np.asarray(ora, dtype=np.float64)
+    assert g.shape == o.shape, (g.shape, o.shape)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    diff = np.abs(g - o).max() if g.size else 0.0
+    if half:
+        scale = np.abs(o).max() if o.size else 1.0
+        return diff / max(scale, 1e-30)
+    return diff / max(1.0, np.abs(o).max() if o.size else 1.0)
+
+
+def _check(name, gpu, ora, half, report):
+    e = _err(gpu, ora, half)
+    tol = TOL_HALF if half else TOL_F32
+    report[name] = e
+    assert e <= tol, "%s: error %.3e > %.1e" % (name, e, tol)
+
+
+def run_case(m, oracle_lib, w, seed=0, chunk=0, h0=False, conv_state0=False, d_u_extra=False, D=True):
+    inp = workloads.make_inputs(w, seed, h0=h0, conv_state0=conv_state0, d_u_extra=d_u_extra)
+    if not D:
+        inp["D"] = None
+    dev = _device_inputs(w, inp)
+    dims = _dims(m, w, chunk)
+    core = m.LayerCore(dims, gate=w.gate, keep_u=True)
+    core.zero_grads()
+    core.forward(dev)
+    core.backward(dev, dev["dout"])
+    torch.cuda.synchronize()
+    f, g = _oracle(oracle_lib, w, inp, chunk)
+    half = w.act != "f32"
+    rep = {}
+    _check("out", core.out, f["out"], half, rep)
+    if w.gate:
+        _check("y", core.y, f["y"], half, rep)
+    _check("h_last", core.h_last, f["h_last"], False, rep)
+    _check("ckpt", core.ckpt, f["ckpt"], False, rep)
+    if w.d_conv:
+        _check("u", core.u_out, f["u"], half, rep)
+        _check("conv_state_last", core.conv_state_last, f["conv_state_last"], False, rep)
+        _check("d_conv_w", core.d_conv_w, g["d_conv_w"], False, rep)
+        _check("d_conv_b", core.d_conv_b, g["d_conv_b"], False, rep)
+    _check("d_x", core.d_x, g["d_x"], half, rep)
+    _check("d_delta_raw", core.d_delta_raw, g["d_delta_raw"], half, rep)
+    if w.gate:
+        _check("d_z", core.d_z, g["d_z"], half, rep)
+    R, Ds = w.dt_rank, w.d_state
+    _check("d_B", core.d_xdbl[..., R:R + Ds], g["d_xdbl"][..., R:R + Ds], False, rep)
+    _check("d_C", core.d_xdbl[..., R + Ds:], g["d_xdbl"][..., R + Ds:], False, rep)
+    _check("d_a_log", core.d_a_log, g["d_a_log"], False, rep)
+    _check("d_D", core.d_D, g["d_D"], False, rep)
+    print(w.name, "chunk", chunk, {k: "%.2e" % v for k, v in rep.items()}, flush=True)
+    return core, dev, inp, f, g
+
+
+# --------------------------------------------------------------------- cases
+
+TINY = workloads.CONFIGS["tiny_f32"]
+SMALL_FUSED = workloads.CONFIGS["fused_small_bf16"]
+
+
+@pytest.mark.parametrize("chunk", [64, 32, 16])
+def test_tiny_f32(mscan, oracle_lib, chunk):
+    run_case(mscan, oracle_lib, TINY, chunk=chunk)
+
+
+def test_fused_small_bf16(mscan, oracle_lib):
+    run_case(mscan, oracle_lib, SMALL_FUSED)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16", "f32"])
+def test_scan_gate_ragged(mscan, oracle_lib, act):
+    # T not a multiple of the chunk, d_inner not a multiple of 64, odd batch
+    w = workloads.Workload("ragged_" + act, 3, 77, 100, 16, 0, 0, act, True)
+    run_case(mscan, oracle_lib, w, chunk=32, h0=True)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_fused_ragged_states_and_extras(mscan, oracle_lib, act):
+    w = workloads.Workload("fused_ragged_" + act, 2, 45, 68, 16, 5, 4, act, True)
+    run_case(mscan, oracle_lib, w, chunk=16, h0=True, conv_state0=True, d_u_extra=True)
+
+
+@pytest.mark.parametrize("ds,chunk", [(4, 64), (8, 32), (8, 16), (16, 16), (32, 16)])
+def test_state_sizes(mscan, oracle_lib, ds, chunk):
+    w = workloads.Workload("ds%d" % ds, 2, 70, 132, ds, 3, 0, "bf16", True)
+    run_case(mscan, oracle_lib, w, chunk=chunk, h0=True)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_conv_taps(mscan, oracle_lib, K):
+    w = workloads.Workload("taps%d" % K, 2, 40, 64, 16, 0, K, "f32", True)
+    run_case(mscan, oracle_lib, w, chunk=16, conv_state0=True)
+
+
+def test_no_gate_no_D(mscan, oracle_lib):
+    w = workloads.Workload("nogate", 2, 50, 64, 16, 0, 0, "bf16", False)
+    run_case(mscan, oracle_lib, w, chunk=32, D=False)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3])
+def test_degenerate_short_sequences(mscan, oracle_lib, T):
+    # T = 1; and T < d_conv so the outgoing conv state mixes old state and input
+    w = workloads.Workload("short%d" % T, 2, T, 64, 16, 0, 4, "bf16", True)
+    run_case(mscan, oracle_lib, w, chunk=32, h0=True, conv_state0=True)
+
+
+def test_single_channel_group_min_width(mscan, oracle_lib):
+    w = workloads.Workload("di4", 1, 33, 4, 4, 0, 0, "f32", True)
+    run_case(mscan, oracle_lib, w, chunk=16)
+
+
+def test_accumulate_canaries_and_determinism(mscan, oracle_lib):
+    """Parameter grads and d_xdbl B/C accumulate; dt columns stay bitwise
+    untouched; the backward is bitwise reproducible run to run."""
+    w = workloads.Workload("accum", 2, 96, 192, 16, 6, 4, "bf16", True)
+    core, dev, inp, f, g = run_case(mscan, oracle_lib, w, chunk=32)
+    first = {k: getattr(core, k).clone() for k in ("d_x", "d_delta_raw", "d_z", "d_xdbl", "d_a_log", "d_D",
+                                                   "d_conv_w", "d_conv_b")}
+    canary = torch.full_like(core.d_xdbl, 7.25)
+    core.d_xdbl.copy_(canary)
+    core.backward(dev, dev["dout"])      # no zeroing: accumulate on top
+    torch.cuda.synchronize()
+    R = w.dt_rank
+    assert torch.equal(core.d_xdbl[..., :R], canary[..., :R])
+    assert torch.equal(core.d_xdbl[..., R:], canary[..., R:] + first["d_xdbl"][..., R:])
+    for k in ("d_a_log", "d_D", "d_conv_w", "d_conv_b"):
+        assert torch.equal(getattr(core, k), 2 * first[k]), k   # x + x is exact
+    for k in ("d_x", "d_delta_raw", "d_z"):
+        assert torch.equal(getattr(core, k), first[k]), k        # overwritten, same bits
+    # bitwise reproducible d_xdbl (no atomics)
+    core.zero_grads()
+    core.backward(dev, dev["dout"])
+    torch.cuda.synchronize()
+    assert torch.equal(core.d_xdbl, first["d_xdbl"])
+
+
+def test_state_carry_split_on_gpu(mscan, oracle_lib):
+    """fwd(0..T) equals fwd(0..T1) then fwd(T1..T) with the carried states."""
+    w = workloads.Workload("split", 2, 64, 64, 16, 0, 4, "f32", True)
+    inp = workloads.make_inputs(w, 3, h0=True, conv_state0=True)
+    dev = _device_inputs(w, inp)
+    full = mscan.LayerCore(_dims(mscan, w, 16), gate=True)
+    full.forward(dev)
+    T1 = 23
+    parts = []
+    h, cs = dev["h0"], dev["conv_state0"]
+    for lo, hi in ((0, T1), (T1, w.seqlen)):
+        wp = w.with_(seqlen=hi - lo)
+        dp = dict(dev)
+        for k in ("x", "delta_raw", "z", "xdbl"):
+            dp[k] = dev[k][:, lo:hi].contiguous()
+        dp["h0"], dp["conv_state0"] = h, cs
+        core = mscan.LayerCore(_dims(mscan, wp, 16), gate=True)
+        core.forward(dp)
+        parts.append(core.out)
+        h, cs = core.h_last, core.conv_state_last
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(torch.cat(parts, 1).cpu().numpy(), full.out.cpu().numpy(), rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(h.cpu().numpy(), full.h_last.cpu().numpy(), rtol=1e-5, atol=1e-6)
+    assert torch.equal(cs, full.conv_state_last)
+
+
+def test_abi_errors_on_device(mscan):
+    """A rejected call returns a status with the entry point's name and enqueues nothing."""
+    w = workloads.Workload("err", 1, 8, 64, 16, 0, 0, "bf16", True)
+    dims = _dims(mscan, w, 32)
+    core = mscan.LayerCore(dims)
+    inp = _device_inputs(w, workloads.make_inputs(w, 0))
+    bad = mscan.Dims.make(1, 8, 64, 16, 0, 0, 48, "bf16")
+    with pytest.raises(mscan.MambaScanError, match="chunk"):
+        mscan.scan_fwd(bad, inp["x"], inp["delta_raw"], inp["a_log"], inp["xdbl"], out=core.out)
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    core.forward(inp)
+    with pytest.raises(mscan.MambaScanError, match="workspace"):
+        mscan.scan_bwd(dims, inp["x"], inp["delta_raw"], inp["a_log"], inp["xdbl"], inp["D"], inp["z"], core.y,
+                       core.ckpt, inp["dout"], d_u=core.d_x, d_delta_raw=core.d_delta_raw, d_z=core.d_z,
+                       d_xdbl=core.d_xdbl, d_a_log=core.d_a_log, d_D=core.d_D, workspace=small_ws)
+
+
+# ------------------------------------------------- full-size, sampled channels
+
+
+def _sampled_full(mscan, oracle_lib, name, sample):
+    w = workloads.CONFIGS[name]
+    inp = workloads.make_inputs(w, 0)
+    dev = _device_inputs(w, inp)
+    dims = _dims(mscan, w, 32)
+    core = mscan.LayerCore(dims, gate=w.gate)
+    core.zero_grads()
+    core.forward(dev)
+    core.backward(dev, dev["dout"])
+    torch.cuda.synchronize()
+    S = np.asarray(sample)
+    f, g = _oracle(oracle_lib, w, inp, 32, channels=S)
+    rep = {}
+    half = w.act != "f32"
+    _check("out", core.out[..., S], f["out"], half, rep)
+    _check("y", core.y[..., S], f["y"], half, rep)
+    _check("h_last", core.h_last[:, S], f["h_last"], False, rep)
+    _check("ckpt", core.ckpt[..., S], f["ckpt"], False, rep)
+    _check("d_x", core.d_x[..., S], g["d_x"], half, rep)
+    _check("d_delta_raw", core.d_delta_raw[..., S], g["d_delta_raw"], half, rep)
+    _check("d_z", core.d_z[..., S], g["d_z"], half, rep)
+    _check("d_a_log", core.d_a_log[S], g["d_a_log"], False, rep)
+    _check("d_D", core.d_D[S], g["d_D"], False, rep)
+    # d_C at the step before each checkpoint, from the (just checked) checkpoints:
+    # d_C[b, cL-1, n] = sum_i dy[b, cL-1, i] h_{cL-1}[b, i, n], dy = dout silu(z)
+    L = dims.L
+    ck = core.ckpt.double().cpu().numpy()                     # [B, nC, Ds, Di]
+    z = inp["z"].astype(np.float64)
+    dy = inp["dout"].astype(np.float64) * z / (1 + np.exp(-z))
+    ts = np.arange(1, ck.shape[1]) * L - 1
+    dC = np.einsum("bci,bcni->bcn", dy[:, ts, :], ck[:, 1:])
+    R, Ds = w.dt_rank, w.d_state
+    _check("d_C@ckpt", core.d_xdbl[:, ts, R + Ds:], dC, False, rep)
+    print(name, "sampled", {k: "%.2e" % v for k, v in rep.items()}, flush=True)
+
+
+def test_full_size_130m_sampled(mscan, oracle_lib):
+    _sampled_full(mscan, oracle_lib, "scan_130m_bf16", [0, 1, 63, 64, 700, 1535])
+
+
+def test_full_size_t8192_sampled(mscan, oracle_lib):
+    _sampled_full(mscan, oracle_lib, "scan_2p8b_t8192_bf16", [0, 5, 2047, 5119])
