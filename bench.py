@@ -1,0 +1,230 @@
+"""Benchmark: selective-scan layer core, forward + backward, on one MI355X.
+
+A step is one training pass of the layer core over one batch of synthetic
+input: zero the accumulated gradients, forward (conv+SiLU when the workload
+has it, softplus, exp(delta*A) recurrence, C.h + D*u, gate), backward (the
+full reverse-time adjoint).  Inputs are resident in HBM before timing
+starts.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+# fp32 FMA rate without packed-FP32 instructions: 256 CUs x 4 SIMDs x 16 lanes
+# x 2 flops x 2.4 GHz = 78.6 TFLOP/s (the 157.3 figure needs packed FP32)
+VALU_PEAK_TFLOPS = 78.6
+# algorithmic fp32 flops per (t, channel, state) element, FMA = 2, exp = 1:
+#   forward   : delta*A, exp, delta*u*B, h = dA*h + x, y += C*h          ->  7
+#   backward  : recompute (delta*A, exp, delta*u*B, h update)            ->  5
+#               adjoint (dh, dA*h_prev, q, d_A acc, carry, sum dh*B,
+#               sum q*A, d_B and d_C contractions)                      -> 16
+FLOPS_FWD_ELEM = 7
+FLOPS_BWD_ELEM = 21
+
+
+def act_bytes(act):
+    return 4 if act == "f32" else 2
+
+
+def algorithmic_bytes(w: workloads.Workload, L: int):
+    """HBM bytes the method must move (inputs read once, outputs written once).
+
+    Per token-channel: forward reads x|u, delta_raw, [z] and writes out;
+    backward reads x|u, delta_raw, [z], dout and writes d_x|d_u,
+    d_delta_raw, [d_z].  Per token: B and C rows (act dtype) in both
+    passes, d_B/d_C f32 in the backward.  Checkpoints: 4*Ds/L bytes per
+    token-channel written by the forward and read by the backward.
+    """
+    s = act_bytes(w.act)
+    N, Di, Ds = w.batch * w.seqlen, w.d_inner, w.d_state
+    g = 1 if w.gate else 0
+    ckpt = w.batch * -(-w.seqlen // L) * Di * Ds * 4
+    conv_par = (w.d_inner * (w.d_conv + 1) * 4) if w.d_conv else 0
+    fwd = N * Di * s * (3 + g) + N * 2 * Ds * s + ckpt + conv_par
+    bwd = N * Di * s * (5 + 2 * g) + N * 2 * Ds * s + N * 2 * Ds * 4 + ckpt + conv_par
+    return fwd, bwd
+
+
+def device_inputs(torch, w, inp):
+    at = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.act]
+    dev = {}
+    for k in ("x", "delta_raw", "z", "dout", "xdbl"):
+        if inp.get(k) is not None:
+            dev[k] = torch.from_numpy(inp[k]).to("cuda", at)
+    for k in ("a_log", "D", "conv_w", "conv_b"):
+        if inp.get(k) is not None:
+            dev[k] = torch.from_numpy(inp[k]).to("cuda", torch.float32)
+    return dev
+
+
+def cpu_baseline(w: workloads.Workload, L: int, budget_s: float):
+    """The CPU oracle as it stands (double precision, sequential in time,
+    threads over batch rows), timed on a bounded channel sample of the same
+    workload and scaled to the full channel count."""
+    import oracle
+    oracle.build(force=False)
+    chans = 256 if w.d_inner >= 256 else w.d_inner
+    while True:
+        sw = w.with_(d_inner=chans)
+        inp = workloads.make_inputs(sw, 0)
+        kw = dict(x=inp["x"], delta_raw=inp["delta_raw"], a_log=inp["a_log"], xdbl=inp["xdbl"], D=inp["D"],
+                  z=inp.get("z"))
+        if w.d_conv:
+            kw.update(conv_w=inp["conv_w"], conv_b=inp["conv_b"])
+        threads = min(w.batch, oracle.default_threads())
+        t0 = time.perf_counter()
+        oracle.forward(chunk=L, threads=threads, **kw)
+        oracle.backward(dout=inp["dout"], threads=threads, **kw)
+        dt = time.perf_counter() - t0
+        if dt > 0.25 * budget_s or chans >= w.d_inner:
+            break
+        chans = min(w.d_inner, chans * max(2, int(0.5 * budget_s / max(dt, 1e-3))))
+    full_s = dt * (w.d_inner / chans) * w.layers
+    tokens = w.batch * w.seqlen
+    return {"value": tokens / full_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d channels, all %d batch rows x %d steps%s, fwd+bwd in %.1f s; scaled by %d/%d%s"
+                      % (chans, w.d_inner, w.batch, w.seqlen, "" if w.layers == 1 else " (one layer)", dt,
+                         w.d_inner, chans, "" if w.layers == 1 else " x %d layers" % w.layers)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="scan_2p8b_t8192_bf16", choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--chunk", type=int, default=32)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (HBM counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the kernel on one GPU's share); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import state_space_sequence_selective_amd as pkg
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 5}))
+        return
+
+    w = workloads.CONFIGS[args.workload]
+    L = args.chunk
+    torch.cuda.set_device(0)
+    pkg.load()
+    inp = workloads.make_inputs(w, args.seed)
+    layers = []
+    for l in range(w.layers):
+        if l > 0:
+            inp = workloads.make_inputs(w, args.seed + l)
+        dev = device_inputs(torch, w, inp)
+        dims = pkg.Dims.make(w.batch, w.seqlen, w.d_inner, w.d_state, w.dt_rank, w.d_conv, L, w.act)
+        layers.append((pkg.LayerCore(dims, gate=w.gate), dev))
+    del inp
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        for core, _ in layers:
+            core.zero_grads()
+        for j, (core, dev) in enumerate(layers):
+            if evs is not None and j == 0:
+                evs[0].record(stream)
+            core.forward(dev, stream=stream)
+            if evs is not None and j == 0:
+                evs[1].record(stream)
+        for j, (core, dev) in reversed(list(enumerate(layers))):
+            if evs is not None and j == 0:
+                evs[2].record(stream)
+            core.backward(dev, dev["dout"], stream=stream)
+            if evs is not None and j == 0:
+                evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        step(ev[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+
+    tokens = w.batch * w.seqlen
+    value = tokens / (ms_step / 1e3)
+    fb, bb = algorithmic_bytes(w, L)
+    elems = w.batch * w.seqlen * w.d_inner * w.d_state
+    step_bytes = (fb + bb) * w.layers
+    hbm_gbps = step_bytes / (ms_step / 1e3) / 1e9
+    # dominant kernel: the backward entry (scan_bwd_kernel + its fixed-order reduce)
+    bwd_tflops = elems * FLOPS_BWD_ELEM / (bwd_ms / 1e3) / 1e12
+    roofline = {"bound": "alu", "achieved": round(bwd_tflops, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(bwd_tflops / VALU_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "mamba_scan_bwd (scan_bwd_kernel + mscan_reduce_kernel), layer 0",
+                "launch_ms": round(bwd_ms, 4),
+                "algorithmic_flops_per_launch": elems * FLOPS_BWD_ELEM,
+                "algorithmic_bytes_per_launch": bb,
+                "hbm_GBps_at_algorithmic_bytes": round(bb / (bwd_ms / 1e3) / 1e9, 1)}
+    res = {
+        "metric": "selective-scan fwd+bwd tokens/sec and achieved HBM GB/s (% of MI355X peak)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.act,
+        "data": "synthetic (seeded, distributions of the workload)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_inner": w.d_inner,
+                   "d_state": w.d_state, "dt_rank": w.dt_rank, "d_conv": w.d_conv, "gate": w.gate,
+                   "layers": w.layers, "chunk": L, "parallelism": "single GPU"},
+        "hbm_GBps": round(hbm_gbps, 1),
+        "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "wall_s": round(t_wall, 3),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, L, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

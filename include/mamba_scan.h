@@ -43,8 +43,10 @@
  *                         an incoming state reach the output)
  *       ckpt:             [B, ceil(T/L), Ds, Di] f32; ckpt[b, c] is the
  *                         state entering step c*L (ckpt[b, 0] = h0)
- *   - Activation pointers need the alignment of their element type, f32
- *     pointers 4-byte alignment.  Inputs and outputs must not overlap.
+ *   - The activation inputs read in bulk (u or x, delta_raw, z, dout,
+ *     y_saved) must be 4-byte aligned for 16-bit types and 16-byte aligned
+ *     for f32; every other activation pointer needs its element alignment,
+ *     every f32 pointer 4 bytes.  Inputs and outputs must not overlap.
  *   - Parameter gradients (d_a_log, d_D, d_conv_w, d_conv_b) and the B/C
  *     columns of d_xdbl are ACCUMULATED (+=): zero them once per training
  *     step.  The dt columns [0, R) of d_xdbl are never touched.
@@ -85,10 +87,9 @@ typedef struct mamba_dims {
   int64_t d_state;  /* Ds in {4, 8, 16, 32} */
   int64_t dt_rank;  /* R >= 0: xdbl row = [dt (R) | B (Ds) | C (Ds)] */
   int32_t d_conv;   /* K in 1..4 for the fused entry points; ignored by mamba_scan_* */
-  int32_t chunk;    /* checkpoint interval L in {16, 32, 64}; 0 = 32.  The
+  int32_t chunk;    /* checkpoint interval L in {16, 32}; 0 = 32.  The
                        backward holds L steps of state in registers, so
-                       Ds 8 and 16 need L <= 32 and Ds 32 needs L = 16
-                       (Ds 4 takes all three) */
+                       Ds 32 needs L = 16 */
   int32_t act;      /* mamba_dtype_t of every activation tensor (and xdbl) */
   int32_t reserved; /* must be 0 */
 } mamba_dims_t;

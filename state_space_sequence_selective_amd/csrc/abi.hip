@@ -53,6 +53,7 @@ struct Plan {
   int spl_fwd;    // states per lane in the forward kernel
   mscan::Act act;
   int esize;      // bytes per activation element
+  int bulk_align; // alignment of activation inputs staged with 4 / 16-byte granules
 };
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;
@@ -70,15 +71,13 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   if (d->d_state < 1) return fail(MAMBA_ERR_INVALID, fn, "d_state must be >= 1");
   if (d->d_state != 4 && d->d_state != 8 && d->d_state != 16 && d->d_state != 32)
     return fail(MAMBA_ERR_UNSUPPORTED, fn, "d_state must be 4, 8, 16 or 32");
-  if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
+  if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32)
     return fail(d->chunk < 0 ? MAMBA_ERR_INVALID : MAMBA_ERR_UNSUPPORTED, fn,
-                "chunk must be 0 (default 32), 16, 32 or 64");
+                "chunk must be 0 (default 32), 16 or 32");
   const int L = d->chunk ? d->chunk : 32;
-  // the backward keeps L steps of state in registers: supported pairs
-  const bool pair_ok = (d->d_state == 4) || (d->d_state <= 16 && L <= 32) || (d->d_state == 32 && L == 16);
-  if (!pair_ok)
-    return fail(MAMBA_ERR_UNSUPPORTED, fn,
-                "chunk must be <= 32 for d_state 8 or 16, and 16 for d_state 32");
+  // the backward keeps L steps of state in registers
+  if (d->d_state == 32 && L != 16)
+    return fail(MAMBA_ERR_UNSUPPORTED, fn, "chunk must be 16 for d_state 32");
   int K = 0;
   if (fused) {
     if (d->d_conv < 1) return fail(MAMBA_ERR_INVALID, fn, "d_conv must be >= 1");
@@ -98,9 +97,10 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   pl->nC = (d->seqlen + L - 1) / L;
   pl->nG = (d->d_inner + 63) / 64;
   pl->K = K;
-  pl->spl_fwd = d->d_state >= 8 ? 2 : 1;
+  pl->spl_fwd = d->d_state == 4 ? 1 : (d->d_state == 32 ? 4 : 2);
   pl->act = static_cast<mscan::Act>(d->act);
   pl->esize = d->act == MAMBA_F32 ? 4 : 2;
+  pl->bulk_align = d->act == MAMBA_F32 ? 16 : 4;
   return MAMBA_OK;
 }
 
@@ -136,13 +136,13 @@ int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_
                const float* conv_state0, const void* delta_raw, const float* a_log, const void* xdbl,
                const float* D, const void* z, const float* h0, void* out, void* u_out, void* y_save,
                float* h_last, float* conv_state_last, float* ckpt, void* stream) {
-  const int e = pl.esize;
-  MSCAN_TRY(check_ptr(fn, pl.K ? "x" : "u", x, true, e));
-  MSCAN_TRY(check_ptr(fn, "delta_raw", delta_raw, true, e));
+  const int e = pl.esize, ba = pl.bulk_align;
+  MSCAN_TRY(check_ptr(fn, pl.K ? "x" : "u", x, true, ba));
+  MSCAN_TRY(check_ptr(fn, "delta_raw", delta_raw, true, ba));
   MSCAN_TRY(check_ptr(fn, "a_log", a_log, true, 4));
   MSCAN_TRY(check_ptr(fn, "xdbl", xdbl, true, e));
   MSCAN_TRY(check_ptr(fn, "D", D, false, 4));
-  MSCAN_TRY(check_ptr(fn, "z", z, false, e));
+  MSCAN_TRY(check_ptr(fn, "z", z, false, ba));
   MSCAN_TRY(check_ptr(fn, "h0", h0, false, 4));
   MSCAN_TRY(check_ptr(fn, "out", out, true, e));
   MSCAN_TRY(check_ptr(fn, "y_save", y_save, false, e));
@@ -193,16 +193,16 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
                 const void* d_u_extra, void* d_x, void* d_delta_raw, void* d_z, float* d_xdbl,
                 float* d_a_log, float* d_D, float* d_conv_w, float* d_conv_b, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  const int e = pl.esize;
-  MSCAN_TRY(check_ptr(fn, pl.K ? "x" : "u", x, true, e));
-  MSCAN_TRY(check_ptr(fn, "delta_raw", delta_raw, true, e));
+  const int e = pl.esize, ba = pl.bulk_align;
+  MSCAN_TRY(check_ptr(fn, pl.K ? "x" : "u", x, true, ba));
+  MSCAN_TRY(check_ptr(fn, "delta_raw", delta_raw, true, ba));
   MSCAN_TRY(check_ptr(fn, "a_log", a_log, true, 4));
   MSCAN_TRY(check_ptr(fn, "xdbl", xdbl, true, e));
   MSCAN_TRY(check_ptr(fn, "D", D, false, 4));
-  MSCAN_TRY(check_ptr(fn, "z", z, false, e));
-  MSCAN_TRY(check_ptr(fn, "y_saved", y_saved, z != nullptr, e));
+  MSCAN_TRY(check_ptr(fn, "z", z, false, ba));
+  MSCAN_TRY(check_ptr(fn, "y_saved", y_saved, z != nullptr, ba));
   MSCAN_TRY(check_ptr(fn, "ckpt", ckpt, true, 4));
-  MSCAN_TRY(check_ptr(fn, "dout", dout, true, e));
+  MSCAN_TRY(check_ptr(fn, "dout", dout, true, ba));
   MSCAN_TRY(check_ptr(fn, pl.K ? "d_x" : "d_u", d_x, true, e));
   MSCAN_TRY(check_ptr(fn, "d_delta_raw", d_delta_raw, true, e));
   MSCAN_TRY(check_ptr(fn, "d_z", d_z, z != nullptr, e));

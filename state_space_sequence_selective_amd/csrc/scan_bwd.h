@@ -1,5 +1,5 @@
 // Backward of the selective-scan layer core (gfx950): the reverse-time
-// adjoint of scan_fwd.hip.
+// adjoint of the forward in scan_fwd.h.
 //
 // What it produces follows the backward scratch of the mamba-rs 0.3.1
 // forward_mixed.rs page (GpuMambaMixedTrainScratch): d_y from the gate,
@@ -12,25 +12,29 @@
 //   d_A     += dh delta_t dA h_{t-1}       carry = dh dA
 // with d_u_t += D dy_t, d_D += dy_t u_t and d_a_log = A d_A (A = -exp(a_log)).
 //
-// Mapping.  As in the forward: a workgroup owns 64 channels (lanes) of one
-// batch row; wave g owns states [g*SPL, (g+1)*SPL).  The sequence is walked
-// backwards in tiles of L steps, L being the checkpoint interval:
-//   stage     : per (t, channel) item, delta, delta*u and dy = dout*silu(z)
-//               go to LDS; d_z = dout * y * silu'(z) is written at once from
-//               the saved y; the rest of the item's scalars stay in the
-//               staging thread's registers for the epilogue.
-//   recompute : from ckpt, each wave re-runs its states over the tile and
-//               keeps h_t and dA_t for every step in registers (SPL*L = 64
-//               of each).  Every G steps the wave sums dy*h over its 64
-//               channels (d_C) in a wave-private LDS block.
-//   reverse   : G steps at a time, each wave runs the adjoint for its states,
+// Mapping.  A workgroup owns 64 channels (lanes) of one batch row; wave g
+// owns states [g*SPL, (g+1)*SPL).  The sequence is walked backwards in
+// tiles of L steps, L being the checkpoint interval.  Per tile:
+//   stage     : the tile's raw activations (already in LDS, copied there
+//               asynchronously during the previous tile) become, per
+//               (t, channel) item, {delta, delta*u, dy, u} in LDS; d_z =
+//               dout * y * silu'(z) is written at once from the saved y.
+//               Then the copies for the next tile are issued.
+//   recompute : from the checkpoint each wave re-runs its states over the
+//               tile and keeps h_t and dA_t of every step in registers
+//               (SPL*L = 64 of each).  Every G steps the wave sums dy*h over
+//               its 64 channels (d_C) in a wave-private LDS block.
+//   reverse   : G steps at a time each wave runs the adjoint of its states,
 //               sums delta*u*dh over its channels (d_B) the same way, and
 //               leaves per-(t, channel) partials of sum_n dh B and
 //               sum_n dh A dA h_{t-1} in LDS; the epilogue threads add the
 //               partials of all waves and write d_u (or, fused, push d_u
 //               through SiLU and the conv) and d_delta_raw.
-// d_B / d_C per channel group, and d_a_log / d_D / conv grads per batch row,
-// go to a workspace; mscan_reduce_kernel adds them up in a fixed order.
+// Past the end of the sequence the staged values are zero, which makes the
+// extra steps of a short last tile identities, so the step loops need no
+// bounds tests.  d_B / d_C per channel group and d_a_log / d_D / conv grads
+// per batch row go to a workspace; mscan_reduce_kernel sums them in a fixed
+// order.
 #pragma once
 #include "scan_common.h"
 
@@ -67,15 +71,21 @@ scan_bwd_kernel(const BwdArgs p) {
   constexpr int NT = 64 * G;
   constexpr int SUB = G;               // steps per reverse sub-tile
   static_assert(L % SUB == 0, "sub-tiles must tile the chunk");
-  constexpr int NSUB = L / SUB;        // = stage items per thread
+  constexpr int NSUB = L / SUB;        // = staged items per thread
   constexpr int NO = SUB * SPL;        // channel sums per wave per sub-tile
-  constexpr int KMAX = FUSED ? 4 : 1;   // conv taps supported: 1..4
+  constexpr int KMAX = FUSED ? 4 : 1;  // conv taps supported: 1..4
+  constexpr int ES = A == Act::F32 ? 4 : 2;
+  constexpr int RB = 64 * ES;          // bytes per raw row
+  constexpr int XR = pad4(L + KMAX - 1);   // raw x rows: conv halo, then the tile
+  constexpr int NBC = L * 2 * DS;      // B/C values per tile
+  constexpr int BCPT = (NBC + NT - 1) / NT;
   using io = IO<A>;
 
-  __shared__ float s_dl[L][64];        // delta
-  __shared__ float s_du[L][64];        // delta * u
-  __shared__ float s_dy[L][64];        // dy = dout * silu(z)
-  __shared__ float s_bc[L][2 * DS];
+  // raw tile: x (with halo) | delta_raw | dout | z | y
+  __shared__ __attribute__((aligned(16))) char s_raw[(XR + 4 * L) * RB];
+  __shared__ float4 s_st[L][64];       // delta, delta*u, dy, u
+  __shared__ float s_x[FUSED ? L + KMAX - 1 : 1][64];
+  __shared__ float s_bc[L][2][DS];
   __shared__ float s_su[G][SUB][64];   // per-wave sum_n dh B
   __shared__ float s_sd[G][SUB][64];   // per-wave sum_n dh A dA h_{t-1}
   __shared__ float s_red[G][64 * (NO + 1)];
@@ -86,12 +96,19 @@ scan_bwd_kernel(const BwdArgs p) {
   const int g = tid >> 6;
   const int64_t b = blockIdx.y;
   const int64_t cg = blockIdx.x;
-  const int64_t i = cg * 64 + c;
+  const int64_t i0 = cg * 64;
+  const int64_t i = i0 + c;
   const bool on = i < p.Di;
-  const int64_t T = p.T, Di = p.Di, BT = p.B * p.T;
+  const int64_t T = p.T, Di = p.Di, BT = p.B * p.T, row0 = b * p.T;
   const bool gate = p.z != nullptr;
   const int K = FUSED ? p.K : 0;
   float* red = s_red[g];
+  lds_char_t* raw_l = (lds_char_t*)s_raw;
+  const char* raw_x = s_raw;
+  const char* raw_dr = s_raw + XR * RB;
+  const char* raw_go = s_raw + (XR + L) * RB;
+  const char* raw_z = s_raw + (XR + 2 * L) * RB;
+  const char* raw_y = s_raw + (XR + 3 * L) * RB;
 
   float a2[SPL], an[SPL], carry[SPL], dacc[SPL];
 #pragma unroll
@@ -115,157 +132,218 @@ scan_bwd_kernel(const BwdArgs p) {
   if (FUSED)
     for (int j = tid; j < (SUB + KMAX) * 64; j += NT) (&s_dp[0][0])[j] = 0.0f;
 
+  // ---- prefetch of one tile: raw activations to LDS (async), B/C rows and
+  // the checkpoint to registers
+  float bcn[BCPT], hn[SPL];
+  auto prefetch = [&](int64_t kt) {
+    const int64_t t0 = kt * L;
+    async_rows<ES>(raw_l, p.x, row0, t0 - (KMAX - 1), T, Di, i0, XR, g, G, c);
+    async_rows<ES>(raw_l + XR * RB, p.delta_raw, row0, t0, T, Di, i0, L, g, G, c);
+    async_rows<ES>(raw_l + (XR + L) * RB, p.dout, row0, t0, T, Di, i0, L, g, G, c);
+    if (gate) {
+      async_rows<ES>(raw_l + (XR + 2 * L) * RB, p.z, row0, t0, T, Di, i0, L, g, G, c);
+      async_rows<ES>(raw_l + (XR + 3 * L) * RB, p.y_saved, row0, t0, T, Di, i0, L, g, G, c);
+    }
+#pragma unroll
+    for (int q = 0; q < BCPT; ++q) {
+      const int j = tid + q * NT;
+      const int tt = j / (2 * DS), m = j % (2 * DS);
+      const bool ok = j < NBC && t0 + tt < T;
+      bcn[q] = ok ? io::ld(p.xdbl, (row0 + t0 + tt) * p.X + p.R + m) : 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < SPL; ++s)
+      hn[s] = on ? p.ckpt[((b * p.nC + kt) * DS + g * SPL + s) * Di + i] : 0.0f;
+  };
+
   const int64_t ntiles = (T + L - 1) / L;
+  prefetch(ntiles - 1);
+
   for (int64_t kt = ntiles - 1; kt >= 0; --kt) {
     const int64_t t0 = kt * L;
     const int len = static_cast<int>(T - t0 < L ? T - t0 : L);
-    float e_dl[NSUB], e_u[NSUB], e_sig[NSUB], e_dy[NSUB], e_dsp[NSUB];
+    float e_sig[NSUB], e_dsp[NSUB], e_due[NSUB];
+    float h[SPL];
 
     // ---------------------------------------------------------------- stage
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) h[s] = hn[s];
+#pragma unroll
+    for (int q = 0; q < BCPT; ++q) {
+      const int j = tid + q * NT;
+      if (j < NBC) (&s_bc[0][0][0])[j] = bcn[q];
+    }
+    if (FUSED) {
+      for (int j = tid; j < (L + KMAX - 1) * 64; j += NT) {
+        const int r = j >> 6, cc = j & 63;
+        const int64_t s = t0 - (KMAX - 1) + r;
+        float xv = 0.0f;
+        if (i0 + cc < Di) {
+          if (s >= 0) xv = raw_ld<A>(raw_x, r, cc);
+          else if (p.conv_state0 && s >= -(int64_t)K) xv = p.conv_state0[(b * Di + i0 + cc) * K + (K + s)];
+        }
+        s_x[r][cc] = xv;
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int k = 0; k < NSUB; ++k) {
       const int tt = g + G * k;
-      float dl = 0.0f, u = 0.0f, sig = 0.0f, dy = 0.0f, dsp = 0.0f;
+      float dl = 0.0f, u = 0.0f, sig = 0.0f, dy = 0.0f, dsp = 0.0f, due = 0.0f;
       if (tt < len && on) {
-        const int64_t row = b * T + t0 + tt;
-        const int64_t e = row * Di + i;
-        const float dr = io::ld(p.delta_raw, e);
+        const int64_t e = (row0 + t0 + tt) * Di + i;
+        const float dr = raw_ld<A>(raw_dr, tt, c);
         dl = softplus(dr);
         sig = sigmoid(dr);
         if (FUSED) {
           float pre = cb;
 #pragma unroll
-          for (int k2 = 0; k2 < KMAX; ++k2) {
-            if (k2 < K) {
-              const int64_t s = t0 + tt - (K - 1) + k2;
-              float xv;
-              if (s >= 0) xv = io::ld(p.x, (b * T + s) * Di + i);
-              else xv = p.conv_state0 ? p.conv_state0[(b * Di + i) * K + (K + s)] : 0.0f;
-              pre = fmaf(cw[k2], xv, pre);
-            }
-          }
+          for (int k2 = 0; k2 < KMAX; ++k2)
+            if (k2 < K) pre = fmaf(cw[k2], s_x[tt + (KMAX - 1) - (K - 1) + k2][c], pre);
           const float sp = sigmoid(pre);
           u = pre * sp;
           dsp = sp * (1.0f + pre * (1.0f - sp));
+          if (p.d_u_extra) due = io::ld(p.d_u_extra, e);   // consumed in the epilogue
         } else {
-          u = io::ld(p.x, e);
+          u = raw_ld<A>(raw_x, tt, c);
         }
-        const float go = io::ld(p.dout, e);
+        const float go = raw_ld<A>(raw_go, tt, c);
         if (gate) {
-          const float zv = io::ld(p.z, e);
+          const float zv = raw_ld<A>(raw_z, tt, c);
           const float sz = sigmoid(zv);
           dy = go * zv * sz;
-          const float yv = io::ld(p.y_saved, e);
+          const float yv = raw_ld<A>(raw_y, tt, c);
           io::st(p.d_z, e, go * yv * (sz * (1.0f + zv * (1.0f - sz))));
         } else {
           dy = go;
         }
       }
-      s_dl[tt][c] = dl;
-      s_du[tt][c] = dl * u;
-      s_dy[tt][c] = dy;
-      e_dl[k] = dl;
-      e_u[k] = u;
+      s_st[tt][c] = make_float4(dl, dl * u, dy, u);
       e_sig[k] = sig;
-      e_dy[k] = dy;
       e_dsp[k] = dsp;
-    }
-    for (int j = tid; j < L * 2 * DS; j += NT) {
-      const int tt = j / (2 * DS), m = j % (2 * DS);
-      s_bc[tt][m] = tt < len ? io::ld(p.xdbl, (b * T + t0 + tt) * p.X + p.R + m) : 0.0f;
+      e_due[k] = due;
     }
     __syncthreads();
+    if (kt > 0) prefetch(kt - 1);
 
     // ------------------------------------------------------------ recompute
     float hs[L][SPL], das[L][SPL];
     {
-      float h[SPL];
+      float4 cur = s_st[0][c];
+      float cB[SPL], cC[SPL];
 #pragma unroll
-      for (int s = 0; s < SPL; ++s)
-        h[s] = on ? p.ckpt[((b * p.nC + kt) * DS + g * SPL + s) * Di + i] : 0.0f;
+      for (int s = 0; s < SPL; ++s) {
+        cB[s] = s_bc[0][0][g * SPL + s];
+        cC[s] = s_bc[0][1][g * SPL + s];
+      }
 #pragma unroll
       for (int sb = 0; sb < NSUB; ++sb) {
 #pragma unroll
         for (int q = 0; q < SUB; ++q) {
           const int tt = sb * SUB + q;
-          if (tt < len) {
-            const float dl = s_dl[tt][c];
-            const float du = s_du[tt][c];
-            const float dy = s_dy[tt][c];
+          float4 nxt = cur;
+          float nB[SPL], nC[SPL];
+#pragma unroll
+          for (int s = 0; s < SPL; ++s) {
+            nB[s] = cB[s];
+            nC[s] = cC[s];
+          }
+          if (tt + 1 < L) {
+            nxt = s_st[tt + 1][c];
 #pragma unroll
             for (int s = 0; s < SPL; ++s) {
-              const int n = g * SPL + s;
-              const float dA = exp2_fast(dl * a2[s]);
-              h[s] = fmaf(dA, h[s], du * s_bc[tt][n]);
-              hs[tt][s] = h[s];
-              das[tt][s] = dA;
-              red[c * (NO + 1) + q * SPL + s] = dy * h[s];
-            }
-          } else {
-#pragma unroll
-            for (int s = 0; s < SPL; ++s) {
-              hs[tt][s] = 0.0f;
-              das[tt][s] = 0.0f;
-              red[c * (NO + 1) + q * SPL + s] = 0.0f;
+              nB[s] = s_bc[tt + 1][0][g * SPL + s];
+              nC[s] = s_bc[tt + 1][1][g * SPL + s];
             }
           }
-          // keep the scheduler from hoisting later steps' LDS reads (each
-          // would hold a register across the whole unrolled chunk)
+#pragma unroll
+          for (int s = 0; s < SPL; ++s) {
+            const float dA = exp2_fast(cur.x * a2[s]);
+            h[s] = fmaf(dA, h[s], cur.y * cB[s]);
+            hs[tt][s] = h[s];
+            das[tt][s] = dA;
+            red[c * (NO + 1) + q * SPL + s] = cur.z * h[s];
+          }
+          cur = nxt;
+#pragma unroll
+          for (int s = 0; s < SPL; ++s) {
+            cB[s] = nB[s];
+            cC[s] = nC[s];
+          }
+          // keeps later steps' LDS reads from being hoisted (each would hold
+          // a register across the whole unrolled chunk)
           __builtin_amdgcn_sched_barrier(0);
         }
         wave_lds_sync();
         const float v = wave_channel_sum<NO>(red, c);
         if (c < NO) {
-          const int q = c / SPL, s = c % SPL;
-          const int tt = sb * SUB + q;
+          const int tt = sb * SUB + c / SPL;
           if (tt < len)
-            p.part_bc[(cg * BT + b * T + t0 + tt) * (2 * DS) + DS + g * SPL + s] = v;
+            p.part_bc[(cg * BT + row0 + t0 + tt) * (2 * DS) + DS + g * SPL + c % SPL] = v;
         }
         wave_lds_sync();
       }
     }
 
     // -------------------------------------------------------------- reverse
+    float4 cur = s_st[L - 1][c];
+    float cB[SPL], cC[SPL];
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) {
+      cB[s] = s_bc[L - 1][0][g * SPL + s];
+      cC[s] = s_bc[L - 1][1][g * SPL + s];
+    }
 #pragma unroll
     for (int sb = NSUB - 1; sb >= 0; --sb) {
 #pragma unroll
       for (int q = SUB - 1; q >= 0; --q) {
         const int tt = sb * SUB + q;
-        float su = 0.0f, sd = 0.0f;
-        if (tt < len) {
-          const float dl = s_dl[tt][c];
-          const float du = s_du[tt][c];
-          const float dy = s_dy[tt][c];
+        float4 nxt = cur;
+        float nB[SPL], nC[SPL];
+#pragma unroll
+        for (int s = 0; s < SPL; ++s) {
+          nB[s] = cB[s];
+          nC[s] = cC[s];
+        }
+        if (tt > 0) {
+          nxt = s_st[tt - 1][c];
 #pragma unroll
           for (int s = 0; s < SPL; ++s) {
-            const int n = g * SPL + s;
-            const float Bn = s_bc[tt][n];
-            const float Cn = s_bc[tt][DS + n];
-            const float dh = fmaf(dy, Cn, carry[s]);
-            const float dah = fmaf(-du, Bn, hs[tt][s]);   // dA h_{t-1} = h_t - delta u B
-            const float qv = dh * dah;
-            dacc[s] = fmaf(qv, dl, dacc[s]);
-            carry[s] = dh * das[tt][s];
-            su = fmaf(dh, Bn, su);
-            sd = fmaf(qv, an[s], sd);
-            red[c * (NO + 1) + q * SPL + s] = dh * du;
+            nB[s] = s_bc[tt - 1][0][g * SPL + s];
+            nC[s] = s_bc[tt - 1][1][g * SPL + s];
           }
-        } else {
+        }
+        float su = 0.0f, sd = 0.0f;
 #pragma unroll
-          for (int s = 0; s < SPL; ++s) red[c * (NO + 1) + q * SPL + s] = 0.0f;
+        for (int s = 0; s < SPL; ++s) {
+          const float dh = fmaf(cur.z, cC[s], carry[s]);
+          const float dah = fmaf(-cur.y, cB[s], hs[tt][s]);   // dA h_{t-1} = h_t - delta u B
+          const float qv = dh * dah;
+          dacc[s] = fmaf(qv, cur.x, dacc[s]);
+          carry[s] = dh * das[tt][s];
+          su = fmaf(dh, cB[s], su);
+          sd = fmaf(qv, an[s], sd);
+          red[c * (NO + 1) + q * SPL + s] = dh * cur.y;
         }
         s_su[g][q][c] = su;
         s_sd[g][q][c] = sd;
+        cur = nxt;
+#pragma unroll
+        for (int s = 0; s < SPL; ++s) {
+          cB[s] = nB[s];
+          cC[s] = nC[s];
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       wave_lds_sync();
       {
         const float v = wave_channel_sum<NO>(red, c);
         if (c < NO) {
-          const int q = c / SPL, s = c % SPL;
-          const int tt = sb * SUB + q;
+          const int tt = sb * SUB + c / SPL;
           if (tt < len)
-            p.part_bc[(cg * BT + b * T + t0 + tt) * (2 * DS) + g * SPL + s] = v;
+            p.part_bc[(cg * BT + row0 + t0 + tt) * (2 * DS) + g * SPL + c % SPL] = v;
         }
       }
       __syncthreads();
@@ -273,40 +351,34 @@ scan_bwd_kernel(const BwdArgs p) {
       // ---- epilogue: item (t0 + sb*SUB + g, channel c); stage slot k = sb
       const int tt = sb * SUB + g;
       const bool live = tt < len && on;
-      const int64_t e = (b * T + t0 + tt) * Di + i;
+      const int64_t e = (row0 + t0 + tt) * Di + i;
       float dp = 0.0f;
       if (live) {
+        const float4 st = s_st[tt][c];   // delta, delta*u, dy, u
         float su = 0.0f, sd = 0.0f;
 #pragma unroll
         for (int w = 0; w < G; ++w) {
           su += s_su[w][g][c];
           sd += s_sd[w][g][c];
         }
-        float du = fmaf(e_dl[sb], su, Dv * e_dy[sb]);
-        const float ddl = fmaf(e_u[sb], su, sd);
+        float du = fmaf(st.x, su, Dv * st.z);
+        const float ddl = fmaf(st.w, su, sd);
         io::st(p.d_delta_raw, e, ddl * e_sig[sb]);
-        acc_dD = fmaf(e_dy[sb], e_u[sb], acc_dD);
+        acc_dD = fmaf(st.z, st.w, acc_dD);
         if (FUSED) {
-          if (p.d_u_extra) du += io::ld(p.d_u_extra, e);
+          du += e_due[sb];
           dp = du * e_dsp[sb];
           acc_cb += dp;
 #pragma unroll
-          for (int k2 = 0; k2 < KMAX; ++k2) {
-            if (k2 < K) {
-              const int64_t s = t0 + tt - (K - 1) + k2;
-              float xv;
-              if (s >= 0) xv = io::ld(p.x, (b * T + s) * Di + i);
-              else xv = p.conv_state0 ? p.conv_state0[(b * Di + i) * K + (K + s)] : 0.0f;
-              acc_cw[k2] = fmaf(dp, xv, acc_cw[k2]);
-            }
-          }
+          for (int k2 = 0; k2 < KMAX; ++k2)
+            if (k2 < K) acc_cw[k2] = fmaf(dp, s_x[tt + (KMAX - 1) - (K - 1) + k2][c], acc_cw[k2]);
         } else {
           io::st(p.d_x, e, du);
         }
       }
       if (FUSED) {
         // d_x[s] = sum_k w_k dp[s + K-1-k]; rows >= SUB of s_dp hold the
-        // first K-1 dp of the later sub-tile (zero past the sequence end)
+        // dp of the K-1 steps after this sub-tile (zero past the end)
         s_dp[g][c] = dp;
         __syncthreads();
         if (live) {
@@ -368,7 +440,7 @@ template <Act A>
 hipError_t launch_bwd_a(const BwdArgs& p, int ds, int L, hipStream_t st) {
 #define MSCAN_CASE(DS_, L_) \
   if (ds == DS_ && L == L_) return launch_bwd_t<A, DS_, (64 / L_), L_>(p, st);
-  MSCAN_CASE(4, 16) MSCAN_CASE(4, 32) MSCAN_CASE(4, 64)
+  MSCAN_CASE(4, 16) MSCAN_CASE(4, 32)
   MSCAN_CASE(8, 16) MSCAN_CASE(8, 32)
   MSCAN_CASE(16, 16) MSCAN_CASE(16, 32)
   MSCAN_CASE(32, 16)

@@ -81,6 +81,58 @@ __device__ __forceinline__ float sigmoid(float x) {
   return rcp_fast(1.0f + exp2_fast(-x * kLog2e));
 }
 
+// ---------------------------------------------------------------- LDS staging
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+constexpr int pad4(int n) { return (n + 3) & ~3; }
+
+// Asynchronous copy (global_load_lds, no registers) of `nrows` time rows of
+// one 64-channel group of an activation tensor [B, T, Di] into LDS, one row
+// of 64 * ES bytes after another starting at `dst`.  Each lane moves one
+// granule of 4 bytes (16-bit types: 2 channels) or 16 bytes (f32: 4
+// channels); time rows are clamped to [0, T) and granules past Di re-read the
+// last granule of the row, so no load leaves the tensor (Di % 4 == 0).  The
+// caller ends the copy with a full s_waitcnt and a workgroup barrier.
+// nrows must be a multiple of 4; instructions are spread over the waves.
+template <int ES>
+__device__ __forceinline__ void async_rows(lds_char_t* dst, const void* src, int64_t row0, int64_t t_lo,
+                                           int64_t T, int64_t Di, int64_t i0, int nrows, int wave,
+                                           int nwaves, int lane) {
+  constexpr int GB = ES == 4 ? 16 : 4;   // bytes per lane
+  constexpr int GC = GB / ES;            // channels per lane
+  constexpr int LPR = 64 / GC;           // lanes per row
+  constexpr int RPI = 64 / LPR;          // rows per instruction
+  const int ninst = nrows / RPI;
+  int64_t ch = i0 + (lane % LPR) * GC;
+  if (ch > Di - GC) ch = Di - GC;
+  for (int j = wave; j < ninst; j += nwaves) {
+    int64_t t = t_lo + j * RPI + lane / LPR;
+    t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+    const char* g = static_cast<const char*>(src) + ((row0 + t) * Di + ch) * ES;
+    if constexpr (ES == 4)
+      __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(dst + j * 64 * GB), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(dst + j * 64 * GB), 4, 0, 0);
+  }
+}
+
+// read element c of raw row r (64 * ES bytes per row) as f32
+template <Act A>
+__device__ __forceinline__ float raw_ld(const char* base, int r, int c);
+template <>
+__device__ __forceinline__ float raw_ld<Act::F32>(const char* base, int r, int c) {
+  return reinterpret_cast<const float*>(base)[r * 64 + c];
+}
+template <>
+__device__ __forceinline__ float raw_ld<Act::BF16>(const char* base, int r, int c) {
+  return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(base)[r * 64 + c]) << 16);
+}
+template <>
+__device__ __forceinline__ float raw_ld<Act::F16>(const char* base, int r, int c) {
+  return static_cast<float>(reinterpret_cast<const _Float16*>(base)[r * 64 + c]);
+}
+
 // ---------------------------------------------------------------- arguments
 struct FwdArgs {
   const void* x;            // u (scan entry) or conv input (fused entry) [B,T,Di]

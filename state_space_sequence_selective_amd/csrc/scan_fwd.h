@@ -11,9 +11,10 @@
 // whole sequence.  Lane c of every wave is channel c; wave g holds states
 // [g*SPL, (g+1)*SPL) of all 64 channels in registers, so B_t / C_t reads are
 // wave-uniform LDS broadcasts.  Time advances in tiles of TT steps:
-//   stage   : every thread turns a few (t, channel) items of the tile into
-//             delta and delta*u (one softplus per item, shared by all
-//             waves through LDS); B/C rows of the tile go to LDS as f32.
+//   stage   : the tile's raw activations (copied to LDS asynchronously while
+//             the previous tile ran) become, per (t, channel) item, delta and
+//             delta*u in LDS (one softplus per item, shared by all waves);
+//             then the copies for the next tile are issued.
 //   scan    : each wave runs the recurrence for its states and leaves its
 //             partial C.h per (t, channel) in LDS.
 //   output  : the staging threads add the partials of all waves, add D*u,
@@ -31,22 +32,34 @@ scan_fwd_kernel(const FwdArgs p) {
   constexpr int NT = 64 * G;           // threads
   static_assert(TT % G == 0, "tile must hold a whole number of items per thread");
   constexpr int IPT = TT / G;          // (t, channel) items per thread per tile
+  constexpr int KMAX = 4;              // conv taps supported: 1..4
+  constexpr int ES = A == Act::F32 ? 4 : 2;
+  constexpr int RB = 64 * ES;
+  constexpr int XR = pad4(TT + KMAX - 1);   // raw x rows: conv halo, then the tile
+  constexpr int NBC = TT * 2 * DS;
+  constexpr int BCPT = (NBC + NT - 1) / NT;
   using io = IO<A>;
 
-  __shared__ float s_dl[TT][64];       // delta
-  __shared__ float s_du[TT][64];       // delta * u
-  __shared__ float s_bc[TT][2 * DS];   // B_t | C_t as f32
+  // raw tile: x (with halo) | delta_raw | z
+  __shared__ __attribute__((aligned(16))) char s_raw[(XR + 2 * TT) * RB];
+  __shared__ float2 s_st[TT][64];      // delta, delta*u
+  __shared__ float s_bc[TT][2][DS];    // B_t | C_t as f32
   __shared__ float s_yp[G][TT][64];    // per-wave partial C.h
 
   const int tid = threadIdx.x;
   const int c = tid & 63;
   const int g = tid >> 6;
   const int64_t b = blockIdx.y;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + c;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t i = i0 + c;
   const bool on = i < p.Di;
-  const int64_t T = p.T, Di = p.Di;
+  const int64_t T = p.T, Di = p.Di, row0 = b * p.T;
   const bool gate = p.z != nullptr;
   const int K = p.K;
+  lds_char_t* raw_l = (lds_char_t*)s_raw;
+  const char* raw_x = s_raw;
+  const char* raw_dr = s_raw + XR * RB;
+  const char* raw_z = s_raw + (XR + TT) * RB;
 
   float a2[SPL], h[SPL];
 #pragma unroll
@@ -56,27 +69,45 @@ scan_fwd_kernel(const FwdArgs p) {
     h[s] = (on && p.h0) ? p.h0[(b * Di + i) * DS + n] : 0.0f;
   }
   const float Dv = (on && p.D) ? p.D[i] : 0.0f;
-  constexpr int KMAX = 4;   // conv taps supported: 1..4
   float cw[KMAX];
   float cb = 0.0f;
-  if (K > 0) {
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) cw[k] = (on && k < K) ? p.conv_w[i * K + k] : 0.0f;
-    cb = (on && p.conv_b) ? p.conv_b[i] : 0.0f;
-  }
+  for (int k = 0; k < KMAX; ++k) cw[k] = (K > 0 && on && k < K) ? p.conv_w[i * K + k] : 0.0f;
+  if (K > 0) cb = (on && p.conv_b) ? p.conv_b[i] : 0.0f;
 
+  float bcn[BCPT];
+  auto prefetch = [&](int64_t t0) {
+    const int halo = K > 0 ? KMAX - 1 : 0;
+    async_rows<ES>(raw_l, p.x, row0, t0 - halo, T, Di, i0, XR, g, G, c);
+    async_rows<ES>(raw_l + XR * RB, p.delta_raw, row0, t0, T, Di, i0, TT, g, G, c);
+    if (gate) async_rows<ES>(raw_l + (XR + TT) * RB, p.z, row0, t0, T, Di, i0, TT, g, G, c);
+#pragma unroll
+    for (int q = 0; q < BCPT; ++q) {
+      const int j = tid + q * NT;
+      const int tt = j / (2 * DS), m = j % (2 * DS);
+      const bool ok = j < NBC && t0 + tt < T;
+      bcn[q] = ok ? io::ld(p.xdbl, (row0 + t0 + tt) * p.X + p.R + m) : 0.0f;
+    }
+  };
+
+  prefetch(0);
   for (int64_t t0 = 0; t0 < T; t0 += TT) {
     const int len = static_cast<int>(T - t0 < TT ? T - t0 : TT);
     float e_u[IPT], e_sz[IPT];
 
     // ---- stage
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < BCPT; ++q) {
+      const int j = tid + q * NT;
+      if (j < NBC) (&s_bc[0][0][0])[j] = bcn[q];
+    }
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       const int tt = g + G * k;
-      float dl = 0.0f, du = 0.0f, u = 0.0f, sz = 1.0f;
+      float dl = 0.0f, u = 0.0f, sz = 1.0f;
       if (tt < len && on) {
-        const int64_t row = b * T + t0 + tt;
-        const int64_t e = row * Di + i;
         if (K > 0) {
           float pre = cb;
 #pragma unroll
@@ -84,32 +115,27 @@ scan_fwd_kernel(const FwdArgs p) {
             if (k2 < K) {
               const int64_t s = t0 + tt - (K - 1) + k2;
               float xv;
-              if (s >= 0) xv = io::ld(p.x, (b * T + s) * Di + i);
+              if (s >= 0) xv = raw_ld<A>(raw_x, tt + (KMAX - 1) - (K - 1) + k2, c);
               else xv = p.conv_state0 ? p.conv_state0[(b * Di + i) * K + (K + s)] : 0.0f;
               pre = fmaf(cw[k2], xv, pre);
             }
           }
           u = pre * sigmoid(pre);
         } else {
-          u = io::ld(p.x, e);
+          u = raw_ld<A>(raw_x, tt, c);
         }
-        dl = softplus(io::ld(p.delta_raw, e));
-        du = dl * u;
+        dl = softplus(raw_ld<A>(raw_dr, tt, c));
         if (gate) {
-          const float zv = io::ld(p.z, e);
+          const float zv = raw_ld<A>(raw_z, tt, c);
           sz = zv * sigmoid(zv);
         }
       }
-      s_dl[tt][c] = dl;
-      s_du[tt][c] = du;
+      s_st[tt][c] = make_float2(dl, dl * u);
       e_u[k] = u;
       e_sz[k] = sz;
     }
-    for (int j = tid; j < TT * 2 * DS; j += NT) {
-      const int tt = j / (2 * DS), m = j % (2 * DS);
-      s_bc[tt][m] = tt < len ? io::ld(p.xdbl, (b * T + t0 + tt) * p.X + p.R + m) : 0.0f;
-    }
     __syncthreads();
+    if (t0 + TT < T) prefetch(t0 + TT);
 
     // ---- checkpoint: the state entering step t0 (TT divides L)
     if (p.ckpt && on && (t0 % p.L) == 0) {
@@ -119,22 +145,20 @@ scan_fwd_kernel(const FwdArgs p) {
         p.ckpt[((b * p.nC + cidx) * DS + g * SPL + s) * Di + i] = h[s];
     }
 
-    // ---- scan
+    // ---- scan (steps past the end of the sequence see delta = 0, B = C = 0:
+    // identities that leave h unchanged)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      if (tt < len) {
-        const float dl = s_dl[tt][c];
-        const float du = s_du[tt][c];
-        float yp = 0.0f;
+      const float2 st = s_st[tt][c];
+      float yp = 0.0f;
 #pragma unroll
-        for (int s = 0; s < SPL; ++s) {
-          const int n = g * SPL + s;
-          const float dA = exp2_fast(dl * a2[s]);
-          h[s] = fmaf(dA, h[s], du * s_bc[tt][n]);
-          yp = fmaf(s_bc[tt][DS + n], h[s], yp);
-        }
-        s_yp[g][tt][c] = yp;
+      for (int s = 0; s < SPL; ++s) {
+        const int n = g * SPL + s;
+        const float dA = exp2_fast(st.x * a2[s]);
+        h[s] = fmaf(dA, h[s], st.y * s_bc[tt][0][n]);
+        yp = fmaf(s_bc[tt][1][n], h[s], yp);
       }
+      s_yp[g][tt][c] = yp;
     }
     __syncthreads();
 
@@ -146,13 +170,12 @@ scan_fwd_kernel(const FwdArgs p) {
         float y = Dv * e_u[k];
 #pragma unroll
         for (int w = 0; w < G; ++w) y += s_yp[w][tt][c];
-        const int64_t e = (b * T + t0 + tt) * Di + i;
+        const int64_t e = (row0 + t0 + tt) * Di + i;
         io::st(p.out, e, gate ? y * e_sz[k] : y);
         if (p.y_save) io::st(p.y_save, e, y);
         if (p.u_out) io::st(p.u_out, e, e_u[k]);
       }
     }
-    __syncthreads();
   }
 
   if (p.h_last && on) {
@@ -163,7 +186,7 @@ scan_fwd_kernel(const FwdArgs p) {
     for (int k = 0; k < K; ++k) {
       const int64_t s = T - K + k;
       float xv;
-      if (s >= 0) xv = io::ld(p.x, (b * T + s) * Di + i);
+      if (s >= 0) xv = io::ld(p.x, (row0 + s) * Di + i);
       else xv = p.conv_state0 ? p.conv_state0[(b * Di + i) * K + (K + s)] : 0.0f;
       p.conv_state_last[(b * Di + i) * K + k] = xv;
     }
@@ -171,10 +194,9 @@ scan_fwd_kernel(const FwdArgs p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <Act A, int DS, int SPL>
+template <Act A, int DS, int SPL, int TT>
 static hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t st) {
   constexpr int G = DS / SPL;
-  constexpr int TT = G >= 16 ? G : 16;
   dim3 grid(static_cast<unsigned>((p.Di + 63) / 64), static_cast<unsigned>(p.B));
   hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT>), grid, dim3(64 * G), 0, st, p);
   return hipGetLastError();
@@ -182,13 +204,11 @@ static hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t st) {
 
 template <Act A>
 hipError_t launch_fwd_a(const FwdArgs& p, int ds, int spl, hipStream_t st) {
-#define MSCAN_CASE(DS_, SPL_) \
-  if (ds == DS_ && spl == SPL_) return launch_fwd_t<A, DS_, SPL_>(p, st);
-  MSCAN_CASE(4, 1) MSCAN_CASE(4, 2) MSCAN_CASE(4, 4)
-  MSCAN_CASE(8, 1) MSCAN_CASE(8, 2) MSCAN_CASE(8, 4)
-  MSCAN_CASE(16, 1) MSCAN_CASE(16, 2) MSCAN_CASE(16, 4)
-  MSCAN_CASE(32, 2) MSCAN_CASE(32, 4)
-  MSCAN_CASE(64, 4)
+  // tiles of 32 steps (16 when the checkpoint interval is 16)
+#define MSCAN_CASE(DS_, SPL_)                                                         \
+  if (ds == DS_ && spl == SPL_)                                                       \
+    return p.L % 32 == 0 ? launch_fwd_t<A, DS_, SPL_, 32>(p, st) : launch_fwd_t<A, DS_, SPL_, 16>(p, st);
+  MSCAN_CASE(4, 1) MSCAN_CASE(8, 2) MSCAN_CASE(16, 2) MSCAN_CASE(32, 4)
 #undef MSCAN_CASE
   return hipErrorInvalidValue;
 }

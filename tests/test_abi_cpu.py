@@ -69,7 +69,7 @@ def test_sizes(pkg):
     (dict(d_state=64), 2, "d_state"),
     (dict(chunk=48), 2, "chunk"),
     (dict(chunk=-16), 1, "chunk"),
-    (dict(chunk=64), 2, "chunk"),                 # d_state 16 holds at most 32 steps
+    (dict(chunk=64), 2, "chunk"),
     (dict(d_state=32, chunk=32), 2, "chunk"),
     (dict(dt_rank=-1), 1, "dt_rank"),
     (dict(act=5), 1, "act"),

@@ -139,7 +139,7 @@ TINY = workloads.CONFIGS["tiny_f32"]
 SMALL_FUSED = workloads.CONFIGS["fused_small_bf16"]
 
 
-@pytest.mark.parametrize("chunk", [64, 32, 16])
+@pytest.mark.parametrize("chunk", [32, 16])
 def test_tiny_f32(mscan, oracle_lib, chunk):
     run_case(mscan, oracle_lib, TINY, chunk=chunk)
 
@@ -161,7 +161,7 @@ def test_fused_ragged_states_and_extras(mscan, oracle_lib, act):
     run_case(mscan, oracle_lib, w, chunk=16, h0=True, conv_state0=True, d_u_extra=True)
 
 
-@pytest.mark.parametrize("ds,chunk", [(4, 64), (8, 32), (8, 16), (16, 16), (32, 16)])
+@pytest.mark.parametrize("ds,chunk", [(4, 32), (4, 16), (8, 32), (8, 16), (16, 16), (32, 16)])
 def test_state_sizes(mscan, oracle_lib, ds, chunk):
     w = workloads.Workload("ds%d" % ds, 2, 70, 132, ds, 3, 0, "bf16", True)
     run_case(mscan, oracle_lib, w, chunk=chunk, h0=True)

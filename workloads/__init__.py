@@ -49,15 +49,13 @@ class Workload:
 
 CONFIGS = {
     # single layer, f32 throughout, no conv and no gate
-    "tiny_f32": Workload("tiny_f32", 1, 64, 16, 4, 0, 0, "f32", False, chunk=64,
-                         delta_mean=0.0),
+    "tiny_f32": Workload("tiny_f32", 1, 64, 16, 4, 0, 0, "f32", False, delta_mean=0.0),
     # conv1d(4) + SiLU + scan + gate, bf16 activations (d_model 128 -> d_inner 256)
     "fused_small_bf16": Workload("fused_small_bf16", 8, 128, 256, 16, 8, 4, "bf16", True),
     # scan + gate at a ~130M-model layer shape, bf16
-    "scan_130m_bf16": Workload("scan_130m_bf16", 4, 2048, 1536, 16, 0, 0, "bf16", True, chunk=64),
+    "scan_130m_bf16": Workload("scan_130m_bf16", 4, 2048, 1536, 16, 0, 0, "bf16", True),
     # long-sequence scan + gate at a ~2.8B-model layer shape, bf16
-    "scan_2p8b_t8192_bf16": Workload("scan_2p8b_t8192_bf16", 2, 8192, 5120, 16, 0, 0, "bf16", True,
-                                     chunk=64),
+    "scan_2p8b_t8192_bf16": Workload("scan_2p8b_t8192_bf16", 2, 8192, 5120, 16, 0, 0, "bf16", True),
     # 24 stacked fused layers (d_model 1024 -> d_inner 2048), f16
     "fused_24l_f16": Workload("fused_24l_f16", 8, 4096, 2048, 16, 64, 4, "f16", True, layers=24),
 }
