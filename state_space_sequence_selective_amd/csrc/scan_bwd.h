@@ -79,6 +79,13 @@ scan_bwd_kernel(const BwdArgs p) {
   constexpr int XR = pad4(L + KMAX - 1);   // raw x rows: conv halo, then the tile
   constexpr int NBC = L * 2 * DS;      // B/C values per tile
   constexpr int BCPT = (NBC + NT - 1) / NT;
+  // The cross-state partials are double-buffered when LDS allows it: the
+  // next sub-tile's producers then need not wait for this sub-tile's
+  // epilogue (one barrier per sub-tile instead of two).
+  constexpr int LDS_FIXED = (XR + 4 * L) * RB + L * 64 * 16 + (FUSED ? (L + KMAX - 1) * 64 * 4 : 256) +
+                            L * 2 * DS * 4 + G * 64 * (NO + 1) * 4 + (SUB + KMAX) * 64 * 4;
+  constexpr int PART = 2 * G * SUB * 64 * 4;
+  constexpr int NBUF = LDS_FIXED + 2 * PART <= 160 * 1024 ? 2 : 1;
   using io = IO<A>;
 
   // raw tile: x (with halo) | delta_raw | dout | z | y
@@ -86,8 +93,8 @@ scan_bwd_kernel(const BwdArgs p) {
   __shared__ float4 s_st[L][64];       // delta, delta*u, dy, u
   __shared__ float s_x[FUSED ? L + KMAX - 1 : 1][64];
   __shared__ float s_bc[L][2][DS];
-  __shared__ float s_su[G][SUB][64];   // per-wave sum_n dh B
-  __shared__ float s_sd[G][SUB][64];   // per-wave sum_n dh A dA h_{t-1}
+  __shared__ float s_su[NBUF][G][SUB][64];   // per-wave sum_n dh B
+  __shared__ float s_sd[NBUF][G][SUB][64];   // per-wave sum_n dh A dA h_{t-1}
   __shared__ float s_red[G][64 * (NO + 1)];
   __shared__ float s_dp[SUB + KMAX][64];
 
@@ -297,6 +304,7 @@ scan_bwd_kernel(const BwdArgs p) {
     }
 #pragma unroll
     for (int sb = NSUB - 1; sb >= 0; --sb) {
+      const int bi = NBUF == 2 ? (sb & 1) : 0;
 #pragma unroll
       for (int q = SUB - 1; q >= 0; --q) {
         const int tt = sb * SUB + q;
@@ -327,8 +335,8 @@ scan_bwd_kernel(const BwdArgs p) {
           sd = fmaf(qv, an[s], sd);
           red[c * (NO + 1) + q * SPL + s] = dh * cur.y;
         }
-        s_su[g][q][c] = su;
-        s_sd[g][q][c] = sd;
+        s_su[bi][g][q][c] = su;
+        s_sd[bi][g][q][c] = sd;
         cur = nxt;
 #pragma unroll
         for (int s = 0; s < SPL; ++s) {
@@ -358,8 +366,8 @@ scan_bwd_kernel(const BwdArgs p) {
         float su = 0.0f, sd = 0.0f;
 #pragma unroll
         for (int w = 0; w < G; ++w) {
-          su += s_su[w][g][c];
-          sd += s_sd[w][g][c];
+          su += s_su[bi][w][g][c];
+          sd += s_sd[bi][w][g][c];
         }
         float du = fmaf(st.x, su, Dv * st.z);
         const float ddl = fmaf(st.w, su, sd);
@@ -395,9 +403,10 @@ scan_bwd_kernel(const BwdArgs p) {
         if (g == 0)
           for (int j = K - 2; j >= 0; --j) s_dp[SUB + j][c] = s_dp[j][c];
       }
-      __syncthreads();
+      if (NBUF == 1) __syncthreads();
     }
   }
+  __syncthreads();
 
   // ------------------------------------------------ per batch-row partials
   const int64_t pb = (b * Di + i) * p.PW;
@@ -411,11 +420,11 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int k2 = 0; k2 < KMAX; ++k2)
       if (qd == k2 + 2) v = acc_cw[k2];
-    s_su[g][0][c] = v;
+    s_su[0][g][0][c] = v;
     __syncthreads();
     if (g == 0 && on) {
       float tot = 0.0f;
-      for (int w = 0; w < G; ++w) tot += s_su[w][0][c];
+      for (int w = 0; w < G; ++w) tot += s_su[0][w][0][c];
       // layout within PW: [Ds a_log | 1 D | K conv_w | 1 conv_b]
       const int slot = qd == 0 ? DS : (qd == 1 ? DS + 1 + K : DS + 1 + (qd - 2));
       p.part_par[pb + slot] = tot;

@@ -32,16 +32,9 @@ struct IO<Act::BF16> {
     const uint32_t b = static_cast<const uint16_t*>(p)[i];
     return __uint_as_float(b << 16);
   }
-  // round to nearest even; NaN stays a (quiet) NaN
+  // hardware conversion (v_cvt_pk_bf16_f32), round to nearest even
   static __device__ __forceinline__ void st(void* p, int64_t i, float v) {
-    const uint32_t u = __float_as_uint(v);
-    uint16_t r;
-    if ((u & 0x7fffffffu) > 0x7f800000u) {
-      r = static_cast<uint16_t>((u >> 16) | 0x40u);
-    } else {
-      r = static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-    }
-    static_cast<uint16_t*>(p)[i] = r;
+    static_cast<__bf16*>(p)[i] = static_cast<__bf16>(v);
   }
 };
 
@@ -67,7 +60,7 @@ __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ float log1p_small(float e) {
   const float w = 1.0f + e;
   if (w == 1.0f) return e;
-  return __builtin_amdgcn_logf(w) * 0.6931471805599453f * (e / (w - 1.0f));
+  return __builtin_amdgcn_logf(w) * 0.6931471805599453f * (e * rcp_fast(w - 1.0f));
 }
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|)

@@ -90,14 +90,10 @@ scan_fwd_kernel(const FwdArgs p) {
     }
   };
 
-  prefetch(0);
-  for (int64_t t0 = 0; t0 < T; t0 += TT) {
+  float e_u[IPT], e_sz[IPT];
+  // per-item work of one tile: delta, delta*u to LDS; u and silu(z) kept
+  auto stage = [&](int64_t t0) {
     const int len = static_cast<int>(T - t0 < TT ? T - t0 : TT);
-    float e_u[IPT], e_sz[IPT];
-
-    // ---- stage
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 #pragma unroll
     for (int q = 0; q < BCPT; ++q) {
       const int j = tid + q * NT;
@@ -134,9 +130,34 @@ scan_fwd_kernel(const FwdArgs p) {
       e_u[k] = u;
       e_sz[k] = sz;
     }
-    __syncthreads();
-    if (t0 + TT < T) prefetch(t0 + TT);
+  };
+  // combine the per-wave partials of one tile, gate, store
+  auto output = [&](int64_t t0) {
+    const int len = static_cast<int>(T - t0 < TT ? T - t0 : TT);
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int tt = g + G * k;
+      if (tt < len && on) {
+        float y = Dv * e_u[k];
+#pragma unroll
+        for (int w = 0; w < G; ++w) y += s_yp[w][tt][c];
+        const int64_t e = (row0 + t0 + tt) * Di + i;
+        io::st(p.out, e, gate ? y * e_sz[k] : y);
+        if (p.y_save) io::st(p.y_save, e, y);
+        if (p.u_out) io::st(p.u_out, e, e_u[k]);
+      }
+    }
+  };
 
+  // Two barriers per tile: (scan k) | wait + barrier | output k, stage k+1 |
+  // barrier | issue copies for k+2, (scan k+1) ...
+  prefetch(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  stage(0);
+  __syncthreads();
+  if (TT < T) prefetch(TT);
+  for (int64_t t0 = 0; t0 < T; t0 += TT) {
     // ---- checkpoint: the state entering step t0 (TT divides L)
     if (p.ckpt && on && (t0 % p.L) == 0) {
       const int64_t cidx = t0 / p.L;
@@ -160,22 +181,13 @@ scan_fwd_kernel(const FwdArgs p) {
       }
       s_yp[g][tt][c] = yp;
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    // ---- output
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-      const int tt = g + G * k;
-      if (tt < len && on) {
-        float y = Dv * e_u[k];
-#pragma unroll
-        for (int w = 0; w < G; ++w) y += s_yp[w][tt][c];
-        const int64_t e = (row0 + t0 + tt) * Di + i;
-        io::st(p.out, e, gate ? y * e_sz[k] : y);
-        if (p.y_save) io::st(p.y_save, e, y);
-        if (p.u_out) io::st(p.u_out, e, e_u[k]);
-      }
-    }
+    output(t0);
+    const bool more = t0 + TT < T;
+    if (more) stage(t0 + TT);
+    __syncthreads();
+    if (t0 + 2 * TT < T) prefetch(t0 + 2 * TT);
   }
 
   if (p.h_last && on) {
