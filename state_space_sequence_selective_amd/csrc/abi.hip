@@ -95,7 +95,7 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   pl->X = X;
   pl->L = L;
   pl->nC = (d->seqlen + L - 1) / L;
-  pl->nG = (d->d_inner + 63) / 64;
+  pl->nG = (d->d_inner + mscan::kBwdCpw - 1) / mscan::kBwdCpw;
   pl->K = K;
   pl->spl_fwd = d->d_state == 4 ? 1 : (d->d_state == 32 ? 4 : 2);
   pl->act = static_cast<mscan::Act>(d->act);

@@ -12,23 +12,25 @@
 //   d_A     += dh delta_t dA h_{t-1}       carry = dh dA
 // with d_u_t += D dy_t, d_D += dy_t u_t and d_a_log = A d_A (A = -exp(a_log)).
 //
-// Mapping.  A workgroup owns 64 channels (lanes) of one batch row; wave g
-// owns states [g*SPL, (g+1)*SPL).  The sequence is walked backwards in
-// tiles of L steps, L being the checkpoint interval.  Per tile:
+// Mapping.  A workgroup owns CPW channels of one batch row; thread (gs, c)
+// owns channel c's states [gs*SPL, (gs+1)*SPL) and a wave covers 64 / CPW
+// state groups.  The sequence is walked backwards in tiles of L steps, L
+// being the checkpoint interval.  Per tile:
 //   stage     : the tile's raw activations (already in LDS, copied there
 //               asynchronously during the previous tile) become, per
 //               (t, channel) item, {delta, delta*u, dy, u} in LDS; d_z =
 //               dout * y * silu'(z) is written at once from the saved y.
 //               Then the copies for the next tile are issued.
-//   recompute : from the checkpoint each wave re-runs its states over the
+//   recompute : from the checkpoint each thread re-runs its states over the
 //               tile and keeps h_t and dA_t of every step in registers
-//               (SPL*L = 64 of each).  Every G steps the wave sums dy*h over
-//               its 64 channels (d_C) in a wave-private LDS block.
-//   reverse   : G steps at a time each wave runs the adjoint of its states,
-//               sums delta*u*dh over its channels (d_B) the same way, and
+//               (SPL*L = 64 of each).  Every G steps each state group sums
+//               dy*h over its CPW channels (d_C) in a private LDS block.
+//   reverse   : G steps at a time each thread runs the adjoint of its states,
+//               its state group sums delta*u*dh over the channels (d_B) the
+//               same way, and
 //               leaves per-(t, channel) partials of sum_n dh B and
 //               sum_n dh A dA h_{t-1} in LDS; the epilogue threads add the
-//               partials of all waves and write d_u (or, fused, push d_u
+//               partials of all groups and write d_u (or, fused, push d_u
 //               through SiLU and the conv) and d_delta_raw.
 // Past the end of the sequence the staged values are zero, which makes the
 // extra steps of a short last tile identities, so the step loops need no
@@ -47,63 +49,71 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// Sum a wave-private block red[c][o] (64 channels x NO outputs, row stride
-// NO + 1) over c.  Returns the total for output o = lane % NO on the lanes
-// with lane / NO == 0.
-template <int NO>
-__device__ __forceinline__ float wave_channel_sum(const float* red, int lane) {
-  static_assert(NO <= 64 && (64 % NO) == 0, "outputs per block");
-  constexpr int LPO = 64 / NO;     // lanes per output
-  constexpr int CPL = 64 / LPO;    // channels per lane
-  const int o = lane % NO, part = lane / NO;
+// Sum a group-private block red[c][o] (CPW channels x NO outputs, row
+// stride NO + 1) over c; the group is the CPW consecutive lanes of one wave
+// with channel index c.  Returns the total for output o = c % NO on the
+// lanes with c / NO == 0.
+template <int NO, int CPW>
+__device__ __forceinline__ float group_channel_sum(const float* red, int c) {
+  static_assert(NO <= CPW && (CPW % NO) == 0, "outputs per block");
+  constexpr int LPO = CPW / NO;    // lanes per output
+  constexpr int CPL = CPW / LPO;   // channels per lane
+  const int o = c % NO, part = c / NO;
   float acc = 0.0f;
 #pragma unroll
   for (int m = 0; m < CPL; ++m) acc += red[(part * CPL + m) * (NO + 1) + o];
 #pragma unroll
-  for (int off = NO; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  for (int off = NO; off < CPW; off <<= 1) acc += __shfl_xor(acc, off, 64);
   return acc;
 }
 
-template <Act A, int DS, int SPL, int L, bool FUSED>
-__global__ void __launch_bounds__(64 * (DS / SPL))
+template <Act A, int DS, int SPL, int L, bool FUSED, int CPW>
+__global__ void __launch_bounds__(CPW * (DS / SPL))
 scan_bwd_kernel(const BwdArgs p) {
-  constexpr int G = DS / SPL;          // waves
-  constexpr int NT = 64 * G;
+  constexpr int G = DS / SPL;          // state groups
+  constexpr int NT = CPW * G;          // threads: (state group, channel)
+  static_assert(NT % 64 == 0, "whole waves");
   constexpr int SUB = G;               // steps per reverse sub-tile
   static_assert(L % SUB == 0, "sub-tiles must tile the chunk");
   constexpr int NSUB = L / SUB;        // = staged items per thread
-  constexpr int NO = SUB * SPL;        // channel sums per wave per sub-tile
+  constexpr int NO = SUB * SPL;        // channel sums per group per sub-tile (= DS)
   constexpr int KMAX = FUSED ? 4 : 1;  // conv taps supported: 1..4
   constexpr int ES = A == Act::F32 ? 4 : 2;
-  constexpr int RB = 64 * ES;          // bytes per raw row
-  constexpr int XR = pad4(L + KMAX - 1);   // raw x rows: conv halo, then the tile
+  constexpr int RB = CPW * ES;         // bytes per raw row
+  constexpr int RPI = rows_per_inst<ES, CPW>();
+  constexpr int XR = round_up(L + KMAX - 1, RPI);   // raw x rows: conv halo, then the tile
+  constexpr int TR = round_up(L, RPI);
   constexpr int NBC = L * 2 * DS;      // B/C values per tile
   constexpr int BCPT = (NBC + NT - 1) / NT;
   // The cross-state partials are double-buffered when LDS allows it: the
   // next sub-tile's producers then need not wait for this sub-tile's
   // epilogue (one barrier per sub-tile instead of two).
-  constexpr int LDS_FIXED = (XR + 4 * L) * RB + L * 64 * 16 + (FUSED ? (L + KMAX - 1) * 64 * 4 : 256) +
-                            L * 2 * DS * 4 + G * 64 * (NO + 1) * 4 + (SUB + KMAX) * 64 * 4;
-  constexpr int PART = 2 * G * SUB * 64 * 4;
+  constexpr int LDS_FIXED = (XR + 4 * TR) * RB + L * CPW * 16 + (FUSED ? (L + KMAX - 1) * CPW * 4 : 4) +
+                            L * 2 * DS * 4 + G * CPW * (NO + 1) * 4 + (SUB + KMAX) * CPW * 4;
+  constexpr int PART = 2 * G * SUB * CPW * 4;
   constexpr int NBUF = LDS_FIXED + 2 * PART <= 160 * 1024 ? 2 : 1;
   using io = IO<A>;
 
   // raw tile: x (with halo) | delta_raw | dout | z | y
-  __shared__ __attribute__((aligned(16))) char s_raw[(XR + 4 * L) * RB];
-  __shared__ float4 s_st[L][64];       // delta, delta*u, dy, u
-  __shared__ float s_x[FUSED ? L + KMAX - 1 : 1][64];
+  __shared__ __attribute__((aligned(16))) char s_raw[(XR + 4 * TR) * RB];
+  __shared__ float4 s_st[L][CPW];      // delta, delta*u, dy, u
+  __shared__ float s_x[FUSED ? L + KMAX - 1 : 1][CPW];
   __shared__ float s_bc[L][2][DS];
-  __shared__ float s_su[NBUF][G][SUB][64];   // per-wave sum_n dh B
-  __shared__ float s_sd[NBUF][G][SUB][64];   // per-wave sum_n dh A dA h_{t-1}
-  __shared__ float s_red[G][64 * (NO + 1)];
-  __shared__ float s_dp[SUB + KMAX][64];
+  __shared__ float s_su[NBUF][G][SUB][CPW];   // per-group sum_n dh B
+  __shared__ float s_sd[NBUF][G][SUB][CPW];   // per-group sum_n dh A dA h_{t-1}
+  __shared__ float s_red[G][CPW * (NO + 1)];
+  __shared__ float s_dp[SUB + KMAX][CPW];
 
   const int tid = threadIdx.x;
-  const int c = tid & 63;
-  const int g = tid >> 6;
-  const int64_t b = blockIdx.y;
-  const int64_t cg = blockIdx.x;
-  const int64_t i0 = cg * 64;
+  const int c = tid % CPW;             // channel within the group
+  const int g = tid / CPW;             // state group
+  const int wave = tid >> 6, lane = tid & 63;
+  constexpr int NW = (NT + 63) / 64;
+  const int64_t ngrp = (p.Di + CPW - 1) / CPW;
+  const int64_t wg = xcd_pair_map(blockIdx.x, ngrp * p.B);
+  const int64_t b = wg / ngrp;
+  const int64_t cg = wg % ngrp;
+  const int64_t i0 = cg * CPW;
   const int64_t i = i0 + c;
   const bool on = i < p.Di;
   const int64_t T = p.T, Di = p.Di, BT = p.B * p.T, row0 = b * p.T;
@@ -113,9 +123,9 @@ scan_bwd_kernel(const BwdArgs p) {
   lds_char_t* raw_l = (lds_char_t*)s_raw;
   const char* raw_x = s_raw;
   const char* raw_dr = s_raw + XR * RB;
-  const char* raw_go = s_raw + (XR + L) * RB;
-  const char* raw_z = s_raw + (XR + 2 * L) * RB;
-  const char* raw_y = s_raw + (XR + 3 * L) * RB;
+  const char* raw_go = s_raw + (XR + TR) * RB;
+  const char* raw_z = s_raw + (XR + 2 * TR) * RB;
+  const char* raw_y = s_raw + (XR + 3 * TR) * RB;
 
   float a2[SPL], an[SPL], carry[SPL], dacc[SPL];
 #pragma unroll
@@ -137,19 +147,19 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) acc_cw[k] = 0.0f;
   if (FUSED)
-    for (int j = tid; j < (SUB + KMAX) * 64; j += NT) (&s_dp[0][0])[j] = 0.0f;
+    for (int j = tid; j < (SUB + KMAX) * CPW; j += NT) (&s_dp[0][0])[j] = 0.0f;
 
   // ---- prefetch of one tile: raw activations to LDS (async), B/C rows and
   // the checkpoint to registers
   float bcn[BCPT], hn[SPL];
   auto prefetch = [&](int64_t kt) {
     const int64_t t0 = kt * L;
-    async_rows<ES>(raw_l, p.x, row0, t0 - (KMAX - 1), T, Di, i0, XR, g, G, c);
-    async_rows<ES>(raw_l + XR * RB, p.delta_raw, row0, t0, T, Di, i0, L, g, G, c);
-    async_rows<ES>(raw_l + (XR + L) * RB, p.dout, row0, t0, T, Di, i0, L, g, G, c);
+    async_rows<ES, CPW>(raw_l, p.x, row0, t0 - (KMAX - 1), T, Di, i0, XR, wave, NW, lane);
+    async_rows<ES, CPW>(raw_l + XR * RB, p.delta_raw, row0, t0, T, Di, i0, TR, wave, NW, lane);
+    async_rows<ES, CPW>(raw_l + (XR + TR) * RB, p.dout, row0, t0, T, Di, i0, TR, wave, NW, lane);
     if (gate) {
-      async_rows<ES>(raw_l + (XR + 2 * L) * RB, p.z, row0, t0, T, Di, i0, L, g, G, c);
-      async_rows<ES>(raw_l + (XR + 3 * L) * RB, p.y_saved, row0, t0, T, Di, i0, L, g, G, c);
+      async_rows<ES, CPW>(raw_l + (XR + 2 * TR) * RB, p.z, row0, t0, T, Di, i0, TR, wave, NW, lane);
+      async_rows<ES, CPW>(raw_l + (XR + 3 * TR) * RB, p.y_saved, row0, t0, T, Di, i0, TR, wave, NW, lane);
     }
 #pragma unroll
     for (int q = 0; q < BCPT; ++q) {
@@ -183,12 +193,12 @@ scan_bwd_kernel(const BwdArgs p) {
       if (j < NBC) (&s_bc[0][0][0])[j] = bcn[q];
     }
     if (FUSED) {
-      for (int j = tid; j < (L + KMAX - 1) * 64; j += NT) {
-        const int r = j >> 6, cc = j & 63;
+      for (int j = tid; j < (L + KMAX - 1) * CPW; j += NT) {
+        const int r = j / CPW, cc = j % CPW;
         const int64_t s = t0 - (KMAX - 1) + r;
         float xv = 0.0f;
         if (i0 + cc < Di) {
-          if (s >= 0) xv = raw_ld<A>(raw_x, r, cc);
+          if (s >= 0) xv = raw_ld<A>(raw_x, r * CPW + cc);
           else if (p.conv_state0 && s >= -(int64_t)K) xv = p.conv_state0[(b * Di + i0 + cc) * K + (K + s)];
         }
         s_x[r][cc] = xv;
@@ -201,7 +211,7 @@ scan_bwd_kernel(const BwdArgs p) {
       float dl = 0.0f, u = 0.0f, sig = 0.0f, dy = 0.0f, dsp = 0.0f, due = 0.0f;
       if (tt < len && on) {
         const int64_t e = (row0 + t0 + tt) * Di + i;
-        const float dr = raw_ld<A>(raw_dr, tt, c);
+        const float dr = raw_ld<A>(raw_dr, tt * CPW + c);
         dl = softplus(dr);
         sig = sigmoid(dr);
         if (FUSED) {
@@ -214,14 +224,14 @@ scan_bwd_kernel(const BwdArgs p) {
           dsp = sp * (1.0f + pre * (1.0f - sp));
           if (p.d_u_extra) due = io::ld(p.d_u_extra, e);   // consumed in the epilogue
         } else {
-          u = raw_ld<A>(raw_x, tt, c);
+          u = raw_ld<A>(raw_x, tt * CPW + c);
         }
-        const float go = raw_ld<A>(raw_go, tt, c);
+        const float go = raw_ld<A>(raw_go, tt * CPW + c);
         if (gate) {
-          const float zv = raw_ld<A>(raw_z, tt, c);
+          const float zv = raw_ld<A>(raw_z, tt * CPW + c);
           const float sz = sigmoid(zv);
           dy = go * zv * sz;
-          const float yv = raw_ld<A>(raw_y, tt, c);
+          const float yv = raw_ld<A>(raw_y, tt * CPW + c);
           io::st(p.d_z, e, go * yv * (sz * (1.0f + zv * (1.0f - sz))));
         } else {
           dy = go;
@@ -284,7 +294,7 @@ scan_bwd_kernel(const BwdArgs p) {
           __builtin_amdgcn_sched_barrier(0);
         }
         wave_lds_sync();
-        const float v = wave_channel_sum<NO>(red, c);
+        const float v = group_channel_sum<NO, CPW>(red, c);
         if (c < NO) {
           const int tt = sb * SUB + c / SPL;
           if (tt < len)
@@ -347,7 +357,7 @@ scan_bwd_kernel(const BwdArgs p) {
       }
       wave_lds_sync();
       {
-        const float v = wave_channel_sum<NO>(red, c);
+        const float v = group_channel_sum<NO, CPW>(red, c);
         if (c < NO) {
           const int tt = sb * SUB + c / SPL;
           if (tt < len)
@@ -437,18 +447,23 @@ scan_bwd_kernel(const BwdArgs p) {
 template <Act A, int DS, int SPL, int L>
 static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
   constexpr int G = DS / SPL;
-  dim3 grid(static_cast<unsigned>((p.Di + 63) / 64), static_cast<unsigned>(p.B));
+  constexpr int CPW = kBwdCpw;
+  const int64_t ng = (p.Di + CPW - 1) / CPW;
+  dim3 grid(static_cast<unsigned>(ng * p.B));
   if (p.K > 0)
-    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true>), grid, dim3(64 * G), 0, st, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true, CPW>), grid, dim3(CPW * G), 0, st, p);
   else
-    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false>), grid, dim3(64 * G), 0, st, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false, CPW>), grid, dim3(CPW * G), 0, st, p);
   return hipGetLastError();
 }
 
 template <Act A>
 hipError_t launch_bwd_a(const BwdArgs& p, int ds, int L, hipStream_t st) {
-#define MSCAN_CASE(DS_, L_) \
-  if (ds == DS_ && L == L_) return launch_bwd_t<A, DS_, (64 / L_), L_>(p, st);
+  // states per thread: L of them are held in registers, so SPL * L <= 64;
+  // at least two state groups so that a workgroup has whole waves
+#define MSCAN_CASE(DS_, L_)                                                    \
+  if (ds == DS_ && L == L_)                                                    \
+    return launch_bwd_t<A, DS_, ((64 / L_) < (DS_ / 2) ? (64 / L_) : (DS_ / 2)), L_>(p, st);
   MSCAN_CASE(4, 16) MSCAN_CASE(4, 32)
   MSCAN_CASE(8, 16) MSCAN_CASE(8, 32)
   MSCAN_CASE(16, 16) MSCAN_CASE(16, 32)

@@ -12,6 +12,12 @@ enum class Act : int { F32 = 0, BF16 = 1, F16 = 2 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Channels per workgroup.  A thread is (state group, channel): with 32
+// channels a wave holds 32 channels x 2 state groups, so a workgroup stays
+// small enough (LDS, waves) for two of them to share a CU.
+constexpr int kFwdCpw = 32;
+constexpr int kBwdCpw = 32;
+
 // ---------------------------------------------------------------- dtype I/O
 template <Act A>
 struct IO;
@@ -74,35 +80,57 @@ __device__ __forceinline__ float sigmoid(float x) {
   return rcp_fast(1.0f + exp2_fast(-x * kLog2e));
 }
 
+// ---------------------------------------------------------------- XCD mapping
+// Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
+// linear id.  Two neighbouring channel groups share every 128-byte line of a
+// 16-bit activation row, so the logical workgroups 2q and 2q+1 are given the
+// linear ids x + 16m and x + 16m + 8 of one XCD x (same L2).  Ids past the
+// last whole block of 16 keep their own index.  Returns the logical id.
+__device__ __forceinline__ int64_t xcd_pair_map(int64_t k, int64_t n) {
+  const int64_t full = n & ~static_cast<int64_t>(15);
+  if (k >= full) return k;
+  const int64_t x = k & 7, j = k >> 3;
+  return ((j >> 1) << 4) + 2 * x + (j & 1);
+}
+
 // ---------------------------------------------------------------- LDS staging
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
-constexpr int pad4(int n) { return (n + 3) & ~3; }
+constexpr int round_up(int n, int m) { return (n + m - 1) / m * m; }
+
+// Rows one async_rows instruction covers: lanes move 4-byte granules
+// (16-bit types: 2 channels) or 16-byte granules (f32: 4 channels).
+template <int ES, int CPW>
+constexpr int rows_per_inst() {
+  return 64 / (CPW / ((ES == 4 ? 16 : 4) / ES));
+}
 
 // Asynchronous copy (global_load_lds, no registers) of `nrows` time rows of
-// one 64-channel group of an activation tensor [B, T, Di] into LDS, one row
-// of 64 * ES bytes after another starting at `dst`.  Each lane moves one
-// granule of 4 bytes (16-bit types: 2 channels) or 16 bytes (f32: 4
-// channels); time rows are clamped to [0, T) and granules past Di re-read the
-// last granule of the row, so no load leaves the tensor (Di % 4 == 0).  The
-// caller ends the copy with a full s_waitcnt and a workgroup barrier.
-// nrows must be a multiple of 4; instructions are spread over the waves.
-template <int ES>
+// one CPW-channel group of an activation tensor [B, T, Di] into LDS, one row
+// of CPW * ES bytes after another starting at `dst`.  Time rows are clamped
+// to [0, T) and granules past Di re-read the last granule of the row, so no
+// load leaves the tensor (Di % 4 == 0).  nrows must be a multiple of
+// rows_per_inst; instructions are spread over the waves.  The caller ends
+// the copy with a full s_waitcnt and a workgroup barrier.
+template <int ES, int CPW>
 __device__ __forceinline__ void async_rows(lds_char_t* dst, const void* src, int64_t row0, int64_t t_lo,
                                            int64_t T, int64_t Di, int64_t i0, int nrows, int wave,
                                            int nwaves, int lane) {
   constexpr int GB = ES == 4 ? 16 : 4;   // bytes per lane
   constexpr int GC = GB / ES;            // channels per lane
-  constexpr int LPR = 64 / GC;           // lanes per row
+  constexpr int LPR = CPW / GC;          // lanes per row
   constexpr int RPI = 64 / LPR;          // rows per instruction
+  static_assert(LPR >= 1 && 64 % LPR == 0, "row width");
   const int ninst = nrows / RPI;
   int64_t ch = i0 + (lane % LPR) * GC;
   if (ch > Di - GC) ch = Di - GC;
+  const char* base = static_cast<const char*>(src) + (row0 * Di + ch) * ES;
+  const int64_t rstride = Di * ES;
   for (int j = wave; j < ninst; j += nwaves) {
     int64_t t = t_lo + j * RPI + lane / LPR;
     t = t < 0 ? 0 : (t >= T ? T - 1 : t);
-    const char* g = static_cast<const char*>(src) + ((row0 + t) * Di + ch) * ES;
+    const char* g = base + t * rstride;
     if constexpr (ES == 4)
       __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(dst + j * 64 * GB), 16, 0, 0);
     else
@@ -110,20 +138,20 @@ __device__ __forceinline__ void async_rows(lds_char_t* dst, const void* src, int
   }
 }
 
-// read element c of raw row r (64 * ES bytes per row) as f32
+// element idx of a raw LDS tile (row-major, CPW channels per row) as f32
 template <Act A>
-__device__ __forceinline__ float raw_ld(const char* base, int r, int c);
+__device__ __forceinline__ float raw_ld(const char* base, int idx);
 template <>
-__device__ __forceinline__ float raw_ld<Act::F32>(const char* base, int r, int c) {
-  return reinterpret_cast<const float*>(base)[r * 64 + c];
+__device__ __forceinline__ float raw_ld<Act::F32>(const char* base, int idx) {
+  return reinterpret_cast<const float*>(base)[idx];
 }
 template <>
-__device__ __forceinline__ float raw_ld<Act::BF16>(const char* base, int r, int c) {
-  return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(base)[r * 64 + c]) << 16);
+__device__ __forceinline__ float raw_ld<Act::BF16>(const char* base, int idx) {
+  return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(base)[idx]) << 16);
 }
 template <>
-__device__ __forceinline__ float raw_ld<Act::F16>(const char* base, int r, int c) {
-  return static_cast<float>(reinterpret_cast<const _Float16*>(base)[r * 64 + c]);
+__device__ __forceinline__ float raw_ld<Act::F16>(const char* base, int idx) {
+  return static_cast<float>(reinterpret_cast<const _Float16*>(base)[idx]);
 }
 
 // ---------------------------------------------------------------- arguments

@@ -7,17 +7,17 @@
 // with A = -exp(a_log) (mamba-rs 0.7.3 trainer.rs, recompute_a_neg_all),
 // and F4e out = y * silu(z).
 //
-// Mapping.  A workgroup owns 64 channels of one batch row and walks the
-// whole sequence.  Lane c of every wave is channel c; wave g holds states
-// [g*SPL, (g+1)*SPL) of all 64 channels in registers, so B_t / C_t reads are
-// wave-uniform LDS broadcasts.  Time advances in tiles of TT steps:
+// Mapping.  A workgroup owns CPW channels of one batch row and walks the
+// whole sequence.  Thread (gs, c) holds channel c's states
+// [gs*SPL, (gs+1)*SPL) in registers; a wave covers 64 / CPW state groups, so
+// B_t / C_t reads are LDS broadcasts.  Time advances in tiles of TT steps:
 //   stage   : the tile's raw activations (copied to LDS asynchronously while
 //             the previous tile ran) become, per (t, channel) item, delta and
 //             delta*u in LDS (one softplus per item, shared by all waves);
 //             then the copies for the next tile are issued.
-//   scan    : each wave runs the recurrence for its states and leaves its
+//   scan    : each thread runs the recurrence for its states and leaves its
 //             partial C.h per (t, channel) in LDS.
-//   output  : the staging threads add the partials of all waves, add D*u,
+//   output  : the staging threads add the partials of all groups, add D*u,
 //             apply the gate and write out (and y, u when asked).
 // The state entering every L-th step is written to ckpt for the backward.
 #pragma once
@@ -25,32 +25,39 @@
 
 namespace mscan {
 
-template <Act A, int DS, int SPL, int TT>
-__global__ void __launch_bounds__(64 * (DS / SPL))
+template <Act A, int DS, int SPL, int TT, int CPW>
+__global__ void __launch_bounds__(CPW * (DS / SPL))
 scan_fwd_kernel(const FwdArgs p) {
-  constexpr int G = DS / SPL;          // waves per workgroup
-  constexpr int NT = 64 * G;           // threads
+  constexpr int G = DS / SPL;          // state groups
+  constexpr int NT = CPW * G;          // threads: (state group, channel)
+  static_assert(NT % 64 == 0, "whole waves");
   static_assert(TT % G == 0, "tile must hold a whole number of items per thread");
   constexpr int IPT = TT / G;          // (t, channel) items per thread per tile
   constexpr int KMAX = 4;              // conv taps supported: 1..4
   constexpr int ES = A == Act::F32 ? 4 : 2;
-  constexpr int RB = 64 * ES;
-  constexpr int XR = pad4(TT + KMAX - 1);   // raw x rows: conv halo, then the tile
+  constexpr int RB = CPW * ES;         // bytes per raw row
+  constexpr int RPI = rows_per_inst<ES, CPW>();
+  constexpr int XR = round_up(TT + KMAX - 1, RPI);   // raw x rows: conv halo, then the tile
+  constexpr int TR = round_up(TT, RPI);
   constexpr int NBC = TT * 2 * DS;
   constexpr int BCPT = (NBC + NT - 1) / NT;
   using io = IO<A>;
 
   // raw tile: x (with halo) | delta_raw | z
-  __shared__ __attribute__((aligned(16))) char s_raw[(XR + 2 * TT) * RB];
-  __shared__ float2 s_st[TT][64];      // delta, delta*u
+  __shared__ __attribute__((aligned(16))) char s_raw[(XR + 2 * TR) * RB];
+  __shared__ float2 s_st[TT][CPW];     // delta, delta*u
   __shared__ float s_bc[TT][2][DS];    // B_t | C_t as f32
-  __shared__ float s_yp[G][TT][64];    // per-wave partial C.h
+  __shared__ float s_yp[G][TT][CPW];   // per-state-group partial C.h
 
   const int tid = threadIdx.x;
-  const int c = tid & 63;
-  const int g = tid >> 6;
-  const int64_t b = blockIdx.y;
-  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int c = tid % CPW;             // channel within the group
+  const int gs = tid / CPW;            // state group
+  const int wave = tid >> 6, lane = tid & 63;
+  constexpr int NW = (NT + 63) / 64;
+  const int64_t ngrp = (p.Di + CPW - 1) / CPW;
+  const int64_t wg = xcd_pair_map(blockIdx.x, ngrp * p.B);
+  const int64_t b = wg / ngrp;
+  const int64_t i0 = (wg % ngrp) * CPW;
   const int64_t i = i0 + c;
   const bool on = i < p.Di;
   const int64_t T = p.T, Di = p.Di, row0 = b * p.T;
@@ -59,12 +66,12 @@ scan_fwd_kernel(const FwdArgs p) {
   lds_char_t* raw_l = (lds_char_t*)s_raw;
   const char* raw_x = s_raw;
   const char* raw_dr = s_raw + XR * RB;
-  const char* raw_z = s_raw + (XR + TT) * RB;
+  const char* raw_z = s_raw + (XR + TR) * RB;
 
   float a2[SPL], h[SPL];
 #pragma unroll
   for (int s = 0; s < SPL; ++s) {
-    const int n = g * SPL + s;
+    const int n = gs * SPL + s;
     a2[s] = on ? -expf(p.a_log[i * DS + n]) * kLog2e : 0.0f;
     h[s] = (on && p.h0) ? p.h0[(b * Di + i) * DS + n] : 0.0f;
   }
@@ -78,9 +85,9 @@ scan_fwd_kernel(const FwdArgs p) {
   float bcn[BCPT];
   auto prefetch = [&](int64_t t0) {
     const int halo = K > 0 ? KMAX - 1 : 0;
-    async_rows<ES>(raw_l, p.x, row0, t0 - halo, T, Di, i0, XR, g, G, c);
-    async_rows<ES>(raw_l + XR * RB, p.delta_raw, row0, t0, T, Di, i0, TT, g, G, c);
-    if (gate) async_rows<ES>(raw_l + (XR + TT) * RB, p.z, row0, t0, T, Di, i0, TT, g, G, c);
+    async_rows<ES, CPW>(raw_l, p.x, row0, t0 - halo, T, Di, i0, XR, wave, NW, lane);
+    async_rows<ES, CPW>(raw_l + XR * RB, p.delta_raw, row0, t0, T, Di, i0, TR, wave, NW, lane);
+    if (gate) async_rows<ES, CPW>(raw_l + (XR + TR) * RB, p.z, row0, t0, T, Di, i0, TR, wave, NW, lane);
 #pragma unroll
     for (int q = 0; q < BCPT; ++q) {
       const int j = tid + q * NT;
@@ -101,7 +108,7 @@ scan_fwd_kernel(const FwdArgs p) {
     }
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
-      const int tt = g + G * k;
+      const int tt = gs + G * k;
       float dl = 0.0f, u = 0.0f, sz = 1.0f;
       if (tt < len && on) {
         if (K > 0) {
@@ -111,18 +118,18 @@ scan_fwd_kernel(const FwdArgs p) {
             if (k2 < K) {
               const int64_t s = t0 + tt - (K - 1) + k2;
               float xv;
-              if (s >= 0) xv = raw_ld<A>(raw_x, tt + (KMAX - 1) - (K - 1) + k2, c);
+              if (s >= 0) xv = raw_ld<A>(raw_x, (tt + (KMAX - 1) - (K - 1) + k2) * CPW + c);
               else xv = p.conv_state0 ? p.conv_state0[(b * Di + i) * K + (K + s)] : 0.0f;
               pre = fmaf(cw[k2], xv, pre);
             }
           }
           u = pre * sigmoid(pre);
         } else {
-          u = raw_ld<A>(raw_x, tt, c);
+          u = raw_ld<A>(raw_x, tt * CPW + c);
         }
-        dl = softplus(raw_ld<A>(raw_dr, tt, c));
+        dl = softplus(raw_ld<A>(raw_dr, tt * CPW + c));
         if (gate) {
-          const float zv = raw_ld<A>(raw_z, tt, c);
+          const float zv = raw_ld<A>(raw_z, tt * CPW + c);
           sz = zv * sigmoid(zv);
         }
       }
@@ -131,12 +138,12 @@ scan_fwd_kernel(const FwdArgs p) {
       e_sz[k] = sz;
     }
   };
-  // combine the per-wave partials of one tile, gate, store
+  // combine the per-group partials of one tile, gate, store
   auto output = [&](int64_t t0) {
     const int len = static_cast<int>(T - t0 < TT ? T - t0 : TT);
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
-      const int tt = g + G * k;
+      const int tt = gs + G * k;
       if (tt < len && on) {
         float y = Dv * e_u[k];
 #pragma unroll
@@ -163,7 +170,7 @@ scan_fwd_kernel(const FwdArgs p) {
       const int64_t cidx = t0 / p.L;
 #pragma unroll
       for (int s = 0; s < SPL; ++s)
-        p.ckpt[((b * p.nC + cidx) * DS + g * SPL + s) * Di + i] = h[s];
+        p.ckpt[((b * p.nC + cidx) * DS + gs * SPL + s) * Di + i] = h[s];
     }
 
     // ---- scan (steps past the end of the sequence see delta = 0, B = C = 0:
@@ -174,27 +181,26 @@ scan_fwd_kernel(const FwdArgs p) {
       float yp = 0.0f;
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
-        const int n = g * SPL + s;
+        const int n = gs * SPL + s;
         const float dA = exp2_fast(st.x * a2[s]);
         h[s] = fmaf(dA, h[s], st.y * s_bc[tt][0][n]);
         yp = fmaf(s_bc[tt][1][n], h[s], yp);
       }
-      s_yp[g][tt][c] = yp;
+      s_yp[gs][tt][c] = yp;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     output(t0);
-    const bool more = t0 + TT < T;
-    if (more) stage(t0 + TT);
+    if (t0 + TT < T) stage(t0 + TT);
     __syncthreads();
     if (t0 + 2 * TT < T) prefetch(t0 + 2 * TT);
   }
 
   if (p.h_last && on) {
 #pragma unroll
-    for (int s = 0; s < SPL; ++s) p.h_last[(b * Di + i) * DS + g * SPL + s] = h[s];
+    for (int s = 0; s < SPL; ++s) p.h_last[(b * Di + i) * DS + gs * SPL + s] = h[s];
   }
-  if (p.conv_state_last && on && g == 0) {
+  if (p.conv_state_last && on && gs == 0) {
     for (int k = 0; k < K; ++k) {
       const int64_t s = T - K + k;
       float xv;
@@ -206,20 +212,23 @@ scan_fwd_kernel(const FwdArgs p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <Act A, int DS, int SPL, int TT>
+template <Act A, int DS, int SPL, int TT, int CPW>
 static hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t st) {
   constexpr int G = DS / SPL;
-  dim3 grid(static_cast<unsigned>((p.Di + 63) / 64), static_cast<unsigned>(p.B));
-  hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT>), grid, dim3(64 * G), 0, st, p);
+  const int64_t ng = (p.Di + CPW - 1) / CPW;
+  dim3 grid(static_cast<unsigned>(ng * p.B));
+  hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW>), grid, dim3(CPW * G), 0, st, p);
   return hipGetLastError();
 }
 
 template <Act A>
 hipError_t launch_fwd_a(const FwdArgs& p, int ds, int spl, hipStream_t st) {
-  // tiles of 32 steps (16 when the checkpoint interval is 16)
-#define MSCAN_CASE(DS_, SPL_)                                                         \
-  if (ds == DS_ && spl == SPL_)                                                       \
-    return p.L % 32 == 0 ? launch_fwd_t<A, DS_, SPL_, 32>(p, st) : launch_fwd_t<A, DS_, SPL_, 16>(p, st);
+  // channel groups of kFwdCpw; tiles of 32 steps (16 when the checkpoint
+  // interval is 16)
+#define MSCAN_CASE(DS_, SPL_)                                                            \
+  if (ds == DS_ && spl == SPL_)                                                          \
+    return p.L % 32 == 0 ? launch_fwd_t<A, DS_, SPL_, 32, kFwdCpw>(p, st)                \
+                         : launch_fwd_t<A, DS_, SPL_, 16, kFwdCpw>(p, st);
   MSCAN_CASE(4, 1) MSCAN_CASE(8, 2) MSCAN_CASE(16, 2) MSCAN_CASE(32, 4)
 #undef MSCAN_CASE
   return hipErrorInvalidValue;
