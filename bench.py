@@ -36,6 +36,30 @@ FLOPS_FWD_ELEM = 7
 FLOPS_BWD_ELEM = 21
 
 
+def kernel_source_hash():
+    """sha256 over the HIP sources (file names and contents, sorted)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "state_space_sequence_selective_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per backward launch from the committed rocprofv3 counter runs
+    (profiles/traffic.json), or None when the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload)
+    if not rec or rec.get("kernel_src_sha256") != kernel_source_hash():
+        return None
+    return rec["bwd_entry_bytes"]
+
+
 def act_bytes(act):
     return 4 if act == "f32" else 2
 
@@ -192,7 +216,7 @@ def main():
     # dominant kernel: the backward entry (scan_bwd_kernel + its fixed-order reduce)
     bwd_tflops = elems * FLOPS_BWD_ELEM / (bwd_ms / 1e3) / 1e12
     roofline = {"bound": "alu", "achieved": round(bwd_tflops, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(bwd_tflops / VALU_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(bwd_tflops / VALU_PEAK_TFLOPS, 4), "traffic": measured_traffic(w.name),
                 "kernel": "mamba_scan_bwd (scan_bwd_kernel + mscan_reduce_kernel), layer 0",
                 "launch_ms": round(bwd_ms, 4),
                 "algorithmic_flops_per_launch": elems * FLOPS_BWD_ELEM,
