@@ -97,7 +97,7 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   pl->nC = (d->seqlen + L - 1) / L;
   pl->nG = (d->d_inner + mscan::kBwdCpw - 1) / mscan::kBwdCpw;
   pl->K = K;
-  pl->spl_fwd = d->d_state == 4 ? 1 : (d->d_state == 32 ? 4 : 2);
+  pl->spl_fwd = d->d_state == 32 ? 2 : 1;   // one state per thread: most waves per SIMD
   pl->act = static_cast<mscan::Act>(d->act);
   pl->esize = d->act == MAMBA_F32 ? 4 : 2;
   pl->bulk_align = d->act == MAMBA_F32 ? 16 : 4;

@@ -42,13 +42,6 @@
 
 namespace mscan {
 
-// wave-local ordering point for LDS traffic between lanes of one wave
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 // Sum a group-private block red[c][o] (CPW channels x NO outputs, row
 // stride NO + 1) over c; the group is the CPW consecutive lanes of one wave
 // with channel index c.  Returns the total for output o = c % NO on the
@@ -65,6 +58,18 @@ __device__ __forceinline__ float group_channel_sum(const float* red, int c) {
 #pragma unroll
   for (int off = NO; off < CPW; off <<= 1) acc += __shfl_xor(acc, off, 64);
   return acc;
+}
+
+// Bytes of the raw tile: x (with the conv halo) | delta_raw | dout | z | y.
+// It lives in dynamic LDS: the compiler then sees it as an object of its own
+// and does not hold LDS accesses to the other arrays until the tile's
+// asynchronous copies land (with all arrays static it did, at the first
+// channel-sum read after the copies were issued).
+template <Act A, int L, bool FUSED, int CPW>
+constexpr int bwd_raw_bytes() {
+  constexpr int ES = A == Act::F32 ? 4 : 2;
+  constexpr int RPI = rows_per_inst<ES, CPW>();
+  return (round_up(L + (FUSED ? 3 : 0), RPI) + 4 * round_up(L, RPI)) * CPW * ES;
 }
 
 template <Act A, int DS, int SPL, int L, bool FUSED, int CPW>
@@ -84,7 +89,8 @@ scan_bwd_kernel(const BwdArgs p) {
   constexpr int XR = round_up(L + KMAX - 1, RPI);   // raw x rows: conv halo, then the tile
   constexpr int TR = round_up(L, RPI);
   constexpr int NBC = L * 2 * DS;      // B/C values per tile
-  constexpr int BCPT = (NBC + NT - 1) / NT;
+  static_assert(NBC % NT == 0, "B/C values of a tile spread evenly over the threads");
+  constexpr int BCPT = NBC / NT;
   // The cross-state partials are double-buffered when LDS allows it: the
   // next sub-tile's producers then need not wait for this sub-tile's
   // epilogue (one barrier per sub-tile instead of two).
@@ -95,7 +101,8 @@ scan_bwd_kernel(const BwdArgs p) {
   using io = IO<A>;
 
   // raw tile: x (with halo) | delta_raw | dout | z | y
-  __shared__ __attribute__((aligned(16))) char s_raw[(XR + 4 * TR) * RB];
+  static_assert(bwd_raw_bytes<A, L, FUSED, CPW>() == (XR + 4 * TR) * RB, "raw tile size");
+  extern __shared__ __attribute__((aligned(16))) char s_raw[];
   __shared__ float4 s_st[L][CPW];      // delta, delta*u, dy, u
   __shared__ float s_x[FUSED ? L + KMAX - 1 : 1][CPW];
   __shared__ float s_bc[L][2][DS];
@@ -150,8 +157,10 @@ scan_bwd_kernel(const BwdArgs p) {
     for (int j = tid; j < (SUB + KMAX) * CPW; j += NT) (&s_dp[0][0])[j] = 0.0f;
 
   // ---- prefetch of one tile: raw activations to LDS (async), B/C rows and
-  // the checkpoint to registers
-  float bcn[BCPT], hn[SPL];
+  // the checkpoint to registers (B/C as raw bits, converted in the stage, so
+  // nothing waits for these loads before the tile's own copies are waited for)
+  uint32_t bcn[BCPT];
+  float hn[SPL];
   auto prefetch = [&](int64_t kt) {
     const int64_t t0 = kt * L;
     async_rows<ES, CPW>(raw_l, p.x, row0, t0 - (KMAX - 1), T, Di, i0, XR, wave, NW, lane);
@@ -165,8 +174,8 @@ scan_bwd_kernel(const BwdArgs p) {
     for (int q = 0; q < BCPT; ++q) {
       const int j = tid + q * NT;
       const int tt = j / (2 * DS), m = j % (2 * DS);
-      const bool ok = j < NBC && t0 + tt < T;
-      bcn[q] = ok ? io::ld(p.xdbl, (row0 + t0 + tt) * p.X + p.R + m) : 0.0f;
+      const int64_t t = t0 + tt < T ? t0 + tt : T - 1;   // rows past the end: zeroed in the stage
+      bcn[q] = io::ldraw(p.xdbl, (row0 + t) * p.X + p.R + m);
     }
 #pragma unroll
     for (int s = 0; s < SPL; ++s)
@@ -179,7 +188,8 @@ scan_bwd_kernel(const BwdArgs p) {
   for (int64_t kt = ntiles - 1; kt >= 0; --kt) {
     const int64_t t0 = kt * L;
     const int len = static_cast<int>(T - t0 < L ? T - t0 : L);
-    float e_sig[NSUB], e_dsp[NSUB], e_due[NSUB];
+    float e_sig[NSUB], e_dsp[NSUB];
+    uint32_t e_due[NSUB];
     float h[SPL];
 
     // ---------------------------------------------------------------- stage
@@ -190,7 +200,7 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int q = 0; q < BCPT; ++q) {
       const int j = tid + q * NT;
-      if (j < NBC) (&s_bc[0][0][0])[j] = bcn[q];
+      (&s_bc[0][0][0])[j] = j / (2 * DS) < len ? io::cvt(bcn[q]) : 0.0f;
     }
     if (FUSED) {
       for (int j = tid; j < (L + KMAX - 1) * CPW; j += NT) {
@@ -208,7 +218,8 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int k = 0; k < NSUB; ++k) {
       const int tt = g + G * k;
-      float dl = 0.0f, u = 0.0f, sig = 0.0f, dy = 0.0f, dsp = 0.0f, due = 0.0f;
+      float dl = 0.0f, u = 0.0f, sig = 0.0f, dy = 0.0f, dsp = 0.0f;
+      uint32_t due = 0;   // raw bits of d_u_extra (0 is +0.0 in every dtype)
       if (tt < len && on) {
         const int64_t e = (row0 + t0 + tt) * Di + i;
         const float dr = raw_ld<A>(raw_dr, tt * CPW + c);
@@ -222,7 +233,7 @@ scan_bwd_kernel(const BwdArgs p) {
           const float sp = sigmoid(pre);
           u = pre * sp;
           dsp = sp * (1.0f + pre * (1.0f - sp));
-          if (p.d_u_extra) due = io::ld(p.d_u_extra, e);   // consumed in the epilogue
+          if (p.d_u_extra) due = io::ldraw(p.d_u_extra, e);   // converted in the epilogue
         } else {
           u = raw_ld<A>(raw_x, tt * CPW + c);
         }
@@ -364,7 +375,7 @@ scan_bwd_kernel(const BwdArgs p) {
             p.part_bc[(cg * BT + row0 + t0 + tt) * (2 * DS) + g * SPL + c % SPL] = v;
         }
       }
-      __syncthreads();
+      lds_barrier();
 
       // ---- epilogue: item (t0 + sb*SUB + g, channel c); stage slot k = sb
       const int tt = sb * SUB + g;
@@ -384,7 +395,7 @@ scan_bwd_kernel(const BwdArgs p) {
         io::st(p.d_delta_raw, e, ddl * e_sig[sb]);
         acc_dD = fmaf(st.z, st.w, acc_dD);
         if (FUSED) {
-          du += e_due[sb];
+          du += io::cvt(e_due[sb]);
           dp = du * e_dsp[sb];
           acc_cb += dp;
 #pragma unroll
@@ -398,7 +409,7 @@ scan_bwd_kernel(const BwdArgs p) {
         // d_x[s] = sum_k w_k dp[s + K-1-k]; rows >= SUB of s_dp hold the
         // dp of the K-1 steps after this sub-tile (zero past the end)
         s_dp[g][c] = dp;
-        __syncthreads();
+        lds_barrier();
         if (live) {
           float gx = 0.0f;
 #pragma unroll
@@ -406,14 +417,14 @@ scan_bwd_kernel(const BwdArgs p) {
             if (k2 < K) gx = fmaf(cw[k2], s_dp[g + K - 1 - k2][c], gx);
           io::st(p.d_x, e, gx);
         }
-        __syncthreads();
+        lds_barrier();
         // the K-1 steps after the next sub-tile: this sub-tile's first steps,
         // then (when SUB < K-1) older entries; descending keeps reads ahead
         // of writes
         if (g == 0)
           for (int j = K - 2; j >= 0; --j) s_dp[SUB + j][c] = s_dp[j][c];
       }
-      if (NBUF == 1) __syncthreads();
+      if (NBUF == 1) lds_barrier();
     }
   }
   __syncthreads();
@@ -450,10 +461,12 @@ static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
   constexpr int CPW = kBwdCpw;
   const int64_t ng = (p.Di + CPW - 1) / CPW;
   dim3 grid(static_cast<unsigned>(ng * p.B));
+  constexpr unsigned raw_fused = bwd_raw_bytes<A, L, true, CPW>();
+  constexpr unsigned raw_plain = bwd_raw_bytes<A, L, false, CPW>();
   if (p.K > 0)
-    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true, CPW>), grid, dim3(CPW * G), 0, st, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true, CPW>), grid, dim3(CPW * G), raw_fused, st, p);
   else
-    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false, CPW>), grid, dim3(CPW * G), 0, st, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false, CPW>), grid, dim3(CPW * G), raw_plain, st, p);
   return hipGetLastError();
 }
 

@@ -22,11 +22,18 @@ constexpr int kBwdCpw = 32;
 template <Act A>
 struct IO;
 
+// ld: load and convert to f32.  ldraw / cvt: the same split in two, so a
+// value can be fetched early and converted where it is used; converting at
+// once would make the compiler wait for the load right there.
 template <>
 struct IO<Act::F32> {
   static __device__ __forceinline__ float ld(const void* p, int64_t i) {
     return static_cast<const float*>(p)[i];
   }
+  static __device__ __forceinline__ uint32_t ldraw(const void* p, int64_t i) {
+    return static_cast<const uint32_t*>(p)[i];
+  }
+  static __device__ __forceinline__ float cvt(uint32_t b) { return __uint_as_float(b); }
   static __device__ __forceinline__ void st(void* p, int64_t i, float v) {
     static_cast<float*>(p)[i] = v;
   }
@@ -38,6 +45,10 @@ struct IO<Act::BF16> {
     const uint32_t b = static_cast<const uint16_t*>(p)[i];
     return __uint_as_float(b << 16);
   }
+  static __device__ __forceinline__ uint32_t ldraw(const void* p, int64_t i) {
+    return static_cast<const uint16_t*>(p)[i];
+  }
+  static __device__ __forceinline__ float cvt(uint32_t b) { return __uint_as_float(b << 16); }
   // hardware conversion (v_cvt_pk_bf16_f32), round to nearest even
   static __device__ __forceinline__ void st(void* p, int64_t i, float v) {
     static_cast<__bf16*>(p)[i] = static_cast<__bf16>(v);
@@ -48,6 +59,12 @@ template <>
 struct IO<Act::F16> {
   static __device__ __forceinline__ float ld(const void* p, int64_t i) {
     return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+  }
+  static __device__ __forceinline__ uint32_t ldraw(const void* p, int64_t i) {
+    return static_cast<const uint16_t*>(p)[i];
+  }
+  static __device__ __forceinline__ float cvt(uint32_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
   }
   // the hardware conversion rounds to nearest even (default mode)
   static __device__ __forceinline__ void st(void* p, int64_t i, float v) {
@@ -91,6 +108,33 @@ __device__ __forceinline__ int64_t xcd_pair_map(int64_t k, int64_t n) {
   if (k >= full) return k;
   const int64_t x = k & 7, j = k >> 3;
   return ((j >> 1) << 4) + 2 * x + (j & 1);
+}
+
+// ---------------------------------------------------------------- barriers
+// __syncthreads() is a workgroup-scope release/acquire around s_barrier; the
+// release also waits for every global_load_lds copy in flight (they write
+// LDS), which would turn a copy meant to overlap the next tile's work into a
+// synchronous one.  The two helpers below order LDS traffic only: the fences
+// are wavefront-scope (no hardware wait, but the compiler keeps memory
+// accesses on their side), the hardware wait is lgkmcnt(0), i.e. this wave's
+// LDS reads and writes are done.  Code that reads data brought in by
+// global_load_lds waits for it explicitly (s_waitcnt 0) before a barrier.
+constexpr int kWaitLgkmOnly = 0xC07F;   // s_waitcnt vmcnt(63) expcnt(7) lgkmcnt(0)
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkmOnly);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Ordering point for LDS traffic between the lanes of one wave.  A wave's
+// LDS instructions execute in issue order, so keeping the compiler from
+// moving accesses across this point is enough.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ---------------------------------------------------------------- LDS staging

@@ -16,7 +16,9 @@
 //             delta*u in LDS (one softplus per item, shared by all waves);
 //             then the copies for the next tile are issued.
 //   scan    : each thread runs the recurrence for its states and leaves its
-//             partial C.h per (t, channel) in LDS.
+//             partial C.h per (t, channel) in LDS; a step's LDS operands are
+//             read PD steps before the step (one LDS latency per tile, not
+//             one per step).
 //   output  : the staging threads add the partials of all groups, add D*u,
 //             apply the gate and write out (and y, u when asked).
 // The state entering every L-th step is written to ckpt for the backward.
@@ -25,7 +27,7 @@
 
 namespace mscan {
 
-template <Act A, int DS, int SPL, int TT, int CPW>
+template <Act A, int DS, int SPL, int TT, int CPW, bool FUSED>
 __global__ void __launch_bounds__(CPW * (DS / SPL))
 scan_fwd_kernel(const FwdArgs p) {
   constexpr int G = DS / SPL;          // state groups
@@ -33,18 +35,23 @@ scan_fwd_kernel(const FwdArgs p) {
   static_assert(NT % 64 == 0, "whole waves");
   static_assert(TT % G == 0, "tile must hold a whole number of items per thread");
   constexpr int IPT = TT / G;          // (t, channel) items per thread per tile
-  constexpr int KMAX = 4;              // conv taps supported: 1..4
+  constexpr int KMAX = FUSED ? 4 : 1;  // conv taps supported: 1..4 (fused)
   constexpr int ES = A == Act::F32 ? 4 : 2;
   constexpr int RB = CPW * ES;         // bytes per raw row
   constexpr int RPI = rows_per_inst<ES, CPW>();
   constexpr int XR = round_up(TT + KMAX - 1, RPI);   // raw x rows: conv halo, then the tile
   constexpr int TR = round_up(TT, RPI);
   constexpr int NBC = TT * 2 * DS;
-  constexpr int BCPT = (NBC + NT - 1) / NT;
+  static_assert(NBC % NT == 0, "B/C values of a tile spread evenly over the threads");
+  constexpr int BCPT = NBC / NT;
+  constexpr int PD = 4;                // scan operand look-ahead, steps
+  static_assert(TT % PD == 0, "look-ahead ring");
   using io = IO<A>;
 
-  // raw tile: x (with halo) | delta_raw | z
-  __shared__ __attribute__((aligned(16))) char s_raw[(XR + 2 * TR) * RB];
+  // raw tiles, double-buffered (even / odd tiles): x (with halo) | delta_raw | z
+  constexpr int RAW = (XR + 2 * TR) * RB;
+  __shared__ __attribute__((aligned(16))) char s_raw0[RAW];
+  __shared__ __attribute__((aligned(16))) char s_raw1[RAW];
   __shared__ float2 s_st[TT][CPW];     // delta, delta*u
   __shared__ float s_bc[TT][2][DS];    // B_t | C_t as f32
   __shared__ float s_yp[G][TT][CPW];   // per-state-group partial C.h
@@ -62,11 +69,7 @@ scan_fwd_kernel(const FwdArgs p) {
   const bool on = i < p.Di;
   const int64_t T = p.T, Di = p.Di, row0 = b * p.T;
   const bool gate = p.z != nullptr;
-  const int K = p.K;
-  lds_char_t* raw_l = (lds_char_t*)s_raw;
-  const char* raw_x = s_raw;
-  const char* raw_dr = s_raw + XR * RB;
-  const char* raw_z = s_raw + (XR + TR) * RB;
+  const int K = FUSED ? p.K : 0;
 
   float a2[SPL], h[SPL];
 #pragma unroll
@@ -79,39 +82,50 @@ scan_fwd_kernel(const FwdArgs p) {
   float cw[KMAX];
   float cb = 0.0f;
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k) cw[k] = (K > 0 && on && k < K) ? p.conv_w[i * K + k] : 0.0f;
-  if (K > 0) cb = (on && p.conv_b) ? p.conv_b[i] : 0.0f;
+  for (int k = 0; k < KMAX; ++k) cw[k] = (FUSED && on && k < K) ? p.conv_w[i * K + k] : 0.0f;
+  if (FUSED) cb = (on && p.conv_b) ? p.conv_b[i] : 0.0f;
 
-  float bcn[BCPT];
-  auto prefetch = [&](int64_t t0) {
-    const int halo = K > 0 ? KMAX - 1 : 0;
-    async_rows<ES, CPW>(raw_l, p.x, row0, t0 - halo, T, Di, i0, XR, wave, NW, lane);
-    async_rows<ES, CPW>(raw_l + XR * RB, p.delta_raw, row0, t0, T, Di, i0, TR, wave, NW, lane);
-    if (gate) async_rows<ES, CPW>(raw_l + (XR + TR) * RB, p.z, row0, t0, T, Di, i0, TR, wave, NW, lane);
+  // copies of tile number kt (time t0 = kt * TT) into raw buffer `raw` and
+  // its B/C values into bc, as raw bits: they are converted in the stage, so
+  // nothing waits for these loads early.  Even tiles use (bc0, s_raw0), odd
+  // tiles (bc1, s_raw1); the tile loop below is unrolled by two so that the
+  // choice is static (a run-time choice would make the compiler merge the two
+  // register sets, and a merge waits for the loads).
+  uint32_t bc0[BCPT], bc1[BCPT];
+  auto prefetch = [&](int64_t kt, uint32_t (&bc)[BCPT], char* raw) {
+    const int64_t t0 = kt * TT;
+    lds_char_t* r = (lds_char_t*)raw;
+    async_rows<ES, CPW>(r, p.x, row0, t0 - (KMAX - 1), T, Di, i0, XR, wave, NW, lane);
+    async_rows<ES, CPW>(r + XR * RB, p.delta_raw, row0, t0, T, Di, i0, TR, wave, NW, lane);
+    if (gate) async_rows<ES, CPW>(r + (XR + TR) * RB, p.z, row0, t0, T, Di, i0, TR, wave, NW, lane);
 #pragma unroll
     for (int q = 0; q < BCPT; ++q) {
       const int j = tid + q * NT;
       const int tt = j / (2 * DS), m = j % (2 * DS);
-      const bool ok = j < NBC && t0 + tt < T;
-      bcn[q] = ok ? io::ld(p.xdbl, (row0 + t0 + tt) * p.X + p.R + m) : 0.0f;
+      const int64_t t = t0 + tt < T ? t0 + tt : T - 1;   // rows past the end: zeroed in the stage
+      bc[q] = io::ldraw(p.xdbl, (row0 + t) * p.X + p.R + m);
     }
   };
 
   float e_u[IPT], e_sz[IPT];
   // per-item work of one tile: delta, delta*u to LDS; u and silu(z) kept
-  auto stage = [&](int64_t t0) {
+  auto stage = [&](int64_t kt, const uint32_t (&bc)[BCPT], const char* raw) {
+    const int64_t t0 = kt * TT;
     const int len = static_cast<int>(T - t0 < TT ? T - t0 : TT);
+    const char* raw_x = raw;
+    const char* raw_dr = raw_x + XR * RB;
+    const char* raw_z = raw_x + (XR + TR) * RB;
 #pragma unroll
     for (int q = 0; q < BCPT; ++q) {
       const int j = tid + q * NT;
-      if (j < NBC) (&s_bc[0][0][0])[j] = bcn[q];
+      (&s_bc[0][0][0])[j] = j / (2 * DS) < len ? io::cvt(bc[q]) : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       const int tt = gs + G * k;
       float dl = 0.0f, u = 0.0f, sz = 1.0f;
       if (tt < len && on) {
-        if (K > 0) {
+        if (FUSED) {
           float pre = cb;
 #pragma unroll
           for (int k2 = 0; k2 < KMAX; ++k2) {
@@ -156,15 +170,16 @@ scan_fwd_kernel(const FwdArgs p) {
     }
   };
 
-  // Two barriers per tile: (scan k) | wait + barrier | output k, stage k+1 |
-  // barrier | issue copies for k+2, (scan k+1) ...
-  prefetch(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  stage(0);
-  __syncthreads();
-  if (TT < T) prefetch(TT);
-  for (int64_t t0 = 0; t0 < T; t0 += TT) {
+  // Two barriers per tile.  Copies run two tiles ahead:
+  //   (scan k) | wait + barrier | issue copies for k+2 | output k, stage k+1 |
+  //   LDS barrier | (scan k+1) ...
+  // tile(kt, bcS, rawS, bcP, rawP): scan and output of tile kt, stage of tile
+  // kt + 1 from (bcS, rawS), copies for tile kt + 2 into (bcP, rawP), the
+  // buffers of tile kt, free once stage kt is done.
+  const int64_t ntiles = (T + TT - 1) / TT;
+  auto tile = [&](int64_t kt, const uint32_t (&bcS)[BCPT], const char* rawS, uint32_t (&bcP)[BCPT],
+                  char* rawP) {
+    const int64_t t0 = kt * TT;
     // ---- checkpoint: the state entering step t0 (TT divides L)
     if (p.ckpt && on && (t0 % p.L) == 0) {
       const int64_t cidx = t0 / p.L;
@@ -174,26 +189,61 @@ scan_fwd_kernel(const FwdArgs p) {
     }
 
     // ---- scan (steps past the end of the sequence see delta = 0, B = C = 0:
-    // identities that leave h unchanged)
+    // identities that leave h unchanged).  Operands of step tt sit in ring
+    // slot tt % PD, read PD steps earlier; the scheduling barrier per step
+    // keeps the compiler from pulling the reads closer to their use.
+    float2 q_st[PD];
+    float q_b[PD][SPL], q_c[PD][SPL];
+    auto operands = [&](int tt, int sl) {
+      q_st[sl] = s_st[tt][c];
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) {
+        q_b[sl][s] = s_bc[tt][0][gs * SPL + s];
+        q_c[sl][s] = s_bc[tt][1][gs * SPL + s];
+      }
+    };
+#pragma unroll
+    for (int d = 0; d < PD; ++d) operands(d, d);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      const float2 st = s_st[tt][c];
+      const int sl = tt % PD;
+      const float2 st = q_st[sl];
+      float bb[SPL], cc[SPL];
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) {
+        bb[s] = q_b[sl][s];
+        cc[s] = q_c[sl][s];
+      }
+      if (tt + PD < TT) operands(tt + PD, sl);
       float yp = 0.0f;
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
-        const int n = gs * SPL + s;
         const float dA = exp2_fast(st.x * a2[s]);
-        h[s] = fmaf(dA, h[s], st.y * s_bc[tt][0][n]);
-        yp = fmaf(s_bc[tt][1][n], h[s], yp);
+        h[s] = fmaf(dA, h[s], st.y * bb[s]);
+        yp = fmaf(cc[s], h[s], yp);
       }
       s_yp[gs][tt][c] = yp;
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the copies of tile kt + 1 are complete and visible to all waves
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (kt + 2 < ntiles) prefetch(kt + 2, bcP, rawP);
     output(t0);
-    if (t0 + TT < T) stage(t0 + TT);
-    __syncthreads();
-    if (t0 + 2 * TT < T) prefetch(t0 + 2 * TT);
+    if (kt + 1 < ntiles) stage(kt + 1, bcS, rawS);
+    // LDS-only: the copies for tile kt + 2 stay in flight through scan kt + 1
+    lds_barrier();
+  };
+
+  prefetch(0, bc0, s_raw0);
+  if (ntiles > 1) prefetch(1, bc1, s_raw1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  stage(0, bc0, s_raw0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < ntiles; kt += 2) {
+    tile(kt, bc1, s_raw1, bc0, s_raw0);
+    if (kt + 1 < ntiles) tile(kt + 1, bc0, s_raw0, bc1, s_raw1);
   }
 
   if (p.h_last && on) {
@@ -217,19 +267,19 @@ static hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t st) {
   constexpr int G = DS / SPL;
   const int64_t ng = (p.Di + CPW - 1) / CPW;
   dim3 grid(static_cast<unsigned>(ng * p.B));
-  hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW>), grid, dim3(CPW * G), 0, st, p);
+  if (p.K > 0)
+    hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW, true>), grid, dim3(CPW * G), 0, st, p);
+  else
+    hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW, false>), grid, dim3(CPW * G), 0, st, p);
   return hipGetLastError();
 }
 
 template <Act A>
 hipError_t launch_fwd_a(const FwdArgs& p, int ds, int spl, hipStream_t st) {
-  // channel groups of kFwdCpw; tiles of 32 steps (16 when the checkpoint
-  // interval is 16)
-#define MSCAN_CASE(DS_, SPL_)                                                            \
-  if (ds == DS_ && spl == SPL_)                                                          \
-    return p.L % 32 == 0 ? launch_fwd_t<A, DS_, SPL_, 32, kFwdCpw>(p, st)                \
-                         : launch_fwd_t<A, DS_, SPL_, 16, kFwdCpw>(p, st);
-  MSCAN_CASE(4, 1) MSCAN_CASE(8, 2) MSCAN_CASE(16, 2) MSCAN_CASE(32, 4)
+  // channel groups of kFwdCpw; tiles of 16 steps
+#define MSCAN_CASE(DS_, SPL_) \
+  if (ds == DS_ && spl == SPL_) return launch_fwd_t<A, DS_, SPL_, 16, kFwdCpw>(p, st);
+  MSCAN_CASE(4, 1) MSCAN_CASE(8, 1) MSCAN_CASE(16, 1) MSCAN_CASE(32, 2)
 #undef MSCAN_CASE
   return hipErrorInvalidValue;
 }
