@@ -87,7 +87,7 @@ typedef struct mamba_dims {
   int64_t d_state;  /* Ds in {4, 8, 16, 32} */
   int64_t dt_rank;  /* R >= 0: xdbl row = [dt (R) | B (Ds) | C (Ds)] */
   int32_t d_conv;   /* K in 1..4 for the fused entry points; ignored by mamba_scan_* */
-  int32_t chunk;    /* checkpoint interval L in {16, 32}; 0 = 32.  The
+  int32_t chunk;    /* checkpoint interval L in {16, 32}; 0 = 16.  The
                        backward holds L steps of state in registers, so
                        Ds 32 needs L = 16 */
   int32_t act;      /* mamba_dtype_t of every activation tensor (and xdbl) */

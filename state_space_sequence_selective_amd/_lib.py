@@ -44,7 +44,7 @@ class Dims(ctypes.Structure):
 
     @property
     def L(self) -> int:
-        return self.chunk if self.chunk else 32
+        return self.chunk if self.chunk else 16
 
     @property
     def xdbl_dim(self) -> int:

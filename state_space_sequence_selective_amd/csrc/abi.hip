@@ -73,8 +73,8 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
     return fail(MAMBA_ERR_UNSUPPORTED, fn, "d_state must be 4, 8, 16 or 32");
   if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32)
     return fail(d->chunk < 0 ? MAMBA_ERR_INVALID : MAMBA_ERR_UNSUPPORTED, fn,
-                "chunk must be 0 (default 32), 16 or 32");
-  const int L = d->chunk ? d->chunk : 32;
+                "chunk must be 0 (default 16), 16 or 32");
+  const int L = d->chunk ? d->chunk : 16;
   // the backward keeps L steps of state in registers
   if (d->d_state == 32 && L != 16)
     return fail(MAMBA_ERR_UNSUPPORTED, fn, "chunk must be 16 for d_state 32");

@@ -44,20 +44,45 @@ namespace mscan {
 
 // Sum a group-private block red[c][o] (CPW channels x NO outputs, row
 // stride NO + 1) over c; the group is the CPW consecutive lanes of one wave
-// with channel index c.  Returns the total for output o = c % NO on the
-// lanes with c / NO == 0.
+// with channel index c.  Each lane gets NOL = max(1, NO / CPW) results in
+// out[]; group_sum_output() names the output of out[k] on lane c (-1: none).
 template <int NO, int CPW>
-__device__ __forceinline__ float group_channel_sum(const float* red, int c) {
-  static_assert(NO <= CPW && (CPW % NO) == 0, "outputs per block");
-  constexpr int LPO = CPW / NO;    // lanes per output
-  constexpr int CPL = CPW / LPO;   // channels per lane
-  const int o = c % NO, part = c / NO;
-  float acc = 0.0f;
+constexpr int group_sum_outputs_per_lane() {
+  return NO > CPW ? NO / CPW : 1;
+}
+
+template <int NO, int CPW>
+__device__ __forceinline__ int group_sum_output(int c, int k) {
+  if constexpr (NO >= CPW) return c + k * CPW;
+  else return c < NO ? c : -1;
+}
+
+template <int NO, int CPW>
+__device__ __forceinline__ void group_channel_sum(const float* red, int c,
+                                                  float (&out)[group_sum_outputs_per_lane<NO, CPW>()]) {
+  if constexpr (NO >= CPW) {
+    // every lane sums whole columns: outputs c, c + CPW, ...
+    static_assert(NO % CPW == 0, "outputs per block");
 #pragma unroll
-  for (int m = 0; m < CPL; ++m) acc += red[(part * CPL + m) * (NO + 1) + o];
+    for (int k = 0; k < NO / CPW; ++k) {
+      float acc = 0.0f;
 #pragma unroll
-  for (int off = NO; off < CPW; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  return acc;
+      for (int m = 0; m < CPW; ++m) acc += red[m * (NO + 1) + c + k * CPW];
+      out[k] = acc;
+    }
+  } else {
+    // CPW / NO lanes per output, each summing NO channels, then a butterfly
+    static_assert((CPW % NO) == 0, "outputs per block");
+    constexpr int LPO = CPW / NO;    // lanes per output
+    constexpr int CPL = CPW / LPO;   // channels per lane
+    const int o = c % NO, part = c / NO;
+    float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) acc += red[(part * CPL + m) * (NO + 1) + o];
+#pragma unroll
+    for (int off = NO; off < CPW; off <<= 1) acc += __shfl_xor(acc, off, 64);
+    out[0] = acc;
+  }
 }
 
 // Bytes of the raw tile: x (with the conv halo) | delta_raw | dout | z | y.
@@ -72,7 +97,7 @@ constexpr int bwd_raw_bytes() {
   return (round_up(L + (FUSED ? 3 : 0), RPI) + 4 * round_up(L, RPI)) * CPW * ES;
 }
 
-template <Act A, int DS, int SPL, int L, bool FUSED, int CPW>
+template <Act A, int DS, int SPL, int L, bool FUSED, int CPW, int PD>
 __global__ void __launch_bounds__(CPW * (DS / SPL))
 scan_bwd_kernel(const BwdArgs p) {
   constexpr int G = DS / SPL;          // state groups
@@ -82,6 +107,8 @@ scan_bwd_kernel(const BwdArgs p) {
   static_assert(L % SUB == 0, "sub-tiles must tile the chunk");
   constexpr int NSUB = L / SUB;        // = staged items per thread
   constexpr int NO = SUB * SPL;        // channel sums per group per sub-tile (= DS)
+  static_assert(PD >= 1 && PD <= L, "operand look-ahead");
+  constexpr int NOL = group_sum_outputs_per_lane<NO, CPW>();
   constexpr int KMAX = FUSED ? 4 : 1;  // conv taps supported: 1..4
   constexpr int ES = A == Act::F32 ? 4 : 2;
   constexpr int RB = CPW * ES;         // bytes per raw row
@@ -117,7 +144,7 @@ scan_bwd_kernel(const BwdArgs p) {
   const int wave = tid >> 6, lane = tid & 63;
   constexpr int NW = (NT + 63) / 64;
   const int64_t ngrp = (p.Di + CPW - 1) / CPW;
-  const int64_t wg = xcd_pair_map(blockIdx.x, ngrp * p.B);
+  const int64_t wg = xcd_group_map<line_sharing_groups<ES, CPW>()>(blockIdx.x, ngrp * p.B);
   const int64_t b = wg / ngrp;
   const int64_t cg = wg % ngrp;
   const int64_t i0 = cg * CPW;
@@ -256,94 +283,78 @@ scan_bwd_kernel(const BwdArgs p) {
     __syncthreads();
     if (kt > 0) prefetch(kt - 1);
 
-    // ------------------------------------------------------------ recompute
-    float hs[L][SPL], das[L][SPL];
-    {
-      float4 cur = s_st[0][c];
-      float cB[SPL], cC[SPL];
+    // Step operands {delta, delta*u, dy, u} and this thread's B_t, C_t are
+    // read PD steps before their step into a ring of registers (slot = steps
+    // since the start of the sweep, mod PD); the scheduling barrier per step
+    // keeps the compiler from moving the reads closer to their use, so a
+    // wave waits for LDS about once per sweep rather than once per step.
+    float4 q_st[PD];
+    float q_b[PD][SPL], q_c[PD][SPL];
+    auto operands = [&](int tt, int sl) {
+      q_st[sl] = s_st[tt][c];
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
-        cB[s] = s_bc[0][0][g * SPL + s];
-        cC[s] = s_bc[0][1][g * SPL + s];
+        q_b[sl][s] = s_bc[tt][0][g * SPL + s];
+        q_c[sl][s] = s_bc[tt][1][g * SPL + s];
       }
+    };
+
+    // ------------------------------------------------------------ recompute
+    float hs[L][SPL], das[L][SPL];
 #pragma unroll
-      for (int sb = 0; sb < NSUB; ++sb) {
+    for (int d = 0; d < PD; ++d) operands(d, d);
 #pragma unroll
-        for (int q = 0; q < SUB; ++q) {
-          const int tt = sb * SUB + q;
-          float4 nxt = cur;
-          float nB[SPL], nC[SPL];
+    for (int sb = 0; sb < NSUB; ++sb) {
 #pragma unroll
-          for (int s = 0; s < SPL; ++s) {
-            nB[s] = cB[s];
-            nC[s] = cC[s];
-          }
-          if (tt + 1 < L) {
-            nxt = s_st[tt + 1][c];
+      for (int q = 0; q < SUB; ++q) {
+        const int tt = sb * SUB + q;
+        const int sl = tt % PD;
+        const float4 cur = q_st[sl];
+        float cB[SPL];
 #pragma unroll
-            for (int s = 0; s < SPL; ++s) {
-              nB[s] = s_bc[tt + 1][0][g * SPL + s];
-              nC[s] = s_bc[tt + 1][1][g * SPL + s];
-            }
-          }
+        for (int s = 0; s < SPL; ++s) cB[s] = q_b[sl][s];
+        if (tt + PD < L) operands(tt + PD, sl);
 #pragma unroll
-          for (int s = 0; s < SPL; ++s) {
-            const float dA = exp2_fast(cur.x * a2[s]);
-            h[s] = fmaf(dA, h[s], cur.y * cB[s]);
-            hs[tt][s] = h[s];
-            das[tt][s] = dA;
-            red[c * (NO + 1) + q * SPL + s] = cur.z * h[s];
-          }
-          cur = nxt;
-#pragma unroll
-          for (int s = 0; s < SPL; ++s) {
-            cB[s] = nB[s];
-            cC[s] = nC[s];
-          }
-          // keeps later steps' LDS reads from being hoisted (each would hold
-          // a register across the whole unrolled chunk)
-          __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < SPL; ++s) {
+          const float dA = exp2_fast(cur.x * a2[s]);
+          h[s] = fmaf(dA, h[s], cur.y * cB[s]);
+          hs[tt][s] = h[s];
+          das[tt][s] = dA;
+          red[c * (NO + 1) + q * SPL + s] = cur.z * h[s];
         }
-        wave_lds_sync();
-        const float v = group_channel_sum<NO, CPW>(red, c);
-        if (c < NO) {
-          const int tt = sb * SUB + c / SPL;
-          if (tt < len)
-            p.part_bc[(cg * BT + row0 + t0 + tt) * (2 * DS) + DS + g * SPL + c % SPL] = v;
-        }
-        wave_lds_sync();
+        __builtin_amdgcn_sched_barrier(0);
       }
+      wave_lds_sync();
+      float v[NOL];
+      group_channel_sum<NO, CPW>(red, c, v);
+#pragma unroll
+      for (int k = 0; k < NOL; ++k) {
+        const int o = group_sum_output<NO, CPW>(c, k);   // o = step-in-sub-tile * SPL + state
+        const int tt = sb * SUB + o / SPL;
+        if (o >= 0 && tt < len)
+          p.part_bc[(cg * BT + row0 + t0 + tt) * (2 * DS) + DS + g * SPL + o % SPL] = v[k];
+      }
+      wave_lds_sync();
     }
 
     // -------------------------------------------------------------- reverse
-    float4 cur = s_st[L - 1][c];
-    float cB[SPL], cC[SPL];
 #pragma unroll
-    for (int s = 0; s < SPL; ++s) {
-      cB[s] = s_bc[L - 1][0][g * SPL + s];
-      cC[s] = s_bc[L - 1][1][g * SPL + s];
-    }
+    for (int d = 0; d < PD; ++d) operands(L - 1 - d, d);
 #pragma unroll
     for (int sb = NSUB - 1; sb >= 0; --sb) {
       const int bi = NBUF == 2 ? (sb & 1) : 0;
 #pragma unroll
       for (int q = SUB - 1; q >= 0; --q) {
         const int tt = sb * SUB + q;
-        float4 nxt = cur;
-        float nB[SPL], nC[SPL];
+        const int sl = (L - 1 - tt) % PD;
+        const float4 cur = q_st[sl];
+        float cB[SPL], cC[SPL];
 #pragma unroll
         for (int s = 0; s < SPL; ++s) {
-          nB[s] = cB[s];
-          nC[s] = cC[s];
+          cB[s] = q_b[sl][s];
+          cC[s] = q_c[sl][s];
         }
-        if (tt > 0) {
-          nxt = s_st[tt - 1][c];
-#pragma unroll
-          for (int s = 0; s < SPL; ++s) {
-            nB[s] = s_bc[tt - 1][0][g * SPL + s];
-            nC[s] = s_bc[tt - 1][1][g * SPL + s];
-          }
-        }
+        if (tt - PD >= 0) operands(tt - PD, sl);
         float su = 0.0f, sd = 0.0f;
 #pragma unroll
         for (int s = 0; s < SPL; ++s) {
@@ -358,21 +369,18 @@ scan_bwd_kernel(const BwdArgs p) {
         }
         s_su[bi][g][q][c] = su;
         s_sd[bi][g][q][c] = sd;
-        cur = nxt;
-#pragma unroll
-        for (int s = 0; s < SPL; ++s) {
-          cB[s] = nB[s];
-          cC[s] = nC[s];
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
       wave_lds_sync();
       {
-        const float v = group_channel_sum<NO, CPW>(red, c);
-        if (c < NO) {
-          const int tt = sb * SUB + c / SPL;
-          if (tt < len)
-            p.part_bc[(cg * BT + row0 + t0 + tt) * (2 * DS) + g * SPL + c % SPL] = v;
+        float v[NOL];
+        group_channel_sum<NO, CPW>(red, c, v);
+#pragma unroll
+        for (int k = 0; k < NOL; ++k) {
+          const int o = group_sum_output<NO, CPW>(c, k);
+          const int tt = sb * SUB + o / SPL;
+          if (o >= 0 && tt < len)
+            p.part_bc[(cg * BT + row0 + t0 + tt) * (2 * DS) + g * SPL + o % SPL] = v[k];
         }
       }
       lds_barrier();
@@ -455,7 +463,7 @@ scan_bwd_kernel(const BwdArgs p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <Act A, int DS, int SPL, int L>
+template <Act A, int DS, int SPL, int L, int PD>
 static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
   constexpr int G = DS / SPL;
   constexpr int CPW = kBwdCpw;
@@ -464,23 +472,23 @@ static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
   constexpr unsigned raw_fused = bwd_raw_bytes<A, L, true, CPW>();
   constexpr unsigned raw_plain = bwd_raw_bytes<A, L, false, CPW>();
   if (p.K > 0)
-    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true, CPW>), grid, dim3(CPW * G), raw_fused, st, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true, CPW, PD>), grid, dim3(CPW * G), raw_fused, st, p);
   else
-    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false, CPW>), grid, dim3(CPW * G), raw_plain, st, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false, CPW, PD>), grid, dim3(CPW * G), raw_plain, st, p);
   return hipGetLastError();
 }
 
 template <Act A>
 hipError_t launch_bwd_a(const BwdArgs& p, int ds, int L, hipStream_t st) {
-  // states per thread: L of them are held in registers, so SPL * L <= 64;
-  // at least two state groups so that a workgroup has whole waves
-#define MSCAN_CASE(DS_, L_)                                                    \
-  if (ds == DS_ && L == L_)                                                    \
-    return launch_bwd_t<A, DS_, ((64 / L_) < (DS_ / 2) ? (64 / L_) : (DS_ / 2)), L_>(p, st);
-  MSCAN_CASE(4, 16) MSCAN_CASE(4, 32)
-  MSCAN_CASE(8, 16) MSCAN_CASE(8, 32)
-  MSCAN_CASE(16, 16) MSCAN_CASE(16, 32)
-  MSCAN_CASE(32, 16)
+  // (d_state, checkpoint interval) -> states per thread, operand look-ahead.
+  // A thread keeps h_t and dA_t of its SPL states for all L steps of a tile
+  // in registers (2 * SPL * L of them); a workgroup must be whole waves.
+#define MSCAN_CASE(DS_, L_, SPL_, PD_) \
+  if (ds == DS_ && L == L_) return launch_bwd_t<A, DS_, SPL_, L_, PD_>(p, st);
+  MSCAN_CASE(4, 16, 1, 4) MSCAN_CASE(4, 32, 1, 4)
+  MSCAN_CASE(8, 16, 2, 4) MSCAN_CASE(8, 32, 2, 2)
+  MSCAN_CASE(16, 16, 2, 4) MSCAN_CASE(16, 32, 2, 2)
+  MSCAN_CASE(32, 16, 4, 2)
 #undef MSCAN_CASE
   return hipErrorInvalidValue;
 }

@@ -12,11 +12,12 @@ enum class Act : int { F32 = 0, BF16 = 1, F16 = 2 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Channels per workgroup.  A thread is (state group, channel): with 32
-// channels a wave holds 32 channels x 2 state groups, so a workgroup stays
-// small enough (LDS, waves) for two of them to share a CU.
-constexpr int kFwdCpw = 32;
-constexpr int kBwdCpw = 32;
+// Channels per workgroup.  A thread is (state group, channel): with 16
+// channels a wave holds 16 channels x 4 state groups.  Small workgroups give
+// many of them per CU (2 to 3 at the long-sequence 2.8B layer shape), which
+// evens out the load across SIMDs better than few large ones.
+constexpr int kFwdCpw = 16;
+constexpr int kBwdCpw = 16;
 
 // ---------------------------------------------------------------- dtype I/O
 template <Act A>
@@ -99,15 +100,25 @@ __device__ __forceinline__ float sigmoid(float x) {
 
 // ---------------------------------------------------------------- XCD mapping
 // Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
-// linear id.  Two neighbouring channel groups share every 128-byte line of a
-// 16-bit activation row, so the logical workgroups 2q and 2q+1 are given the
-// linear ids x + 16m and x + 16m + 8 of one XCD x (same L2).  Ids past the
-// last whole block of 16 keep their own index.  Returns the logical id.
-__device__ __forceinline__ int64_t xcd_pair_map(int64_t k, int64_t n) {
-  const int64_t full = n & ~static_cast<int64_t>(15);
+// linear id.  Q neighbouring channel groups share every 128-byte line of an
+// activation row, so the logical workgroups Q*r .. Q*r + Q-1 are given the
+// linear ids x + 8m, x + 8(m+1), ..., x + 8(m+Q-1) of one XCD x (same L2).
+// Ids past the last whole block of 8*Q keep their own index.  A bijection on
+// [0, n); returns the logical id.
+template <int Q>
+__device__ __forceinline__ int64_t xcd_group_map(int64_t k, int64_t n) {
+  static_assert(Q >= 1, "group size");
+  if (Q == 1) return k;
+  const int64_t full = n - n % (8 * Q);
   if (k >= full) return k;
-  const int64_t x = k & 7, j = k >> 3;
-  return ((j >> 1) << 4) + 2 * x + (j & 1);
+  const int64_t x = k & 7, j = k >> 3;   // XCD, round
+  return (j / Q) * (8 * Q) + Q * x + (j % Q);
+}
+
+// channel groups of CPW channels of ES-byte elements that share a 128-byte line
+template <int ES, int CPW>
+constexpr int line_sharing_groups() {
+  return CPW * ES >= 128 ? 1 : 128 / (CPW * ES);
 }
 
 // ---------------------------------------------------------------- barriers

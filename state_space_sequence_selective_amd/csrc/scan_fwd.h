@@ -62,7 +62,7 @@ scan_fwd_kernel(const FwdArgs p) {
   const int wave = tid >> 6, lane = tid & 63;
   constexpr int NW = (NT + 63) / 64;
   const int64_t ngrp = (p.Di + CPW - 1) / CPW;
-  const int64_t wg = xcd_pair_map(blockIdx.x, ngrp * p.B);
+  const int64_t wg = xcd_group_map<line_sharing_groups<ES, CPW>()>(blockIdx.x, ngrp * p.B);
   const int64_t b = wg / ngrp;
   const int64_t i0 = (wg % ngrp) * CPW;
   const int64_t i = i0 + c;

@@ -51,12 +51,12 @@ def _dims(pkg, **kw):
 def test_sizes(pkg):
     d = _dims(pkg)
     assert pkg.ckpt_bytes(d) == 2 * 4 * 16 * 64 * 4            # ceil(100/32) = 4 checkpoints
-    # per-group d_B|d_C partials (groups of 32 channels: 2) padded to 256 B,
+    # per-group d_B|d_C partials (groups of 16 channels: 4) padded to 256 B,
     # then per-row param partials
-    bc = 2 * 2 * 100 * 32 * 4
+    bc = 4 * 2 * 100 * 32 * 4
     assert pkg.workspace_bytes(d) == ((bc + 255) // 256) * 256 + 2 * 64 * 17 * 4
     dc = _dims(pkg, d_conv=4, d_inner=128)
-    bc = 4 * 2 * 100 * 32 * 4
+    bc = 8 * 2 * 100 * 32 * 4
     assert pkg.workspace_bytes(dc) == ((bc + 255) // 256) * 256 + 2 * 128 * 22 * 4
 
 

@@ -71,7 +71,7 @@ def _oracle(oracle_lib, w, inp, chunk, channels=None):
                 kw[k] = kw[k][:, S]
         dout = dout[..., S]
         due = None if due is None else due[..., S]
-    L = chunk if chunk else 32
+    L = chunk if chunk else 16
     f = oracle_lib.forward(chunk=L, **kw)
     g = oracle_lib.backward(dout=dout, d_u_extra=due, **kw)
     return f, g
