@@ -57,6 +57,23 @@
  *     MAMBA_ERR_HIP, stops at the failing launch) and leaves a message
  *     naming the entry point in mamba_last_error().
  *   - Half-precision outputs are rounded to nearest even.
+ *
+ * Segmented schedule.  When few (batch row, channel group) pairs would fill
+ * the GPU, the sequence is cut into segments of whole checkpoint intervals
+ * that are scanned in parallel, in the spirit of the parallel prefix scan
+ * the forward_mixed page's F4d step switches to for long sequences.  The
+ * recurrence is affine in the state, so a segment started from zero yields
+ * its end state H_s, and the product of its dA is exp(A * sum of delta):
+ *   forward : an aggregate pass gives (H_s, sum delta) per segment; the main
+ *             pass starts segment s from the fold of the earlier pairs
+ *             (h <- exp(A sum delta) h + H), starting at h0.
+ *   backward: an aggregate pass runs each segment's adjoint of h from a zero
+ *             carry, giving the carry it hands to the earlier steps; the main
+ *             pass starts segment s from the fold of the later segments'
+ *             pairs.
+ * The schedule changes only the order of floating-point operations.  The
+ * fused backward always sweeps whole sequences (its conv tail would cross
+ * segment borders).  The pairs live in the workspace.
  */
 #ifndef MAMBA_SCAN_H
 #define MAMBA_SCAN_H
@@ -68,7 +85,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 1
+#define MAMBA_SCAN_ABI_VERSION 2
 
 typedef enum mamba_dtype { MAMBA_F32 = 0, MAMBA_BF16 = 1, MAMBA_F16 = 2 } mamba_dtype_t;
 
@@ -91,7 +108,9 @@ typedef struct mamba_dims {
                        backward holds L steps of state in registers, so
                        Ds 32 needs L = 16 */
   int32_t act;      /* mamba_dtype_t of every activation tensor (and xdbl) */
-  int32_t reserved; /* must be 0 */
+  int32_t segments; /* sequence segments scanned in parallel (see below):
+                       0 = chosen from the sizes; n in 1 .. 4096 = at most
+                       n (1 = one sweep per channel group) */
 } mamba_dims_t;
 
 /* Version of this ABI (MAMBA_SCAN_ABI_VERSION of the built library). */
@@ -104,9 +123,10 @@ const char* mamba_last_error(void);
 /* Bytes of the f32 checkpoint buffer: B * ceil(T/L) * Ds * Di * 4. */
 int mamba_ckpt_bytes(const mamba_dims_t* dims, size_t* bytes);
 
-/* Bytes of device scratch the backward entry points need (per-group partial
-   sums reduced in a fixed order, so the result is run-to-run reproducible);
-   the forward entry points need none. */
+/* Bytes of device scratch the entry points need: the backward's per-group
+   partial sums (reduced in a fixed order, so the result is run-to-run
+   reproducible) and the segment pairs of the segmented schedule.  One
+   buffer of this size serves the forward and the backward of these dims. */
 int mamba_workspace_bytes(const mamba_dims_t* dims, size_t* bytes);
 
 /*
@@ -116,11 +136,13 @@ int mamba_workspace_bytes(const mamba_dims_t* dims, size_t* bytes);
  * Outputs: out [act]; y_save [act] or NULL: the pre-gate y (saved
  *   activation for the backward; required later when z is given);
  *   h_last f32 or NULL; ckpt f32 or NULL (needed by the backward).
+ * workspace: device scratch of at least mamba_workspace_bytes(dims) bytes
+ *   (NULL allowed when that is 0), contents irrelevant on entry.
  */
 int mamba_scan_fwd(const mamba_dims_t* dims, const void* u, const void* delta_raw,
                    const float* a_log, const void* xdbl, const float* D, const void* z,
                    const float* h0, void* out, void* y_save, float* h_last, float* ckpt,
-                   void* stream);
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward of mamba_scan_fwd (the reverse-time adjoint) for a given dout.
@@ -144,12 +166,14 @@ int mamba_scan_bwd(const mamba_dims_t* dims, const void* u, const void* delta_ra
  *   conv_state0 f32 or NULL (= zeros); the rest as in mamba_scan_fwd.
  * Outputs: out [act]; u_out [act] or NULL: the conv+SiLU output;
  *   y_save, h_last, ckpt as in mamba_scan_fwd; conv_state_last f32 or NULL.
+ * workspace: as in mamba_scan_fwd.
  */
 int mamba_conv_scan_gate_fwd(const mamba_dims_t* dims, const void* x, const float* conv_w,
                              const float* conv_b, const float* conv_state0, const void* delta_raw,
                              const float* a_log, const void* xdbl, const float* D, const void* z,
                              const float* h0, void* out, void* u_out, void* y_save,
-                             float* h_last, float* conv_state_last, float* ckpt, void* stream);
+                             float* h_last, float* conv_state_last, float* ckpt,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward of mamba_conv_scan_gate_fwd.  d_u_extra [act] or NULL: an extra

@@ -35,12 +35,12 @@ class Dims(ctypes.Structure):
     """mamba_dims_t."""
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_inner", ctypes.c_int64),
                 ("d_state", ctypes.c_int64), ("dt_rank", ctypes.c_int64), ("d_conv", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("act", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("chunk", ctypes.c_int32), ("act", ctypes.c_int32), ("segments", ctypes.c_int32)]
 
     @classmethod
-    def make(cls, batch, seqlen, d_inner, d_state, dt_rank=0, d_conv=0, chunk=0, act="bf16"):
+    def make(cls, batch, seqlen, d_inner, d_state, dt_rank=0, d_conv=0, chunk=0, act="bf16", segments=0):
         code = ACT_CODES[act] if isinstance(act, str) else int(act)
-        return cls(batch, seqlen, d_inner, d_state, dt_rank, d_conv, chunk, code, 0)
+        return cls(batch, seqlen, d_inner, d_state, dt_rank, d_conv, chunk, code, segments)
 
     @property
     def L(self) -> int:
@@ -80,11 +80,11 @@ def load():
         f.restype = ctypes.c_int
         f.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
     lib.mamba_scan_fwd.restype = ctypes.c_int
-    lib.mamba_scan_fwd.argtypes = [D] + [P] * 12
+    lib.mamba_scan_fwd.argtypes = [D] + [P] * 12 + [ctypes.c_size_t, P]
     lib.mamba_scan_bwd.restype = ctypes.c_int
     lib.mamba_scan_bwd.argtypes = [D] + [P] * 16 + [ctypes.c_size_t, P]
     lib.mamba_conv_scan_gate_fwd.restype = ctypes.c_int
-    lib.mamba_conv_scan_gate_fwd.argtypes = [D] + [P] * 17
+    lib.mamba_conv_scan_gate_fwd.argtypes = [D] + [P] * 17 + [ctypes.c_size_t, P]
     lib.mamba_conv_scan_gate_bwd.restype = ctypes.c_int
     lib.mamba_conv_scan_gate_bwd.argtypes = [D] + [P] * 22 + [ctypes.c_size_t, P]
     _lib = lib
@@ -141,6 +141,12 @@ def _ptr(t, name, dtype, shape, required=False):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _workspace(workspace):
+    if workspace is None:
+        return None, ctypes.c_size_t(0)
+    return _ptr(workspace, "workspace", torch.uint8, (workspace.numel(),), True), ctypes.c_size_t(workspace.numel())
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -155,20 +161,21 @@ def _shapes(d: Dims):
 
 
 def scan_fwd(d: Dims, u, delta_raw, a_log, xdbl, D=None, z=None, h0=None, *, out, y_save=None,
-             h_last=None, ckpt=None, stream=None):
+             h_last=None, ckpt=None, workspace=None, stream=None):
     s, at, f = _shapes(d), d.act_dtype, torch.float32
     args = [ctypes.byref(d), _ptr(u, "u", at, s["act"], True), _ptr(delta_raw, "delta_raw", at, s["act"], True),
             _ptr(a_log, "a_log", f, s["a_log"], True), _ptr(xdbl, "xdbl", at, s["xdbl"], True),
             _ptr(D, "D", f, s["vec"]), _ptr(z, "z", at, s["act"]), _ptr(h0, "h0", f, s["state"]),
             _ptr(out, "out", at, s["act"], True), _ptr(y_save, "y_save", at, s["act"]),
-            _ptr(h_last, "h_last", f, s["state"]), _ptr(ckpt, "ckpt", f, s["ckpt"]), _stream(stream)]
+            _ptr(h_last, "h_last", f, s["state"]), _ptr(ckpt, "ckpt", f, s["ckpt"]), *_workspace(workspace),
+            _stream(stream)]
     _check(load().mamba_scan_fwd(*args))
 
 
 def scan_bwd(d: Dims, u, delta_raw, a_log, xdbl, D, z, y_saved, ckpt, dout, *, d_u, d_delta_raw, d_z,
              d_xdbl, d_a_log, d_D, workspace, stream=None):
     s, at, f = _shapes(d), d.act_dtype, torch.float32
-    ws = _ptr(workspace, "workspace", torch.uint8, (workspace.numel(),), True) if workspace is not None else None
+    ws, wsn = _workspace(workspace)
     args = [ctypes.byref(d), _ptr(u, "u", at, s["act"], True), _ptr(delta_raw, "delta_raw", at, s["act"], True),
             _ptr(a_log, "a_log", f, s["a_log"], True), _ptr(xdbl, "xdbl", at, s["xdbl"], True),
             _ptr(D, "D", f, s["vec"]), _ptr(z, "z", at, s["act"]), _ptr(y_saved, "y_saved", at, s["act"]),
@@ -176,13 +183,13 @@ def scan_bwd(d: Dims, u, delta_raw, a_log, xdbl, D, z, y_saved, ckpt, dout, *, d
             _ptr(d_u, "d_u", at, s["act"], True), _ptr(d_delta_raw, "d_delta_raw", at, s["act"], True),
             _ptr(d_z, "d_z", at, s["act"]), _ptr(d_xdbl, "d_xdbl", f, s["xdbl"], True),
             _ptr(d_a_log, "d_a_log", f, s["a_log"], True), _ptr(d_D, "d_D", f, s["vec"], True),
-            ws, ctypes.c_size_t(0 if workspace is None else workspace.numel()), _stream(stream)]
+            ws, wsn, _stream(stream)]
     _check(load().mamba_scan_bwd(*args))
 
 
 def conv_scan_gate_fwd(d: Dims, x, conv_w, conv_b, conv_state0, delta_raw, a_log, xdbl, D=None, z=None,
                        h0=None, *, out, u_out=None, y_save=None, h_last=None, conv_state_last=None, ckpt=None,
-                       stream=None):
+                       workspace=None, stream=None):
     s, at, f = _shapes(d), d.act_dtype, torch.float32
     args = [ctypes.byref(d), _ptr(x, "x", at, s["act"], True), _ptr(conv_w, "conv_w", f, s["conv_w"], True),
             _ptr(conv_b, "conv_b", f, s["vec"]), _ptr(conv_state0, "conv_state0", f, s["conv_state"]),
@@ -191,7 +198,7 @@ def conv_scan_gate_fwd(d: Dims, x, conv_w, conv_b, conv_state0, delta_raw, a_log
             _ptr(h0, "h0", f, s["state"]), _ptr(out, "out", at, s["act"], True),
             _ptr(u_out, "u_out", at, s["act"]), _ptr(y_save, "y_save", at, s["act"]),
             _ptr(h_last, "h_last", f, s["state"]), _ptr(conv_state_last, "conv_state_last", f, s["conv_state"]),
-            _ptr(ckpt, "ckpt", f, s["ckpt"]), _stream(stream)]
+            _ptr(ckpt, "ckpt", f, s["ckpt"]), *_workspace(workspace), _stream(stream)]
     _check(load().mamba_conv_scan_gate_fwd(*args))
 
 
@@ -199,7 +206,7 @@ def conv_scan_gate_bwd(d: Dims, x, conv_w, conv_b, conv_state0, delta_raw, a_log
                        dout, d_u_extra=None, *, d_x, d_delta_raw, d_z, d_xdbl, d_a_log, d_D, d_conv_w, d_conv_b,
                        workspace, stream=None):
     s, at, f = _shapes(d), d.act_dtype, torch.float32
-    ws = _ptr(workspace, "workspace", torch.uint8, (workspace.numel(),), True) if workspace is not None else None
+    ws, wsn = _workspace(workspace)
     args = [ctypes.byref(d), _ptr(x, "x", at, s["act"], True), _ptr(conv_w, "conv_w", f, s["conv_w"], True),
             _ptr(conv_b, "conv_b", f, s["vec"]), _ptr(conv_state0, "conv_state0", f, s["conv_state"]),
             _ptr(delta_raw, "delta_raw", at, s["act"], True), _ptr(a_log, "a_log", f, s["a_log"], True),
@@ -210,5 +217,5 @@ def conv_scan_gate_bwd(d: Dims, x, conv_w, conv_b, conv_state0, delta_raw, a_log
             _ptr(d_z, "d_z", at, s["act"]), _ptr(d_xdbl, "d_xdbl", f, s["xdbl"], True),
             _ptr(d_a_log, "d_a_log", f, s["a_log"], True), _ptr(d_D, "d_D", f, s["vec"], True),
             _ptr(d_conv_w, "d_conv_w", f, s["conv_w"], True), _ptr(d_conv_b, "d_conv_b", f, s["vec"], True),
-            ws, ctypes.c_size_t(0 if workspace is None else workspace.numel()), _stream(stream)]
+            ws, wsn, _stream(stream)]
     _check(load().mamba_conv_scan_gate_bwd(*args))

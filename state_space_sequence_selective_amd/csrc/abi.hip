@@ -16,6 +16,9 @@ hipError_t launch_fwd_f16(const FwdArgs& p, int ds, int spl, hipStream_t st);
 hipError_t launch_bwd_f32(const BwdArgs& p, int ds, int L, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& p, int ds, int L, hipStream_t st);
 hipError_t launch_bwd_f16(const BwdArgs& p, int ds, int L, hipStream_t st);
+hipError_t launch_carry_f32(const CarryArgs& p, int ds, hipStream_t st);
+hipError_t launch_carry_bf16(const CarryArgs& p, int ds, hipStream_t st);
+hipError_t launch_carry_f16(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& p, hipStream_t st);
 
 static hipError_t launch_fwd(const FwdArgs& p, Act act, int ds, int spl, hipStream_t st) {
@@ -32,6 +35,15 @@ static hipError_t launch_bwd(const BwdArgs& p, Act act, int ds, int L, hipStream
     case Act::F32: return launch_bwd_f32(p, ds, L, st);
     case Act::BF16: return launch_bwd_bf16(p, ds, L, st);
     case Act::F16: return launch_bwd_f16(p, ds, L, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_carry(const CarryArgs& p, Act act, int ds, hipStream_t st) {
+  switch (act) {
+    case Act::F32: return launch_carry_f32(p, ds, st);
+    case Act::BF16: return launch_carry_bf16(p, ds, st);
+    case Act::F16: return launch_carry_f16(p, ds, st);
   }
   return hipErrorInvalidValue;
 }
@@ -54,13 +66,43 @@ struct Plan {
   mscan::Act act;
   int esize;      // bytes per activation element
   int bulk_align; // alignment of activation inputs staged with 4 / 16-byte granules
+  int Sf, Sb;     // segments of the forward / backward schedule
+  int64_t segf_tiles, segb_tiles;   // 16-step tiles per forward segment, L-step tiles per backward one
 };
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;
+constexpr int kMaxSegments = 4096;
+
+// Segment count for a schedule over `ntiles` tiles and `nwg` workgroups per
+// segment: the caller's cap `hint`, or enough segments for about `want`
+// workgroups, keeping at least `min_tiles` tiles per segment.  Returns the
+// count actually used (no empty segment) and the tiles per segment.
+void choose_segments(int hint, int64_t nwg, int64_t ntiles, int64_t want, int64_t min_tiles, int* S,
+                     int64_t* per) {
+  int64_t s = 1;
+  if (hint > 0) {
+    s = hint;
+  } else if (nwg < want) {
+    s = (want + nwg - 1) / nwg;
+    const int64_t cap = ntiles / min_tiles;
+    s = s < cap ? s : cap;
+  }
+  s = s < ntiles ? s : ntiles;
+  s = s < 1 ? 1 : s;
+  *per = (ntiles + s - 1) / s;
+  *S = static_cast<int>((ntiles + *per - 1) / *per);
+}
+
+// Workgroups that fill the GPU well: the forward has room for several per
+// CU; the backward balances best with several rounds of them (256 CUs).
+constexpr int64_t kWantFwdWorkgroups = 512;
+constexpr int64_t kWantBwdWorkgroups = 4096;
+constexpr int64_t kMinSegmentTiles = 8;
 
 int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   if (!d) return fail(MAMBA_ERR_INVALID, fn, "dims is NULL");
-  if (d->reserved != 0) return fail(MAMBA_ERR_INVALID, fn, "dims.reserved must be 0");
+  if (d->segments < 0 || d->segments > kMaxSegments)
+    return fail(MAMBA_ERR_INVALID, fn, "dims.segments must be in [0, " + std::to_string(kMaxSegments) + "]");
   if (d->act < 0 || d->act > 2) return fail(MAMBA_ERR_INVALID, fn, "dims.act is not a mamba_dtype_t");
   if (d->batch < 1 || d->batch > 65535)
     return fail(d->batch < 1 ? MAMBA_ERR_INVALID : MAMBA_ERR_CAPACITY, fn, "batch must be in [1, 65535]");
@@ -101,6 +143,16 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   pl->act = static_cast<mscan::Act>(d->act);
   pl->esize = d->act == MAMBA_F32 ? 4 : 2;
   pl->bulk_align = d->act == MAMBA_F32 ? 16 : 4;
+  const int64_t nwg_f = (d->d_inner + mscan::kFwdCpw - 1) / mscan::kFwdCpw * d->batch;
+  const int64_t nwg_b = pl->nG * d->batch;
+  choose_segments(d->segments, nwg_f, (d->seqlen + 15) / 16, kWantFwdWorkgroups, kMinSegmentTiles, &pl->Sf,
+                  &pl->segf_tiles);
+  if (fused) {   // the conv backward of a segment's tail needs the next segment's head
+    pl->Sb = 1;
+    pl->segb_tiles = pl->nC;
+  } else {
+    choose_segments(d->segments, nwg_b, pl->nC, kWantBwdWorkgroups, kMinSegmentTiles, &pl->Sb, &pl->segb_tiles);
+  }
   return MAMBA_OK;
 }
 
@@ -128,14 +180,40 @@ size_t bc_part_bytes(const Plan& pl) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Workspace layouts.  Forward: [seg_h | seg_sd] when segmented.  Backward:
+// [part_bc | part_par | seg_q | seg_sd], the last two when segmented.
+size_t seg_state_bytes(const Plan& pl, int S) { return align256(sizeof(float) * pl.B * S * pl.Di * pl.Ds); }
+size_t seg_sum_bytes(const Plan& pl, int S) { return align256(sizeof(float) * pl.B * S * pl.Di); }
+size_t par_part_bytes(const Plan& pl) { return align256(sizeof(float) * pl.Sb * pl.B * pl.Di * param_width(pl)); }
+
+size_t workspace_need_fwd(const Plan& pl) {
+  return pl.Sf > 1 ? seg_state_bytes(pl, pl.Sf) + seg_sum_bytes(pl, pl.Sf) : 0;
+}
+
+size_t workspace_need_bwd(const Plan& pl) {
+  return align256(bc_part_bytes(pl)) + par_part_bytes(pl) +
+         (pl.Sb > 1 ? seg_state_bytes(pl, pl.Sb) + seg_sum_bytes(pl, pl.Sb) : 0);
+}
+
 size_t workspace_need(const Plan& pl) {
-  return align256(bc_part_bytes(pl)) + static_cast<size_t>(pl.B) * pl.Di * param_width(pl) * sizeof(float);
+  const size_t f = workspace_need_fwd(pl), b = workspace_need_bwd(pl);
+  return f > b ? f : b;
+}
+
+int check_workspace(const char* fn, const void* workspace, size_t workspace_bytes, size_t need) {
+  if (need == 0) return MAMBA_OK;
+  MSCAN_TRY(check_ptr(fn, "workspace", workspace, true, 256));
+  if (workspace_bytes < need)
+    return fail(MAMBA_ERR_CAPACITY, fn,
+                "workspace_bytes " + std::to_string(workspace_bytes) + " < required " + std::to_string(need));
+  return MAMBA_OK;
 }
 
 int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_w, const float* conv_b,
                const float* conv_state0, const void* delta_raw, const float* a_log, const void* xdbl,
                const float* D, const void* z, const float* h0, void* out, void* u_out, void* y_save,
-               float* h_last, float* conv_state_last, float* ckpt, void* stream) {
+               float* h_last, float* conv_state_last, float* ckpt, void* workspace, size_t workspace_bytes,
+               void* stream) {
   const int e = pl.esize, ba = pl.bulk_align;
   MSCAN_TRY(check_ptr(fn, pl.K ? "x" : "u", x, true, ba));
   MSCAN_TRY(check_ptr(fn, "delta_raw", delta_raw, true, ba));
@@ -155,6 +233,7 @@ int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_
     MSCAN_TRY(check_ptr(fn, "u_out", u_out, false, e));
     MSCAN_TRY(check_ptr(fn, "conv_state_last", conv_state_last, false, 4));
   }
+  MSCAN_TRY(check_workspace(fn, workspace, workspace_bytes, workspace_need_fwd(pl)));
   mscan::FwdArgs a{};
   a.x = x;
   a.delta_raw = delta_raw;
@@ -180,6 +259,12 @@ int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_
   a.nC = pl.nC;
   a.K = pl.K;
   a.L = pl.L;
+  a.S = pl.Sf;
+  a.seg_tiles = pl.segf_tiles;
+  if (pl.Sf > 1) {
+    a.seg_h = static_cast<float*>(workspace);
+    a.seg_sd = reinterpret_cast<float*>(static_cast<char*>(workspace) + seg_state_bytes(pl, pl.Sf));
+  }
   hipError_t err = mscan::launch_fwd(a, pl.act, static_cast<int>(pl.Ds), pl.spl_fwd,
                                      static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("forward launch: ") + hipGetErrorString(err));
@@ -218,14 +303,34 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
     MSCAN_TRY(check_ptr(fn, "d_conv_b", d_conv_b, true, 4));
   }
   MSCAN_TRY(check_ptr(fn, "workspace", workspace, true, 256));
-  const size_t need = workspace_need(pl);
-  if (workspace_bytes < need)
-    return fail(MAMBA_ERR_CAPACITY, fn,
-                "workspace_bytes " + std::to_string(workspace_bytes) + " < required " + std::to_string(need));
-  float* part_bc = static_cast<float*>(workspace);
-  float* part_par = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(bc_part_bytes(pl)));
+  MSCAN_TRY(check_workspace(fn, workspace, workspace_bytes, workspace_need_bwd(pl)));
+  char* ws = static_cast<char*>(workspace);
+  float* part_bc = reinterpret_cast<float*>(ws);
+  float* part_par = reinterpret_cast<float*>(ws + align256(bc_part_bytes(pl)));
+  float* seg_q = reinterpret_cast<float*>(ws + align256(bc_part_bytes(pl)) + par_part_bytes(pl));
+  float* seg_sd = reinterpret_cast<float*>(reinterpret_cast<char*>(seg_q) + seg_state_bytes(pl, pl.Sb));
   const int PW = static_cast<int>(param_width(pl));
   hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (pl.Sb > 1) {   // aggregate pass: carries the segments hand back from a zero start
+    mscan::CarryArgs c{};
+    c.delta_raw = delta_raw;
+    c.a_log = a_log;
+    c.xdbl = xdbl;
+    c.z = z;
+    c.dout = dout;
+    c.seg_q = seg_q;
+    c.seg_sd = seg_sd;
+    c.B = pl.B;
+    c.T = pl.T;
+    c.Di = pl.Di;
+    c.R = pl.R;
+    c.X = pl.X;
+    c.seg_steps = pl.segb_tiles * pl.L;
+    c.S = pl.Sb;
+    hipError_t err = mscan::launch_carry(c, pl.act, static_cast<int>(pl.Ds), st);
+    if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("carry launch: ") + hipGetErrorString(err));
+  }
 
   mscan::BwdArgs a{};
   a.x = x;
@@ -255,6 +360,12 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   a.K = pl.K;
   a.L = pl.L;
   a.PW = PW;
+  a.S = pl.Sb;
+  a.seg_tiles = pl.segb_tiles;
+  if (pl.Sb > 1) {
+    a.seg_q = seg_q;
+    a.seg_sd = seg_sd;
+  }
   hipError_t err = mscan::launch_bwd(a, pl.act, static_cast<int>(pl.Ds), pl.L, st);
   if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("backward launch: ") + hipGetErrorString(err));
 
@@ -273,6 +384,7 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   r.R = pl.R;
   r.X = pl.X;
   r.nG = pl.nG;
+  r.par_rows = static_cast<int64_t>(pl.Sb) * pl.B;
   r.K = pl.K;
   r.PW = PW;
   err = mscan::launch_reduce(r, st);
@@ -302,22 +414,29 @@ int mamba_ckpt_bytes(const mamba_dims_t* dims, size_t* bytes) {
 int mamba_workspace_bytes(const mamba_dims_t* dims, size_t* bytes) {
   const char* fn = "mamba_workspace_bytes";
   Plan pl;
-  const bool fused = dims && dims->d_conv > 0;
-  MSCAN_TRY(plan_dims(dims, fused, fn, &pl));
+  MSCAN_TRY(plan_dims(dims, false, fn, &pl));
   if (!bytes) return fail(MAMBA_ERR_INVALID, fn, "bytes is NULL");
-  *bytes = workspace_need(pl);
+  size_t need = workspace_need(pl);
+  if (dims->d_conv > 0) {   // the fused entry points plan with the conv taps
+    Plan pf;
+    MSCAN_TRY(plan_dims(dims, true, fn, &pf));
+    const size_t nf = workspace_need(pf);
+    need = nf > need ? nf : need;
+  }
+  *bytes = need;
   g_err.clear();
   return MAMBA_OK;
 }
 
 int mamba_scan_fwd(const mamba_dims_t* dims, const void* u, const void* delta_raw, const float* a_log,
                    const void* xdbl, const float* D, const void* z, const float* h0, void* out,
-                   void* y_save, float* h_last, float* ckpt, void* stream) {
+                   void* y_save, float* h_last, float* ckpt, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   const char* fn = "mamba_scan_fwd";
   Plan pl;
   MSCAN_TRY(plan_dims(dims, false, fn, &pl));
   return do_forward(fn, pl, u, nullptr, nullptr, nullptr, delta_raw, a_log, xdbl, D, z, h0, out, nullptr,
-                    y_save, h_last, nullptr, ckpt, stream);
+                    y_save, h_last, nullptr, ckpt, workspace, workspace_bytes, stream);
 }
 
 int mamba_scan_bwd(const mamba_dims_t* dims, const void* u, const void* delta_raw, const float* a_log,
@@ -336,12 +455,12 @@ int mamba_conv_scan_gate_fwd(const mamba_dims_t* dims, const void* x, const floa
                              const float* conv_state0, const void* delta_raw, const float* a_log,
                              const void* xdbl, const float* D, const void* z, const float* h0, void* out,
                              void* u_out, void* y_save, float* h_last, float* conv_state_last, float* ckpt,
-                             void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "mamba_conv_scan_gate_fwd";
   Plan pl;
   MSCAN_TRY(plan_dims(dims, true, fn, &pl));
   return do_forward(fn, pl, x, conv_w, conv_b, conv_state0, delta_raw, a_log, xdbl, D, z, h0, out, u_out,
-                    y_save, h_last, conv_state_last, ckpt, stream);
+                    y_save, h_last, conv_state_last, ckpt, workspace, workspace_bytes, stream);
 }
 
 int mamba_conv_scan_gate_bwd(const mamba_dims_t* dims, const void* x, const float* conv_w, const float* conv_b,

@@ -5,4 +5,7 @@ namespace mscan {
 hipError_t launch_bwd_bf16(const BwdArgs& p, int ds, int L, hipStream_t st) {
   return launch_bwd_a<Act::BF16>(p, ds, L, st);
 }
+hipError_t launch_carry_bf16(const CarryArgs& p, int ds, hipStream_t st) {
+  return launch_carry_a<Act::BF16>(p, ds, st);
+}
 }  // namespace mscan

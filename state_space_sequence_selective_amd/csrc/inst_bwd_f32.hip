@@ -5,4 +5,7 @@ namespace mscan {
 hipError_t launch_bwd_f32(const BwdArgs& p, int ds, int L, hipStream_t st) {
   return launch_bwd_a<Act::F32>(p, ds, L, st);
 }
+hipError_t launch_carry_f32(const CarryArgs& p, int ds, hipStream_t st) {
+  return launch_carry_a<Act::F32>(p, ds, st);
+}
 }  // namespace mscan

@@ -35,9 +35,18 @@
 // Past the end of the sequence the staged values are zero, which makes the
 // extra steps of a short last tile identities, so the step loops need no
 // bounds tests.  d_B / d_C per channel group and d_a_log / d_D / conv grads
-// per batch row go to a workspace; mscan_reduce_kernel sums them in a fixed
-// order.
+// per segment and batch row go to a workspace; mscan_reduce_kernel sums them
+// in a fixed order.
+//
+// Segments.  The grid is S copies of the channel-group grid; copy s walks
+// the tiles [s * seg_tiles, (s+1) * seg_tiles) backwards, starting from the
+// carry the later segments hand it: the pairs (Q, sum delta) of segments
+// S-1 .. s+1 from scan_bwd_carry_kernel, folded as
+//   carry <- exp(A * sum delta) carry + Q.
+// The fused entry runs one segment (the conv backward of a segment's last
+// K-1 steps needs the next segment's first ones).
 #pragma once
+#include "scan_carry.h"
 #include "scan_common.h"
 
 namespace mscan {
@@ -97,16 +106,20 @@ constexpr int bwd_raw_bytes() {
   return (round_up(L + (FUSED ? 3 : 0), RPI) + 4 * round_up(L, RPI)) * CPW * ES;
 }
 
-template <Act A, int DS, int SPL, int L, bool FUSED, int CPW, int PD>
+template <Act A, int DS, int SPL, int L, bool FUSED, int CPW, int PD, int SUB>
 __global__ void __launch_bounds__(CPW * (DS / SPL))
 scan_bwd_kernel(const BwdArgs p) {
   constexpr int G = DS / SPL;          // state groups
   constexpr int NT = CPW * G;          // threads: (state group, channel)
   static_assert(NT % 64 == 0, "whole waves");
-  constexpr int SUB = G;               // steps per reverse sub-tile
-  static_assert(L % SUB == 0, "sub-tiles must tile the chunk");
-  constexpr int NSUB = L / SUB;        // = staged items per thread
-  constexpr int NO = SUB * SPL;        // channel sums per group per sub-tile (= DS)
+  // SUB steps per sub-tile (the unit of the channel sums and the epilogue).
+  // Item (step tt of the tile, channel c) is staged, and finished in the
+  // epilogue, by thread (tt % G, c) as its item number tt / G; SUB divides G
+  // so the items of one sub-tile belong to one block of SUB state groups.
+  static_assert(L % SUB == 0 && G % SUB == 0 && L % G == 0, "sub-tiles, items");
+  constexpr int NSUB = L / SUB;        // sub-tiles per tile
+  constexpr int NIT = L / G;           // staged items per thread
+  constexpr int NO = SUB * SPL;        // channel sums per group per sub-tile
   static_assert(PD >= 1 && PD <= L, "operand look-ahead");
   constexpr int NOL = group_sum_outputs_per_lane<NO, CPW>();
   constexpr int KMAX = FUSED ? 4 : 1;  // conv taps supported: 1..4
@@ -123,8 +136,9 @@ scan_bwd_kernel(const BwdArgs p) {
   // epilogue (one barrier per sub-tile instead of two).
   constexpr int LDS_FIXED = (XR + 4 * TR) * RB + L * CPW * 16 + (FUSED ? (L + KMAX - 1) * CPW * 4 : 4) +
                             L * 2 * DS * 4 + G * CPW * (NO + 1) * 4 + (SUB + KMAX) * CPW * 4;
-  constexpr int PART = 2 * G * SUB * CPW * 4;
-  constexpr int NBUF = LDS_FIXED + 2 * PART <= 160 * 1024 ? 2 : 1;
+  constexpr int SPS = SUB * CPW + group_pad<CPW>(SUB * CPW);
+  constexpr int PART = 2 * G * SPS * 4;
+  constexpr int NBUF = LDS_FIXED + 2 * PART <= 52 * 1024 ? 2 : 1;   // 3 workgroups per CU
   using io = IO<A>;
 
   // raw tile: x (with halo) | delta_raw | dout | z | y
@@ -133,8 +147,10 @@ scan_bwd_kernel(const BwdArgs p) {
   __shared__ float4 s_st[L][CPW];      // delta, delta*u, dy, u
   __shared__ float s_x[FUSED ? L + KMAX - 1 : 1][CPW];
   __shared__ float s_bc[L][2][DS];
-  __shared__ float s_su[NBUF][G][SUB][CPW];   // per-group sum_n dh B
-  __shared__ float s_sd[NBUF][G][SUB][CPW];   // per-group sum_n dh A dA h_{t-1}
+  // per-group partials per (step of the sub-tile, channel), padded against
+  // bank conflicts
+  __shared__ float s_su[NBUF][G][SPS];   // per-group sum_n dh B
+  __shared__ float s_sd[NBUF][G][SPS];   // per-group sum_n dh A dA h_{t-1}
   __shared__ float s_red[G][CPW * (NO + 1)];
   __shared__ float s_dp[SUB + KMAX][CPW];
 
@@ -144,7 +160,9 @@ scan_bwd_kernel(const BwdArgs p) {
   const int wave = tid >> 6, lane = tid & 63;
   constexpr int NW = (NT + 63) / 64;
   const int64_t ngrp = (p.Di + CPW - 1) / CPW;
-  const int64_t wg = xcd_group_map<line_sharing_groups<ES, CPW>()>(blockIdx.x, ngrp * p.B);
+  const int64_t nwg = ngrp * p.B;
+  const int64_t seg = FUSED ? 0 : blockIdx.x / nwg;
+  const int64_t wg = xcd_group_map<line_sharing_groups<ES, CPW>()>(blockIdx.x % nwg, nwg);
   const int64_t b = wg / ngrp;
   const int64_t cg = wg % ngrp;
   const int64_t i0 = cg * CPW;
@@ -167,7 +185,14 @@ scan_bwd_kernel(const BwdArgs p) {
     const int n = g * SPL + s;
     an[s] = on ? -expf(p.a_log[i * DS + n]) : 0.0f;
     a2[s] = an[s] * kLog2e;
-    carry[s] = 0.0f;
+    float cv = 0.0f;
+    if (!FUSED && on) {
+      for (int64_t q = p.S - 1; q > seg; --q) {   // carry handed back by the later segments
+        const int64_t r = b * p.S + q;
+        cv = fmaf(exp2_fast(a2[s] * p.seg_sd[r * Di + i]), cv, p.seg_q[(r * Di + i) * DS + n]);
+      }
+    }
+    carry[s] = cv;
     dacc[s] = 0.0f;
   }
   const float Dv = (on && p.D) ? p.D[i] : 0.0f;
@@ -210,13 +235,15 @@ scan_bwd_kernel(const BwdArgs p) {
   };
 
   const int64_t ntiles = (T + L - 1) / L;
-  prefetch(ntiles - 1);
+  const int64_t kb = seg * p.seg_tiles;                               // this segment's tiles
+  const int64_t ke = kb + p.seg_tiles < ntiles ? kb + p.seg_tiles : ntiles;
+  prefetch(ke - 1);
 
-  for (int64_t kt = ntiles - 1; kt >= 0; --kt) {
+  for (int64_t kt = ke - 1; kt >= kb; --kt) {
     const int64_t t0 = kt * L;
     const int len = static_cast<int>(T - t0 < L ? T - t0 : L);
-    float e_sig[NSUB], e_dsp[NSUB];
-    uint32_t e_due[NSUB];
+    float e_sig[NIT], e_dsp[NIT];
+    uint32_t e_due[NIT];
     float h[SPL];
 
     // ---------------------------------------------------------------- stage
@@ -243,7 +270,7 @@ scan_bwd_kernel(const BwdArgs p) {
       __syncthreads();
     }
 #pragma unroll
-    for (int k = 0; k < NSUB; ++k) {
+    for (int k = 0; k < NIT; ++k) {
       const int tt = g + G * k;
       float dl = 0.0f, u = 0.0f, sig = 0.0f, dy = 0.0f, dsp = 0.0f;
       uint32_t due = 0;   // raw bits of d_u_extra (0 is +0.0 in every dtype)
@@ -281,7 +308,7 @@ scan_bwd_kernel(const BwdArgs p) {
       e_due[k] = due;
     }
     __syncthreads();
-    if (kt > 0) prefetch(kt - 1);
+    if (kt > kb) prefetch(kt - 1);
 
     // Step operands {delta, delta*u, dy, u} and this thread's B_t, C_t are
     // read PD steps before their step into a ring of registers (slot = steps
@@ -367,8 +394,8 @@ scan_bwd_kernel(const BwdArgs p) {
           sd = fmaf(qv, an[s], sd);
           red[c * (NO + 1) + q * SPL + s] = dh * cur.y;
         }
-        s_su[bi][g][q][c] = su;
-        s_sd[bi][g][q][c] = sd;
+        s_su[bi][g][q * CPW + c] = su;
+        s_sd[bi][g][q * CPW + c] = sd;
         __builtin_amdgcn_sched_barrier(0);
       }
       wave_lds_sync();
@@ -385,9 +412,13 @@ scan_bwd_kernel(const BwdArgs p) {
       }
       lds_barrier();
 
-      // ---- epilogue: item (t0 + sb*SUB + g, channel c); stage slot k = sb
-      const int tt = sb * SUB + g;
-      const bool live = tt < len && on;
+      // ---- epilogue: the sub-tile's items belong to state groups
+      // [gb, gb + SUB), item number kk; thread g finishes step q = g - gb
+      const int kk = sb * SUB / G, gb = sb * SUB % G;
+      const int q = g - gb;
+      const bool mine = q >= 0 && q < SUB;
+      const int tt = sb * SUB + q;
+      const bool live = mine && tt < len && on;
       const int64_t e = (row0 + t0 + tt) * Di + i;
       float dp = 0.0f;
       if (live) {
@@ -395,16 +426,16 @@ scan_bwd_kernel(const BwdArgs p) {
         float su = 0.0f, sd = 0.0f;
 #pragma unroll
         for (int w = 0; w < G; ++w) {
-          su += s_su[bi][w][g][c];
-          sd += s_sd[bi][w][g][c];
+          su += s_su[bi][w][q * CPW + c];
+          sd += s_sd[bi][w][q * CPW + c];
         }
         float du = fmaf(st.x, su, Dv * st.z);
         const float ddl = fmaf(st.w, su, sd);
-        io::st(p.d_delta_raw, e, ddl * e_sig[sb]);
+        io::st(p.d_delta_raw, e, ddl * e_sig[kk]);
         acc_dD = fmaf(st.z, st.w, acc_dD);
         if (FUSED) {
-          du += io::cvt(e_due[sb]);
-          dp = du * e_dsp[sb];
+          du += io::cvt(e_due[kk]);
+          dp = du * e_dsp[kk];
           acc_cb += dp;
 #pragma unroll
           for (int k2 = 0; k2 < KMAX; ++k2)
@@ -416,20 +447,20 @@ scan_bwd_kernel(const BwdArgs p) {
       if (FUSED) {
         // d_x[s] = sum_k w_k dp[s + K-1-k]; rows >= SUB of s_dp hold the
         // dp of the K-1 steps after this sub-tile (zero past the end)
-        s_dp[g][c] = dp;
+        if (mine) s_dp[q][c] = dp;
         lds_barrier();
         if (live) {
           float gx = 0.0f;
 #pragma unroll
           for (int k2 = 0; k2 < KMAX; ++k2)
-            if (k2 < K) gx = fmaf(cw[k2], s_dp[g + K - 1 - k2][c], gx);
+            if (k2 < K) gx = fmaf(cw[k2], s_dp[q + K - 1 - k2][c], gx);
           io::st(p.d_x, e, gx);
         }
         lds_barrier();
         // the K-1 steps after the next sub-tile: this sub-tile's first steps,
         // then (when SUB < K-1) older entries; descending keeps reads ahead
         // of writes
-        if (g == 0)
+        if (mine && q == 0)
           for (int j = K - 2; j >= 0; --j) s_dp[SUB + j][c] = s_dp[j][c];
       }
       if (NBUF == 1) lds_barrier();
@@ -438,7 +469,7 @@ scan_bwd_kernel(const BwdArgs p) {
   __syncthreads();
 
   // ------------------------------------------------ per batch-row partials
-  const int64_t pb = (b * Di + i) * p.PW;
+  const int64_t pb = ((seg * p.B + b) * Di + i) * p.PW;
   if (on) {
 #pragma unroll
     for (int s = 0; s < SPL; ++s) p.part_par[pb + g * SPL + s] = an[s] * dacc[s];
@@ -449,11 +480,11 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int k2 = 0; k2 < KMAX; ++k2)
       if (qd == k2 + 2) v = acc_cw[k2];
-    s_su[0][g][0][c] = v;
+    s_su[0][g][c] = v;
     __syncthreads();
     if (g == 0 && on) {
       float tot = 0.0f;
-      for (int w = 0; w < G; ++w) tot += s_su[0][w][0][c];
+      for (int w = 0; w < G; ++w) tot += s_su[0][w][c];
       // layout within PW: [Ds a_log | 1 D | K conv_w | 1 conv_b]
       const int slot = qd == 0 ? DS : (qd == 1 ? DS + 1 + K : DS + 1 + (qd - 2));
       p.part_par[pb + slot] = tot;
@@ -463,32 +494,35 @@ scan_bwd_kernel(const BwdArgs p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <Act A, int DS, int SPL, int L, int PD>
+template <Act A, int DS, int SPL, int L, int PD, int SUB>
 static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
   constexpr int G = DS / SPL;
   constexpr int CPW = kBwdCpw;
   const int64_t ng = (p.Di + CPW - 1) / CPW;
-  dim3 grid(static_cast<unsigned>(ng * p.B));
+  dim3 grid(static_cast<unsigned>(ng * p.B * (p.K > 0 ? 1 : p.S)));
   constexpr unsigned raw_fused = bwd_raw_bytes<A, L, true, CPW>();
   constexpr unsigned raw_plain = bwd_raw_bytes<A, L, false, CPW>();
   if (p.K > 0)
-    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true, CPW, PD>), grid, dim3(CPW * G), raw_fused, st, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true, CPW, PD, SUB>), grid, dim3(CPW * G), raw_fused, st, p);
   else
-    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false, CPW, PD>), grid, dim3(CPW * G), raw_plain, st, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false, CPW, PD, SUB>), grid, dim3(CPW * G), raw_plain, st, p);
   return hipGetLastError();
 }
 
+// main backward: one launch over all segments (the aggregate pass, when
+// S > 1, is enqueued before it by the caller)
 template <Act A>
 hipError_t launch_bwd_a(const BwdArgs& p, int ds, int L, hipStream_t st) {
-  // (d_state, checkpoint interval) -> states per thread, operand look-ahead.
-  // A thread keeps h_t and dA_t of its SPL states for all L steps of a tile
-  // in registers (2 * SPL * L of them); a workgroup must be whole waves.
-#define MSCAN_CASE(DS_, L_, SPL_, PD_) \
-  if (ds == DS_ && L == L_) return launch_bwd_t<A, DS_, SPL_, L_, PD_>(p, st);
-  MSCAN_CASE(4, 16, 1, 4) MSCAN_CASE(4, 32, 1, 4)
-  MSCAN_CASE(8, 16, 2, 4) MSCAN_CASE(8, 32, 2, 2)
-  MSCAN_CASE(16, 16, 2, 4) MSCAN_CASE(16, 32, 2, 2)
-  MSCAN_CASE(32, 16, 4, 2)
+  // (d_state, checkpoint interval) -> states per thread, operand look-ahead,
+  // sub-tile steps.  A thread keeps h_t and dA_t of its SPL states for all L
+  // steps of a tile in registers (2 * SPL * L of them); a workgroup must be
+  // whole waves.
+#define MSCAN_CASE(DS_, L_, SPL_, PD_, SUB_) \
+  if (ds == DS_ && L == L_) return launch_bwd_t<A, DS_, SPL_, L_, PD_, SUB_>(p, st);
+  MSCAN_CASE(4, 16, 1, 4, 4) MSCAN_CASE(4, 32, 1, 4, 4)
+  MSCAN_CASE(8, 16, 2, 4, 4) MSCAN_CASE(8, 32, 2, 2, 4)
+  MSCAN_CASE(16, 16, 2, 4, 8) MSCAN_CASE(16, 32, 2, 2, 8)
+  MSCAN_CASE(32, 16, 4, 2, 8)
 #undef MSCAN_CASE
   return hipErrorInvalidValue;
 }

@@ -115,6 +115,17 @@ __device__ __forceinline__ int64_t xcd_group_map(int64_t k, int64_t n) {
   return (j / Q) * (8 * Q) + Q * x + (j % Q);
 }
 
+// Padding (in floats) for an LDS array [group][stride] that the rows of a
+// wave (one row = CPW lanes = one state group) write at the same offset.
+// LDS serves 32 lanes (one per bank) at a time; with CPW = 16 two groups
+// share those 32 lanes, and a stride that is a multiple of 32 banks puts both
+// on the same 16 banks.  A 16-float pad moves every other group to the other
+// half of the banks.
+template <int CPW>
+constexpr int group_pad(int stride) {
+  return (CPW < 32 && stride % 32 == 0) ? 16 : 0;
+}
+
 // channel groups of CPW channels of ES-byte elements that share a 128-byte line
 template <int ES, int CPW>
 constexpr int line_sharing_groups() {
@@ -227,9 +238,14 @@ struct FwdArgs {
   float* h_last;            // [B,Di,Ds] or null
   float* conv_state_last;   // [B,Di,K] or null
   float* ckpt;              // [B,nC,Ds,Di] or null
+  // segmented schedule: segment s covers tiles [s * seg_tiles, ...) of TT steps
+  float* seg_h;             // [B,S,Di,Ds] end state of each segment scanned from zero
+  float* seg_sd;            // [B,S,Di] sum of delta over each segment
   int64_t B, T, Di, R, X, nC;
+  int64_t seg_tiles;        // tiles per segment
   int K;                    // conv taps, 0 = no conv
   int L;                    // checkpoint interval
+  int S;                    // segments
 };
 
 struct BwdArgs {
@@ -250,11 +266,30 @@ struct BwdArgs {
   void* d_delta_raw;        // [B,T,Di]
   void* d_z;                // [B,T,Di] (gate only)
   float* part_bc;           // [nG, B*T, 2*Ds]: per channel-group sums of d_B | d_C
-  float* part_par;          // [B, Di, PW]: per batch row d_a_log | d_D | d_conv_w | d_conv_b
+  float* part_par;          // [S, B, Di, PW]: per segment and batch row d_a_log | d_D | d_conv_w | d_conv_b
+  // segmented schedule: segment s covers tiles [s * seg_tiles, ...) of L steps
+  const float* seg_q;       // [B,S,Di,Ds] carry each segment hands to earlier steps, from a zero start
+  const float* seg_sd;      // [B,S,Di] sum of delta over each segment
   int64_t B, T, Di, R, X, nC;
+  int64_t seg_tiles;        // tiles per segment
   int K;
   int L;
   int PW;                   // Ds + 1 + K + 1 (conv terms only when K > 0)
+  int S;                    // segments (1 for the fused entry)
+};
+
+// aggregate pass of the segmented backward
+struct CarryArgs {
+  const void* delta_raw;    // [B,T,Di]
+  const float* a_log;       // [Di,Ds]
+  const void* xdbl;         // [B,T,X]
+  const void* z;            // [B,T,Di] or null
+  const void* dout;         // [B,T,Di]
+  float* seg_q;             // [B,S,Di,Ds] out
+  float* seg_sd;            // [B,S,Di] out
+  int64_t B, T, Di, R, X;
+  int64_t seg_steps;        // steps per segment (a multiple of 16)
+  int S;
 };
 
 struct ReduceArgs {
@@ -266,6 +301,7 @@ struct ReduceArgs {
   float* d_conv_w;          // [Di,K] += or null
   float* d_conv_b;          // [Di] += or null
   int64_t B, T, Di, Ds, R, X, nG;
+  int64_t par_rows;         // rows of part_par summed per element: segments * B
   int K;
   int PW;
 };

@@ -22,12 +22,19 @@
 //   output  : the staging threads add the partials of all groups, add D*u,
 //             apply the gate and write out (and y, u when asked).
 // The state entering every L-th step is written to ckpt for the backward.
+//
+// Segments.  The grid is S copies of the channel-group grid; copy s walks
+// tiles [s * seg_tiles, (s+1) * seg_tiles).  With AGG the kernel is the
+// aggregate pass: segments 0 .. S-2 are scanned from a zero state and only
+// their end state and sum of delta are kept.  The main pass then starts
+// segment s from h0 folded through the pairs of segments 0 .. s-1:
+//   h <- exp(A * sum delta) h + H      (exp of a sum = product of the dA).
 #pragma once
 #include "scan_common.h"
 
 namespace mscan {
 
-template <Act A, int DS, int SPL, int TT, int CPW, bool FUSED>
+template <Act A, int DS, int SPL, int TT, int CPW, bool FUSED, bool AGG>
 __global__ void __launch_bounds__(CPW * (DS / SPL))
 scan_fwd_kernel(const FwdArgs p) {
   constexpr int G = DS / SPL;          // state groups
@@ -54,7 +61,9 @@ scan_fwd_kernel(const FwdArgs p) {
   __shared__ __attribute__((aligned(16))) char s_raw1[RAW];
   __shared__ float2 s_st[TT][CPW];     // delta, delta*u
   __shared__ float s_bc[TT][2][DS];    // B_t | C_t as f32
-  __shared__ float s_yp[G][TT][CPW];   // per-state-group partial C.h
+  // per-state-group partial C.h per (t, channel), padded against bank conflicts
+  constexpr int YPS = TT * CPW + group_pad<CPW>(TT * CPW);
+  __shared__ float s_yp[G][YPS];
 
   const int tid = threadIdx.x;
   const int c = tid % CPW;             // channel within the group
@@ -62,7 +71,9 @@ scan_fwd_kernel(const FwdArgs p) {
   const int wave = tid >> 6, lane = tid & 63;
   constexpr int NW = (NT + 63) / 64;
   const int64_t ngrp = (p.Di + CPW - 1) / CPW;
-  const int64_t wg = xcd_group_map<line_sharing_groups<ES, CPW>()>(blockIdx.x, ngrp * p.B);
+  const int64_t nwg = ngrp * p.B;
+  const int64_t seg = blockIdx.x / nwg;
+  const int64_t wg = xcd_group_map<line_sharing_groups<ES, CPW>()>(blockIdx.x % nwg, nwg);
   const int64_t b = wg / ngrp;
   const int64_t i0 = (wg % ngrp) * CPW;
   const int64_t i = i0 + c;
@@ -70,14 +81,24 @@ scan_fwd_kernel(const FwdArgs p) {
   const int64_t T = p.T, Di = p.Di, row0 = b * p.T;
   const bool gate = p.z != nullptr;
   const int K = FUSED ? p.K : 0;
+  const int lshift = p.L == 32 ? 1 : 0;          // checkpoint every 1 << lshift tiles
+  const int64_t lmask = (int64_t(1) << lshift) - 1;
 
   float a2[SPL], h[SPL];
 #pragma unroll
   for (int s = 0; s < SPL; ++s) {
     const int n = gs * SPL + s;
     a2[s] = on ? -expf(p.a_log[i * DS + n]) * kLog2e : 0.0f;
-    h[s] = (on && p.h0) ? p.h0[(b * Di + i) * DS + n] : 0.0f;
+    float hv = (!AGG && on && p.h0) ? p.h0[(b * Di + i) * DS + n] : 0.0f;
+    if (!AGG && on) {
+      for (int64_t q = 0; q < seg; ++q) {
+        const int64_t r = b * p.S + q;
+        hv = fmaf(exp2_fast(a2[s] * p.seg_sd[r * Di + i]), hv, p.seg_h[(r * Di + i) * DS + n]);
+      }
+    }
+    h[s] = hv;
   }
+  float sd_acc = 0.0f;   // AGG: this thread's share of the segment's sum of delta
   const float Dv = (on && p.D) ? p.D[i] : 0.0f;
   float cw[KMAX];
   float cb = 0.0f;
@@ -148,6 +169,7 @@ scan_fwd_kernel(const FwdArgs p) {
         }
       }
       s_st[tt][c] = make_float2(dl, dl * u);
+      if (AGG) sd_acc += dl;
       e_u[k] = u;
       e_sz[k] = sz;
     }
@@ -161,7 +183,7 @@ scan_fwd_kernel(const FwdArgs p) {
       if (tt < len && on) {
         float y = Dv * e_u[k];
 #pragma unroll
-        for (int w = 0; w < G; ++w) y += s_yp[w][tt][c];
+        for (int w = 0; w < G; ++w) y += s_yp[w][tt * CPW + c];
         const int64_t e = (row0 + t0 + tt) * Di + i;
         io::st(p.out, e, gate ? y * e_sz[k] : y);
         if (p.y_save) io::st(p.y_save, e, y);
@@ -177,12 +199,14 @@ scan_fwd_kernel(const FwdArgs p) {
   // kt + 1 from (bcS, rawS), copies for tile kt + 2 into (bcP, rawP), the
   // buffers of tile kt, free once stage kt is done.
   const int64_t ntiles = (T + TT - 1) / TT;
+  const int64_t kb = seg * p.seg_tiles;                               // this segment's tiles
+  const int64_t ke = kb + p.seg_tiles < ntiles ? kb + p.seg_tiles : ntiles;
   auto tile = [&](int64_t kt, const uint32_t (&bcS)[BCPT], const char* rawS, uint32_t (&bcP)[BCPT],
                   char* rawP) {
     const int64_t t0 = kt * TT;
-    // ---- checkpoint: the state entering step t0 (TT divides L)
-    if (p.ckpt && on && (t0 % p.L) == 0) {
-      const int64_t cidx = t0 / p.L;
+    // ---- checkpoint: the state entering step t0 (TT divides L; L is 16 or 32)
+    if (!AGG && p.ckpt && on && (kt & lmask) == 0) {
+      const int64_t cidx = kt >> lshift;
 #pragma unroll
       for (int s = 0; s < SPL; ++s)
         p.ckpt[((b * p.nC + cidx) * DS + gs * SPL + s) * Di + i] = h[s];
@@ -222,29 +246,48 @@ scan_fwd_kernel(const FwdArgs p) {
         h[s] = fmaf(dA, h[s], st.y * bb[s]);
         yp = fmaf(cc[s], h[s], yp);
       }
-      s_yp[gs][tt][c] = yp;
+      if (!AGG) s_yp[gs][tt * CPW + c] = yp;
       __builtin_amdgcn_sched_barrier(0);
     }
     // the copies of tile kt + 1 are complete and visible to all waves
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 2 < ntiles) prefetch(kt + 2, bcP, rawP);
-    output(t0);
-    if (kt + 1 < ntiles) stage(kt + 1, bcS, rawS);
+    if (kt + 2 < ke) prefetch(kt + 2, bcP, rawP);
+    if (!AGG) output(t0);
+    if (kt + 1 < ke) stage(kt + 1, bcS, rawS);
     // LDS-only: the copies for tile kt + 2 stay in flight through scan kt + 1
     lds_barrier();
   };
 
-  prefetch(0, bc0, s_raw0);
-  if (ntiles > 1) prefetch(1, bc1, s_raw1);
+  prefetch(kb, bc0, s_raw0);
+  if (kb + 1 < ke) prefetch(kb + 1, bc1, s_raw1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  stage(0, bc0, s_raw0);
+  stage(kb, bc0, s_raw0);
   __syncthreads();
-  for (int64_t kt = 0; kt < ntiles; kt += 2) {
+  for (int64_t kt = kb; kt < ke; kt += 2) {
     tile(kt, bc1, s_raw1, bc0, s_raw0);
-    if (kt + 1 < ntiles) tile(kt + 1, bc0, s_raw0, bc1, s_raw1);
+    if (kt + 1 < ke) tile(kt + 1, bc0, s_raw0, bc1, s_raw1);
   }
+
+  if (AGG) {
+    // the segment's end state from zero, and its sum of delta (the partial
+    // sums of the state groups meet in LDS; s_yp is free here)
+    if (on) {
+      const int64_t r = b * p.S + seg;
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) p.seg_h[(r * Di + i) * DS + gs * SPL + s] = h[s];
+    }
+    s_yp[gs][c] = sd_acc;
+    __syncthreads();
+    if (gs == 0 && on) {
+      float tot = 0.0f;
+      for (int w = 0; w < G; ++w) tot += s_yp[w][c];
+      p.seg_sd[(b * p.S + seg) * Di + i] = tot;
+    }
+    return;
+  }
+  if (seg != p.S - 1) return;   // the last segment ends the sequence
 
   if (p.h_last && on) {
 #pragma unroll
@@ -264,13 +307,23 @@ scan_fwd_kernel(const FwdArgs p) {
 // ------------------------------------------------------------------ launch
 template <Act A, int DS, int SPL, int TT, int CPW>
 static hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t st) {
+  static_assert(TT == 16, "checkpoint tiles: L is 16 or 32");
   constexpr int G = DS / SPL;
-  const int64_t ng = (p.Di + CPW - 1) / CPW;
-  dim3 grid(static_cast<unsigned>(ng * p.B));
+  const int64_t nwg = (p.Di + CPW - 1) / CPW * p.B;
+  if (p.S > 1) {   // aggregate pass over segments 0 .. S-2
+    dim3 grid(static_cast<unsigned>(nwg * (p.S - 1)));
+    if (p.K > 0)
+      hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW, true, true>), grid, dim3(CPW * G), 0, st, p);
+    else
+      hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW, false, true>), grid, dim3(CPW * G), 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(static_cast<unsigned>(nwg * p.S));
   if (p.K > 0)
-    hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW, true>), grid, dim3(CPW * G), 0, st, p);
+    hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW, true, false>), grid, dim3(CPW * G), 0, st, p);
   else
-    hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW, false>), grid, dim3(CPW * G), 0, st, p);
+    hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW, false, false>), grid, dim3(CPW * G), 0, st, p);
   return hipGetLastError();
 }
 

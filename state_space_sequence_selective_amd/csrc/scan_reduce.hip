@@ -1,8 +1,8 @@
-// Fixed-order reduction of the backward's per-group / per-batch-row
-// partials into the caller's accumulated gradients (d_xdbl B/C columns,
-// d_a_log, d_D, d_conv_w, d_conv_b).  No atomics: every output element is
-// summed by one thread in ascending group / batch order, so repeated runs
-// give identical bits.
+// Fixed-order reduction of the backward's per-group / per-(segment, batch
+// row) partials into the caller's accumulated gradients (d_xdbl B/C
+// columns, d_a_log, d_D, d_conv_w, d_conv_b).  No atomics: every output
+// element is summed by one thread in ascending group / row order, so
+// repeated runs give identical bits.
 #include "scan_common.h"
 
 namespace mscan {
@@ -23,7 +23,7 @@ __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
   if (jp >= p.Di * p.PW) return;
   const int64_t i = jp / p.PW, slot = jp % p.PW;
   float acc = 0.0f;
-  for (int64_t b = 0; b < p.B; ++b) acc += p.part_par[(b * p.Di + i) * p.PW + slot];
+  for (int64_t rr = 0; rr < p.par_rows; ++rr) acc += p.part_par[(rr * p.Di + i) * p.PW + slot];
   if (slot < p.Ds) {
     p.d_a_log[i * p.Ds + slot] += acc;
   } else if (slot == p.Ds) {

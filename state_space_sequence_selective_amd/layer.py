@@ -1,7 +1,7 @@
 """One layer's device buffers around the C entry points.
 
 ``LayerCore`` owns the saved activations (y, checkpoints), the outputs and
-the backward workspace of one layer, allocated once, so that ``forward`` and
+the workspace of one layer, allocated once, so that ``forward`` and
 ``backward`` issue only kernel launches (no allocation on the hot path).
 """
 from __future__ import annotations
@@ -48,11 +48,12 @@ class LayerCore:
             _lib.conv_scan_gate_fwd(d, inp["x"], inp["conv_w"], inp.get("conv_b"), inp.get("conv_state0"),
                                     inp["delta_raw"], inp["a_log"], inp["xdbl"], inp.get("D"), z, inp.get("h0"),
                                     out=self.out, u_out=self.u_out, y_save=self.y, h_last=self.h_last,
-                                    conv_state_last=self.conv_state_last, ckpt=self.ckpt, stream=stream)
+                                    conv_state_last=self.conv_state_last, ckpt=self.ckpt,
+                                    workspace=self.workspace, stream=stream)
         else:
             _lib.scan_fwd(d, inp["x"], inp["delta_raw"], inp["a_log"], inp["xdbl"], inp.get("D"), z,
                           inp.get("h0"), out=self.out, y_save=self.y, h_last=self.h_last, ckpt=self.ckpt,
-                          stream=stream)
+                          workspace=self.workspace, stream=stream)
         return self.out
 
     def backward(self, inp: dict, dout, stream=None):

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(pkg):
 
 
 def test_abi_version(pkg):
-    assert pkg.abi_version() == 1
+    assert pkg.abi_version() == 2
 
 
 def _dims(pkg, **kw):
@@ -84,11 +84,35 @@ def test_bad_dims_rejected(pkg, kw, status, msg):
     assert msg in str(ei.value) and "mamba_ckpt_bytes" in str(ei.value)
 
 
-def test_reserved_must_be_zero(pkg):
-    d = _dims(pkg)
-    d.reserved = 1
-    with pytest.raises(pkg.MambaScanError, match="reserved"):
+@pytest.mark.parametrize("segments", [-1, 4097])
+def test_segments_range(pkg, segments):
+    d = _dims(pkg, segments=segments)
+    with pytest.raises(pkg.MambaScanError, match="segments") as ei:
         pkg.ckpt_bytes(d)
+    assert ei.value.status == 1
+
+
+def test_segmented_workspace_layout(pkg):
+    # B=1, T=1024, Di=64, Ds=16, L=16: 64 checkpoint tiles, 64 forward tiles;
+    # four segments each way
+    d = _dims(pkg, batch=1, seqlen=1024, chunk=16, segments=4)
+    al = lambda x: (x + 255) // 256 * 256
+    fwd = al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)                  # seg_h | seg_sd
+    bwd = (al(4 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4)          # part_bc | part_par (4 segments)
+           + al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4))              # seg_q | seg_sd
+    assert pkg.workspace_bytes(d) == max(fwd, bwd)
+    # a cap above the tile count gives one segment per tile
+    d = _dims(pkg, batch=1, seqlen=64, chunk=16, segments=4096)
+    fwd = al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
+    bwd = al(4 * 1 * 64 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
+    assert pkg.workspace_bytes(d) == max(fwd, bwd)
+    # the fused backward always runs one segment; its forward may split
+    d = _dims(pkg, batch=1, seqlen=1024, chunk=16, segments=4, d_conv=4)
+    fwd = al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
+    bwd_fused = al(4 * 1 * 1024 * 32 * 4) + al(1 * 64 * 22 * 4)
+    bwd_scan = (al(4 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4)
+                + al(1 * 4 * 64 * 4))
+    assert pkg.workspace_bytes(d) == max(fwd, bwd_fused, bwd_scan)
 
 
 def _raw(pkg):
@@ -101,15 +125,16 @@ def test_null_and_misaligned_pointers_rejected_before_launch(pkg):
     P = ctypes.c_void_p
     good = P(0x10000)           # never dereferenced: the call fails before any launch
     # u NULL
-    rc = lib.mamba_scan_fwd(ctypes.byref(d), None, good, good, good, None, None, None, good, None, None, None, None)
+    nows = (None, ctypes.c_size_t(0), None)   # workspace, its size, stream
+    rc = lib.mamba_scan_fwd(ctypes.byref(d), None, good, good, good, None, None, None, good, None, None, None, *nows)
     assert rc == 1 and "mamba_scan_fwd: u is NULL" == pkg.last_error()
     # out misaligned (bf16 needs 2-byte alignment)
     rc = lib.mamba_scan_fwd(ctypes.byref(d), good, good, good, good, None, None, None, P(0x10001), None, None,
-                            None, None)
+                            None, *nows)
     assert rc == 1 and "out is not 2-byte aligned" in pkg.last_error()
     # a_log misaligned (f32)
     rc = lib.mamba_scan_fwd(ctypes.byref(d), good, good, P(0x10002), good, None, None, None, good, None, None,
-                            None, None)
+                            None, *nows)
     assert rc == 1 and "a_log" in pkg.last_error()
     # backward: z given but y_saved missing
     args = [ctypes.byref(d), good, good, good, good, None, good, None, good, good, good, good, good, good, good,
@@ -121,9 +146,17 @@ def test_null_and_misaligned_pointers_rejected_before_launch(pkg):
             good, P(0x100000), ctypes.c_size_t(16), None]
     rc = lib.mamba_scan_bwd(*args)
     assert rc == 3 and "workspace_bytes" in pkg.last_error()
+    # a segmented forward needs its workspace
+    ds = _dims(pkg, batch=1, seqlen=1024, chunk=16, segments=4)
+    rc = lib.mamba_scan_fwd(ctypes.byref(ds), good, good, good, good, None, None, None, good, None, None, None,
+                            *nows)
+    assert rc == 1 and "mamba_scan_fwd: workspace is NULL" == pkg.last_error()
+    rc = lib.mamba_scan_fwd(ctypes.byref(ds), good, good, good, good, None, None, None, good, None, None, None,
+                            P(0x100000), ctypes.c_size_t(256), None)
+    assert rc == 3 and "workspace_bytes 256 < required" in pkg.last_error()
     # fused: d_conv out of range
     dc = _dims(pkg, d_conv=5)
-    rc = lib.mamba_conv_scan_gate_fwd(ctypes.byref(dc), *([good] * 17))
+    rc = lib.mamba_conv_scan_gate_fwd(ctypes.byref(dc), *([good] * 16), *nows)
     assert rc == 2 and "d_conv" in pkg.last_error()
     dc = _dims(pkg, d_conv=0)
     rc = lib.mamba_conv_scan_gate_bwd(ctypes.byref(dc), *([good] * 22), ctypes.c_size_t(1 << 30), None)

@@ -48,8 +48,8 @@ def _device_inputs(w, inp):
     return dev
 
 
-def _dims(m, w, chunk):
-    return m.Dims.make(w.batch, w.seqlen, w.d_inner, w.d_state, w.dt_rank, w.d_conv, chunk, w.act)
+def _dims(m, w, chunk, segments=0):
+    return m.Dims.make(w.batch, w.seqlen, w.d_inner, w.d_state, w.dt_rank, w.d_conv, chunk, w.act, segments)
 
 
 def _oracle(oracle_lib, w, inp, chunk, channels=None):
@@ -96,12 +96,13 @@ def _check(name, gpu, ora, half, report):
     assert e <= tol, "%s: error %.3e > %.1e" % (name, e, tol)
 
 
-def run_case(m, oracle_lib, w, seed=0, chunk=0, h0=False, conv_state0=False, d_u_extra=False, D=True):
+def run_case(m, oracle_lib, w, seed=0, chunk=0, h0=False, conv_state0=False, d_u_extra=False, D=True,
+             segments=0):
     inp = workloads.make_inputs(w, seed, h0=h0, conv_state0=conv_state0, d_u_extra=d_u_extra)
     if not D:
         inp["D"] = None
     dev = _device_inputs(w, inp)
-    dims = _dims(m, w, chunk)
+    dims = _dims(m, w, chunk, segments)
     core = m.LayerCore(dims, gate=w.gate, keep_u=True)
     core.zero_grads()
     core.forward(dev)
@@ -129,7 +130,7 @@ def run_case(m, oracle_lib, w, seed=0, chunk=0, h0=False, conv_state0=False, d_u
     _check("d_C", core.d_xdbl[..., R + Ds:], g["d_xdbl"][..., R + Ds:], False, rep)
     _check("d_a_log", core.d_a_log, g["d_a_log"], False, rep)
     _check("d_D", core.d_D, g["d_D"], False, rep)
-    print(w.name, "chunk", chunk, {k: "%.2e" % v for k, v in rep.items()}, flush=True)
+    print(w.name, "chunk", chunk, "segments", segments, {k: "%.2e" % v for k, v in rep.items()}, flush=True)
     return core, dev, inp, f, g
 
 
@@ -215,6 +216,52 @@ def test_accumulate_canaries_and_determinism(mscan, oracle_lib):
     assert torch.equal(core.d_xdbl, first["d_xdbl"])
 
 
+# ------------------------------------------------------- segmented schedule
+# T = 300 at L = 16: 19 tiles each way, so the last segment is short and
+# ends inside a tile; 19 segments is one tile per segment.
+
+
+@pytest.mark.parametrize("act,segments", [("f32", 2), ("f32", 7), ("bf16", 3), ("bf16", 19), ("f16", 5)])
+def test_segments_scan(mscan, oracle_lib, act, segments):
+    w = workloads.Workload("seg_" + act, 2, 300, 100, 16, 0, 0, act, True)
+    run_case(mscan, oracle_lib, w, chunk=16, h0=True, segments=segments)
+
+
+@pytest.mark.parametrize("ds,chunk", [(4, 16), (8, 32), (32, 16), (16, 32)])
+def test_segments_state_sizes(mscan, oracle_lib, ds, chunk):
+    w = workloads.Workload("seg_ds%d" % ds, 2, 260, 68, ds, 3, 0, "bf16", True)
+    run_case(mscan, oracle_lib, w, chunk=chunk, h0=True, segments=3)
+
+
+def test_segments_no_gate_tiny(mscan, oracle_lib):
+    run_case(mscan, oracle_lib, TINY, chunk=16, segments=4)      # one 16-step tile per segment
+
+
+def test_segments_fused(mscan, oracle_lib):
+    # the forward splits; the fused backward runs one segment
+    w = workloads.Workload("seg_fused", 2, 200, 68, 16, 5, 4, "bf16", True)
+    run_case(mscan, oracle_lib, w, chunk=16, h0=True, conv_state0=True, d_u_extra=True, segments=4)
+
+
+def test_segments_chosen_for_a_small_grid(mscan, oracle_lib):
+    # one batch row of 64 channels: 4 channel groups, so the library splits
+    # the 2048 steps into segments on its own
+    w = workloads.Workload("seg_auto", 1, 2048, 64, 16, 0, 0, "bf16", True)
+    run_case(mscan, oracle_lib, w, chunk=16, h0=True)
+
+
+def test_segments_deterministic(mscan, oracle_lib):
+    w = workloads.Workload("seg_det", 2, 300, 100, 16, 0, 0, "bf16", True)
+    core, dev, inp, f, g = run_case(mscan, oracle_lib, w, chunk=16, segments=5)
+    first = {k: getattr(core, k).clone() for k in ("out", "ckpt", "d_x", "d_delta_raw", "d_xdbl", "d_a_log")}
+    core.zero_grads()
+    core.forward(dev)
+    core.backward(dev, dev["dout"])
+    torch.cuda.synchronize()
+    for k, v in first.items():
+        assert torch.equal(getattr(core, k), v), k
+
+
 def test_state_carry_split_on_gpu(mscan, oracle_lib):
     """fwd(0..T) equals fwd(0..T1) then fwd(T1..T) with the carried states."""
     w = workloads.Workload("split", 2, 64, 64, 16, 0, 4, "f32", True)
@@ -265,14 +312,14 @@ def _sampled_full(mscan, oracle_lib, name, sample):
     w = workloads.CONFIGS[name]
     inp = workloads.make_inputs(w, 0)
     dev = _device_inputs(w, inp)
-    dims = _dims(mscan, w, 32)
+    dims = _dims(mscan, w, 16)           # the launch configuration bench.py times
     core = mscan.LayerCore(dims, gate=w.gate)
     core.zero_grads()
     core.forward(dev)
     core.backward(dev, dev["dout"])
     torch.cuda.synchronize()
     S = np.asarray(sample)
-    f, g = _oracle(oracle_lib, w, inp, 32, channels=S)
+    f, g = _oracle(oracle_lib, w, inp, 16, channels=S)
     rep = {}
     half = w.act != "f32"
     _check("out", core.out[..., S], f["out"], half, rep)
