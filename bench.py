@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="scan_2p8b_t8192_bf16", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--chunk", type=int, default=16)
+    ap.add_argument("--segments", type=int, default=0,
+                    help="cap on sequence segments scanned in parallel (0: chosen by the library)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -167,7 +169,8 @@ def main():
         if l > 0:
             inp = workloads.make_inputs(w, args.seed + l)
         dev = device_inputs(torch, w, inp)
-        dims = pkg.Dims.make(w.batch, w.seqlen, w.d_inner, w.d_state, w.dt_rank, w.d_conv, L, w.act)
+        dims = pkg.Dims.make(w.batch, w.seqlen, w.d_inner, w.d_state, w.dt_rank, w.d_conv, L, w.act,
+                             args.segments)
         layers.append((pkg.LayerCore(dims, gate=w.gate), dev))
     del inp
     stream = torch.cuda.current_stream()
@@ -237,7 +240,8 @@ def main():
         "data": "synthetic (seeded, distributions of the workload)",
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_inner": w.d_inner,
                    "d_state": w.d_state, "dt_rank": w.dt_rank, "d_conv": w.d_conv, "gate": w.gate,
-                   "layers": w.layers, "chunk": L, "parallelism": "single GPU"},
+                   "layers": w.layers, "chunk": L, "segments": args.segments or "auto",
+                   "parallelism": "single GPU"},
         "hbm_GBps": round(hbm_gbps, 1),
         "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
         "fwd_ms": round(fwd_ms, 4),

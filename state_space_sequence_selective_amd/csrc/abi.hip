@@ -73,17 +73,18 @@ struct Plan {
 constexpr int64_t kMaxElems = int64_t(1) << 46;
 constexpr int kMaxSegments = 4096;
 
-// Segment count for a schedule over `ntiles` tiles and `nwg` workgroups per
-// segment: the caller's cap `hint`, or enough segments for about `want`
-// workgroups, keeping at least `min_tiles` tiles per segment.  Returns the
-// count actually used (no empty segment) and the tiles per segment.
-void choose_segments(int hint, int64_t nwg, int64_t ntiles, int64_t want, int64_t min_tiles, int* S,
-                     int64_t* per) {
+// Segment count for a schedule over `ntiles` tiles with `waves` waves per
+// segment: the caller's cap `hint`; otherwise one segment when `waves`
+// reaches `enough`, else enough segments for about `want` waves, keeping at
+// least `min_tiles` tiles per segment.  Returns the count actually used (no
+// empty segment) and the tiles per segment.
+void choose_segments(int hint, int64_t waves, int64_t ntiles, int64_t enough, int64_t want, int64_t min_tiles,
+                     int* S, int64_t* per) {
   int64_t s = 1;
   if (hint > 0) {
     s = hint;
-  } else if (nwg < want) {
-    s = (want + nwg - 1) / nwg;
+  } else if (waves < enough) {
+    s = (want + waves - 1) / waves;
     const int64_t cap = ntiles / min_tiles;
     s = s < cap ? s : cap;
   }
@@ -93,11 +94,17 @@ void choose_segments(int hint, int64_t nwg, int64_t ntiles, int64_t want, int64_
   *S = static_cast<int>((ntiles + *per - 1) / *per);
 }
 
-// Workgroups that fill the GPU well: the forward has room for several per
-// CU; the backward balances best with several rounds of them (256 CUs).
-constexpr int64_t kWantFwdWorkgroups = 512;
-constexpr int64_t kWantBwdWorkgroups = 4096;
+// Waves that fill the GPU (1024 SIMDs).  The forward's aggregate pass costs
+// about 40% of a forward, so it splits only below 2 waves per SIMD; the
+// backward's costs about a fifth of a backward and always pays for itself
+// until about 8 waves per SIMD are queued.
+constexpr int64_t kFwdEnoughWaves = 2048;
+constexpr int64_t kWantWaves = 8192;
 constexpr int64_t kMinSegmentTiles = 8;
+
+// threads per workgroup of the forward / backward kernels (their launch tables)
+int64_t fwd_threads(int64_t ds) { return mscan::kFwdCpw * (ds == 32 ? ds / 2 : ds); }
+int64_t bwd_threads(int64_t ds) { return mscan::kBwdCpw * (ds == 4 ? 4 : ds == 8 ? 4 : 8); }
 
 int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   if (!d) return fail(MAMBA_ERR_INVALID, fn, "dims is NULL");
@@ -143,15 +150,17 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   pl->act = static_cast<mscan::Act>(d->act);
   pl->esize = d->act == MAMBA_F32 ? 4 : 2;
   pl->bulk_align = d->act == MAMBA_F32 ? 16 : 4;
-  const int64_t nwg_f = (d->d_inner + mscan::kFwdCpw - 1) / mscan::kFwdCpw * d->batch;
-  const int64_t nwg_b = pl->nG * d->batch;
-  choose_segments(d->segments, nwg_f, (d->seqlen + 15) / 16, kWantFwdWorkgroups, kMinSegmentTiles, &pl->Sf,
-                  &pl->segf_tiles);
+  const int64_t waves_f = (d->d_inner + mscan::kFwdCpw - 1) / mscan::kFwdCpw * d->batch *
+                          (fwd_threads(d->d_state) / 64);
+  const int64_t waves_b = pl->nG * d->batch * (bwd_threads(d->d_state) / 64);
+  choose_segments(d->segments, waves_f, (d->seqlen + 15) / 16, kFwdEnoughWaves, kWantWaves, kMinSegmentTiles,
+                  &pl->Sf, &pl->segf_tiles);
   if (fused) {   // the conv backward of a segment's tail needs the next segment's head
     pl->Sb = 1;
     pl->segb_tiles = pl->nC;
   } else {
-    choose_segments(d->segments, nwg_b, pl->nC, kWantBwdWorkgroups, kMinSegmentTiles, &pl->Sb, &pl->segb_tiles);
+    choose_segments(d->segments, waves_b, pl->nC, kWantWaves, kWantWaves, kMinSegmentTiles, &pl->Sb,
+                    &pl->segb_tiles);
   }
   return MAMBA_OK;
 }
