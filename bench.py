@@ -216,11 +216,12 @@ def main():
     elems = w.batch * w.seqlen * w.d_inner * w.d_state
     step_bytes = (fb + bb) * w.layers
     hbm_gbps = step_bytes / (ms_step / 1e3) / 1e9
-    # dominant kernel: the backward entry (scan_bwd_kernel + its fixed-order reduce)
+    # dominant kernel: the backward entry (segment carry pass when segmented,
+    # scan_bwd_kernel, and its fixed-order reduce)
     bwd_tflops = elems * FLOPS_BWD_ELEM / (bwd_ms / 1e3) / 1e12
     roofline = {"bound": "alu", "achieved": round(bwd_tflops, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(bwd_tflops / VALU_PEAK_TFLOPS, 4), "traffic": measured_traffic(w.name),
-                "kernel": "mamba_scan_bwd (scan_bwd_kernel + mscan_reduce_kernel), layer 0",
+                "kernel": "mamba_scan_bwd (scan_bwd_carry_kernel + scan_bwd_kernel + mscan_reduce_kernel), layer 0",
                 "launch_ms": round(bwd_ms, 4),
                 "algorithmic_flops_per_launch": elems * FLOPS_BWD_ELEM,
                 "algorithmic_bytes_per_launch": bb,

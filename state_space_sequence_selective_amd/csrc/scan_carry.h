@@ -34,8 +34,7 @@ scan_bwd_carry_kernel(const CarryArgs p) {
   constexpr int RPI = rows_per_inst<ES, CPW>();
   constexpr int TR = round_up(TT, RPI);
   constexpr int NCV = TT * DS;         // C values per tile
-  static_assert(NCV % NT == 0, "C values spread evenly over the threads");
-  constexpr int CPT = NCV / NT;
+  constexpr int CPT = (NCV + NT - 1) / NT;
   using io = IO<A>;
 
   __shared__ __attribute__((aligned(16))) char s_raw[3 * TR * RB];   // delta_raw | dout | z
@@ -85,7 +84,7 @@ scan_bwd_carry_kernel(const CarryArgs p) {
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int j = tid + q * NT;
-      const int tt = j / DS, n = j % DS;
+      const int tt = (j < NCV ? j : NCV - 1) / DS, n = j % DS;
       const int64_t t = t0 + tt < T ? t0 + tt : T - 1;   // rows past the end: zeroed in the stage
       cbits[q] = io::ldraw(p.xdbl, (row0 + t) * p.X + p.R + DS + n);
     }
@@ -100,7 +99,7 @@ scan_bwd_carry_kernel(const CarryArgs p) {
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int j = tid + q * NT;
-      (&s_c[0][0])[j] = j / DS < len ? io::cvt(cbits[q]) : 0.0f;
+      if (NCV % NT == 0 || j < NCV) (&s_c[0][0])[j] = j / DS < len ? io::cvt(cbits[q]) : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
