@@ -100,9 +100,9 @@ typedef enum mamba_status {
 typedef struct mamba_dims {
   int64_t batch;    /* B, 1 .. 65535 */
   int64_t seqlen;   /* T >= 1 */
-  int64_t d_inner;  /* Di >= 4, a multiple of 4 (the pages' MambaConfig rule) */
+  int64_t d_inner;  /* Di >= 4, a multiple of 4 (the pages' MambaConfig rule), <= 2^24 */
   int64_t d_state;  /* Ds in {4, 8, 16, 32} */
-  int64_t dt_rank;  /* R >= 0: xdbl row = [dt (R) | B (Ds) | C (Ds)] */
+  int64_t dt_rank;  /* R in 0 .. 2^24: xdbl row = [dt (R) | B (Ds) | C (Ds)] */
   int32_t d_conv;   /* K in 1..4 for the fused entry points; ignored by mamba_scan_* */
   int32_t chunk;    /* checkpoint interval L in {16, 32}; 0 = 16.  The
                        backward holds L steps of state in registers, so

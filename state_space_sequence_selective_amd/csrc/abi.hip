@@ -71,6 +71,7 @@ struct Plan {
 };
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;
+constexpr int64_t kMaxWidth = int64_t(1) << 24;
 constexpr int kMaxSegments = 4096;
 
 // Segment count for a schedule over `ntiles` tiles with `waves` waves per
@@ -116,7 +117,10 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   if (d->seqlen < 1) return fail(MAMBA_ERR_INVALID, fn, "seqlen must be >= 1");
   if (d->d_inner < 4 || d->d_inner % 4 != 0)
     return fail(MAMBA_ERR_INVALID, fn, "d_inner must be a positive multiple of 4");
+  if (d->d_inner > kMaxWidth)   // per-tile offsets (step * d_inner) are 32-bit in the kernels
+    return fail(MAMBA_ERR_CAPACITY, fn, "d_inner must be <= 2^24");
   if (d->dt_rank < 0) return fail(MAMBA_ERR_INVALID, fn, "dt_rank must be >= 0");
+  if (d->dt_rank > kMaxWidth) return fail(MAMBA_ERR_CAPACITY, fn, "dt_rank must be <= 2^24");
   if (d->d_state < 1) return fail(MAMBA_ERR_INVALID, fn, "d_state must be >= 1");
   if (d->d_state != 4 && d->d_state != 8 && d->d_state != 16 && d->d_state != 32)
     return fail(MAMBA_ERR_UNSUPPORTED, fn, "d_state must be 4, 8, 16 or 32");

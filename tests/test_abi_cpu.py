@@ -73,6 +73,8 @@ def test_sizes(pkg):
     (dict(chunk=64), 2, "chunk"),
     (dict(d_state=32, chunk=32), 2, "chunk"),
     (dict(dt_rank=-1), 1, "dt_rank"),
+    (dict(dt_rank=(1 << 24) + 1), 3, "dt_rank"),
+    (dict(d_inner=(1 << 24) + 4), 3, "d_inner"),
     (dict(act=5), 1, "act"),
     (dict(seqlen=1 << 40), 3, "2^46"),
 ])
