@@ -105,7 +105,10 @@ constexpr int64_t kMinSegmentTiles = 8;
 
 // threads per workgroup of the forward / backward kernels (their launch tables)
 int64_t fwd_threads(int64_t ds) { return mscan::kFwdCpw * (ds == 32 ? ds / 2 : ds); }
-int64_t bwd_threads(int64_t ds) { return mscan::kBwdCpw * (ds == 4 ? 4 : ds == 8 ? 4 : 8); }
+int64_t bwd_threads(int64_t ds, int L) {
+  const int64_t spl = ds == 4 ? 1 : ds == 8 ? (L == 32 ? 1 : 2) : ds == 16 ? (L == 32 ? 1 : 2) : 2;
+  return mscan::kBwdCpw * (ds / spl);
+}
 
 int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   if (!d) return fail(MAMBA_ERR_INVALID, fn, "dims is NULL");
@@ -156,7 +159,7 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   pl->bulk_align = d->act == MAMBA_F32 ? 16 : 4;
   const int64_t waves_f = (d->d_inner + mscan::kFwdCpw - 1) / mscan::kFwdCpw * d->batch *
                           (fwd_threads(d->d_state) / 64);
-  const int64_t waves_b = pl->nG * d->batch * (bwd_threads(d->d_state) / 64);
+  const int64_t waves_b = pl->nG * d->batch * (bwd_threads(d->d_state, L) / 64);
   choose_segments(d->segments, waves_f, (d->seqlen + 15) / 16, kFwdEnoughWaves, kWantWaves, kMinSegmentTiles,
                   &pl->Sf, &pl->segf_tiles);
   if (fused) {   // the conv backward of a segment's tail needs the next segment's head

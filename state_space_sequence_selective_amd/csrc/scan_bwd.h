@@ -519,10 +519,10 @@ hipError_t launch_bwd_a(const BwdArgs& p, int ds, int L, hipStream_t st) {
   // whole waves.
 #define MSCAN_CASE(DS_, L_, SPL_, PD_, SUB_) \
   if (ds == DS_ && L == L_) return launch_bwd_t<A, DS_, SPL_, L_, PD_, SUB_>(p, st);
-  MSCAN_CASE(4, 16, 1, 4, 4) MSCAN_CASE(4, 32, 1, 4, 4)
-  MSCAN_CASE(8, 16, 2, 4, 4) MSCAN_CASE(8, 32, 2, 2, 4)
-  MSCAN_CASE(16, 16, 2, 4, 8) MSCAN_CASE(16, 32, 2, 2, 8)
-  MSCAN_CASE(32, 16, 4, 2, 8)
+  MSCAN_CASE(4, 16, 1, 4, 4) MSCAN_CASE(4, 32, 1, 1, 4)
+  MSCAN_CASE(8, 16, 2, 4, 4) MSCAN_CASE(8, 32, 1, 4, 8)
+  MSCAN_CASE(16, 16, 2, 4, 8) MSCAN_CASE(16, 32, 1, 4, 8)
+  MSCAN_CASE(32, 16, 2, 4, 8)
 #undef MSCAN_CASE
   return hipErrorInvalidValue;
 }
