@@ -12,12 +12,13 @@ enum class Act : int { F32 = 0, BF16 = 1, F16 = 2 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Channels per workgroup.  A thread is (state group, channel): with 16
-// channels a wave holds 16 channels x 4 state groups.  Small workgroups give
-// many of them per CU (2 to 3 at the long-sequence 2.8B layer shape), which
-// evens out the load across SIMDs better than few large ones.
+// Channels per workgroup.  A thread is (state group, channel).  The forward
+// uses 16 channels (a wave = 16 channels x 4 state groups): small workgroups
+// give 2 to 3 per CU at the long-sequence 2.8B layer shape, which evens the
+// load across SIMDs.  The backward balances through sequence segments
+// instead and uses 32 channels, which halves its per-group d_B/d_C partials.
 constexpr int kFwdCpw = 16;
-constexpr int kBwdCpw = 16;
+constexpr int kBwdCpw = 32;
 
 // ---------------------------------------------------------------- dtype I/O
 template <Act A>

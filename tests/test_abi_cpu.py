@@ -51,12 +51,12 @@ def _dims(pkg, **kw):
 def test_sizes(pkg):
     d = _dims(pkg)
     assert pkg.ckpt_bytes(d) == 2 * 4 * 16 * 64 * 4            # ceil(100/32) = 4 checkpoints
-    # per-group d_B|d_C partials (groups of 16 channels: 4) padded to 256 B,
+    # per-group d_B|d_C partials (groups of 32 channels: 2) padded to 256 B,
     # then per-row param partials
-    bc = 4 * 2 * 100 * 32 * 4
+    bc = 2 * 2 * 100 * 32 * 4
     assert pkg.workspace_bytes(d) == ((bc + 255) // 256) * 256 + 2 * 64 * 17 * 4
     dc = _dims(pkg, d_conv=4, d_inner=128)
-    bc = 8 * 2 * 100 * 32 * 4
+    bc = 4 * 2 * 100 * 32 * 4
     assert pkg.workspace_bytes(dc) == ((bc + 255) // 256) * 256 + 2 * 128 * 22 * 4
 
 
@@ -100,19 +100,19 @@ def test_segmented_workspace_layout(pkg):
     d = _dims(pkg, batch=1, seqlen=1024, chunk=16, segments=4)
     al = lambda x: (x + 255) // 256 * 256
     fwd = al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)                  # seg_h | seg_sd
-    bwd = (al(4 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4)          # part_bc | part_par (4 segments)
+    bwd = (al(2 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4)          # part_bc | part_par (4 segments)
            + al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4))              # seg_q | seg_sd
     assert pkg.workspace_bytes(d) == max(fwd, bwd)
     # a cap above the tile count gives one segment per tile
     d = _dims(pkg, batch=1, seqlen=64, chunk=16, segments=4096)
     fwd = al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
-    bwd = al(4 * 1 * 64 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
+    bwd = al(2 * 1 * 64 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
     assert pkg.workspace_bytes(d) == max(fwd, bwd)
     # the fused backward always runs one segment; its forward may split
     d = _dims(pkg, batch=1, seqlen=1024, chunk=16, segments=4, d_conv=4)
     fwd = al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
-    bwd_fused = al(4 * 1 * 1024 * 32 * 4) + al(1 * 64 * 22 * 4)
-    bwd_scan = (al(4 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4)
+    bwd_fused = al(2 * 1 * 1024 * 32 * 4) + al(1 * 64 * 22 * 4)
+    bwd_scan = (al(2 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4)
                 + al(1 * 4 * 64 * 4))
     assert pkg.workspace_bytes(d) == max(fwd, bwd_fused, bwd_scan)
 
