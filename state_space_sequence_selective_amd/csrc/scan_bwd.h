@@ -106,8 +106,10 @@ constexpr int bwd_raw_bytes() {
   return (round_up(L + (FUSED ? 3 : 0), RPI) + 4 * round_up(L, RPI)) * CPW * ES;
 }
 
-template <Act A, int DS, int SPL, int L, bool FUSED, int CPW, int PD, int SUB>
-__global__ void __launch_bounds__(CPW * (DS / SPL))
+// WPE: waves per SIMD the register allocation must allow (the compiler
+// keeps the kernel within 512 / WPE registers).
+template <Act A, int DS, int SPL, int L, bool FUSED, int CPW, int PD, int SUB, int WPE>
+__global__ void __launch_bounds__(CPW * (DS / SPL)) __attribute__((amdgpu_waves_per_eu(WPE)))
 scan_bwd_kernel(const BwdArgs p) {
   constexpr int G = DS / SPL;          // state groups
   constexpr int NT = CPW * G;          // threads: (state group, channel)
@@ -494,7 +496,7 @@ scan_bwd_kernel(const BwdArgs p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <Act A, int DS, int SPL, int L, int PD, int SUB>
+template <Act A, int DS, int SPL, int L, int SUB, int PD, int WPE, int PD_FUSED, int WPE_FUSED>
 static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
   constexpr int G = DS / SPL;
   constexpr int CPW = kBwdCpw;
@@ -503,9 +505,11 @@ static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
   constexpr unsigned raw_fused = bwd_raw_bytes<A, L, true, CPW>();
   constexpr unsigned raw_plain = bwd_raw_bytes<A, L, false, CPW>();
   if (p.K > 0)
-    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true, CPW, PD, SUB>), grid, dim3(CPW * G), raw_fused, st, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, true, CPW, PD_FUSED, SUB, WPE_FUSED>), grid, dim3(CPW * G),
+                       raw_fused, st, p);
   else
-    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false, CPW, PD, SUB>), grid, dim3(CPW * G), raw_plain, st, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<A, DS, SPL, L, false, CPW, PD, SUB, WPE>), grid, dim3(CPW * G), raw_plain,
+                       st, p);
   return hipGetLastError();
 }
 
@@ -513,16 +517,19 @@ static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
 // S > 1, is enqueued before it by the caller)
 template <Act A>
 hipError_t launch_bwd_a(const BwdArgs& p, int ds, int L, hipStream_t st) {
-  // (d_state, checkpoint interval) -> states per thread, operand look-ahead,
-  // sub-tile steps.  A thread keeps h_t and dA_t of its SPL states for all L
+  // (d_state, checkpoint interval) -> states per thread, sub-tile steps, then
+  // operand look-ahead and waves per SIMD for the scan entry and for the
+  // fused entry.  A thread keeps h_t and dA_t of its SPL states for all L
   // steps of a tile in registers (2 * SPL * L of them); a workgroup must be
-  // whole waves.
-#define MSCAN_CASE(DS_, L_, SPL_, PD_, SUB_) \
-  if (ds == DS_ && L == L_) return launch_bwd_t<A, DS_, SPL_, L_, PD_, SUB_>(p, st);
-  MSCAN_CASE(4, 16, 1, 4, 4) MSCAN_CASE(4, 32, 1, 1, 4)
-  MSCAN_CASE(8, 16, 2, 4, 4) MSCAN_CASE(8, 32, 1, 4, 8)
-  MSCAN_CASE(16, 16, 2, 4, 8) MSCAN_CASE(16, 32, 1, 4, 8)
-  MSCAN_CASE(32, 16, 2, 4, 8)
+  // whole waves.  Three waves per SIMD hide the LDS and barrier waits best
+  // (measured: T=8192 backward 2.04 -> 1.81 ms) where the registers allow
+  // it without spilling (168 or fewer: the look-ahead is shortened to fit).
+#define MSCAN_CASE(DS_, L_, SPL_, SUB_, PD_, W_, PDF_, WF_) \
+  if (ds == DS_ && L == L_) return launch_bwd_t<A, DS_, SPL_, L_, SUB_, PD_, W_, PDF_, WF_>(p, st);
+  MSCAN_CASE(4, 16, 1, 4, 4, 3, 4, 2) MSCAN_CASE(4, 32, 1, 4, 1, 2, 1, 2)
+  MSCAN_CASE(8, 16, 2, 4, 4, 2, 4, 2) MSCAN_CASE(8, 32, 1, 8, 4, 2, 4, 2)
+  MSCAN_CASE(16, 16, 2, 8, 1, 3, 4, 2) MSCAN_CASE(16, 32, 1, 8, 4, 2, 4, 2)
+  MSCAN_CASE(32, 16, 2, 8, 4, 2, 4, 2)
 #undef MSCAN_CASE
   return hipErrorInvalidValue;
 }
