@@ -67,7 +67,8 @@ struct Plan {
   int esize;      // bytes per activation element
   int bulk_align; // alignment of activation inputs staged with 4 / 16-byte granules
   int Sf, Sb;     // segments of the forward / backward schedule
-  int64_t segf_tiles, segb_tiles;   // 16-step tiles per forward segment, L-step tiles per backward one
+  int fwd_tile;   // steps per forward tile
+  int64_t segf_tiles, segb_tiles;   // fwd_tile-step tiles per forward segment, L-step tiles per backward one
 };
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;
@@ -160,8 +161,13 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   const int64_t waves_f = (d->d_inner + mscan::kFwdCpw - 1) / mscan::kFwdCpw * d->batch *
                           (fwd_threads(d->d_state) / 64);
   const int64_t waves_b = pl->nG * d->batch * (bwd_threads(d->d_state, L) / 64);
-  choose_segments(d->segments, waves_f, (d->seqlen + 15) / 16, kFwdEnoughWaves, kWantWaves, kMinSegmentTiles,
-                  &pl->Sf, &pl->segf_tiles);
+  choose_segments(d->segments, waves_f, (d->seqlen + mscan::kFwdTileShort - 1) / mscan::kFwdTileShort,
+                  kFwdEnoughWaves, kWantWaves, kMinSegmentTiles, &pl->Sf, &pl->segf_tiles);
+  pl->fwd_tile = mscan::kFwdTileShort;
+  if (pl->Sf == 1) {
+    pl->fwd_tile = mscan::kFwdTileLong;
+    pl->segf_tiles = (d->seqlen + mscan::kFwdTileLong - 1) / mscan::kFwdTileLong;
+  }
   if (fused) {   // the conv backward of a segment's tail needs the next segment's head
     pl->Sb = 1;
     pl->segb_tiles = pl->nC;
@@ -277,6 +283,7 @@ int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_
   a.L = pl.L;
   a.S = pl.Sf;
   a.seg_tiles = pl.segf_tiles;
+  a.tile = pl.fwd_tile;
   if (pl.Sf > 1) {
     a.seg_h = static_cast<float*>(workspace);
     a.seg_sd = reinterpret_cast<float*>(static_cast<char*>(workspace) + seg_state_bytes(pl, pl.Sf));

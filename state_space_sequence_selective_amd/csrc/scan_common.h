@@ -20,6 +20,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kFwdCpw = 16;
 constexpr int kBwdCpw = 32;
 
+// Steps per forward tile.  An unsegmented forward (few waves per SIMD) uses
+// long tiles, which halve the per-tile overheads; a segmented one has many
+// waves queued and uses short tiles, whose half-size LDS footprint fits
+// twice as many workgroups per CU.  Checkpoints (every 16 or 32 steps) fall
+// on 16-step boundaries inside a tile.
+constexpr int kFwdTileLong = 32;
+constexpr int kFwdTileShort = 16;
+
 // ---------------------------------------------------------------- dtype I/O
 template <Act A>
 struct IO;
@@ -247,6 +255,7 @@ struct FwdArgs {
   int K;                    // conv taps, 0 = no conv
   int L;                    // checkpoint interval
   int S;                    // segments
+  int tile;                 // steps per tile: kFwdTileLong (S == 1) or kFwdTileShort
 };
 
 struct BwdArgs {

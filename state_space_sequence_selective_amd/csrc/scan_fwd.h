@@ -81,7 +81,7 @@ scan_fwd_kernel(const FwdArgs p) {
   const int64_t T = p.T, Di = p.Di, row0 = b * p.T;
   const bool gate = p.z != nullptr;
   const int K = FUSED ? p.K : 0;
-  const int lshift = p.L == 32 ? 1 : 0;          // checkpoint every 1 << lshift tiles
+  const int lshift = p.L == 32 ? 5 : 4;          // checkpoint interval 1 << lshift steps
   const int64_t lmask = (int64_t(1) << lshift) - 1;
 
   float a2[SPL], h[SPL];
@@ -204,13 +204,6 @@ scan_fwd_kernel(const FwdArgs p) {
   auto tile = [&](int64_t kt, const uint32_t (&bcS)[BCPT], const char* rawS, uint32_t (&bcP)[BCPT],
                   char* rawP) {
     const int64_t t0 = kt * TT;
-    // ---- checkpoint: the state entering step t0 (TT divides L; L is 16 or 32)
-    if (!AGG && p.ckpt && on && (kt & lmask) == 0) {
-      const int64_t cidx = kt >> lshift;
-#pragma unroll
-      for (int s = 0; s < SPL; ++s)
-        p.ckpt[((b * p.nC + cidx) * DS + gs * SPL + s) * Di + i] = h[s];
-    }
 
     // ---- scan (steps past the end of the sequence see delta = 0, B = C = 0:
     // identities that leave h unchanged).  Operands of step tt sit in ring
@@ -230,6 +223,17 @@ scan_fwd_kernel(const FwdArgs p) {
     for (int d = 0; d < PD; ++d) operands(d, d);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
+      // checkpoint: the state entering step t0 + tt, every L steps (L is 16
+      // or 32, so only 16-step boundaries can hold one)
+      if (!AGG && tt % 16 == 0 && p.ckpt && on) {
+        const int64_t ts = t0 + tt;
+        if ((ts & lmask) == 0 && ts < T) {
+          const int64_t cidx = ts >> lshift;
+#pragma unroll
+          for (int s = 0; s < SPL; ++s)
+            p.ckpt[((b * p.nC + cidx) * DS + gs * SPL + s) * Di + i] = h[s];
+        }
+      }
       const int sl = tt % PD;
       const float2 st = q_st[sl];
       float bb[SPL], cc[SPL];
@@ -307,10 +311,10 @@ scan_fwd_kernel(const FwdArgs p) {
 // ------------------------------------------------------------------ launch
 template <Act A, int DS, int SPL, int TT, int CPW>
 static hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t st) {
-  static_assert(TT == 16, "checkpoint tiles: L is 16 or 32");
+  static_assert(TT % 16 == 0, "checkpoints fall on 16-step boundaries");
   constexpr int G = DS / SPL;
   const int64_t nwg = (p.Di + CPW - 1) / CPW * p.B;
-  if (p.S > 1) {   // aggregate pass over segments 0 .. S-2
+  if constexpr (TT == kFwdTileShort) if (p.S > 1) {   // aggregate pass over segments 0 .. S-2
     dim3 grid(static_cast<unsigned>(nwg * (p.S - 1)));
     if (p.K > 0)
       hipLaunchKernelGGL((scan_fwd_kernel<A, DS, SPL, TT, CPW, true, true>), grid, dim3(CPW * G), 0, st, p);
@@ -329,9 +333,14 @@ static hipError_t launch_fwd_t(const FwdArgs& p, hipStream_t st) {
 
 template <Act A>
 hipError_t launch_fwd_a(const FwdArgs& p, int ds, int spl, hipStream_t st) {
-  // channel groups of kFwdCpw; tiles of 16 steps
-#define MSCAN_CASE(DS_, SPL_) \
-  if (ds == DS_ && spl == SPL_) return launch_fwd_t<A, DS_, SPL_, 16, kFwdCpw>(p, st);
+  // channel groups of kFwdCpw; long tiles only without segments
+#define MSCAN_CASE(DS_, SPL_)                                                       \
+  if (ds == DS_ && spl == SPL_) {                                                   \
+    if (p.tile == kFwdTileLong && p.S == 1)                                         \
+      return launch_fwd_t<A, DS_, SPL_, kFwdTileLong, kFwdCpw>(p, st);              \
+    if (p.tile == kFwdTileShort) return launch_fwd_t<A, DS_, SPL_, kFwdTileShort, kFwdCpw>(p, st); \
+    return hipErrorInvalidValue;                                                    \
+  }
   MSCAN_CASE(4, 1) MSCAN_CASE(8, 1) MSCAN_CASE(16, 1) MSCAN_CASE(32, 2)
 #undef MSCAN_CASE
   return hipErrorInvalidValue;
