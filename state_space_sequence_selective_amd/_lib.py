@@ -124,40 +124,57 @@ def ckpt_shape(dims: Dims):
 
 
 def _ptr(t, name, dtype, shape, required=False):
+    """Device address of ``t`` after checking it (None passes as NULL unless required).
+
+    The common case is one conjunction of cheap attribute tests; the specific
+    error is worked out only when it fails (a recurrent step calls this for
+    every tensor on every call)."""
     if t is None:
         if required:
             raise ValueError("%s is required" % name)
         return None
+    if isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and t.shape == shape and t.is_contiguous():
+        return t.data_ptr()
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.device.type != "cuda":
         raise ValueError("%s must be a device tensor, got %s" % (name, t.device))
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
     if tuple(t.shape) != tuple(shape):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
-    return ctypes.c_void_p(t.data_ptr())
+    raise ValueError("%s must be contiguous" % name)
 
 
 def _workspace(workspace):
     if workspace is None:
-        return None, ctypes.c_size_t(0)
-    return _ptr(workspace, "workspace", torch.uint8, (workspace.numel(),), True), ctypes.c_size_t(workspace.numel())
+        return None, 0
+    n = workspace.numel()
+    return _ptr(workspace, "workspace", torch.uint8, (n,), True), n
 
 
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return stream.cuda_stream
+
+
+_SHAPES = {}
 
 
 def _shapes(d: Dims):
-    act = (d.batch, d.seqlen, d.d_inner)
-    return dict(act=act, xdbl=(d.batch, d.seqlen, d.xdbl_dim), a_log=(d.d_inner, d.d_state),
-                vec=(d.d_inner,), state=(d.batch, d.d_inner, d.d_state), ckpt=ckpt_shape(d),
-                conv_w=(d.d_inner, d.d_conv), conv_state=(d.batch, d.d_inner, d.d_conv))
+    """Expected tensor shapes for ``d`` (cached per distinct dims)."""
+    key = bytes(d)
+    s = _SHAPES.get(key)
+    if s is None:
+        act = (d.batch, d.seqlen, d.d_inner)
+        s = dict(act=act, xdbl=(d.batch, d.seqlen, d.xdbl_dim), a_log=(d.d_inner, d.d_state),
+                 vec=(d.d_inner,), state=(d.batch, d.d_inner, d.d_state), ckpt=ckpt_shape(d),
+                 conv_w=(d.d_inner, d.d_conv), conv_state=(d.batch, d.d_inner, d.d_conv))
+        if len(_SHAPES) > 256:
+            _SHAPES.clear()
+        _SHAPES[key] = s
+    return s
 
 
 def scan_fwd(d: Dims, u, delta_raw, a_log, xdbl, D=None, z=None, h0=None, *, out, y_save=None,

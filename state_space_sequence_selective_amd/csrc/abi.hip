@@ -16,6 +16,9 @@ hipError_t launch_fwd_f16(const FwdArgs& p, int ds, int spl, hipStream_t st);
 hipError_t launch_bwd_f32(const BwdArgs& p, int ds, int L, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& p, int ds, int L, hipStream_t st);
 hipError_t launch_bwd_f16(const BwdArgs& p, int ds, int L, hipStream_t st);
+hipError_t launch_step_f32(const FwdArgs& p, int ds, hipStream_t st);
+hipError_t launch_step_bf16(const FwdArgs& p, int ds, hipStream_t st);
+hipError_t launch_step_f16(const FwdArgs& p, int ds, hipStream_t st);
 hipError_t launch_carry_f32(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_carry_bf16(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_carry_f16(const CarryArgs& p, int ds, hipStream_t st);
@@ -35,6 +38,15 @@ static hipError_t launch_bwd(const BwdArgs& p, Act act, int ds, int L, hipStream
     case Act::F32: return launch_bwd_f32(p, ds, L, st);
     case Act::BF16: return launch_bwd_bf16(p, ds, L, st);
     case Act::F16: return launch_bwd_f16(p, ds, L, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_step(const FwdArgs& p, Act act, int ds, hipStream_t st) {
+  switch (act) {
+    case Act::F32: return launch_step_f32(p, ds, st);
+    case Act::BF16: return launch_step_bf16(p, ds, st);
+    case Act::F16: return launch_step_f16(p, ds, st);
   }
   return hipErrorInvalidValue;
 }
@@ -175,6 +187,16 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
     choose_segments(d->segments, waves_b, pl->nC, kWantWaves, kWantWaves, kMinSegmentTiles, &pl->Sb,
                     &pl->segb_tiles);
   }
+  // a launch holds at most 2^32 - 1 threads: the tiled forward and backward
+  // (all segments in one grid) and the reduction (one thread per d_xdbl B/C
+  // element plus one per parameter-grad slot) are the largest
+  const int64_t thr_f = (d->d_inner + mscan::kFwdCpw - 1) / mscan::kFwdCpw * d->batch * fwd_threads(d->d_state) * pl->Sf;
+  const int64_t thr_b = pl->nG * d->batch * bwd_threads(d->d_state, L) * pl->Sb;
+  const int64_t thr_r = d->batch * d->seqlen * 2 * d->d_state + d->d_inner * (d->d_state + 2 + K);
+  const int64_t thr = thr_f > thr_b ? (thr_f > thr_r ? thr_f : thr_r) : (thr_b > thr_r ? thr_b : thr_r);
+  if (thr > static_cast<int64_t>(UINT32_MAX))
+    return fail(MAMBA_ERR_CAPACITY, fn, "a launch would need " + std::to_string(thr) +
+                                            " threads (> 2^32 - 1): reduce batch * seqlen or d_inner");
   return MAMBA_OK;
 }
 
@@ -288,8 +310,11 @@ int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_
     a.seg_h = static_cast<float*>(workspace);
     a.seg_sd = reinterpret_cast<float*>(static_cast<char*>(workspace) + seg_state_bytes(pl, pl.Sf));
   }
-  hipError_t err = mscan::launch_fwd(a, pl.act, static_cast<int>(pl.Ds), pl.spl_fwd,
-                                     static_cast<hipStream_t>(stream));
+  // short sequences (recurrent steps): one thread per channel, no staging
+  hipError_t err = pl.T <= mscan::kStepMaxT
+                       ? mscan::launch_step(a, pl.act, static_cast<int>(pl.Ds), static_cast<hipStream_t>(stream))
+                       : mscan::launch_fwd(a, pl.act, static_cast<int>(pl.Ds), pl.spl_fwd,
+                                           static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("forward launch: ") + hipGetErrorString(err));
   g_err.clear();
   return MAMBA_OK;

@@ -28,6 +28,10 @@ constexpr int kBwdCpw = 32;
 constexpr int kFwdTileLong = 32;
 constexpr int kFwdTileShort = 16;
 
+// Forward sequences up to this length take scan_step_kernel (one thread per
+// channel, no staging); it must not exceed the smallest checkpoint interval.
+constexpr int kStepMaxT = 16;
+
 // ---------------------------------------------------------------- dtype I/O
 template <Act A>
 struct IO;

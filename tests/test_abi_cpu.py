@@ -77,6 +77,9 @@ def test_sizes(pkg):
     (dict(d_inner=(1 << 24) + 4), 3, "d_inner"),
     (dict(act=5), 1, "act"),
     (dict(seqlen=1 << 40), 3, "2^46"),
+    # within the element cap, but the tiled launches would exceed 2^32 - 1 threads
+    (dict(batch=65535, seqlen=1, d_inner=1 << 24), 3, "threads"),
+    (dict(batch=4096, seqlen=1 << 16, d_inner=64), 3, "threads"),
 ])
 def test_bad_dims_rejected(pkg, kw, status, msg):
     d = _dims(pkg, **kw)

@@ -186,6 +186,29 @@ def test_degenerate_short_sequences(mscan, oracle_lib, T):
     run_case(mscan, oracle_lib, w, chunk=32, h0=True, conv_state0=True)
 
 
+# ---------------------------------------- short sequences (recurrent step path)
+
+
+@pytest.mark.parametrize("ds", [4, 8, 16, 32])
+@pytest.mark.parametrize("T", [1, 5, 16, 17])
+def test_step_path_scan(mscan, oracle_lib, ds, T):
+    # T <= 16 takes the one-thread-per-channel step kernel; 17 the tiled one
+    w = workloads.Workload("step_ds%d_T%d" % (ds, T), 3, T, 68, ds, 2, 0, "bf16", True)
+    run_case(mscan, oracle_lib, w, chunk=16, h0=True)
+
+
+@pytest.mark.parametrize("act", ["f32", "f16"])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_step_path_fused(mscan, oracle_lib, act, K):
+    w = workloads.Workload("step_fused_K%d_%s" % (K, act), 2, 6, 36, 16, 3, K, act, True)
+    run_case(mscan, oracle_lib, w, chunk=16, h0=True, conv_state0=True, d_u_extra=True)
+
+
+def test_step_path_no_state_no_gate(mscan, oracle_lib):
+    w = workloads.Workload("step_plain", 2, 3, 40, 16, 0, 4, "bf16", False)
+    run_case(mscan, oracle_lib, w, chunk=32, D=False)
+
+
 def test_single_channel_group_min_width(mscan, oracle_lib):
     w = workloads.Workload("di4", 1, 33, 4, 4, 0, 0, "f32", True)
     run_case(mscan, oracle_lib, w, chunk=16)
