@@ -7,6 +7,11 @@ full reverse-time adjoint).  Inputs are resident in HBM before timing
 starts.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME]
+
+``--recurrent`` instead times the recurrent-step path: one-step forward
+calls of the fused entry (conv state and SSM state in, new states out, the
+state ping-ponging between two buffers as in decoding), one JSON line per
+(batch, d_inner) shape.
 """
 from __future__ import annotations
 
@@ -95,6 +100,61 @@ def device_inputs(torch, w, inp):
     return dev
 
 
+# (batch, d_inner) of the recurrent-step timings; d_state 16, dt_rank
+# d_inner / 32, conv width 4, bf16 activations, gate on
+RECURRENT_SHAPES = [(1, 2048), (64, 2048), (1, 5120), (16, 5120), (64, 5120)]
+
+
+def recurrent_bytes(w: workloads.Workload):
+    """Bytes one step call must move: per channel the SSM state and conv
+    state in and out (f32), x, delta_raw, z read and out written; per batch
+    row the B/C row; per channel the parameters (a_log, D, conv_w, conv_b)."""
+    s = act_bytes(w.act)
+    per_chan = 2 * w.d_state * 4 + 2 * w.d_conv * 4 + 4 * s
+    params = w.d_inner * (w.d_state + 1 + w.d_conv + 1) * 4
+    return w.batch * w.d_inner * per_chan + w.batch * 2 * w.d_state * s + params
+
+
+def recurrent(torch, pkg, calls: int, warmup: int):
+    from state_space_sequence_selective_amd import _lib
+    stream = torch.cuda.current_stream()
+    for B, Di in RECURRENT_SHAPES:
+        w = workloads.Workload("recurrent_step_b%d_di%d_bf16" % (B, Di), B, 1, Di, 16, Di // 32, 4, "bf16", True)
+        inp = workloads.make_inputs(w, 0, h0=True, conv_state0=True)
+        dev = device_inputs(torch, w, inp)
+        dims = pkg.Dims.make(B, 1, Di, w.d_state, w.dt_rank, w.d_conv, 16, w.act)
+        f32 = dict(device="cuda", dtype=torch.float32)
+        h = [torch.from_numpy(inp["h0"]).to(**f32), torch.empty((B, Di, w.d_state), **f32)]
+        cs = [torch.from_numpy(inp["conv_state0"]).to(**f32), torch.empty((B, Di, w.d_conv), **f32)]
+        out = torch.empty((B, 1, Di), device="cuda", dtype=torch.bfloat16)
+        ws = torch.empty(_lib.workspace_bytes(dims), device="cuda", dtype=torch.uint8)
+
+        def call(k):
+            _lib.conv_scan_gate_fwd(dims, dev["x"], dev["conv_w"], dev["conv_b"], cs[k % 2], dev["delta_raw"],
+                                    dev["a_log"], dev["xdbl"], dev["D"], dev["z"], h[k % 2], out=out,
+                                    h_last=h[(k + 1) % 2], conv_state_last=cs[(k + 1) % 2], workspace=ws,
+                                    stream=stream)
+
+        for k in range(warmup):
+            call(k)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(calls):
+            call(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / calls
+        nb = recurrent_bytes(w)
+        print(json.dumps({"metric": "recurrent step latency (one-step fused forward, state in/out)",
+                          "value": round(us, 2), "unit": "us/call", "higher_is_better": False, "calls": calls,
+                          "dtype": w.act, "data": "synthetic",
+                          "config": {"workload": w.name, "batch": B, "d_inner": Di, "d_state": w.d_state,
+                                     "dt_rank": w.dt_rank, "d_conv": w.d_conv},
+                          "algorithmic_bytes_per_call": nb,
+                          "GBps_at_algorithmic_bytes": round(nb / (us / 1e6) / 1e9, 1)}), flush=True)
+
+
 def cpu_baseline(w: workloads.Workload, L: int, budget_s: float):
     """The CPU oracle as it stands (double precision, sequential in time,
     threads over batch rows), timed on a bounded channel sample of the same
@@ -137,6 +197,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--recurrent", action="store_true",
+                    help="time one-step forward calls with state in/out (see RECURRENT_SHAPES) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -159,10 +221,14 @@ def main():
         print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 5}))
         return
 
-    w = workloads.CONFIGS[args.workload]
-    L = args.chunk
     torch.cuda.set_device(0)
     pkg.load()
+    if args.recurrent:
+        recurrent(torch, pkg, calls=max(args.steps, 200), warmup=max(args.warmup, 20))
+        return
+
+    w = workloads.CONFIGS[args.workload]
+    L = args.chunk
     inp = workloads.make_inputs(w, args.seed)
     layers = []
     for l in range(w.layers):

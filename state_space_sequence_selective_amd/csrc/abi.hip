@@ -175,8 +175,11 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   const int64_t waves_b = pl->nG * d->batch * (bwd_threads(d->d_state, L) / 64);
   choose_segments(d->segments, waves_f, (d->seqlen + mscan::kFwdTileShort - 1) / mscan::kFwdTileShort,
                   kFwdEnoughWaves, kWantWaves, kMinSegmentTiles, &pl->Sf, &pl->segf_tiles);
+  // 32-step tiles pay only without the conv: with its halo rows and staging
+  // the fused forward's larger tile costs occupancy (measured 0.66 -> 0.81 ms
+  // per layer at B=8, T=4096, d_inner 2048, f16)
   pl->fwd_tile = mscan::kFwdTileShort;
-  if (pl->Sf == 1) {
+  if (pl->Sf == 1 && !fused) {
     pl->fwd_tile = mscan::kFwdTileLong;
     pl->segf_tiles = (d->seqlen + mscan::kFwdTileLong - 1) / mscan::kFwdTileLong;
   }
