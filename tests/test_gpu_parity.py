@@ -311,6 +311,62 @@ def test_state_carry_split_on_gpu(mscan, oracle_lib):
     assert torch.equal(cs, full.conv_state_last)
 
 
+def _chained_forward(mscan, w, dev, cuts):
+    """Forward over [0, T) as consecutive calls split at ``cuts``, each call
+    starting from the previous call's h_last / conv_state_last."""
+    parts = []
+    h, cs = dev["h0"], dev.get("conv_state0")
+    bounds = [0] + list(cuts) + [w.seqlen]
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        wp = w.with_(seqlen=hi - lo)
+        dp = dict(dev)
+        for k in ("x", "delta_raw", "z", "xdbl"):
+            dp[k] = dev[k][:, lo:hi].contiguous()
+        dp["h0"], dp["conv_state0"] = h, cs
+        core = mscan.LayerCore(_dims(mscan, wp, 16), gate=True)
+        core.forward(dp)
+        parts.append(core.out)
+        h, cs = core.h_last, core.conv_state_last
+    torch.cuda.synchronize()
+    return torch.cat(parts, 1), h, cs
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_recurrent_steps_match_one_call(mscan, oracle_lib, act):
+    """Decoding one step at a time (state handed from call to call) gives the
+    same bits as one 12-step call: both run the step kernel, with the same
+    f32 state, in the same order."""
+    w = workloads.Workload("decode_" + act, 3, 12, 100, 16, 5, 4, act, True)
+    inp = workloads.make_inputs(w, 5, h0=True, conv_state0=True)
+    dev = _device_inputs(w, inp)
+    full = mscan.LayerCore(_dims(mscan, w, 16), gate=True)
+    full.forward(dev)
+    out, h, cs = _chained_forward(mscan, w, dev, range(1, w.seqlen))
+    assert torch.equal(out, full.out)
+    assert torch.equal(h, full.h_last)
+    assert torch.equal(cs, full.conv_state_last)
+    f, _ = _oracle(oracle_lib, w, inp, 16)
+    rep = {}
+    _check("out", out, f["out"], act != "f32", rep)
+    _check("h_last", h, f["h_last"], False, rep)
+    _check("conv_state_last", cs, f["conv_state_last"], False, rep)
+
+
+def test_recurrent_steps_after_a_long_prompt(mscan, oracle_lib):
+    """A 40-step prompt in one call (tiled forward), then single steps and a
+    5-step call (step kernel), against the oracle over all 50 steps."""
+    w = workloads.Workload("prompt_then_decode", 2, 50, 68, 16, 3, 4, "bf16", True)
+    inp = workloads.make_inputs(w, 6, h0=True, conv_state0=True)
+    dev = _device_inputs(w, inp)
+    out, h, cs = _chained_forward(mscan, w, dev, [40, 41, 42, 43, 44, 45])
+    f, _ = _oracle(oracle_lib, w, inp, 16)
+    rep = {}
+    _check("out", out, f["out"], True, rep)
+    _check("h_last", h, f["h_last"], False, rep)
+    _check("conv_state_last", cs, f["conv_state_last"], False, rep)
+    print(w.name, {k: "%.2e" % v for k, v in rep.items()}, flush=True)
+
+
 def test_abi_errors_on_device(mscan):
     """A rejected call returns a status with the entry point's name and enqueues nothing."""
     w = workloads.Workload("err", 1, 8, 64, 16, 0, 0, "bf16", True)
