@@ -155,6 +155,11 @@ scan_bwd_kernel(const BwdArgs p) {
   __shared__ float s_sd[NBUF][G][SPS];   // per-group sum_n dh A dA h_{t-1}
   __shared__ float s_red[G][CPW * (NO + 1)];
   __shared__ float s_dp[SUB + KMAX][CPW];
+  // the compiler checks only the static arrays; with the dynamic raw tile a
+  // launch over the limit fails at dispatch
+  static_assert(bwd_raw_bytes<A, L, FUSED, CPW>() + sizeof(s_st) + sizeof(s_x) + sizeof(s_bc) + sizeof(s_su) +
+                        sizeof(s_sd) + sizeof(s_red) + sizeof(s_dp) <= kLdsBytes,
+                "workgroup LDS (static + dynamic raw tile) exceeds what gfx950 allows");
 
   const int tid = threadIdx.x;
   const int c = tid % CPW;             // channel within the group

@@ -25,6 +25,9 @@ constexpr int kBwdCpw = 32;
 // waves queued and uses short tiles, whose half-size LDS footprint fits
 // twice as many workgroups per CU.  Checkpoints (every 16 or 32 steps) fall
 // on 16-step boundaries inside a tile.
+// LDS a workgroup may hold on gfx950 (static and dynamic together)
+constexpr int kLdsBytes = 160 * 1024;
+
 constexpr int kFwdTileLong = 32;
 constexpr int kFwdTileShort = 16;
 

@@ -7,6 +7,23 @@
 
 namespace mscan {
 
+// sum_{r < n} src[r * stride] in ascending r.  Eight loads are issued before
+// their adds so each thread keeps several in flight; the adds keep the order.
+__device__ __forceinline__ float ordered_sum(const float* src, int64_t n, int64_t stride) {
+  constexpr int U = 8;
+  float acc = 0.0f;
+  int64_t r = 0;
+  for (; r + U <= n; r += U) {
+    float v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = src[(r + k) * stride];
+#pragma unroll
+    for (int k = 0; k < U; ++k) acc += v[k];
+  }
+  for (; r < n; ++r) acc += src[r * stride];
+  return acc;
+}
+
 __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t BT = p.B * p.T;
@@ -14,16 +31,13 @@ __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
   const int64_t nbc = BT * W;
   if (j < nbc) {
     const int64_t row = j / W, m = j % W;
-    float acc = 0.0f;
-    for (int64_t cgi = 0; cgi < p.nG; ++cgi) acc += p.part_bc[(cgi * BT + row) * W + m];
-    p.d_xdbl[row * p.X + p.R + m] += acc;
+    p.d_xdbl[row * p.X + p.R + m] += ordered_sum(p.part_bc + row * W + m, p.nG, BT * W);
     return;
   }
   const int64_t jp = j - nbc;
   if (jp >= p.Di * p.PW) return;
   const int64_t i = jp / p.PW, slot = jp % p.PW;
-  float acc = 0.0f;
-  for (int64_t rr = 0; rr < p.par_rows; ++rr) acc += p.part_par[(rr * p.Di + i) * p.PW + slot];
+  const float acc = ordered_sum(p.part_par + i * p.PW + slot, p.par_rows, p.Di * p.PW);
   if (slot < p.Ds) {
     p.d_a_log[i * p.Ds + slot] += acc;
   } else if (slot == p.Ds) {
