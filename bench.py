@@ -193,7 +193,7 @@ def main():
     ap.add_argument("--workload", default="scan_2p8b_t8192_bf16", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--chunk", type=int, default=16)
     ap.add_argument("--segments", type=int, default=0,
-                    help="cap on sequence segments scanned in parallel (0: chosen by the library)")
+                    help="sequence segments scanned in parallel (0: chosen by the library)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)

@@ -109,8 +109,10 @@ typedef struct mamba_dims {
                        Ds 32 needs L = 16 */
   int32_t act;      /* mamba_dtype_t of every activation tensor (and xdbl) */
   int32_t segments; /* sequence segments scanned in parallel (see below):
-                       0 = chosen from the sizes; n in 1 .. 4096 = at most
-                       n (1 = one sweep per channel group) */
+                       0 = chosen from the sizes; n in 1 .. 4096 = n
+                       segments in both passes, fewer only when the
+                       sequence has fewer tiles (1 = one sweep per channel
+                       group); the fused backward always uses 1 */
 } mamba_dims_t;
 
 /* Version of this ABI (MAMBA_SCAN_ABI_VERSION of the built library). */
