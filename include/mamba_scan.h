@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 2
+#define MAMBA_SCAN_ABI_VERSION 3
 
 typedef enum mamba_dtype { MAMBA_F32 = 0, MAMBA_BF16 = 1, MAMBA_F16 = 2 } mamba_dtype_t;
 

@@ -24,7 +24,9 @@ same causal cross-correlation the core oracle reads (tap K-1 on x_t).
 Everything is float64.  ``act`` ("bf16" / "f16" / None) rounds, to nearest
 even, exactly the tensors the GPU layer stores in the activation dtype
 (listed in ``ROUNDED_FWD`` / ``ROUNDED_BWD``); with None nothing is rounded,
-which is what the finite-difference pins use.  The matrix products are
+which is what the finite-difference pins use.  The gate's adjoint reads y
+as the forward stored it (the forward_mixed page keeps y among the typed
+saved activations), so with ``act`` set d_z uses the rounded y.  The matrix products are
 numpy's (a library primitive as one step).
 """
 from __future__ import annotations
@@ -37,7 +39,7 @@ from . import forward as core_forward
 NORM_EPS = 1e-5
 
 # tensors held in the activation dtype between steps (forward, then backward)
-ROUNDED_FWD = ("xn", "x", "z", "u", "xdbl", "delta_raw", "gated")
+ROUNDED_FWD = ("xn", "x", "z", "u", "xdbl", "delta_raw", "gated", "y")
 ROUNDED_BWD = ("dy_act", "d_gated", "d_u_core", "d_delta_raw", "d_z", "d_xdbl_act", "d_x")
 
 
@@ -106,6 +108,12 @@ def conv_silu_backward(du, x, conv_w, p):
     return dx, dw, np.sum(dp, axis=(0, 1))
 
 
+def gate_backward(dout, y, z):
+    """d_z of out = y * silu(z): dout * y * silu'(z), silu'(z) = s (1 + z (1 - s))."""
+    s = sigmoid(z)
+    return dout * y * s * (1.0 + z * (1.0 - s))
+
+
 def layer_forward(resid, p, act=None, chunk=16):
     """One layer.  ``resid``: [B, T, d_model]; ``p``: dict of weights
     (norm_w [dm], w_in [2Di, dm], conv_w [Di, K], conv_b [Di], w_x [R+2Ds, Di],
@@ -127,7 +135,7 @@ def layer_forward(resid, p, act=None, chunk=16):
     gated = r(core["out"])
     out = resid + gated @ p["w_out"].T
     saved = dict(xn=xn, rstd=rstd, x=x, z=z, pre=pre, u=u, xdbl=xdbl, delta_raw=delta_raw, gated=gated,
-                 y=core["y"], Ds=Ds, R=R)
+                 y=r(core["y"]), Ds=Ds, R=R)
     return out, saved
 
 
@@ -143,7 +151,8 @@ def layer_backward(resid, p, saved, d_out, act=None):
     g["w_out"] = np.einsum("btm,bti->mi", dy, s["gated"])
     d_gated = r(dy @ p["w_out"])
     cb = core_backward(s["u"], s["delta_raw"], p["a_log"], s["xdbl"], d_gated, D=p["D"], z=s["z"])
-    d_u_core, d_delta_raw, d_z = r(cb["d_x"]), r(cb["d_delta_raw"]), r(cb["d_z"])
+    d_u_core, d_delta_raw = r(cb["d_x"]), r(cb["d_delta_raw"])
+    d_z = r(gate_backward(d_gated, s["y"], s["z"]))
     g["a_log"], g["D"] = cb["d_a_log"], cb["d_D"]
     d_xdbl = cb["d_xdbl"].copy()                           # B/C columns; dt columns next
     d_xdbl[..., :R] = d_delta_raw @ p["w_dt"]

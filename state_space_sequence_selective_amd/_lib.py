@@ -1,4 +1,4 @@
-"""ctypes binding of libmamba_scan.so (include/mamba_scan.h).
+"""ctypes binding of libmamba_scan.so (include/mamba_scan.h, include/mamba_layer.h).
 
 Argument marshalling only: tensors are checked for device, dtype, layout and
 size, their device pointers are handed to the C entry points, and a non-zero
@@ -22,7 +22,13 @@ ACT_CODES = {"f32": MAMBA_F32, "bf16": MAMBA_BF16, "f16": MAMBA_F16}
 TORCH_DTYPES = {MAMBA_F32: torch.float32, MAMBA_BF16: torch.bfloat16, MAMBA_F16: torch.float16}
 
 EXPORTED = ("mamba_abi_version", "mamba_last_error", "mamba_ckpt_bytes", "mamba_workspace_bytes",
-            "mamba_scan_fwd", "mamba_scan_bwd", "mamba_conv_scan_gate_fwd", "mamba_conv_scan_gate_bwd")
+            "mamba_scan_fwd", "mamba_scan_bwd", "mamba_conv_scan_gate_fwd", "mamba_conv_scan_gate_bwd",
+            "mamba_layer_saved_bytes", "mamba_layer_workspace_bytes", "mamba_layer_fwd", "mamba_layer_bwd")
+
+# weights of one layer (mamba_layer_weights_t / mamba_layer_grads_t field order)
+LAYER_PARAMS = ("norm_w", "w_in", "conv_w", "conv_b", "w_x", "w_dt", "b_dt", "a_log", "D", "w_out")
+# those held in the activation dtype (the others, and every gradient, are f32)
+LAYER_TYPED = ("w_in", "w_x", "w_dt", "w_out")
 
 
 class MambaScanError(RuntimeError):
@@ -87,6 +93,17 @@ def load():
     lib.mamba_conv_scan_gate_fwd.argtypes = [D] + [P] * 17 + [ctypes.c_size_t, P]
     lib.mamba_conv_scan_gate_bwd.restype = ctypes.c_int
     lib.mamba_conv_scan_gate_bwd.argtypes = [D] + [P] * 22 + [ctypes.c_size_t, P]
+    LD = ctypes.POINTER(LayerDims)
+    for name in ("mamba_layer_saved_bytes", "mamba_layer_workspace_bytes"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [LD, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mamba_layer_fwd.restype = ctypes.c_int
+    lib.mamba_layer_fwd.argtypes = [LD, ctypes.POINTER(LayerWeights), P, P, P, ctypes.c_size_t, P,
+                                    ctypes.c_size_t, P]
+    lib.mamba_layer_bwd.restype = ctypes.c_int
+    lib.mamba_layer_bwd.argtypes = [LD, ctypes.POINTER(LayerWeights), P, P, ctypes.c_size_t, P, P,
+                                    ctypes.POINTER(LayerGrads), P, ctypes.c_size_t, P]
     _lib = lib
     return lib
 
@@ -236,3 +253,85 @@ def conv_scan_gate_bwd(d: Dims, x, conv_w, conv_b, conv_state0, delta_raw, a_log
             _ptr(d_conv_w, "d_conv_w", f, s["conv_w"], True), _ptr(d_conv_b, "d_conv_b", f, s["vec"], True),
             ws, wsn, _stream(stream)]
     _check(load().mamba_conv_scan_gate_bwd(*args))
+
+
+# ------------------------------------------------------------- whole layer
+
+
+class LayerDims(ctypes.Structure):
+    """mamba_layer_dims_t."""
+    _fields_ = [("core", Dims), ("d_model", ctypes.c_int64)]
+
+    @classmethod
+    def make(cls, batch, seqlen, d_model, d_inner, d_state, dt_rank, d_conv, chunk=0, act="bf16", segments=0):
+        return cls(Dims.make(batch, seqlen, d_inner, d_state, dt_rank, d_conv, chunk, act, segments), d_model)
+
+
+class LayerWeights(ctypes.Structure):
+    """mamba_layer_weights_t (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_PARAMS]
+
+
+class LayerGrads(ctypes.Structure):
+    """mamba_layer_grads_t (device pointers, f32, accumulated)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_PARAMS]
+
+
+def layer_param_shapes(ld: LayerDims) -> dict:
+    c = ld.core
+    Di, Ds, R, K, dm = c.d_inner, c.d_state, c.dt_rank, c.d_conv, ld.d_model
+    return dict(norm_w=(dm,), w_in=(2 * Di, dm), conv_w=(Di, K), conv_b=(Di,), w_x=(R + 2 * Ds, Di),
+                w_dt=(Di, R), b_dt=(Di,), a_log=(Di, Ds), D=(Di,), w_out=(dm, Di))
+
+
+def layer_saved_bytes(ld: LayerDims) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mamba_layer_saved_bytes(ctypes.byref(ld), ctypes.byref(out)))
+    return out.value
+
+
+def layer_workspace_bytes(ld: LayerDims) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mamba_layer_workspace_bytes(ctypes.byref(ld), ctypes.byref(out)))
+    return out.value
+
+
+def _layer_struct(cls, ld, tensors: dict, grads: bool):
+    shapes = layer_param_shapes(ld)
+    at = ld.core.act_dtype
+    vals = []
+    for n in LAYER_PARAMS:
+        dt = at if (n in LAYER_TYPED and not grads) else torch.float32
+        vals.append(_ptr(tensors.get(n), ("grads." if grads else "w.") + n, dt, shapes[n], True))
+    return cls(*vals)
+
+
+def _buffer(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    return _ptr(t, name, torch.uint8, (t.numel(),), True), t.numel()
+
+
+def layer_fwd(ld: LayerDims, weights: dict, resid_in, *, resid_out, saved, workspace, stream=None):
+    c = ld.core
+    rs = (c.batch, c.seqlen, ld.d_model)
+    w = _layer_struct(LayerWeights, ld, weights, False)
+    sp, sn = _buffer(saved, "saved")
+    wp, wn = _buffer(workspace, "workspace")
+    _check(load().mamba_layer_fwd(ctypes.byref(ld), ctypes.byref(w), _ptr(resid_in, "resid_in", torch.float32, rs, True),
+                                  _ptr(resid_out, "resid_out", torch.float32, rs, True), sp, sn, wp, wn,
+                                  _stream(stream)))
+
+
+def layer_bwd(ld: LayerDims, weights: dict, resid_in, saved, d_resid_out, *, d_resid_in, grads: dict, workspace,
+              stream=None):
+    c = ld.core
+    rs = (c.batch, c.seqlen, ld.d_model)
+    w = _layer_struct(LayerWeights, ld, weights, False)
+    g = _layer_struct(LayerGrads, ld, grads, True)
+    sp, sn = _buffer(saved, "saved")
+    wp, wn = _buffer(workspace, "workspace")
+    _check(load().mamba_layer_bwd(ctypes.byref(ld), ctypes.byref(w), _ptr(resid_in, "resid_in", torch.float32, rs, True),
+                                  sp, sn, _ptr(d_resid_out, "d_resid_out", torch.float32, rs, True),
+                                  _ptr(d_resid_in, "d_resid_in", torch.float32, rs, True), ctypes.byref(g), wp, wn,
+                                  _stream(stream)))

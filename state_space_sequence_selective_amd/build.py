@@ -1,7 +1,8 @@
 """Build the HIP library libmamba_scan.so for gfx950 (in-tree).
 
 Every .hip file under csrc/ is compiled to an object with hipcc (in
-parallel), then linked into state_space_sequence_selective_amd/libmamba_scan.so.
+parallel), then linked into state_space_sequence_selective_amd/libmamba_scan.so
+(with rocBLAS, which the layer entry points use for their projections).
 """
 from __future__ import annotations
 
@@ -21,6 +22,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # no packed-FP32 instructions: the compiler emits plain v_fma/v_mul/v_add only
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# the layer entry points hand their dense projections to rocBLAS
+LINK = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 
@@ -51,7 +54,7 @@ def build(verbose: bool = False) -> str:
         if verbose and msg.strip():
             print(msg)
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + [o for o, _ in results]
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + [o for o, _ in results] + LINK
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
     return LIB

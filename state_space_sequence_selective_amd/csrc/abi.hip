@@ -70,6 +70,15 @@ int fail(int code, const char* fn, const std::string& msg) {
   return code;
 }
 
+}  // namespace
+
+namespace mscan {
+// the layer entry points (layer_abi.hip) report through the same message
+void set_last_error(const std::string& msg) { g_err = msg; }
+}  // namespace mscan
+
+namespace {
+
 struct Plan {
   int64_t B, T, Di, Ds, R, X, nC, nG;
   int K;          // conv taps (0 for the scan entry points)

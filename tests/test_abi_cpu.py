@@ -7,7 +7,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mamba_scan.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -20,7 +21,7 @@ def pkg():
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = "\n".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(mamba_\w+)\s*\(", src)))
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol(pkg):
 
 
 def test_abi_version(pkg):
-    assert pkg.abi_version() == 2
+    assert pkg.abi_version() == 3
 
 
 def _dims(pkg, **kw):
@@ -185,3 +186,39 @@ def test_product_does_not_touch_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.lower() or f == "__init__.py" and "oracle" not in src, f
                 assert "import workloads" not in src and "from workloads" not in src, f
+
+
+def _ldims(pkg, **kw):
+    base = dict(batch=2, seqlen=100, d_model=48, d_inner=64, d_state=16, dt_rank=4, d_conv=4, chunk=16, act="bf16")
+    base.update(kw)
+    return pkg.LayerDims.make(**base)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d_model=0), 1, "d_model"),
+    (dict(d_model=(1 << 24) + 1), 3, "d_model"),
+    (dict(d_conv=0), 1, "d_conv"),
+    (dict(dt_rank=0), 1, "dt_rank"),
+    (dict(d_state=12), 2, "core dims: mamba_ckpt_bytes: d_state"),
+    (dict(batch=0), 1, "core dims"),
+])
+def test_layer_bad_dims_rejected(pkg, kw, status, msg):
+    with pytest.raises(pkg.MambaScanError) as ei:
+        pkg.layer_saved_bytes(_ldims(pkg, **kw))
+    assert ei.value.status == status
+    assert msg in str(ei.value) and "mamba_layer_saved_bytes" in str(ei.value)
+
+
+def test_layer_buffer_sizes(pkg):
+    """The saved buffer holds the typed activations the backward reads (plus
+    RMSNorm statistics and the core checkpoints); the workspace is at least
+    the backward's temporaries."""
+    ld = _ldims(pkg)
+    N, dm, Di, X = 200, 48, 64, 4 + 32
+    saved = pkg.layer_saved_bytes(ld)
+    typed = 2 * (N * dm + N * X + 6 * N * Di)
+    assert typed + N * 4 + pkg.ckpt_bytes(ld.core) <= saved <= typed + N * 4 + pkg.ckpt_bytes(ld.core) + 11 * 256
+    ws = pkg.layer_workspace_bytes(ld)
+    assert ws >= 2 * N * dm + 4 * N * dm + 4 * 2 * N * Di + 4 * N * X
+    # f32 activations double the typed parts
+    assert pkg.layer_saved_bytes(_ldims(pkg, act="f32")) > 1.9 * typed

@@ -1,0 +1,144 @@
+"""GPU parity of the whole-layer entry points (mamba_layer_fwd / _bwd,
+through the C ABI) against the layer oracle (oracle/layer.py).
+
+The oracle rounds to the activation dtype exactly the tensors the GPU layer
+stores typed, so both sides start every step from the same values.  What
+remains are elements whose f32 (GPU) and f64 (oracle) values fall on
+opposite sides of a rounding boundary: such an element differs by one unit
+in the last place of the activation dtype (2^-8 relative in bf16) and enters
+the f32 outputs as one term of a sum.  Tolerance per tensor, as
+max|gpu - oracle| / max(1, max|oracle|): 2e-3 for the f32 outputs of a
+bf16 / f16 layer, 1e-4 for an f32 layer.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import layer as OL
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-3, "f16": 2e-3}
+
+
+@pytest.fixture(scope="module")
+def mscan():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import state_space_sequence_selective_amd as m
+    m.load()
+    return m
+
+
+def _device_weights(m, w, inp):
+    at = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.act]
+    return {n: torch.from_numpy(np.ascontiguousarray(inp[n])).to("cuda", at if n in m.LAYER_TYPED else torch.float32)
+            for n in m.LAYER_PARAMS}
+
+
+def _ldims(m, w, chunk=16, segments=0):
+    return m.LayerDims.make(w.batch, w.seqlen, w.d_model, w.d_inner, w.d_state, w.dt_rank, w.d_conv, chunk, w.act,
+                            segments)
+
+
+def _oracle(w, inp, chunk=16):
+    p = {n: np.asarray(inp[n], dtype=np.float64) for n in OL_PARAMS}
+    resid = inp["resid"].astype(np.float64)
+    out, saved = OL.layer_forward(resid, p, act=w.act, chunk=chunk)
+    d_resid, g = OL.layer_backward(resid, p, saved, inp["d_resid_out"].astype(np.float64), act=w.act)
+    return out, d_resid, g
+
+
+OL_PARAMS = ("norm_w", "w_in", "conv_w", "conv_b", "w_x", "w_dt", "b_dt", "a_log", "D", "w_out")
+
+
+def _err(gpu, ora):
+    g = gpu.detach().double().cpu().numpy()
+    assert g.shape == ora.shape, (g.shape, ora.shape)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    return np.abs(g - ora).max() / max(1.0, np.abs(ora).max())
+
+
+def run_layer(m, w, seed=0, chunk=16, segments=0):
+    inp = workloads.make_layer_inputs(w, seed)
+    weights = _device_weights(m, w, inp)
+    layer = m.MambaLayer(_ldims(m, w, chunk, segments), weights)
+    resid = torch.from_numpy(inp["resid"]).cuda()
+    d_out = torch.from_numpy(inp["d_resid_out"]).cuda()
+    layer.zero_grads()
+    layer.forward(resid)
+    layer.backward(resid, d_out)
+    torch.cuda.synchronize()
+    return layer, inp, resid, d_out
+
+
+def check_layer(m, w, seed=0, chunk=16, segments=0):
+    layer, inp, _, _ = run_layer(m, w, seed, chunk, segments)
+    out, d_resid, g = _oracle(w, inp, chunk)
+    tol = TOL[w.act]
+    rep = {"resid_out": _err(layer.resid_out, out), "d_resid_in": _err(layer.d_resid_in, d_resid)}
+    for n in OL_PARAMS:
+        rep["d_" + n] = _err(layer.grads[n], g[n])
+    print(w.name, "segments", segments, {k: "%.2e" % v for k, v in rep.items()}, flush=True)
+    bad = {k: v for k, v in rep.items() if not v <= tol}
+    assert not bad, "over %.0e: %s" % (tol, bad)
+    return layer
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16", "f32"])
+def test_layer_small(mscan, act):
+    w = workloads.LAYER_CONFIGS["layer_small_bf16"].with_(name="layer_small_" + act, act=act)
+    check_layer(mscan, w)
+
+
+def test_layer_segmented_core(mscan):
+    """A longer sequence with the core split into segments inside the layer."""
+    w = workloads.LayerWorkload("layer_seg", 2, 300, 64, 128, 16, 4, 4, "bf16")
+    check_layer(mscan, w, segments=3)
+
+
+@pytest.mark.parametrize("ds,K", [(4, 2), (8, 3), (32, 1)])
+def test_layer_ragged_sizes(mscan, ds, K):
+    """Odd widths: d_model 50, d_inner 68 (partial channel groups), odd dt_rank."""
+    w = workloads.LayerWorkload("layer_ragged_ds%d" % ds, 3, 41, 50, 68, ds, 3, K, "bf16")
+    check_layer(mscan, w)
+
+
+def test_layer_deterministic_and_accumulating(mscan):
+    """Two backward passes from zeroed gradients give identical bits; without
+    zeroing in between, every gradient doubles exactly (x + x is exact)."""
+    w = workloads.LayerWorkload("layer_det", 2, 96, 64, 128, 16, 4, 4, "bf16")
+    layer, inp, resid, d_out = run_layer(mscan, w)
+    first = {k: v.clone() for k, v in layer.grads.items()}
+    d_first = layer.d_resid_in.clone()
+    out_first = layer.resid_out.clone()
+    layer.zero_grads()
+    layer.forward(resid)
+    layer.backward(resid, d_out)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.resid_out, out_first)
+    assert torch.equal(layer.d_resid_in, d_first)
+    for k, v in first.items():
+        assert torch.equal(layer.grads[k], v), k
+    layer.backward(resid, d_out)
+    torch.cuda.synchronize()
+    for k, v in first.items():
+        assert torch.equal(layer.grads[k], 2 * v), k
+
+
+def test_layer_errors(mscan):
+    """Rejected calls name the entry point and leave the outputs untouched."""
+    w = workloads.LayerWorkload("layer_err", 1, 16, 32, 64, 16, 4, 4, "bf16")
+    inp = workloads.make_layer_inputs(w, 0)
+    weights = _device_weights(mscan, w, inp)
+    layer = mscan.MambaLayer(_ldims(mscan, w), weights)
+    resid = torch.from_numpy(inp["resid"]).cuda()
+    layer.resid_out.fill_(7.0)
+    small = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mscan.MambaScanError, match="mamba_layer_fwd: workspace"):
+        mscan.layer_fwd(layer.dims, weights, resid, resid_out=layer.resid_out, saved=layer.saved, workspace=small)
+    with pytest.raises(mscan.MambaScanError, match="mamba_layer_fwd: resid_out must not alias"):
+        mscan.layer_fwd(layer.dims, weights, resid, resid_out=resid, saved=layer.saved, workspace=layer.workspace)
+    torch.cuda.synchronize()
+    assert torch.all(layer.resid_out == 7.0)

@@ -60,6 +60,20 @@ def test_layer_gradients_match_finite_differences():
         np.testing.assert_allclose(an, num, rtol=1e-5, atol=1e-7, err_msg=name)
 
 
+def test_gate_backward_matches_the_core_oracle():
+    """The layer's d_z formula (used so that it can read the stored, rounded
+    y) equals the core oracle's d_z when nothing is rounded."""
+    rng = np.random.default_rng(9)
+    B, T, Di, Ds = 2, 11, 6, 4
+    u, dr, z, dout = (rng.standard_normal((B, T, Di)) for _ in range(4))
+    dr -= 3.0
+    xdbl = rng.standard_normal((B, T, 2 * Ds))
+    a_log = np.log(np.tile(np.arange(1.0, Ds + 1), (Di, 1)))
+    f = oracle.forward(u, dr, a_log, xdbl, D=np.ones(Di), z=z, chunk=16)
+    g = oracle.backward(u, dr, a_log, xdbl, dout, D=np.ones(Di), z=z)
+    np.testing.assert_allclose(L.gate_backward(dout, f["y"], z), g["d_z"], rtol=1e-12, atol=1e-14)
+
+
 def test_conv_matches_the_core_oracle_conv_path():
     """The layer's conv + SiLU (numpy, tap by tap) equals the u the core
     oracle's fused path computes (C, step by step) from the same input."""

@@ -128,3 +128,66 @@ def make_inputs(w: Workload, seed: int = 0, h0: bool = False, conv_state0: bool 
     if d_u_extra:
         out["d_u_extra"] = round_to(w.act, normal(shape, std=0.5))
     return out
+
+
+# ------------------------------------------------------------- whole layer
+
+
+@dataclass(frozen=True)
+class LayerWorkload:
+    """One Mamba-1 layer: residual width d_model around the core's sizes."""
+    name: str
+    batch: int
+    seqlen: int
+    d_model: int
+    d_inner: int
+    d_state: int
+    dt_rank: int
+    d_conv: int
+    act: str
+
+    def with_(self, **kw) -> "LayerWorkload":
+        return replace(self, **kw)
+
+
+LAYER_CONFIGS = {
+    # small layer the oracle finishes in seconds (several tiles, ragged tail)
+    "layer_small_bf16": LayerWorkload("layer_small_bf16", 2, 150, 96, 192, 16, 6, 4, "bf16"),
+    # the 130M model's layer shape (d_model 768, d_inner 1536, dt_rank 48), B=4, T=2048
+    "layer_130m_bf16": LayerWorkload("layer_130m_bf16", 4, 2048, 768, 1536, 16, 48, 4, "bf16"),
+}
+
+
+def make_layer_inputs(w: LayerWorkload, seed: int = 0) -> dict:
+    """Draw a layer's weights, input residual and output-residual gradient.
+
+    Readings (the pages give shapes, not initialisations): residual and its
+    gradient N(0, 1); norm weight 1 + N(0, 0.1^2); projections N(0, 1/fan_in);
+    conv weight and bias N(0, 0.5^2); dt bias the inverse softplus of
+    dt = exp(U(log 1e-3, log 1e-1)); a_log S4D-real; D = 1.  The projection
+    weights come back rounded to the activation dtype (the compute copies
+    a layer multiplies with), everything else float32.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, dm, Di, Ds, R, K = w.batch, w.seqlen, w.d_model, w.d_inner, w.d_state, w.dt_rank, w.d_conv
+    X = R + 2 * Ds
+
+    def normal(size, std=1.0):
+        a = rng.standard_normal(size, dtype=np.float32)
+        return a * np.float32(std) if std != 1.0 else a
+
+    out = {}
+    out["resid"] = normal((B, T, dm))
+    out["norm_w"] = 1.0 + normal((dm,), 0.1)
+    out["w_in"] = round_to(w.act, normal((2 * Di, dm), dm ** -0.5))
+    out["conv_w"] = normal((Di, K), 0.5)
+    out["conv_b"] = normal((Di,), 0.5)
+    out["w_x"] = round_to(w.act, normal((X, Di), Di ** -0.5))
+    out["w_dt"] = round_to(w.act, normal((Di, R), R ** -0.5))
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), Di))
+    out["b_dt"] = (dt + np.log(-np.expm1(-dt))).astype(np.float32)
+    out["a_log"] = s4d_real_a_log(Di, Ds)
+    out["D"] = np.ones(Di, dtype=np.float32)
+    out["w_out"] = round_to(w.act, normal((dm, Di), Di ** -0.5))
+    out["d_resid_out"] = normal((B, T, dm))
+    return out
