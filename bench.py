@@ -8,6 +8,10 @@ starts.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME]
 
+``--layer NAME`` instead times one whole Mamba-1 layer (RMSNorm,
+projections, conv, scan core, residual; include/mamba_layer.h), forward +
+backward per step, at a shape of ``workloads.LAYER_CONFIGS``.
+
 ``--recurrent`` instead times the recurrent-step path: one-step forward
 calls of the fused entry (conv state and SSM state in, new states out, the
 state ping-ponging between two buffers as in decoding), one JSON line per
@@ -155,6 +159,87 @@ def recurrent(torch, pkg, calls: int, warmup: int):
                           "GBps_at_algorithmic_bytes": round(nb / (us / 1e6) / 1e9, 1)}), flush=True)
 
 
+def layer_flops(w: workloads.LayerWorkload):
+    """Dense-projection flops of one layer step (forward + both backward
+    products of every projection), 2 per multiply-add."""
+    N, dm, Di, R = w.batch * w.seqlen, w.d_model, w.d_inner, w.dt_rank
+    X = R + 2 * w.d_state
+    per_pass = 2 * N * (dm * 2 * Di + Di * X + R * Di + Di * dm)
+    return 3 * per_pass
+
+
+def layer_bench(torch, pkg, name: str, steps: int, warmup: int, no_cpu: bool, budget_s: float):
+    w = workloads.LAYER_CONFIGS[name]
+    inp = workloads.make_layer_inputs(w, 0)
+    at = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.act]
+    weights = {n: torch.from_numpy(inp[n]).to("cuda", at if n in pkg.LAYER_TYPED else torch.float32)
+               for n in pkg.LAYER_PARAMS}
+    dims = pkg.LayerDims.make(w.batch, w.seqlen, w.d_model, w.d_inner, w.d_state, w.dt_rank, w.d_conv, 16, w.act)
+    layer = pkg.MambaLayer(dims, weights)
+    resid = torch.from_numpy(inp["resid"]).cuda()
+    d_out = torch.from_numpy(inp["d_resid_out"]).cuda()
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        layer.zero_grads()
+        if ev:
+            ev[0].record(stream)
+        layer.forward(resid, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        layer.backward(resid, d_out, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(steps):
+        step(evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    tokens = w.batch * w.seqlen
+    res = {"metric": "Mamba-1 layer fwd+bwd tokens/sec", "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
+           "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": w.act, "data": "synthetic (seeded)",
+           "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_model": w.d_model,
+                      "d_inner": w.d_inner, "d_state": w.d_state, "dt_rank": w.dt_rank, "d_conv": w.d_conv,
+                      "chunk": 16, "parallelism": "single GPU"},
+           "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+           "projection_flops_per_step": layer_flops(w)}
+    if not no_cpu:
+        res["cpu_baseline"] = layer_cpu_baseline(w, budget_s)
+    print(json.dumps(res), flush=True)
+
+
+def layer_cpu_baseline(w: workloads.LayerWorkload, budget_s: float):
+    """The layer oracle as it stands (float64), forward + backward, on a
+    bounded sample of the same widths (fewer steps), scaled to the tokens of
+    the workload."""
+    from oracle import layer as OL
+    T = 64
+    while True:
+        sw = w.with_(batch=1, seqlen=T)
+        inp = workloads.make_layer_inputs(sw, 0)
+        p = {n: inp[n].astype(np.float64) for n in ("norm_w", "w_in", "conv_w", "conv_b", "w_x", "w_dt", "b_dt",
+                                                   "a_log", "D", "w_out")}
+        t0 = time.perf_counter()
+        out, saved = OL.layer_forward(inp["resid"].astype(np.float64), p, act=w.act)
+        OL.layer_backward(inp["resid"].astype(np.float64), p, saved, inp["d_resid_out"].astype(np.float64), act=w.act)
+        dt = time.perf_counter() - t0
+        if dt > 0.25 * budget_s or T >= w.seqlen * w.batch:
+            break
+        T = min(w.seqlen * w.batch, T * max(2, int(0.5 * budget_s / max(dt, 1e-3))))
+    return {"value": T / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": "1 batch row x %d steps of the same widths, fwd+bwd in %.1f s" % (T, dt)}
+
+
 def cpu_baseline(w: workloads.Workload, L: int, budget_s: float):
     """The CPU oracle as it stands (double precision, sequential in time,
     threads over batch rows), timed on a bounded channel sample of the same
@@ -197,6 +282,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--layer", default=None, choices=sorted(workloads.LAYER_CONFIGS),
+                    help="time one whole Mamba-1 layer at this shape and exit")
     ap.add_argument("--recurrent", action="store_true",
                     help="time one-step forward calls with state in/out (see RECURRENT_SHAPES) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -225,6 +312,9 @@ def main():
     pkg.load()
     if args.recurrent:
         recurrent(torch, pkg, calls=max(args.steps, 200), warmup=max(args.warmup, 20))
+        return
+    if args.layer:
+        layer_bench(torch, pkg, args.layer, args.steps, args.warmup, args.no_cpu_baseline, args.cpu_budget)
         return
 
     w = workloads.CONFIGS[args.workload]

@@ -28,7 +28,7 @@ using mlayer::OpKind;
 constexpr float kNormEps = 1e-5f;   // the forward_mixed page's RMSNorm epsilon
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxModel = int64_t(1) << 24;
-constexpr int64_t kPartBlocks = 256;   // row blocks of the fixed-order column reductions
+constexpr int64_t kPartBlocks = 32;   // row blocks of the fixed-order column reductions
 
 int fail(int code, const char* fn, const std::string& msg) {
   mscan::set_last_error(std::string(fn) + ": " + msg);
@@ -130,6 +130,9 @@ int plan_layer(const mamba_layer_dims_t* d, const char* fn, LPlan* pl) {
   pl->conv_spb = (pl->T + per_row - 1) / per_row;
   pl->conv_nblk_t = (pl->T + pl->conv_spb - 1) / pl->conv_spb;
   if (pl->B * pl->conv_nblk_t > 65535) return fail(MAMBA_ERR_CAPACITY, fn, "batch must be <= 65535");
+  // row-blocked elementwise launches: rows * ceil(d_inner / 256) workgroups
+  if (pl->N * ((pl->Di + 255) / 256) > static_cast<int64_t>(UINT_MAX))
+    return fail(MAMBA_ERR_CAPACITY, fn, "batch * seqlen * ceil(d_inner / 256) must be < 2^32");
   const size_t nconv = static_cast<size_t>(pl->B * pl->conv_nblk_t);
   Layout wb;
   pl->w_dy = wb.take(N * dm * es);
@@ -330,6 +333,7 @@ int mamba_layer_fwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
   o.f0 = dt;
   o.f1 = w->b_dt;
   o.v0 = dr;
+  o.T = pl.T;
   o.cols = Di;
   o.n = N * Di;
   LAYER_TRY(run(fn, "dt bias", o, act, st));

@@ -19,7 +19,7 @@ enum class OpKind {
   ConvDx,            // dp f0, conv_w f1 -> d_x v0; T, cols, K, n
   ConvWgradPart,     // dp f0, x c0 -> part_w f3 [nblk, cols, K], part_b f6 [nblk, cols]; T, cols, K,
                      // per_blk (steps), nblk_t (step blocks per batch row), nblk = batch * nblk_t
-  BiasRound,         // dt f0, b f1 -> out v0 (act); cols, n
+  BiasRound,         // dt f0, b f1 -> out v0 (act); T, cols, n
   Cast,              // f0 -> v0 (act); n
   ColPart,           // m c0 (act) -> part f3 [nblk, cols]; rows, cols, per_blk, nblk
   ColSum,            // part f0 -> out f3 (+=); nblk, cols

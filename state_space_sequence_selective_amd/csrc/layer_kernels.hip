@@ -37,6 +37,20 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// Element of a [rows, Di] activation for a grid of rows * nchb workgroups,
+// nchb = ceil(Di / 256) channel blocks per row: the row (and its step t)
+// comes from one 32-bit division per workgroup, not a 64-bit one per
+// element.  False past the last channel.
+__device__ __forceinline__ bool row_channel(int64_t T, int64_t Di, unsigned nchb, int64_t* e, int64_t* i,
+                                            int64_t* t) {
+  const unsigned row = blockIdx.x / nchb;
+  *i = static_cast<int64_t>(blockIdx.x - row * nchb) * kThreads + threadIdx.x;
+  if (*i >= Di) return false;
+  *t = static_cast<int64_t>(row % static_cast<unsigned>(T));
+  *e = static_cast<int64_t>(row) * Di + *i;
+  return true;
+}
+
 // F1: one workgroup per row
 template <Act A>
 __global__ void __launch_bounds__(kThreads) rmsnorm_fwd_kernel(const float* __restrict__ x, const float* __restrict__ w,
@@ -86,8 +100,17 @@ __global__ void __launch_bounds__(kThreads) rmsnorm_wgrad_part_kernel(const floa
   const int64_t blk = blockIdx.y;
   const int64_t r0 = blk * rows_per_blk;
   const int64_t r1 = r0 + rows_per_blk < rows ? r0 + rows_per_blk : rows;
+  constexpr int U = 8;
   float acc = 0.0f;
-  for (int64_t r = r0; r < r1; ++r) acc = fmaf(dy[r * dm + j] * x[r * dm + j], rstd[r], acc);
+  int64_t r = r0;
+  for (; r + U <= r1; r += U) {   // eight rows' loads in flight, products added in row order
+    float v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = dy[(r + k) * dm + j] * x[(r + k) * dm + j] * rstd[r + k];
+#pragma unroll
+    for (int k = 0; k < U; ++k) acc += v[k];
+  }
+  for (; r < r1; ++r) acc += dy[r * dm + j] * x[r * dm + j] * rstd[r];
   part[blk * dm + j] = acc;
 }
 
@@ -96,10 +119,9 @@ template <Act A>
 __global__ void __launch_bounds__(kThreads) conv_silu_fwd_kernel(const void* __restrict__ x,
                                                                 const float* __restrict__ cw,
                                                                 const float* __restrict__ cb, void* __restrict__ u,
-                                                                int64_t T, int64_t Di, int K, int64_t n) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= n) return;
-  const int64_t i = e % Di, t = (e / Di) % T;
+                                                                int64_t T, int64_t Di, int K, unsigned nchb) {
+  int64_t e, i, t;
+  if (!row_channel(T, Di, nchb, &e, &i, &t)) return;
   float p = cb[i];
   for (int k = 0; k < K; ++k) {
     const int64_t back = K - 1 - k;   // tap k reads x_{t - back}
@@ -116,10 +138,9 @@ __global__ void __launch_bounds__(kThreads) conv_silu_dp_kernel(const void* __re
                                                                const void* __restrict__ du,
                                                                const float* __restrict__ du_extra,
                                                                float* __restrict__ dp, int64_t T, int64_t Di, int K,
-                                                               int64_t n) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= n) return;
-  const int64_t i = e % Di, t = (e / Di) % T;
+                                                               unsigned nchb) {
+  int64_t e, i, t;
+  if (!row_channel(T, Di, nchb, &e, &i, &t)) return;
   float p = cb[i];
   for (int k = 0; k < K; ++k) {
     const int64_t back = K - 1 - k;
@@ -133,10 +154,9 @@ __global__ void __launch_bounds__(kThreads) conv_silu_dp_kernel(const void* __re
 template <Act A>
 __global__ void __launch_bounds__(kThreads) conv_dx_kernel(const float* __restrict__ dp, const float* __restrict__ cw,
                                                           void* __restrict__ dx, int64_t T, int64_t Di, int K,
-                                                          int64_t n) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= n) return;
-  const int64_t i = e % Di, t = (e / Di) % T;
+                                                          unsigned nchb) {
+  int64_t e, i, t;
+  if (!row_channel(T, Di, nchb, &e, &i, &t)) return;
   float g = 0.0f;
   for (int k = 0; k < K; ++k) {
     const int64_t ahead = K - 1 - k;   // dp_{t + ahead} read x_t through tap k
@@ -185,10 +205,10 @@ __global__ void __launch_bounds__(kThreads) conv_wgrad_part_kernel(const float* 
 template <Act A>
 __global__ void __launch_bounds__(kThreads) bias_round_kernel(const float* __restrict__ dt,
                                                              const float* __restrict__ b, void* __restrict__ out,
-                                                             int64_t Di, int64_t n) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= n) return;
-  IO<A>::st(out, e, dt[e] + b[e % Di]);
+                                                             int64_t T, int64_t Di, unsigned nchb) {
+  int64_t e, i, t;
+  if (!row_channel(T, Di, nchb, &e, &i, &t)) return;
+  IO<A>::st(out, e, dt[e] + b[i]);
 }
 
 template <Act A>
@@ -208,8 +228,17 @@ __global__ void __launch_bounds__(kThreads) colpart_kernel(const void* __restric
   const int64_t blk = blockIdx.y;
   const int64_t r0 = blk * rows_per_blk;
   const int64_t r1 = r0 + rows_per_blk < rows ? r0 + rows_per_blk : rows;
+  constexpr int U = 8;
   float acc = 0.0f;
-  for (int64_t r = r0; r < r1; ++r) acc += IO<A>::ld(m, r * cols + j);
+  int64_t r = r0;
+  for (; r + U <= r1; r += U) {
+    float v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = IO<A>::ld(m, (r + k) * cols + j);
+#pragma unroll
+    for (int k = 0; k < U; ++k) acc += v[k];
+  }
+  for (; r < r1; ++r) acc += IO<A>::ld(m, r * cols + j);
   part[blk * cols + j] = acc;
 }
 
@@ -218,9 +247,7 @@ __global__ void __launch_bounds__(kThreads) colsum_kernel(const float* __restric
                                                          int64_t nblk, int64_t cols) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (j >= cols) return;
-  float acc = 0.0f;
-  for (int64_t b = 0; b < nblk; ++b) acc += part[b * cols + j];
-  out[j] += acc;
+  out[j] += mscan::ordered_sum(part + j, nblk, cols);
 }
 
 __global__ void __launch_bounds__(kThreads) zero_kernel(float* __restrict__ p, int64_t n) {
@@ -229,6 +256,10 @@ __global__ void __launch_bounds__(kThreads) zero_kernel(float* __restrict__ p, i
 }
 
 dim3 grid1(int64_t n) { return dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)); }
+
+// row-blocked elementwise launches: rows = n / cols, ceil(cols / 256) blocks per row
+unsigned nchb(const Op& o) { return static_cast<unsigned>((o.cols + kThreads - 1) / kThreads); }
+dim3 grid_rows(const Op& o) { return dim3(static_cast<unsigned>(o.n / o.cols) * nchb(o)); }
 
 template <Act A>
 hipError_t dispatch(const Op& o, hipStream_t st) {
@@ -239,22 +270,22 @@ hipError_t dispatch(const Op& o, hipStream_t st) {
                          o.f3, o.cols, o.eps);
       break;
     case OpKind::ConvSiluFwd:
-      hipLaunchKernelGGL(conv_silu_fwd_kernel<A>, grid1(o.n), blk, 0, st, o.c0, o.f0, o.f1, o.v0, o.T, o.cols, o.K,
-                         o.n);
+      hipLaunchKernelGGL(conv_silu_fwd_kernel<A>, grid_rows(o), blk, 0, st, o.c0, o.f0, o.f1, o.v0, o.T, o.cols, o.K,
+                         nchb(o));
       break;
     case OpKind::ConvSiluDp:
-      hipLaunchKernelGGL(conv_silu_dp_kernel<A>, grid1(o.n), blk, 0, st, o.c0, o.f0, o.f1, o.c1, o.f2, o.f3, o.T,
-                         o.cols, o.K, o.n);
+      hipLaunchKernelGGL(conv_silu_dp_kernel<A>, grid_rows(o), blk, 0, st, o.c0, o.f0, o.f1, o.c1, o.f2, o.f3, o.T,
+                         o.cols, o.K, nchb(o));
       break;
     case OpKind::ConvDx:
-      hipLaunchKernelGGL(conv_dx_kernel<A>, grid1(o.n), blk, 0, st, o.f0, o.f1, o.v0, o.T, o.cols, o.K, o.n);
+      hipLaunchKernelGGL(conv_dx_kernel<A>, grid_rows(o), blk, 0, st, o.f0, o.f1, o.v0, o.T, o.cols, o.K, nchb(o));
       break;
     case OpKind::ConvWgradPart:
       hipLaunchKernelGGL(conv_wgrad_part_kernel<A>, dim3(grid1(o.cols).x, static_cast<unsigned>(o.nblk)), blk, 0, st,
                          o.f0, o.c0, o.f3, o.f6, o.T, o.cols, o.K, o.per_blk, o.nblk_t);
       break;
     case OpKind::BiasRound:
-      hipLaunchKernelGGL(bias_round_kernel<A>, grid1(o.n), blk, 0, st, o.f0, o.f1, o.v0, o.cols, o.n);
+      hipLaunchKernelGGL(bias_round_kernel<A>, grid_rows(o), blk, 0, st, o.f0, o.f1, o.v0, o.T, o.cols, nchb(o));
       break;
     case OpKind::Cast:
       hipLaunchKernelGGL(cast_kernel<A>, grid1(o.n), blk, 0, st, o.f0, o.v0, o.n);

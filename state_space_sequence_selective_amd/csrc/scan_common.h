@@ -89,6 +89,24 @@ struct IO<Act::F16> {
   }
 };
 
+// sum_{r < n} src[r * stride] in ascending r.  Eight loads are issued before
+// their adds so each thread keeps several in flight; the adds keep the order
+// (the result is that of the plain sequential loop, bit for bit).
+__device__ __forceinline__ float ordered_sum(const float* src, int64_t n, int64_t stride) {
+  constexpr int U = 8;
+  float acc = 0.0f;
+  int64_t r = 0;
+  for (; r + U <= n; r += U) {
+    float v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = src[(r + k) * stride];
+#pragma unroll
+    for (int k = 0; k < U; ++k) acc += v[k];
+  }
+  for (; r < n; ++r) acc += src[r * stride];
+  return acc;
+}
+
 // ---------------------------------------------------------------- math
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

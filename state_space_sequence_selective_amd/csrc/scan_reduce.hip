@@ -7,23 +7,6 @@
 
 namespace mscan {
 
-// sum_{r < n} src[r * stride] in ascending r.  Eight loads are issued before
-// their adds so each thread keeps several in flight; the adds keep the order.
-__device__ __forceinline__ float ordered_sum(const float* src, int64_t n, int64_t stride) {
-  constexpr int U = 8;
-  float acc = 0.0f;
-  int64_t r = 0;
-  for (; r + U <= n; r += U) {
-    float v[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) v[k] = src[(r + k) * stride];
-#pragma unroll
-    for (int k = 0; k < U; ++k) acc += v[k];
-  }
-  for (; r < n; ++r) acc += src[r * stride];
-  return acc;
-}
-
 __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t BT = p.B * p.T;

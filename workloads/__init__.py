@@ -155,6 +155,8 @@ LAYER_CONFIGS = {
     "layer_small_bf16": LayerWorkload("layer_small_bf16", 2, 150, 96, 192, 16, 6, 4, "bf16"),
     # the 130M model's layer shape (d_model 768, d_inner 1536, dt_rank 48), B=4, T=2048
     "layer_130m_bf16": LayerWorkload("layer_130m_bf16", 4, 2048, 768, 1536, 16, 48, 4, "bf16"),
+    # the 2.8B model's layer widths (d_model 2560, d_inner 5120, dt_rank 160), B=2, T=2048
+    "layer_2p8b_t2048_bf16": LayerWorkload("layer_2p8b_t2048_bf16", 2, 2048, 2560, 5120, 16, 160, 4, "bf16"),
 }
 
 
