@@ -53,9 +53,9 @@ struct LPlan {
   // workspace: forward
   size_t w_dt, w_core_f, wf_total;
   // workspace: backward
-  size_t w_dy, w_dgated, w_du, w_ddr, w_dz, w_dxdbl, w_dxdbl_a, w_duex, w_dp, w_dx, w_dxn, w_pnorm, w_pbdt,
-      w_pconv_w, w_pconv_b, w_core_b, wb_total;
-  int64_t norm_per, norm_nblk, bdt_per, bdt_nblk, conv_spb, conv_nblk_t;
+  size_t w_dy, w_dgated, w_du, w_ddr, w_dz, w_dxdbl, w_dxdbl_a, w_duex, w_dx, w_dxn, w_pnorm, w_pbdt, w_pconv_w,
+      w_pconv_b, w_core_b, wb_total;
+  int64_t norm_per, norm_nblk, bdt_per, bdt_nblk, conv_nblk;
 };
 
 // Lays out consecutive 256-byte-aligned regions.
@@ -126,14 +126,12 @@ int plan_layer(const mamba_layer_dims_t* d, const char* fn, LPlan* pl) {
   pl->norm_nblk = (pl->N + pl->norm_per - 1) / pl->norm_per;
   pl->bdt_nblk = pl->norm_nblk;
   pl->bdt_per = pl->norm_per;
-  const int64_t per_row = kPartBlocks / pl->B > 1 ? kPartBlocks / pl->B : 1;   // step blocks per batch row
-  pl->conv_spb = (pl->T + per_row - 1) / per_row;
-  pl->conv_nblk_t = (pl->T + pl->conv_spb - 1) / pl->conv_spb;
-  if (pl->B * pl->conv_nblk_t > 65535) return fail(MAMBA_ERR_CAPACITY, fn, "batch must be <= 65535");
+  // conv weight partials: one per (batch row, step tile)
+  pl->conv_nblk = pl->B * mlayer::conv_step_tiles(pl->T);
   // row-blocked elementwise launches: rows * ceil(d_inner / 256) workgroups
   if (pl->N * ((pl->Di + 255) / 256) > static_cast<int64_t>(UINT_MAX))
     return fail(MAMBA_ERR_CAPACITY, fn, "batch * seqlen * ceil(d_inner / 256) must be < 2^32");
-  const size_t nconv = static_cast<size_t>(pl->B * pl->conv_nblk_t);
+  const size_t nconv = static_cast<size_t>(pl->conv_nblk);
   Layout wb;
   pl->w_dy = wb.take(N * dm * es);
   pl->w_dgated = wb.take(N * Di * es);
@@ -143,7 +141,6 @@ int plan_layer(const mamba_layer_dims_t* d, const char* fn, LPlan* pl) {
   pl->w_dxdbl = wb.take(N * X * f);
   pl->w_dxdbl_a = wb.take(N * X * es);
   pl->w_duex = wb.take(N * Di * f);
-  pl->w_dp = wb.take(N * Di * f);
   pl->w_dx = wb.take(N * Di * es);
   pl->w_dxn = wb.take(N * dm * f);
   pl->w_pnorm = wb.take(static_cast<size_t>(pl->norm_nblk) * dm * f);
@@ -398,7 +395,6 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
   float* d_xdbl = reinterpret_cast<float*>(W + pl.w_dxdbl);
   void* d_xdbl_a = W + pl.w_dxdbl_a;
   float* d_uex = reinterpret_cast<float*>(W + pl.w_duex);
-  float* dp = reinterpret_cast<float*>(W + pl.w_dp);
   void* d_x = W + pl.w_dx;
   float* d_xn = reinterpret_cast<float*>(W + pl.w_dxn);
   float* pnorm = reinterpret_cast<float*>(W + pl.w_pnorm);
@@ -455,44 +451,25 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
                  Di));
   LAYER_TRY(gemm(fn, "x_proj wgrad", h, true, false, X, Di, N, d_xdbl_a, at, X, u, at, Di, 1.0f, g->w_x, g->w_x, f32,
                  Di));
-  // conv + SiLU adjoint
-  o = Op{OpKind::ConvSiluDp};
+  // conv + SiLU adjoint: d_x and the weight / bias partials in one pass
+  o = Op{OpKind::ConvBwd};
   o.c0 = x;
   o.f0 = w->conv_w;
   o.f1 = w->conv_b;
   o.c1 = d_u;
   o.f2 = d_uex;
-  o.f3 = dp;
-  o.T = pl.T;
-  o.cols = Di;
-  o.K = static_cast<int>(pl.K);
-  o.n = N * Di;
-  LAYER_TRY(run(fn, "silu adjoint", o, act, st));
-  o = Op{OpKind::ConvDx};
-  o.f0 = dp;
-  o.f1 = w->conv_w;
   o.v0 = d_x;
-  o.T = pl.T;
-  o.cols = Di;
-  o.K = static_cast<int>(pl.K);
-  o.n = N * Di;
-  LAYER_TRY(run(fn, "conv dgrad", o, act, st));
-  o = Op{OpKind::ConvWgradPart};
-  o.f0 = dp;
-  o.c0 = x;
   o.f3 = pcw;
   o.f6 = pcb;
   o.T = pl.T;
   o.cols = Di;
   o.K = static_cast<int>(pl.K);
-  o.per_blk = pl.conv_spb;
-  o.nblk_t = pl.conv_nblk_t;
-  o.nblk = pl.B * pl.conv_nblk_t;
-  LAYER_TRY(run(fn, "conv wgrad partials", o, act, st));
+  o.n = N * Di;
+  LAYER_TRY(run(fn, "conv adjoint", o, act, st));
   o = Op{OpKind::ColSum};
   o.f0 = pcw;
   o.f3 = g->conv_w;
-  o.nblk = pl.B * pl.conv_nblk_t;
+  o.nblk = pl.conv_nblk;
   o.cols = Di * pl.K;
   LAYER_TRY(run(fn, "conv_w sum", o, act, st));
   o.f0 = pcb;

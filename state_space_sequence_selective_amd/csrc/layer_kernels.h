@@ -15,10 +15,9 @@ enum class OpKind {
   RmsnormBwd,        // dy f0, x f1, w f2, rstd f4, d_out f5 -> d_in f3; rows, cols
   RmsnormWgradPart,  // dy f0, x f1, rstd f2 -> part f3 [nblk, cols]; rows, cols, per_blk, nblk
   ConvSiluFwd,       // x c0, conv_w f0, conv_b f1 -> u v0; T, cols = d_inner, K, n
-  ConvSiluDp,        // x c0, conv_w f0, conv_b f1, d_u c1 (act), d_u_extra f2 -> dp f3; T, cols, K, n
-  ConvDx,            // dp f0, conv_w f1 -> d_x v0; T, cols, K, n
-  ConvWgradPart,     // dp f0, x c0 -> part_w f3 [nblk, cols, K], part_b f6 [nblk, cols]; T, cols, K,
-                     // per_blk (steps), nblk_t (step blocks per batch row), nblk = batch * nblk_t
+  ConvBwd,           // x c0, conv_w f0, conv_b f1, d_u c1 (act), d_u_extra f2 -> d_x v0 (act),
+                     // part_w f3 [batch * ntiles, cols, K], part_b f6 [batch * ntiles, cols]; T, cols, K, n
+                     // (ntiles = conv_step_tiles(T))
   BiasRound,         // dt f0, b f1 -> out v0 (act); T, cols, n
   Cast,              // f0 -> v0 (act); n
   ColPart,           // m c0 (act) -> part f3 [nblk, cols]; rows, cols, per_blk, nblk
@@ -44,5 +43,9 @@ struct Op {
 };
 
 hipError_t launch(const Op& o, mscan::Act act, hipStream_t st);
+
+// step tiles per batch row of the conv kernels (their weight partials come
+// one per batch row and tile)
+int64_t conv_step_tiles(int64_t T);
 
 }  // namespace mlayer

@@ -114,91 +114,117 @@ __global__ void __launch_bounds__(kThreads) rmsnorm_wgrad_part_kernel(const floa
   part[blk * dm + j] = acc;
 }
 
-// F4a: u = SiLU(b + sum_k w[i,k] x[t-K+1+k]) with zero history
+// Tiles of the conv kernels: a workgroup walks kConvTT steps of one batch
+// row for 256 channels, the conv window in registers, so each input is read
+// once (plus a K-1 step halo).  Block id = (b * ntb + tb) * nchb + channel
+// block, ntb = ceil(T / kConvTT).
+constexpr int kConvTT = 64;
+
+struct ConvTile {
+  int64_t b, t0, t1, i;
+};
+
+__device__ __forceinline__ bool conv_tile(int64_t T, int64_t Di, unsigned nchb, unsigned ntb, ConvTile* c) {
+  const unsigned cbk = blockIdx.x % nchb, rest = blockIdx.x / nchb;
+  c->i = static_cast<int64_t>(cbk) * kThreads + threadIdx.x;
+  if (c->i >= Di) return false;
+  c->b = rest / ntb;
+  c->t0 = static_cast<int64_t>(rest % ntb) * kConvTT;
+  c->t1 = c->t0 + kConvTT < T ? c->t0 + kConvTT : T;
+  return true;
+}
+
+// F4a: u_t = SiLU(b + sum_k w[i,k] x_{t-(K-1-k)}), zero history.  win[m] holds
+// x_{t-1-m}; tap k < K-1 reads win[K-2-k], tap K-1 reads x_t.
 template <Act A>
 __global__ void __launch_bounds__(kThreads) conv_silu_fwd_kernel(const void* __restrict__ x,
                                                                 const float* __restrict__ cw,
                                                                 const float* __restrict__ cb, void* __restrict__ u,
-                                                                int64_t T, int64_t Di, int K, unsigned nchb) {
-  int64_t e, i, t;
-  if (!row_channel(T, Di, nchb, &e, &i, &t)) return;
-  float p = cb[i];
-  for (int k = 0; k < K; ++k) {
-    const int64_t back = K - 1 - k;   // tap k reads x_{t - back}
-    if (t >= back) p = fmaf(cw[i * K + k], IO<A>::ld(x, e - back * Di), p);
-  }
-  IO<A>::st(u, e, p * sigmoid_f(p));
-}
-
-// adjoint of the SiLU: dp = (d_u + d_u_extra) * silu'(p), p recomputed
-template <Act A>
-__global__ void __launch_bounds__(kThreads) conv_silu_dp_kernel(const void* __restrict__ x,
-                                                               const float* __restrict__ cw,
-                                                               const float* __restrict__ cb,
-                                                               const void* __restrict__ du,
-                                                               const float* __restrict__ du_extra,
-                                                               float* __restrict__ dp, int64_t T, int64_t Di, int K,
-                                                               unsigned nchb) {
-  int64_t e, i, t;
-  if (!row_channel(T, Di, nchb, &e, &i, &t)) return;
-  float p = cb[i];
-  for (int k = 0; k < K; ++k) {
-    const int64_t back = K - 1 - k;
-    if (t >= back) p = fmaf(cw[i * K + k], IO<A>::ld(x, e - back * Di), p);
-  }
-  const float s = sigmoid_f(p);
-  dp[e] = (IO<A>::ld(du, e) + du_extra[e]) * (s * (1.0f + p * (1.0f - s)));
-}
-
-// adjoint of the conv for the input: d_x[s] = sum_k w[i,k] dp[s + K-1-k]
-template <Act A>
-__global__ void __launch_bounds__(kThreads) conv_dx_kernel(const float* __restrict__ dp, const float* __restrict__ cw,
-                                                          void* __restrict__ dx, int64_t T, int64_t Di, int K,
-                                                          unsigned nchb) {
-  int64_t e, i, t;
-  if (!row_channel(T, Di, nchb, &e, &i, &t)) return;
-  float g = 0.0f;
-  for (int k = 0; k < K; ++k) {
-    const int64_t ahead = K - 1 - k;   // dp_{t + ahead} read x_t through tap k
-    if (t + ahead < T) g = fmaf(cw[i * K + k], dp[e + ahead * Di], g);
-  }
-  IO<A>::st(dx, e, g);
-}
-
-// conv weight / bias gradient partials over a block of steps of one batch
-// row: part_w[(b, tb), i, k] = sum_t dp_t x_{t-K+1+k}, part_b[(b, tb), i] =
-// sum_t dp_t; steps in ascending order
-template <Act A>
-__global__ void __launch_bounds__(kThreads) conv_wgrad_part_kernel(const float* __restrict__ dp,
-                                                                  const void* __restrict__ x,
-                                                                  float* __restrict__ part_w,
-                                                                  float* __restrict__ part_b, int64_t T, int64_t Di,
-                                                                  int K, int64_t steps_per_blk, int64_t nblk_t) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= Di) return;
-  const int64_t b = blockIdx.y / nblk_t, tb = blockIdx.y % nblk_t;
-  const int64_t t0 = tb * steps_per_blk;
-  const int64_t t1 = t0 + steps_per_blk < T ? t0 + steps_per_blk : T;
-  float acc[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  float win[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // win[m] = x_{t-1-m} (zero before t = 0)
-  for (int m = 0; m < 3; ++m)
-    if (t0 - 1 - m >= 0) win[m] = IO<A>::ld(x, ((b * T) + t0 - 1 - m) * Di + i);
-  for (int64_t t = t0; t < t1; ++t) {
-    const int64_t e = (b * T + t) * Di + i;
-    const float xt = IO<A>::ld(x, e);
-    const float g = dp[e];
-    // tap k reads x_{t-(K-1-k)}: x_t for k = K-1, else win[K-2-k]
+                                                                int64_t T, int64_t Di, int K, unsigned nchb,
+                                                                unsigned ntb) {
+  ConvTile c;
+  if (!conv_tile(T, Di, nchb, ntb, &c)) return;
+  float w[4] = {0.0f, 0.0f, 0.0f, 0.0f}, win[3] = {0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < K; ++k) w[k] = cw[c.i * K + k];
+  const float bias = cb[c.i];
+  const int64_t base = c.b * T * Di + c.i;
+  for (int m = 0; m < K - 1; ++m)
+    if (c.t0 - 1 - m >= 0) win[m] = IO<A>::ld(x, base + (c.t0 - 1 - m) * Di);
+  for (int64_t t = c.t0; t < c.t1; ++t) {
+    const float xt = IO<A>::ld(x, base + t * Di);
+    float p = fmaf(w[K - 1], xt, bias);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (k < K) acc[k] = fmaf(g, k == K - 1 ? xt : win[K - 2 - k], acc[k]);
-    acc[4] += g;
+    for (int k = 0; k < 3; ++k)
+      if (k < K - 1) p = fmaf(w[k], win[K - 2 - k], p);
+    IO<A>::st(u, base + t * Di, p * sigmoid_f(p));
     win[2] = win[1];
     win[1] = win[0];
     win[0] = xt;
   }
-  float* out = part_w + (static_cast<int64_t>(blockIdx.y) * Di + i) * K;
-  for (int k = 0; k < K; ++k) out[k] = acc[k];
-  part_b[static_cast<int64_t>(blockIdx.y) * Di + i] = acc[4];
+}
+
+// Adjoint of F4a in one pass over a tile, forward in time:
+//   dp_t   = (d_u_t + d_u_extra_t) * silu'(p_t)          (p_t recomputed)
+//   d_x_s  = sum_k w[i,k] dp_{s+K-1-k}, emitted at t = s + K-1 as
+//            sum_k w[i,k] dp_{t-k} (dpw[k] holds dp_{t-k})
+//   part_w[blk, i, k] = sum_t dp_t x_{t-(K-1-k)},  part_b[blk, i] = sum_t dp_t
+// The K-1 steps after the tile are recomputed for the d_x of its last steps
+// (they enter no weight partial); past the sequence end dp is zero.
+template <Act A>
+__global__ void __launch_bounds__(kThreads) conv_bwd_kernel(const void* __restrict__ x, const float* __restrict__ cw,
+                                                           const float* __restrict__ cb, const void* __restrict__ du,
+                                                           const float* __restrict__ du_extra,
+                                                           void* __restrict__ dx, float* __restrict__ part_w,
+                                                           float* __restrict__ part_b, int64_t T, int64_t Di, int K,
+                                                           unsigned nchb, unsigned ntb) {
+  ConvTile c;
+  if (!conv_tile(T, Di, nchb, ntb, &c)) return;
+  float w[4] = {0.0f, 0.0f, 0.0f, 0.0f}, win[3] = {0.0f, 0.0f, 0.0f}, dpw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc_b = 0.0f;
+  for (int k = 0; k < K; ++k) w[k] = cw[c.i * K + k];
+  const float bias = cb[c.i];
+  const int64_t base = c.b * T * Di + c.i;
+  for (int m = 0; m < K - 1; ++m)
+    if (c.t0 - 1 - m >= 0) win[m] = IO<A>::ld(x, base + (c.t0 - 1 - m) * Di);
+  const int64_t t_stop = c.t1 + (K - 1);                  // last emitted d_x is step t1 - 1
+  const int64_t t_data = t_stop < T ? t_stop : T;          // steps with data
+  for (int64_t t = c.t0; t < t_stop; ++t) {
+    float g = 0.0f;
+    if (t < t_data) {
+      const int64_t e = base + t * Di;
+      const float xt = IO<A>::ld(x, e);
+      float p = fmaf(w[K - 1], xt, bias);
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        if (k < K - 1) p = fmaf(w[k], win[K - 2 - k], p);
+      const float sg = sigmoid_f(p);
+      g = (IO<A>::ld(du, e) + du_extra[e]) * (sg * (1.0f + p * (1.0f - sg)));
+      if (t < c.t1) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (k < K) acc[k] = fmaf(g, k == K - 1 ? xt : win[K - 2 - k], acc[k]);
+        acc_b += g;
+      }
+      win[2] = win[1];
+      win[1] = win[0];
+      win[0] = xt;
+    }
+    dpw[3] = dpw[2];
+    dpw[2] = dpw[1];
+    dpw[1] = dpw[0];
+    dpw[0] = g;
+    const int64_t s = t - (K - 1);
+    if (s >= c.t0 && s < T) {
+      float gx = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < K) gx = fmaf(w[k], dpw[k], gx);
+      IO<A>::st(dx, base + s * Di, gx);
+    }
+  }
+  const int64_t blk = static_cast<int64_t>(blockIdx.x / nchb);   // b * ntb + tb
+  for (int k = 0; k < K; ++k) part_w[(blk * Di + c.i) * K + k] = acc[k];
+  part_b[blk * Di + c.i] = acc_b;
 }
 
 // F4c tail: delta_raw = round(dt + b_dt[i])
@@ -260,6 +286,9 @@ dim3 grid1(int64_t n) { return dim3(static_cast<unsigned>((n + kThreads - 1) / k
 // row-blocked elementwise launches: rows = n / cols, ceil(cols / 256) blocks per row
 unsigned nchb(const Op& o) { return static_cast<unsigned>((o.cols + kThreads - 1) / kThreads); }
 dim3 grid_rows(const Op& o) { return dim3(static_cast<unsigned>(o.n / o.cols) * nchb(o)); }
+// conv tiles: batch rows * step tiles * channel blocks
+unsigned ntb(const Op& o) { return static_cast<unsigned>((o.T + kConvTT - 1) / kConvTT); }
+dim3 grid_conv(const Op& o) { return dim3(static_cast<unsigned>(o.n / o.cols / o.T) * ntb(o) * nchb(o)); }
 
 template <Act A>
 hipError_t dispatch(const Op& o, hipStream_t st) {
@@ -270,19 +299,12 @@ hipError_t dispatch(const Op& o, hipStream_t st) {
                          o.f3, o.cols, o.eps);
       break;
     case OpKind::ConvSiluFwd:
-      hipLaunchKernelGGL(conv_silu_fwd_kernel<A>, grid_rows(o), blk, 0, st, o.c0, o.f0, o.f1, o.v0, o.T, o.cols, o.K,
-                         nchb(o));
+      hipLaunchKernelGGL(conv_silu_fwd_kernel<A>, grid_conv(o), blk, 0, st, o.c0, o.f0, o.f1, o.v0, o.T, o.cols, o.K,
+                         nchb(o), ntb(o));
       break;
-    case OpKind::ConvSiluDp:
-      hipLaunchKernelGGL(conv_silu_dp_kernel<A>, grid_rows(o), blk, 0, st, o.c0, o.f0, o.f1, o.c1, o.f2, o.f3, o.T,
-                         o.cols, o.K, nchb(o));
-      break;
-    case OpKind::ConvDx:
-      hipLaunchKernelGGL(conv_dx_kernel<A>, grid_rows(o), blk, 0, st, o.f0, o.f1, o.v0, o.T, o.cols, o.K, nchb(o));
-      break;
-    case OpKind::ConvWgradPart:
-      hipLaunchKernelGGL(conv_wgrad_part_kernel<A>, dim3(grid1(o.cols).x, static_cast<unsigned>(o.nblk)), blk, 0, st,
-                         o.f0, o.c0, o.f3, o.f6, o.T, o.cols, o.K, o.per_blk, o.nblk_t);
+    case OpKind::ConvBwd:
+      hipLaunchKernelGGL(conv_bwd_kernel<A>, grid_conv(o), blk, 0, st, o.c0, o.f0, o.f1, o.c1, o.f2, o.v0, o.f3, o.f6,
+                         o.T, o.cols, o.K, nchb(o), ntb(o));
       break;
     case OpKind::BiasRound:
       hipLaunchKernelGGL(bias_round_kernel<A>, grid_rows(o), blk, 0, st, o.f0, o.f1, o.v0, o.T, o.cols, nchb(o));
@@ -301,6 +323,8 @@ hipError_t dispatch(const Op& o, hipStream_t st) {
 }
 
 }  // namespace
+
+int64_t conv_step_tiles(int64_t T) { return (T + kConvTT - 1) / kConvTT; }
 
 hipError_t launch(const Op& o, Act act, hipStream_t st) {
   const dim3 blk(kThreads);
