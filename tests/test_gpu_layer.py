@@ -6,9 +6,13 @@ stores typed, so both sides start every step from the same values.  What
 remains are elements whose f32 (GPU) and f64 (oracle) values fall on
 opposite sides of a rounding boundary: such an element differs by one unit
 in the last place of the activation dtype (2^-8 relative in bf16) and enters
-the f32 outputs as one term of a sum.  Tolerance per tensor, as
-max|gpu - oracle| / max(1, max|oracle|): 2e-3 for the f32 outputs of a
-bf16 / f16 layer, 1e-4 for an f32 layer.
+every later step, and the longer the core's recurrence the more often its
+f32 and f64 values straddle a boundary.  An f32 layer (no 16-bit rounding)
+at the same widths and length matches to about 1e-6, which separates that
+effect from the arithmetic.  Tolerance per tensor, as
+max|gpu - oracle| / max(1, max|oracle|): 1e-2 for the f32 outputs of a
+bf16 / f16 layer (half of the core's 2e-2 for typed outputs; measured up to
+5e-3 at the 2.8B widths), 1e-4 for an f32 layer.
 """
 import numpy as np
 import pytest
@@ -19,7 +23,7 @@ from oracle import layer as OL
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-3, "f16": 2e-3}
+TOL = {"f32": 1e-4, "bf16": 1e-2, "f16": 1e-2}
 
 
 @pytest.fixture(scope="module")
@@ -142,3 +146,12 @@ def test_layer_errors(mscan):
         mscan.layer_fwd(layer.dims, weights, resid, resid_out=resid, saved=layer.saved, workspace=layer.workspace)
     torch.cuda.synchronize()
     assert torch.all(layer.resid_out == 7.0)
+
+
+@pytest.mark.parametrize("dm,Di,R,T,act", [(768, 1536, 48, 2048, "bf16"), (768, 1536, 48, 2048, "f32"),
+                                            (2560, 5120, 160, 256, "bf16")])
+def test_layer_full_widths_one_row(mscan, dm, Di, R, T, act):
+    """The measured layer widths (130M: d_model 768, d_inner 1536; 2.8B:
+    2560, 5120) at one batch row, every output against the oracle."""
+    w = workloads.LayerWorkload("layer_full_dm%d_%s" % (dm, act), 1, T, dm, Di, 16, R, 4, act)
+    check_layer(mscan, w)
