@@ -6,6 +6,7 @@
 #include <cstring>
 #include <string>
 
+#include "bwd_table.h"
 #include "mamba_scan.h"
 #include "scan_common.h"
 
@@ -117,6 +118,13 @@ void choose_segments(int hint, int64_t waves, int64_t ntiles, int64_t enough, in
   *S = static_cast<int>((ntiles + *per - 1) / *per);
 }
 
+// Backward segment count (see kCarryShare below): the caller's `hint`, else
+// one segment when `waves` reaches kWantWaves, else the S in 1 .. about twice
+// kWantWaves / waves (at least kMinSegmentTiles tiles per segment) with the
+// smallest ceil(S * waves / resident) / S + kCarryShare * (S-1) / S; ties go
+// to fewer segments.
+void choose_segments_bwd(int hint, int64_t waves, int64_t resident, int64_t ntiles, int* S, int64_t* per);
+
 // Waves that fill the GPU (1024 SIMDs).  The forward's aggregate pass costs
 // about 40% of a forward, so it splits only below 2 waves per SIMD; the
 // backward's costs about a fifth of a backward and always pays for itself
@@ -124,12 +132,44 @@ void choose_segments(int hint, int64_t waves, int64_t ntiles, int64_t enough, in
 constexpr int64_t kFwdEnoughWaves = 2048;
 constexpr int64_t kWantWaves = 8192;
 constexpr int64_t kMinSegmentTiles = 8;
+// Backward segments.  The main pass runs in rounds of `resident` waves (the
+// waves per SIMD its kernel is built for, on all 1024 SIMDs), and a segment
+// takes 1/S of an unsplit sweep, so S segments cost about
+// ceil(S * waves / resident) / S sweeps; the carry pass adds about
+// kCarryShare of a sweep times (S-1)/S.  Measured at T=8192, d_inner 5120
+// (1280 waves per segment, 3072 resident): S = 3 / 4 / 5 / 7 / 12 gave
+// backward 2.12 / 1.85 / 1.99 / 1.77 / 1.71 ms, the order this cost predicts.
+constexpr double kCarryShare = 0.1;
+
+void choose_segments_bwd(int hint, int64_t waves, int64_t resident, int64_t ntiles, int* S, int64_t* per) {
+  int64_t s = 1;
+  if (hint > 0) {
+    s = hint;
+  } else if (waves < kWantWaves && resident > 0) {
+    int64_t hi = 2 * ((kWantWaves + waves - 1) / waves);
+    const int64_t cap = ntiles / kMinSegmentTiles;
+    hi = hi < cap ? hi : cap;
+    hi = hi < kMaxSegments ? hi : kMaxSegments;
+    double best = 0.0;
+    for (int64_t c = 1; c <= (hi > 1 ? hi : 1); ++c) {
+      const double rounds = static_cast<double>((c * waves + resident - 1) / resident);
+      const double cost = rounds / static_cast<double>(c) + kCarryShare * static_cast<double>(c - 1) / static_cast<double>(c);
+      if (c == 1 || cost < best - 1e-12) {
+        best = cost;
+        s = c;
+      }
+    }
+  }
+  s = s < ntiles ? s : ntiles;
+  s = s < 1 ? 1 : s;
+  *per = (ntiles + s - 1) / s;
+  *S = static_cast<int>((ntiles + *per - 1) / *per);
+}
 
 // threads per workgroup of the forward / backward kernels (their launch tables)
 int64_t fwd_threads(int64_t ds) { return mscan::kFwdCpw * (ds == 32 ? ds / 2 : ds); }
 int64_t bwd_threads(int64_t ds, int L) {
-  const int64_t spl = ds == 4 ? 1 : ds == 8 ? (L == 32 ? 1 : 2) : ds == 16 ? (L == 32 ? 1 : 2) : 2;
-  return mscan::kBwdCpw * (ds / spl);
+  return mscan::kBwdCpw * (ds / mscan::bwd_states_per_thread(static_cast<int>(ds), L));
 }
 
 int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
@@ -196,8 +236,8 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
     pl->Sb = 1;
     pl->segb_tiles = pl->nC;
   } else {
-    choose_segments(d->segments, waves_b, pl->nC, kWantWaves, kWantWaves, kMinSegmentTiles, &pl->Sb,
-                    &pl->segb_tiles);
+    const int64_t resident = 1024 * static_cast<int64_t>(mscan::bwd_waves_per_simd(static_cast<int>(d->d_state), L, false));
+    choose_segments_bwd(d->segments, waves_b, resident, pl->nC, &pl->Sb, &pl->segb_tiles);
   }
   // a launch holds at most 2^32 - 1 threads: the tiled forward and backward
   // (all segments in one grid) and the reduction (one thread per d_xdbl B/C

@@ -46,6 +46,7 @@
 // The fused entry runs one segment (the conv backward of a segment's last
 // K-1 steps needs the next segment's first ones).
 #pragma once
+#include "bwd_table.h"
 #include "scan_carry.h"
 #include "scan_common.h"
 
@@ -522,19 +523,10 @@ static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
 // S > 1, is enqueued before it by the caller)
 template <Act A>
 hipError_t launch_bwd_a(const BwdArgs& p, int ds, int L, hipStream_t st) {
-  // (d_state, checkpoint interval) -> states per thread, sub-tile steps, then
-  // operand look-ahead and waves per SIMD for the scan entry and for the
-  // fused entry.  A thread keeps h_t and dA_t of its SPL states for all L
-  // steps of a tile in registers (2 * SPL * L of them); a workgroup must be
-  // whole waves.  Three waves per SIMD hide the LDS and barrier waits best
-  // (measured: T=8192 backward 2.04 -> 1.81 ms) where the registers allow
-  // it without spilling (168 or fewer: the look-ahead is shortened to fit).
+  // the configurations are listed in bwd_table.h
 #define MSCAN_CASE(DS_, L_, SPL_, SUB_, PD_, W_, PDF_, WF_) \
   if (ds == DS_ && L == L_) return launch_bwd_t<A, DS_, SPL_, L_, SUB_, PD_, W_, PDF_, WF_>(p, st);
-  MSCAN_CASE(4, 16, 1, 4, 4, 3, 4, 2) MSCAN_CASE(4, 32, 1, 4, 1, 2, 1, 2)
-  MSCAN_CASE(8, 16, 2, 4, 4, 2, 4, 2) MSCAN_CASE(8, 32, 1, 8, 4, 2, 4, 2)
-  MSCAN_CASE(16, 16, 2, 8, 1, 3, 4, 2) MSCAN_CASE(16, 32, 1, 8, 4, 2, 4, 2)
-  MSCAN_CASE(32, 16, 2, 8, 4, 2, 4, 2)
+  MSCAN_BWD_CONFIGS(MSCAN_CASE)
 #undef MSCAN_CASE
   return hipErrorInvalidValue;
 }
