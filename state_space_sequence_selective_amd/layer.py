@@ -28,18 +28,25 @@ class LayerCore:
         self.d_x = torch.empty(act, dtype=at, **kw)
         self.d_delta_raw = torch.empty(act, dtype=at, **kw)
         self.d_z = torch.empty(act, dtype=at, **kw) if gate else None
-        self.d_xdbl = torch.zeros((d.batch, d.seqlen, d.xdbl_dim), dtype=f, **kw)
-        self.d_a_log = torch.zeros((d.d_inner, d.d_state), dtype=f, **kw)
-        self.d_D = torch.zeros((d.d_inner,), dtype=f, **kw)
-        self.d_conv_w = torch.zeros((d.d_inner, d.d_conv), dtype=f, **kw) if self.fused else None
-        self.d_conv_b = torch.zeros((d.d_inner,), dtype=f, **kw) if self.fused else None
+        # the accumulated gradients share one arena (256-byte aligned views), so
+        # clearing them once per step is a single fill
+        shapes = [("d_xdbl", (d.batch, d.seqlen, d.xdbl_dim)), ("d_a_log", (d.d_inner, d.d_state)),
+                  ("d_D", (d.d_inner,))]
+        if self.fused:
+            shapes += [("d_conv_w", (d.d_inner, d.d_conv)), ("d_conv_b", (d.d_inner,))]
+        sizes = [-(-torch.Size(s).numel() // 64) * 64 for _, s in shapes]   # floats, rounded up to 256 bytes
+        self._grad_arena = torch.zeros(sum(sizes), dtype=f, **kw)
+        off = 0
+        for (name, shape), n in zip(shapes, sizes):
+            setattr(self, name, self._grad_arena[off:off + torch.Size(shape).numel()].view(shape))
+            off += n
+        if not self.fused:
+            self.d_conv_w = self.d_conv_b = None
         self.workspace = torch.empty(_lib.workspace_bytes(d), dtype=torch.uint8, **kw)
 
     def zero_grads(self):
         """Parameter grads and d_xdbl accumulate; clear them once per step."""
-        for t in (self.d_xdbl, self.d_a_log, self.d_D, self.d_conv_w, self.d_conv_b):
-            if t is not None:
-                t.zero_()
+        self._grad_arena.zero_()
 
     def forward(self, inp: dict, stream=None):
         d = self.dims
