@@ -149,17 +149,16 @@ scan_bwd_kernel(const BwdArgs p) {
   extern __shared__ __attribute__((aligned(16))) char s_raw[];
   __shared__ float4 s_st[L][CPW];      // delta, delta*u, dy, u
   __shared__ float s_x[FUSED ? L + KMAX - 1 : 1][CPW];
-  __shared__ float s_bc[L][2][DS];
+  __shared__ float s_bc[L][DS][2];     // (B_t[n], C_t[n]) per state
   // per-group partials per (step of the sub-tile, channel), padded against
   // bank conflicts
-  __shared__ float s_su[NBUF][G][SPS];   // per-group sum_n dh B
-  __shared__ float s_sd[NBUF][G][SPS];   // per-group sum_n dh A dA h_{t-1}
+  __shared__ float2 s_part[NBUF][G][SPS];   // per-group (sum_n dh B, sum_n dh A dA h_{t-1})
   __shared__ float s_red[G][CPW * (NO + 1)];
   __shared__ float s_dp[SUB + KMAX][CPW];
   // the compiler checks only the static arrays; with the dynamic raw tile a
   // launch over the limit fails at dispatch
-  static_assert(bwd_raw_bytes<A, L, FUSED, CPW>() + sizeof(s_st) + sizeof(s_x) + sizeof(s_bc) + sizeof(s_su) +
-                        sizeof(s_sd) + sizeof(s_red) + sizeof(s_dp) <= kLdsBytes,
+  static_assert(bwd_raw_bytes<A, L, FUSED, CPW>() + sizeof(s_st) + sizeof(s_x) + sizeof(s_bc) + sizeof(s_part) +
+                        sizeof(s_red) + sizeof(s_dp) <= kLdsBytes,
                 "workgroup LDS (static + dynamic raw tile) exceeds what gfx950 allows");
 
   const int tid = threadIdx.x;
@@ -262,7 +261,8 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int q = 0; q < BCPT; ++q) {
       const int j = tid + q * NT;
-      (&s_bc[0][0][0])[j] = j / (2 * DS) < len ? io::cvt(bcn[q]) : 0.0f;
+      const int tt = j / (2 * DS), m = j % (2 * DS);   // row order: B_0..B_{DS-1}, C_0..C_{DS-1}
+      (&s_bc[0][0][0])[tt * 2 * DS + (m < DS ? 2 * m : 2 * (m - DS) + 1)] = tt < len ? io::cvt(bcn[q]) : 0.0f;
     }
     if (FUSED) {
       for (int j = tid; j < (L + KMAX - 1) * CPW; j += NT) {
@@ -329,8 +329,8 @@ scan_bwd_kernel(const BwdArgs p) {
       q_st[sl] = s_st[tt][c];
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
-        q_b[sl][s] = s_bc[tt][0][g * SPL + s];
-        q_c[sl][s] = s_bc[tt][1][g * SPL + s];
+        q_b[sl][s] = s_bc[tt][g * SPL + s][0];
+        q_c[sl][s] = s_bc[tt][g * SPL + s][1];
       }
     };
 
@@ -402,8 +402,7 @@ scan_bwd_kernel(const BwdArgs p) {
           sd = fmaf(qv, an[s], sd);
           red[c * (NO + 1) + q * SPL + s] = dh * cur.y;
         }
-        s_su[bi][g][q * CPW + c] = su;
-        s_sd[bi][g][q * CPW + c] = sd;
+        s_part[bi][g][q * CPW + c] = make_float2(su, sd);
         __builtin_amdgcn_sched_barrier(0);
       }
       wave_lds_sync();
@@ -434,8 +433,9 @@ scan_bwd_kernel(const BwdArgs p) {
         float su = 0.0f, sd = 0.0f;
 #pragma unroll
         for (int w = 0; w < G; ++w) {
-          su += s_su[bi][w][q * CPW + c];
-          sd += s_sd[bi][w][q * CPW + c];
+          const float2 pv = s_part[bi][w][q * CPW + c];
+          su += pv.x;
+          sd += pv.y;
         }
         float du = fmaf(st.x, su, Dv * st.z);
         const float ddl = fmaf(st.w, su, sd);
@@ -488,11 +488,11 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int k2 = 0; k2 < KMAX; ++k2)
       if (qd == k2 + 2) v = acc_cw[k2];
-    s_su[0][g][c] = v;
+    s_part[0][g][c].x = v;
     __syncthreads();
     if (g == 0 && on) {
       float tot = 0.0f;
-      for (int w = 0; w < G; ++w) tot += s_su[0][w][c];
+      for (int w = 0; w < G; ++w) tot += s_part[0][w][c].x;
       // layout within PW: [Ds a_log | 1 D | K conv_w | 1 conv_b]
       const int slot = qd == 0 ? DS : (qd == 1 ? DS + 1 + K : DS + 1 + (qd - 2));
       p.part_par[pb + slot] = tot;
