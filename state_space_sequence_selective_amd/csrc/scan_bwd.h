@@ -141,7 +141,10 @@ scan_bwd_kernel(const BwdArgs p) {
                             L * 2 * DS * 4 + G * CPW * (NO + 1) * 4 + (SUB + KMAX) * CPW * 4;
   constexpr int SPS = SUB * CPW + group_pad<CPW>(SUB * CPW);
   constexpr int PART = 2 * G * SPS * 4;
-  constexpr int NBUF = LDS_FIXED + 2 * PART <= 52 * 1024 ? 2 : 1;   // 3 workgroups per CU
+  // double-buffer when LDS still allows the workgroups per CU that WPE waves
+  // per SIMD need (CPW * G / 64 waves per workgroup, 4 SIMDs per CU)
+  constexpr int WG_PER_CU = (WPE * 4) / ((CPW * G + 63) / 64) > 0 ? (WPE * 4) / ((CPW * G + 63) / 64) : 1;
+  constexpr int NBUF = LDS_FIXED + 2 * PART <= kLdsBytes / WG_PER_CU - 1024 ? 2 : 1;
   using io = IO<A>;
 
   // raw tile: x (with halo) | delta_raw | dout | z | y
