@@ -119,6 +119,7 @@ __global__ void __launch_bounds__(kThreads) rmsnorm_wgrad_part_kernel(const floa
 // once (plus a K-1 step halo).  Block id = (b * ntb + tb) * nchb + channel
 // block, ntb = ceil(T / kConvTT).
 constexpr int kConvTT = 64;
+constexpr int kConvU = 8;   // steps whose inputs are loaded together
 
 struct ConvTile {
   int64_t b, t0, t1, i;
@@ -150,16 +151,27 @@ __global__ void __launch_bounds__(kThreads) conv_silu_fwd_kernel(const void* __r
   const int64_t base = c.b * T * Di + c.i;
   for (int m = 0; m < K - 1; ++m)
     if (c.t0 - 1 - m >= 0) win[m] = IO<A>::ld(x, base + (c.t0 - 1 - m) * Di);
-  for (int64_t t = c.t0; t < c.t1; ++t) {
-    const float xt = IO<A>::ld(x, base + t * Di);
-    float p = fmaf(w[K - 1], xt, bias);
+  // kConvU steps' inputs are loaded before any is used (addresses clamped to
+  // the tile, so every load is unconditional): several loads in flight per
+  // thread instead of one round trip per step
+  for (int64_t t0 = c.t0; t0 < c.t1; t0 += kConvU) {
+    float xs[kConvU];
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
-      if (k < K - 1) p = fmaf(w[k], win[K - 2 - k], p);
-    IO<A>::st(u, base + t * Di, p * sigmoid_f(p));
-    win[2] = win[1];
-    win[1] = win[0];
-    win[0] = xt;
+    for (int j = 0; j < kConvU; ++j) xs[j] = IO<A>::ld(x, base + (t0 + j < c.t1 ? t0 + j : c.t1 - 1) * Di);
+#pragma unroll
+    for (int j = 0; j < kConvU; ++j) {
+      if (t0 + j < c.t1) {
+        const float xt = xs[j];
+        float p = fmaf(w[K - 1], xt, bias);
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+          if (k < K - 1) p = fmaf(w[k], win[K - 2 - k], p);
+        IO<A>::st(u, base + (t0 + j) * Di, p * sigmoid_f(p));
+        win[2] = win[1];
+        win[1] = win[0];
+        win[0] = xt;
+      }
+    }
   }
 }
 
@@ -188,38 +200,50 @@ __global__ void __launch_bounds__(kThreads) conv_bwd_kernel(const void* __restri
     if (c.t0 - 1 - m >= 0) win[m] = IO<A>::ld(x, base + (c.t0 - 1 - m) * Di);
   const int64_t t_stop = c.t1 + (K - 1);                  // last emitted d_x is step t1 - 1
   const int64_t t_data = t_stop < T ? t_stop : T;          // steps with data
-  for (int64_t t = c.t0; t < t_stop; ++t) {
-    float g = 0.0f;
-    if (t < t_data) {
-      const int64_t e = base + t * Di;
-      const float xt = IO<A>::ld(x, e);
-      float p = fmaf(w[K - 1], xt, bias);
+  for (int64_t t0 = c.t0; t0 < t_stop; t0 += kConvU) {
+    // kConvU steps' inputs first (clamped to the data, so unconditional)
+    float xs[kConvU], gs[kConvU];
 #pragma unroll
-      for (int k = 0; k < 3; ++k)
-        if (k < K - 1) p = fmaf(w[k], win[K - 2 - k], p);
-      const float sg = sigmoid_f(p);
-      g = (IO<A>::ld(du, e) + du_extra[e]) * (sg * (1.0f + p * (1.0f - sg)));
-      if (t < c.t1) {
+    for (int j = 0; j < kConvU; ++j) {
+      const int64_t e = base + (t0 + j < t_data ? t0 + j : t_data - 1) * Di;
+      xs[j] = IO<A>::ld(x, e);
+      gs[j] = IO<A>::ld(du, e) + du_extra[e];
+    }
+#pragma unroll
+    for (int j = 0; j < kConvU; ++j) {
+      const int64_t t = t0 + j;
+      if (t >= t_stop) break;
+      float g = 0.0f;
+      if (t < t_data) {
+        const float xt = xs[j];
+        float p = fmaf(w[K - 1], xt, bias);
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+          if (k < K - 1) p = fmaf(w[k], win[K - 2 - k], p);
+        const float sg = sigmoid_f(p);
+        g = gs[j] * (sg * (1.0f + p * (1.0f - sg)));
+        if (t < c.t1) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (k < K) acc[k] = fmaf(g, k == K - 1 ? xt : win[K - 2 - k], acc[k]);
+          acc_b += g;
+        }
+        win[2] = win[1];
+        win[1] = win[0];
+        win[0] = xt;
+      }
+      dpw[3] = dpw[2];
+      dpw[2] = dpw[1];
+      dpw[1] = dpw[0];
+      dpw[0] = g;
+      const int64_t s = t - (K - 1);
+      if (s >= c.t0 && s < T) {
+        float gx = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (k < K) acc[k] = fmaf(g, k == K - 1 ? xt : win[K - 2 - k], acc[k]);
-        acc_b += g;
+          if (k < K) gx = fmaf(w[k], dpw[k], gx);
+        IO<A>::st(dx, base + s * Di, gx);
       }
-      win[2] = win[1];
-      win[1] = win[0];
-      win[0] = xt;
-    }
-    dpw[3] = dpw[2];
-    dpw[2] = dpw[1];
-    dpw[1] = dpw[0];
-    dpw[0] = g;
-    const int64_t s = t - (K - 1);
-    if (s >= c.t0 && s < T) {
-      float gx = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (k < K) gx = fmaf(w[k], dpw[k], gx);
-      IO<A>::st(dx, base + s * Di, gx);
     }
   }
   const int64_t blk = static_cast<int64_t>(blockIdx.x / nchb);   // b * ntb + tb

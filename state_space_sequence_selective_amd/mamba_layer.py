@@ -24,12 +24,19 @@ class MambaLayer:
         self.d_resid_in = torch.empty(rs, dtype=torch.float32, **kw)
         self.saved = torch.empty(_lib.layer_saved_bytes(d), dtype=torch.uint8, **kw)
         self.workspace = torch.empty(_lib.layer_workspace_bytes(d), dtype=torch.uint8, **kw)
-        self.grads = {n: torch.zeros(s, dtype=torch.float32, **kw) for n, s in _lib.layer_param_shapes(d).items()}
+        # the gradients share one arena (views on 256-byte boundaries), so
+        # clearing them once per step is a single fill
+        shapes = _lib.layer_param_shapes(d)
+        sizes = {n: -(-torch.Size(s).numel() // 64) * 64 for n, s in shapes.items()}
+        self._grad_arena = torch.zeros(sum(sizes.values()), dtype=torch.float32, **kw)
+        self.grads, off = {}, 0
+        for n, s in shapes.items():
+            self.grads[n] = self._grad_arena[off:off + torch.Size(s).numel()].view(s)
+            off += sizes[n]
 
     def zero_grads(self):
         """Weight gradients accumulate; clear them once per step."""
-        for t in self.grads.values():
-            t.zero_()
+        self._grad_arena.zero_()
 
     def forward(self, resid_in, stream=None):
         _lib.layer_fwd(self.dims, self.weights, resid_in, resid_out=self.resid_out, saved=self.saved,
