@@ -46,12 +46,14 @@ FLOPS_BWD_ELEM = 21
 
 
 def kernel_source_hash():
-    """sha256 over the HIP sources (file names and contents, sorted)."""
+    """sha256 over the sources the scan core's kernels are built from (file
+    names and contents, sorted); the whole-layer kernels (layer_*) are left
+    out, since the counters it guards are those of the core's kernels."""
     import hashlib
     csrc = os.path.join(ROOT, "state_space_sequence_selective_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
+        if f.endswith((".hip", ".h")) and not f.startswith("layer_"):
             h.update(f.encode())
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
