@@ -60,7 +60,7 @@ scan_fwd_kernel(const FwdArgs p) {
   __shared__ __attribute__((aligned(16))) char s_raw0[RAW];
   __shared__ __attribute__((aligned(16))) char s_raw1[RAW];
   __shared__ float2 s_st[TT][CPW];     // delta, delta*u
-  __shared__ float s_bc[TT][2][DS];    // B_t | C_t as f32
+  __shared__ float s_bc[TT][DS][2];    // (B_t[n], C_t[n]) per state, f32
   // per-state-group partial C.h per (t, channel), padded against bank conflicts
   constexpr int YPS = TT * CPW + group_pad<CPW>(TT * CPW);
   __shared__ float s_yp[G][YPS];
@@ -139,7 +139,8 @@ scan_fwd_kernel(const FwdArgs p) {
 #pragma unroll
     for (int q = 0; q < BCPT; ++q) {
       const int j = tid + q * NT;
-      (&s_bc[0][0][0])[j] = j / (2 * DS) < len ? io::cvt(bc[q]) : 0.0f;
+      const int tt = j / (2 * DS), m = j % (2 * DS);   // row order: B_0..B_{DS-1}, C_0..C_{DS-1}
+      (&s_bc[0][0][0])[tt * 2 * DS + (m < DS ? 2 * m : 2 * (m - DS) + 1)] = tt < len ? io::cvt(bc[q]) : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
@@ -215,8 +216,8 @@ scan_fwd_kernel(const FwdArgs p) {
       q_st[sl] = s_st[tt][c];
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
-        q_b[sl][s] = s_bc[tt][0][gs * SPL + s];
-        q_c[sl][s] = s_bc[tt][1][gs * SPL + s];
+        q_b[sl][s] = s_bc[tt][gs * SPL + s][0];
+        q_c[sl][s] = s_bc[tt][gs * SPL + s][1];
       }
     };
 #pragma unroll
