@@ -110,6 +110,7 @@ def device_inputs(torch, w, inp):
 # (batch, d_inner) of the recurrent-step timings; d_state 16, dt_rank
 # d_inner / 32, conv width 4, bf16 activations, gate on
 RECURRENT_SHAPES = [(1, 2048), (64, 2048), (1, 5120), (16, 5120), (64, 5120)]
+GRAPH_STEPS = 64   # one-step calls captured per HIP graph
 
 
 def recurrent_bytes(w: workloads.Workload):
@@ -139,8 +140,7 @@ def recurrent(torch, pkg, calls: int, warmup: int):
         def call(k):
             _lib.conv_scan_gate_fwd(dims, dev["x"], dev["conv_w"], dev["conv_b"], cs[k % 2], dev["delta_raw"],
                                     dev["a_log"], dev["xdbl"], dev["D"], dev["z"], h[k % 2], out=out,
-                                    h_last=h[(k + 1) % 2], conv_state_last=cs[(k + 1) % 2], workspace=ws,
-                                    stream=stream)
+                                    h_last=h[(k + 1) % 2], conv_state_last=cs[(k + 1) % 2], workspace=ws)
 
         for k in range(warmup):
             call(k)
@@ -152,6 +152,29 @@ def recurrent(torch, pkg, calls: int, warmup: int):
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / calls
+        # the same ping-pong captured as one HIP graph of GRAPH_STEPS calls and
+        # replayed: the per-step cost without the host-side launch path
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for k in range(2):
+                call(k)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(GRAPH_STEPS):
+                call(k)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, calls // GRAPH_STEPS)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_graph = e0.elapsed_time(e1) * 1e3 / (reps * GRAPH_STEPS)
         nb = recurrent_bytes(w)
         print(json.dumps({"metric": "recurrent step latency (one-step fused forward, state in/out)",
                           "value": round(us, 2), "unit": "us/call", "higher_is_better": False, "calls": calls,
@@ -159,7 +182,8 @@ def recurrent(torch, pkg, calls: int, warmup: int):
                           "config": {"workload": w.name, "batch": B, "d_inner": Di, "d_state": w.d_state,
                                      "dt_rank": w.dt_rank, "d_conv": w.d_conv},
                           "algorithmic_bytes_per_call": nb,
-                          "GBps_at_algorithmic_bytes": round(nb / (us / 1e6) / 1e9, 1)}), flush=True)
+                          "GBps_at_algorithmic_bytes": round(nb / (us / 1e6) / 1e9, 1),
+                          "us_per_step_graph": round(us_graph, 2), "graph_steps": GRAPH_STEPS}), flush=True)
 
 
 def layer_flops(w: workloads.LayerWorkload):

@@ -1,0 +1,132 @@
+"""HIP-graph capture of the hot path.  The core entry points only enqueue
+kernels (no allocation, no memset, no synchronisation), so a whole training
+step of the layer core (clear the accumulated gradients, forward, backward)
+and a chain of recurrent decode steps can be captured once and replayed.
+Every replay is compared bit for bit with the eager result, with eager
+work (the outputs overwritten with NaN) and synchronisations between the
+replays.  Inputs come from the seeded workload generator; the oracle is not
+needed here (the eager path is pinned to it by test_gpu_parity.py)."""
+import numpy as np
+import pytest
+
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 3
+
+
+@pytest.fixture(scope="module")
+def mscan():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import state_space_sequence_selective_amd as m
+    m.load()
+    return m
+
+
+def _device_inputs(w, inp):
+    at = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.act]
+    dev = {}
+    for k, v in inp.items():
+        if v is None:
+            continue
+        dt = at if k in ("x", "delta_raw", "z", "dout", "xdbl", "d_u_extra") else torch.float32
+        dev[k] = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to("cuda", dt)
+    return dev
+
+
+def _replay_and_compare(graph, outputs: dict, ref: dict):
+    for r in range(REPLAYS):
+        for t in outputs.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, t in outputs.items():
+            assert torch.equal(t, ref[k]), "replay %d: %s differs from the eager step" % (r, k)
+
+
+def _capture(fn):
+    """Warm up on a side stream (default priority), then capture fn."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("name,seg", [("scan_gate_bf16", 0), ("scan_gate_bf16", 3), ("fused_f16", 0)])
+def test_training_step_replays(mscan, name, seg):
+    """zero_grads + forward + backward of LayerCore, captured and replayed:
+    the scan entry (unsplit and with 3 backward / forward segments, which
+    adds the aggregate passes) and the fused conv entry."""
+    if name == "fused_f16":
+        w = workloads.Workload("graph_fused", 2, 150, 96, 16, 6, 4, "f16", True)
+    else:
+        w = workloads.Workload("graph_scan", 2, 300, 160, 16, 6, 0, "bf16", True)
+    inp = workloads.make_inputs(w, 11)
+    dev = _device_inputs(w, inp)
+    dims = mscan.Dims.make(w.batch, w.seqlen, w.d_inner, w.d_state, w.dt_rank, w.d_conv, 16, w.act, seg)
+    core = mscan.LayerCore(dims, gate=True)
+
+    def step():
+        core.zero_grads()
+        core.forward(dev)
+        core.backward(dev, dev["dout"])
+
+    names = ["out", "y", "h_last", "ckpt", "d_x", "d_delta_raw", "d_z", "d_xdbl", "d_a_log", "d_D"]
+    if w.d_conv:
+        names += ["conv_state_last", "d_conv_w", "d_conv_b"]
+    step()
+    torch.cuda.synchronize()
+    ref = {n: getattr(core, n).clone() for n in names}
+    for n, t in ref.items():
+        assert torch.isfinite(t.float()).all(), n
+    g = _capture(step)
+    _replay_and_compare(g, {n: getattr(core, n) for n in names}, ref)
+
+
+def test_decode_chain_replays(mscan):
+    """Eight one-step fused forward calls, each reading the previous call's
+    SSM and conv state (decoding), captured as one graph."""
+    from state_space_sequence_selective_amd import _lib
+    B, Di, Ds, K, steps = 4, 256, 16, 4, 8
+    w = workloads.Workload("graph_decode", B, steps, Di, Ds, 8, K, "bf16", True)
+    inp = workloads.make_inputs(w, 12, h0=True, conv_state0=True)
+    dev = _device_inputs(w, inp)
+    per = [{k: dev[k][:, t:t + 1].contiguous() for k in ("x", "delta_raw", "z", "xdbl")} for t in range(steps)]
+    dims = mscan.Dims.make(B, 1, Di, Ds, w.dt_rank, K, 16, "bf16")
+    f32 = dict(device="cuda", dtype=torch.float32)
+    h = [dev["h0"]] + [torch.empty((B, Di, Ds), **f32) for _ in range(steps)]
+    cs = [dev["conv_state0"]] + [torch.empty((B, Di, K), **f32) for _ in range(steps)]
+    outs = [torch.empty((B, 1, Di), device="cuda", dtype=torch.bfloat16) for _ in range(steps)]
+    ws = torch.empty(_lib.workspace_bytes(dims), device="cuda", dtype=torch.uint8)
+
+    def chain():
+        for t in range(steps):
+            _lib.conv_scan_gate_fwd(dims, per[t]["x"], dev["conv_w"], dev["conv_b"], cs[t], per[t]["delta_raw"],
+                                    dev["a_log"], per[t]["xdbl"], dev["D"], per[t]["z"], h[t], out=outs[t],
+                                    h_last=h[t + 1], conv_state_last=cs[t + 1], workspace=ws)
+
+    chain()
+    torch.cuda.synchronize()
+    tensors = {"out%d" % t: outs[t] for t in range(steps)}
+    tensors.update({"h%d" % (t + 1): h[t + 1] for t in range(steps)})
+    tensors.update({"cs%d" % (t + 1): cs[t + 1] for t in range(steps)})
+    ref = {k: v.clone() for k, v in tensors.items()}
+    # the chain equals one 8-step call (the same step kernel, state kept in registers)
+    core = mscan.LayerCore(mscan.Dims.make(B, steps, Di, Ds, w.dt_rank, K, 16, "bf16"), gate=True)
+    core.forward(dev)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, 1), core.out)
+    assert torch.equal(h[steps], core.h_last)
+    g = _capture(chain)
+    _replay_and_compare(g, tensors, ref)
