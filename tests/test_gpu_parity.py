@@ -423,6 +423,33 @@ def _sampled_full(mscan, oracle_lib, name, sample):
     print(name, "sampled", {k: "%.2e" % v for k, v in rep.items()}, flush=True)
 
 
+def test_long_sequence_many_segments(mscan, oracle_lib):
+    """2^16 steps of one batch row at a narrow width: the library splits the
+    sequence into many segments, and 4096 segments when asked (one 16-step
+    tile each, the most the sequence allows), so the folds run chains of
+    thousands of (sum of delta, state) pairs in both directions.  Every
+    output against one oracle pass."""
+    w = workloads.Workload("long_T65536", 1, 1 << 16, 128, 16, 8, 0, "bf16", True)
+    inp = workloads.make_inputs(w, 13)
+    dev = _device_inputs(w, inp)
+    f, g = _oracle(oracle_lib, w, inp, 16)
+    for segments in (0, 4096):
+        core = mscan.LayerCore(_dims(mscan, w, 16, segments), gate=True)
+        core.zero_grads()
+        core.forward(dev)
+        core.backward(dev, dev["dout"])
+        torch.cuda.synchronize()
+        rep = {}
+        for name, gpu, ora, half in (("out", core.out, f["out"], True), ("y", core.y, f["y"], True),
+                                     ("h_last", core.h_last, f["h_last"], False),
+                                     ("ckpt", core.ckpt, f["ckpt"], False), ("d_x", core.d_x, g["d_x"], True),
+                                     ("d_delta_raw", core.d_delta_raw, g["d_delta_raw"], True),
+                                     ("d_z", core.d_z, g["d_z"], True), ("d_xdbl", core.d_xdbl, g["d_xdbl"], False),
+                                     ("d_a_log", core.d_a_log, g["d_a_log"], False), ("d_D", core.d_D, g["d_D"], False)):
+            _check(name, gpu, ora, half, rep)
+        print(w.name, "segments", segments, {k: "%.2e" % v for k, v in rep.items()}, flush=True)
+
+
 def test_full_size_130m_sampled(mscan, oracle_lib):
     _sampled_full(mscan, oracle_lib, "scan_130m_bf16", [0, 1, 63, 64, 700, 1535])
 
