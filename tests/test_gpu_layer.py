@@ -131,6 +131,23 @@ def test_layer_deterministic_and_accumulating(mscan):
         assert torch.equal(layer.grads[k], 2 * v), k
 
 
+def test_layer_backward_in_place(mscan):
+    """d_resid_in may be the d_resid_out buffer (the header allows it): the
+    same bits as with two buffers, gradients included."""
+    w = workloads.LayerWorkload("layer_inplace", 2, 80, 64, 128, 16, 4, 4, "bf16")
+    layer, inp, resid, d_out = run_layer(mscan, w)
+    ref_d = layer.d_resid_in.clone()
+    ref_g = {k: v.clone() for k, v in layer.grads.items()}
+    layer.zero_grads()
+    buf = d_out.clone()
+    mscan.layer_bwd(layer.dims, layer.weights, resid, layer.saved, buf, d_resid_in=buf, grads=layer.grads,
+                    workspace=layer.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref_d)
+    for k, v in ref_g.items():
+        assert torch.equal(layer.grads[k], v), k
+
+
 def test_layer_errors(mscan):
     """Rejected calls name the entry point and leave the outputs untouched."""
     w = workloads.LayerWorkload("layer_err", 1, 16, 32, 64, 16, 4, 4, "bf16")
