@@ -410,6 +410,10 @@ def _sampled_full(mscan, oracle_lib, name, sample):
     _check("d_z", core.d_z[..., S], g["d_z"], half, rep)
     _check("d_a_log", core.d_a_log[S], g["d_a_log"], False, rep)
     _check("d_D", core.d_D[S], g["d_D"], False, rep)
+    if w.d_conv:
+        _check("conv_state_last", core.conv_state_last[:, S], f["conv_state_last"], False, rep)
+        _check("d_conv_w", core.d_conv_w[S], g["d_conv_w"], False, rep)
+        _check("d_conv_b", core.d_conv_b[S], g["d_conv_b"], False, rep)
     # d_C at the step before each checkpoint, from the (just checked) checkpoints:
     # d_C[b, cL-1, n] = sum_i dy[b, cL-1, i] h_{cL-1}[b, i, n], dy = dout silu(z)
     L = dims.L
@@ -452,6 +456,12 @@ def test_long_sequence_many_segments(mscan, oracle_lib):
 
 def test_full_size_130m_sampled(mscan, oracle_lib):
     _sampled_full(mscan, oracle_lib, "scan_130m_bf16", [0, 1, 63, 64, 700, 1535])
+
+
+def test_full_size_fused_layer_sampled(mscan, oracle_lib):
+    """One layer of the 24-layer fused f16 workload (B=8, T=4096, d_inner
+    2048, conv width 4, dt_rank 64) at full size, conv outputs included."""
+    _sampled_full(mscan, oracle_lib, "fused_24l_f16", [0, 1, 1023, 2047])
 
 
 def test_full_size_t8192_sampled(mscan, oracle_lib):
