@@ -169,6 +169,40 @@ def test_null_and_misaligned_pointers_rejected_before_launch(pkg):
     assert rc == 1 and "mamba_conv_scan_gate_bwd: d_conv" in pkg.last_error()
 
 
+def test_last_error_is_per_thread(pkg):
+    """mamba_last_error() is thread-local: two threads whose calls fail for
+    different reasons, interleaved, each read back their own message (the
+    library drops the interpreter lock during a call, so they do overlap)."""
+    import threading
+    lib = _raw(pkg)
+    good = ctypes.c_void_p(0x10000)      # never dereferenced: the calls fail before any launch
+    d = _dims(pkg)
+    bad = _dims(pkg, segments=-1)
+    wrong = []
+
+    def worker(kind):
+        size = ctypes.c_size_t(0)
+        for _ in range(3000):
+            if kind == 0:
+                rc = lib.mamba_scan_fwd(ctypes.byref(d), None, good, good, good, None, None, None, good, None, None,
+                                        None, None, ctypes.c_size_t(0), None)
+                msg = pkg.last_error()
+                ok = rc == 1 and msg == "mamba_scan_fwd: u is NULL"
+            else:
+                rc = lib.mamba_workspace_bytes(ctypes.byref(bad), ctypes.byref(size))
+                msg = pkg.last_error()
+                ok = rc == 1 and msg.startswith("mamba_workspace_bytes: dims.segments")
+            if not ok:
+                wrong.append((kind, rc, msg))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in (0, 1, 0, 1)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not wrong, wrong[:3]
+
+
 def test_binding_rejects_host_tensors(pkg):
     torch = pytest.importorskip("torch")
     d = _dims(pkg, batch=1, seqlen=4)
