@@ -430,6 +430,10 @@ def main():
         "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
+        # the forward alone (one layer's, timed on layer 0): tokens/s and HBM
+        # GB/s at its algorithmic bytes
+        "fwd_tokens_per_s": round(tokens / (fwd_ms / 1e3), 1),
+        "fwd_hbm_GBps": round(fb / (fwd_ms / 1e3) / 1e9, 1),
         "wall_s": round(t_wall, 3),
         "roofline": roofline,
     }
