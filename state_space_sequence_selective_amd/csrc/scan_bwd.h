@@ -257,6 +257,7 @@ scan_bwd_kernel(const BwdArgs p) {
     float h[SPL];
 
     // ---------------------------------------------------------------- stage
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
@@ -320,6 +321,11 @@ scan_bwd_kernel(const BwdArgs p) {
     }
     __syncthreads();
     if (kt > kb) prefetch(kt - 1);
+    // The step loops issue at a raised wave priority, the tile boundary
+    // (stage, copies, barriers) at the normal one: on a SIMD shared by
+    // several workgroups the waves inside their step loops go first
+    // (measured: T=8192 backward 1.69 -> 1.66 ms).
+    __builtin_amdgcn_s_setprio(2);
 
     // Step operands {delta, delta*u, dy, u} and this thread's B_t, C_t are
     // read PD steps before their step into a ring of registers (slot = steps

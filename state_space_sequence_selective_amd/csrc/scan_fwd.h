@@ -222,6 +222,10 @@ scan_fwd_kernel(const FwdArgs p) {
     };
 #pragma unroll
     for (int d = 0; d < PD; ++d) operands(d, d);
+    // the steps issue at a raised wave priority, the tile boundary at the
+    // normal one, so that waves in their step loop go first on a shared SIMD
+    // (measured: T=8192 forward 0.86 -> 0.78 ms)
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       // checkpoint: the state entering step t0 + tt, every L steps (L is 16
@@ -254,6 +258,7 @@ scan_fwd_kernel(const FwdArgs p) {
       if (!AGG) s_yp[gs][tt * CPW + c] = yp;
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // the copies of tile kt + 1 are complete and visible to all waves
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
