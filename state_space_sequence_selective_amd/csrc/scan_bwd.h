@@ -321,11 +321,13 @@ scan_bwd_kernel(const BwdArgs p) {
     }
     __syncthreads();
     if (kt > kb) prefetch(kt - 1);
-    // The step loops issue at a raised wave priority, the tile boundary
-    // (stage, copies, barriers) at the normal one: on a SIMD shared by
-    // several workgroups the waves inside their step loops go first
-    // (measured: T=8192 backward 1.69 -> 1.66 ms).
-    __builtin_amdgcn_s_setprio(2);
+    // Wave priorities: the tile boundary (stage, copies, barriers) issues at
+    // the normal one, the recompute one higher and the reverse pass higher
+    // still, so that on a SIMD shared by several workgroups the waves deepest
+    // into a tile go first (measured: T=8192 backward 1.69 -> 1.64 ms with the
+    // two loops raised alike, a further 2 % with the reverse pass above the
+    // recompute).
+    __builtin_amdgcn_s_setprio(1);
 
     // Step operands {delta, delta*u, dy, u} and this thread's B_t, C_t are
     // read PD steps before their step into a ring of registers (slot = steps
@@ -381,6 +383,7 @@ scan_bwd_kernel(const BwdArgs p) {
       wave_lds_sync();
     }
 
+    __builtin_amdgcn_s_setprio(2);
     // -------------------------------------------------------------- reverse
 #pragma unroll
     for (int d = 0; d < PD; ++d) operands(L - 1 - d, d);
