@@ -33,6 +33,14 @@
  * nothing.  Layer calls on one device from several host threads at once
  * are serialised.
  *
+ * Streams.  The forward runs on `stream`.  The backward runs its weight-
+ * gradient products on a second stream of the device (created, with its
+ * own rocBLAS handle and events, on the first backward call; default
+ * priority), each forked from `stream` once its operands are final, and
+ * joins that stream back into `stream` before returning, also when it
+ * fails: work enqueued on `stream` afterwards sees every result.  The
+ * fork and join are event records and waits; the host never blocks.
+ *
  * Buffers.  All pointers are caller-owned device memory, row-major:
  *   resid_in, resid_out, d_resid_out, d_resid_in: f32 [batch, seqlen, d_model]
  *   saved: mamba_layer_saved_bytes(dims) bytes; written by the forward,

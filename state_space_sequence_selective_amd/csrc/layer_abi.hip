@@ -204,6 +204,44 @@ int blas_handle(const char* fn, hipStream_t st, rocblas_handle* out) {
   return MAMBA_OK;
 }
 
+// The backward's weight-gradient products run on a second stream of the
+// same device (default priority), forked from the caller's stream once
+// their operands are final and joined back before the call returns.
+struct Side {
+  hipStream_t s = nullptr;
+  rocblas_handle h = nullptr;
+  hipEvent_t ev[6] = {};
+};
+Side g_side[64];
+
+int side_res(const char* fn, Side** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(MAMBA_ERR_HIP, fn, "no usable current device");
+  Side& sd = g_side[dev];
+  if (!sd.s) {
+    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess)
+      return fail(MAMBA_ERR_HIP, fn, "hipStreamCreateWithFlags failed");
+    for (auto& e : sd.ev)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+        return fail(MAMBA_ERR_HIP, fn, "hipEventCreateWithFlags failed");
+    if (rocblas_create_handle(&sd.h) != rocblas_status_success)
+      return fail(MAMBA_ERR_HIP, fn, "rocblas_create_handle failed");
+    rocblas_set_atomics_mode(sd.h, rocblas_atomics_not_allowed);
+    if (rocblas_set_stream(sd.h, sd.s) != rocblas_status_success)
+      return fail(MAMBA_ERR_HIP, fn, "rocblas_set_stream failed");
+  }
+  *out = &sd;
+  return MAMBA_OK;
+}
+
+// work on `to` after what is enqueued on `from` so far
+int fork_wait(const char* fn, hipStream_t from, hipStream_t to, hipEvent_t e) {
+  if (hipEventRecord(e, from) != hipSuccess || hipStreamWaitEvent(to, e, 0) != hipSuccess)
+    return fail(MAMBA_ERR_HIP, fn, "stream fork / join failed");
+  return MAMBA_OK;
+}
+
 rocblas_datatype blas_type(mscan::Act a) {
   switch (a) {
     case mscan::Act::F32: return rocblas_datatype_f32_r;
@@ -372,147 +410,163 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
   std::lock_guard<std::mutex> lock(g_blas_mu);
   rocblas_handle h = nullptr;
   LAYER_TRY(blas_handle(fn, st, &h));
+  Side* sd = nullptr;
+  LAYER_TRY(side_res(fn, &sd));
+  const rocblas_handle hw = sd->h;
+  // Everything below runs in `body`; the join that follows it runs on every
+  // path, so a call that fails part-way still leaves no product of this call
+  // unordered with the caller's later work.
+  auto body = [&]() -> int {
+    const char* S = static_cast<const char*>(saved);
+    char* W = static_cast<char*>(workspace);
+    const mscan::Act act = pl.act;
+    const rocblas_datatype at = blas_type(act), f32 = rocblas_datatype_f32_r;
+    const void* xn = S + pl.s_xn;
+    const float* rstd = reinterpret_cast<const float*>(S + pl.s_rstd);
+    const void* x = S + pl.s_x;
+    const void* z = S + pl.s_z;
+    const void* u = S + pl.s_u;
+    const void* xdbl = S + pl.s_xdbl;
+    const void* dr = S + pl.s_dr;
+    const void* gated = S + pl.s_gated;
+    const void* y = S + pl.s_y;
+    const float* ckpt = reinterpret_cast<const float*>(S + pl.s_ckpt);
+    void* dy = W + pl.w_dy;
+    void* d_gated = W + pl.w_dgated;
+    void* d_u = W + pl.w_du;
+    void* d_dr = W + pl.w_ddr;
+    void* d_z = W + pl.w_dz;
+    float* d_xdbl = reinterpret_cast<float*>(W + pl.w_dxdbl);
+    void* d_xdbl_a = W + pl.w_dxdbl_a;
+    float* d_uex = reinterpret_cast<float*>(W + pl.w_duex);
+    void* d_x = W + pl.w_dx;
+    float* d_xn = reinterpret_cast<float*>(W + pl.w_dxn);
+    float* pnorm = reinterpret_cast<float*>(W + pl.w_pnorm);
+    float* pbdt = reinterpret_cast<float*>(W + pl.w_pbdt);
+    float* pcw = reinterpret_cast<float*>(W + pl.w_pconv_w);
+    float* pcb = reinterpret_cast<float*>(W + pl.w_pconv_b);
+    const int64_t N = pl.N, Di = pl.Di, dm = pl.dm, X = pl.X, R = pl.R;
+    const char* w_in_z = static_cast<const char*>(w->w_in) + Di * dm * pl.es;
 
-  const char* S = static_cast<const char*>(saved);
-  char* W = static_cast<char*>(workspace);
-  const mscan::Act act = pl.act;
-  const rocblas_datatype at = blas_type(act), f32 = rocblas_datatype_f32_r;
-  const void* xn = S + pl.s_xn;
-  const float* rstd = reinterpret_cast<const float*>(S + pl.s_rstd);
-  const void* x = S + pl.s_x;
-  const void* z = S + pl.s_z;
-  const void* u = S + pl.s_u;
-  const void* xdbl = S + pl.s_xdbl;
-  const void* dr = S + pl.s_dr;
-  const void* gated = S + pl.s_gated;
-  const void* y = S + pl.s_y;
-  const float* ckpt = reinterpret_cast<const float*>(S + pl.s_ckpt);
-  void* dy = W + pl.w_dy;
-  void* d_gated = W + pl.w_dgated;
-  void* d_u = W + pl.w_du;
-  void* d_dr = W + pl.w_ddr;
-  void* d_z = W + pl.w_dz;
-  float* d_xdbl = reinterpret_cast<float*>(W + pl.w_dxdbl);
-  void* d_xdbl_a = W + pl.w_dxdbl_a;
-  float* d_uex = reinterpret_cast<float*>(W + pl.w_duex);
-  void* d_x = W + pl.w_dx;
-  float* d_xn = reinterpret_cast<float*>(W + pl.w_dxn);
-  float* pnorm = reinterpret_cast<float*>(W + pl.w_pnorm);
-  float* pbdt = reinterpret_cast<float*>(W + pl.w_pbdt);
-  float* pcw = reinterpret_cast<float*>(W + pl.w_pconv_w);
-  float* pcb = reinterpret_cast<float*>(W + pl.w_pconv_b);
-  const int64_t N = pl.N, Di = pl.Di, dm = pl.dm, X = pl.X, R = pl.R;
-  const char* w_in_z = static_cast<const char*>(w->w_in) + Di * dm * pl.es;
-
-  // out_proj adjoint (the products take typed operands)
-  Op o{OpKind::Cast};
-  o.f0 = d_resid_out;
-  o.v0 = dy;
-  o.n = N * dm;
-  LAYER_TRY(run(fn, "cast d_resid_out", o, act, st));
-  LAYER_TRY(gemm(fn, "out_proj dgrad", h, false, false, N, Di, dm, dy, at, dm, w->w_out, at, Di, 0.0f, d_gated, d_gated,
-                 at, Di));
-  LAYER_TRY(gemm(fn, "out_proj wgrad", h, true, false, dm, Di, N, dy, at, dm, gated, at, Di, 1.0f, g->w_out, g->w_out,
-                 f32, Di));
-  // the core; it adds into the B/C columns of d_xdbl, which start at zero
-  o = Op{OpKind::Zero};
-  o.f3 = d_xdbl;
-  o.n = N * X;
-  LAYER_TRY(run(fn, "zero d_xdbl", o, act, st));
-  LAYER_TRY(core_call(fn, "scan backward",
-                      mamba_scan_bwd(&pl.core, u, dr, w->a_log, xdbl, w->D, z, y, ckpt, d_gated, d_u, d_dr, d_z,
-                                     d_xdbl, g->a_log, g->D, W + pl.w_core_b, pl.core_ws, stream)));
-  // dt_proj adjoint: the dt columns of d_xdbl, W_dt and b_dt
-  LAYER_TRY(gemm(fn, "dt_proj dgrad", h, false, false, N, R, Di, d_dr, at, Di, w->w_dt, at, R, 0.0f, d_xdbl, d_xdbl,
-                 f32, X));
-  LAYER_TRY(gemm(fn, "dt_proj wgrad", h, true, false, Di, R, N, d_dr, at, Di, xdbl, at, X, 1.0f, g->w_dt, g->w_dt, f32,
-                 R));
-  o = Op{OpKind::ColPart};
-  o.c0 = d_dr;
-  o.f3 = pbdt;
-  o.rows = N;
-  o.cols = Di;
-  o.per_blk = pl.bdt_per;
-  o.nblk = pl.bdt_nblk;
-  LAYER_TRY(run(fn, "b_dt partials", o, act, st));
-  o = Op{OpKind::ColSum};
-  o.f0 = pbdt;
-  o.f3 = g->b_dt;
-  o.nblk = pl.bdt_nblk;
-  o.cols = Di;
-  LAYER_TRY(run(fn, "b_dt sum", o, act, st));
-  // x_proj adjoint
-  o = Op{OpKind::Cast};
-  o.f0 = d_xdbl;
-  o.v0 = d_xdbl_a;
-  o.n = N * X;
-  LAYER_TRY(run(fn, "cast d_xdbl", o, act, st));
-  LAYER_TRY(gemm(fn, "x_proj dgrad", h, false, false, N, Di, X, d_xdbl_a, at, X, w->w_x, at, Di, 0.0f, d_uex, d_uex, f32,
-                 Di));
-  LAYER_TRY(gemm(fn, "x_proj wgrad", h, true, false, X, Di, N, d_xdbl_a, at, X, u, at, Di, 1.0f, g->w_x, g->w_x, f32,
-                 Di));
-  // conv + SiLU adjoint: d_x and the weight / bias partials in one pass
-  o = Op{OpKind::ConvBwd};
-  o.c0 = x;
-  o.f0 = w->conv_w;
-  o.f1 = w->conv_b;
-  o.c1 = d_u;
-  o.f2 = d_uex;
-  o.v0 = d_x;
-  o.f3 = pcw;
-  o.f6 = pcb;
-  o.T = pl.T;
-  o.cols = Di;
-  o.K = static_cast<int>(pl.K);
-  o.n = N * Di;
-  LAYER_TRY(run(fn, "conv adjoint", o, act, st));
-  o = Op{OpKind::ColSum};
-  o.f0 = pcw;
-  o.f3 = g->conv_w;
-  o.nblk = pl.conv_nblk;
-  o.cols = Di * pl.K;
-  LAYER_TRY(run(fn, "conv_w sum", o, act, st));
-  o.f0 = pcb;
-  o.f3 = g->conv_b;
-  o.cols = Di;
-  LAYER_TRY(run(fn, "conv_b sum", o, act, st));
-  // in_proj adjoint: d_xn = d_x W_in[:Di] + d_z W_in[Di:]
-  LAYER_TRY(gemm(fn, "in_proj dgrad x", h, false, false, N, dm, Di, d_x, at, Di, w->w_in, at, dm, 0.0f, d_xn, d_xn, f32,
-                 dm));
-  LAYER_TRY(gemm(fn, "in_proj dgrad z", h, false, false, N, dm, Di, d_z, at, Di, w_in_z, at, dm, 1.0f, d_xn, d_xn, f32,
-                 dm));
-  LAYER_TRY(gemm(fn, "in_proj wgrad x", h, true, false, Di, dm, N, d_x, at, Di, xn, at, dm, 1.0f, g->w_in, g->w_in, f32,
-                 dm));
-  float* gw_in_z = g->w_in + Di * dm;
-  LAYER_TRY(gemm(fn, "in_proj wgrad z", h, true, false, Di, dm, N, d_z, at, Di, xn, at, dm, 1.0f, gw_in_z, gw_in_z, f32,
-                 dm));
-  // RMSNorm adjoint and the residual
-  o = Op{OpKind::RmsnormBwd};
-  o.f0 = d_xn;
-  o.f1 = resid_in;
-  o.f2 = w->norm_w;
-  o.f4 = rstd;
-  o.f5 = d_resid_out;
-  o.f3 = d_resid_in;
-  o.rows = N;
-  o.cols = dm;
-  LAYER_TRY(run(fn, "rmsnorm adjoint", o, act, st));
-  o = Op{OpKind::RmsnormWgradPart};
-  o.f0 = d_xn;
-  o.f1 = resid_in;
-  o.f2 = rstd;
-  o.f3 = pnorm;
-  o.rows = N;
-  o.cols = dm;
-  o.per_blk = pl.norm_per;
-  o.nblk = pl.norm_nblk;
-  LAYER_TRY(run(fn, "norm_w partials", o, act, st));
-  o = Op{OpKind::ColSum};
-  o.f0 = pnorm;
-  o.f3 = g->norm_w;
-  o.nblk = pl.norm_nblk;
-  o.cols = dm;
-  LAYER_TRY(run(fn, "norm_w sum", o, act, st));
+    // out_proj adjoint (the products take typed operands)
+    Op o{OpKind::Cast};
+    o.f0 = d_resid_out;
+    o.v0 = dy;
+    o.n = N * dm;
+    LAYER_TRY(run(fn, "cast d_resid_out", o, act, st));
+    LAYER_TRY(gemm(fn, "out_proj dgrad", h, false, false, N, Di, dm, dy, at, dm, w->w_out, at, Di, 0.0f, d_gated, d_gated,
+                   at, Di));
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[0]));
+    LAYER_TRY(gemm(fn, "out_proj wgrad", hw, true, false, dm, Di, N, dy, at, dm, gated, at, Di, 1.0f, g->w_out, g->w_out,
+                   f32, Di));
+    // the core; it adds into the B/C columns of d_xdbl, which start at zero
+    o = Op{OpKind::Zero};
+    o.f3 = d_xdbl;
+    o.n = N * X;
+    LAYER_TRY(run(fn, "zero d_xdbl", o, act, st));
+    LAYER_TRY(core_call(fn, "scan backward",
+                        mamba_scan_bwd(&pl.core, u, dr, w->a_log, xdbl, w->D, z, y, ckpt, d_gated, d_u, d_dr, d_z,
+                                       d_xdbl, g->a_log, g->D, W + pl.w_core_b, pl.core_ws, stream)));
+    // dt_proj adjoint: the dt columns of d_xdbl, W_dt and b_dt
+    LAYER_TRY(gemm(fn, "dt_proj dgrad", h, false, false, N, R, Di, d_dr, at, Di, w->w_dt, at, R, 0.0f, d_xdbl, d_xdbl,
+                   f32, X));
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[1]));
+    LAYER_TRY(gemm(fn, "dt_proj wgrad", hw, true, false, Di, R, N, d_dr, at, Di, xdbl, at, X, 1.0f, g->w_dt, g->w_dt, f32,
+                   R));
+    o = Op{OpKind::ColPart};
+    o.c0 = d_dr;
+    o.f3 = pbdt;
+    o.rows = N;
+    o.cols = Di;
+    o.per_blk = pl.bdt_per;
+    o.nblk = pl.bdt_nblk;
+    LAYER_TRY(run(fn, "b_dt partials", o, act, st));
+    o = Op{OpKind::ColSum};
+    o.f0 = pbdt;
+    o.f3 = g->b_dt;
+    o.nblk = pl.bdt_nblk;
+    o.cols = Di;
+    LAYER_TRY(run(fn, "b_dt sum", o, act, st));
+    // x_proj adjoint
+    o = Op{OpKind::Cast};
+    o.f0 = d_xdbl;
+    o.v0 = d_xdbl_a;
+    o.n = N * X;
+    LAYER_TRY(run(fn, "cast d_xdbl", o, act, st));
+    LAYER_TRY(gemm(fn, "x_proj dgrad", h, false, false, N, Di, X, d_xdbl_a, at, X, w->w_x, at, Di, 0.0f, d_uex, d_uex, f32,
+                   Di));
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[2]));
+    LAYER_TRY(gemm(fn, "x_proj wgrad", hw, true, false, X, Di, N, d_xdbl_a, at, X, u, at, Di, 1.0f, g->w_x, g->w_x, f32,
+                   Di));
+    // conv + SiLU adjoint: d_x and the weight / bias partials in one pass
+    o = Op{OpKind::ConvBwd};
+    o.c0 = x;
+    o.f0 = w->conv_w;
+    o.f1 = w->conv_b;
+    o.c1 = d_u;
+    o.f2 = d_uex;
+    o.v0 = d_x;
+    o.f3 = pcw;
+    o.f6 = pcb;
+    o.T = pl.T;
+    o.cols = Di;
+    o.K = static_cast<int>(pl.K);
+    o.n = N * Di;
+    LAYER_TRY(run(fn, "conv adjoint", o, act, st));
+    o = Op{OpKind::ColSum};
+    o.f0 = pcw;
+    o.f3 = g->conv_w;
+    o.nblk = pl.conv_nblk;
+    o.cols = Di * pl.K;
+    LAYER_TRY(run(fn, "conv_w sum", o, act, st));
+    o.f0 = pcb;
+    o.f3 = g->conv_b;
+    o.cols = Di;
+    LAYER_TRY(run(fn, "conv_b sum", o, act, st));
+    // in_proj adjoint: d_xn = d_x W_in[:Di] + d_z W_in[Di:]
+    LAYER_TRY(gemm(fn, "in_proj dgrad x", h, false, false, N, dm, Di, d_x, at, Di, w->w_in, at, dm, 0.0f, d_xn, d_xn, f32,
+                   dm));
+    LAYER_TRY(gemm(fn, "in_proj dgrad z", h, false, false, N, dm, Di, d_z, at, Di, w_in_z, at, dm, 1.0f, d_xn, d_xn, f32,
+                   dm));
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[3]));
+    LAYER_TRY(gemm(fn, "in_proj wgrad x", hw, true, false, Di, dm, N, d_x, at, Di, xn, at, dm, 1.0f, g->w_in, g->w_in, f32,
+                   dm));
+    float* gw_in_z = g->w_in + Di * dm;
+    LAYER_TRY(gemm(fn, "in_proj wgrad z", hw, true, false, Di, dm, N, d_z, at, Di, xn, at, dm, 1.0f, gw_in_z, gw_in_z, f32,
+                   dm));
+    // RMSNorm adjoint and the residual
+    o = Op{OpKind::RmsnormBwd};
+    o.f0 = d_xn;
+    o.f1 = resid_in;
+    o.f2 = w->norm_w;
+    o.f4 = rstd;
+    o.f5 = d_resid_out;
+    o.f3 = d_resid_in;
+    o.rows = N;
+    o.cols = dm;
+    LAYER_TRY(run(fn, "rmsnorm adjoint", o, act, st));
+    o = Op{OpKind::RmsnormWgradPart};
+    o.f0 = d_xn;
+    o.f1 = resid_in;
+    o.f2 = rstd;
+    o.f3 = pnorm;
+    o.rows = N;
+    o.cols = dm;
+    o.per_blk = pl.norm_per;
+    o.nblk = pl.norm_nblk;
+    LAYER_TRY(run(fn, "norm_w partials", o, act, st));
+    o = Op{OpKind::ColSum};
+    o.f0 = pnorm;
+    o.f3 = g->norm_w;
+    o.nblk = pl.norm_nblk;
+    o.cols = dm;
+    LAYER_TRY(run(fn, "norm_w sum", o, act, st));
+    return MAMBA_OK;
+  };
+  const int rc = body();
+  const int rj = fork_wait(fn, sd->s, st, sd->ev[4]);   // join: the caller's stream covers every product
+  if (rc != MAMBA_OK) return rc;
+  if (rj != MAMBA_OK) return rj;
   mscan::set_last_error("");
   return MAMBA_OK;
 }
