@@ -427,6 +427,27 @@ def _sampled_full(mscan, oracle_lib, name, sample):
     print(name, "sampled", {k: "%.2e" % v for k, v in rep.items()}, flush=True)
 
 
+@pytest.mark.parametrize("case", range(24))
+def test_random_configurations(mscan, oracle_lib, case):
+    """Seeded random combinations of d_state, checkpoint interval,
+    activation type, conv width (or none), dt_rank (odd ones included),
+    gate, D, optional states and extra gradient, ragged widths and lengths,
+    and segment counts, each against the oracle."""
+    rng = np.random.default_rng(1000 + case)
+    ds = int(rng.choice([4, 8, 16, 32]))
+    chunk = 16 if ds == 32 else int(rng.choice([16, 32]))
+    act = str(rng.choice(["f32", "bf16", "f16"]))
+    K = int(rng.choice([0, 0, 1, 2, 3, 4]))
+    B, T, Di, R = int(rng.integers(1, 4)), int(rng.integers(1, 300)), 4 * int(rng.integers(1, 40)), int(rng.integers(0, 9))
+    gate = bool(rng.integers(0, 2))
+    w = workloads.Workload("rand%d" % case, B, T, Di, ds, R, K, act, gate)
+    flags = dict(h0=bool(rng.integers(0, 2)), conv_state0=K > 0 and bool(rng.integers(0, 2)),
+                 d_u_extra=K > 0 and bool(rng.integers(0, 2)), D=bool(rng.integers(0, 2)),
+                 segments=int(rng.choice([0, 0, 2, 5])))
+    print(w, chunk, flags, flush=True)
+    run_case(mscan, oracle_lib, w, seed=case, chunk=chunk, **flags)
+
+
 def test_long_sequence_many_segments(mscan, oracle_lib):
     """2^16 steps of one batch row at a narrow width: the library splits the
     sequence into many segments, and 4096 segments when asked (one 16-step
