@@ -96,6 +96,20 @@ def test_layer_small(mscan, act):
     check_layer(mscan, w)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_layer_random_configurations(mscan, case):
+    """Seeded random layer shapes: every activation type, ragged d_model and
+    d_inner, odd dt_ranks, conv widths 1..4 and d_state 4..32."""
+    rng = np.random.default_rng(2000 + case)
+    act = str(rng.choice(["f32", "bf16", "f16"]))
+    ds = int(rng.choice([4, 8, 16, 32]))
+    w = workloads.LayerWorkload("layer_rand%d" % case, int(rng.integers(1, 4)), int(rng.integers(2, 120)),
+                                int(rng.integers(8, 100)), 4 * int(rng.integers(2, 30)), ds,
+                                int(rng.integers(1, 9)), int(rng.integers(1, 5)), act)
+    print(w, flush=True)
+    check_layer(mscan, w, seed=case)
+
+
 def test_layer_segmented_core(mscan):
     """A longer sequence with the core split into segments inside the layer."""
     w = workloads.LayerWorkload("layer_seg", 2, 300, 64, 128, 16, 4, 4, "bf16")
