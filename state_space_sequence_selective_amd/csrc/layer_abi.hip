@@ -210,28 +210,47 @@ int blas_handle(const char* fn, hipStream_t st, rocblas_handle* out) {
 struct Side {
   hipStream_t s = nullptr;
   rocblas_handle h = nullptr;
-  hipEvent_t ev[6] = {};
+  hipEvent_t ev[5] = {};   // four forks and the join of one backward call
 };
 Side g_side[64];
 
+// The device's side resources, created on first use; published only when
+// every part was created, so a failed creation is retried by the next call
+// (what it did create is released).
 int side_res(const char* fn, Side** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
     return fail(MAMBA_ERR_HIP, fn, "no usable current device");
-  Side& sd = g_side[dev];
-  if (!sd.s) {
-    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess)
-      return fail(MAMBA_ERR_HIP, fn, "hipStreamCreateWithFlags failed");
-    for (auto& e : sd.ev)
-      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
-        return fail(MAMBA_ERR_HIP, fn, "hipEventCreateWithFlags failed");
-    if (rocblas_create_handle(&sd.h) != rocblas_status_success)
-      return fail(MAMBA_ERR_HIP, fn, "rocblas_create_handle failed");
-    rocblas_set_atomics_mode(sd.h, rocblas_atomics_not_allowed);
-    if (rocblas_set_stream(sd.h, sd.s) != rocblas_status_success)
-      return fail(MAMBA_ERR_HIP, fn, "rocblas_set_stream failed");
+  if (!g_side[dev].s) {
+    Side n;
+    const char* what = nullptr;
+    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) {
+      n.s = nullptr;
+      what = "hipStreamCreateWithFlags failed";
+    }
+    for (auto& e : n.ev)
+      if (!what && hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+        e = nullptr;
+        what = "hipEventCreateWithFlags failed";
+      }
+    if (!what && rocblas_create_handle(&n.h) != rocblas_status_success) {
+      n.h = nullptr;
+      what = "rocblas_create_handle failed";
+    }
+    if (!what) {
+      rocblas_set_atomics_mode(n.h, rocblas_atomics_not_allowed);
+      if (rocblas_set_stream(n.h, n.s) != rocblas_status_success) what = "rocblas_set_stream failed";
+    }
+    if (what) {
+      if (n.h) rocblas_destroy_handle(n.h);
+      for (auto& e : n.ev)
+        if (e) (void)hipEventDestroy(e);
+      if (n.s) (void)hipStreamDestroy(n.s);
+      return fail(MAMBA_ERR_HIP, fn, what);
+    }
+    g_side[dev] = n;
   }
-  *out = &sd;
+  *out = &g_side[dev];
   return MAMBA_OK;
 }
 
