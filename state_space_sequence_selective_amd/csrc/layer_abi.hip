@@ -28,7 +28,7 @@ using mlayer::OpKind;
 constexpr float kNormEps = 1e-5f;   // the forward_mixed page's RMSNorm epsilon
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxModel = int64_t(1) << 24;
-constexpr int64_t kPartBlocks = 32;   // row blocks of the fixed-order column reductions
+constexpr int64_t kPartBlocks = 128;   // row blocks of the fixed-order column reductions
 
 int fail(int code, const char* fn, const std::string& msg) {
   mscan::set_last_error(std::string(fn) + ": " + msg);

@@ -18,7 +18,7 @@ enum class OpKind {
   ConvBwd,           // x c0, conv_w f0, conv_b f1, d_u c1 (act), d_u_extra f2 -> d_x v0 (act),
                      // part_w f3 [batch * ntiles, cols, K], part_b f6 [batch * ntiles, cols]; T, cols, K, n
                      // (ntiles = conv_step_tiles(T))
-  BiasRound,         // dt f0, b f1 -> out v0 (act); T, cols, n
+  BiasRound,         // dt f0, b f1 -> out v0 (act); cols = d_inner (% 4 == 0), n
   Cast,              // f0 -> v0 (act); n
   ColPart,           // m c0 (act) -> part f3 [nblk, cols]; rows, cols, per_blk, nblk
   ColSum,            // part f0 -> out f3 (+=); nblk, cols

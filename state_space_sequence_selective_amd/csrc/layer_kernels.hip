@@ -3,8 +3,8 @@
 // fixed-order column reductions of the layer's parameter gradients.  The
 // steps are those of the per-layer forward on the mamba-rs 0.3.1
 // forward_mixed.rs page (F1 RMSNorm, F4a conv + SiLU, F4c dt bias) and their
-// adjoints.  All of them stream HBM once; none needs LDS beyond a row
-// reduction.
+// adjoints.  All of them stream HBM once; none uses LDS beyond the 1 KB
+// that the final column sums add their runs in.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -20,71 +20,120 @@ using mscan::IO;
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / 64;   // row kernels: one wave per row
+constexpr int kRowU = 4;                       // row kernels: loads in flight per lane and array
 
-// sum over the 256 threads of a workgroup; every thread gets the result
-__device__ __forceinline__ float block_sum(float v, float* red) {
+// sum over the 64 lanes of a wave; every lane gets the result
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float t = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) t += red[w];
-  __syncthreads();
-  return t;
+  return v;
 }
 
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
-
-// Element of a [rows, Di] activation for a grid of rows * nchb workgroups,
-// nchb = ceil(Di / 256) channel blocks per row: the row (and its step t)
-// comes from one 32-bit division per workgroup, not a 64-bit one per
-// element.  False past the last channel.
-__device__ __forceinline__ bool row_channel(int64_t T, int64_t Di, unsigned nchb, int64_t* e, int64_t* i,
-                                            int64_t* t) {
-  const unsigned row = blockIdx.x / nchb;
-  *i = static_cast<int64_t>(blockIdx.x - row * nchb) * kThreads + threadIdx.x;
-  if (*i >= Di) return false;
-  *t = static_cast<int64_t>(row % static_cast<unsigned>(T));
-  *e = static_cast<int64_t>(row) * Di + *i;
-  return true;
+// Four f32 values to elements e .. e+3 of an activation (e % 4 == 0, the
+// buffer 16-byte aligned), converted as IO<A>::st converts one.
+template <Act A>
+__device__ __forceinline__ void st4(void* p, int64_t e, float4 v);
+template <>
+__device__ __forceinline__ void st4<Act::F32>(void* p, int64_t e, float4 v) {
+  *reinterpret_cast<float4*>(static_cast<float*>(p) + e) = v;
+}
+template <>
+__device__ __forceinline__ void st4<Act::BF16>(void* p, int64_t e, float4 v) {
+  struct alignas(8) H4 {
+    __bf16 h[4];
+  };
+  const H4 q = {{static_cast<__bf16>(v.x), static_cast<__bf16>(v.y), static_cast<__bf16>(v.z), static_cast<__bf16>(v.w)}};
+  *reinterpret_cast<H4*>(static_cast<__bf16*>(p) + e) = q;
+}
+template <>
+__device__ __forceinline__ void st4<Act::F16>(void* p, int64_t e, float4 v) {
+  struct alignas(8) H4 {
+    _Float16 h[4];
+  };
+  const H4 q = {{static_cast<_Float16>(v.x), static_cast<_Float16>(v.y), static_cast<_Float16>(v.z),
+                 static_cast<_Float16>(v.w)}};
+  *reinterpret_cast<H4*>(static_cast<_Float16*>(p) + e) = q;
 }
 
-// F1: one workgroup per row
+// F1: one wave per row (lane l takes columns l, l + 64, ...), kRowsPerBlock
+// rows per workgroup; no workgroup barrier, so a wave past the last row
+// simply exits
 template <Act A>
 __global__ void __launch_bounds__(kThreads) rmsnorm_fwd_kernel(const float* __restrict__ x, const float* __restrict__ w,
                                                               void* __restrict__ y, float* __restrict__ rstd,
-                                                              int64_t dm, float eps) {
-  __shared__ float red[kThreads / 64];
-  const int64_t row = blockIdx.x;
+                                                              int64_t rows, int64_t dm, float eps) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
   const float* xr = x + row * dm;
   float ss = 0.0f;
-  for (int64_t j = threadIdx.x; j < dm; j += kThreads) ss = fmaf(xr[j], xr[j], ss);
-  ss = block_sum(ss, red);
+  for (int64_t j0 = lane; j0 < dm; j0 += kRowU * 64) {
+    float xv[kRowU];
+#pragma unroll
+    for (int k = 0; k < kRowU; ++k) xv[k] = j0 + 64 * k < dm ? xr[j0 + 64 * k] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < kRowU; ++k) ss = fmaf(xv[k], xv[k], ss);
+  }
+  ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / static_cast<float>(dm) + eps);
-  for (int64_t j = threadIdx.x; j < dm; j += kThreads) IO<A>::st(y, row * dm + j, xr[j] * r * w[j]);
-  if (threadIdx.x == 0) rstd[row] = r;
+  for (int64_t j0 = lane; j0 < dm; j0 += kRowU * 64) {
+    float xv[kRowU], wv[kRowU];
+#pragma unroll
+    for (int k = 0; k < kRowU; ++k) {
+      const bool in = j0 + 64 * k < dm;
+      xv[k] = in ? xr[j0 + 64 * k] : 0.0f;
+      wv[k] = in ? w[j0 + 64 * k] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kRowU; ++k)
+      if (j0 + 64 * k < dm) IO<A>::st(y, row * dm + j0 + 64 * k, xv[k] * r * wv[k]);
+  }
+  if (lane == 0) rstd[row] = r;
 }
 
 // adjoint of F1 for one row: d_x = r w dy - x r^3 mean(dy w x);
-// d_resid_in = d_resid_out + d_x (may alias)
+// d_resid_in = d_resid_out + d_x (may alias: each element is read and then
+// written by the same lane).  Rows are mapped as in the forward.
 __global__ void __launch_bounds__(kThreads) rmsnorm_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
                                                               const float* __restrict__ w,
                                                               const float* __restrict__ rstd, const float* dres_out,
-                                                              float* dres_in, int64_t dm) {
-  __shared__ float red[kThreads / 64];
-  const int64_t row = blockIdx.x;
+                                                              float* dres_in, int64_t rows, int64_t dm) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
   const float* dyr = dy + row * dm;
   const float* xr = x + row * dm;
   float c = 0.0f;
-  for (int64_t j = threadIdx.x; j < dm; j += kThreads) c = fmaf(dyr[j] * w[j], xr[j], c);
-  c = block_sum(c, red) / static_cast<float>(dm);
+  for (int64_t j0 = lane; j0 < dm; j0 += kRowU * 64) {
+    float gv[kRowU], wv[kRowU], xv[kRowU];
+#pragma unroll
+    for (int k = 0; k < kRowU; ++k) {
+      const bool in = j0 + 64 * k < dm;
+      gv[k] = in ? dyr[j0 + 64 * k] : 0.0f;
+      wv[k] = in ? w[j0 + 64 * k] : 0.0f;
+      xv[k] = in ? xr[j0 + 64 * k] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kRowU; ++k) c = fmaf(gv[k] * wv[k], xv[k], c);
+  }
+  c = wave_sum(c) / static_cast<float>(dm);
   const float r = rstd[row];
   const float r3c = r * r * r * c;
-  for (int64_t j = threadIdx.x; j < dm; j += kThreads) {
-    const int64_t e = row * dm + j;
-    dres_in[e] = dres_out[e] + (r * w[j] * dyr[j] - xr[j] * r3c);
+  for (int64_t j0 = lane; j0 < dm; j0 += kRowU * 64) {
+    float gv[kRowU], wv[kRowU], xv[kRowU], ov[kRowU];
+#pragma unroll
+    for (int k = 0; k < kRowU; ++k) {
+      const bool in = j0 + 64 * k < dm;
+      const int64_t e = row * dm + j0 + 64 * k;
+      gv[k] = in ? dyr[j0 + 64 * k] : 0.0f;
+      wv[k] = in ? w[j0 + 64 * k] : 0.0f;
+      xv[k] = in ? xr[j0 + 64 * k] : 0.0f;
+      ov[k] = in ? dres_out[e] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kRowU; ++k)
+      if (j0 + 64 * k < dm) dres_in[row * dm + j0 + 64 * k] = ov[k] + (r * wv[k] * gv[k] - xv[k] * r3c);
   }
 }
 
@@ -100,10 +149,10 @@ __global__ void __launch_bounds__(kThreads) rmsnorm_wgrad_part_kernel(const floa
   const int64_t blk = blockIdx.y;
   const int64_t r0 = blk * rows_per_blk;
   const int64_t r1 = r0 + rows_per_blk < rows ? r0 + rows_per_blk : rows;
-  constexpr int U = 8;
+  constexpr int U = 16;
   float acc = 0.0f;
   int64_t r = r0;
-  for (; r + U <= r1; r += U) {   // eight rows' loads in flight, products added in row order
+  for (; r + U <= r1; r += U) {   // sixteen rows' loads in flight, products added in row order
     float v[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) v[k] = dy[(r + k) * dm + j] * x[(r + k) * dm + j] * rstd[r + k];
@@ -166,7 +215,7 @@ __global__ void __launch_bounds__(kThreads) conv_silu_fwd_kernel(const void* __r
 #pragma unroll
         for (int k = 0; k < 3; ++k)
           if (k < K - 1) p = fmaf(w[k], win[K - 2 - k], p);
-        IO<A>::st(u, base + (t0 + j) * Di, p * sigmoid_f(p));
+        IO<A>::st(u, base + (t0 + j) * Di, p * mscan::sigmoid(p));
         win[2] = win[1];
         win[1] = win[0];
         win[0] = xt;
@@ -220,7 +269,7 @@ __global__ void __launch_bounds__(kThreads) conv_bwd_kernel(const void* __restri
 #pragma unroll
         for (int k = 0; k < 3; ++k)
           if (k < K - 1) p = fmaf(w[k], win[K - 2 - k], p);
-        const float sg = sigmoid_f(p);
+        const float sg = mscan::sigmoid(p);
         g = gs[j] * (sg * (1.0f + p * (1.0f - sg)));
         if (t < c.t1) {
 #pragma unroll
@@ -251,22 +300,35 @@ __global__ void __launch_bounds__(kThreads) conv_bwd_kernel(const void* __restri
   part_b[blk * Di + c.i] = acc_b;
 }
 
-// F4c tail: delta_raw = round(dt + b_dt[i])
+// F4c tail: delta_raw = round(dt + b_dt[i]), four channels per thread
+// (d_inner % 4 == 0 and 16-byte aligned buffers); a grid of rows * nq4
+// workgroups, nq4 = ceil(d_inner / 1024) blocks of four-channel groups per
+// row, so the row comes from one 32-bit division per workgroup
 template <Act A>
 __global__ void __launch_bounds__(kThreads) bias_round_kernel(const float* __restrict__ dt,
                                                              const float* __restrict__ b, void* __restrict__ out,
-                                                             int64_t T, int64_t Di, unsigned nchb) {
-  int64_t e, i, t;
-  if (!row_channel(T, Di, nchb, &e, &i, &t)) return;
-  IO<A>::st(out, e, dt[e] + b[i]);
+                                                             int64_t Di, unsigned nq4) {
+  const unsigned row = blockIdx.x / nq4;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x - row * nq4) * kThreads + threadIdx.x) * 4;
+  if (i >= Di) return;
+  const int64_t e = static_cast<int64_t>(row) * Di + i;
+  const float4 d = *reinterpret_cast<const float4*>(dt + e);
+  const float4 bb = *reinterpret_cast<const float4*>(b + i);
+  st4<A>(out, e, make_float4(d.x + bb.x, d.y + bb.y, d.z + bb.z, d.w + bb.w));
 }
 
+// out = round(in), four elements per thread (16-byte aligned buffers); the
+// thread at the end takes the n % 4 elements left one by one
 template <Act A>
 __global__ void __launch_bounds__(kThreads) cast_kernel(const float* __restrict__ in, void* __restrict__ out,
                                                        int64_t n) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
   if (e >= n) return;
-  IO<A>::st(out, e, in[e]);
+  if (e + 4 <= n) {
+    st4<A>(out, e, *reinterpret_cast<const float4*>(in + e));
+  } else {
+    for (int64_t k = e; k < n; ++k) IO<A>::st(out, k, in[k]);
+  }
 }
 
 // part[blk, j] = sum over the rows of block blk of m[r, j] (act dtype)
@@ -278,7 +340,7 @@ __global__ void __launch_bounds__(kThreads) colpart_kernel(const void* __restric
   const int64_t blk = blockIdx.y;
   const int64_t r0 = blk * rows_per_blk;
   const int64_t r1 = r0 + rows_per_blk < rows ? r0 + rows_per_blk : rows;
-  constexpr int U = 8;
+  constexpr int U = 16;
   float acc = 0.0f;
   int64_t r = r0;
   for (; r + U <= r1; r += U) {
@@ -292,12 +354,27 @@ __global__ void __launch_bounds__(kThreads) colpart_kernel(const void* __restric
   part[blk * cols + j] = acc;
 }
 
-// out[j] += sum_{blk < nblk} part[blk, j], blocks in ascending order
+// out[j] += sum_{blk < nblk} part[blk, j] for the 64 columns of a
+// workgroup: wave w sums the w-th of four contiguous runs of blocks in
+// ascending order, then the four run sums are added in run order (a fixed
+// order, so the result does not vary between runs)
 __global__ void __launch_bounds__(kThreads) colsum_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                          int64_t nblk, int64_t cols) {
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (j >= cols) return;
-  out[j] += mscan::ordered_sum(part + j, nblk, cols);
+  constexpr int NW = kThreads / 64;
+  __shared__ float run[NW][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const int64_t per = (nblk + NW - 1) / NW;
+  const int64_t b0 = wave * per < nblk ? wave * per : nblk;
+  const int64_t b1 = b0 + per < nblk ? b0 + per : nblk;
+  run[wave][lane] = j < cols ? mscan::ordered_sum(part + b0 * cols + j, b1 - b0, cols) : 0.0f;
+  __syncthreads();
+  if (wave == 0 && j < cols) {
+    float t = run[0][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) t += run[w][lane];
+    out[j] += t;
+  }
 }
 
 __global__ void __launch_bounds__(kThreads) zero_kernel(float* __restrict__ p, int64_t n) {
@@ -307,9 +384,12 @@ __global__ void __launch_bounds__(kThreads) zero_kernel(float* __restrict__ p, i
 
 dim3 grid1(int64_t n) { return dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)); }
 
-// row-blocked elementwise launches: rows = n / cols, ceil(cols / 256) blocks per row
+// channel blocks of 256 threads per row (conv kernels)
 unsigned nchb(const Op& o) { return static_cast<unsigned>((o.cols + kThreads - 1) / kThreads); }
-dim3 grid_rows(const Op& o) { return dim3(static_cast<unsigned>(o.n / o.cols) * nchb(o)); }
+// blocks of 256 four-channel groups per row (dt bias)
+unsigned nq4(const Op& o) { return static_cast<unsigned>((o.cols + 4 * kThreads - 1) / (4 * kThreads)); }
+// one wave per row (RMSNorm)
+dim3 grid_wave_rows(int64_t rows) { return dim3(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock)); }
 // conv tiles: batch rows * step tiles * channel blocks
 unsigned ntb(const Op& o) { return static_cast<unsigned>((o.T + kConvTT - 1) / kConvTT); }
 dim3 grid_conv(const Op& o) { return dim3(static_cast<unsigned>(o.n / o.cols / o.T) * ntb(o) * nchb(o)); }
@@ -319,8 +399,8 @@ hipError_t dispatch(const Op& o, hipStream_t st) {
   const dim3 blk(kThreads);
   switch (o.kind) {
     case OpKind::RmsnormFwd:
-      hipLaunchKernelGGL(rmsnorm_fwd_kernel<A>, dim3(static_cast<unsigned>(o.rows)), blk, 0, st, o.f0, o.f1, o.v0,
-                         o.f3, o.cols, o.eps);
+      hipLaunchKernelGGL(rmsnorm_fwd_kernel<A>, grid_wave_rows(o.rows), blk, 0, st, o.f0, o.f1, o.v0, o.f3, o.rows,
+                         o.cols, o.eps);
       break;
     case OpKind::ConvSiluFwd:
       hipLaunchKernelGGL(conv_silu_fwd_kernel<A>, grid_conv(o), blk, 0, st, o.c0, o.f0, o.f1, o.v0, o.T, o.cols, o.K,
@@ -331,10 +411,11 @@ hipError_t dispatch(const Op& o, hipStream_t st) {
                          o.T, o.cols, o.K, nchb(o), ntb(o));
       break;
     case OpKind::BiasRound:
-      hipLaunchKernelGGL(bias_round_kernel<A>, grid_rows(o), blk, 0, st, o.f0, o.f1, o.v0, o.T, o.cols, nchb(o));
+      hipLaunchKernelGGL(bias_round_kernel<A>, dim3(static_cast<unsigned>(o.n / o.cols) * nq4(o)), blk, 0, st, o.f0,
+                         o.f1, o.v0, o.cols, nq4(o));
       break;
     case OpKind::Cast:
-      hipLaunchKernelGGL(cast_kernel<A>, grid1(o.n), blk, 0, st, o.f0, o.v0, o.n);
+      hipLaunchKernelGGL(cast_kernel<A>, grid1((o.n + 3) / 4), blk, 0, st, o.f0, o.v0, o.n);
       break;
     case OpKind::ColPart:
       hipLaunchKernelGGL(colpart_kernel<A>, dim3(grid1(o.cols).x, static_cast<unsigned>(o.nblk)), blk, 0, st, o.c0,
@@ -354,15 +435,16 @@ hipError_t launch(const Op& o, Act act, hipStream_t st) {
   const dim3 blk(kThreads);
   switch (o.kind) {   // dtype-free kernels
     case OpKind::RmsnormBwd:
-      hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(static_cast<unsigned>(o.rows)), blk, 0, st, o.f0, o.f1, o.f2,
-                         o.f4, o.f5, o.f3, o.cols);
+      hipLaunchKernelGGL(rmsnorm_bwd_kernel, grid_wave_rows(o.rows), blk, 0, st, o.f0, o.f1, o.f2, o.f4, o.f5, o.f3,
+                         o.rows, o.cols);
       return hipGetLastError();
     case OpKind::RmsnormWgradPart:
       hipLaunchKernelGGL(rmsnorm_wgrad_part_kernel, dim3(grid1(o.cols).x, static_cast<unsigned>(o.nblk)), blk, 0, st,
                          o.f0, o.f1, o.f2, o.f3, o.rows, o.cols, o.per_blk);
       return hipGetLastError();
     case OpKind::ColSum:
-      hipLaunchKernelGGL(colsum_kernel, grid1(o.cols), blk, 0, st, o.f0, o.f3, o.nblk, o.cols);
+      hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>((o.cols + 63) / 64)), blk, 0, st, o.f0, o.f3,
+                         o.nblk, o.cols);
       return hipGetLastError();
     case OpKind::Zero:
       hipLaunchKernelGGL(zero_kernel, grid1(o.n), blk, 0, st, o.f3, o.n);
