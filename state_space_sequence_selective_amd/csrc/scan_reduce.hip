@@ -7,17 +7,50 @@
 
 namespace mscan {
 
+// four adjacent B/C columns (W = 2 * d_state is a multiple of 4, the
+// partials 16-byte aligned) summed over the groups in ascending order
+__device__ __forceinline__ float4 ordered_sum4(const float* src, int64_t n, int64_t stride) {
+  constexpr int U = 8;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  int64_t r = 0;
+  for (; r + U <= n; r += U) {
+    float4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = *reinterpret_cast<const float4*>(src + (r + k) * stride);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      acc.x += v[k].x;
+      acc.y += v[k].y;
+      acc.z += v[k].z;
+      acc.w += v[k].w;
+    }
+  }
+  for (; r < n; ++r) {
+    const float4 v = *reinterpret_cast<const float4*>(src + r * stride);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  return acc;
+}
+
 __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t BT = p.B * p.T;
   const int64_t W = 2 * p.Ds;
-  const int64_t nbc = BT * W;
-  if (j < nbc) {
-    const int64_t row = j / W, m = j % W;
-    p.d_xdbl[row * p.X + p.R + m] += ordered_sum(p.part_bc + row * W + m, p.nG, BT * W);
+  const int64_t nbc4 = BT * W / 4;
+  if (j < nbc4) {
+    const int64_t row = j / (W / 4), m = (j % (W / 4)) * 4;
+    const float4 s = ordered_sum4(p.part_bc + row * W + m, p.nG, BT * W);
+    float* o = p.d_xdbl + row * p.X + p.R + m;
+    o[0] += s.x;
+    o[1] += s.y;
+    o[2] += s.z;
+    o[3] += s.w;
     return;
   }
-  const int64_t jp = j - nbc;
+  const int64_t jp = j - nbc4;
   if (jp >= p.Di * p.PW) return;
   const int64_t i = jp / p.PW, slot = jp % p.PW;
   const float acc = ordered_sum(p.part_par + i * p.PW + slot, p.par_rows, p.Di * p.PW);
@@ -33,7 +66,7 @@ __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
 }
 
 hipError_t launch_reduce(const ReduceArgs& p, hipStream_t st) {
-  const int64_t n = p.B * p.T * 2 * p.Ds + p.Di * p.PW;
+  const int64_t n = p.B * p.T * 2 * p.Ds / 4 + p.Di * p.PW;
   dim3 grid(static_cast<unsigned>((n + 255) / 256));
   hipLaunchKernelGGL(mscan_reduce_kernel, grid, dim3(256), 0, st, p);
   return hipGetLastError();
