@@ -96,7 +96,7 @@ def test_layer_small(mscan, act):
     check_layer(mscan, w)
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(32))
 def test_layer_random_configurations(mscan, case):
     """Seeded random layer shapes: every activation type, ragged d_model and
     d_inner, odd dt_ranks, conv widths 1..4 and d_state 4..32."""

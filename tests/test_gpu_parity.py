@@ -427,7 +427,7 @@ def _sampled_full(mscan, oracle_lib, name, sample):
     print(name, "sampled", {k: "%.2e" % v for k, v in rep.items()}, flush=True)
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(96))
 def test_random_configurations(mscan, oracle_lib, case):
     """Seeded random combinations of d_state, checkpoint interval,
     activation type, conv width (or none), dt_rank (odd ones included),
