@@ -448,6 +448,27 @@ def test_random_configurations(mscan, oracle_lib, case):
     run_case(mscan, oracle_lib, w, seed=case, chunk=chunk, **flags)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_random_medium_configurations(mscan, oracle_lib, case):
+    """As the random configurations above, at shapes spanning many tiles,
+    channel groups and segments: B up to 4, T 300..3000, d_inner 64..1020,
+    dt_rank up to 64, segment counts up to 16; every output against the
+    oracle."""
+    rng = np.random.default_rng(5000 + case)
+    ds = int(rng.choice([4, 8, 16, 32]))
+    chunk = 16 if ds == 32 else int(rng.choice([16, 32]))
+    act = str(rng.choice(["f32", "bf16", "f16"]))
+    K = int(rng.choice([0, 0, 1, 2, 3, 4]))
+    B, T, Di, R = int(rng.integers(1, 5)), int(rng.integers(300, 3000)), 4 * int(rng.integers(16, 256)), int(rng.integers(0, 65))
+    gate = bool(rng.integers(0, 2))
+    w = workloads.Workload("med%d" % case, B, T, Di, ds, R, K, act, gate)
+    flags = dict(h0=bool(rng.integers(0, 2)), conv_state0=K > 0 and bool(rng.integers(0, 2)),
+                 d_u_extra=K > 0 and bool(rng.integers(0, 2)), D=bool(rng.integers(0, 2)),
+                 segments=int(rng.choice([0, 0, 3, 16])))
+    print(w, chunk, flags, flush=True)
+    run_case(mscan, oracle_lib, w, seed=case, chunk=chunk, **flags)
+
+
 def test_long_sequence_many_segments(mscan, oracle_lib):
     """2^16 steps of one batch row at a narrow width: the library splits the
     sequence into many segments, and 4096 segments when asked (one 16-step
