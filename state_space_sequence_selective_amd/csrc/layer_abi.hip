@@ -210,7 +210,7 @@ int blas_handle(const char* fn, hipStream_t st, rocblas_handle* out) {
 struct Side {
   hipStream_t s = nullptr;
   rocblas_handle h = nullptr;
-  hipEvent_t ev[5] = {};   // four forks and the join of one backward call
+  hipEvent_t ev[6] = {};   // five forks and the join of one backward call
 };
 Side g_side[64];
 
@@ -486,10 +486,16 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     LAYER_TRY(core_call(fn, "scan backward",
                         mamba_scan_bwd(&pl.core, u, dr, w->a_log, xdbl, w->D, z, y, ckpt, d_gated, d_u, d_dr, d_z,
                                        d_xdbl, g->a_log, g->D, W + pl.w_core_b, pl.core_ws, stream)));
+    // d_z is final here: its in_proj weight product starts now rather than
+    // after the conv adjoint
+    float* gw_in_z = g->w_in + Di * dm;
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[1]));
+    LAYER_TRY(gemm(fn, "in_proj wgrad z", hw, true, false, Di, dm, N, d_z, at, Di, xn, at, dm, 1.0f, gw_in_z, gw_in_z, f32,
+                   dm));
     // dt_proj adjoint: the dt columns of d_xdbl, W_dt and b_dt
     LAYER_TRY(gemm(fn, "dt_proj dgrad", h, false, false, N, R, Di, d_dr, at, Di, w->w_dt, at, R, 0.0f, d_xdbl, d_xdbl,
                    f32, X));
-    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[1]));
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[2]));
     LAYER_TRY(gemm(fn, "dt_proj wgrad", hw, true, false, Di, R, N, d_dr, at, Di, xdbl, at, X, 1.0f, g->w_dt, g->w_dt, f32,
                    R));
     o = Op{OpKind::ColPart};
@@ -514,7 +520,7 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     LAYER_TRY(run(fn, "cast d_xdbl", o, act, st));
     LAYER_TRY(gemm(fn, "x_proj dgrad", h, false, false, N, Di, X, d_xdbl_a, at, X, w->w_x, at, Di, 0.0f, d_uex, d_uex, f32,
                    Di));
-    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[2]));
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[3]));
     LAYER_TRY(gemm(fn, "x_proj wgrad", hw, true, false, X, Di, N, d_xdbl_a, at, X, u, at, Di, 1.0f, g->w_x, g->w_x, f32,
                    Di));
     // conv + SiLU adjoint: d_x and the weight / bias partials in one pass
@@ -532,6 +538,10 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     o.K = static_cast<int>(pl.K);
     o.n = N * Di;
     LAYER_TRY(run(fn, "conv adjoint", o, act, st));
+    // d_x is final here: its in_proj weight product starts beside the rest
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[4]));
+    LAYER_TRY(gemm(fn, "in_proj wgrad x", hw, true, false, Di, dm, N, d_x, at, Di, xn, at, dm, 1.0f, g->w_in, g->w_in, f32,
+                   dm));
     o = Op{OpKind::ColSum};
     o.f0 = pcw;
     o.f3 = g->conv_w;
@@ -546,12 +556,6 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     LAYER_TRY(gemm(fn, "in_proj dgrad x", h, false, false, N, dm, Di, d_x, at, Di, w->w_in, at, dm, 0.0f, d_xn, d_xn, f32,
                    dm));
     LAYER_TRY(gemm(fn, "in_proj dgrad z", h, false, false, N, dm, Di, d_z, at, Di, w_in_z, at, dm, 1.0f, d_xn, d_xn, f32,
-                   dm));
-    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[3]));
-    LAYER_TRY(gemm(fn, "in_proj wgrad x", hw, true, false, Di, dm, N, d_x, at, Di, xn, at, dm, 1.0f, g->w_in, g->w_in, f32,
-                   dm));
-    float* gw_in_z = g->w_in + Di * dm;
-    LAYER_TRY(gemm(fn, "in_proj wgrad z", hw, true, false, Di, dm, N, d_z, at, Di, xn, at, dm, 1.0f, gw_in_z, gw_in_z, f32,
                    dm));
     // RMSNorm adjoint and the residual
     o = Op{OpKind::RmsnormBwd};
@@ -583,7 +587,7 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     return MAMBA_OK;
   };
   const int rc = body();
-  const int rj = fork_wait(fn, sd->s, st, sd->ev[4]);   // join: the caller's stream covers every product
+  const int rj = fork_wait(fn, sd->s, st, sd->ev[5]);   // join: the caller's stream covers every product
   if (rc != MAMBA_OK) return rc;
   if (rj != MAMBA_OK) return rj;
   mscan::set_last_error("");
