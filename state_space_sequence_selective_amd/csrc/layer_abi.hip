@@ -54,9 +54,24 @@ struct LPlan {
   size_t w_dt, w_core_f, wf_total;
   // workspace: backward
   size_t w_dy, w_dgated, w_du, w_ddr, w_dz, w_dxdbl, w_dxdbl_a, w_duex, w_dx, w_dxn, w_pnorm, w_pbdt, w_pconv_w,
-      w_pconv_b, w_core_b, wb_total;
+      w_pconv_b, w_pwg, w_core_b, wb_total;
   int64_t norm_per, norm_nblk, bdt_per, bdt_nblk, conv_nblk;
+  int64_t P_dt, P_x;   // K chunks of the dt_proj / x_proj weight products
 };
+
+// K chunks for a weight product grad[M, N] += A^T B over K token rows.  Its
+// output is small next to K, so a single product covers the chip with few
+// tiles, each looping over all of K; P chunks run as one batched product
+// into P partials that a fixed-order sum adds (no atomics).  P aims at
+// about 512 tiles of 64 x 64 and keeps at least 256 rows per chunk.
+int64_t wgrad_chunks(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  int64_t P = (512 + tiles - 1) / tiles;
+  P = P < 16 ? P : 16;
+  const int64_t by_rows = K / 256;
+  P = P < by_rows ? P : by_rows;
+  return P < 1 ? 1 : P;
+}
 
 // Lays out consecutive 256-byte-aligned regions.
 struct Layout {
@@ -147,6 +162,13 @@ int plan_layer(const mamba_layer_dims_t* d, const char* fn, LPlan* pl) {
   pl->w_pbdt = wb.take(static_cast<size_t>(pl->bdt_nblk) * Di * f);
   pl->w_pconv_w = wb.take(nconv * Di * static_cast<size_t>(pl->K) * f);
   pl->w_pconv_b = wb.take(nconv * Di * f);
+  // partials of the split weight products (one region, the two run in turn
+  // on one stream): P chunks plus a tail chunk when P does not divide N
+  pl->P_dt = wgrad_chunks(pl->Di, pl->R, pl->N);
+  pl->P_x = wgrad_chunks(pl->X, pl->Di, pl->N);
+  const size_t pdt = pl->P_dt > 1 ? static_cast<size_t>(pl->P_dt + 1) * Di * static_cast<size_t>(pl->R) : 0;
+  const size_t px = pl->P_x > 1 ? static_cast<size_t>(pl->P_x + 1) * X * Di : 0;
+  pl->w_pwg = wb.take((pdt > px ? pdt : px) * f);
   pl->w_core_b = wb.take(ws);
   pl->wb_total = wb.off;
   return MAMBA_OK;
@@ -292,6 +314,42 @@ int run(const char* fn, const char* what, const Op& o, mscan::Act act, hipStream
   const hipError_t e = mlayer::launch(o, act, st);
   if (e != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string(what) + " launch: " + hipGetErrorString(e));
   return MAMBA_OK;
+}
+
+// grad[M, N] (f32, row-major, contiguous) += A^T B, A [K, M] and B [K, N]
+// row-major typed (es bytes per element), on stream s with handle h.  With
+// P > 1: P chunks of K / P rows as one strided-batched product into part
+// [P, M, N], the K % P rows left as one more product into part[P], then the
+// partials added in chunk order onto grad.
+int wgrad(const char* fn, const char* what, rocblas_handle h, hipStream_t s, mscan::Act act, int64_t M, int64_t N,
+          int64_t K, const void* A, rocblas_datatype at, int64_t lda, const void* B, rocblas_datatype bt, int64_t ldb,
+          int64_t es, float* grad, float* part, int64_t P) {
+  const rocblas_datatype f32 = rocblas_datatype_f32_r;
+  if (P <= 1) return gemm(fn, what, h, true, false, M, N, K, A, at, lda, B, bt, ldb, 1.0f, grad, grad, f32, N);
+  const int64_t Kc = K / P, Kt = K - P * Kc;
+  const float alpha = 1.0f, beta = 0.0f;
+  const rocblas_status st = rocblas_gemm_strided_batched_ex(
+      h, rocblas_operation_none, rocblas_operation_transpose, static_cast<rocblas_int>(N), static_cast<rocblas_int>(M),
+      static_cast<rocblas_int>(Kc), &alpha, B, bt, static_cast<rocblas_int>(ldb), Kc * ldb, A, at,
+      static_cast<rocblas_int>(lda), Kc * lda, &beta, part, f32, static_cast<rocblas_int>(N), M * N, part, f32,
+      static_cast<rocblas_int>(N), M * N, static_cast<rocblas_int>(P), f32, rocblas_gemm_algo_standard, 0, 0);
+  if (st != rocblas_status_success)
+    return fail(MAMBA_ERR_HIP, fn, std::string(what) + ": rocblas_gemm_strided_batched_ex: " +
+                                       rocblas_status_to_string(st));
+  int64_t nparts = P;
+  if (Kt > 0) {
+    const char* a_t = static_cast<const char*>(A) + P * Kc * lda * es;
+    const char* b_t = static_cast<const char*>(B) + P * Kc * ldb * es;
+    float* p_t = part + P * M * N;
+    LAYER_TRY(gemm(fn, what, h, true, false, M, N, Kt, a_t, at, lda, b_t, bt, ldb, 0.0f, p_t, p_t, f32, N));
+    ++nparts;
+  }
+  Op o{OpKind::ColSum};
+  o.f0 = part;
+  o.f3 = grad;
+  o.nblk = nparts;
+  o.cols = M * N;
+  return run(fn, what, o, act, s);
 }
 
 int core_call(const char* fn, const char* what, int rc) {
@@ -464,6 +522,7 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     float* pbdt = reinterpret_cast<float*>(W + pl.w_pbdt);
     float* pcw = reinterpret_cast<float*>(W + pl.w_pconv_w);
     float* pcb = reinterpret_cast<float*>(W + pl.w_pconv_b);
+    float* pwg = reinterpret_cast<float*>(W + pl.w_pwg);
     const int64_t N = pl.N, Di = pl.Di, dm = pl.dm, X = pl.X, R = pl.R;
     const char* w_in_z = static_cast<const char*>(w->w_in) + Di * dm * pl.es;
 
@@ -496,8 +555,8 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     LAYER_TRY(gemm(fn, "dt_proj dgrad", h, false, false, N, R, Di, d_dr, at, Di, w->w_dt, at, R, 0.0f, d_xdbl, d_xdbl,
                    f32, X));
     LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[2]));
-    LAYER_TRY(gemm(fn, "dt_proj wgrad", hw, true, false, Di, R, N, d_dr, at, Di, xdbl, at, X, 1.0f, g->w_dt, g->w_dt, f32,
-                   R));
+    LAYER_TRY(wgrad(fn, "dt_proj wgrad", hw, sd->s, act, Di, R, N, d_dr, at, Di, xdbl, at, X, pl.es, g->w_dt, pwg,
+                    pl.P_dt));
     o = Op{OpKind::ColPart};
     o.c0 = d_dr;
     o.f3 = pbdt;
@@ -521,8 +580,8 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     LAYER_TRY(gemm(fn, "x_proj dgrad", h, false, false, N, Di, X, d_xdbl_a, at, X, w->w_x, at, Di, 0.0f, d_uex, d_uex, f32,
                    Di));
     LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[3]));
-    LAYER_TRY(gemm(fn, "x_proj wgrad", hw, true, false, X, Di, N, d_xdbl_a, at, X, u, at, Di, 1.0f, g->w_x, g->w_x, f32,
-                   Di));
+    LAYER_TRY(wgrad(fn, "x_proj wgrad", hw, sd->s, act, X, Di, N, d_xdbl_a, at, X, u, at, Di, pl.es, g->w_x, pwg,
+                    pl.P_x));
     // conv + SiLU adjoint: d_x and the weight / bias partials in one pass
     o = Op{OpKind::ConvBwd};
     o.c0 = x;

@@ -116,6 +116,14 @@ def test_layer_segmented_core(mscan):
     check_layer(mscan, w, segments=3)
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_layer_split_weight_products(mscan, act):
+    """1041 token rows: the dt_proj and x_proj weight products split into 4
+    chunks of 260 rows plus a 1-row tail, their partials added in order."""
+    w = workloads.LayerWorkload("layer_splitk_" + act, 3, 347, 64, 128, 16, 4, 4, act)
+    check_layer(mscan, w)
+
+
 @pytest.mark.parametrize("ds,K", [(4, 2), (8, 3), (32, 1)])
 def test_layer_ragged_sizes(mscan, ds, K):
     """Odd widths: d_model 50, d_inner 68 (partial channel groups), odd dt_rank."""
