@@ -133,8 +133,10 @@ def test_layer_ragged_sizes(mscan, ds, K):
 
 def test_layer_deterministic_and_accumulating(mscan):
     """Two backward passes from zeroed gradients give identical bits; without
-    zeroing in between, every gradient doubles exactly (x + x is exact)."""
-    w = workloads.LayerWorkload("layer_det", 2, 96, 64, 128, 16, 4, 4, "bf16")
+    zeroing in between, every gradient doubles exactly (x + x is exact).
+    600 token rows, so the dt_proj / x_proj weight products take their split
+    (two-chunk) path."""
+    w = workloads.LayerWorkload("layer_det", 2, 300, 64, 128, 16, 4, 4, "bf16")
     layer, inp, resid, d_out = run_layer(mscan, w)
     first = {k: v.clone() for k, v in layer.grads.items()}
     d_first = layer.d_resid_in.clone()
