@@ -22,7 +22,8 @@
  *    d_delta, d_u, d_D and d_a_log per sample, d_delta_raw (softplus
  *    backward) and conv weight/bias grads.
  *
- * Everything is double precision and sequential in time.  Per (b, i)
+ * Everything is double precision (the type `real` below) and sequential in
+ * time.  Per (b, i)
  * channel the forward is
  *     u_t      = silu(conv_b[i] + sum_k conv_w[i,k] x_{t-K+1+k})   (fused)
  *              = x_t                                               (no conv)
@@ -34,10 +35,19 @@
  * and the backward is the exact reverse-time adjoint of those lines.
  * Readings taken where the pages are silent are listed next to the code.
  */
-#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <tgmath.h>
+
+/* The parity build is double precision (the default).  Building with
+ * -DORA_REAL=float gives the same code in single precision; that build
+ * only times the oracle on the host and never serves as a reference. */
+#ifndef ORA_REAL
+#define ORA_REAL double
+#endif
+typedef ORA_REAL real;
+#define RC(c) ((real)(c))
 
 typedef struct {
   int64_t batch;    /* B */
@@ -50,23 +60,23 @@ typedef struct {
 } ora_dims;
 
 /* softplus(x) = log(1 + e^x), written so that neither branch overflows. */
-static double ora_softplus(double x) {
-  return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+static real ora_softplus(real x) {
+  return (x > RC(0) ? x : RC(0)) + log1p(exp(-fabs(x)));
 }
 
 /* logistic sigmoid, evaluated on the side where exp() cannot overflow. */
-static double ora_sigmoid(double x) {
-  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
-  double e = exp(x);
-  return e / (1.0 + e);
+static real ora_sigmoid(real x) {
+  if (x >= RC(0)) return RC(1) / (RC(1) + exp(-x));
+  real e = exp(x);
+  return e / (RC(1) + e);
 }
 
-static double ora_silu(double x) { return x * ora_sigmoid(x); }
+static real ora_silu(real x) { return x * ora_sigmoid(x); }
 
 /* d silu / dx = s (1 + x (1 - s)), s = sigmoid(x) */
-static double ora_dsilu(double x) {
-  double s = ora_sigmoid(x);
-  return s * (1.0 + x * (1.0 - s));
+static real ora_dsilu(real x) {
+  real s = ora_sigmoid(x);
+  return s * (RC(1) + x * (RC(1) - s));
 }
 
 static int ora_check(const ora_dims* d) {
@@ -80,20 +90,20 @@ static int ora_check(const ora_dims* d) {
  * Reading (the pages give only the [B*d_inner*d_conv] state shape):
  * the state holds the K most recent inputs, oldest first; positions s < 0
  * read state[K + s], so only its last K-1 entries are ever used. */
-static double ora_conv_in(const ora_dims* d, const double* x, const double* conv_state0,
+static real ora_conv_in(const ora_dims* d, const real* x, const real* conv_state0,
                           int64_t b, int64_t i, int64_t s) {
   const int64_t T = d->seqlen, Di = d->d_inner, K = d->d_conv;
   if (s >= 0) return x[(b * T + s) * Di + i];
-  if (!conv_state0) return 0.0;
+  if (!conv_state0) return RC(0);
   return conv_state0[(b * Di + i) * K + (K + s)];
 }
 
 /* Pre-activation of the convolution at time t: conv_b[i] + sum_k w[i,k] x_{t-K+1+k}. */
-static double ora_conv_pre(const ora_dims* d, const double* x, const double* conv_w,
-                           const double* conv_b, const double* conv_state0,
+static real ora_conv_pre(const ora_dims* d, const real* x, const real* conv_w,
+                           const real* conv_b, const real* conv_state0,
                            int64_t b, int64_t i, int64_t t) {
   const int64_t K = d->d_conv;
-  double p = conv_b ? conv_b[i] : 0.0;
+  real p = conv_b ? conv_b[i] : RC(0);
   for (int64_t k = 0; k < K; ++k)
     p += conv_w[i * K + k] * ora_conv_in(d, x, conv_state0, b, i, t - K + 1 + k);
   return p;
@@ -104,41 +114,42 @@ static double ora_conv_pre(const ora_dims* d, const double* x, const double* con
  * hist[(T+1)*Ds] (hist[t+1] = h_t, hist[0] = h_{-1} = h0) and y[T].
  */
 static void ora_channel_forward(const ora_dims* d, int64_t b, int64_t i,
-                                const double* x, const double* conv_w, const double* conv_b,
-                                const double* conv_state0, const double* delta_raw,
-                                const double* a_log, const double* xdbl, const double* D,
-                                const double* h0, double* u, double* delta, double* hist,
-                                double* y) {
+                                const real* x, const real* conv_w, const real* conv_b,
+                                const real* conv_state0, const real* delta_raw,
+                                const real* a_log, const real* xdbl, const real* D,
+                                const real* h0, real* u, real* delta, real* hist,
+                                real* y) {
   const int64_t T = d->seqlen, Di = d->d_inner, Ds = d->d_state, R = d->dt_rank;
   const int64_t X = R + 2 * Ds;
-  for (int64_t n = 0; n < Ds; ++n) hist[n] = h0 ? h0[(b * Di + i) * Ds + n] : 0.0;
+  for (int64_t n = 0; n < Ds; ++n) hist[n] = h0 ? h0[(b * Di + i) * Ds + n] : RC(0);
   for (int64_t t = 0; t < T; ++t) {
     const int64_t row = b * T + t;
-    double ut;
+    real ut;
     if (d->d_conv > 0)
       ut = ora_silu(ora_conv_pre(d, x, conv_w, conv_b, conv_state0, b, i, t));
     else
       ut = x[row * Di + i];
-    const double dt = ora_softplus(delta_raw[row * Di + i]);
+    const real dt = ora_softplus(delta_raw[row * Di + i]);
     u[t] = ut;
     delta[t] = dt;
-    double yt = 0.0;
+    real yt = RC(0);
     for (int64_t n = 0; n < Ds; ++n) {
-      const double A = -exp(a_log[i * Ds + n]);
-      const double Bn = xdbl[row * X + R + n];
-      const double Cn = xdbl[row * X + R + Ds + n];
-      const double hprev = hist[t * Ds + n];
-      const double h = exp(dt * A) * hprev + dt * Bn * ut;
+      const real A = -exp(a_log[i * Ds + n]);
+      const real Bn = xdbl[row * X + R + n];
+      const real Cn = xdbl[row * X + R + Ds + n];
+      const real hprev = hist[t * Ds + n];
+      const real h = exp(dt * A) * hprev + dt * Bn * ut;
       hist[(t + 1) * Ds + n] = h;
       yt += Cn * h;
     }
-    y[t] = yt + (D ? D[i] : 0.0) * ut;
+    y[t] = yt + (D ? D[i] : RC(0)) * ut;
   }
 }
 
 /*
- * Forward over batch rows [b_begin, b_end).  Output pointers other than
- * `out` may be NULL.  Layouts (row-major):
+ * Forward over batch rows [b_begin, b_end) and channels [i_begin, i_end).
+ * Channels never interact in the forward, so any split of them gives the
+ * same values.  Output pointers other than `out` may be NULL.  Layouts (row-major):
  *   x, delta_raw, z, out, y_out, u_out : [B, T, Di]
  *   xdbl                               : [B, T, R + 2 Ds]
  *   a_log                              : [Di, Ds]
@@ -151,27 +162,29 @@ static void ora_channel_forward(const ora_dims* d, int64_t b, int64_t i,
  *                                        step c*L (so ckpt[b, 0] = h0).
  * Returns 0, or 1 on bad arguments, 2 on allocation failure.
  */
-int ora_forward(const ora_dims* d, int64_t b_begin, int64_t b_end, const double* x,
-                const double* conv_w, const double* conv_b, const double* conv_state0,
-                const double* delta_raw, const double* a_log, const double* xdbl,
-                const double* D, const double* z, const double* h0, double* out,
-                double* y_out, double* u_out, double* h_last, double* conv_state_last,
-                double* ckpt) {
+int ora_forward(const ora_dims* d, int64_t b_begin, int64_t b_end, int64_t i_begin,
+                int64_t i_end, const real* x,
+                const real* conv_w, const real* conv_b, const real* conv_state0,
+                const real* delta_raw, const real* a_log, const real* xdbl,
+                const real* D, const real* z, const real* h0, real* out,
+                real* y_out, real* u_out, real* h_last, real* conv_state_last,
+                real* ckpt) {
   if (ora_check(d) || !x || !delta_raw || !a_log || !xdbl || !out) return 1;
   if (d->d_conv > 0 && !conv_w) return 1;
   if (b_begin < 0 || b_end > d->batch || b_begin > b_end) return 1;
+  if (i_begin < 0 || i_end > d->d_inner || i_begin > i_end) return 1;
   const int64_t T = d->seqlen, Di = d->d_inner, Ds = d->d_state, K = d->d_conv;
   const int64_t L = d->chunk, nC = (T + L - 1) / L;
-  double* u = malloc(sizeof(double) * T);
-  double* delta = malloc(sizeof(double) * T);
-  double* y = malloc(sizeof(double) * T);
-  double* hist = malloc(sizeof(double) * (T + 1) * Ds);
+  real* u = malloc(sizeof(real) * T);
+  real* delta = malloc(sizeof(real) * T);
+  real* y = malloc(sizeof(real) * T);
+  real* hist = malloc(sizeof(real) * (T + 1) * Ds);
   if (!u || !delta || !y || !hist) {
     free(u); free(delta); free(y); free(hist);
     return 2;
   }
   for (int64_t b = b_begin; b < b_end; ++b) {
-    for (int64_t i = 0; i < Di; ++i) {
+    for (int64_t i = i_begin; i < i_end; ++i) {
       ora_channel_forward(d, b, i, x, conv_w, conv_b, conv_state0, delta_raw, a_log, xdbl, D,
                           h0, u, delta, hist, y);
       for (int64_t t = 0; t < T; ++t) {
@@ -198,66 +211,72 @@ int ora_forward(const ora_dims* d, int64_t b_begin, int64_t b_end, const double*
 }
 
 /*
- * Backward over batch rows [b_begin, b_end): the reverse-time adjoint of
- * ora_forward for the loss  sum(dout * out) + sum(d_u_extra * u).
+ * Backward over batch rows [b_begin, b_end) and channels [i_begin, i_end):
+ * the reverse-time adjoint of ora_forward for the loss
+ * sum(dout * out) + sum(d_u_extra * u).
  *
  * Outputs (all written, none accumulated):
  *   d_x         [B,T,Di]  gradient w.r.t. x (w.r.t. u when d_conv == 0)
  *   d_delta_raw [B,T,Di]  gradient w.r.t. delta_raw (softplus backward)
  *   d_delta     [B,T,Di]  gradient w.r.t. delta = softplus(delta_raw); may be NULL
  *   d_z         [B,T,Di]  may be NULL when z is NULL
- *   d_xdbl      [B,T,X]   only the B and C columns are written; the dt
+ *   d_xdbl      [B,T,X]   only the B and C columns of the rows
+ *                         [b_begin, b_end) are written (zeroed, then the
+ *                         channels [i_begin, i_end) summed in); the dt
  *                         columns are left untouched
  *   d_a_log     [Di,Ds], d_D [Di], d_conv_w [Di,K], d_conv_b [Di]:
- *                         sums over the rows [b_begin, b_end) only
+ *                         channels [i_begin, i_end) only, summed over the
+ *                         rows [b_begin, b_end)
  * No gradient is returned for h0 or conv_state0 (truncated BPTT).
  */
-int ora_backward(const ora_dims* d, int64_t b_begin, int64_t b_end, const double* x,
-                 const double* conv_w, const double* conv_b, const double* conv_state0,
-                 const double* delta_raw, const double* a_log, const double* xdbl,
-                 const double* D, const double* z, const double* h0, const double* dout,
-                 const double* d_u_extra, double* d_x, double* d_delta_raw, double* d_delta,
-                 double* d_z, double* d_xdbl, double* d_a_log, double* d_D, double* d_conv_w,
-                 double* d_conv_b) {
+int ora_backward(const ora_dims* d, int64_t b_begin, int64_t b_end, int64_t i_begin,
+                 int64_t i_end, const real* x,
+                 const real* conv_w, const real* conv_b, const real* conv_state0,
+                 const real* delta_raw, const real* a_log, const real* xdbl,
+                 const real* D, const real* z, const real* h0, const real* dout,
+                 const real* d_u_extra, real* d_x, real* d_delta_raw, real* d_delta,
+                 real* d_z, real* d_xdbl, real* d_a_log, real* d_D, real* d_conv_w,
+                 real* d_conv_b) {
   if (ora_check(d) || !x || !delta_raw || !a_log || !xdbl || !dout) return 1;
   if (!d_x || !d_delta_raw || !d_xdbl || !d_a_log || !d_D) return 1;
   if (z && !d_z) return 1;
   if (d->d_conv > 0 && (!conv_w || !d_conv_w || !d_conv_b)) return 1;
   if (b_begin < 0 || b_end > d->batch || b_begin > b_end) return 1;
+  if (i_begin < 0 || i_end > d->d_inner || i_begin > i_end) return 1;
   const int64_t T = d->seqlen, Di = d->d_inner, Ds = d->d_state, R = d->dt_rank;
   const int64_t K = d->d_conv, X = R + 2 * Ds;
 
-  double* u = malloc(sizeof(double) * T);
-  double* delta = malloc(sizeof(double) * T);
-  double* y = malloc(sizeof(double) * T);
-  double* hist = malloc(sizeof(double) * (T + 1) * Ds);
-  double* dy = malloc(sizeof(double) * T);
-  double* du = malloc(sizeof(double) * T);
-  double* dh = malloc(sizeof(double) * Ds);
-  double* dA = malloc(sizeof(double) * Ds);
-  double* dp = malloc(sizeof(double) * T);
+  real* u = malloc(sizeof(real) * T);
+  real* delta = malloc(sizeof(real) * T);
+  real* y = malloc(sizeof(real) * T);
+  real* hist = malloc(sizeof(real) * (T + 1) * Ds);
+  real* dy = malloc(sizeof(real) * T);
+  real* du = malloc(sizeof(real) * T);
+  real* dh = malloc(sizeof(real) * Ds);
+  real* dA = malloc(sizeof(real) * Ds);
+  real* dp = malloc(sizeof(real) * T);
   if (!u || !delta || !y || !hist || !dy || !du || !dh || !dA || !dp) {
     free(u); free(delta); free(y); free(hist); free(dy); free(du); free(dh); free(dA); free(dp);
     return 2;
   }
 
-  for (int64_t i = 0; i < Di; ++i) {
-    for (int64_t n = 0; n < Ds; ++n) d_a_log[i * Ds + n] = 0.0;
-    d_D[i] = 0.0;
+  for (int64_t i = i_begin; i < i_end; ++i) {
+    for (int64_t n = 0; n < Ds; ++n) d_a_log[i * Ds + n] = RC(0);
+    d_D[i] = RC(0);
     if (K > 0) {
-      for (int64_t k = 0; k < K; ++k) d_conv_w[i * K + k] = 0.0;
-      d_conv_b[i] = 0.0;
+      for (int64_t k = 0; k < K; ++k) d_conv_w[i * K + k] = RC(0);
+      d_conv_b[i] = RC(0);
     }
   }
   for (int64_t b = b_begin; b < b_end; ++b)
     for (int64_t t = 0; t < T; ++t)
-      for (int64_t j = R; j < X; ++j) d_xdbl[(b * T + t) * X + j] = 0.0;
+      for (int64_t j = R; j < X; ++j) d_xdbl[(b * T + t) * X + j] = RC(0);
 
   for (int64_t b = b_begin; b < b_end; ++b) {
-    for (int64_t i = 0; i < Di; ++i) {
+    for (int64_t i = i_begin; i < i_end; ++i) {
       ora_channel_forward(d, b, i, x, conv_w, conv_b, conv_state0, delta_raw, a_log, xdbl, D,
                           h0, u, delta, hist, y);
-      const double Di_ = D ? D[i] : 0.0;
+      const real Di_ = D ? D[i] : RC(0);
 
       /* gating backward: out = y * silu(z) */
       for (int64_t t = 0; t < T; ++t) {
@@ -271,21 +290,21 @@ int ora_backward(const ora_dims* d, int64_t b_begin, int64_t b_end, const double
       }
 
       /* reverse-time pass through the recurrence */
-      for (int64_t n = 0; n < Ds; ++n) { dh[n] = 0.0; dA[n] = 0.0; }
+      for (int64_t n = 0; n < Ds; ++n) { dh[n] = RC(0); dA[n] = RC(0); }
       for (int64_t t = T - 1; t >= 0; --t) {
         const int64_t row = b * T + t;
         const int64_t e = row * Di + i;
-        const double dt = delta[t], ut = u[t];
-        double du_t = Di_ * dy[t];   /* y = ... + D u */
-        double ddelta_t = 0.0;
+        const real dt = delta[t], ut = u[t];
+        real du_t = Di_ * dy[t];   /* y = ... + D u */
+        real ddelta_t = RC(0);
         d_D[i] += dy[t] * ut;
         for (int64_t n = 0; n < Ds; ++n) {
-          const double A = -exp(a_log[i * Ds + n]);
-          const double Bn = xdbl[row * X + R + n];
-          const double Cn = xdbl[row * X + R + Ds + n];
-          const double hprev = hist[t * Ds + n];
-          const double h = hist[(t + 1) * Ds + n];
-          const double decay = exp(dt * A);
+          const real A = -exp(a_log[i * Ds + n]);
+          const real Bn = xdbl[row * X + R + n];
+          const real Cn = xdbl[row * X + R + Ds + n];
+          const real hprev = hist[t * Ds + n];
+          const real h = hist[(t + 1) * Ds + n];
+          const real decay = exp(dt * A);
           /* y_t = sum_n C_t[n] h_t[n] + ... */
           dh[n] += dy[t] * Cn;
           d_xdbl[row * X + R + Ds + n] += dy[t] * h;
@@ -310,14 +329,14 @@ int ora_backward(const ora_dims* d, int64_t b_begin, int64_t b_end, const double
       if (K > 0) {
         /* u = silu(p), p = conv_b + sum_k w_k x_{t-K+1+k} */
         for (int64_t t = 0; t < T; ++t) {
-          const double p = ora_conv_pre(d, x, conv_w, conv_b, conv_state0, b, i, t);
+          const real p = ora_conv_pre(d, x, conv_w, conv_b, conv_state0, b, i, t);
           dp[t] = du[t] * ora_dsilu(p);
           d_conv_b[i] += dp[t];
           for (int64_t k = 0; k < K; ++k)
             d_conv_w[i * K + k] += dp[t] * ora_conv_in(d, x, conv_state0, b, i, t - K + 1 + k);
         }
         for (int64_t s = 0; s < T; ++s) {
-          double g = 0.0;
+          real g = RC(0);
           for (int64_t k = 0; k < K; ++k) {
             const int64_t t = s + K - 1 - k; /* output step that reads x_s through tap k */
             if (t < T) g += conv_w[i * K + k] * dp[t];

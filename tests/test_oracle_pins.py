@@ -417,3 +417,44 @@ def test_workload_generator_is_seeded_and_rounded():
     assert np.all(bits & 0xFFFF == 0)            # bf16-representable
     np.testing.assert_array_equal(workloads.round_to("f16", a["x"]), a["x"].astype(np.float16).astype(np.float32))
     np.testing.assert_allclose(a["a_log"][0], np.log(np.arange(1, 17)), rtol=1e-7)
+
+
+@pytest.mark.parametrize("threads", [1, 3, 7])
+def test_channel_ranges_do_not_change_results(oracle_lib, threads):
+    """Channels are independent except in d_xdbl (a sum over channels): any
+    split of the channels over threads gives the same forward bits and the
+    same backward bits, and d_xdbl up to the order of its channel sum."""
+    w = workloads.Workload("split_ch", 2, 37, 13, 4, 3, 3, "f32", True)
+    inp = workloads.make_inputs(w, 21, h0=True, conv_state0=True, d_u_extra=True)
+    kw = dict(x=inp["x"], delta_raw=inp["delta_raw"], a_log=inp["a_log"], xdbl=inp["xdbl"], D=inp["D"],
+              z=inp["z"], h0=inp["h0"], conv_w=inp["conv_w"], conv_b=inp["conv_b"],
+              conv_state0=inp["conv_state0"])
+    f1 = oracle_lib.forward(chunk=16, threads=1, **kw)
+    fn = oracle_lib.forward(chunk=16, threads=threads, **kw)
+    for k in f1:
+        assert np.array_equal(f1[k], fn[k]), k
+    g1 = oracle_lib.backward(dout=inp["dout"], d_u_extra=inp["d_u_extra"], threads=1, **kw)
+    gn = oracle_lib.backward(dout=inp["dout"], d_u_extra=inp["d_u_extra"], threads=threads, **kw)
+    for k in g1:
+        if k == "d_xdbl":
+            np.testing.assert_allclose(gn[k], g1[k], rtol=1e-13, atol=1e-13)
+            assert np.all(gn[k][..., :w.dt_rank] == 0.0)
+        else:
+            assert np.array_equal(g1[k], gn[k]), k
+
+
+def test_single_precision_build_tracks_double(oracle_lib):
+    """The float build (host timing only) computes the same definition: its
+    results stay within single-precision rounding of the double build."""
+    w = workloads.Workload("f32_build", 2, 50, 24, 8, 2, 4, "f32", True)
+    inp = workloads.make_inputs(w, 4)
+    kw = dict(x=inp["x"], delta_raw=inp["delta_raw"], a_log=inp["a_log"], xdbl=inp["xdbl"], D=inp["D"],
+              z=inp["z"], conv_w=inp["conv_w"], conv_b=inp["conv_b"])
+    f64 = oracle_lib.forward(chunk=16, **kw)
+    f32 = oracle_lib.forward(chunk=16, precision="f32", **kw)
+    g64 = oracle_lib.backward(dout=inp["dout"], **kw)
+    g32 = oracle_lib.backward(dout=inp["dout"], precision="f32", **kw)
+    assert f32["out"].dtype == np.float32 and g32["d_x"].dtype == np.float32
+    for a, b in [(f32[k], f64[k]) for k in f64] + [(g32[k], g64[k]) for k in g64]:
+        scale = max(1.0, np.abs(b).max())
+        assert np.abs(a.astype(np.float64) - b).max() / scale < 1e-4
