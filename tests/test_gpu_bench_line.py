@@ -50,15 +50,26 @@ def test_default_workload_line():
     # value is tokens per second of the whole step
     assert d["value"] == pytest.approx(w.batch * w.seqlen / (d["ms_per_step"] / 1e3), rel=2e-3)
     r = d["roofline"]
-    assert r["bound"] == "alu" and r["unit"] == "TFLOP/s" and r["peak"] == bench.VALU_PEAK_TFLOPS
-    assert r["achieved"] == pytest.approx(r["algorithmic_flops_per_launch"] / (r["launch_ms"] / 1e3) / 1e12,
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == bench.HBM_PEAK_GBPS
+    assert r["algorithmic_bytes_per_launch"] == bench.algorithmic_bytes(w)[1]
+    assert r["achieved"] == pytest.approx(r["algorithmic_bytes_per_launch"] / (r["launch_ms"] / 1e3) / 1e9,
                                           rel=2e-3)
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=2e-3) and 0 < r["frac"] < 1
     assert r["launch_ms"] < d["ms_per_step"]
-    # the committed counters were taken on these backward sources
-    assert r["traffic"] is not None and r["traffic"] >= r["algorithmic_bytes_per_launch"]
+    # counters are reported only when taken on these backward sources at this interval
+    if r["traffic"] is not None:
+        assert r["traffic"] >= 0.5 * r["algorithmic_bytes_per_launch"]
+    a = d["alu_roofline"]
+    assert a["bound"] == "alu" and 0 < a["frac"] < 1
+    assert a["achieved"] == pytest.approx(a["elements_per_launch"] * a["slots_per_element"] /
+                                          (r["launch_ms"] / 1e3) / 1e12, rel=5e-3)
+    # the step's HBM figure is the model's bytes over the step time
+    assert d["hbm_GBps"] == pytest.approx(sum(bench.algorithmic_bytes(w)) / (d["ms_per_step"] / 1e3) / 1e9,
+                                          rel=2e-3)
+    assert d["copy_GBps"] > 1000
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["unit"] == "tokens/s"
+    assert c["precision"] == "f32" and c["host_logical_cpus"] >= c["cores"] and c["cpu_model"]
     assert "channels" in c["sample"]
 
 

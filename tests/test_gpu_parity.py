@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_F32 = 1e-4
 TOL_HALF = 2e-2
+DEFAULT_CHUNK = 16     # checkpoint interval the library takes for chunk = 0
 
 
 def _need_gpu():
@@ -52,36 +53,34 @@ def _dims(m, w, chunk, segments=0):
     return m.Dims.make(w.batch, w.seqlen, w.d_inner, w.d_state, w.dt_rank, w.d_conv, chunk, w.act, segments)
 
 
-def _oracle(oracle_lib, w, inp, chunk, channels=None):
+def _oracle(oracle_lib, w, inp, chunk):
+    """Oracle forward + backward on the same (rounded) inputs, all channels,
+    checkpoints at the interval the library uses for ``chunk``."""
     kw = dict(x=inp["x"], delta_raw=inp["delta_raw"], a_log=inp["a_log"], xdbl=inp["xdbl"], D=inp.get("D"),
               z=inp.get("z"), h0=inp.get("h0"))
     if w.d_conv:
         kw.update(conv_w=inp["conv_w"], conv_b=inp.get("conv_b"), conv_state0=inp.get("conv_state0"))
-    dout, due = inp["dout"], inp.get("d_u_extra")
-    if channels is not None:
-        S = np.asarray(channels)
-        for k in ("x", "delta_raw", "z"):
-            if kw.get(k) is not None:
-                kw[k] = kw[k][..., S]
-        for k in ("a_log", "D", "conv_w", "conv_b"):
-            if kw.get(k) is not None:
-                kw[k] = kw[k][S]
-        for k in ("h0", "conv_state0"):
-            if kw.get(k) is not None:
-                kw[k] = kw[k][:, S]
-        dout = dout[..., S]
-        due = None if due is None else due[..., S]
-    L = chunk if chunk else 16
+    L = chunk if chunk else DEFAULT_CHUNK
     f = oracle_lib.forward(chunk=L, **kw)
-    g = oracle_lib.backward(dout=dout, d_u_extra=due, **kw)
+    g = oracle_lib.backward(dout=inp["dout"], d_u_extra=inp.get("d_u_extra"), **kw)
     return f, g
 
 
-def _err(gpu, ora, half):
+def _err(gpu, ora, half, nonfinite=False):
+    """Scaled max error of one output tensor.  With ``nonfinite`` the GPU must
+    be non-finite at exactly the oracle's non-finite elements, and the error
+    is taken over the finite ones; otherwise every GPU value must be finite."""
     g = gpu.detach().float().cpu().numpy().astype(np.float64) if isinstance(gpu, torch.Tensor) else gpu
     o = np.asarray(ora, dtype=np.float64)
     assert g.shape == o.shape, (g.shape, o.shape)
-    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    if nonfinite:
+        fg, fo = np.isfinite(g), np.isfinite(o)
+        bad = np.flatnonzero(fg != fo)
+        assert bad.size == 0, "non-finite pattern differs at %d elements, first flat index %d (gpu %r, oracle %r)" % (
+            bad.size, bad[0], g.flat[bad[0]], o.flat[bad[0]])
+        g, o = g[fo], o[fo]
+    else:
+        assert np.all(np.isfinite(g)), "non-finite GPU output"
     diff = np.abs(g - o).max() if g.size else 0.0
     if half:
         scale = np.abs(o).max() if o.size else 1.0
@@ -89,16 +88,45 @@ def _err(gpu, ora, half):
     return diff / max(1.0, np.abs(o).max() if o.size else 1.0)
 
 
-def _check(name, gpu, ora, half, report):
-    e = _err(gpu, ora, half)
+def _check(name, gpu, ora, half, report, nonfinite=False):
+    e = _err(gpu, ora, half, nonfinite)
     tol = TOL_HALF if half else TOL_F32
     report[name] = e
     assert e <= tol, "%s: error %.3e > %.1e" % (name, e, tol)
 
 
+def _check_all(core, w, f, g, rep, nonfinite=False):
+    """Every output of one forward + backward against the oracle."""
+    half = w.act != "f32"
+    _check("out", core.out, f["out"], half, rep, nonfinite)
+    if w.gate:
+        _check("y", core.y, f["y"], half, rep, nonfinite)
+    _check("h_last", core.h_last, f["h_last"], False, rep, nonfinite)
+    _check("ckpt", core.ckpt, f["ckpt"], False, rep, nonfinite)
+    if w.d_conv:
+        if core.u_out is not None:
+            _check("u", core.u_out, f["u"], half, rep, nonfinite)
+        _check("conv_state_last", core.conv_state_last, f["conv_state_last"], False, rep, nonfinite)
+        _check("d_conv_w", core.d_conv_w, g["d_conv_w"], False, rep, nonfinite)
+        _check("d_conv_b", core.d_conv_b, g["d_conv_b"], False, rep, nonfinite)
+    _check("d_x", core.d_x, g["d_x"], half, rep, nonfinite)
+    _check("d_delta_raw", core.d_delta_raw, g["d_delta_raw"], half, rep, nonfinite)
+    if w.gate:
+        _check("d_z", core.d_z, g["d_z"], half, rep, nonfinite)
+    R, Ds = w.dt_rank, w.d_state
+    # the whole of d_xdbl: B and C columns on every row, dt columns untouched (zero)
+    _check("d_B", core.d_xdbl[..., R:R + Ds], g["d_xdbl"][..., R:R + Ds], False, rep, nonfinite)
+    _check("d_C", core.d_xdbl[..., R + Ds:], g["d_xdbl"][..., R + Ds:], False, rep, nonfinite)
+    if R:
+        assert not torch.any(core.d_xdbl[..., :R] != 0), "dt columns of d_xdbl touched"
+    _check("d_a_log", core.d_a_log, g["d_a_log"], False, rep, nonfinite)
+    _check("d_D", core.d_D, g["d_D"], False, rep, nonfinite)
+
+
 def run_case(m, oracle_lib, w, seed=0, chunk=0, h0=False, conv_state0=False, d_u_extra=False, D=True,
-             segments=0):
-    inp = workloads.make_inputs(w, seed, h0=h0, conv_state0=conv_state0, d_u_extra=d_u_extra)
+             segments=0, inp=None, nonfinite=False):
+    if inp is None:
+        inp = workloads.make_inputs(w, seed, h0=h0, conv_state0=conv_state0, d_u_extra=d_u_extra)
     if not D:
         inp["D"] = None
     dev = _device_inputs(w, inp)
@@ -109,27 +137,8 @@ def run_case(m, oracle_lib, w, seed=0, chunk=0, h0=False, conv_state0=False, d_u
     core.backward(dev, dev["dout"])
     torch.cuda.synchronize()
     f, g = _oracle(oracle_lib, w, inp, chunk)
-    half = w.act != "f32"
     rep = {}
-    _check("out", core.out, f["out"], half, rep)
-    if w.gate:
-        _check("y", core.y, f["y"], half, rep)
-    _check("h_last", core.h_last, f["h_last"], False, rep)
-    _check("ckpt", core.ckpt, f["ckpt"], False, rep)
-    if w.d_conv:
-        _check("u", core.u_out, f["u"], half, rep)
-        _check("conv_state_last", core.conv_state_last, f["conv_state_last"], False, rep)
-        _check("d_conv_w", core.d_conv_w, g["d_conv_w"], False, rep)
-        _check("d_conv_b", core.d_conv_b, g["d_conv_b"], False, rep)
-    _check("d_x", core.d_x, g["d_x"], half, rep)
-    _check("d_delta_raw", core.d_delta_raw, g["d_delta_raw"], half, rep)
-    if w.gate:
-        _check("d_z", core.d_z, g["d_z"], half, rep)
-    R, Ds = w.dt_rank, w.d_state
-    _check("d_B", core.d_xdbl[..., R:R + Ds], g["d_xdbl"][..., R:R + Ds], False, rep)
-    _check("d_C", core.d_xdbl[..., R + Ds:], g["d_xdbl"][..., R + Ds:], False, rep)
-    _check("d_a_log", core.d_a_log, g["d_a_log"], False, rep)
-    _check("d_D", core.d_D, g["d_D"], False, rep)
+    _check_all(core, w, f, g, rep, nonfinite)
     print(w.name, "chunk", chunk, "segments", segments, {k: "%.2e" % v for k, v in rep.items()}, flush=True)
     return core, dev, inp, f, g
 
@@ -384,47 +393,25 @@ def test_abi_errors_on_device(mscan):
                        d_xdbl=core.d_xdbl, d_a_log=core.d_a_log, d_D=core.d_D, workspace=small_ws)
 
 
-# ------------------------------------------------- full-size, sampled channels
+# ------------------------------------------------------ full size, every element
 
 
-def _sampled_full(mscan, oracle_lib, name, sample):
+def _full_size(mscan, oracle_lib, name, chunk):
+    """One workload at its full size in the launch configuration bench.py
+    times, every output element against the oracle (all channels: d_B and
+    d_C are sums over every channel of a row)."""
     w = workloads.CONFIGS[name]
     inp = workloads.make_inputs(w, 0)
     dev = _device_inputs(w, inp)
-    dims = _dims(mscan, w, 16)           # the launch configuration bench.py times
-    core = mscan.LayerCore(dims, gate=w.gate)
+    core = mscan.LayerCore(_dims(mscan, w, chunk), gate=w.gate, keep_u=True)
     core.zero_grads()
     core.forward(dev)
     core.backward(dev, dev["dout"])
     torch.cuda.synchronize()
-    S = np.asarray(sample)
-    f, g = _oracle(oracle_lib, w, inp, 16, channels=S)
+    f, g = _oracle(oracle_lib, w, inp, chunk)
     rep = {}
-    half = w.act != "f32"
-    _check("out", core.out[..., S], f["out"], half, rep)
-    _check("y", core.y[..., S], f["y"], half, rep)
-    _check("h_last", core.h_last[:, S], f["h_last"], False, rep)
-    _check("ckpt", core.ckpt[..., S], f["ckpt"], False, rep)
-    _check("d_x", core.d_x[..., S], g["d_x"], half, rep)
-    _check("d_delta_raw", core.d_delta_raw[..., S], g["d_delta_raw"], half, rep)
-    _check("d_z", core.d_z[..., S], g["d_z"], half, rep)
-    _check("d_a_log", core.d_a_log[S], g["d_a_log"], False, rep)
-    _check("d_D", core.d_D[S], g["d_D"], False, rep)
-    if w.d_conv:
-        _check("conv_state_last", core.conv_state_last[:, S], f["conv_state_last"], False, rep)
-        _check("d_conv_w", core.d_conv_w[S], g["d_conv_w"], False, rep)
-        _check("d_conv_b", core.d_conv_b[S], g["d_conv_b"], False, rep)
-    # d_C at the step before each checkpoint, from the (just checked) checkpoints:
-    # d_C[b, cL-1, n] = sum_i dy[b, cL-1, i] h_{cL-1}[b, i, n], dy = dout silu(z)
-    L = dims.L
-    ck = core.ckpt.double().cpu().numpy()                     # [B, nC, Ds, Di]
-    z = inp["z"].astype(np.float64)
-    dy = inp["dout"].astype(np.float64) * z / (1 + np.exp(-z))
-    ts = np.arange(1, ck.shape[1]) * L - 1
-    dC = np.einsum("bci,bcni->bcn", dy[:, ts, :], ck[:, 1:])
-    R, Ds = w.dt_rank, w.d_state
-    _check("d_C@ckpt", core.d_xdbl[:, ts, R + Ds:], dC, False, rep)
-    print(name, "sampled", {k: "%.2e" % v for k, v in rep.items()}, flush=True)
+    _check_all(core, w, f, g, rep)
+    print(name, "chunk", chunk, {k: "%.2e" % v for k, v in rep.items()}, flush=True)
 
 
 @pytest.mark.parametrize("case", range(96))
@@ -496,15 +483,71 @@ def test_long_sequence_many_segments(mscan, oracle_lib):
         print(w.name, "segments", segments, {k: "%.2e" % v for k, v in rep.items()}, flush=True)
 
 
-def test_full_size_130m_sampled(mscan, oracle_lib):
-    _sampled_full(mscan, oracle_lib, "scan_130m_bf16", [0, 1, 63, 64, 700, 1535])
+def test_full_size_130m(mscan, oracle_lib):
+    _full_size(mscan, oracle_lib, "scan_130m_bf16", 16)
 
 
-def test_full_size_fused_layer_sampled(mscan, oracle_lib):
+def test_full_size_fused_layer(mscan, oracle_lib):
     """One layer of the 24-layer fused f16 workload (B=8, T=4096, d_inner
     2048, conv width 4, dt_rank 64) at full size, conv outputs included."""
-    _sampled_full(mscan, oracle_lib, "fused_24l_f16", [0, 1, 1023, 2047])
+    _full_size(mscan, oracle_lib, "fused_24l_f16", 16)
 
 
-def test_full_size_t8192_sampled(mscan, oracle_lib):
-    _sampled_full(mscan, oracle_lib, "scan_2p8b_t8192_bf16", [0, 5, 2047, 5119])
+def test_full_size_t8192(mscan, oracle_lib):
+    _full_size(mscan, oracle_lib, "scan_2p8b_t8192_bf16", 16)
+
+
+# -------------------------------------------------- edge cases of the method
+
+
+def _edge_inputs(w, seed, h0=True, delta=None, a_log=None, conv_state0=False):
+    inp = workloads.make_inputs(w, seed, h0=h0, conv_state0=conv_state0)
+    rng = np.random.default_rng(seed + 99)
+    if delta is not None:
+        inp["delta_raw"] = workloads.round_to(w.act, delta(rng, inp["delta_raw"].shape))
+    if a_log is not None:
+        inp["a_log"] = np.full_like(inp["a_log"], a_log)
+    return inp
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_edge_delta_zero_keeps_state(mscan, oracle_lib, fused):
+    """delta_raw = -1000: softplus is exactly 0, so dA = 1 and the state stays
+    h0 bit for bit at every checkpoint and at the end (through the segment
+    folds too), and d_delta_raw is exactly 0."""
+    w = workloads.Workload("delta0", 2, 300, 100, 16, 3, 4 if fused else 0, "bf16", True)
+    inp = _edge_inputs(w, 31, delta=lambda r, sh: np.full(sh, -1000.0), conv_state0=fused)
+    core, *_ = run_case(mscan, oracle_lib, w, chunk=16, segments=4, inp=inp)
+    h0 = torch.from_numpy(inp["h0"]).cuda()
+    assert torch.equal(core.h_last, h0)
+    assert torch.equal(core.ckpt, h0.permute(0, 2, 1).unsqueeze(1).expand_as(core.ckpt))
+    assert not torch.any(core.d_delta_raw != 0)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_edge_large_delta_underflow(mscan, oracle_lib, act):
+    """delta_raw ~ N(8, 4^2): softplus in its linear range, dA = exp(delta A)
+    and the segment folds exp(A * sum delta) underflow to 0 for most states."""
+    w = workloads.Workload("delta_large_" + act, 2, 300, 100, 16, 3, 0, act, True)
+    inp = _edge_inputs(w, 32, delta=lambda r, sh: r.normal(8.0, 4.0, sh))
+    run_case(mscan, oracle_lib, w, chunk=16, segments=5, inp=inp)
+
+
+def test_edge_memoryless(mscan, oracle_lib):
+    """a_log = log(1e4) with delta_raw ~ N(0, 1): dA = exp(-1e4 delta) is 0 in
+    both precisions, so every step forgets the state (y = delta u B.C + D u)."""
+    w = workloads.Workload("memoryless", 2, 200, 68, 16, 0, 0, "bf16", True)
+    inp = _edge_inputs(w, 33, delta=lambda r, sh: r.normal(0.0, 1.0, sh), a_log=np.log(1e4))
+    run_case(mscan, oracle_lib, w, chunk=16, segments=3, inp=inp)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_edge_nan_propagates_like_the_oracle(mscan, oracle_lib, fused):
+    """One NaN in x and one in dout: every output is non-finite exactly where
+    the oracle's is (no clamping, nothing lost across segment folds or the
+    channel sums), and the finite elements agree."""
+    w = workloads.Workload("nan", 2, 300, 100, 16, 3, 4 if fused else 0, "bf16", True)
+    inp = _edge_inputs(w, 34, h0=True)
+    inp["x"][0, 150, 5] = np.nan
+    inp["dout"][1, 97, 42] = np.nan
+    run_case(mscan, oracle_lib, w, chunk=16, segments=3, inp=inp, nonfinite=True)
