@@ -162,6 +162,28 @@ int mamba_scan_bwd(const mamba_dims_t* dims, const void* u, const void* delta_ra
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mamba_scan_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid hipMalloc).  Same arguments,
+ * outputs and accumulation as mamba_scan_bwd; its scratch (the per-group
+ * partial sums and segment pairs) lives in a static device array of
+ * MAMBA_STATIC_SCRATCH_BYTES per GPU, set up on the first call on a device
+ * (with that device current) and held until the process ends.  The call
+ * allocates and frees nothing.  Dims whose scratch (mamba_workspace_bytes)
+ * exceeds the array return MAMBA_ERR_CAPACITY before anything is enqueued.
+ * All calls on one GPU share its array: calls that may overlap on that GPU
+ * (other streams, other threads) race and must be serialised by the
+ * caller.  `stream` must belong to the current device.
+ */
+#define MAMBA_STATIC_SCRATCH_BYTES (64u << 20)
+
+int mamba_scan_bwd_static(const mamba_dims_t* dims, const void* u, const void* delta_raw,
+                          const float* a_log, const void* xdbl, const float* D, const void* z,
+                          const void* y_saved, const float* ckpt, const void* dout, void* d_u,
+                          void* d_delta_raw, void* d_z, float* d_xdbl, float* d_a_log, float* d_D,
+                          void* stream);
+
+/*
  * Fused forward: causal depthwise conv1d (dims->d_conv taps) + SiLU, then
  * the scan and the gate (steps F4a..F4e on the forward_mixed page).
  *   x [act]: conv input; conv_w f32; conv_b f32 or NULL (= 0);

@@ -10,12 +10,12 @@ forward/backward pair can be issued repeatedly.
 from ._lib import (EXPORTED, LAYER_PARAMS, LAYER_TYPED, LIB_PATH, MAMBA_BF16, MAMBA_F16, MAMBA_F32, Dims,
                    LayerDims, MambaScanError, abi_version, ckpt_bytes, ckpt_shape, conv_scan_gate_bwd,
                    conv_scan_gate_fwd, last_error, layer_bwd, layer_fwd, layer_param_shapes, layer_saved_bytes,
-                   layer_workspace_bytes, load, scan_bwd, scan_fwd, workspace_bytes)
+                   layer_workspace_bytes, load, scan_bwd, scan_bwd_static, scan_fwd, workspace_bytes)
 from .layer import LayerCore
 from .mamba_layer import MambaLayer
 
 __all__ = ["Dims", "MambaScanError", "LayerCore", "abi_version", "last_error", "ckpt_bytes", "ckpt_shape",
-           "workspace_bytes", "scan_fwd", "scan_bwd", "conv_scan_gate_fwd", "conv_scan_gate_bwd", "load",
+           "workspace_bytes", "scan_fwd", "scan_bwd", "scan_bwd_static", "conv_scan_gate_fwd", "conv_scan_gate_bwd", "load",
            "LIB_PATH", "EXPORTED", "MAMBA_F32", "MAMBA_BF16", "MAMBA_F16", "LayerDims", "MambaLayer",
            "LAYER_PARAMS", "LAYER_TYPED", "layer_param_shapes", "layer_saved_bytes", "layer_workspace_bytes",
            "layer_fwd", "layer_bwd"]

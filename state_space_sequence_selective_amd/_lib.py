@@ -22,7 +22,8 @@ ACT_CODES = {"f32": MAMBA_F32, "bf16": MAMBA_BF16, "f16": MAMBA_F16}
 TORCH_DTYPES = {MAMBA_F32: torch.float32, MAMBA_BF16: torch.bfloat16, MAMBA_F16: torch.float16}
 
 EXPORTED = ("mamba_abi_version", "mamba_last_error", "mamba_ckpt_bytes", "mamba_workspace_bytes",
-            "mamba_scan_fwd", "mamba_scan_bwd", "mamba_conv_scan_gate_fwd", "mamba_conv_scan_gate_bwd",
+            "mamba_scan_fwd", "mamba_scan_bwd", "mamba_scan_bwd_static", "mamba_conv_scan_gate_fwd",
+            "mamba_conv_scan_gate_bwd",
             "mamba_layer_saved_bytes", "mamba_layer_workspace_bytes", "mamba_layer_fwd", "mamba_layer_bwd")
 
 # weights of one layer (mamba_layer_weights_t / mamba_layer_grads_t field order)
@@ -89,6 +90,8 @@ def load():
     lib.mamba_scan_fwd.argtypes = [D] + [P] * 12 + [ctypes.c_size_t, P]
     lib.mamba_scan_bwd.restype = ctypes.c_int
     lib.mamba_scan_bwd.argtypes = [D] + [P] * 16 + [ctypes.c_size_t, P]
+    lib.mamba_scan_bwd_static.restype = ctypes.c_int
+    lib.mamba_scan_bwd_static.argtypes = [D] + [P] * 16
     lib.mamba_conv_scan_gate_fwd.restype = ctypes.c_int
     lib.mamba_conv_scan_gate_fwd.argtypes = [D] + [P] * 17 + [ctypes.c_size_t, P]
     lib.mamba_conv_scan_gate_bwd.restype = ctypes.c_int
@@ -219,6 +222,22 @@ def scan_bwd(d: Dims, u, delta_raw, a_log, xdbl, D, z, y_saved, ckpt, dout, *, d
             _ptr(d_a_log, "d_a_log", f, s["a_log"], True), _ptr(d_D, "d_D", f, s["vec"], True),
             ws, wsn, _stream(stream)]
     _check(load().mamba_scan_bwd(*args))
+
+
+def scan_bwd_static(d: Dims, u, delta_raw, a_log, xdbl, D, z, y_saved, ckpt, dout, *, d_u, d_delta_raw, d_z,
+                    d_xdbl, d_a_log, d_D, stream=None):
+    """mamba_scan_bwd_static: scan_bwd with the library's static device
+    scratch instead of a workspace (nothing is allocated)."""
+    s, at, f = _shapes(d), d.act_dtype, torch.float32
+    args = [ctypes.byref(d), _ptr(u, "u", at, s["act"], True), _ptr(delta_raw, "delta_raw", at, s["act"], True),
+            _ptr(a_log, "a_log", f, s["a_log"], True), _ptr(xdbl, "xdbl", at, s["xdbl"], True),
+            _ptr(D, "D", f, s["vec"]), _ptr(z, "z", at, s["act"]), _ptr(y_saved, "y_saved", at, s["act"]),
+            _ptr(ckpt, "ckpt", f, s["ckpt"], True), _ptr(dout, "dout", at, s["act"], True),
+            _ptr(d_u, "d_u", at, s["act"], True), _ptr(d_delta_raw, "d_delta_raw", at, s["act"], True),
+            _ptr(d_z, "d_z", at, s["act"]), _ptr(d_xdbl, "d_xdbl", f, s["xdbl"], True),
+            _ptr(d_a_log, "d_a_log", f, s["a_log"], True), _ptr(d_D, "d_D", f, s["vec"], True),
+            _stream(stream)]
+    _check(load().mamba_scan_bwd_static(*args))
 
 
 def conv_scan_gate_fwd(d: Dims, x, conv_w, conv_b, conv_state0, delta_raw, a_log, xdbl, D=None, z=None,

@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "bwd_table.h"
@@ -305,6 +306,37 @@ int check_workspace(const char* fn, const void* workspace, size_t workspace_byte
   return MAMBA_OK;
 }
 
+// ------------------------------------------------ backward without a workspace
+// Device scratch of mamba_scan_bwd_static: one array per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not the device array: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = size_t(MAMBA_STATIC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int static_scratch(const char* fn, void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MAMBA_ERR_HIP, fn, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MAMBA_ERR_HIP, fn, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return MAMBA_OK;
+}
+
 int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_w, const float* conv_b,
                const float* conv_state0, const void* delta_raw, const float* a_log, const void* xdbl,
                const float* D, const void* z, const float* h0, void* out, void* u_out, void* y_save,
@@ -377,7 +409,7 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
                 const float* D, const void* z, const void* y_saved, const float* ckpt, const void* dout,
                 const void* d_u_extra, void* d_x, void* d_delta_raw, void* d_z, float* d_xdbl,
                 float* d_a_log, float* d_D, float* d_conv_w, float* d_conv_b, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, bool use_static = false) {
   const int e = pl.esize, ba = pl.bulk_align;
   MSCAN_TRY(check_ptr(fn, pl.K ? "x" : "u", x, true, ba));
   MSCAN_TRY(check_ptr(fn, "delta_raw", delta_raw, true, ba));
@@ -401,6 +433,16 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
     MSCAN_TRY(check_ptr(fn, "d_u_extra", d_u_extra, false, e));
     MSCAN_TRY(check_ptr(fn, "d_conv_w", d_conv_w, true, 4));
     MSCAN_TRY(check_ptr(fn, "d_conv_b", d_conv_b, true, 4));
+  }
+  if (use_static) {   // after every argument check: the device is touched only for a valid call
+    const size_t need = workspace_need_bwd(pl);
+    if (need > kStaticScratchBytes)
+      return fail(MAMBA_ERR_CAPACITY, fn,
+                  "these dims need " + std::to_string(need) + " bytes of scratch, more than the " +
+                      std::to_string(kStaticScratchBytes) +
+                      " of the static array: call mamba_scan_bwd with a workspace");
+    MSCAN_TRY(static_scratch(fn, &workspace));
+    workspace_bytes = kStaticScratchBytes;
   }
   MSCAN_TRY(check_ptr(fn, "workspace", workspace, true, 256));
   MSCAN_TRY(check_workspace(fn, workspace, workspace_bytes, workspace_need_bwd(pl)));
@@ -549,6 +591,20 @@ int mamba_scan_bwd(const mamba_dims_t* dims, const void* u, const void* delta_ra
   return do_backward(fn, pl, u, nullptr, nullptr, nullptr, delta_raw, a_log, xdbl, D, z, y_saved, ckpt, dout,
                      nullptr, d_u, d_delta_raw, d_z, d_xdbl, d_a_log, d_D, nullptr, nullptr, workspace,
                      workspace_bytes, stream);
+}
+
+int mamba_scan_bwd_static(const mamba_dims_t* dims, const void* u, const void* delta_raw, const float* a_log,
+                          const void* xdbl, const float* D, const void* z, const void* y_saved, const float* ckpt,
+                          const void* dout, void* d_u, void* d_delta_raw, void* d_z, float* d_xdbl,
+                          float* d_a_log, float* d_D, void* stream) {
+  const char* fn = "mamba_scan_bwd_static";
+  Plan pl;
+  MSCAN_TRY(plan_dims(dims, false, fn, &pl));
+  // every scratch byte the kernels read is written earlier in the same call
+  // (per-group partials, per-segment pairs), so nothing needs clearing
+  return do_backward(fn, pl, u, nullptr, nullptr, nullptr, delta_raw, a_log, xdbl, D, z, y_saved, ckpt, dout,
+                     nullptr, d_u, d_delta_raw, d_z, d_xdbl, d_a_log, d_D, nullptr, nullptr, nullptr, 0, stream,
+                     true);
 }
 
 int mamba_conv_scan_gate_fwd(const mamba_dims_t* dims, const void* x, const float* conv_w, const float* conv_b,

@@ -169,6 +169,25 @@ def test_null_and_misaligned_pointers_rejected_before_launch(pkg):
     assert rc == 1 and "mamba_conv_scan_gate_bwd: d_conv" in pkg.last_error()
 
 
+def test_static_backward_rejects_dims_beyond_its_scratch(pkg):
+    """mamba_scan_bwd_static refuses dims whose scratch exceeds its static
+    array before it touches the device (no GPU here)."""
+    lib = _raw(pkg)
+    good = ctypes.c_void_p(0x10000)      # never dereferenced
+    d = _dims(pkg, batch=2, seqlen=8192, d_inner=5120)
+    assert pkg.workspace_bytes(d) > 64 << 20
+    rc = lib.mamba_scan_bwd_static(ctypes.byref(d), *([good] * 5), None, None, good, good, good, good, None, good,
+                                   good, good, None)
+    assert rc == 3
+    msg = pkg.last_error()
+    assert msg.startswith("mamba_scan_bwd_static: these dims need") and str(64 << 20) in msg
+    # argument checks as in mamba_scan_bwd
+    small = _dims(pkg)
+    rc = lib.mamba_scan_bwd_static(ctypes.byref(small), None, *([good] * 4), None, None, good, good, good, good,
+                                   None, good, good, good, None)
+    assert rc == 1 and pkg.last_error() == "mamba_scan_bwd_static: u is NULL"
+
+
 def test_last_error_is_per_thread(pkg):
     """mamba_last_error() is thread-local: two threads whose calls fail for
     different reasons, interleaved, each read back their own message (the
