@@ -58,10 +58,10 @@
  *     naming the entry point in mamba_last_error().
  *   - Half-precision outputs are rounded to nearest even.
  *
- * Segmented schedule.  When few (batch row, channel group) pairs would fill
- * the GPU, the sequence is cut into segments of whole checkpoint intervals
- * that are scanned in parallel, in the spirit of the parallel prefix scan
- * the forward_mixed page's F4d step switches to for long sequences.  The
+ * Segmented schedule.  When too few (batch row, channel group) pairs would
+ * fill the GPU, the sequence is cut into segments that are scanned in
+ * parallel, in the spirit of the parallel prefix scan the forward_mixed
+ * page's F4d step switches to for long sequences.  The
  * recurrence is affine in the state, so a segment started from zero yields
  * its end state H_s, and the product of its dA is exp(A * sum of delta):
  *   forward : an aggregate pass gives (H_s, sum delta) per segment; the main
@@ -101,12 +101,16 @@ typedef struct mamba_dims {
   int64_t batch;    /* B, 1 .. 65535 */
   int64_t seqlen;   /* T >= 1 */
   int64_t d_inner;  /* Di >= 4, a multiple of 4 (the pages' MambaConfig rule), <= 2^24 */
-  int64_t d_state;  /* Ds in {4, 8, 16, 32} */
+  int64_t d_state;  /* Ds in {4, 8, 16, 32, 64} */
   int64_t dt_rank;  /* R in 0 .. 2^24: xdbl row = [dt (R) | B (Ds) | C (Ds)] */
   int32_t d_conv;   /* K in 1..4 for the fused entry points; ignored by mamba_scan_* */
-  int32_t chunk;    /* checkpoint interval L in {16, 32}; 0 = 16.  The
-                       backward holds L steps of state in registers, so
-                       Ds 32 needs L = 16 */
+  int32_t chunk;    /* checkpoint interval L: a multiple of 16 up to 4096;
+                       0 = 64.  The backward re-runs the recurrence over
+                       tiles of 16 (or, where compiled, 32) steps held in
+                       registers; for a longer L it first regenerates the
+                       states at every 16th step from the checkpoints
+                       (into its workspace), trading one more forward pass
+                       for L/16 times less checkpoint memory */
   int32_t act;      /* mamba_dtype_t of every activation tensor (and xdbl) */
   int32_t segments; /* sequence segments scanned in parallel (see below):
                        0 = chosen from the sizes; n in 1 .. 4096 = n
@@ -125,10 +129,12 @@ const char* mamba_last_error(void);
 /* Bytes of the f32 checkpoint buffer: B * ceil(T/L) * Ds * Di * 4. */
 int mamba_ckpt_bytes(const mamba_dims_t* dims, size_t* bytes);
 
-/* Bytes of device scratch the entry points need: the backward's per-group
-   partial sums (reduced in a fixed order, so the result is run-to-run
-   reproducible) and the segment pairs of the segmented schedule.  One
-   buffer of this size serves the forward and the backward of these dims. */
+/* Bytes of device scratch the entry points need: an f32 copy of the B / C
+   columns (forward for T > 16; backward when it regenerates checkpoints),
+   the backward's per-group partial sums (reduced in a fixed order, so the
+   result is run-to-run reproducible), the segment pairs of the segmented
+   schedule and the regenerated 16-step checkpoints.  One buffer of this
+   size serves the forward and the backward of these dims. */
 int mamba_workspace_bytes(const mamba_dims_t* dims, size_t* bytes);
 
 /*
@@ -139,7 +145,8 @@ int mamba_workspace_bytes(const mamba_dims_t* dims, size_t* bytes);
  *   activation for the backward; required later when z is given);
  *   h_last f32 or NULL; ckpt f32 or NULL (needed by the backward).
  * workspace: device scratch of at least mamba_workspace_bytes(dims) bytes
- *   (NULL allowed when that is 0), contents irrelevant on entry.
+ *   (NULL allowed when T <= 16: the short-sequence path needs none),
+ *   contents irrelevant on entry.
  */
 int mamba_scan_fwd(const mamba_dims_t* dims, const void* u, const void* delta_raw,
                    const float* a_log, const void* xdbl, const float* D, const void* z,

@@ -51,7 +51,8 @@ class Dims(ctypes.Structure):
 
     @property
     def L(self) -> int:
-        return self.chunk if self.chunk else 16
+        """Checkpoint interval: dims.chunk, or the library's default of 64."""
+        return self.chunk if self.chunk else 64
 
     @property
     def xdbl_dim(self) -> int:

@@ -10,11 +10,9 @@
 #include "bwd_table.h"
 #include "mamba_scan.h"
 #include "scan_common.h"
+#include "scan_fwd2.h"
 
 namespace mscan {
-hipError_t launch_fwd_f32(const FwdArgs& p, int ds, int spl, hipStream_t st);
-hipError_t launch_fwd_bf16(const FwdArgs& p, int ds, int spl, hipStream_t st);
-hipError_t launch_fwd_f16(const FwdArgs& p, int ds, int spl, hipStream_t st);
 hipError_t launch_bwd_f32(const BwdArgs& p, int ds, int L, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& p, int ds, int L, hipStream_t st);
 hipError_t launch_bwd_f16(const BwdArgs& p, int ds, int L, hipStream_t st);
@@ -25,12 +23,27 @@ hipError_t launch_carry_f32(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_carry_bf16(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_carry_f16(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& p, hipStream_t st);
+hipError_t launch_fwd2_f32(const Fwd2Args& p, int ds, bool regen, hipStream_t st);
+hipError_t launch_fwd2_bf16(const Fwd2Args& p, int ds, bool regen, hipStream_t st);
+hipError_t launch_fwd2_f16(const Fwd2Args& p, int ds, bool regen, hipStream_t st);
+hipError_t launch_bc_f32_f32(const BcArgs& p, hipStream_t st);
+hipError_t launch_bc_f32_bf16(const BcArgs& p, hipStream_t st);
+hipError_t launch_bc_f32_f16(const BcArgs& p, hipStream_t st);
 
-static hipError_t launch_fwd(const FwdArgs& p, Act act, int ds, int spl, hipStream_t st) {
+static hipError_t launch_fwd2(const Fwd2Args& p, Act act, int ds, bool regen, hipStream_t st) {
   switch (act) {
-    case Act::F32: return launch_fwd_f32(p, ds, spl, st);
-    case Act::BF16: return launch_fwd_bf16(p, ds, spl, st);
-    case Act::F16: return launch_fwd_f16(p, ds, spl, st);
+    case Act::F32: return launch_fwd2_f32(p, ds, regen, st);
+    case Act::BF16: return launch_fwd2_bf16(p, ds, regen, st);
+    case Act::F16: return launch_fwd2_f16(p, ds, regen, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_bc(const BcArgs& p, Act act, hipStream_t st) {
+  switch (act) {
+    case Act::F32: return launch_bc_f32_f32(p, st);
+    case Act::BF16: return launch_bc_f32_bf16(p, st);
+    case Act::F16: return launch_bc_f32_f16(p, st);
   }
   return hipErrorInvalidValue;
 }
@@ -84,40 +97,23 @@ namespace {
 struct Plan {
   int64_t B, T, Di, Ds, R, X, nC, nG;
   int K;          // conv taps (0 for the scan entry points)
-  int L;          // checkpoint interval
-  int spl_fwd;    // states per lane in the forward kernel
+  int L;          // checkpoint interval of the caller's ckpt
+  int Lb;         // interval the backward kernel walks: L, or 16 from regenerated checkpoints
+  int64_t nCb;    // ceil(T / Lb)
   mscan::Act act;
   int esize;      // bytes per activation element
   int bulk_align; // alignment of activation inputs staged with 4 / 16-byte granules
   int Sf, Sb;     // segments of the forward / backward schedule
-  int fwd_tile;   // steps per forward tile
-  int64_t segf_tiles, segb_tiles;   // fwd_tile-step tiles per forward segment, L-step tiles per backward one
+  int64_t segf_steps;   // steps per forward segment (a multiple of 16)
+  int64_t segb_tiles;   // Lb-step tiles per backward segment
+  bool regen() const { return Lb != L; }
 };
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;
+constexpr int kDefaultChunk = 64;   // checkpoint interval when dims.chunk is 0
+constexpr int kMaxChunk = 4096;
 constexpr int64_t kMaxWidth = int64_t(1) << 24;
 constexpr int kMaxSegments = 4096;
-
-// Segment count for a schedule over `ntiles` tiles with `waves` waves per
-// segment: the caller's cap `hint`; otherwise one segment when `waves`
-// reaches `enough`, else enough segments for about `want` waves, keeping at
-// least `min_tiles` tiles per segment.  Returns the count actually used (no
-// empty segment) and the tiles per segment.
-void choose_segments(int hint, int64_t waves, int64_t ntiles, int64_t enough, int64_t want, int64_t min_tiles,
-                     int* S, int64_t* per) {
-  int64_t s = 1;
-  if (hint > 0) {
-    s = hint;
-  } else if (waves < enough) {
-    s = (want + waves - 1) / waves;
-    const int64_t cap = ntiles / min_tiles;
-    s = s < cap ? s : cap;
-  }
-  s = s < ntiles ? s : ntiles;
-  s = s < 1 ? 1 : s;
-  *per = (ntiles + s - 1) / s;
-  *S = static_cast<int>((ntiles + *per - 1) / *per);
-}
 
 // Backward segment count (see kCarryShare below): the caller's `hint`, else
 // one segment when `waves` reaches kWantWaves, else the S in 1 .. about twice
@@ -126,11 +122,9 @@ void choose_segments(int hint, int64_t waves, int64_t ntiles, int64_t enough, in
 // to fewer segments.
 void choose_segments_bwd(int hint, int64_t waves, int64_t resident, int64_t ntiles, int* S, int64_t* per);
 
-// Waves that fill the GPU (1024 SIMDs).  The forward's aggregate pass costs
-// about 40% of a forward, so it splits only below 2 waves per SIMD; the
-// backward's costs about a fifth of a backward and always pays for itself
-// until about 8 waves per SIMD are queued.
-constexpr int64_t kFwdEnoughWaves = 2048;
+// Backward waves that fill the GPU (1024 SIMDs): the backward's aggregate
+// pass costs about a fifth of a backward and always pays for itself until
+// about 8 waves per SIMD are queued.
 constexpr int64_t kWantWaves = 8192;
 constexpr int64_t kMinSegmentTiles = 8;
 // Backward segments.  The main pass runs in rounds of `resident` waves (the
@@ -167,8 +161,43 @@ void choose_segments_bwd(int hint, int64_t waves, int64_t resident, int64_t ntil
   *S = static_cast<int>((ntiles + *per - 1) / *per);
 }
 
-// threads per workgroup of the forward / backward kernels (their launch tables)
-int64_t fwd_threads(int64_t ds) { return mscan::kFwdCpw * (ds == 32 ? ds / 2 : ds); }
+// Forward segments (one single-wave workgroup per 64 channels of a batch
+// row and segment).  Each segment past the first costs an aggregate pass
+// over it, so the forward splits only as far as it takes to fill the GPU in
+// ONE round of resident waves: about `k` waves on each of the 1024 SIMDs,
+// k being what the kernel's registers and LDS ring allow per SIMD.  More
+// segments than that leave a second, mostly idle round; fewer leave SIMDs
+// with fewer waves than others (measured at T=8192, d_inner 5120, 160 waves
+// per segment: 12 / 19 / 25 / 32 segments gave 0.83 / 0.68 / 0.90 / 0.89 ms).
+// The caller's `hint` overrides; segments are whole multiples of 16 steps
+// and, when chosen here, at least kFwdMinSteps long.
+constexpr int64_t kFwdMinSteps = 64;
+
+int64_t fwd_waves_per_simd(int64_t ds, int esize) {
+  const int64_t vgpr_waves = ds <= 16 ? 4 : (ds == 32 ? 3 : 2);   // the kernel's register target
+  const int64_t lds = 3 * (mscan::kFwd2Tile * 2 * ds * 4 + 3 * mscan::kFwd2Tile * 64 * esize);
+  const int64_t lds_waves = (mscan::kLdsBytes / lds) / 4;            // per SIMD, 4 SIMDs per CU
+  const int64_t k = vgpr_waves < lds_waves ? vgpr_waves : lds_waves;
+  return k < 1 ? 1 : k;
+}
+
+void choose_segments_fwd(int hint, int64_t waves, int64_t k, int64_t T, int* S, int64_t* steps) {
+  const int64_t t16 = (T + 15) / 16;   // 16-step units
+  int64_t s = 1;
+  if (hint > 0) {
+    s = hint;
+  } else if (waves < k * 1024) {
+    s = k * 1024 / waves;
+    const int64_t cap = T / kFwdMinSteps;
+    s = s < cap ? s : cap;
+  }
+  s = s < t16 ? s : t16;
+  s = s < 1 ? 1 : s;
+  *steps = (t16 + s - 1) / s * 16;
+  *S = static_cast<int>((T + *steps - 1) / *steps);
+}
+
+// threads per workgroup of the backward kernel (its launch table)
 int64_t bwd_threads(int64_t ds, int L) {
   return mscan::kBwdCpw * (ds / mscan::bwd_states_per_thread(static_cast<int>(ds), L));
 }
@@ -188,15 +217,14 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   if (d->dt_rank < 0) return fail(MAMBA_ERR_INVALID, fn, "dt_rank must be >= 0");
   if (d->dt_rank > kMaxWidth) return fail(MAMBA_ERR_CAPACITY, fn, "dt_rank must be <= 2^24");
   if (d->d_state < 1) return fail(MAMBA_ERR_INVALID, fn, "d_state must be >= 1");
-  if (d->d_state != 4 && d->d_state != 8 && d->d_state != 16 && d->d_state != 32)
-    return fail(MAMBA_ERR_UNSUPPORTED, fn, "d_state must be 4, 8, 16 or 32");
-  if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32)
-    return fail(d->chunk < 0 ? MAMBA_ERR_INVALID : MAMBA_ERR_UNSUPPORTED, fn,
-                "chunk must be 0 (default 16), 16 or 32");
-  const int L = d->chunk ? d->chunk : 16;
-  // the backward keeps L steps of state in registers
-  if (d->d_state == 32 && L != 16)
-    return fail(MAMBA_ERR_UNSUPPORTED, fn, "chunk must be 16 for d_state 32");
+  if (d->d_state != 4 && d->d_state != 8 && d->d_state != 16 && d->d_state != 32 && d->d_state != 64)
+    return fail(MAMBA_ERR_UNSUPPORTED, fn, "d_state must be 4, 8, 16, 32 or 64");
+  if (d->chunk < 0) return fail(MAMBA_ERR_INVALID, fn, "chunk must be >= 0");
+  if (d->chunk % 16 != 0 || d->chunk > kMaxChunk)
+    return fail(MAMBA_ERR_UNSUPPORTED, fn,
+                "chunk must be 0 (default " + std::to_string(kDefaultChunk) + ") or a multiple of 16 up to " +
+                    std::to_string(kMaxChunk));
+  const int L = d->chunk ? d->chunk : kDefaultChunk;
   int K = 0;
   if (fused) {
     if (d->d_conv < 1) return fail(MAMBA_ERR_INVALID, fn, "d_conv must be >= 1");
@@ -214,37 +242,34 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   pl->X = X;
   pl->L = L;
   pl->nC = (d->seqlen + L - 1) / L;
+  // the backward kernel keeps a tile of Lb steps of state in registers; it is
+  // built for 16 and, for some d_state, 32 steps.  Other intervals are walked
+  // in 16-step tiles from checkpoints regenerated out of the caller's.
+  pl->Lb = (L == 16 || mscan::bwd_waves_per_simd(static_cast<int>(d->d_state), L, fused) > 0) ? L : 16;
+  pl->nCb = (d->seqlen + pl->Lb - 1) / pl->Lb;
   pl->nG = (d->d_inner + mscan::kBwdCpw - 1) / mscan::kBwdCpw;
   pl->K = K;
-  pl->spl_fwd = d->d_state == 32 ? 2 : 1;   // one state per thread: most waves per SIMD
   pl->act = static_cast<mscan::Act>(d->act);
   pl->esize = d->act == MAMBA_F32 ? 4 : 2;
   pl->bulk_align = d->act == MAMBA_F32 ? 16 : 4;
-  const int64_t waves_f = (d->d_inner + mscan::kFwdCpw - 1) / mscan::kFwdCpw * d->batch *
-                          (fwd_threads(d->d_state) / 64);
-  const int64_t waves_b = pl->nG * d->batch * (bwd_threads(d->d_state, L) / 64);
-  choose_segments(d->segments, waves_f, (d->seqlen + mscan::kFwdTileShort - 1) / mscan::kFwdTileShort,
-                  kFwdEnoughWaves, kWantWaves, kMinSegmentTiles, &pl->Sf, &pl->segf_tiles);
-  // 32-step tiles pay only without the conv: with its halo rows and staging
-  // the fused forward's larger tile costs occupancy (measured 0.66 -> 0.81 ms
-  // per layer at B=8, T=4096, d_inner 2048, f16)
-  pl->fwd_tile = mscan::kFwdTileShort;
-  if (pl->Sf == 1 && !fused) {
-    pl->fwd_tile = mscan::kFwdTileLong;
-    pl->segf_tiles = (d->seqlen + mscan::kFwdTileLong - 1) / mscan::kFwdTileLong;
-  }
+  const int64_t waves_f = (d->d_inner + 63) / 64 * d->batch;   // one wave per 64 channels and segment
+  const int64_t waves_b = pl->nG * d->batch * (bwd_threads(d->d_state, pl->Lb) / 64);
+  choose_segments_fwd(d->segments, waves_f, fwd_waves_per_simd(d->d_state, pl->esize), d->seqlen, &pl->Sf,
+                      &pl->segf_steps);
   if (fused) {   // the conv backward of a segment's tail needs the next segment's head
     pl->Sb = 1;
-    pl->segb_tiles = pl->nC;
+    pl->segb_tiles = pl->nCb;
   } else {
-    const int64_t resident = 1024 * static_cast<int64_t>(mscan::bwd_waves_per_simd(static_cast<int>(d->d_state), L, false));
-    choose_segments_bwd(d->segments, waves_b, resident, pl->nC, &pl->Sb, &pl->segb_tiles);
+    const int64_t resident =
+        1024 * static_cast<int64_t>(mscan::bwd_waves_per_simd(static_cast<int>(d->d_state), pl->Lb, false));
+    choose_segments_bwd(d->segments, waves_b, resident, pl->nCb, &pl->Sb, &pl->segb_tiles);
   }
-  // a launch holds at most 2^32 - 1 threads: the tiled forward and backward
-  // (all segments in one grid) and the reduction (one thread per d_xdbl B/C
-  // element plus one per parameter-grad slot) are the largest
-  const int64_t thr_f = (d->d_inner + mscan::kFwdCpw - 1) / mscan::kFwdCpw * d->batch * fwd_threads(d->d_state) * pl->Sf;
-  const int64_t thr_b = pl->nG * d->batch * bwd_threads(d->d_state, L) * pl->Sb;
+  // a launch holds at most 2^32 - 1 threads: the forward and backward (all
+  // segments in one grid), the checkpoint regeneration and the reduction
+  // (one thread per d_xdbl B/C element plus one per parameter-grad slot)
+  // are the largest
+  const int64_t thr_f = waves_f * 64 * (pl->Sf > pl->nC ? pl->Sf : pl->nC);
+  const int64_t thr_b = pl->nG * d->batch * bwd_threads(d->d_state, pl->Lb) * pl->Sb;
   const int64_t thr_r = d->batch * d->seqlen * 2 * d->d_state + d->d_inner * (d->d_state + 2 + K);
   const int64_t thr = thr_f > thr_b ? (thr_f > thr_r ? thr_f : thr_r) : (thr_b > thr_r ? thr_b : thr_r);
   if (thr > static_cast<int64_t>(UINT32_MAX))
@@ -277,19 +302,25 @@ size_t bc_part_bytes(const Plan& pl) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Workspace layouts.  Forward: [seg_h | seg_sd] when segmented.  Backward:
-// [part_bc | part_par | seg_q | seg_sd], the last two when segmented.
+// Workspace layouts.  Forward: [bc | seg_h | seg_sd], the last two when
+// segmented (nothing for the short-sequence step kernel).  Backward:
+// [part_bc | part_par | seg_q | seg_sd | bc | sub], seg_q and seg_sd when
+// segmented, bc and sub when the checkpoints are regenerated.
 size_t seg_state_bytes(const Plan& pl, int S) { return align256(sizeof(float) * pl.B * S * pl.Di * pl.Ds); }
 size_t seg_sum_bytes(const Plan& pl, int S) { return align256(sizeof(float) * pl.B * S * pl.Di); }
 size_t par_part_bytes(const Plan& pl) { return align256(sizeof(float) * pl.Sb * pl.B * pl.Di * param_width(pl)); }
+size_t bc_f32_bytes(const Plan& pl) { return align256(sizeof(float) * pl.B * pl.T * 2 * pl.Ds); }
+size_t sub_ckpt_bytes(const Plan& pl) { return align256(sizeof(float) * pl.B * ((pl.T + 15) / 16) * pl.Ds * pl.Di); }
 
 size_t workspace_need_fwd(const Plan& pl) {
-  return pl.Sf > 1 ? seg_state_bytes(pl, pl.Sf) + seg_sum_bytes(pl, pl.Sf) : 0;
+  if (pl.T <= mscan::kStepMaxT) return 0;
+  return bc_f32_bytes(pl) + (pl.Sf > 1 ? seg_state_bytes(pl, pl.Sf) + seg_sum_bytes(pl, pl.Sf) : 0);
 }
 
 size_t workspace_need_bwd(const Plan& pl) {
   return align256(bc_part_bytes(pl)) + par_part_bytes(pl) +
-         (pl.Sb > 1 ? seg_state_bytes(pl, pl.Sb) + seg_sum_bytes(pl, pl.Sb) : 0);
+         (pl.Sb > 1 ? seg_state_bytes(pl, pl.Sb) + seg_sum_bytes(pl, pl.Sb) : 0) +
+         (pl.regen() ? bc_f32_bytes(pl) + sub_ckpt_bytes(pl) : 0);
 }
 
 size_t workspace_need(const Plan& pl) {
@@ -386,19 +417,54 @@ int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_
   a.X = pl.X;
   a.nC = pl.nC;
   a.K = pl.K;
-  a.L = pl.L;
-  a.S = pl.Sf;
-  a.seg_tiles = pl.segf_tiles;
-  a.tile = pl.fwd_tile;
-  if (pl.Sf > 1) {
-    a.seg_h = static_cast<float*>(workspace);
-    a.seg_sd = reinterpret_cast<float*>(static_cast<char*>(workspace) + seg_state_bytes(pl, pl.Sf));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (pl.T <= mscan::kStepMaxT) {
+    // short sequences (recurrent steps): one thread per channel, no staging
+    err = mscan::launch_step(a, pl.act, static_cast<int>(pl.Ds), st);
+  } else {
+    char* ws = static_cast<char*>(workspace);
+    mscan::BcArgs c{};
+    c.xdbl = xdbl;
+    c.bc = reinterpret_cast<float*>(ws);
+    c.rows = pl.B * pl.T;
+    c.X = pl.X;
+    c.R = pl.R;
+    c.Ds = pl.Ds;
+    err = mscan::launch_bc(c, pl.act, st);
+    if (err == hipSuccess) {
+      mscan::Fwd2Args f{};
+      f.x = x;
+      f.delta_raw = delta_raw;
+      f.a_log = a_log;
+      f.bc = c.bc;
+      f.D = D;
+      f.z = z;
+      f.h0 = h0;
+      f.conv_w = conv_w;
+      f.conv_b = conv_b;
+      f.conv_state0 = conv_state0;
+      f.out = out;
+      f.u_out = u_out;
+      f.y_save = y_save;
+      f.h_last = h_last;
+      f.conv_state_last = conv_state_last;
+      f.ckpt = ckpt;
+      f.B = pl.B;
+      f.T = pl.T;
+      f.Di = pl.Di;
+      f.nC = pl.nC;
+      f.seg_steps = pl.segf_steps;
+      f.K = pl.K;
+      f.L = pl.L;
+      f.S = pl.Sf;
+      if (pl.Sf > 1) {
+        f.seg_h = reinterpret_cast<float*>(ws + bc_f32_bytes(pl));
+        f.seg_sd = reinterpret_cast<float*>(ws + bc_f32_bytes(pl) + seg_state_bytes(pl, pl.Sf));
+      }
+      err = mscan::launch_fwd2(f, pl.act, static_cast<int>(pl.Ds), false, st);
+    }
   }
-  // short sequences (recurrent steps): one thread per channel, no staging
-  hipError_t err = pl.T <= mscan::kStepMaxT
-                       ? mscan::launch_step(a, pl.act, static_cast<int>(pl.Ds), static_cast<hipStream_t>(stream))
-                       : mscan::launch_fwd(a, pl.act, static_cast<int>(pl.Ds), pl.spl_fwd,
-                                           static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("forward launch: ") + hipGetErrorString(err));
   g_err.clear();
   return MAMBA_OK;
@@ -449,10 +515,49 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   char* ws = static_cast<char*>(workspace);
   float* part_bc = reinterpret_cast<float*>(ws);
   float* part_par = reinterpret_cast<float*>(ws + align256(bc_part_bytes(pl)));
-  float* seg_q = reinterpret_cast<float*>(ws + align256(bc_part_bytes(pl)) + par_part_bytes(pl));
-  float* seg_sd = reinterpret_cast<float*>(reinterpret_cast<char*>(seg_q) + seg_state_bytes(pl, pl.Sb));
+  char* after_par = ws + align256(bc_part_bytes(pl)) + par_part_bytes(pl);
+  float* seg_q = reinterpret_cast<float*>(after_par);
+  float* seg_sd = reinterpret_cast<float*>(after_par + seg_state_bytes(pl, pl.Sb));
+  char* after_seg = after_par + (pl.Sb > 1 ? seg_state_bytes(pl, pl.Sb) + seg_sum_bytes(pl, pl.Sb) : 0);
   const int PW = static_cast<int>(param_width(pl));
   hipStream_t st = static_cast<hipStream_t>(stream);
+
+  const float* ckpt_b = ckpt;   // checkpoints the backward kernel walks, every Lb steps
+  if (pl.regen()) {
+    // states entering every 16th step, regenerated from the caller's
+    // checkpoints (every L steps) by the forward recurrence
+    mscan::BcArgs c{};
+    c.xdbl = xdbl;
+    c.bc = reinterpret_cast<float*>(after_seg);
+    c.rows = pl.B * pl.T;
+    c.X = pl.X;
+    c.R = pl.R;
+    c.Ds = pl.Ds;
+    hipError_t err = mscan::launch_bc(c, pl.act, st);
+    if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("B/C copy launch: ") + hipGetErrorString(err));
+    mscan::Fwd2Args f{};
+    f.x = x;
+    f.delta_raw = delta_raw;
+    f.a_log = a_log;
+    f.bc = c.bc;
+    f.conv_w = conv_w;
+    f.conv_b = conv_b;
+    f.conv_state0 = conv_state0;
+    f.ckpt = const_cast<float*>(ckpt);   // read only in this mode
+    f.sub = reinterpret_cast<float*>(after_seg + bc_f32_bytes(pl));
+    f.B = pl.B;
+    f.T = pl.T;
+    f.Di = pl.Di;
+    f.nC = pl.nC;
+    f.seg_steps = pl.L;
+    f.K = pl.K;
+    f.L = pl.L;
+    f.S = static_cast<int>(pl.nC);
+    err = mscan::launch_fwd2(f, pl.act, static_cast<int>(pl.Ds), true, st);
+    if (err != hipSuccess)
+      return fail(MAMBA_ERR_HIP, fn, std::string("checkpoint regeneration launch: ") + hipGetErrorString(err));
+    ckpt_b = f.sub;
+  }
 
   if (pl.Sb > 1) {   // aggregate pass: carries the segments hand back from a zero start
     mscan::CarryArgs c{};
@@ -468,7 +573,7 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
     c.Di = pl.Di;
     c.R = pl.R;
     c.X = pl.X;
-    c.seg_steps = pl.segb_tiles * pl.L;
+    c.seg_steps = pl.segb_tiles * pl.Lb;
     c.S = pl.Sb;
     hipError_t err = mscan::launch_carry(c, pl.act, static_cast<int>(pl.Ds), st);
     if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("carry launch: ") + hipGetErrorString(err));
@@ -485,7 +590,7 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   a.conv_w = conv_w;
   a.conv_b = conv_b;
   a.conv_state0 = conv_state0;
-  a.ckpt = ckpt;
+  a.ckpt = ckpt_b;
   a.dout = dout;
   a.d_u_extra = d_u_extra;
   a.d_x = d_x;
@@ -498,9 +603,9 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   a.Di = pl.Di;
   a.R = pl.R;
   a.X = pl.X;
-  a.nC = pl.nC;
+  a.nC = pl.nCb;
   a.K = pl.K;
-  a.L = pl.L;
+  a.L = pl.Lb;
   a.PW = PW;
   a.S = pl.Sb;
   a.seg_tiles = pl.segb_tiles;
@@ -508,7 +613,7 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
     a.seg_q = seg_q;
     a.seg_sd = seg_sd;
   }
-  hipError_t err = mscan::launch_bwd(a, pl.act, static_cast<int>(pl.Ds), pl.L, st);
+  hipError_t err = mscan::launch_bwd(a, pl.act, static_cast<int>(pl.Ds), pl.Lb, st);
   if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("backward launch: ") + hipGetErrorString(err));
 
   mscan::ReduceArgs r{};

@@ -164,6 +164,7 @@ hipError_t launch_carry_a(const CarryArgs& p, int ds, hipStream_t st) {
   if (ds == 8) return launch_carry_t<A, 8, 2>(p, st);
   if (ds == 16) return launch_carry_t<A, 16, 2>(p, st);
   if (ds == 32) return launch_carry_t<A, 32, 2>(p, st);
+  if (ds == 64) return launch_carry_t<A, 64, 4>(p, st);
   return hipErrorInvalidValue;
 }
 

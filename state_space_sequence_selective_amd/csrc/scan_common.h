@@ -12,24 +12,13 @@ enum class Act : int { F32 = 0, BF16 = 1, F16 = 2 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Channels per workgroup.  A thread is (state group, channel).  The forward
-// uses 16 channels (a wave = 16 channels x 4 state groups): small workgroups
-// give 2 to 3 per CU at the long-sequence 2.8B layer shape, which evens the
-// load across SIMDs.  The backward balances through sequence segments
-// instead and uses 32 channels, which halves its per-group d_B/d_C partials.
-constexpr int kFwdCpw = 16;
+// Channels per backward workgroup.  A thread is (state group, channel).
+// The backward balances through sequence segments and uses 32 channels,
+// which halves its per-group d_B/d_C partials against 16.
 constexpr int kBwdCpw = 32;
 
-// Steps per forward tile.  An unsegmented forward (few waves per SIMD) uses
-// long tiles, which halve the per-tile overheads; a segmented one has many
-// waves queued and uses short tiles, whose half-size LDS footprint fits
-// twice as many workgroups per CU.  Checkpoints (every 16 or 32 steps) fall
-// on 16-step boundaries inside a tile.
 // LDS a workgroup may hold on gfx950 (static and dynamic together)
 constexpr int kLdsBytes = 160 * 1024;
-
-constexpr int kFwdTileLong = 32;
-constexpr int kFwdTileShort = 16;
 
 // Forward sequences up to this length take scan_step_kernel (one thread per
 // channel, no staging); it must not exceed the smallest checkpoint interval.
@@ -177,6 +166,11 @@ constexpr int line_sharing_groups() {
 // global_load_lds waits for it explicitly (s_waitcnt 0) before a barrier.
 constexpr int kWaitLgkmOnly = 0xC07F;   // s_waitcnt vmcnt(63) expcnt(7) lgkmcnt(0)
 
+// s_waitcnt operand that waits until at most n (0..63) vector-memory
+// operations of this wave are in flight, and for nothing else (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (0xF << 8); }
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_s_waitcnt(kWaitLgkmOnly);
@@ -255,6 +249,7 @@ __device__ __forceinline__ float raw_ld<Act::F16>(const char* base, int idx) {
 }
 
 // ---------------------------------------------------------------- arguments
+// short-sequence forward (scan_step_kernel)
 struct FwdArgs {
   const void* x;            // u (scan entry) or conv input (fused entry) [B,T,Di]
   const void* delta_raw;    // [B,T,Di]
@@ -272,15 +267,8 @@ struct FwdArgs {
   float* h_last;            // [B,Di,Ds] or null
   float* conv_state_last;   // [B,Di,K] or null
   float* ckpt;              // [B,nC,Ds,Di] or null
-  // segmented schedule: segment s covers tiles [s * seg_tiles, ...) of TT steps
-  float* seg_h;             // [B,S,Di,Ds] end state of each segment scanned from zero
-  float* seg_sd;            // [B,S,Di] sum of delta over each segment
   int64_t B, T, Di, R, X, nC;
-  int64_t seg_tiles;        // tiles per segment
   int K;                    // conv taps, 0 = no conv
-  int L;                    // checkpoint interval
-  int S;                    // segments
-  int tile;                 // steps per tile: kFwdTileLong (S == 1) or kFwdTileShort
 };
 
 struct BwdArgs {

@@ -190,7 +190,7 @@ hipError_t launch_step_a(const FwdArgs& p, int ds, hipStream_t st) {
     else hipLaunchKernelGGL((scan_step_kernel<A, DS_, false>), grid, dim3(256), 0, st, p);       \
     return hipGetLastError();                                                                   \
   }
-  MSCAN_CASE(4) MSCAN_CASE(8) MSCAN_CASE(16) MSCAN_CASE(32)
+  MSCAN_CASE(4) MSCAN_CASE(8) MSCAN_CASE(16) MSCAN_CASE(32) MSCAN_CASE(64)
 #undef MSCAN_CASE
   return hipErrorInvalidValue;
 }

@@ -68,11 +68,11 @@ def test_sizes(pkg):
     (dict(d_inner=66), 1, "d_inner"),
     (dict(d_inner=0), 1, "d_inner"),
     (dict(d_state=12), 2, "d_state"),
-    (dict(d_state=64), 2, "d_state"),
-    (dict(chunk=48), 2, "chunk"),
+    (dict(d_state=128), 2, "d_state"),
+    (dict(chunk=20), 2, "chunk"),
+    (dict(chunk=8), 2, "chunk"),
     (dict(chunk=-16), 1, "chunk"),
-    (dict(chunk=64), 2, "chunk"),
-    (dict(d_state=32, chunk=32), 2, "chunk"),
+    (dict(chunk=4096 + 16), 2, "chunk"),
     (dict(dt_rank=-1), 1, "dt_rank"),
     (dict(dt_rank=(1 << 24) + 1), 3, "dt_rank"),
     (dict(d_inner=(1 << 24) + 4), 3, "d_inner"),

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_F32 = 1e-4
 TOL_HALF = 2e-2
-DEFAULT_CHUNK = 16     # checkpoint interval the library takes for chunk = 0
+DEFAULT_CHUNK = 64     # checkpoint interval the library takes for chunk = 0
 
 
 def _need_gpu():
@@ -171,7 +171,8 @@ def test_fused_ragged_states_and_extras(mscan, oracle_lib, act):
     run_case(mscan, oracle_lib, w, chunk=16, h0=True, conv_state0=True, d_u_extra=True)
 
 
-@pytest.mark.parametrize("ds,chunk", [(4, 32), (4, 16), (8, 32), (8, 16), (16, 16), (32, 16)])
+@pytest.mark.parametrize("ds,chunk", [(4, 32), (4, 16), (8, 32), (8, 16), (16, 16), (32, 16), (64, 16), (64, 64),
+                                      (32, 32), (16, 64), (8, 48), (4, 128)])
 def test_state_sizes(mscan, oracle_lib, ds, chunk):
     w = workloads.Workload("ds%d" % ds, 2, 70, 132, ds, 3, 0, "bf16", True)
     run_case(mscan, oracle_lib, w, chunk=chunk, h0=True)
@@ -382,7 +383,7 @@ def test_abi_errors_on_device(mscan):
     dims = _dims(mscan, w, 32)
     core = mscan.LayerCore(dims)
     inp = _device_inputs(w, workloads.make_inputs(w, 0))
-    bad = mscan.Dims.make(1, 8, 64, 16, 0, 0, 48, "bf16")
+    bad = mscan.Dims.make(1, 8, 64, 16, 0, 0, 40, "bf16")
     with pytest.raises(mscan.MambaScanError, match="chunk"):
         mscan.scan_fwd(bad, inp["x"], inp["delta_raw"], inp["a_log"], inp["xdbl"], out=core.out)
     small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
@@ -416,13 +417,14 @@ def _full_size(mscan, oracle_lib, name, chunk):
 
 @pytest.mark.parametrize("case", range(96))
 def test_random_configurations(mscan, oracle_lib, case):
-    """Seeded random combinations of d_state, checkpoint interval,
-    activation type, conv width (or none), dt_rank (odd ones included),
-    gate, D, optional states and extra gradient, ragged widths and lengths,
-    and segment counts, each against the oracle."""
+    """Seeded random combinations of d_state, checkpoint interval (intervals
+    the backward walks directly and longer ones it regenerates 16-step
+    checkpoints for), activation type, conv width (or none), dt_rank (odd
+    ones included), gate, D, optional states and extra gradient, ragged
+    widths and lengths, and segment counts, each against the oracle."""
     rng = np.random.default_rng(1000 + case)
-    ds = int(rng.choice([4, 8, 16, 32]))
-    chunk = 16 if ds == 32 else int(rng.choice([16, 32]))
+    ds = int(rng.choice([4, 8, 16, 32, 64]))
+    chunk = int(rng.choice([0, 16, 32, 48, 64]))
     act = str(rng.choice(["f32", "bf16", "f16"]))
     K = int(rng.choice([0, 0, 1, 2, 3, 4]))
     B, T, Di, R = int(rng.integers(1, 4)), int(rng.integers(1, 300)), 4 * int(rng.integers(1, 40)), int(rng.integers(0, 9))
@@ -442,8 +444,8 @@ def test_random_medium_configurations(mscan, oracle_lib, case):
     dt_rank up to 64, segment counts up to 16; every output against the
     oracle."""
     rng = np.random.default_rng(5000 + case)
-    ds = int(rng.choice([4, 8, 16, 32]))
-    chunk = 16 if ds == 32 else int(rng.choice([16, 32]))
+    ds = int(rng.choice([4, 8, 16, 32, 64]))
+    chunk = int(rng.choice([0, 16, 32, 64, 128]))
     act = str(rng.choice(["f32", "bf16", "f16"]))
     K = int(rng.choice([0, 0, 1, 2, 3, 4]))
     B, T, Di, R = int(rng.integers(1, 5)), int(rng.integers(300, 3000)), 4 * int(rng.integers(16, 256)), int(rng.integers(0, 65))
@@ -483,8 +485,11 @@ def test_long_sequence_many_segments(mscan, oracle_lib):
         print(w.name, "segments", segments, {k: "%.2e" % v for k, v in rep.items()}, flush=True)
 
 
-def test_full_size_130m(mscan, oracle_lib):
-    _full_size(mscan, oracle_lib, "scan_130m_bf16", 16)
+@pytest.mark.parametrize("chunk", [64, 16])
+def test_full_size_130m(mscan, oracle_lib, chunk):
+    """The 130M shape; 64 is the workload's stated chunk size (the backward
+    regenerates 16-step checkpoints from it)."""
+    _full_size(mscan, oracle_lib, "scan_130m_bf16", chunk)
 
 
 def test_full_size_fused_layer(mscan, oracle_lib):
@@ -493,8 +498,9 @@ def test_full_size_fused_layer(mscan, oracle_lib):
     _full_size(mscan, oracle_lib, "fused_24l_f16", 16)
 
 
-def test_full_size_t8192(mscan, oracle_lib):
-    _full_size(mscan, oracle_lib, "scan_2p8b_t8192_bf16", 16)
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_full_size_t8192(mscan, oracle_lib, chunk):
+    _full_size(mscan, oracle_lib, "scan_2p8b_t8192_bf16", chunk)
 
 
 # -------------------------------------------------- edge cases of the method
