@@ -10,6 +10,7 @@
 #include "bwd_table.h"
 #include "mamba_scan.h"
 #include "scan_common.h"
+#include "scan_conv.h"
 #include "scan_fwd2.h"
 
 namespace mscan {
@@ -23,6 +24,18 @@ hipError_t launch_carry_f32(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_carry_bf16(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_carry_f16(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& p, hipStream_t st);
+hipError_t launch_conv_bwd_f32(const ConvBwdArgs& p, hipStream_t st);
+hipError_t launch_conv_bwd_bf16(const ConvBwdArgs& p, hipStream_t st);
+hipError_t launch_conv_bwd_f16(const ConvBwdArgs& p, hipStream_t st);
+
+static hipError_t launch_conv_bwd(const ConvBwdArgs& p, Act act, hipStream_t st) {
+  switch (act) {
+    case Act::F32: return launch_conv_bwd_f32(p, st);
+    case Act::BF16: return launch_conv_bwd_bf16(p, st);
+    case Act::F16: return launch_conv_bwd_f16(p, st);
+  }
+  return hipErrorInvalidValue;
+}
 hipError_t launch_fwd2_f32(const Fwd2Args& p, int ds, bool regen, hipStream_t st);
 hipError_t launch_fwd2_bf16(const Fwd2Args& p, int ds, bool regen, hipStream_t st);
 hipError_t launch_fwd2_f16(const Fwd2Args& p, int ds, bool regen, hipStream_t st);
@@ -256,12 +269,9 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   const int64_t waves_b = pl->nG * d->batch * (bwd_threads(d->d_state, pl->Lb) / 64);
   choose_segments_fwd(d->segments, waves_f, fwd_waves_per_simd(d->d_state, pl->esize), d->seqlen, &pl->Sf,
                       &pl->segf_steps);
-  if (fused) {   // the conv backward of a segment's tail needs the next segment's head
-    pl->Sb = 1;
-    pl->segb_tiles = pl->nCb;
-  } else {
+  {
     const int64_t resident =
-        1024 * static_cast<int64_t>(mscan::bwd_waves_per_simd(static_cast<int>(d->d_state), pl->Lb, false));
+        1024 * static_cast<int64_t>(mscan::bwd_waves_per_simd(static_cast<int>(d->d_state), pl->Lb, fused));
     choose_segments_bwd(d->segments, waves_b, resident, pl->nCb, &pl->Sb, &pl->segb_tiles);
   }
   // a launch holds at most 2^32 - 1 threads: the forward and backward (all
@@ -294,7 +304,7 @@ int check_ptr(const char* fn, const char* name, const void* p, bool need, int al
     if (rc_ != MAMBA_OK) return rc_;  \
   } while (0)
 
-int64_t param_width(const Plan& pl) { return pl.Ds + 1 + (pl.K > 0 ? pl.K + 1 : 0); }
+int64_t param_width(const Plan& pl) { return pl.Ds + 1; }
 
 size_t bc_part_bytes(const Plan& pl) {
   return static_cast<size_t>(pl.nG) * pl.B * pl.T * 2 * pl.Ds * sizeof(float);
@@ -304,11 +314,18 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace layouts.  Forward: [bc | seg_h | seg_sd], the last two when
 // segmented (nothing for the short-sequence step kernel).  Backward:
-// [part_bc | part_par | seg_q | seg_sd | bc | sub], seg_q and seg_sd when
-// segmented, bc and sub when the checkpoints are regenerated.
+// [part_bc | part_par | seg_q | seg_sd | bc | sub | du | part_conv], seg_q
+// and seg_sd when segmented, bc and sub when the checkpoints are
+// regenerated, du and part_conv for the fused entry.
 size_t seg_state_bytes(const Plan& pl, int S) { return align256(sizeof(float) * pl.B * S * pl.Di * pl.Ds); }
 size_t seg_sum_bytes(const Plan& pl, int S) { return align256(sizeof(float) * pl.B * S * pl.Di); }
 size_t par_part_bytes(const Plan& pl) { return align256(sizeof(float) * pl.Sb * pl.B * pl.Di * param_width(pl)); }
+// fused entry: d_u (f32) from the scan backward, and the conv adjoint's
+// weight / bias partials per (batch row, conv tile)
+size_t du_bytes(const Plan& pl) { return pl.K > 0 ? align256(sizeof(float) * pl.B * pl.T * pl.Di) : 0; }
+size_t conv_part_bytes(const Plan& pl) {
+  return pl.K > 0 ? align256(sizeof(float) * pl.B * mscan::conv_bwd_tiles(pl.T) * pl.Di * (pl.K + 1)) : 0;
+}
 size_t bc_f32_bytes(const Plan& pl) { return align256(sizeof(float) * pl.B * pl.T * 2 * pl.Ds); }
 size_t sub_ckpt_bytes(const Plan& pl) { return align256(sizeof(float) * pl.B * ((pl.T + 15) / 16) * pl.Ds * pl.Di); }
 
@@ -320,7 +337,7 @@ size_t workspace_need_fwd(const Plan& pl) {
 size_t workspace_need_bwd(const Plan& pl) {
   return align256(bc_part_bytes(pl)) + par_part_bytes(pl) +
          (pl.Sb > 1 ? seg_state_bytes(pl, pl.Sb) + seg_sum_bytes(pl, pl.Sb) : 0) +
-         (pl.regen() ? bc_f32_bytes(pl) + sub_ckpt_bytes(pl) : 0);
+         (pl.regen() ? bc_f32_bytes(pl) + sub_ckpt_bytes(pl) : 0) + du_bytes(pl) + conv_part_bytes(pl);
 }
 
 size_t workspace_need(const Plan& pl) {
@@ -522,6 +539,9 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   const int PW = static_cast<int>(param_width(pl));
   hipStream_t st = static_cast<hipStream_t>(stream);
 
+  char* after_regen = after_seg + (pl.regen() ? bc_f32_bytes(pl) + sub_ckpt_bytes(pl) : 0);
+  float* du_buf = reinterpret_cast<float*>(after_regen);                     // fused: d_u, f32
+  float* part_conv = reinterpret_cast<float*>(after_regen + du_bytes(pl));  // fused: conv partials
   const float* ckpt_b = ckpt;   // checkpoints the backward kernel walks, every Lb steps
   if (pl.regen()) {
     // states entering every 16th step, regenerated from the caller's
@@ -592,8 +612,8 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   a.conv_state0 = conv_state0;
   a.ckpt = ckpt_b;
   a.dout = dout;
-  a.d_u_extra = d_u_extra;
   a.d_x = d_x;
+  a.du_out = du_buf;
   a.d_delta_raw = d_delta_raw;
   a.d_z = d_z;
   a.part_bc = part_bc;
@@ -615,6 +635,23 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   }
   hipError_t err = mscan::launch_bwd(a, pl.act, static_cast<int>(pl.Ds), pl.Lb, st);
   if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("backward launch: ") + hipGetErrorString(err));
+  if (pl.K > 0) {   // the conv + SiLU adjoint over the d_u just written
+    mscan::ConvBwdArgs cv{};
+    cv.x = x;
+    cv.conv_w = conv_w;
+    cv.conv_b = conv_b;
+    cv.conv_state0 = conv_state0;
+    cv.du = du_buf;
+    cv.d_u_extra = d_u_extra;
+    cv.d_x = d_x;
+    cv.part = part_conv;
+    cv.B = pl.B;
+    cv.T = pl.T;
+    cv.Di = pl.Di;
+    cv.K = pl.K;
+    err = mscan::launch_conv_bwd(cv, pl.act, st);
+    if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("conv backward launch: ") + hipGetErrorString(err));
+  }
 
   mscan::ReduceArgs r{};
   r.part_bc = part_bc;
@@ -632,6 +669,8 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   r.X = pl.X;
   r.nG = pl.nG;
   r.par_rows = static_cast<int64_t>(pl.Sb) * pl.B;
+  r.part_conv = part_conv;
+  r.conv_rows = pl.B * mscan::conv_bwd_tiles(pl.T);
   r.K = pl.K;
   r.PW = PW;
   err = mscan::launch_reduce(r, st);

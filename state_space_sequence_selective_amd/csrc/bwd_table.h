@@ -14,7 +14,7 @@
 #define MSCAN_BWD_CONFIGS(X)                                     \
   X(4, 16, 1, 4, 4, 3, 4, 2) X(4, 32, 1, 4, 1, 2, 1, 2)          \
   X(8, 16, 2, 4, 4, 2, 4, 2) X(8, 32, 1, 8, 4, 2, 4, 2)          \
-  X(16, 16, 2, 8, 1, 3, 4, 2) X(16, 32, 1, 8, 4, 2, 4, 2)        \
+  X(16, 16, 2, 8, 1, 3, 1, 3) X(16, 32, 1, 8, 4, 2, 4, 2)        \
   X(32, 16, 2, 8, 4, 2, 4, 2) X(64, 16, 4, 4, 4, 2, 4, 2)
 
 namespace mscan {

@@ -30,8 +30,9 @@
 //               same way, and
 //               leaves per-(t, channel) partials of sum_n dh B and
 //               sum_n dh A dA h_{t-1} in LDS; the epilogue threads add the
-//               partials of all groups and write d_u (or, fused, push d_u
-//               through SiLU and the conv) and d_delta_raw.
+//               partials of all groups and write d_u (fused: as f32 to
+//               du_out, for the conv adjoint pass in scan_conv.h) and
+//               d_delta_raw.
 // Past the end of the sequence the staged values are zero, which makes the
 // extra steps of a short last tile identities, so the step loops need no
 // bounds tests.  d_B / d_C per channel group and d_a_log / d_D / conv grads
@@ -43,8 +44,10 @@
 // carry the later segments hand it: the pairs (Q, sum delta) of segments
 // S-1 .. s+1 from scan_bwd_carry_kernel, folded as
 //   carry <- exp(A * sum delta) carry + Q.
-// The fused entry runs one segment (the conv backward of a segment's last
-// K-1 steps needs the next segment's first ones).
+// The fused entry recomputes u = silu(conv(x)) in the stage (the conv halo
+// of a tile is read from x, or the incoming conv state before step 0) and
+// leaves the conv adjoint, whose d_x crosses tile and segment borders, to a
+// pass of its own over d_u.
 #pragma once
 #include "bwd_table.h"
 #include "scan_carry.h"
@@ -138,7 +141,7 @@ scan_bwd_kernel(const BwdArgs p) {
   // next sub-tile's producers then need not wait for this sub-tile's
   // epilogue (one barrier per sub-tile instead of two).
   constexpr int LDS_FIXED = (XR + 4 * TR) * RB + L * CPW * 16 + (FUSED ? (L + KMAX - 1) * CPW * 4 : 4) +
-                            L * 2 * DS * 4 + G * CPW * (NO + 1) * 4 + (SUB + KMAX) * CPW * 4;
+                            L * 2 * DS * 4 + G * CPW * (NO + 1) * 4;
   constexpr int SPS = SUB * CPW + group_pad<CPW>(SUB * CPW);
   constexpr int PART = 2 * G * SPS * 4;
   // double-buffer when LDS still allows the workgroups per CU that WPE waves
@@ -157,11 +160,10 @@ scan_bwd_kernel(const BwdArgs p) {
   // bank conflicts
   __shared__ float2 s_part[NBUF][G][SPS];   // per-group (sum_n dh B, sum_n dh A dA h_{t-1})
   __shared__ float s_red[G][CPW * (NO + 1)];
-  __shared__ float s_dp[SUB + KMAX][CPW];
   // the compiler checks only the static arrays; with the dynamic raw tile a
   // launch over the limit fails at dispatch
   static_assert(bwd_raw_bytes<A, L, FUSED, CPW>() + sizeof(s_st) + sizeof(s_x) + sizeof(s_bc) + sizeof(s_part) +
-                        sizeof(s_red) + sizeof(s_dp) <= kLdsBytes,
+                        sizeof(s_red) <= kLdsBytes,
                 "workgroup LDS (static + dynamic raw tile) exceeds what gfx950 allows");
 
   const int tid = threadIdx.x;
@@ -171,7 +173,7 @@ scan_bwd_kernel(const BwdArgs p) {
   constexpr int NW = (NT + 63) / 64;
   const int64_t ngrp = (p.Di + CPW - 1) / CPW;
   const int64_t nwg = ngrp * p.B;
-  const int64_t seg = FUSED ? 0 : blockIdx.x / nwg;
+  const int64_t seg = blockIdx.x / nwg;
   const int64_t wg = xcd_group_map<line_sharing_groups<ES, CPW>()>(blockIdx.x % nwg, nwg);
   const int64_t b = wg / ngrp;
   const int64_t cg = wg % ngrp;
@@ -196,7 +198,7 @@ scan_bwd_kernel(const BwdArgs p) {
     an[s] = on ? -expf(p.a_log[i * DS + n]) : 0.0f;
     a2[s] = an[s] * kLog2e;
     float cv = 0.0f;
-    if (!FUSED && on) {
+    if (on) {
       for (int64_t q = p.S - 1; q > seg; --q) {   // carry handed back by the later segments
         const int64_t r = b * p.S + q;
         cv = fmaf(exp2_fast(a2[s] * p.seg_sd[r * Di + i]), cv, p.seg_q[(r * Di + i) * DS + n]);
@@ -211,12 +213,7 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) cw[k] = (FUSED && on && k < K) ? p.conv_w[i * K + k] : 0.0f;
   if (FUSED) cb = (on && p.conv_b) ? p.conv_b[i] : 0.0f;
-  float acc_dD = 0.0f, acc_cb = 0.0f;
-  float acc_cw[KMAX];
-#pragma unroll
-  for (int k = 0; k < KMAX; ++k) acc_cw[k] = 0.0f;
-  if (FUSED)
-    for (int j = tid; j < (SUB + KMAX) * CPW; j += NT) (&s_dp[0][0])[j] = 0.0f;
+  float acc_dD = 0.0f;
 
   // ---- prefetch of one tile: raw activations to LDS (async), B/C rows and
   // the checkpoint to registers (B/C as raw bits, converted in the stage, so
@@ -252,8 +249,7 @@ scan_bwd_kernel(const BwdArgs p) {
   for (int64_t kt = ke - 1; kt >= kb; --kt) {
     const int64_t t0 = kt * L;
     const int len = static_cast<int>(T - t0 < L ? T - t0 : L);
-    float e_sig[NIT], e_dsp[NIT];
-    uint32_t e_due[NIT];
+    float e_sig[NIT];
     float h[SPL], h_in[SPL];   // h_in: the state entering the tile
 
     // ---------------------------------------------------------------- stage
@@ -284,8 +280,7 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int k = 0; k < NIT; ++k) {
       const int tt = g + G * k;
-      float dl = 0.0f, u = 0.0f, sig = 0.0f, dy = 0.0f, dsp = 0.0f;
-      uint32_t due = 0;   // raw bits of d_u_extra (0 is +0.0 in every dtype)
+      float dl = 0.0f, u = 0.0f, sig = 0.0f, dy = 0.0f;
       if (tt < len && on) {
         const int64_t e = (row0 + t0 + tt) * Di + i;
         const float dr = raw_ld<A>(raw_dr, tt * CPW + c);
@@ -296,10 +291,7 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
           for (int k2 = 0; k2 < KMAX; ++k2)
             if (k2 < K) pre = fmaf(cw[k2], s_x[tt + (KMAX - 1) - (K - 1) + k2][c], pre);
-          const float sp = sigmoid(pre);
-          u = pre * sp;
-          dsp = sp * (1.0f + pre * (1.0f - sp));
-          if (p.d_u_extra) due = io::ldraw(p.d_u_extra, e);   // converted in the epilogue
+          u = pre * sigmoid(pre);
         } else {
           u = raw_ld<A>(raw_x, tt * CPW + c);
         }
@@ -316,8 +308,6 @@ scan_bwd_kernel(const BwdArgs p) {
       }
       s_st[tt][c] = make_float4(dl, dl * u, dy, u);
       e_sig[k] = sig;
-      e_dsp[k] = dsp;
-      e_due[k] = due;
     }
     __syncthreads();
     if (kt > kb) prefetch(kt - 1);
@@ -442,7 +432,6 @@ scan_bwd_kernel(const BwdArgs p) {
       const int tt = sb * SUB + q;
       const bool live = mine && tt < len && on;
       const int64_t e = (row0 + t0 + tt) * Di + i;
-      float dp = 0.0f;
       if (live) {
         const float4 st = s_st[tt][c];   // delta, delta*u, dy, u
         float su = 0.0f, sd = 0.0f;
@@ -452,39 +441,12 @@ scan_bwd_kernel(const BwdArgs p) {
           su += pv.x;
           sd += pv.y;
         }
-        float du = fmaf(st.x, su, Dv * st.z);
+        const float du = fmaf(st.x, su, Dv * st.z);
         const float ddl = fmaf(st.w, su, sd);
         io::st(p.d_delta_raw, e, ddl * e_sig[kk]);
         acc_dD = fmaf(st.z, st.w, acc_dD);
-        if (FUSED) {
-          du += io::cvt(e_due[kk]);
-          dp = du * e_dsp[kk];
-          acc_cb += dp;
-#pragma unroll
-          for (int k2 = 0; k2 < KMAX; ++k2)
-            if (k2 < K) acc_cw[k2] = fmaf(dp, s_x[tt + (KMAX - 1) - (K - 1) + k2][c], acc_cw[k2]);
-        } else {
-          io::st(p.d_x, e, du);
-        }
-      }
-      if (FUSED) {
-        // d_x[s] = sum_k w_k dp[s + K-1-k]; rows >= SUB of s_dp hold the
-        // dp of the K-1 steps after this sub-tile (zero past the end)
-        if (mine) s_dp[q][c] = dp;
-        lds_barrier();
-        if (live) {
-          float gx = 0.0f;
-#pragma unroll
-          for (int k2 = 0; k2 < KMAX; ++k2)
-            if (k2 < K) gx = fmaf(cw[k2], s_dp[q + K - 1 - k2][c], gx);
-          io::st(p.d_x, e, gx);
-        }
-        lds_barrier();
-        // the K-1 steps after the next sub-tile: this sub-tile's first steps,
-        // then (when SUB < K-1) older entries; descending keeps reads ahead
-        // of writes
-        if (mine && q == 0)
-          for (int j = K - 2; j >= 0; --j) s_dp[SUB + j][c] = s_dp[j][c];
+        if (FUSED) p.du_out[e] = du;   // through SiLU and the conv in scan_conv.h
+        else io::st(p.d_x, e, du);
       }
       if (NBUF == 1) lds_barrier();
     }
@@ -497,22 +459,14 @@ scan_bwd_kernel(const BwdArgs p) {
 #pragma unroll
     for (int s = 0; s < SPL; ++s) p.part_par[pb + g * SPL + s] = an[s] * dacc[s];
   }
-  const int nq = FUSED ? K + 2 : 1;
-  for (int qd = 0; qd < nq; ++qd) {
-    float v = qd == 0 ? acc_dD : (qd == 1 ? acc_cb : 0.0f);
-#pragma unroll
-    for (int k2 = 0; k2 < KMAX; ++k2)
-      if (qd == k2 + 2) v = acc_cw[k2];
-    s_part[0][g][c].x = v;
-    __syncthreads();
-    if (g == 0 && on) {
-      float tot = 0.0f;
-      for (int w = 0; w < G; ++w) tot += s_part[0][w][c].x;
-      // layout within PW: [Ds a_log | 1 D | K conv_w | 1 conv_b]
-      const int slot = qd == 0 ? DS : (qd == 1 ? DS + 1 + K : DS + 1 + (qd - 2));
-      p.part_par[pb + slot] = tot;
-    }
-    __syncthreads();
+  // d_D: the state groups' partial sums of this thread's items, added in
+  // group order (layout within PW: [Ds a_log | 1 D])
+  s_part[0][g][c].x = acc_dD;
+  __syncthreads();
+  if (g == 0 && on) {
+    float tot = 0.0f;
+    for (int w = 0; w < G; ++w) tot += s_part[0][w][c].x;
+    p.part_par[pb + DS] = tot;
   }
 }
 
@@ -522,7 +476,7 @@ static hipError_t launch_bwd_t(const BwdArgs& p, hipStream_t st) {
   constexpr int G = DS / SPL;
   constexpr int CPW = kBwdCpw;
   const int64_t ng = (p.Di + CPW - 1) / CPW;
-  dim3 grid(static_cast<unsigned>(ng * p.B * (p.K > 0 ? 1 : p.S)));
+  dim3 grid(static_cast<unsigned>(ng * p.B * p.S));
   constexpr unsigned raw_fused = bwd_raw_bytes<A, L, true, CPW>();
   constexpr unsigned raw_plain = bwd_raw_bytes<A, L, false, CPW>();
   if (p.K > 0)

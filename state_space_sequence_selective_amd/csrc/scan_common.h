@@ -284,12 +284,12 @@ struct BwdArgs {
   const float* conv_state0;
   const float* ckpt;        // [B,nC,Ds,Di]
   const void* dout;
-  const void* d_u_extra;    // [B,T,Di] or null (fused only)
-  void* d_x;                // d_u (scan) or d_x (fused) [B,T,Di]
+  void* d_x;                // d_u [B,T,Di] (scan entry)
+  float* du_out;            // d_u [B,T,Di] f32 (fused entry: the conv adjoint pass reads it)
   void* d_delta_raw;        // [B,T,Di]
   void* d_z;                // [B,T,Di] (gate only)
   float* part_bc;           // [nG, B*T, 2*Ds]: per channel-group sums of d_B | d_C
-  float* part_par;          // [S, B, Di, PW]: per segment and batch row d_a_log | d_D | d_conv_w | d_conv_b
+  float* part_par;          // [S, B, Di, PW]: per segment and batch row d_a_log | d_D
   // segmented schedule: segment s covers tiles [s * seg_tiles, ...) of L steps
   const float* seg_q;       // [B,S,Di,Ds] carry each segment hands to earlier steps, from a zero start
   const float* seg_sd;      // [B,S,Di] sum of delta over each segment
@@ -297,8 +297,8 @@ struct BwdArgs {
   int64_t seg_tiles;        // tiles per segment
   int K;
   int L;
-  int PW;                   // Ds + 1 + K + 1 (conv terms only when K > 0)
-  int S;                    // segments (1 for the fused entry)
+  int PW;                   // Ds + 1
+  int S;                    // segments
 };
 
 // aggregate pass of the segmented backward
@@ -317,7 +317,8 @@ struct CarryArgs {
 
 struct ReduceArgs {
   const float* part_bc;
-  const float* part_par;
+  const float* part_par;    // [par_rows, Di, PW]: d_a_log | d_D
+  const float* part_conv;   // [conv_rows, Di, K + 1]: d_conv_w | d_conv_b (K > 0)
   float* d_xdbl;            // [B,T,X], B/C columns +=
   float* d_a_log;           // [Di,Ds] +=
   float* d_D;               // [Di] +=
@@ -325,8 +326,9 @@ struct ReduceArgs {
   float* d_conv_b;          // [Di] += or null
   int64_t B, T, Di, Ds, R, X, nG;
   int64_t par_rows;         // rows of part_par summed per element: segments * B
+  int64_t conv_rows;        // rows of part_conv: B * conv tiles
   int K;
-  int PW;
+  int PW;                   // Ds + 1
 };
 
 }  // namespace mscan

@@ -265,9 +265,11 @@ scan_fwd2_kernel(const Fwd2Args p) {
     float u;
     if constexpr (FUSED) {
       const float xn = io::cvt(raw_act(buf, 0, k));
+      // padded taps are skipped by a select, not multiplied by zero: a
+      // non-finite input they would see must not reach the sum
       float pre = cb;
 #pragma unroll
-      for (int k2 = 0; k2 < KMAX - 1; ++k2) pre = fmaf(cw[k2], xw[k2], pre);
+      for (int k2 = 0; k2 < KMAX - 1; ++k2) pre = k2 >= KMAX - K ? fmaf(cw[k2], xw[k2], pre) : pre;
       pre = fmaf(cw[KMAX - 1], xn, pre);
       // slide the window: x_{t-(KMAX-2)..t} for the next step
 #pragma unroll

@@ -1,8 +1,8 @@
 // Fixed-order reduction of the backward's per-group / per-(segment, batch
-// row) partials into the caller's accumulated gradients (d_xdbl B/C
-// columns, d_a_log, d_D, d_conv_w, d_conv_b).  No atomics: every output
-// element is summed by one thread in ascending group / row order, so
-// repeated runs give identical bits.
+// row) / per-(batch row, conv tile) partials into the caller's accumulated
+// gradients (d_xdbl B/C columns, d_a_log, d_D, d_conv_w, d_conv_b).  No
+// atomics: every output element is summed by one thread in ascending
+// group / row order, so repeated runs give identical bits.
 #include "scan_common.h"
 
 namespace mscan {
@@ -51,22 +51,24 @@ __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
     return;
   }
   const int64_t jp = j - nbc4;
-  if (jp >= p.Di * p.PW) return;
-  const int64_t i = jp / p.PW, slot = jp % p.PW;
-  const float acc = ordered_sum(p.part_par + i * p.PW + slot, p.par_rows, p.Di * p.PW);
-  if (slot < p.Ds) {
-    p.d_a_log[i * p.Ds + slot] += acc;
-  } else if (slot == p.Ds) {
-    p.d_D[i] += acc;
-  } else if (slot < p.Ds + 1 + p.K) {
-    p.d_conv_w[i * p.K + (slot - p.Ds - 1)] += acc;
-  } else {
-    p.d_conv_b[i] += acc;
+  if (jp < p.Di * p.PW) {
+    const int64_t i = jp / p.PW, slot = jp % p.PW;
+    const float acc = ordered_sum(p.part_par + i * p.PW + slot, p.par_rows, p.Di * p.PW);
+    if (slot < p.Ds) p.d_a_log[i * p.Ds + slot] += acc;
+    else p.d_D[i] += acc;
+    return;
   }
+  const int64_t jc = jp - p.Di * p.PW;   // conv weight and bias partials
+  const int64_t CW = p.K + 1;
+  if (p.K == 0 || jc >= p.Di * CW) return;
+  const int64_t i = jc / CW, slot = jc % CW;
+  const float acc = ordered_sum(p.part_conv + i * CW + slot, p.conv_rows, p.Di * CW);
+  if (slot < p.K) p.d_conv_w[i * p.K + slot] += acc;
+  else p.d_conv_b[i] += acc;
 }
 
 hipError_t launch_reduce(const ReduceArgs& p, hipStream_t st) {
-  const int64_t n = p.B * p.T * 2 * p.Ds / 4 + p.Di * p.PW;
+  const int64_t n = p.B * p.T * 2 * p.Ds / 4 + p.Di * p.PW + (p.K > 0 ? p.Di * (p.K + 1) : 0);
   dim3 grid(static_cast<unsigned>((n + 255) / 256));
   hipLaunchKernelGGL(mscan_reduce_kernel, grid, dim3(256), 0, st, p);
   return hipGetLastError();

@@ -56,9 +56,13 @@ def test_sizes(pkg):
     # then per-row param partials
     bc = 2 * 2 * 100 * 32 * 4
     assert pkg.workspace_bytes(d) == ((bc + 255) // 256) * 256 + 2 * 64 * 17 * 4
+    # fused: the same, plus d_u (f32) for the conv adjoint pass and its weight
+    # / bias partials per (batch row, 64-step tile)
     dc = _dims(pkg, d_conv=4, d_inner=128)
+    al = lambda x: (x + 255) // 256 * 256
     bc = 4 * 2 * 100 * 32 * 4
-    assert pkg.workspace_bytes(dc) == ((bc + 255) // 256) * 256 + 2 * 128 * 22 * 4
+    assert pkg.workspace_bytes(dc) == (al(bc) + al(2 * 128 * 17 * 4) + al(2 * 100 * 128 * 4)
+                                       + al(2 * 2 * 128 * 5 * 4))
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -112,13 +116,12 @@ def test_segmented_workspace_layout(pkg):
     fwd = al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
     bwd = al(2 * 1 * 64 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
     assert pkg.workspace_bytes(d) == max(fwd, bwd)
-    # the fused backward always runs one segment; its forward may split
+    # the fused backward segments like the scan one and adds d_u (f32) and
+    # the conv partials per (batch row, 64-step tile)
     d = _dims(pkg, batch=1, seqlen=1024, chunk=16, segments=4, d_conv=4)
-    fwd = al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
-    bwd_fused = al(2 * 1 * 1024 * 32 * 4) + al(1 * 64 * 22 * 4)
-    bwd_scan = (al(2 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4)
-                + al(1 * 4 * 64 * 4))
-    assert pkg.workspace_bytes(d) == max(fwd, bwd_fused, bwd_scan)
+    bwd_fused = (al(2 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4)
+                 + al(1 * 4 * 64 * 4) + al(1 * 1024 * 64 * 4) + al(1 * 16 * 64 * 5 * 4))
+    assert pkg.workspace_bytes(d) == bwd_fused
 
 
 def _raw(pkg):
