@@ -232,7 +232,7 @@ int blas_handle(const char* fn, hipStream_t st, rocblas_handle* out) {
 struct Side {
   hipStream_t s = nullptr;
   rocblas_handle h = nullptr;
-  hipEvent_t ev[6] = {};   // five forks and the join of one backward call
+  hipEvent_t ev[5] = {};   // four forks and the join of one backward call
 };
 Side g_side[64];
 
@@ -534,10 +534,11 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     LAYER_TRY(run(fn, "cast d_resid_out", o, act, st));
     LAYER_TRY(gemm(fn, "out_proj dgrad", h, false, false, N, Di, dm, dy, at, dm, w->w_out, at, Di, 0.0f, d_gated, d_gated,
                    at, Di));
-    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[0]));
-    LAYER_TRY(gemm(fn, "out_proj wgrad", hw, true, false, dm, Di, N, dy, at, dm, gated, at, Di, 1.0f, g->w_out, g->w_out,
-                   f32, Di));
-    // the core; it adds into the B/C columns of d_xdbl, which start at zero
+    // the core; it adds into the B/C columns of d_xdbl, which start at zero.
+    // No product runs beside it: its kernels are sized to fill every SIMD in
+    // one round, and workgroups that a concurrent product keeps off some
+    // compute units spill into a second round (a third slower at 130M
+    // widths).
     o = Op{OpKind::Zero};
     o.f3 = d_xdbl;
     o.n = N * X;
@@ -545,16 +546,18 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     LAYER_TRY(core_call(fn, "scan backward",
                         mamba_scan_bwd(&pl.core, u, dr, w->a_log, xdbl, w->D, z, y, ckpt, d_gated, d_u, d_dr, d_z,
                                        d_xdbl, g->a_log, g->D, W + pl.w_core_b, pl.core_ws, stream)));
-    // d_z is final here: its in_proj weight product starts now rather than
-    // after the conv adjoint
+    // the out_proj weight product, and d_z being final, its in_proj one,
+    // start beside the rest of the adjoint
     float* gw_in_z = g->w_in + Di * dm;
-    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[1]));
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[0]));
+    LAYER_TRY(gemm(fn, "out_proj wgrad", hw, true, false, dm, Di, N, dy, at, dm, gated, at, Di, 1.0f, g->w_out, g->w_out,
+                   f32, Di));
     LAYER_TRY(gemm(fn, "in_proj wgrad z", hw, true, false, Di, dm, N, d_z, at, Di, xn, at, dm, 1.0f, gw_in_z, gw_in_z, f32,
                    dm));
     // dt_proj adjoint: the dt columns of d_xdbl, W_dt and b_dt
     LAYER_TRY(gemm(fn, "dt_proj dgrad", h, false, false, N, R, Di, d_dr, at, Di, w->w_dt, at, R, 0.0f, d_xdbl, d_xdbl,
                    f32, X));
-    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[2]));
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[1]));
     LAYER_TRY(wgrad(fn, "dt_proj wgrad", hw, sd->s, act, Di, R, N, d_dr, at, Di, xdbl, at, X, pl.es, g->w_dt, pwg,
                     pl.P_dt));
     o = Op{OpKind::ColPart};
@@ -579,7 +582,7 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     LAYER_TRY(run(fn, "cast d_xdbl", o, act, st));
     LAYER_TRY(gemm(fn, "x_proj dgrad", h, false, false, N, Di, X, d_xdbl_a, at, X, w->w_x, at, Di, 0.0f, d_uex, d_uex, f32,
                    Di));
-    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[3]));
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[2]));
     LAYER_TRY(wgrad(fn, "x_proj wgrad", hw, sd->s, act, X, Di, N, d_xdbl_a, at, X, u, at, Di, pl.es, g->w_x, pwg,
                     pl.P_x));
     // conv + SiLU adjoint: d_x and the weight / bias partials in one pass
@@ -598,7 +601,7 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     o.n = N * Di;
     LAYER_TRY(run(fn, "conv adjoint", o, act, st));
     // d_x is final here: its in_proj weight product starts beside the rest
-    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[4]));
+    LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[3]));
     LAYER_TRY(gemm(fn, "in_proj wgrad x", hw, true, false, Di, dm, N, d_x, at, Di, xn, at, dm, 1.0f, g->w_in, g->w_in, f32,
                    dm));
     o = Op{OpKind::ColSum};
@@ -646,7 +649,7 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     return MAMBA_OK;
   };
   const int rc = body();
-  const int rj = fork_wait(fn, sd->s, st, sd->ev[5]);   // join: the caller's stream covers every product
+  const int rj = fork_wait(fn, sd->s, st, sd->ev[4]);   // join: the caller's stream covers every product
   if (rc != MAMBA_OK) return rc;
   if (rj != MAMBA_OK) return rj;
   mscan::set_last_error("");
