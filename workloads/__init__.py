@@ -193,3 +193,77 @@ def make_layer_inputs(w: LayerWorkload, seed: int = 0) -> dict:
     out["w_out"] = round_to(w.act, normal((dm, Di), Di ** -0.5))
     out["d_resid_out"] = normal((B, T, dm))
     return out
+
+
+# ------------------------------------------------- Mamba-3 SISO state-space core
+
+
+@dataclass(frozen=True)
+class M3Workload:
+    """One Mamba-3 SISO layer core: x split into `heads` heads of `headdim`
+    channels, B/C in `groups` groups of `d_state`, `n_angles` rotation
+    angles per step."""
+    name: str
+    batch: int
+    seqlen: int
+    heads: int
+    headdim: int
+    d_state: int
+    groups: int
+    n_angles: int
+    act: str
+    a_floor: float = 1e-4
+
+    @property
+    def d_inner(self) -> int:
+        return self.heads * self.headdim
+
+    def with_(self, **kw) -> "M3Workload":
+        return replace(self, **kw)
+
+
+M3_CONFIGS = {
+    # small: three 64-step chunks and a ragged tail, two B/C groups
+    "m3_small_bf16": M3Workload("m3_small_bf16", 2, 200, 4, 64, 64, 2, 16, "bf16"),
+    # d_model 768 -> d_inner 1536 = 24 heads of 64, d_state 128, half of the
+    # state dims turned (32 angles), B=4, T=2048
+    "m3_siso_bf16": M3Workload("m3_siso_bf16", 4, 2048, 24, 64, 128, 1, 32, "bf16"),
+}
+
+
+def make_m3_inputs(w: M3Workload, seed: int = 0) -> dict:
+    """Draw one Mamba-3 SISO core's inputs and its output gradient.
+
+    Readings (the pages give names and shapes only): x, the normalised B and
+    C, trap_raw, dd_a_raw and dy N(0, 1); dd_dt_raw N(0, 0.5^2) around a dt
+    bias that is the inverse softplus of dt = exp(U(log 1e-3, log 1e-1)) per
+    head; angles_raw N(0, 1); B and C biases N(0, 0.1^2); D = 1.  The
+    activations (x, B, C, dy) come back rounded to the activation dtype,
+    everything else float32.
+
+    Keys: x [B,T,heads*headdim], b_in / c_in [B,T,groups,d_state],
+    dd_dt_raw / dd_a_raw / trap_raw [B,T,heads], angles_raw [B,T,n_angles],
+    b_bias / c_bias [heads,d_state], dt_bias / D [heads], dy.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, H, P, N, G, NA = w.batch, w.seqlen, w.heads, w.headdim, w.d_state, w.groups, w.n_angles
+
+    def normal(size, std=1.0):
+        a = rng.standard_normal(size, dtype=np.float32)
+        return a * np.float32(std) if std != 1.0 else a
+
+    out = {}
+    out["x"] = round_to(w.act, normal((B, T, H * P)))
+    out["b_in"] = round_to(w.act, normal((B, T, G, N)))
+    out["c_in"] = round_to(w.act, normal((B, T, G, N)))
+    out["dd_dt_raw"] = normal((B, T, H), 0.5)
+    out["dd_a_raw"] = normal((B, T, H))
+    out["trap_raw"] = normal((B, T, H))
+    out["angles_raw"] = normal((B, T, NA))
+    out["b_bias"] = normal((H, N), 0.1)
+    out["c_bias"] = normal((H, N), 0.1)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), H))
+    out["dt_bias"] = (dt + np.log(-np.expm1(-dt))).astype(np.float32)
+    out["D"] = np.ones(H, dtype=np.float32)
+    out["dy"] = round_to(w.act, normal((B, T, H * P)))
+    return out
