@@ -1,4 +1,5 @@
-"""ctypes binding of libmamba_scan.so (include/mamba_scan.h, include/mamba_layer.h).
+"""ctypes binding of libmamba_scan.so (include/mamba_scan.h, include/mamba_layer.h,
+include/mamba3.h).
 
 Argument marshalling only: tensors are checked for device, dtype, layout and
 size, their device pointers are handed to the C entry points, and a non-zero
@@ -24,7 +25,8 @@ TORCH_DTYPES = {MAMBA_F32: torch.float32, MAMBA_BF16: torch.bfloat16, MAMBA_F16:
 EXPORTED = ("mamba_abi_version", "mamba_last_error", "mamba_ckpt_bytes", "mamba_workspace_bytes",
             "mamba_scan_fwd", "mamba_scan_bwd", "mamba_scan_bwd_static", "mamba_conv_scan_gate_fwd",
             "mamba_conv_scan_gate_bwd",
-            "mamba_layer_saved_bytes", "mamba_layer_workspace_bytes", "mamba_layer_fwd", "mamba_layer_bwd")
+            "mamba_layer_saved_bytes", "mamba_layer_workspace_bytes", "mamba_layer_fwd", "mamba_layer_bwd",
+            "mamba3_states_bytes", "mamba3_workspace_bytes", "mamba3_siso_fwd", "mamba3_siso_bwd")
 
 # weights of one layer (mamba_layer_weights_t / mamba_layer_grads_t field order)
 LAYER_PARAMS = ("norm_w", "w_in", "conv_w", "conv_b", "w_x", "w_dt", "b_dt", "a_log", "D", "w_out")
@@ -108,6 +110,15 @@ def load():
     lib.mamba_layer_bwd.restype = ctypes.c_int
     lib.mamba_layer_bwd.argtypes = [LD, ctypes.POINTER(LayerWeights), P, P, ctypes.c_size_t, P, P,
                                     ctypes.POINTER(LayerGrads), P, ctypes.c_size_t, P]
+    M3 = ctypes.POINTER(M3Dims)
+    for name in ("mamba3_states_bytes", "mamba3_workspace_bytes"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [M3, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mamba3_siso_fwd.restype = ctypes.c_int
+    lib.mamba3_siso_fwd.argtypes = [M3] + [P] * 14 + [ctypes.c_size_t, P]
+    lib.mamba3_siso_bwd.restype = ctypes.c_int
+    lib.mamba3_siso_bwd.argtypes = [M3] + [P] * 25 + [ctypes.c_size_t, P]
     _lib = lib
     return lib
 
@@ -355,3 +366,82 @@ def layer_bwd(ld: LayerDims, weights: dict, resid_in, saved, d_resid_out, *, d_r
                                   sp, sn, _ptr(d_resid_out, "d_resid_out", torch.float32, rs, True),
                                   _ptr(d_resid_in, "d_resid_in", torch.float32, rs, True), ctypes.byref(g), wp, wn,
                                   _stream(stream)))
+
+
+# ------------------------------------------------------ Mamba-3 SISO core
+
+
+class M3Dims(ctypes.Structure):
+    """mamba3_dims_t."""
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("heads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("d_state", ctypes.c_int64), ("groups", ctypes.c_int64),
+                ("n_angles", ctypes.c_int64), ("chunk", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("a_floor", ctypes.c_float)]
+
+    @classmethod
+    def make(cls, batch, seqlen, heads, headdim, d_state, groups, n_angles, act="bf16", a_floor=1e-4, chunk=0):
+        code = ACT_CODES[act] if isinstance(act, str) else int(act)
+        return cls(batch, seqlen, heads, headdim, d_state, groups, n_angles, chunk, code, a_floor)
+
+    @property
+    def act_dtype(self) -> torch.dtype:
+        return TORCH_DTYPES[self.act]
+
+    @property
+    def n_chunks(self) -> int:
+        return -(-self.seqlen // 64)
+
+    def shapes(self) -> dict:
+        B, T, H, P, N, G, A = (self.batch, self.seqlen, self.heads, self.headdim, self.d_state, self.groups,
+                               self.n_angles)
+        return dict(x=(B, T, H * P), bc=(B, T, G, N), bth=(B, T, H), ang=(B, T, A), hn=(H, N), h=(H,),
+                    states=(B, H, self.n_chunks, P, N))
+
+
+def m3_states_bytes(d: M3Dims) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mamba3_states_bytes(ctypes.byref(d), ctypes.byref(out)))
+    return out.value
+
+
+def m3_workspace_bytes(d: M3Dims) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mamba3_workspace_bytes(ctypes.byref(d), ctypes.byref(out)))
+    return out.value
+
+
+def _m3_inputs(d: M3Dims, x, b_in, c_in, dd_dt_raw, dd_a_raw, trap_raw, angles_raw, b_bias, c_bias, dt_bias, D):
+    s, at, f = d.shapes(), d.act_dtype, torch.float32
+    return [_ptr(x, "x", at, s["x"], True), _ptr(b_in, "b_in", at, s["bc"], True),
+            _ptr(c_in, "c_in", at, s["bc"], True), _ptr(dd_dt_raw, "dd_dt_raw", f, s["bth"], True),
+            _ptr(dd_a_raw, "dd_a_raw", f, s["bth"], True), _ptr(trap_raw, "trap_raw", f, s["bth"], True),
+            _ptr(angles_raw, "angles_raw", f, s["ang"], d.n_angles > 0), _ptr(b_bias, "b_bias", f, s["hn"], True),
+            _ptr(c_bias, "c_bias", f, s["hn"], True), _ptr(dt_bias, "dt_bias", f, s["h"], True),
+            _ptr(D, "D", f, s["h"])]
+
+
+def m3_fwd(d: M3Dims, x, b_in, c_in, dd_dt_raw, dd_a_raw, trap_raw, angles_raw, b_bias, c_bias, dt_bias, D=None, *,
+           y, states, workspace, stream=None):
+    s = d.shapes()
+    args = [ctypes.byref(d)] + _m3_inputs(d, x, b_in, c_in, dd_dt_raw, dd_a_raw, trap_raw, angles_raw, b_bias,
+                                          c_bias, dt_bias, D)
+    args += [_ptr(y, "y", d.act_dtype, s["x"], True), _ptr(states, "states", torch.float32, s["states"], True),
+             *_workspace(workspace), _stream(stream)]
+    _check(load().mamba3_siso_fwd(*args))
+
+
+def m3_bwd(d: M3Dims, x, b_in, c_in, dd_dt_raw, dd_a_raw, trap_raw, angles_raw, b_bias, c_bias, dt_bias, D, states,
+           dy, *, d_x, d_b_in, d_c_in, d_dd_dt_raw, d_dd_a_raw, d_trap_raw, d_angles_raw, d_b_bias, d_c_bias,
+           d_dt_bias, d_D, workspace, stream=None):
+    s, at, f = d.shapes(), d.act_dtype, torch.float32
+    args = [ctypes.byref(d)] + _m3_inputs(d, x, b_in, c_in, dd_dt_raw, dd_a_raw, trap_raw, angles_raw, b_bias,
+                                          c_bias, dt_bias, D)
+    args += [_ptr(states, "states", f, s["states"], True), _ptr(dy, "dy", at, s["x"], True),
+             _ptr(d_x, "d_x", at, s["x"], True), _ptr(d_b_in, "d_b_in", at, s["bc"], True),
+             _ptr(d_c_in, "d_c_in", at, s["bc"], True), _ptr(d_dd_dt_raw, "d_dd_dt_raw", f, s["bth"], True),
+             _ptr(d_dd_a_raw, "d_dd_a_raw", f, s["bth"], True), _ptr(d_trap_raw, "d_trap_raw", f, s["bth"], True),
+             _ptr(d_angles_raw, "d_angles_raw", f, s["ang"], d.n_angles > 0),
+             _ptr(d_b_bias, "d_b_bias", f, s["hn"], True), _ptr(d_c_bias, "d_c_bias", f, s["hn"], True),
+             _ptr(d_dt_bias, "d_dt_bias", f, s["h"], True), _ptr(d_D, "d_D", f, s["h"], D is not None),
+             *_workspace(workspace), _stream(stream)]
+    _check(load().mamba3_siso_bwd(*args))

@@ -23,7 +23,7 @@ def pkg():
 def declared_functions():
     src = "\n".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mamba3?_\w+)\s*\(", src)))
 
 
 def test_header_declares_the_binding_entry_points(pkg):

@@ -1,0 +1,204 @@
+"""GPU parity of the Mamba-3 SISO core (include/mamba3.h) against the
+float64 oracle (oracle/mamba3.py), through the C ABI.
+
+Tolerances: f32 activations, every output within 1e-4 of the oracle,
+scaled by max(1, max|oracle|); 16-bit activations, every output (the f32
+gradients included) within 2e-2 of max|oracle|, because the kernels keep the
+turned B and C in the activation dtype between passes, as the page keeps its
+Q_rot and K_scaled typed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import mamba3 as m3o
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32, TOL_HALF = 1e-4, 2e-2
+KEYS = ("x", "b_in", "c_in", "dd_dt_raw", "dd_a_raw", "trap_raw", "angles_raw", "b_bias", "c_bias", "dt_bias", "D")
+
+
+@pytest.fixture(scope="module")
+def mscan():
+    import state_space_sequence_selective_amd as m
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.load()
+    return m
+
+
+def device(w, inp):
+    at = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.act]
+    out = {}
+    for k, v in inp.items():
+        if v is None:
+            continue
+        out[k] = torch.from_numpy(np.ascontiguousarray(v)).to("cuda", at if k in ("x", "b_in", "c_in", "dy") else
+                                                               torch.float32)
+    return out
+
+
+def err(gpu, ora, half):
+    g = gpu.detach().float().cpu().numpy().astype(np.float64)
+    o = np.asarray(ora, dtype=np.float64)
+    assert g.shape == o.shape, (g.shape, o.shape)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    d = np.abs(g - o).max() if g.size else 0.0
+    if half:
+        return d / max(np.abs(o).max() if o.size else 1.0, 1e-30)
+    return d / max(1.0, np.abs(o).max() if o.size else 1.0)
+
+
+def oracle_args(w, inp):
+    return dict(x=inp["x"], b_in=inp["b_in"], c_in=inp["c_in"], dd_dt_raw=inp["dd_dt_raw"],
+                dd_a_raw=inp["dd_a_raw"], trap_raw=inp["trap_raw"], angles_raw=inp["angles_raw"],
+                b_bias=inp["b_bias"], c_bias=inp["c_bias"], dt_bias=inp["dt_bias"],
+                D=inp["D"] if inp.get("D") is not None else np.zeros(w.heads), a_floor=w.a_floor,
+                heads=w.heads, headdim=w.headdim)
+
+
+def run(mscan, w, seed=0, D=True, inp=None, report=None):
+    inp = inp if inp is not None else workloads.make_m3_inputs(w, seed)
+    if not D:
+        inp = dict(inp, D=None)
+    dims = mscan.M3Dims.make(w.batch, w.seqlen, w.heads, w.headdim, w.d_state, w.groups, w.n_angles, w.act,
+                             w.a_floor)
+    core = mscan.Mamba3Core(dims)
+    dev = device(w, inp)
+    core.zero_grads()
+    core.forward(dev)
+    core.backward(dev, dev["dy"])
+    torch.cuda.synchronize()
+    args = oracle_args(w, inp)
+    y = m3o.forward(**args)
+    g = m3o.backward(inp["dy"], **args)
+    half = w.act != "f32"
+    tol = TOL_HALF if half else TOL_F32
+    rep = {"y": err(core.y, y, half)}
+    for k in KEYS:
+        if k == "D" and not D:
+            continue
+        if k == "angles_raw" and w.n_angles == 0:
+            continue
+        rep[k] = err(core.grads[k], g[k], half)
+    if report is not None:
+        report.update(rep)
+    bad = {k: v for k, v in rep.items() if not v <= tol}
+    assert not bad, "errors above %.0e: %s (all: %s)" % (tol, bad, {k: "%.1e" % v for k, v in rep.items()})
+    return core, rep
+
+
+def test_small_bf16(mscan):
+    run(mscan, workloads.M3_CONFIGS["m3_small_bf16"])
+
+
+@pytest.mark.parametrize("N,NA,G,H", [(32, 8, 1, 2), (64, 32, 2, 4), (64, 0, 1, 1)])
+def test_f32(mscan, N, NA, G, H):
+    w = workloads.M3Workload("m3_f32", 2, 150, H, 64, N, G, NA, "f32")
+    run(mscan, w, seed=N + NA)
+
+
+@pytest.mark.parametrize("N,NA,act", [(128, 32, "bf16"), (128, 64, "f16"), (32, 16, "bf16"), (128, 0, "f16")])
+def test_state_sizes(mscan, N, NA, act):
+    w = workloads.M3Workload("m3_n", 2, 137, 2, 64, N, 1, NA, act)
+    run(mscan, w, seed=N + NA + 1)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 128, 129])
+def test_ragged_lengths(mscan, T):
+    w = workloads.M3Workload("m3_t", 1, T, 2, 64, 32, 1, 4, "f32")
+    run(mscan, w, seed=T)
+
+
+def test_no_D(mscan):
+    w = workloads.M3Workload("m3_nod", 1, 90, 2, 64, 32, 2, 4, "f32")
+    run(mscan, w, D=False)
+
+
+def test_clamped_decay(mscan):
+    """a_floor above most softplus(dd_a_raw): the clamp's zero gradient."""
+    w = workloads.M3Workload("m3_floor", 1, 100, 2, 64, 32, 1, 4, "f32", a_floor=0.9)
+    run(mscan, w, seed=5)
+
+
+def test_param_grads_accumulate_and_repeat(mscan):
+    """Bitwise reproducible run to run; the parameter gradients double when
+    the backward runs twice without zeroing, the others are overwritten."""
+    w = workloads.M3_CONFIGS["m3_small_bf16"]
+    inp = workloads.make_m3_inputs(w, 3)
+    dims = mscan.M3Dims.make(w.batch, w.seqlen, w.heads, w.headdim, w.d_state, w.groups, w.n_angles, w.act,
+                             w.a_floor)
+    core = mscan.Mamba3Core(dims)
+    dev = device(w, inp)
+    core.zero_grads()
+    core.forward(dev)
+    core.backward(dev, dev["dy"])
+    torch.cuda.synchronize()
+    first = {k: v.clone() for k, v in core.grads.items()}
+    y0 = core.y.clone()
+    core.zero_grads()
+    core.forward(dev)
+    core.backward(dev, dev["dy"])
+    torch.cuda.synchronize()
+    assert torch.equal(core.y, y0)
+    for k, v in first.items():
+        assert torch.equal(core.grads[k], v), k
+    core.backward(dev, dev["dy"])
+    torch.cuda.synchronize()
+    for k, v in first.items():
+        ref = 2 * v if k in ("b_bias", "c_bias", "dt_bias", "D") else v
+        assert torch.equal(core.grads[k], ref), k
+
+
+def test_errors(mscan):
+    w = workloads.M3_CONFIGS["m3_small_bf16"]
+    bad = [dict(headdim=32), dict(d_state=16), dict(groups=3), dict(n_angles=40), dict(chunk=32)]
+    for kw in bad:
+        base = dict(batch=w.batch, seqlen=w.seqlen, heads=w.heads, headdim=64, d_state=w.d_state, groups=w.groups,
+                    n_angles=w.n_angles, act=w.act)
+        base.update(kw)
+        d = mscan.M3Dims.make(**base)
+        with pytest.raises(mscan.MambaScanError):
+            mscan.m3_workspace_bytes(d)
+    d = mscan.M3Dims.make(1, 64, 2, 64, 32, 1, 4, "f32")
+    core = mscan.Mamba3Core(d)
+    inp = device(workloads.M3Workload("e", 1, 64, 2, 64, 32, 1, 4, "f32"),
+                 workloads.make_m3_inputs(workloads.M3Workload("e", 1, 64, 2, 64, 32, 1, 4, "f32"), 0))
+    with pytest.raises(mscan.MambaScanError) as e:
+        mscan.m3_fwd(d, *core._inputs(inp), y=core.y, states=core.states, workspace=core.workspace[:1024])
+    assert e.value.status == 3
+
+
+def test_full_size_sampled_heads(mscan):
+    """The measured shape (B=4, T=2048, 24 heads of 64, d_state 128, 32
+    angles, bf16) as the bench launches it; the per-head outputs of three
+    heads of batch row 0 against the oracle run on those heads alone (they
+    share the single B/C group, so their outputs do not depend on the
+    others)."""
+    w = workloads.M3_CONFIGS["m3_siso_bf16"]
+    inp = workloads.make_m3_inputs(w, 0)
+    dims = mscan.M3Dims.make(w.batch, w.seqlen, w.heads, w.headdim, w.d_state, w.groups, w.n_angles, w.act,
+                             w.a_floor)
+    core = mscan.Mamba3Core(dims)
+    dev = device(w, inp)
+    core.zero_grads()
+    core.forward(dev)
+    core.backward(dev, dev["dy"])
+    torch.cuda.synchronize()
+    heads = [0, 11, 23]
+    P = w.headdim
+    cols = np.concatenate([np.arange(h * P, (h + 1) * P) for h in heads])
+    sub = dict(x=inp["x"][:1, :, cols], b_in=inp["b_in"][:1], c_in=inp["c_in"][:1],
+               dd_dt_raw=inp["dd_dt_raw"][:1, :, heads], dd_a_raw=inp["dd_a_raw"][:1, :, heads],
+               trap_raw=inp["trap_raw"][:1, :, heads], angles_raw=inp["angles_raw"][:1], b_bias=inp["b_bias"][heads],
+               c_bias=inp["c_bias"][heads], dt_bias=inp["dt_bias"][heads], D=inp["D"][heads], a_floor=w.a_floor,
+               heads=len(heads), headdim=P)
+    y = m3o.forward(**sub)
+    g = m3o.backward(inp["dy"][:1, :, cols], **sub)
+    rep = {"y": err(core.y[:1, :, cols], y, True), "x": err(core.grads["x"][:1, :, cols], g["x"], True)}
+    for k in ("dd_dt_raw", "dd_a_raw", "trap_raw"):
+        rep[k] = err(core.grads[k][:1, :, heads], g[k], True)
+    bad = {k: v for k, v in rep.items() if not v <= TOL_HALF}
+    assert not bad, {k: "%.1e" % v for k, v in rep.items()}
