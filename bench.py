@@ -12,6 +12,9 @@ starts.  Prints one JSON line.
 projections, conv, scan core, residual; include/mamba_layer.h), forward +
 backward per step, at a shape of ``workloads.LAYER_CONFIGS``.
 
+``--m3 NAME`` instead times the Mamba-3 SISO core (include/mamba3.h),
+forward + backward per step, at a shape of ``workloads.M3_CONFIGS``.
+
 ``--recurrent`` instead times the recurrent-step path: one-step forward
 calls of the fused entry (conv state and SSM state in, new states out, the
 state ping-ponging between two buffers as in decoding), one JSON line per
@@ -295,6 +298,124 @@ def layer_cpu_baseline(w: workloads.LayerWorkload, budget_s: float):
             "sample": "1 batch row x %d steps of the same widths, fwd+bwd in %.1f s" % (T, dt)}
 
 
+def m3_flops(w: workloads.M3Workload):
+    """(forward, backward) flops of the per-chunk contractions, 2 per
+    multiply-add, per 64-step chunk and head (L = 64 steps, P = headdim,
+    N = d_state):
+      forward : chunk state L*P*N, Q K^T L*L*N, (G o M) V L*L*P, Q S_in L*P*N
+      backward: chunk state of (dY, Q) L*P*N, Q K^T L*L*N, dY V^T L*L*P,
+                dV = (G o M)^T dY L*L*P, dQ and dK from (DV o M) 2*L*L*N, the
+                entering-state and outgoing-gradient terms of dQ, dK, dV 3*L*P*N."""
+    L, P, N = 64, w.headdim, w.d_state
+    chunks = w.batch * w.heads * -(-w.seqlen // L)
+    fwd = 2 * L * (2 * P * N + L * N + L * P) * chunks
+    bwd = 2 * L * (4 * P * N + 3 * L * N + 2 * L * P) * chunks
+    return fwd, bwd
+
+
+def m3_bytes(w: workloads.M3Workload):
+    """(forward, backward) algorithmic bytes: inputs read once, outputs
+    written once, the f32 chunk states written by the forward and read by the
+    backward."""
+    s = act_bytes(w.act)
+    N_tok = w.batch * w.seqlen
+    x = N_tok * w.heads * w.headdim * s
+    bc = 2 * N_tok * w.groups * w.d_state * s
+    scal = 3 * N_tok * w.heads * 4 + N_tok * w.n_angles * 4
+    params = (2 * w.heads * w.d_state + 2 * w.heads) * 4
+    states = w.batch * w.heads * -(-w.seqlen // 64) * w.headdim * w.d_state * 4
+    fwd = x + bc + scal + params + x + states
+    bwd = (x + bc + scal + params + states + x) + (x + bc + scal + params)
+    return fwd, bwd
+
+
+def m3_bench(torch, pkg, name: str, steps: int, warmup: int, no_cpu: bool, budget_s: float):
+    w = workloads.M3_CONFIGS[name]
+    dims = pkg.M3Dims.make(w.batch, w.seqlen, w.heads, w.headdim, w.d_state, w.groups, w.n_angles, w.act, w.a_floor)
+    core = pkg.Mamba3Core(dims)
+    at = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.act]
+    sets = []
+    for k in range(INPUT_SETS):
+        inp = workloads.make_m3_inputs(w, k)
+        sets.append({n: torch.from_numpy(v).to("cuda", at if n in ("x", "b_in", "c_in", "dy") else torch.float32)
+                     for n, v in inp.items()})
+    stream = torch.cuda.current_stream()
+
+    def step(k, ev=None):
+        dev = sets[k % len(sets)]
+        core.zero_grads()
+        if ev:
+            ev[0].record(stream)
+        core.forward(dev, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        core.backward(dev, dev["dy"], stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(steps):
+        step(warmup + k, evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    tokens = w.batch * w.seqlen
+    ff, fb = m3_flops(w)
+    bf, bb = m3_bytes(w)
+    achieved = fb / (bwd / 1e3) / 1e12
+    res = {"metric": "Mamba-3 SISO core fwd+bwd tokens/sec", "value": round(tokens / (ms / 1e3), 1),
+           "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.act,
+           "data": "synthetic (seeded; %d input sets rotated)" % len(sets),
+           "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "heads": w.heads,
+                      "headdim": w.headdim, "d_state": w.d_state, "groups": w.groups, "n_angles": w.n_angles,
+                      "chunk": 64, "parallelism": "single GPU"},
+           "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+           "hbm_GBps": round((bf + bb) / (ms / 1e3) / 1e9, 1),
+           "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": 78.6, "unit": "TFLOP/s",
+                        "frac": round(achieved / 78.6, 4), "traffic": None,
+                        "kernel": "mamba3_siso_bwd entry point (chunk contractions on f32 VALU FMA)",
+                        "launch_ms": round(bwd, 4), "algorithmic_flops_per_launch": fb,
+                        "algorithmic_bytes_per_launch": bb,
+                        "hbm_GBps_at_algorithmic_bytes": round(bb / (bwd / 1e3) / 1e9, 1)},
+           "fwd_flops": ff, "fwd_bytes": bf}
+    if not no_cpu:
+        res["cpu_baseline"] = m3_cpu_baseline(w, budget_s)
+    print(json.dumps(res), flush=True)
+
+
+def m3_cpu_baseline(w: workloads.M3Workload, budget_s: float):
+    """The Mamba-3 oracle as it stands (numpy, float64), forward + backward,
+    on one batch row of the same widths and a bounded number of steps, scaled
+    to the workload's tokens (its cost per step does not depend on T)."""
+    from oracle import mamba3 as m3o
+    T = 16
+    while True:
+        sw = w.with_(batch=1, seqlen=T)
+        inp = workloads.make_m3_inputs(sw, 0)
+        args = {k: inp[k] for k in ("x", "b_in", "c_in", "dd_dt_raw", "dd_a_raw", "trap_raw", "angles_raw", "b_bias",
+                                    "c_bias", "dt_bias", "D")}
+        t0 = time.perf_counter()
+        m3o.forward(a_floor=w.a_floor, heads=w.heads, headdim=w.headdim, **args)
+        m3o.backward(inp["dy"], a_floor=w.a_floor, heads=w.heads, headdim=w.headdim, **args)
+        dt = time.perf_counter() - t0
+        if dt > 0.25 * budget_s or T >= w.seqlen:
+            break
+        T = min(w.seqlen, T * max(2, int(0.5 * budget_s / max(dt, 1e-3))))
+    ncpu, model = host_info()
+    return {"value": T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle", "precision": "f64",
+            "host_logical_cpus": ncpu, "cpu_model": model,
+            "sample": "1 batch row x %d steps of the same widths (all %d heads), fwd+bwd in %.1f s on one thread"
+                      % (T, w.heads, dt)}
+
+
 def host_info():
     """Logical CPUs and CPU model of the host the baseline runs on."""
     model = "unknown"
@@ -382,6 +503,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--layer", default=None, choices=sorted(workloads.LAYER_CONFIGS),
                     help="time one whole Mamba-1 layer at this shape and exit")
+    ap.add_argument("--m3", default=None, choices=sorted(workloads.M3_CONFIGS),
+                    help="time the Mamba-3 SISO core (include/mamba3.h), forward + backward per step")
     ap.add_argument("--recurrent", action="store_true",
                     help="time one-step forward calls with state in/out (see RECURRENT_SHAPES) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -410,6 +533,9 @@ def main():
     pkg.load()
     if args.recurrent:
         recurrent(torch, pkg, calls=max(args.steps, 200), warmup=max(args.warmup, 20))
+        return
+    if args.m3:
+        m3_bench(torch, pkg, args.m3, args.steps, args.warmup, args.no_cpu_baseline, args.cpu_budget)
         return
     if args.layer:
         layer_bench(torch, pkg, args.layer, args.steps, args.warmup, args.no_cpu_baseline, args.cpu_budget)

@@ -19,14 +19,14 @@
 //   St_out = e^{tot} St_in + sum_s e^{tot - cum_s} scale_s V_s K_s^T
 // (gamma_t = lam_t dt_t; the last term of y removes the part of scale_t
 // that belongs to the next step).  The passes:
-//   forward : m3_prep (per-step scalars) -> m3_theta (angle sums) ->
+//   forward : m3_prep (per-step scalars) -> angle sums (chunked scan) ->
 //             m3_rotate (turned Q, K) -> m3_chunk_state (each chunk's own
 //             St_out) -> m3_state_pass (St_in of every chunk, in order) ->
 //             m3_chunk_out (y)
 //   backward: the first three again -> m3_chunk_state on (dY, Q) and a
 //             reverse m3_state_pass (the gradient of every chunk's St_out)
 //             -> m3_chunk_bwd (d_x, the gradients of the turned Q and K and
-//             of each step's cum, scale, gamma) -> m3_rot_bwd -> m3_theta_bwd
+//             of each step's cum, scale, gamma) -> m3_rot_bwd -> angle-sum adjoint
 //             -> m3_scalar_bwd -> fixed-order sums (groups, biases, D,
 //             angles).  No atomics: every output is the same bits run to run.
 #include <hip/hip_runtime.h>
@@ -114,42 +114,89 @@ __global__ void __launch_bounds__(256) m3_prep_kernel(const PrepArgs p) {
 }
 
 // ---------------------------------------------------------------- angles
-// theta[b, h, t, a] = sum_{s<=t} dt[b, h, s] * angles_raw[b, s, a]: one wave
-// per (b, h), lane = angle, sequential in time (as the page's _seq kernel).
-struct ThetaArgs {
-  const float *dt, *ang;
-  float* theta;
+// theta[b, h, t, a] = sum_{s<=t} dt[b, h, s] * angles_raw[b, s, a], and in
+// the backward g[b, h, t, a] = sum_{s>=t} dtheta[b, h, s, a], as two-level
+// scans over the 64-step chunks: each thread scans one (b, h, chunk, angle)
+// and leaves the chunk's total; a pass per (b, h, angle) turns the totals
+// into the sum of the chunks before (after) each one; the last pass adds it.
+struct ScanArgs {
+  const float *dt, *ang, *src;
+  float *out, *ctot;
   Dims d;
 };
 
-__global__ void __launch_bounds__(64) m3_theta_kernel(const ThetaArgs p) {
+template <bool REV>
+__global__ void __launch_bounds__(256) m3_scan_local_kernel(const ScanArgs p) {
   const Dims d = p.d;
-  const int64_t bh = blockIdx.x, b = bh / d.H;
-  const int a = threadIdx.x;
-  if (a >= d.NA) return;
-  const float* dt = p.dt + bh * d.T;
-  const float* ang = p.ang + b * d.T * d.NA + a;
-  float* th = p.theta + bh * d.T * d.NA + a;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= d.B * d.H * d.nc * d.NA) return;
+  const int64_t a = i % d.NA, c = (i / d.NA) % d.nc, bh = i / (d.NA * d.nc), b = bh / d.H;
+  const int64_t t0 = c * kL, t1 = t0 + kL < d.T ? t0 + kL : d.T;
   float acc = 0.0f;
-  int64_t t = 0;
-  constexpr int U = 8;
-  for (; t + U <= d.T; t += U) {
-    float dv[U], av[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      dv[k] = dt[t + k];
-      av[k] = ang[(t + k) * d.NA];
+  if (!REV) {
+    for (int64_t t = t0; t < t1; ++t) {
+      acc = fmaf(p.dt[bh * d.T + t], p.ang[(b * d.T + t) * d.NA + a], acc);
+      p.out[(bh * d.T + t) * d.NA + a] = acc;
     }
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      acc = fmaf(dv[k], av[k], acc);
-      th[(t + k) * d.NA] = acc;
+  } else {
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+      acc += p.src[(bh * d.T + t) * d.NA + a];
+      p.out[(bh * d.T + t) * d.NA + a] = acc;
     }
   }
-  for (; t < d.T; ++t) {
-    acc = fmaf(dt[t], ang[t * d.NA], acc);
-    th[t * d.NA] = acc;
+  p.ctot[(bh * d.nc + c) * d.NA + a] = acc;
+}
+
+template <bool REV>
+__global__ void __launch_bounds__(256) m3_scan_carry_kernel(const ScanArgs p) {
+  const Dims d = p.d;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= d.B * d.H * d.NA) return;
+  const int64_t a = i % d.NA, bh = i / d.NA;
+  float run = 0.0f;
+  for (int64_t k = 0; k < d.nc; ++k) {
+    const int64_t c = REV ? d.nc - 1 - k : k;
+    float* q = p.ctot + (bh * d.nc + c) * d.NA + a;
+    const float v = *q;
+    *q = run;
+    run += v;
   }
+}
+
+// theta: the chunk-local sums plus the sum of the chunks before
+__global__ void __launch_bounds__(256) m3_scan_add_kernel(const ScanArgs p) {
+  const Dims d = p.d;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= d.B * d.H * d.T * d.NA) return;
+  const int64_t a = i % d.NA, bht = i / d.NA, t = bht % d.T, bh = bht / d.T;
+  p.out[i] += p.ctot[(bh * d.nc + t / kL) * d.NA + a];
+}
+
+// Per (b, h, t), from g = the chunk-local suffix sum plus the chunks after:
+// the angle gradient's per-head part g dt_t to `cang` [B, H, T, NA], and
+// sum_a g angles_raw_t[a] (the dt gradient through the angles) to `ddt_ang`.
+struct ThetaBwdArgs {
+  const float *gl, *ctot, *dt, *ang;
+  float *cang, *ddt_ang;
+  Dims d;
+};
+
+__global__ void __launch_bounds__(256) m3_theta_contrib_kernel(const ThetaBwdArgs p) {
+  const Dims d = p.d;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= d.B * d.H * d.T) return;
+  const int64_t t = i % d.T, bh = i / d.T, b = bh / d.H;
+  const float* gl = p.gl + i * d.NA;
+  const float* off = p.ctot + (bh * d.nc + t / kL) * d.NA;
+  const float* ang = p.ang + (b * d.T + t) * d.NA;
+  const float dt = p.dt[i];
+  float acc = 0.0f;
+  for (int64_t a = 0; a < d.NA; ++a) {
+    const float g = gl[a] + off[a];
+    p.cang[i * d.NA + a] = g * dt;
+    acc = fmaf(g, ang[a], acc);
+  }
+  p.ddt_ang[i] = acc;
 }
 
 // ---------------------------------------------------------------- rotate
@@ -763,36 +810,6 @@ __global__ void __launch_bounds__(256) m3_rot_bwd_kernel(const RotBwdArgs p) {
   p.dK[base + n2] = c * gk2 - s * gk1;
 }
 
-// ------------------------------------------------------- angle-sum adjoint
-// One wave per (b, h), lane = angle, reverse in time: g = sum_{t'>=t}
-// dtheta_t'; the angle gradient's per-head part g dt_t to `cang`
-// [B, H, T, NA], and sum_a g angles_raw_t[a] (the dt gradient through the
-// angles) to `ddt_ang` [B, H, T].
-struct ThetaBwdArgs {
-  const float *dtheta, *dt, *ang;
-  float *cang, *ddt_ang;
-  Dims d;
-};
-
-__global__ void __launch_bounds__(64) m3_theta_bwd_kernel(const ThetaBwdArgs p) {
-  const Dims d = p.d;
-  const int64_t bh = blockIdx.x, b = bh / d.H;
-  const int a = threadIdx.x;
-  const bool on = a < d.NA;
-  float g = 0.0f;
-  for (int64_t t = d.T - 1; t >= 0; --t) {
-    const int64_t bt = bh * d.T + t;
-    float v = 0.0f;
-    if (on) {
-      g += p.dtheta[bt * d.NA + a];
-      p.cang[bt * d.NA + a] = g * p.dt[bt];
-      v = g * p.ang[(b * d.T + t) * d.NA + a];
-    }
-    v = wave_sum(v);
-    if (a == 0) p.ddt_ang[bt] = v;
-  }
-}
-
 // ------------------------------------------------------- scalar adjoint
 // Per (b, h, t): from the gradients of dt*A, gamma, scale and the angle
 // part of dt, the gradients of dd_dt_raw, dd_a_raw, trap_raw ([B, T, H]).
@@ -854,7 +871,7 @@ __global__ void __launch_bounds__(256) m3_group_sum_kernel(const GroupArgs p) {
 // Column sums over the (b, t) rows of [B, H, T, W] arrays (W = N for the
 // B / C bias gradients, 1 for the dt-bias gradient laid out [B, H, T]):
 // partial sums over RB row blocks, then a fixed-order sum += into out[h, w].
-constexpr int kRowBlocks = 32;
+constexpr int kRowBlocks = 128;
 
 struct ColArgs {
   const float* src;
@@ -871,7 +888,18 @@ __global__ void __launch_bounds__(256) m3_colpart_kernel(const ColArgs p) {
   const int64_t rows = p.B * p.T, per = (rows + kRowBlocks - 1) / kRowBlocks;
   const int64_t r0 = rb * per, r1 = r0 + per < rows ? r0 + per : rows;
   float acc = 0.0f;
-  for (int64_t r = r0; r < r1; ++r) {
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t b = (r + k) / p.T, t = (r + k) % p.T;
+      v[k] = p.src[((b * p.H + h) * p.T + t) * p.W + w];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc += v[k];
+  }
+  for (; r < r1; ++r) {
     const int64_t b = r / p.T, t = r % p.T;
     acc += p.src[((b * p.H + h) * p.T + t) * p.W + w];
   }
@@ -925,6 +953,12 @@ __global__ void __launch_bounds__(256) m3_bth_to_bht_kernel(const TransArgs p) {
   p.dst[i] = p.src[(b * d.T + t) * d.H + h];
 }
 
+}  // namespace m3
+
+#include "m3_mfma.h"
+
+namespace m3 {
+
 // ================================================================ host side
 
 unsigned blocks(int64_t n, int per = 256) { return static_cast<unsigned>((n + per - 1) / per); }
@@ -937,9 +971,9 @@ hipError_t launch_chunk_kernels_fwd(Act act, const ChunkStateArgs& cs, const Out
       if (o) hipLaunchKernelGGL((m3_chunk_out_kernel<Act::F32, N>), dim3(grid), dim3(kThreads), 0, st, *o);
       else hipLaunchKernelGGL((m3_chunk_state_kernel<Act::F32, N, false>), dim3(grid), dim3(kThreads), 0, st, cs);
       break;
-    case Act::BF16:
-      if (o) hipLaunchKernelGGL((m3_chunk_out_kernel<Act::BF16, N>), dim3(grid), dim3(kThreads), 0, st, *o);
-      else hipLaunchKernelGGL((m3_chunk_state_kernel<Act::BF16, N, false>), dim3(grid), dim3(kThreads), 0, st, cs);
+    case Act::BF16:   // matrix cores
+      if (o) hipLaunchKernelGGL((m3_chunk_out_mfma<N>), dim3(grid), dim3(kThreads), 0, st, *o);
+      else hipLaunchKernelGGL((m3_chunk_state_mfma<N, false>), dim3(grid), dim3(kThreads), 0, st, cs);
       break;
     case Act::F16:
       if (o) hipLaunchKernelGGL((m3_chunk_out_kernel<Act::F16, N>), dim3(grid), dim3(kThreads), 0, st, *o);
@@ -957,9 +991,9 @@ hipError_t launch_chunk_kernels_bwd(Act act, const ChunkStateArgs* cs, const Bwd
       if (bw) hipLaunchKernelGGL((m3_chunk_bwd_kernel<Act::F32, N>), dim3(grid), dim3(kThreads), 0, st, *bw);
       else hipLaunchKernelGGL((m3_chunk_state_kernel<Act::F32, N, true>), dim3(grid), dim3(kThreads), 0, st, *cs);
       break;
-    case Act::BF16:
-      if (bw) hipLaunchKernelGGL((m3_chunk_bwd_kernel<Act::BF16, N>), dim3(grid), dim3(kThreads), 0, st, *bw);
-      else hipLaunchKernelGGL((m3_chunk_state_kernel<Act::BF16, N, true>), dim3(grid), dim3(kThreads), 0, st, *cs);
+    case Act::BF16:   // matrix cores
+      if (bw) hipLaunchKernelGGL((m3_chunk_bwd_mfma<N>), dim3(grid), dim3(kThreads), 0, st, *bw);
+      else hipLaunchKernelGGL((m3_chunk_state_mfma<N, true>), dim3(grid), dim3(kThreads), 0, st, *cs);
       break;
     case Act::F16:
       if (bw) hipLaunchKernelGGL((m3_chunk_bwd_kernel<Act::F16, N>), dim3(grid), dim3(kThreads), 0, st, *bw);
@@ -1060,12 +1094,12 @@ int check_dims(const mamba3_dims_t* dd, Dims* out, Act* act) {
 
 size_t al(size_t v) { return (v + 255) / 256 * 256; }
 
-// workspace: [dt | da | gam | sc : B*H*T f32 each] [tot : B*H*nc] [theta : B*H*T*NA]
+// workspace: [dt | da | gam | sc : B*H*T f32 each] [tot : B*H*nc] [theta : B*H*T*NA] [atot : B*H*nc*NA]
 //            [Qr | Kr : B*H*T*N act]   -- forward and backward
 //            [dst : B*H*nc*P*N] [dQ | dK : B*H*T*N f32] [d_da | d_sc | d_gam | ddt_ang | dt_bht : B*H*T]
 //            [dtheta | cang : B*H*T*NA] [dD_part : B*H*nc] [colpart : kRowBlocks*H*N]   -- backward
 struct Ws {
-  float *dt, *da, *gam, *sc, *tot, *theta;
+  float *dt, *da, *gam, *sc, *tot, *theta, *atot;
   void *Qr, *Kr;
   float *dst, *dQ, *dK, *d_da, *d_sc, *d_gam, *ddt_ang, *dt_bht, *dtheta, *cang, *dD_part, *colpart;
   size_t fwd_bytes, bwd_bytes;
@@ -1087,6 +1121,7 @@ Ws layout(const Dims& d, Act act, char* base) {
   w.sc = reinterpret_cast<float*>(take(bht * f));
   w.tot = reinterpret_cast<float*>(take(bhc * f));
   w.theta = reinterpret_cast<float*>(take(bht * d.NA * f + f));
+  w.atot = reinterpret_cast<float*>(take(bhc * d.NA * f + f));
   w.Qr = take(bht * d.N * es);
   w.Kr = take(bht * d.N * es);
   w.fwd_bytes = off;
@@ -1135,8 +1170,10 @@ int prep(const Dims& d, Act act, const Ws& w, const void* b_in, const void* c_in
   hipLaunchKernelGGL(m3_prep_kernel, dim3(blocks(bht)), dim3(256), 0, st, pa);
   M3_HIP(hipGetLastError());
   if (d.NA > 0) {
-    ThetaArgs ta{w.dt, ang, w.theta, d};
-    hipLaunchKernelGGL(m3_theta_kernel, dim3(static_cast<unsigned>(d.B * d.H)), dim3(64), 0, st, ta);
+    ScanArgs sa{w.dt, ang, nullptr, w.theta, w.atot, d};
+    hipLaunchKernelGGL(m3_scan_local_kernel<false>, dim3(blocks(d.B * d.H * d.nc * d.NA)), dim3(256), 0, st, sa);
+    hipLaunchKernelGGL(m3_scan_carry_kernel<false>, dim3(blocks(d.B * d.H * d.NA)), dim3(256), 0, st, sa);
+    hipLaunchKernelGGL(m3_scan_add_kernel, dim3(blocks(bht * d.NA)), dim3(256), 0, st, sa);
     M3_HIP(hipGetLastError());
   }
   RotArgs ra{b_in, c_in, b_bias, c_bias, w.theta, w.Kr, w.Qr, d};
@@ -1269,8 +1306,12 @@ int mamba3_siso_bwd(const mamba3_dims_t* dims, const void* x, const void* b_in, 
   if (d.NA > 0) {
     RotBwdArgs rb{w.Qr, w.Kr, w.theta, w.dQ, w.dK, w.dtheta, d};
     M3_HIP(launch_rot_bwd(act, rb, blocks(bht * d.NA), st));
-    ThetaBwdArgs tb{w.dtheta, w.dt, angles_raw, w.cang, w.ddt_ang, d};
-    hipLaunchKernelGGL(m3_theta_bwd_kernel, dim3(static_cast<unsigned>(d.B * d.H)), dim3(64), 0, st, tb);
+    // g = suffix sums of dtheta (in place), then the per-step contributions
+    ScanArgs sa{nullptr, nullptr, w.dtheta, w.dtheta, w.atot, d};
+    hipLaunchKernelGGL(m3_scan_local_kernel<true>, dim3(blocks(d.B * d.H * d.nc * d.NA)), dim3(256), 0, st, sa);
+    hipLaunchKernelGGL(m3_scan_carry_kernel<true>, dim3(blocks(d.B * d.H * d.NA)), dim3(256), 0, st, sa);
+    ThetaBwdArgs tb{w.dtheta, w.atot, w.dt, angles_raw, w.cang, w.ddt_ang, d};
+    hipLaunchKernelGGL(m3_theta_contrib_kernel, dim3(blocks(bht)), dim3(256), 0, st, tb);
     M3_HIP(hipGetLastError());
     AngArgs aa{w.cang, d_angles_raw, d};
     hipLaunchKernelGGL(m3_angle_sum_kernel, dim3(blocks(d.B * d.T * d.NA)), dim3(256), 0, st, aa);
