@@ -172,11 +172,13 @@ __global__ void __launch_bounds__(256) m3_scan_add_kernel(const ScanArgs p) {
   p.out[i] += p.ctot[(bh * d.nc + t / kL) * d.NA + a];
 }
 
-// Per (b, h, t), from g = the chunk-local suffix sum plus the chunks after:
-// the angle gradient's per-head part g dt_t to `cang` [B, H, T, NA], and
-// sum_a g angles_raw_t[a] (the dt gradient through the angles) to `ddt_ang`.
+// From g = the chunk-local suffix sum plus the chunks after, per (b, h, t,
+// angle): the angle gradient's per-head part g dt_t to `cang` [B, H, T, NA],
+// and g angles_raw_t[a] in place of g; then per (b, h, t) the sum of the
+// latter over the angles (the dt gradient through the angles) to `ddt_ang`.
 struct ThetaBwdArgs {
-  const float *gl, *ctot, *dt, *ang;
+  float* gl;
+  const float *ctot, *dt, *ang;
   float *cang, *ddt_ang;
   Dims d;
 };
@@ -184,18 +186,20 @@ struct ThetaBwdArgs {
 __global__ void __launch_bounds__(256) m3_theta_contrib_kernel(const ThetaBwdArgs p) {
   const Dims d = p.d;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= d.B * d.H * d.T * d.NA) return;
+  const int64_t a = i % d.NA, bht = i / d.NA, t = bht % d.T, bh = bht / d.T, b = bh / d.H;
+  const float g = p.gl[i] + p.ctot[(bh * d.nc + t / kL) * d.NA + a];
+  p.cang[i] = g * p.dt[bht];
+  p.gl[i] = g * p.ang[(b * d.T + t) * d.NA + a];
+}
+
+__global__ void __launch_bounds__(256) m3_theta_dt_kernel(const ThetaBwdArgs p) {
+  const Dims d = p.d;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= d.B * d.H * d.T) return;
-  const int64_t t = i % d.T, bh = i / d.T, b = bh / d.H;
-  const float* gl = p.gl + i * d.NA;
-  const float* off = p.ctot + (bh * d.nc + t / kL) * d.NA;
-  const float* ang = p.ang + (b * d.T + t) * d.NA;
-  const float dt = p.dt[i];
+  const float* g = p.gl + i * d.NA;
   float acc = 0.0f;
-  for (int64_t a = 0; a < d.NA; ++a) {
-    const float g = gl[a] + off[a];
-    p.cang[i * d.NA + a] = g * dt;
-    acc = fmaf(g, ang[a], acc);
-  }
+  for (int64_t a = 0; a < d.NA; ++a) acc += g[a];
   p.ddt_ang[i] = acc;
 }
 
@@ -239,6 +243,79 @@ __global__ void __launch_bounds__(256) m3_rotate_kernel(const RotArgs p) {
     io::st(p.Kr, dst + n, io::ld(p.b_in, src + n) + p.b_bias[h * d.N + n]);
     io::st(p.Qr, dst + n, io::ld(p.c_in, src + n) + p.c_bias[h * d.N + n]);
   }
+}
+
+// The same for 16-bit activations and n_angles a multiple of 8: a thread
+// makes 8 consecutive dims of one (b, h, t) row of both Qr and Kr, which lie
+// wholly in the first halves of the pairs, the second halves, or past them.
+template <Act A>
+__global__ void __launch_bounds__(256) m3_rotate8_kernel(const RotArgs p) {
+  using io = IO<A>;
+  const Dims d = p.d;
+  const int64_t W = d.N / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= d.B * d.H * d.T * W) return;
+  const int64_t d0 = (i % W) * 8, bht = i / W, t = bht % d.T, bh = bht / d.T, h = bh % d.H, b = bh / d.H;
+  const int64_t g = h / (d.H / d.G);
+  const int64_t src = ((b * d.T + t) * d.G + g) * d.N;
+  auto row = [&](const void* base, int64_t off, float* v) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + src + off);
+    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = io::cvt(wv[k] & 0xffffu);
+      v[2 * k + 1] = io::cvt(wv[k] >> 16);
+    }
+  };
+  float kv[8], qv[8], ko[8], qo[8];
+  row(p.b_in, d0, kv);
+  row(p.c_in, d0, qv);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    kv[k] += p.b_bias[h * d.N + d0 + k];
+    qv[k] += p.c_bias[h * d.N + d0 + k];
+  }
+  if (d0 < 2 * d.NA) {
+    const bool first = d0 < d.NA;
+    const int64_t pd = first ? d0 + d.NA : d0 - d.NA;   // partner dims
+    const int64_t a0 = first ? d0 : d0 - d.NA;
+    float kp[8], qp[8];
+    row(p.b_in, pd, kp);
+    row(p.c_in, pd, qp);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      kp[k] += p.b_bias[h * d.N + pd + k];
+      qp[k] += p.c_bias[h * d.N + pd + k];
+      float sn, cs;
+      __sincosf(p.theta[bht * d.NA + a0 + k], &sn, &cs);
+      // first half: x1 c - x2 s; second half: x1 s + x2 c (x1 = partner)
+      ko[k] = first ? kv[k] * cs - kp[k] * sn : kp[k] * sn + kv[k] * cs;
+      qo[k] = first ? qv[k] * cs - qp[k] * sn : qp[k] * sn + qv[k] * cs;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ko[k] = kv[k];
+      qo[k] = qv[k];
+    }
+  }
+  const int64_t dst = bht * d.N + d0;
+  auto put = [&](void* base, const float* v) {   // 8 values as one 16-byte store
+    uint16_t hv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if constexpr (A == Act::BF16) hv[k] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[k]));
+      else hv[k] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[k]));
+    }
+    uint4 o;
+    o.x = hv[0] | (uint32_t(hv[1]) << 16);
+    o.y = hv[2] | (uint32_t(hv[3]) << 16);
+    o.z = hv[4] | (uint32_t(hv[5]) << 16);
+    o.w = hv[6] | (uint32_t(hv[7]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + dst) = o;
+  };
+  put(p.Kr, ko);
+  put(p.Qr, qo);
 }
 
 // ------------------------------------------------------- chunk state
@@ -992,7 +1069,7 @@ hipError_t launch_chunk_kernels_bwd(Act act, const ChunkStateArgs* cs, const Bwd
       else hipLaunchKernelGGL((m3_chunk_state_kernel<Act::F32, N, true>), dim3(grid), dim3(kThreads), 0, st, *cs);
       break;
     case Act::BF16:   // matrix cores
-      if (bw) hipLaunchKernelGGL((m3_chunk_bwd_mfma<N>), dim3(grid), dim3(kThreads), 0, st, *bw);
+      if (bw) hipLaunchKernelGGL((m3_chunk_bwd_mfma<N>), dim3(grid), dim3(kThreadsB), 0, st, *bw);
       else hipLaunchKernelGGL((m3_chunk_state_mfma<N, true>), dim3(grid), dim3(kThreads), 0, st, *cs);
       break;
     case Act::F16:
@@ -1022,6 +1099,13 @@ hipError_t chunk_bwd(int64_t N, Act act, const ChunkStateArgs* cs, const BwdArgs
 }
 
 hipError_t launch_rotate(Act act, const RotArgs& a, unsigned grid, hipStream_t st) {
+  const Dims& d = a.d;
+  if (act != Act::F32 && d.NA % 8 == 0) {
+    const unsigned g8 = blocks(d.B * d.H * d.T * (d.N / 8));
+    if (act == Act::BF16) hipLaunchKernelGGL(m3_rotate8_kernel<Act::BF16>, dim3(g8), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(m3_rotate8_kernel<Act::F16>, dim3(g8), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   switch (act) {
     case Act::F32: hipLaunchKernelGGL(m3_rotate_kernel<Act::F32>, dim3(grid), dim3(256), 0, st, a); break;
     case Act::BF16: hipLaunchKernelGGL(m3_rotate_kernel<Act::BF16>, dim3(grid), dim3(256), 0, st, a); break;
@@ -1311,7 +1395,8 @@ int mamba3_siso_bwd(const mamba3_dims_t* dims, const void* x, const void* b_in, 
     hipLaunchKernelGGL(m3_scan_local_kernel<true>, dim3(blocks(d.B * d.H * d.nc * d.NA)), dim3(256), 0, st, sa);
     hipLaunchKernelGGL(m3_scan_carry_kernel<true>, dim3(blocks(d.B * d.H * d.NA)), dim3(256), 0, st, sa);
     ThetaBwdArgs tb{w.dtheta, w.atot, w.dt, angles_raw, w.cang, w.ddt_ang, d};
-    hipLaunchKernelGGL(m3_theta_contrib_kernel, dim3(blocks(bht)), dim3(256), 0, st, tb);
+    hipLaunchKernelGGL(m3_theta_contrib_kernel, dim3(blocks(bht * d.NA)), dim3(256), 0, st, tb);
+    hipLaunchKernelGGL(m3_theta_dt_kernel, dim3(blocks(bht)), dim3(256), 0, st, tb);
     M3_HIP(hipGetLastError());
     AngArgs aa{w.cang, d_angles_raw, d};
     hipLaunchKernelGGL(m3_angle_sum_kernel, dim3(blocks(d.B * d.T * d.NA)), dim3(256), 0, st, aa);

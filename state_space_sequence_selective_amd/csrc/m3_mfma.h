@@ -42,6 +42,14 @@ __device__ __forceinline__ void ld8_split(const float* p, bf16x8& hi, bf16x8& lo
 
 __device__ __forceinline__ __bf16 raw_bf16(const void* p, int64_t i) { return static_cast<const __bf16*>(p)[i]; }
 
+// 8 consecutive bf16 of a global row (16-byte aligned), or zeros
+__device__ __forceinline__ bf16x8 g8(const void* p, int64_t i, bool ok) {
+  if (!ok) return bf16x8{};
+  return *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p) + i);
+}
+
+__device__ __forceinline__ void st8(__bf16* p, const bf16x8& v) { *reinterpret_cast<bf16x8*>(p) = v; }
+
 __device__ __forceinline__ float sum16(float v) {   // over the 16 lanes of one l / 16 group
   v += __shfl_xor(v, 1, 64);
   v += __shfl_xor(v, 2, 64);
@@ -77,14 +85,17 @@ __global__ void __launch_bounds__(kThreads) m3_chunk_state_mfma(const ChunkState
     if (tid == 0) p.tot[bh * d.nc + c] = s.tot;
   }
   __syncthreads();
-  for (int e = tid; e < kL * kP; e += kThreads) {
-    const int s = e / kP, q = e % kP;
-    const bool ok = t0 + s < d.T;
-    sXT[q * XS + s] = ok ? sW[s] * IO<Act::BF16>::ld(p.X, ((b * d.T + t0 + s) * d.H + h) * kP + q) : 0.0f;
+  for (int e = tid; e < kL * kP / 8; e += kThreads) {
+    const int s = e / (kP / 8), q = (e % (kP / 8)) * 8;
+    const bf16x8 v = g8(p.X, ((b * d.T + t0 + s) * d.H + h) * kP + q, t0 + s < d.T);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sXT[(q + k) * XS + s] = sW[s] * static_cast<float>(v[k]);
   }
-  for (int e = tid; e < kL * N; e += kThreads) {
-    const int s = e / N, n = e % N;
-    sYT[n * YS + s] = t0 + s < d.T ? raw_bf16(p.Y, (bh * d.T + t0 + s) * N + n) : static_cast<__bf16>(0.0f);
+  for (int e = tid; e < kL * N / 8; e += kThreads) {
+    const int s = e / (N / 8), n = (e % (N / 8)) * 8;
+    const bf16x8 v = g8(p.Y, (bh * d.T + t0 + s) * N + n, t0 + s < d.T);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sYT[(n + k) * YS + s] = v[k];
   }
   __syncthreads();
   const int r = lane & 15, g = lane >> 4;
@@ -136,17 +147,18 @@ __global__ void __launch_bounds__(kThreads) m3_chunk_out_mfma(const OutArgs p) {
     s.sc[tid] = cs.valid ? p.sc[bh * d.T + t0 + tid] : 0.0f;
     s.gam[tid] = cs.valid ? p.gam[bh * d.T + t0 + tid] : 0.0f;
   }
-  for (int e = tid; e < kL * N; e += kThreads) {
-    const int row = e / N, n = e % N;
+  for (int e = tid; e < kL * N / 8; e += kThreads) {
+    const int row = e / (N / 8), n = (e % (N / 8)) * 8;
     const bool ok = t0 + row < d.T;
     const int64_t gi = (bh * d.T + t0 + row) * N + n;
-    s.q[row * QS + n] = ok ? raw_bf16(p.Qr, gi) : static_cast<__bf16>(0.0f);
-    s.k[row * QS + n] = ok ? raw_bf16(p.Kr, gi) : static_cast<__bf16>(0.0f);
+    st8(&s.q[row * QS + n], g8(p.Qr, gi, ok));
+    st8(&s.k[row * QS + n], g8(p.Kr, gi, ok));
   }
-  for (int e = tid; e < kL * kP; e += kThreads) {
-    const int row = e / kP, q = e % kP;
-    s.vT[q * VS + row] =
-        t0 + row < d.T ? raw_bf16(p.x, ((b * d.T + t0 + row) * d.H + h) * kP + q) : static_cast<__bf16>(0.0f);
+  for (int e = tid; e < kL * kP / 8; e += kThreads) {
+    const int row = e / (kP / 8), q = (e % (kP / 8)) * 8;
+    const bf16x8 v = g8(p.x, ((b * d.T + t0 + row) * d.H + h) * kP + q, t0 + row < d.T);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s.vT[(q + k) * VS + row] = v[k];
   }
   __syncthreads();
   bf16x8 qa[N / 32];
@@ -206,11 +218,16 @@ __global__ void __launch_bounds__(kThreads) m3_chunk_out_mfma(const OutArgs p) {
 }
 
 // -------------------------------------------------------- chunk backward
-// Wave w owns the query steps t = 16w .. +15 (rows of G, DV, dQ) and the key
-// steps s = 16w .. +15 (rows of dV, dK).  Phase 1: G and DV tiles, their
-// masked forms and per-step sums; phase 2: the products inside the chunk;
-// phase 3 (with the entering state and the outgoing state's gradient in
-// LDS): the products across chunks; then the outputs.
+// Eight waves: wave w handles block tb = w % 4 of 16 steps, in half hf = w / 4
+// of the tiles: the key blocks sb = hf, hf + 2 of its G / DV row, the p tiles
+// 2 hf, 2 hf + 1 of dV and half of the d_state tiles of dQ and dK (two waves
+// per SIMD hide the LDS and memory latency a single one waits on).  Phase 1:
+// G and DV tiles, their masked forms and per-step sums; phase 2: the
+// products inside the chunk; phase 3 (with the entering state and the
+// outgoing state's gradient in LDS): the products across chunks; then the
+// outputs.
+constexpr int kThreadsB = 512;
+
 template <int N>
 struct BwdLdsM {
   static constexpr int QS = N + 8, VS = kL + 8, FS = kL + 4, TS = kP + 4;
@@ -233,64 +250,70 @@ struct BwdLdsM {
       float dsT[N * TS];     // dSt_out [n][p]
     } c;
   } u;
-  float cum[kL], sc[kL], gam[kL], qk[kL], dvd[kL], rrow[kL], dcq[kL], dus[kL];
+  float cum[kL], sc[kL], gam[kL], qk[kL], dvd[kL];
+  float rrow[2][kL], dcq[2][kL], dus[2][kL];
   float colR[4][kL], colE[4][kL];
-  float red[kThreads];
+  float red[kThreadsB];
+  float tot;
 };
 
 template <int N>
-__global__ void __launch_bounds__(kThreads) m3_chunk_bwd_mfma(const BwdArgs p) {
+__global__ void __launch_bounds__(kThreadsB) m3_chunk_bwd_mfma(const BwdArgs p) {
   using L = BwdLdsM<N>;
   constexpr int QS = L::QS, VS = L::VS, FS = L::FS, TS = L::TS;
-  constexpr int NT = N / 16;
+  constexpr int NT = N / 16, NH = NT / 2;   // d_state tiles, per half
   __shared__ __attribute__((aligned(16))) L s;
   const Dims d = p.d;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tb = wv & 3, hf = wv >> 2;
   const int r = lane & 15, g = lane >> 4;
   const int64_t c = blockIdx.x % d.nc, bh = blockIdx.x / d.nc, h = bh % d.H, b = bh / d.H;
   const int64_t t0 = c * kL;
-  const __bf16 z16 = static_cast<__bf16>(0.0f);
-  float tot = 0.0f;
   if (tid < 64) {
     const ChunkScalars cs = chunk_cum(p.da + bh * d.T, t0, d.T, tid);
     s.cum[tid] = cs.cum;
     s.sc[tid] = cs.valid ? p.sc[bh * d.T + t0 + tid] : 0.0f;
     s.gam[tid] = cs.valid ? p.gam[bh * d.T + t0 + tid] : 0.0f;
-    tot = cs.tot;
+    if (tid == 0) s.tot = cs.tot;
   }
-  for (int e = tid; e < kL * N; e += kThreads) {
-    const int row = e / N, n = e % N;
+  for (int e = tid; e < kL * N / 8; e += kThreadsB) {
+    const int row = e / (N / 8), n = (e % (N / 8)) * 8;
     const bool ok = t0 + row < d.T;
     const int64_t gi = (bh * d.T + t0 + row) * N + n;
-    const __bf16 qv = ok ? raw_bf16(p.Qr, gi) : z16, kv = ok ? raw_bf16(p.Kr, gi) : z16;
-    s.q[row * QS + n] = qv;
-    s.k[row * QS + n] = kv;
-    s.u.a.qT[n * VS + row] = qv;
-    s.u.a.kT[n * VS + row] = kv;
+    const bf16x8 qv = g8(p.Qr, gi, ok), kv = g8(p.Kr, gi, ok);
+    st8(&s.q[row * QS + n], qv);
+    st8(&s.k[row * QS + n], kv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      s.u.a.qT[(n + k) * VS + row] = qv[k];
+      s.u.a.kT[(n + k) * VS + row] = kv[k];
+    }
   }
-  for (int e = tid; e < kL * kP; e += kThreads) {
-    const int row = e / kP, q = e % kP;
+  for (int e = tid; e < kL * kP / 8; e += kThreadsB) {
+    const int row = e / (kP / 8), q = (e % (kP / 8)) * 8;
     const bool ok = t0 + row < d.T;
     const int64_t gi = ((b * d.T + t0 + row) * d.H + h) * kP + q;
-    const __bf16 vv = ok ? raw_bf16(p.x, gi) : z16, yv = ok ? raw_bf16(p.dy, gi) : z16;
-    s.v[row * VS + q] = vv;
-    s.dy[row * VS + q] = yv;
-    s.u.a.dyT[q * VS + row] = yv;
+    const bf16x8 vv = g8(p.x, gi, ok), yv = g8(p.dy, gi, ok);
+    st8(&s.v[row * VS + q], vv);
+    st8(&s.dy[row * VS + q], yv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s.u.a.dyT[(q + k) * VS + row] = yv[k];
   }
   __syncthreads();
 
-  // ---- phase 1: G = Q K^T and DV = dY V^T on the tiles (t-block w, s-block sb)
+  // ---- phase 1: G = Q K^T and DV = dY V^T on the tiles (block tb, key blocks sb = hf, hf + 2)
   {
     bf16x8 qa[N / 32], ya[2];
 #pragma unroll
-    for (int k = 0; k < N / 32; ++k) qa[k] = ld8(&s.q[(16 * w + r) * QS + 32 * k + 8 * g]);
+    for (int k = 0; k < N / 32; ++k) qa[k] = ld8(&s.q[(16 * tb + r) * QS + 32 * k + 8 * g]);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) ya[k] = ld8(&s.dy[(16 * w + r) * VS + 32 * k + 8 * g]);
+    for (int k = 0; k < 2; ++k) ya[k] = ld8(&s.dy[(16 * tb + r) * VS + 32 * k + 8 * g]);
     float rrow[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
+    for (int j = 0; j < 2; ++j) {
+      const int sb = hf + 2 * j;
       f32x4 gt = {0.0f, 0.0f, 0.0f, 0.0f}, dv = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (sb <= w) {
+      if (sb <= tb) {
 #pragma unroll
         for (int k = 0; k < N / 32; ++k) gt = mma(qa[k], ld8(&s.k[(16 * sb + r) * QS + 32 * k + 8 * g]), gt);
 #pragma unroll
@@ -299,7 +322,7 @@ __global__ void __launch_bounds__(kThreads) m3_chunk_bwd_mfma(const BwdArgs p) {
       float cr = 0.0f, ce = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * w + 4 * g + e, sv = 16 * sb + r;
+        const int t = 16 * tb + 4 * g + e, sv = 16 * sb + r;
         const float ee = sv <= t ? expf_fast(s.cum[t] - s.cum[sv]) : 0.0f;
         const float m = ee * s.sc[sv];
         s.u.a.gmT[sv * FS + t] = gt[e] * m;
@@ -317,14 +340,14 @@ __global__ void __launch_bounds__(kThreads) m3_chunk_bwd_mfma(const BwdArgs p) {
       cr = sum_groups(cr);
       ce = sum_groups(ce);
       if (g == 0) {
-        s.colR[w][16 * sb + r] = cr;
-        s.colE[w][16 * sb + r] = ce;
+        s.colR[tb][16 * sb + r] = cr;
+        s.colE[tb][16 * sb + r] = ce;
       }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float v = sum16(rrow[e]);
-      if (r == 0) s.rrow[16 * w + 4 * g + e] = v;
+      if (r == 0) s.rrow[hf][16 * tb + 4 * g + e] = v;
     }
   }
   __syncthreads();
@@ -333,43 +356,45 @@ __global__ void __launch_bounds__(kThreads) m3_chunk_bwd_mfma(const BwdArgs p) {
   //   dV[s][p] = sum_{t>=s} GM[t][s] dY[t][p]   (A = GM^T [s][t], B = dY^T [p][t])
   //   dQ[t][n] = sum_{s<=t} DVM[t][s] K[s][n]    (A = DVM [t][s],  B = K^T [n][s])
   //   dK[s][n] = sum_{t>=s} DVM[t][s] Q[t][n]    (A = DVM^T [s][t], B = Q^T [n][t])
-  f32x4 dV[4], dQ[NT], dK[NT];
-  const int klo = (16 * w) / 32;              // first 32-step block of t that reaches t >= 16w
-  const int khi = (16 * (w + 1) + 31) / 32;   // 32-step blocks of s that reach s <= 16w + 15
+  f32x4 dV[2], dQ[NH], dK[NH];
+  const int klo = (16 * tb) / 32;              // first 32-step block of t that reaches t >= 16 tb
+  const int khi = (16 * (tb + 1) + 31) / 32;   // 32-step blocks of s that reach s <= 16 tb + 15
   {
     bf16x8 ghi[2], glo[2], dhi[2], dlo[2], thi[2], tlo[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      ld8_split(&s.u.a.gmT[(16 * w + r) * FS + 32 * k + 8 * g], ghi[k], glo[k]);
-      ld8_split(&s.u.a.dvm[(16 * w + r) * FS + 32 * k + 8 * g], dhi[k], dlo[k]);
-      ld8_split(&s.u.a.dvmT[(16 * w + r) * FS + 32 * k + 8 * g], thi[k], tlo[k]);
+      ld8_split(&s.u.a.gmT[(16 * tb + r) * FS + 32 * k + 8 * g], ghi[k], glo[k]);
+      ld8_split(&s.u.a.dvm[(16 * tb + r) * FS + 32 * k + 8 * g], dhi[k], dlo[k]);
+      ld8_split(&s.u.a.dvmT[(16 * tb + r) * FS + 32 * k + 8 * g], thi[k], tlo[k]);
     }
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-      dV[pb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 2; ++j) {
+      const int pb = 2 * hf + j;
+      dV[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < 2; ++k)
         if (k >= klo) {
           const bf16x8 bv = ld8(&s.u.a.dyT[(16 * pb + r) * VS + 32 * k + 8 * g]);
-          dV[pb] = mma(ghi[k], bv, dV[pb]);
-          dV[pb] = mma(glo[k], bv, dV[pb]);
+          dV[j] = mma(ghi[k], bv, dV[j]);
+          dV[j] = mma(glo[k], bv, dV[j]);
         }
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      dQ[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      dK[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < NH; ++j) {
+      const int nt = hf * NH + j;
+      dQ[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      dK[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         if (k < khi) {
           const bf16x8 bk = ld8(&s.u.a.kT[(16 * nt + r) * VS + 32 * k + 8 * g]);
-          dQ[nt] = mma(dhi[k], bk, dQ[nt]);
-          dQ[nt] = mma(dlo[k], bk, dQ[nt]);
+          dQ[j] = mma(dhi[k], bk, dQ[j]);
+          dQ[j] = mma(dlo[k], bk, dQ[j]);
         }
         if (k >= klo) {
           const bf16x8 bq = ld8(&s.u.a.qT[(16 * nt + r) * VS + 32 * k + 8 * g]);
-          dK[nt] = mma(thi[k], bq, dK[nt]);
-          dK[nt] = mma(tlo[k], bq, dK[nt]);
+          dK[j] = mma(thi[k], bq, dK[j]);
+          dK[j] = mma(tlo[k], bq, dK[j]);
         }
       }
     }
@@ -380,34 +405,38 @@ __global__ void __launch_bounds__(kThreads) m3_chunk_bwd_mfma(const BwdArgs p) {
   const float* stin = p.st + (bh * d.nc + c) * kP * N;
   const float* dsout = p.dst + (bh * d.nc + c) * kP * N;
   float dtot_part = 0.0f;
-  for (int e = tid; e < kP * N; e += kThreads) {
-    const int q = e / N, n = e % N;
-    const float a = stin[e], bb = dsout[e];
-    s.u.c.stT[n * TS + q] = a;
-    s.u.c.dsT[n * TS + q] = bb;
-    dtot_part = fmaf(a, bb, dtot_part);
+  for (int e = tid; e < kP * N / 4; e += kThreadsB) {
+    const int q = e / (N / 4), n = (e % (N / 4)) * 4;
+    const float4 a = *reinterpret_cast<const float4*>(stin + q * N + n);
+    const float4 bb = *reinterpret_cast<const float4*>(dsout + q * N + n);
+    const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      s.u.c.stT[(n + k) * TS + q] = av[k];
+      s.u.c.dsT[(n + k) * TS + q] = bv[k];
+      dtot_part = fmaf(av[k], bv[k], dtot_part);
+    }
   }
   s.red[tid] = dtot_part;
-  __shared__ float s_tot;
-  if (tid == 0) s_tot = tot;
   __syncthreads();
-  const float totv = s_tot;
+  const float totv = s.tot;
   {
     bf16x8 ya[2], va[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      ya[k] = ld8(&s.dy[(16 * w + r) * VS + 32 * k + 8 * g]);
-      va[k] = ld8(&s.v[(16 * w + r) * VS + 32 * k + 8 * g]);
+      ya[k] = ld8(&s.dy[(16 * tb + r) * VS + 32 * k + 8 * g]);
+      va[k] = ld8(&s.v[(16 * tb + r) * VS + 32 * k + 8 * g]);
     }
     float ec[4], uc[4], dcq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dus[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = 16 * w + 4 * g + e;
+      const int t = 16 * tb + 4 * g + e;
       ec[e] = expf_fast(s.cum[t]);
       uc[e] = expf_fast(totv - s.cum[t]) * s.sc[t];
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int j = 0; j < NH; ++j) {
+      const int nt = hf * NH + j;
       f32x4 zq = {0.0f, 0.0f, 0.0f, 0.0f}, zk = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -421,66 +450,67 @@ __global__ void __launch_bounds__(kThreads) m3_chunk_bwd_mfma(const BwdArgs p) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * w + 4 * g + e, n = 16 * nt + r;
+        const int t = 16 * tb + 4 * g + e, n = 16 * nt + r;
         const float qz = ec[e] * zq[e];
-        dQ[nt][e] += qz;
+        dQ[j][e] += qz;
         dcq[e] = fmaf(static_cast<float>(s.q[t * QS + n]), qz, dcq[e]);
-        dK[nt][e] = fmaf(uc[e], zk[e], dK[nt][e]);
+        dK[j][e] = fmaf(uc[e], zk[e], dK[j][e]);
         dus[e] = fmaf(static_cast<float>(s.k[t * QS + n]), zk[e], dus[e]);
       }
     }
     // dV[s][p] += u_s sum_n K[s][n] dSt[p][n]   (A = K [s][n], B = dSt [p][n] from global)
     bf16x8 ka[N / 32];
 #pragma unroll
-    for (int k = 0; k < N / 32; ++k) ka[k] = ld8(&s.k[(16 * w + r) * QS + 32 * k + 8 * g]);
+    for (int k = 0; k < N / 32; ++k) ka[k] = ld8(&s.k[(16 * tb + r) * QS + 32 * k + 8 * g]);
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-      f32x4 wv = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 2; ++j) {
+      const int pb = 2 * hf + j;
+      f32x4 wacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < N / 32; ++k) {
         bf16x8 hi, lo;
         ld8_split(dsout + (16 * pb + r) * N + 32 * k + 8 * g, hi, lo);
-        wv = mma(ka[k], hi, wv);
-        wv = mma(ka[k], lo, wv);
+        wacc = mma(ka[k], hi, wacc);
+        wacc = mma(ka[k], lo, wacc);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dV[pb][e] = fmaf(uc[e], wv[e], dV[pb][e]);
+      for (int e = 0; e < 4; ++e) dV[j][e] = fmaf(uc[e], wacc[e], dV[j][e]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float a = sum16(dcq[e]), bq = sum16(dus[e]);
       if (r == 0) {
-        s.dcq[16 * w + 4 * g + e] = a;
-        s.dus[16 * w + 4 * g + e] = bq;
+        s.dcq[hf][16 * tb + 4 * g + e] = a;
+        s.dus[hf][16 * tb + 4 * g + e] = bq;
       }
     }
   }
 
-  // ---- outputs of the tiles (rows 16w + 4g + e)
+  // ---- outputs of the tiles (rows 16 tb + 4g + e)
   const float Dh = p.D ? p.D[h] : 0.0f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int t = 16 * w + 4 * g + e;
+    const int t = 16 * tb + 4 * g + e;
     if (t0 + t >= d.T) continue;
     const float dg = s.gam[t] - s.sc[t];
     const float dq_c = dg * s.dvd[t];
     const float dv_c = dg * s.qk[t] + Dh;
     const int64_t xrow = ((b * d.T + t0 + t) * d.H + h) * kP;
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-      const int q = 16 * pb + r;
-      IO<Act::BF16>::st(p.d_x, xrow + q, fmaf(dv_c, static_cast<float>(s.dy[t * VS + q]), dV[pb][e]));
+    for (int j = 0; j < 2; ++j) {
+      const int q = 16 * (2 * hf + j) + r;
+      IO<Act::BF16>::st(p.d_x, xrow + q, fmaf(dv_c, static_cast<float>(s.dy[t * VS + q]), dV[j][e]));
     }
     const int64_t qrow = (bh * d.T + t0 + t) * N;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = 16 * nt + r;
-      p.dQ[qrow + n] = fmaf(dq_c, static_cast<float>(s.k[t * QS + n]), dQ[nt][e]);
-      p.dK[qrow + n] = fmaf(dq_c, static_cast<float>(s.q[t * QS + n]), dK[nt][e]);
+    for (int j = 0; j < NH; ++j) {
+      const int n = 16 * (hf * NH + j) + r;
+      p.dQ[qrow + n] = fmaf(dq_c, static_cast<float>(s.k[t * QS + n]), dQ[j][e]);
+      p.dK[qrow + n] = fmaf(dq_c, static_cast<float>(s.q[t * QS + n]), dK[j][e]);
     }
   }
   __syncthreads();
-  // ---- per-step scalars (wave 0, lane = step)
+  // ---- per-step scalars (wave 0, lane = step); partial sums added in a fixed order
   if (tid < 64) {
     float cr = 0.0f, ce = 0.0f;
 #pragma unroll
@@ -489,11 +519,12 @@ __global__ void __launch_bounds__(kThreads) m3_chunk_bwd_mfma(const BwdArgs p) {
       ce += s.colE[k][tid];
     }
     float dsum = 0.0f;
-    for (int k = 0; k < kThreads; k += 64) dsum += s.red[k + tid];
+    for (int k = 0; k < kThreadsB; k += 64) dsum += s.red[k + tid];
     const float dotSS = wave_sum(dsum);
-    const float us = s.dus[tid];
+    const float tot = s.tot;
+    const float us = s.dus[0][tid] + s.dus[1][tid];
     const float u = expf_fast(tot - s.cum[tid]) * s.sc[tid];
-    const float dcum_t = s.rrow[tid] - cr + s.dcq[tid] - u * us;
+    const float dcum_t = (s.rrow[0][tid] + s.rrow[1][tid]) - cr + (s.dcq[0][tid] + s.dcq[1][tid]) - u * us;
     const float dsc_t = ce - s.qk[tid] * s.dvd[tid] + expf_fast(tot - s.cum[tid]) * us;
     const float dtot = wave_sum(u * us) + expf_fast(tot) * dotSS;
     const float dda = wave_suffix_scan(dcum_t, tid) + dtot;
