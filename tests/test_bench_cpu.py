@@ -109,3 +109,22 @@ def test_measured_traffic_is_none_for_other_sources(tree):
     assert bench.measured_traffic(wl, 16) is None
     path.unlink()
     assert bench.measured_traffic(wl, 16) is None
+
+
+def test_m3_flops_and_bytes():
+    """The Mamba-3 core's counts, by hand for the measured shape (B=4,
+    T=2048, 24 heads of 64, d_state 128, one group, 32 angles, bf16):
+    3072 chunk-heads; per chunk 2*64*(2*64*128 + 64*128 + 64*64) forward and
+    2*64*(4*64*128 + 3*64*128 + 2*64*64) backward flops."""
+    w = workloads.M3_CONFIGS["m3_siso_bf16"]
+    f, b = bench.m3_flops(w)
+    assert f == 3072 * 2 * 64 * (2 * 64 * 128 + 64 * 128 + 64 * 64)
+    assert b == 3072 * 2 * 64 * (4 * 64 * 128 + 3 * 64 * 128 + 2 * 64 * 64)
+    x = 4 * 2048 * 1536 * 2
+    bc = 2 * 4 * 2048 * 128 * 2
+    scal = 3 * 4 * 2048 * 24 * 4 + 4 * 2048 * 32 * 4
+    par = (2 * 24 * 128 + 2 * 24) * 4
+    states = 4 * 24 * 32 * 64 * 128 * 4
+    fb, bb = bench.m3_bytes(w)
+    assert fb == 2 * x + bc + scal + par + states
+    assert bb == 3 * x + 2 * (bc + scal + par) + states

@@ -87,3 +87,22 @@ def test_recurrent_mode_lines():
     for d in lines:
         assert d["higher_is_better"] is False and d["value"] > 0 and d["unit"] == "us/call"
         assert "workload" in d["config"] and d["us_per_step_graph"] > 0
+
+
+def test_m3_mode_line():
+    """--m3: the Mamba-3 core's line, its HBM roofline consistent with its
+    own fields, the matrix-core figure beside it, the oracle CPU baseline."""
+    (d,) = _run(["--m3", "m3_small_bf16", "--steps", "3", "--warmup", "1", "--cpu-budget", "2"])
+    _contract(d, 3, 1)
+    w = bench.workloads.M3_CONFIGS["m3_small_bf16"]
+    assert d["config"]["workload"] == "m3_small_bf16" and d["dtype"] == "bf16"
+    assert abs(d["value"] - w.batch * w.seqlen / (d["ms_per_step"] / 1e3)) <= 1e-3 * d["value"] + 1
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0
+    assert r["algorithmic_bytes_per_launch"] == bench.m3_bytes(w)[1]
+    assert abs(r["achieved"] - r["algorithmic_bytes_per_launch"] / (r["launch_ms"] / 1e3) / 1e9) <= 0.01 * r["achieved"] + 0.2
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    c = d["compute_roofline"]
+    assert c["bound"] == "mfma" and c["algorithmic_flops_per_launch"] == bench.m3_flops(w)[1]
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
