@@ -271,6 +271,15 @@ def layer_bench(torch, pkg, name: str, steps: int, warmup: int, no_cpu: bool, bu
                       "chunk": 16, "parallelism": "single GPU"},
            "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
            "projection_flops_per_step": layer_flops(w)}
+    # the dense products (rocBLAS, bf16 / f16 on the matrix cores) against the
+    # dense 16-bit peak; their flops over the whole step's time, so a lower
+    # bound on their own rate (they share the step with the core and the
+    # elementwise kernels; the kernel-trace profile gives their own time)
+    pt = layer_flops(w) / (ms / 1e3) / 1e12
+    res["roofline"] = {"bound": "mfma", "achieved": round(pt, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                       "frac": round(pt / 2500.0, 4), "traffic": None,
+                       "kernel": "the layer's dense products, averaged over the whole step",
+                       "algorithmic_flops_per_step": layer_flops(w)}
     if not no_cpu:
         res["cpu_baseline"] = layer_cpu_baseline(w, budget_s)
     print(json.dumps(res), flush=True)

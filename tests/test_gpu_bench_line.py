@@ -79,6 +79,9 @@ def test_layer_mode_line():
     assert d["config"]["workload"] == "layer_130m_bf16" and d["dtype"] == "bf16"
     assert d["fwd_ms"] > 0 and d["bwd_ms"] > 0 and d["fwd_ms"] + d["bwd_ms"] <= d["ms_per_step"] * 1.05
     assert d["projection_flops_per_step"] == bench.layer_flops(bench.workloads.LAYER_CONFIGS["layer_130m_bf16"])
+    r = d["roofline"]
+    assert r["bound"] == "mfma" and r["peak"] == 2500.0
+    assert abs(r["achieved"] - d["projection_flops_per_step"] / (d["ms_per_step"] / 1e3) / 1e12) <= 0.01 * r["achieved"] + 0.1
 
 
 def test_recurrent_mode_lines():
