@@ -54,9 +54,12 @@ struct LPlan {
   size_t w_dt, w_core_f, wf_total;
   // workspace: backward
   size_t w_dy, w_dgated, w_du, w_ddr, w_dz, w_dxdbl, w_dxdbl_a, w_duex, w_dx, w_dxn, w_pnorm, w_pbdt, w_pconv_w,
-      w_pconv_b, w_pwg, w_core_b, wb_total;
+      w_pconv_b, w_pwg, w_core_b, w_dtT, w_xT, wb_total;
   int64_t norm_per, norm_nblk, bdt_per, bdt_nblk, conv_nblk;
-  int64_t P_dt, P_x;   // K chunks of the dt_proj / x_proj weight products
+  int64_t P_dt, P_x, P_wide;   // K chunks of the dt_proj / x_proj / in_proj and out_proj weight products
+  // token chunks of the matrix-core dt_proj / x_proj weight products (0: the
+  // library products) and their 32-token steps per chunk
+  int64_t S_dt, S_x, S_dt_chunk, S_x_chunk;
 };
 
 // K chunks for a weight product grad[M, N] += A^T B over K token rows.  Its
@@ -69,6 +72,18 @@ int64_t wgrad_chunks(int64_t M, int64_t N, int64_t K) {
   int64_t P = (512 + tiles - 1) / tiles;
   P = P < 16 ? P : 16;
   const int64_t by_rows = K / 256;
+  P = P < by_rows ? P : by_rows;
+  return P < 1 ? 1 : P;
+}
+
+// The same for the wide weight products (in_proj, out_proj: d_model x
+// d_inner outputs): the library tiles them 128 x 64, so P aims at about 1024
+// tiles of 64 x 64 and keeps at least 512 rows per chunk.
+int64_t wgrad_chunks_wide(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  int64_t P = (1024 + tiles - 1) / tiles;
+  P = P < 8 ? P : 8;
+  const int64_t by_rows = K / 512;
   P = P < by_rows ? P : by_rows;
   return P < 1 ? 1 : P;
 }
@@ -162,14 +177,30 @@ int plan_layer(const mamba_layer_dims_t* d, const char* fn, LPlan* pl) {
   pl->w_pbdt = wb.take(static_cast<size_t>(pl->bdt_nblk) * Di * f);
   pl->w_pconv_w = wb.take(nconv * Di * static_cast<size_t>(pl->K) * f);
   pl->w_pconv_b = wb.take(nconv * Di * f);
-  // partials of the split weight products (one region, the two run in turn
-  // on one stream): P chunks plus a tail chunk when P does not divide N
+  // partials of the split weight products (one region: they run in turn on
+  // one stream): P chunks plus a tail chunk when P does not divide N
   pl->P_dt = wgrad_chunks(pl->Di, pl->R, pl->N);
   pl->P_x = wgrad_chunks(pl->X, pl->Di, pl->N);
   const size_t pdt = pl->P_dt > 1 ? static_cast<size_t>(pl->P_dt + 1) * Di * static_cast<size_t>(pl->R) : 0;
   const size_t px = pl->P_x > 1 ? static_cast<size_t>(pl->P_x + 1) * X * Di : 0;
-  pl->w_pwg = wb.take((pdt > px ? pdt : px) * f);
+  pl->P_wide = wgrad_chunks_wide(pl->Di, pl->dm, pl->N);
+  const size_t pw = pl->P_wide > 1 ? static_cast<size_t>(pl->P_wide + 1) * Di * dm : 0;
+  pl->S_dt = pl->S_x = 0;
+  if (mlayer::skinny_wgrad_supported(pl->act, pl->N, pl->Di, pl->R, pl->X))
+    pl->S_dt = mlayer::skinny_wgrad_chunks(pl->N, pl->Di, pl->R, &pl->S_dt_chunk);
+  if (mlayer::skinny_wgrad_supported(pl->act, pl->N, pl->Di, pl->X, pl->X))
+    pl->S_x = mlayer::skinny_wgrad_chunks(pl->N, pl->Di, pl->X, &pl->S_x_chunk);
+  const size_t sdt = static_cast<size_t>(pl->S_dt) * Di * static_cast<size_t>(pl->R);
+  const size_t sx = static_cast<size_t>(pl->S_x) * Di * X;
+  size_t pmax = pdt > px ? pdt : px;
+  pmax = pmax > pw ? pmax : pw;
+  pmax = pmax > sdt ? pmax : sdt;
+  pmax = pmax > sx ? pmax : sx;
+  pl->w_pwg = wb.take(pmax * f);
   pl->w_core_b = wb.take(ws);
+  // the fused x_proj / dt_proj adjoint reads W_dt and W_x transposed
+  pl->w_dtT = wb.take(static_cast<size_t>(pl->R) * Di * es);
+  pl->w_xT = wb.take(Di * mlayer::xdt_xT_stride(X) * es);
   pl->wb_total = wb.off;
   return MAMBA_OK;
 }
@@ -352,6 +383,20 @@ int wgrad(const char* fn, const char* what, rocblas_handle h, hipStream_t s, msc
   return run(fn, what, o, act, s);
 }
 
+// grad (f32, += ) from the matrix-core skinny weight product: P chunk
+// partials into a.part, then their column sum in chunk order, on stream s
+int skinny_wgrad(const char* fn, const char* what, const mlayer::SkinnyWgradArgs& a, mscan::Act act, bool j_major,
+                 hipStream_t s, float* grad, int64_t P) {
+  const hipError_t e = mlayer::launch_skinny_wgrad(a, act, j_major, s);
+  if (e != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string(what) + " launch: " + hipGetErrorString(e));
+  Op o{OpKind::ColSum};
+  o.f0 = a.part;
+  o.f3 = grad;
+  o.nblk = P;
+  o.cols = a.Di * a.J;
+  return run(fn, what, o, act, s);
+}
+
 int core_call(const char* fn, const char* what, int rc) {
   if (rc == MAMBA_OK) return rc;
   return fail(rc, fn, std::string(what) + ": " + mamba_last_error());
@@ -438,17 +483,34 @@ int mamba_layer_fwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
   o.K = static_cast<int>(pl.K);
   o.n = N * Di;
   LAYER_TRY(run(fn, "conv", o, act, st));
-  // F4b, F4c
-  LAYER_TRY(gemm(fn, "x_proj", h, false, true, N, X, Di, u, at, Di, w->w_x, at, Di, 0.0f, xdbl, xdbl, at, X));
-  LAYER_TRY(gemm(fn, "dt_proj", h, false, true, N, Di, R, xdbl, at, X, w->w_dt, at, R, 0.0f, dt, dt, f32, Di));
-  o = Op{OpKind::BiasRound};
-  o.f0 = dt;
-  o.f1 = w->b_dt;
-  o.v0 = dr;
-  o.T = pl.T;
-  o.cols = Di;
-  o.n = N * Di;
-  LAYER_TRY(run(fn, "dt bias", o, act, st));
+  // F4b, F4c: fused on the matrix cores for 16-bit activations, else two
+  // library products and the bias pass
+  mlayer::XdtArgs xa;
+  xa.u = u;
+  xa.w_x = w->w_x;
+  xa.w_dt = w->w_dt;
+  xa.b_dt = w->b_dt;
+  xa.xdbl = xdbl;
+  xa.dr = dr;
+  xa.N = N;
+  xa.Di = Di;
+  xa.X = static_cast<int>(X);
+  xa.R = static_cast<int>(R);
+  if (mlayer::xdt_supported(xa, act)) {
+    const hipError_t e = mlayer::launch_xdt_fwd(xa, act, st);
+    if (e != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("x_proj / dt_proj launch: ") + hipGetErrorString(e));
+  } else {
+    LAYER_TRY(gemm(fn, "x_proj", h, false, true, N, X, Di, u, at, Di, w->w_x, at, Di, 0.0f, xdbl, xdbl, at, X));
+    LAYER_TRY(gemm(fn, "dt_proj", h, false, true, N, Di, R, xdbl, at, X, w->w_dt, at, R, 0.0f, dt, dt, f32, Di));
+    o = Op{OpKind::BiasRound};
+    o.f0 = dt;
+    o.f1 = w->b_dt;
+    o.v0 = dr;
+    o.T = pl.T;
+    o.cols = Di;
+    o.n = N * Di;
+    LAYER_TRY(run(fn, "dt bias", o, act, st));
+  }
   // F4d/e
   LAYER_TRY(core_call(fn, "scan", mamba_scan_fwd(&pl.core, u, dr, w->a_log, xdbl, w->D, z, nullptr, gated, y,
                                                  nullptr, ckpt, W + pl.w_core_f, pl.core_ws, stream)));
@@ -550,16 +612,45 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     // start beside the rest of the adjoint
     float* gw_in_z = g->w_in + Di * dm;
     LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[0]));
-    LAYER_TRY(gemm(fn, "out_proj wgrad", hw, true, false, dm, Di, N, dy, at, dm, gated, at, Di, 1.0f, g->w_out, g->w_out,
-                   f32, Di));
-    LAYER_TRY(gemm(fn, "in_proj wgrad z", hw, true, false, Di, dm, N, d_z, at, Di, xn, at, dm, 1.0f, gw_in_z, gw_in_z, f32,
-                   dm));
-    // dt_proj adjoint: the dt columns of d_xdbl, W_dt and b_dt
-    LAYER_TRY(gemm(fn, "dt_proj dgrad", h, false, false, N, R, Di, d_dr, at, Di, w->w_dt, at, R, 0.0f, d_xdbl, d_xdbl,
-                   f32, X));
+    LAYER_TRY(wgrad(fn, "out_proj wgrad", hw, sd->s, act, dm, Di, N, dy, at, dm, gated, at, Di, pl.es, g->w_out, pwg,
+                    pl.P_wide));
+    LAYER_TRY(wgrad(fn, "in_proj wgrad z", hw, sd->s, act, Di, dm, N, d_z, at, Di, xn, at, dm, pl.es, gw_in_z, pwg,
+                    pl.P_wide));
+    // dt_proj adjoint: W_dt and b_dt here; the dt columns of d_xdbl with the
+    // x_proj adjoint below
+    mlayer::XdtArgs xa;
+    xa.w_x = w->w_x;
+    xa.w_dt = w->w_dt;
+    xa.d_dr = d_dr;
+    xa.d_xdbl = d_xdbl;
+    xa.d_xdbl_a = d_xdbl_a;
+    xa.d_uex = d_uex;
+    xa.w_dtT = W + pl.w_dtT;
+    xa.w_xT = W + pl.w_xT;
+    xa.N = N;
+    xa.Di = Di;
+    xa.X = static_cast<int>(X);
+    xa.R = static_cast<int>(R);
+    const bool fused_xdt = mlayer::xdt_supported(xa, act);
+    if (!fused_xdt)
+      LAYER_TRY(gemm(fn, "dt_proj dgrad", h, false, false, N, R, Di, d_dr, at, Di, w->w_dt, at, R, 0.0f, d_xdbl,
+                     d_xdbl, f32, X));
     LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[1]));
-    LAYER_TRY(wgrad(fn, "dt_proj wgrad", hw, sd->s, act, Di, R, N, d_dr, at, Di, xdbl, at, X, pl.es, g->w_dt, pwg,
-                    pl.P_dt));
+    if (pl.S_dt > 0) {
+      mlayer::SkinnyWgradArgs sw;
+      sw.big = d_dr;
+      sw.small = xdbl;
+      sw.part = pwg;
+      sw.N = N;
+      sw.Di = Di;
+      sw.J = R;
+      sw.lds = X;
+      sw.chunk = pl.S_dt_chunk;
+      LAYER_TRY(skinny_wgrad(fn, "dt_proj wgrad", sw, act, false, sd->s, g->w_dt, pl.S_dt));
+    } else {
+      LAYER_TRY(wgrad(fn, "dt_proj wgrad", hw, sd->s, act, Di, R, N, d_dr, at, Di, xdbl, at, X, pl.es, g->w_dt, pwg,
+                      pl.P_dt));
+    }
     o = Op{OpKind::ColPart};
     o.c0 = d_dr;
     o.f3 = pbdt;
@@ -574,17 +665,36 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     o.nblk = pl.bdt_nblk;
     o.cols = Di;
     LAYER_TRY(run(fn, "b_dt sum", o, act, st));
-    // x_proj adjoint
-    o = Op{OpKind::Cast};
-    o.f0 = d_xdbl;
-    o.v0 = d_xdbl_a;
-    o.n = N * X;
-    LAYER_TRY(run(fn, "cast d_xdbl", o, act, st));
-    LAYER_TRY(gemm(fn, "x_proj dgrad", h, false, false, N, Di, X, d_xdbl_a, at, X, w->w_x, at, Di, 0.0f, d_uex, d_uex, f32,
-                   Di));
+    // x_proj adjoint (with the dt columns of d_xdbl when fused)
+    if (fused_xdt) {
+      const hipError_t e = mlayer::launch_xdt_bwd(xa, act, st);
+      if (e != hipSuccess)
+        return fail(MAMBA_ERR_HIP, fn, std::string("dt_proj / x_proj adjoint launch: ") + hipGetErrorString(e));
+    } else {
+      o = Op{OpKind::Cast};
+      o.f0 = d_xdbl;
+      o.v0 = d_xdbl_a;
+      o.n = N * X;
+      LAYER_TRY(run(fn, "cast d_xdbl", o, act, st));
+      LAYER_TRY(gemm(fn, "x_proj dgrad", h, false, false, N, Di, X, d_xdbl_a, at, X, w->w_x, at, Di, 0.0f, d_uex, d_uex,
+                     f32, Di));
+    }
     LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[2]));
-    LAYER_TRY(wgrad(fn, "x_proj wgrad", hw, sd->s, act, X, Di, N, d_xdbl_a, at, X, u, at, Di, pl.es, g->w_x, pwg,
-                    pl.P_x));
+    if (pl.S_x > 0) {
+      mlayer::SkinnyWgradArgs sw;
+      sw.big = u;
+      sw.small = d_xdbl_a;
+      sw.part = pwg;
+      sw.N = N;
+      sw.Di = Di;
+      sw.J = X;
+      sw.lds = X;
+      sw.chunk = pl.S_x_chunk;
+      LAYER_TRY(skinny_wgrad(fn, "x_proj wgrad", sw, act, true, sd->s, g->w_x, pl.S_x));
+    } else {
+      LAYER_TRY(wgrad(fn, "x_proj wgrad", hw, sd->s, act, X, Di, N, d_xdbl_a, at, X, u, at, Di, pl.es, g->w_x, pwg,
+                      pl.P_x));
+    }
     // conv + SiLU adjoint: d_x and the weight / bias partials in one pass
     o = Op{OpKind::ConvBwd};
     o.c0 = x;
@@ -602,8 +712,8 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     LAYER_TRY(run(fn, "conv adjoint", o, act, st));
     // d_x is final here: its in_proj weight product starts beside the rest
     LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[3]));
-    LAYER_TRY(gemm(fn, "in_proj wgrad x", hw, true, false, Di, dm, N, d_x, at, Di, xn, at, dm, 1.0f, g->w_in, g->w_in, f32,
-                   dm));
+    LAYER_TRY(wgrad(fn, "in_proj wgrad x", hw, sd->s, act, Di, dm, N, d_x, at, Di, xn, at, dm, pl.es, g->w_in, pwg,
+                    pl.P_wide));
     o = Op{OpKind::ColSum};
     o.f0 = pcw;
     o.f3 = g->conv_w;

@@ -44,6 +44,51 @@ struct Op {
 
 hipError_t launch(const Op& o, mscan::Act act, hipStream_t st);
 
+// The fused x_proj -> dt_proj products (layer_mfma.hip), 16-bit activations.
+// Forward: xdbl [N, X] = round(u W_x^T), delta_raw [N, Di] = round(xdbl[:, :R]
+// W_dt^T + b_dt).  Backward: d_xdbl_a [N, X] = round([d_delta_raw W_dt |
+// the B / C columns of d_xdbl]), d_uex [N, Di] = d_xdbl_a W_x (f32), with
+// W_dt and W_x transposed into w_dtT [R, Di] and w_xT [Di, X] first.
+struct XdtArgs {
+  const void* u = nullptr;        // fwd [N, Di]
+  const void* w_x = nullptr;      // [X, Di]
+  const void* w_dt = nullptr;     // [Di, R]
+  const float* b_dt = nullptr;    // fwd [Di]
+  void* xdbl = nullptr;           // fwd out [N, X]
+  void* dr = nullptr;             // fwd out [N, Di]
+  const void* d_dr = nullptr;     // bwd [N, Di]
+  const float* d_xdbl = nullptr;  // bwd [N, X] f32 (its B / C columns)
+  void* d_xdbl_a = nullptr;       // bwd out [N, X]
+  float* d_uex = nullptr;         // bwd out [N, Di]
+  void* w_dtT = nullptr;          // bwd scratch [R, Di]
+  void* w_xT = nullptr;           // bwd scratch [Di, xdt_xT_stride(X)], zero padded
+  int64_t N = 0, Di = 0;
+  int X = 0, R = 0;
+};
+
+// row stride (elements) of the transposed x_proj weight the backward keeps
+__host__ __device__ inline int64_t xdt_xT_stride(int64_t X) { return (X + 7) / 8 * 8; }
+
+bool xdt_supported(const XdtArgs& p, mscan::Act act);
+hipError_t launch_xdt_fwd(const XdtArgs& p, mscan::Act act, hipStream_t st);
+hipError_t launch_xdt_bwd(const XdtArgs& p, mscan::Act act, hipStream_t st);
+
+// part[P][...] (f32) = per-chunk token sums of BIG[n][c] SMALL[n][j] (c <
+// Di, j < J): the gradient layout [Di][J], or [J][Di] when j_major.  BIG is
+// [N, Di], SMALL [N, lds] (its first J columns), both 16-bit; P chunks of
+// `chunk` 32-token steps.
+struct SkinnyWgradArgs {
+  const void* big = nullptr;
+  const void* small = nullptr;
+  float* part = nullptr;
+  int64_t N = 0, Di = 0, J = 0, lds = 0, chunk = 1;
+};
+
+bool skinny_wgrad_supported(mscan::Act act, int64_t N, int64_t Di, int64_t J, int64_t lds);
+// the chunk count P (and the 32-token steps per chunk)
+int64_t skinny_wgrad_chunks(int64_t N, int64_t Di, int64_t J, int64_t* chunk);
+hipError_t launch_skinny_wgrad(const SkinnyWgradArgs& p, mscan::Act act, bool j_major, hipStream_t st);
+
 // step tiles per batch row of the conv kernels (their weight partials come
 // one per batch row and tile)
 int64_t conv_step_tiles(int64_t T);

@@ -1,0 +1,179 @@
+// Weight gradients of the layer's skinny projections on the matrix cores
+// (gfx950, v_mfma_f32_16x16x32_{bf16,f16}), for 16-bit activations.
+//
+// Backward of steps F4b and F4c of the per-layer forward (mamba-rs 0.3.1
+// src/mamba_ssm/gpu/forward_mixed.rs): the dt_proj weight gradient
+// d_W_dt[c][j] = sum_n d_delta_raw[n][c] xdbl[n][j] (j < dt_rank) and the
+// x_proj one d_W_x[j][c] = sum_n d_xdbl[n][j] u[n][c] (j < X).  Both contract
+// over the N = batch * seqlen tokens a wide [N, d_inner] operand (BIG) with a
+// narrow [N, J] one (SMALL, J = 48 .. 256): bound by reading BIG once.
+//
+// A workgroup owns 64 channels x 64 columns of the result and one chunk of
+// the tokens; its 4 waves take the chunk's 32-token steps in turn.  The
+// matrix cores contract over k = tokens, so a lane needs 8 consecutive tokens
+// of one channel (column): it loads 4 neighbouring channels (8 bytes) of each
+// of its 8 tokens, coalesced along the row (16 lanes cover 128 bytes of one
+// token), and packs them into 4 operands, one per channel of the 4.  Operand
+// q of the A side then holds channels c0 + 4 i + q (i = lane % 16) and of the
+// B side columns j0 + 4 i + q; the 16 products of the 4 x 4 operands cover
+// the 64 x 64 tile.  The 4 waves' tiles meet in LDS and are added in wave
+// order, and each chunk writes its own partial (f32, in the gradient's
+// layout); a column sum adds the chunks in order onto the gradient, so no
+// result depends on timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "layer_kernels.h"
+#include "scan_common.h"
+
+namespace mlayer {
+namespace {
+
+using mscan::Act;
+
+constexpr int kWw = 4;            // waves per workgroup
+constexpr int kTw = 64 * kWw;
+constexpr int kLs = 65;           // LDS row stride (floats): the 4 lane groups of a store land on distinct banks
+
+template <Act A>
+struct Mma;
+
+template <>
+struct Mma<Act::BF16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f4 mma(const v8& a, const v8& b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<Act::F16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f4 mma(const v8& a, const v8& b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// 8 tokens x 4 neighbouring 16-bit elements (d[t].x: elements 0, 1; d[t].y:
+// 2, 3; the lower address in the low half) -> 4 operands of 8 tokens each
+template <class V8>
+__device__ __forceinline__ void pack4(const uint2 (&d)[8], V8 (&out)[4]) {
+  union U {
+    V8 v;
+    uint32_t w[4];
+  };
+  U o[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t x0 = d[2 * m].x, x1 = d[2 * m + 1].x, y0 = d[2 * m].y, y1 = d[2 * m + 1].y;
+    o[0].w[m] = (x0 & 0xffffu) | (x1 << 16);
+    o[1].w[m] = (x0 >> 16) | (x1 & 0xffff0000u);
+    o[2].w[m] = (y0 & 0xffffu) | (y1 << 16);
+    o[3].w[m] = (y0 >> 16) | (y1 & 0xffff0000u);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) out[q] = o[q].v;
+}
+
+template <Act A, bool JMajor>
+__global__ void __launch_bounds__(kTw) skinny_wgrad_kernel(const SkinnyWgradArgs p) {
+  using M = Mma<A>;
+  typedef typename M::v8 v8;
+  typedef typename M::f4 f4;
+  __shared__ float red[kWw][64 * kLs];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int G = (p.J + 63) / 64;
+  const int64_t CB = p.Di / 64;
+  int64_t bid = blockIdx.x;
+  const int grp = static_cast<int>(bid % G);
+  bid /= G;
+  const int64_t c0 = (bid % CB) * 64, pc = bid / CB;
+  const int j0 = 64 * grp;
+  const int64_t KS = (p.N + 31) / 32;
+  const int64_t ks0 = pc * p.chunk;
+  const int64_t ks1 = ks0 + p.chunk < KS ? ks0 + p.chunk : KS;
+  const uint16_t* big = static_cast<const uint16_t*>(p.big) + c0 + 4 * i;
+  const bool jok = j0 + 4 * i < p.J;
+  const uint16_t* small = static_cast<const uint16_t*>(p.small) + (jok ? j0 + 4 * i : 0);
+  f4 acc[4][4];
+#pragma unroll
+  for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) acc[qa][qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+  for (int64_t ks = ks0 + w; ks < ks1; ks += kWw) {
+    uint2 db[8], ds[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int64_t n = 32 * ks + 8 * g + t;
+      const bool ok = n < p.N;
+      db[t] = ok ? *reinterpret_cast<const uint2*>(big + n * p.Di) : make_uint2(0u, 0u);
+      ds[t] = (ok && jok) ? *reinterpret_cast<const uint2*>(small + n * p.lds) : make_uint2(0u, 0u);
+    }
+    v8 a[4], b[4];
+    pack4(db, a);
+    pack4(ds, b);
+#pragma unroll
+    for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) acc[qa][qb] = M::mma(a[qa], b[qb], acc[qa][qb]);
+  }
+  // accumulator lane (i, g), element e of product (qa, qb): channel
+  // c0 + 4 (4 g + e) + qa, column j0 + 4 i + qb; kept at LDS row
+  // 16 g + 4 e + qa, word 16 qb + i
+#pragma unroll
+  for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[w][(16 * g + 4 * e + qa) * kLs + 16 * qb + i] = acc[qa][qb][e];
+  __syncthreads();
+  float* part = p.part + pc * p.Di * p.J;
+  for (int e = threadIdx.x; e < 64 * 64; e += kTw) {
+    const int cl = JMajor ? e % 64 : e / 64, jl = JMajor ? e / 64 : e % 64;
+    if (j0 + jl >= p.J) continue;
+    const int at = cl * kLs + 16 * (jl & 3) + (jl >> 2);
+    float s = red[0][at];
+#pragma unroll
+    for (int ww = 1; ww < kWw; ++ww) s += red[ww][at];
+    if (JMajor) part[static_cast<int64_t>(j0 + jl) * p.Di + c0 + cl] = s;
+    else part[(c0 + cl) * p.J + j0 + jl] = s;
+  }
+}
+
+}  // namespace
+
+bool skinny_wgrad_supported(Act act, int64_t N, int64_t Di, int64_t J, int64_t lds) {
+  return (act == Act::BF16 || act == Act::F16) && N >= 1 && Di >= 64 && Di % 64 == 0 && J >= 4 && J % 4 == 0 &&
+         J <= lds && lds % 4 == 0;
+}
+
+int64_t skinny_wgrad_chunks(int64_t N, int64_t Di, int64_t J, int64_t* chunk) {
+  const int64_t KS = (N + 31) / 32, tiles = (Di / 64) * ((J + 63) / 64);
+  int64_t P = (512 + tiles - 1) / tiles;
+  const int64_t by_steps = KS / 8;   // at least 8 token steps (2 per wave) per chunk
+  P = P < by_steps ? P : by_steps;
+  P = P < 1 ? 1 : P;
+  const int64_t c = (KS + P - 1) / P;
+  if (chunk) *chunk = c;
+  return (KS + c - 1) / c;
+}
+
+hipError_t launch_skinny_wgrad(const SkinnyWgradArgs& p, Act act, bool j_major, hipStream_t st) {
+  const int64_t P = (((p.N + 31) / 32) + p.chunk - 1) / p.chunk;
+  const dim3 grid(static_cast<unsigned>((p.Di / 64) * ((p.J + 63) / 64) * P)), blk(kTw);
+  if (act == Act::BF16) {
+    if (j_major) hipLaunchKernelGGL((skinny_wgrad_kernel<Act::BF16, true>), grid, blk, 0, st, p);
+    else hipLaunchKernelGGL((skinny_wgrad_kernel<Act::BF16, false>), grid, blk, 0, st, p);
+  } else {
+    if (j_major) hipLaunchKernelGGL((skinny_wgrad_kernel<Act::F16, true>), grid, blk, 0, st, p);
+    else hipLaunchKernelGGL((skinny_wgrad_kernel<Act::F16, false>), grid, blk, 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mlayer

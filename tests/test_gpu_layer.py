@@ -119,7 +119,8 @@ def test_layer_segmented_core(mscan):
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_layer_split_weight_products(mscan, act):
     """1041 token rows: the dt_proj and x_proj weight products split into 4
-    chunks of 260 rows plus a 1-row tail, their partials added in order."""
+    chunks of 260 rows plus a 1-row tail, the in_proj and out_proj ones into
+    2 chunks of 520 rows plus a 1-row tail, their partials added in order."""
     w = workloads.LayerWorkload("layer_splitk_" + act, 3, 347, 64, 128, 16, 4, 4, act)
     check_layer(mscan, w)
 
@@ -129,6 +130,23 @@ def test_layer_ragged_sizes(mscan, ds, K):
     """Odd widths: d_model 50, d_inner 68 (partial channel groups), odd dt_rank."""
     w = workloads.LayerWorkload("layer_ragged_ds%d" % ds, 3, 41, 50, 68, ds, 3, K, "bf16")
     check_layer(mscan, w)
+
+
+@pytest.mark.parametrize("Di,ds,R,act", [(64, 4, 1, "bf16"), (96, 8, 3, "f16"), (128, 16, 17, "bf16"),
+                                          (160, 32, 40, "f16"), (64, 32, 63, "bf16"), (256, 16, 200, "bf16"),
+                                          (128, 32, 192, "f16"), (64, 32, 193, "bf16"), (64, 8, 4, "f16"),
+                                          (192, 4, 12, "bf16")])
+def test_layer_projection_shapes(mscan, Di, ds, R, act):
+    """d_inner a multiple of 32 with 16-bit activations, where x_proj ->
+    dt_proj and its adjoint run on the matrix cores: dt_ranks that are not
+    multiples of 8 or 16, xdbl rows (dt_rank + 2 d_state) from 9 to the
+    largest the fused kernels take (256) and one past it (257, the library
+    products); 135 token rows, so the last 16-row tile is partial.  Where
+    d_inner is a multiple of 64 and dt_rank (xdbl row) a multiple of 4, the
+    two weight gradients run on the matrix cores too (the 32-token steps end
+    in a partial one)."""
+    w = workloads.LayerWorkload("layer_proj_Di%d_R%d_%s" % (Di, R, act), 3, 45, 48, Di, ds, R, 4, act)
+    check_layer(mscan, w, seed=Di + R)
 
 
 def test_layer_deterministic_and_accumulating(mscan):
