@@ -51,15 +51,16 @@ struct LPlan {
   // saved
   size_t s_xn, s_rstd, s_x, s_z, s_u, s_xdbl, s_dr, s_gated, s_y, s_ckpt, s_total;
   // workspace: forward
-  size_t w_dt, w_core_f, wf_total;
+  size_t w_dt, w_core_f, w_xpart, wf_total;
   // workspace: backward
   size_t w_dy, w_dgated, w_du, w_ddr, w_dz, w_dxdbl, w_dxdbl_a, w_duex, w_dx, w_dxn, w_pnorm, w_pbdt, w_pconv_w,
-      w_pconv_b, w_pwg, w_core_b, w_dtT, w_xT, wb_total;
+      w_pconv_b, w_pwg, w_core_b, w_dtT, w_xT, w_xpart_b, wb_total;
   int64_t norm_per, norm_nblk, bdt_per, bdt_nblk, conv_nblk;
   int64_t P_dt, P_x, P_wide;   // K chunks of the dt_proj / x_proj / in_proj and out_proj weight products
   // token chunks of the matrix-core dt_proj / x_proj weight products (0: the
   // library products) and their 32-token steps per chunk
   int64_t S_dt, S_x, S_dt_chunk, S_x_chunk;
+  bool xdt;   // x_proj -> dt_proj (and the adjoint) on the matrix-core kernels
 };
 
 // K chunks for a weight product grad[M, N] += A^T B over K token rows.  Its
@@ -148,6 +149,17 @@ int plan_layer(const mamba_layer_dims_t* d, const char* fn, LPlan* pl) {
 
   Layout wf;
   pl->w_dt = wf.take(N * Di * f);
+  {
+    mlayer::XdtArgs q;
+    q.N = pl->N;
+    q.Di = pl->Di;
+    q.X = static_cast<int>(pl->X);
+    q.R = static_cast<int>(pl->R);
+    pl->xdt = mlayer::xdt_supported(q, pl->act);
+  }
+  // partial sums of the matrix-core x_proj (K groups x N x X)
+  const size_t xdt_G = pl->xdt ? static_cast<size_t>(mlayer::xdt_groups(pl->N, pl->Di, nullptr)) : 0;
+  pl->w_xpart = wf.take(xdt_G * N * X * f);
   pl->w_core_f = wf.take(ws);
   pl->wf_total = wf.off;
 
@@ -201,6 +213,7 @@ int plan_layer(const mamba_layer_dims_t* d, const char* fn, LPlan* pl) {
   // the fused x_proj / dt_proj adjoint reads W_dt and W_x transposed
   pl->w_dtT = wb.take(static_cast<size_t>(pl->R) * Di * es);
   pl->w_xT = wb.take(Di * mlayer::xdt_xT_stride(X) * es);
+  pl->w_xpart_b = wb.take(xdt_G * N * static_cast<size_t>(pl->R) * f);
   pl->wb_total = wb.off;
   return MAMBA_OK;
 }
@@ -492,11 +505,12 @@ int mamba_layer_fwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
   xa.b_dt = w->b_dt;
   xa.xdbl = xdbl;
   xa.dr = dr;
+  xa.part = reinterpret_cast<float*>(W + pl.w_xpart);
   xa.N = N;
   xa.Di = Di;
   xa.X = static_cast<int>(X);
   xa.R = static_cast<int>(R);
-  if (mlayer::xdt_supported(xa, act)) {
+  if (pl.xdt) {
     const hipError_t e = mlayer::launch_xdt_fwd(xa, act, st);
     if (e != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("x_proj / dt_proj launch: ") + hipGetErrorString(e));
   } else {
@@ -627,11 +641,12 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     xa.d_uex = d_uex;
     xa.w_dtT = W + pl.w_dtT;
     xa.w_xT = W + pl.w_xT;
+    xa.part = reinterpret_cast<float*>(W + pl.w_xpart_b);
     xa.N = N;
     xa.Di = Di;
     xa.X = static_cast<int>(X);
     xa.R = static_cast<int>(R);
-    const bool fused_xdt = mlayer::xdt_supported(xa, act);
+    const bool fused_xdt = pl.xdt;
     if (!fused_xdt)
       LAYER_TRY(gemm(fn, "dt_proj dgrad", h, false, false, N, R, Di, d_dr, at, Di, w->w_dt, at, R, 0.0f, d_xdbl,
                      d_xdbl, f32, X));

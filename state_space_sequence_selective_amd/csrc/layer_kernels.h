@@ -62,12 +62,41 @@ struct XdtArgs {
   float* d_uex = nullptr;         // bwd out [N, Di]
   void* w_dtT = nullptr;          // bwd scratch [R, Di]
   void* w_xT = nullptr;           // bwd scratch [Di, xdt_xT_stride(X)], zero padded
+  float* part = nullptr;          // scratch: xdt_groups(N, Di) x N x (fwd X, bwd R) f32
   int64_t N = 0, Di = 0;
   int X = 0, R = 0;
 };
 
 // row stride (elements) of the transposed x_proj weight the backward keeps
 __host__ __device__ inline int64_t xdt_xT_stride(int64_t X) { return (X + 7) / 8 * 8; }
+
+// The long product over d_inner: part[g][n][c] = sum over the 32-wide k
+// steps [g kchunk, (g + 1) kchunk) of a[n][k] b[c][k]; a [N][K], b [C][K]
+// (16-bit, rows 16-byte aligned), part f32.
+struct ContractArgs {
+  const void* a = nullptr;
+  const void* b = nullptr;
+  float* part = nullptr;
+  int64_t N = 0, K = 0;
+  int C = 0;
+  int64_t G = 1, kchunk = 1;
+};
+
+// The short product into the wide output: out[n][c] = sum_{k < kmax} x[n][k]
+// w[c][k] (+ bias[c], rounded, forward; f32, backward); x [N][ldx], w
+// [Di][ldw], out [N][Di].
+struct ExpandArgs {
+  const void* x = nullptr;
+  const void* w = nullptr;
+  const float* bias = nullptr;
+  void* out = nullptr;
+  int64_t ldx = 0, ldw = 0, N = 0, Di = 0;
+  int kmax = 0;
+  int64_t cpb = 1;   // 256-channel blocks per workgroup
+};
+
+// K groups of the long product (and its 32-wide k steps per group)
+int64_t xdt_groups(int64_t N, int64_t K, int64_t* kchunk);
 
 bool xdt_supported(const XdtArgs& p, mscan::Act act);
 hipError_t launch_xdt_fwd(const XdtArgs& p, mscan::Act act, hipStream_t st);
