@@ -132,19 +132,18 @@ def test_layer_ragged_sizes(mscan, ds, K):
     check_layer(mscan, w)
 
 
-@pytest.mark.parametrize("Di,ds,R,act", [(64, 4, 1, "bf16"), (96, 8, 3, "f16"), (128, 16, 17, "bf16"),
-                                          (160, 32, 40, "f16"), (64, 32, 63, "bf16"), (256, 16, 200, "bf16"),
-                                          (128, 32, 192, "f16"), (64, 32, 193, "bf16"), (64, 8, 4, "f16"),
-                                          (192, 4, 12, "bf16")])
+@pytest.mark.parametrize("Di,ds,R,act", [(64, 4, 8, "bf16"), (128, 8, 24, "f16"), (192, 16, 40, "bf16"),
+                                          (320, 32, 64, "f16"), (128, 16, 192, "bf16"), (64, 32, 192, "f16"),
+                                          (128, 32, 200, "bf16"), (96, 16, 48, "bf16"), (128, 16, 20, "f16")])
 def test_layer_projection_shapes(mscan, Di, ds, R, act):
-    """d_inner a multiple of 32 with 16-bit activations, where x_proj ->
-    dt_proj and its adjoint run on the matrix cores: dt_ranks that are not
-    multiples of 8 or 16, xdbl rows (dt_rank + 2 d_state) from 9 to the
-    largest the fused kernels take (256) and one past it (257, the library
-    products); 135 token rows, so the last 16-row tile is partial.  Where
-    d_inner is a multiple of 64 and dt_rank (xdbl row) a multiple of 4, the
-    two weight gradients run on the matrix cores too (the 32-token steps end
-    in a partial one)."""
+    """16-bit layers around the edges of the matrix-core projection kernels
+    (d_inner a multiple of 64, dt_rank and the xdbl row dt_rank + 2 d_state
+    multiples of 8, the row at most 256): the smallest widths, channel blocks
+    of 64 and 256 + 64 (partial 256-channel blocks), xdbl rows of 224 and 256
+    (the largest taken) and, on the library products, a row of 264, d_inner
+    96 and dt_rank 20.  135 token rows: the last 64-token block is partial.
+    The dt_proj / x_proj weight gradients run on the matrix cores wherever
+    d_inner is a multiple of 64 and dt_rank a multiple of 4."""
     w = workloads.LayerWorkload("layer_proj_Di%d_R%d_%s" % (Di, R, act), 3, 45, 48, Di, ds, R, 4, act)
     check_layer(mscan, w, seed=Di + R)
 
