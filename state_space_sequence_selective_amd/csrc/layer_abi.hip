@@ -661,6 +661,7 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
       sw.J = R;
       sw.lds = X;
       sw.chunk = pl.S_dt_chunk;
+      sw.P = pl.S_dt;
       LAYER_TRY(skinny_wgrad(fn, "dt_proj wgrad", sw, act, false, sd->s, g->w_dt, pl.S_dt));
     } else {
       LAYER_TRY(wgrad(fn, "dt_proj wgrad", hw, sd->s, act, Di, R, N, d_dr, at, Di, xdbl, at, X, pl.es, g->w_dt, pwg,
@@ -705,6 +706,7 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
       sw.J = X;
       sw.lds = X;
       sw.chunk = pl.S_x_chunk;
+      sw.P = pl.S_x;
       LAYER_TRY(skinny_wgrad(fn, "x_proj wgrad", sw, act, true, sd->s, g->w_x, pl.S_x));
     } else {
       LAYER_TRY(wgrad(fn, "x_proj wgrad", hw, sd->s, act, X, Di, N, d_xdbl_a, at, X, u, at, Di, pl.es, g->w_x, pwg,

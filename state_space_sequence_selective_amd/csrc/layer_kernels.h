@@ -111,6 +111,7 @@ struct SkinnyWgradArgs {
   const void* small = nullptr;
   float* part = nullptr;
   int64_t N = 0, Di = 0, J = 0, lds = 0, chunk = 1;
+  int64_t P = 1;   // token chunks: ceil(ceil(N / 32) / chunk)
 };
 
 bool skinny_wgrad_supported(mscan::Act act, int64_t N, int64_t Di, int64_t J, int64_t lds);

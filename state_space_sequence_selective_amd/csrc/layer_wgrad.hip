@@ -84,14 +84,18 @@ __global__ void __launch_bounds__(kTw) skinny_wgrad_kernel(const SkinnyWgradArgs
   typedef typename M::v8 v8;
   typedef typename M::f4 f4;
   __shared__ float red[kWw][64 * kLs];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int i = lane & 15, g = lane >> 4;
   const int G = (p.J + 63) / 64;
-  const int64_t CB = p.Di / 64;
-  int64_t bid = blockIdx.x;
-  const int grp = static_cast<int>(bid % G);
-  bid /= G;
-  const int64_t c0 = (bid % CB) * 64, pc = bid / CB;
+  const int64_t CB = p.Di / 64, T = CB * p.P;   // (channel block, token chunk) tiles
+  // The G column groups of a tile read the same BIG slice: give them ids 8
+  // apart (consecutive ids go to the 8 XCDs in turn) so they run on one XCD
+  // and the later ones find the slice in its L2.
+  const int64_t bid = blockIdx.x;
+  const int64_t tile = (bid / (8 * G)) * 8 + bid % 8;
+  const int grp = static_cast<int>((bid / 8) % G);
+  if (tile >= T) return;
+  const int64_t c0 = (tile % CB) * 64, pc = tile / CB;
   const int j0 = 64 * grp;
   const int64_t KS = (p.N + 31) / 32;
   const int64_t ks0 = pc * p.chunk;
@@ -104,16 +108,26 @@ __global__ void __launch_bounds__(kTw) skinny_wgrad_kernel(const SkinnyWgradArgs
   for (int qa = 0; qa < 4; ++qa)
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) acc[qa][qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 2
-  for (int64_t ks = ks0 + w; ks < ks1; ks += kWw) {
-    uint2 db[8], ds[8];
+  // One step's loads run ahead of the products.  The loads are unconditional
+  // (tokens past N reload token N - 1, the last step reloads itself); the
+  // narrow side is zeroed where it is used for tokens past N and columns past
+  // J, so no load waits on a select.
+  uint2 db[8], ds[8], dbn[8], dsn[8];
+  auto fetch = [&](int64_t ks, uint2(&b)[8], uint2(&sm)[8]) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int64_t n = 32 * ks + 8 * g + t;
-      const bool ok = n < p.N;
-      db[t] = ok ? *reinterpret_cast<const uint2*>(big + n * p.Di) : make_uint2(0u, 0u);
-      ds[t] = (ok && jok) ? *reinterpret_cast<const uint2*>(small + n * p.lds) : make_uint2(0u, 0u);
+      int64_t n = 32 * ks + 8 * g + t;
+      n = n < p.N ? n : p.N - 1;
+      b[t] = *reinterpret_cast<const uint2*>(big + n * p.Di);
+      sm[t] = *reinterpret_cast<const uint2*>(small + n * p.lds);
     }
+  };
+  if (ks0 + w < ks1) fetch(ks0 + w, db, ds);
+  for (int64_t ks = ks0 + w; ks < ks1; ks += kWw) {
+    fetch(ks + kWw < ks1 ? ks + kWw : ks, dbn, dsn);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (!jok || 32 * ks + 8 * g + t >= p.N) ds[t] = make_uint2(0u, 0u);
     v8 a[4], b[4];
     pack4(db, a);
     pack4(ds, b);
@@ -121,6 +135,11 @@ __global__ void __launch_bounds__(kTw) skinny_wgrad_kernel(const SkinnyWgradArgs
     for (int qa = 0; qa < 4; ++qa)
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) acc[qa][qb] = M::mma(a[qa], b[qb], acc[qa][qb]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      db[t] = dbn[t];
+      ds[t] = dsn[t];
+    }
   }
   // accumulator lane (i, g), element e of product (qa, qb): channel
   // c0 + 4 (4 g + e) + qa, column j0 + 4 i + qb; kept at LDS row
@@ -153,6 +172,7 @@ bool skinny_wgrad_supported(Act act, int64_t N, int64_t Di, int64_t J, int64_t l
 }
 
 int64_t skinny_wgrad_chunks(int64_t N, int64_t Di, int64_t J, int64_t* chunk) {
+  // (the launch rounds the tiles up to a multiple of 8 per column group)
   const int64_t KS = (N + 31) / 32, tiles = (Di / 64) * ((J + 63) / 64);
   int64_t P = (512 + tiles - 1) / tiles;
   const int64_t by_steps = KS / 8;   // at least 8 token steps (2 per wave) per chunk
@@ -164,8 +184,8 @@ int64_t skinny_wgrad_chunks(int64_t N, int64_t Di, int64_t J, int64_t* chunk) {
 }
 
 hipError_t launch_skinny_wgrad(const SkinnyWgradArgs& p, Act act, bool j_major, hipStream_t st) {
-  const int64_t P = (((p.N + 31) / 32) + p.chunk - 1) / p.chunk;
-  const dim3 grid(static_cast<unsigned>((p.Di / 64) * ((p.J + 63) / 64) * P)), blk(kTw);
+  const int64_t T = (p.Di / 64) * p.P;
+  const dim3 grid(static_cast<unsigned>((T + 7) / 8 * 8 * ((p.J + 63) / 64))), blk(kTw);
   if (act == Act::BF16) {
     if (j_major) hipLaunchKernelGGL((skinny_wgrad_kernel<Act::BF16, true>), grid, blk, 0, st, p);
     else hipLaunchKernelGGL((skinny_wgrad_kernel<Act::BF16, false>), grid, blk, 0, st, p);
