@@ -239,19 +239,23 @@ def layer_bench(torch, pkg, name: str, steps: int, warmup: int, no_cpu: bool, bu
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        # the current stream: the caller's here, the capture stream below
+        cur = torch.cuda.current_stream()
         layer.zero_grads()
         if ev:
-            ev[0].record(stream)
-        layer.forward(resid, stream=stream)
+            ev[0].record(cur)
+        layer.forward(resid, stream=cur)
         if ev:
-            ev[1].record(stream)
-        layer.backward(resid, d_out, stream=stream)
+            ev[1].record(cur)
+        layer.backward(resid, d_out, stream=cur)
         if ev:
-            ev[2].record(stream)
+            ev[2].record(cur)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # eager calls: each step enqueues about 50 kernels, library calls and the
+    # second stream's forks and joins from the host
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -259,17 +263,39 @@ def layer_bench(torch, pkg, name: str, steps: int, warmup: int, no_cpu: bool, bu
         step(evs[k])
     end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms_eager = start.elapsed_time(end) / steps
     fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # the same step captured once as a HIP graph and replayed: the identical
+    # kernels without the host's per-call launch work (the replay test checks
+    # replays bit for bit against the eager step)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
     tokens = w.batch * w.seqlen
     res = {"metric": "Mamba-1 layer fwd+bwd tokens/sec", "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
            "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": w.act, "data": "synthetic (seeded)",
            "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_model": w.d_model,
                       "d_inner": w.d_inner, "d_state": w.d_state, "dt_rank": w.dt_rank, "d_conv": w.d_conv,
-                      "chunk": 16, "parallelism": "single GPU"},
-           "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+                      "chunk": 16, "parallelism": "single GPU", "step": "HIP graph replay"},
+           "ms_per_step_eager": round(ms_eager, 4), "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
            "projection_flops_per_step": layer_flops(w)}
     # the dense products (rocBLAS, bf16 / f16 on the matrix cores) against the
     # dense 16-bit peak; their flops over the whole step's time, so a lower

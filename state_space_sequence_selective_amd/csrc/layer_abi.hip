@@ -54,7 +54,7 @@ struct LPlan {
   size_t w_dt, w_core_f, w_xpart, wf_total;
   // workspace: backward
   size_t w_dy, w_dgated, w_du, w_ddr, w_dz, w_dxdbl, w_dxdbl_a, w_duex, w_dx, w_dxn, w_pnorm, w_pbdt, w_pconv_w,
-      w_pconv_b, w_pwg, w_core_b, w_dtT, w_xT, w_xpart_b, wb_total;
+      w_pconv_b, w_pwg, w_core_b, w_dtT, w_xT, w_xpart_b, w_pskb, wb_total;
   int64_t norm_per, norm_nblk, bdt_per, bdt_nblk, conv_nblk;
   int64_t P_dt, P_x, P_wide;   // K chunks of the dt_proj / x_proj / in_proj and out_proj weight products
   // token chunks of the matrix-core dt_proj / x_proj weight products (0: the
@@ -214,6 +214,8 @@ int plan_layer(const mamba_layer_dims_t* d, const char* fn, LPlan* pl) {
   pl->w_dtT = wb.take(static_cast<size_t>(pl->R) * Di * es);
   pl->w_xT = wb.take(Di * mlayer::xdt_xT_stride(X) * es);
   pl->w_xpart_b = wb.take(xdt_G * N * static_cast<size_t>(pl->R) * f);
+  // the dt bias partials beside the matrix-core dt_proj weight gradient
+  pl->w_pskb = wb.take(static_cast<size_t>(pl->S_dt) * Di * f);
   pl->wb_total = wb.off;
   return MAMBA_OK;
 }
@@ -276,7 +278,7 @@ int blas_handle(const char* fn, hipStream_t st, rocblas_handle* out) {
 struct Side {
   hipStream_t s = nullptr;
   rocblas_handle h = nullptr;
-  hipEvent_t ev[5] = {};   // four forks and the join of one backward call
+  hipEvent_t ev[7] = {};   // four forks and the join of one backward call; the weight transposes' fork and end
 };
 Side g_side[64];
 
@@ -399,7 +401,7 @@ int wgrad(const char* fn, const char* what, rocblas_handle h, hipStream_t s, msc
 // grad (f32, += ) from the matrix-core skinny weight product: P chunk
 // partials into a.part, then their column sum in chunk order, on stream s
 int skinny_wgrad(const char* fn, const char* what, const mlayer::SkinnyWgradArgs& a, mscan::Act act, bool j_major,
-                 hipStream_t s, float* grad, int64_t P) {
+                 hipStream_t s, float* grad, int64_t P, float* grad_b = nullptr) {
   const hipError_t e = mlayer::launch_skinny_wgrad(a, act, j_major, s);
   if (e != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string(what) + " launch: " + hipGetErrorString(e));
   Op o{OpKind::ColSum};
@@ -407,6 +409,11 @@ int skinny_wgrad(const char* fn, const char* what, const mlayer::SkinnyWgradArgs
   o.f3 = grad;
   o.nblk = P;
   o.cols = a.Di * a.J;
+  LAYER_TRY(run(fn, what, o, act, s));
+  if (!a.part_b) return MAMBA_OK;
+  o.f0 = a.part_b;
+  o.f3 = grad_b;
+  o.cols = a.Di;
   return run(fn, what, o, act, s);
 }
 
@@ -601,6 +608,30 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     float* pwg = reinterpret_cast<float*>(W + pl.w_pwg);
     const int64_t N = pl.N, Di = pl.Di, dm = pl.dm, X = pl.X, R = pl.R;
     const char* w_in_z = static_cast<const char*>(w->w_in) + Di * dm * pl.es;
+    mlayer::XdtArgs xa;
+    xa.w_x = w->w_x;
+    xa.w_dt = w->w_dt;
+    xa.d_dr = d_dr;
+    xa.d_xdbl = d_xdbl;
+    xa.d_xdbl_a = d_xdbl_a;
+    xa.d_uex = d_uex;
+    xa.w_dtT = W + pl.w_dtT;
+    xa.w_xT = W + pl.w_xT;
+    xa.part = reinterpret_cast<float*>(W + pl.w_xpart_b);
+    xa.N = N;
+    xa.Di = Di;
+    xa.X = static_cast<int>(X);
+    xa.R = static_cast<int>(R);
+    const bool fused_xdt = pl.xdt;
+    if (fused_xdt) {
+      // the transposed weights the x_proj / dt_proj adjoint reads depend on
+      // the weights alone: they are made on the second stream while this one
+      // runs the out_proj adjoint
+      LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[5]));
+      const hipError_t e = mlayer::launch_xdt_bwd_prep(xa, act, sd->s);
+      if (e != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("weight transposes launch: ") + hipGetErrorString(e));
+      if (hipEventRecord(sd->ev[6], sd->s) != hipSuccess) return fail(MAMBA_ERR_HIP, fn, "stream fork / join failed");
+    }
 
     // out_proj adjoint (the products take typed operands)
     Op o{OpKind::Cast};
@@ -632,21 +663,6 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
                     pl.P_wide));
     // dt_proj adjoint: W_dt and b_dt here; the dt columns of d_xdbl with the
     // x_proj adjoint below
-    mlayer::XdtArgs xa;
-    xa.w_x = w->w_x;
-    xa.w_dt = w->w_dt;
-    xa.d_dr = d_dr;
-    xa.d_xdbl = d_xdbl;
-    xa.d_xdbl_a = d_xdbl_a;
-    xa.d_uex = d_uex;
-    xa.w_dtT = W + pl.w_dtT;
-    xa.w_xT = W + pl.w_xT;
-    xa.part = reinterpret_cast<float*>(W + pl.w_xpart_b);
-    xa.N = N;
-    xa.Di = Di;
-    xa.X = static_cast<int>(X);
-    xa.R = static_cast<int>(R);
-    const bool fused_xdt = pl.xdt;
     if (!fused_xdt)
       LAYER_TRY(gemm(fn, "dt_proj dgrad", h, false, false, N, R, Di, d_dr, at, Di, w->w_dt, at, R, 0.0f, d_xdbl,
                      d_xdbl, f32, X));
@@ -662,27 +678,31 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
       sw.lds = X;
       sw.chunk = pl.S_dt_chunk;
       sw.P = pl.S_dt;
-      LAYER_TRY(skinny_wgrad(fn, "dt_proj wgrad", sw, act, false, sd->s, g->w_dt, pl.S_dt));
+      sw.part_b = reinterpret_cast<float*>(W + pl.w_pskb);   // and the dt bias
+      LAYER_TRY(skinny_wgrad(fn, "dt_proj wgrad", sw, act, false, sd->s, g->w_dt, pl.S_dt, g->b_dt));
     } else {
       LAYER_TRY(wgrad(fn, "dt_proj wgrad", hw, sd->s, act, Di, R, N, d_dr, at, Di, xdbl, at, X, pl.es, g->w_dt, pwg,
                       pl.P_dt));
     }
-    o = Op{OpKind::ColPart};
-    o.c0 = d_dr;
-    o.f3 = pbdt;
-    o.rows = N;
-    o.cols = Di;
-    o.per_blk = pl.bdt_per;
-    o.nblk = pl.bdt_nblk;
-    LAYER_TRY(run(fn, "b_dt partials", o, act, st));
-    o = Op{OpKind::ColSum};
-    o.f0 = pbdt;
-    o.f3 = g->b_dt;
-    o.nblk = pl.bdt_nblk;
-    o.cols = Di;
-    LAYER_TRY(run(fn, "b_dt sum", o, act, st));
+    if (pl.S_dt == 0) {   // the dt bias (the matrix-core dt_proj weight gradient takes it beside itself)
+      o = Op{OpKind::ColPart};
+      o.c0 = d_dr;
+      o.f3 = pbdt;
+      o.rows = N;
+      o.cols = Di;
+      o.per_blk = pl.bdt_per;
+      o.nblk = pl.bdt_nblk;
+      LAYER_TRY(run(fn, "b_dt partials", o, act, st));
+      o = Op{OpKind::ColSum};
+      o.f0 = pbdt;
+      o.f3 = g->b_dt;
+      o.nblk = pl.bdt_nblk;
+      o.cols = Di;
+      LAYER_TRY(run(fn, "b_dt sum", o, act, st));
+    }
     // x_proj adjoint (with the dt columns of d_xdbl when fused)
     if (fused_xdt) {
+      if (hipStreamWaitEvent(st, sd->ev[6], 0) != hipSuccess) return fail(MAMBA_ERR_HIP, fn, "stream fork / join failed");
       const hipError_t e = mlayer::launch_xdt_bwd(xa, act, st);
       if (e != hipSuccess)
         return fail(MAMBA_ERR_HIP, fn, std::string("dt_proj / x_proj adjoint launch: ") + hipGetErrorString(e));

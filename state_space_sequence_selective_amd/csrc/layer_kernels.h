@@ -100,16 +100,21 @@ int64_t xdt_groups(int64_t N, int64_t K, int64_t* kchunk);
 
 bool xdt_supported(const XdtArgs& p, mscan::Act act);
 hipError_t launch_xdt_fwd(const XdtArgs& p, mscan::Act act, hipStream_t st);
+// the backward's transposed weights (w_dtT, w_xT) from w_dt and w_x; before
+// launch_xdt_bwd
+hipError_t launch_xdt_bwd_prep(const XdtArgs& p, mscan::Act act, hipStream_t st);
 hipError_t launch_xdt_bwd(const XdtArgs& p, mscan::Act act, hipStream_t st);
 
 // part[P][...] (f32) = per-chunk token sums of BIG[n][c] SMALL[n][j] (c <
 // Di, j < J): the gradient layout [Di][J], or [J][Di] when j_major.  BIG is
 // [N, Di], SMALL [N, lds] (its first J columns), both 16-bit; P chunks of
-// `chunk` 32-token steps.
+// `chunk` 32-token steps.  With part_b (not j_major): part_b[P][Di] = the
+// per-chunk token sums of BIG[n][c] (a column of ones past SMALL's J).
 struct SkinnyWgradArgs {
   const void* big = nullptr;
   const void* small = nullptr;
   float* part = nullptr;
+  float* part_b = nullptr;
   int64_t N = 0, Di = 0, J = 0, lds = 0, chunk = 1;
   int64_t P = 1;   // token chunks: ceil(ceil(N / 32) / chunk)
 };

@@ -420,12 +420,7 @@ hipError_t xdt_fwd(const XdtArgs& p, hipStream_t st) {
 
 template <Act A>
 hipError_t xdt_bwd(const XdtArgs& p, hipStream_t st) {
-  // W_dt [Di][R] -> [R][Di]; W_x [X][Di] -> [Di][Xp], zero padded
   const int64_t Xp = xdt_xT_stride(p.X);
-  hipError_t e = transpose16(p.w_dt, p.w_dtT, p.Di, p.R, p.Di, st);
-  if (e != hipSuccess) return e;
-  e = transpose16(p.w_x, p.w_xT, p.X, p.Di, Xp, st);
-  if (e != hipSuccess) return e;
   int64_t kchunk = 1;
   const int64_t G = xdt_groups(p.N, p.Di, &kchunk);
   ContractArgs c;
@@ -437,7 +432,7 @@ hipError_t xdt_bwd(const XdtArgs& p, hipStream_t st) {
   c.C = p.R;
   c.G = G;
   c.kchunk = kchunk;
-  e = launch_contract<A>(c, st);
+  hipError_t e = launch_contract<A>(c, st);
   if (e != hipSuccess) return e;
   e = launch_round<A>(p.part, p.d_xdbl, p.d_xdbl_a, p.N, p.R, p.X, static_cast<int>(G), st);
   if (e != hipSuccess) return e;
@@ -475,6 +470,13 @@ bool xdt_supported(const XdtArgs& p, Act act) {
 
 hipError_t launch_xdt_fwd(const XdtArgs& p, Act act, hipStream_t st) {
   return act == Act::BF16 ? xdt_fwd<Act::BF16>(p, st) : xdt_fwd<Act::F16>(p, st);
+}
+
+hipError_t launch_xdt_bwd_prep(const XdtArgs& p, Act, hipStream_t st) {
+  // W_dt [Di][R] -> [R][Di]; W_x [X][Di] -> [Di][Xp], zero padded
+  const hipError_t e = transpose16(p.w_dt, p.w_dtT, p.Di, p.R, p.Di, st);
+  if (e != hipSuccess) return e;
+  return transpose16(p.w_x, p.w_xT, p.X, p.Di, xdt_xT_stride(p.X), st);
 }
 
 hipError_t launch_xdt_bwd(const XdtArgs& p, Act act, hipStream_t st) {

@@ -19,7 +19,9 @@
 // the 64 x 64 tile.  The 4 waves' tiles meet in LDS and are added in wave
 // order, and each chunk writes its own partial (f32, in the gradient's
 // layout); a column sum adds the chunks in order onto the gradient, so no
-// result depends on timing.
+// result depends on timing.  With part_b, column J of SMALL is taken as all
+// ones: its products are the column sums of BIG (the dt bias gradient beside
+// the dt_proj weight gradient), written to part_b[P][Di].
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -86,7 +88,8 @@ __global__ void __launch_bounds__(kTw) skinny_wgrad_kernel(const SkinnyWgradArgs
   __shared__ float red[kWw][64 * kLs];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int i = lane & 15, g = lane >> 4;
-  const int G = (p.J + 63) / 64;
+  const int64_t Jt = p.J + (p.part_b ? 1 : 0);   // columns computed
+  const int G = static_cast<int>((Jt + 63) / 64);
   const int64_t CB = p.Di / 64, T = CB * p.P;   // (channel block, token chunk) tiles
   // The G column groups of a tile read the same BIG slice: give them ids 8
   // apart (consecutive ids go to the 8 XCDs in turn) so they run on one XCD
@@ -102,6 +105,9 @@ __global__ void __launch_bounds__(kTw) skinny_wgrad_kernel(const SkinnyWgradArgs
   const int64_t ks1 = ks0 + p.chunk < KS ? ks0 + p.chunk : KS;
   const uint16_t* big = static_cast<const uint16_t*>(p.big) + c0 + 4 * i;
   const bool jok = j0 + 4 * i < p.J;
+  // the lane whose 4 columns start at J, when J is the ones column
+  const bool jone = p.part_b != nullptr && j0 + 4 * i == p.J;
+  const uint32_t one = A == Act::BF16 ? 0x3f80u : 0x3c00u;   // 1.0
   const uint16_t* small = static_cast<const uint16_t*>(p.small) + (jok ? j0 + 4 * i : 0);
   f4 acc[4][4];
 #pragma unroll
@@ -126,8 +132,10 @@ __global__ void __launch_bounds__(kTw) skinny_wgrad_kernel(const SkinnyWgradArgs
   for (int64_t ks = ks0 + w; ks < ks1; ks += kWw) {
     fetch(ks + kWw < ks1 ? ks + kWw : ks, dbn, dsn);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      if (!jok || 32 * ks + 8 * g + t >= p.N) ds[t] = make_uint2(0u, 0u);
+    for (int t = 0; t < 8; ++t) {
+      if (!jok) ds[t] = make_uint2(jone ? one : 0u, 0u);
+      if (32 * ks + 8 * g + t >= p.N) ds[t] = make_uint2(0u, 0u);
+    }
     v8 a[4], b[4];
     pack4(db, a);
     pack4(ds, b);
@@ -154,12 +162,13 @@ __global__ void __launch_bounds__(kTw) skinny_wgrad_kernel(const SkinnyWgradArgs
   float* part = p.part + pc * p.Di * p.J;
   for (int e = threadIdx.x; e < 64 * 64; e += kTw) {
     const int cl = JMajor ? e % 64 : e / 64, jl = JMajor ? e / 64 : e % 64;
-    if (j0 + jl >= p.J) continue;
+    if (j0 + jl >= Jt) continue;
     const int at = cl * kLs + 16 * (jl & 3) + (jl >> 2);
     float s = red[0][at];
 #pragma unroll
     for (int ww = 1; ww < kWw; ++ww) s += red[ww][at];
-    if (JMajor) part[static_cast<int64_t>(j0 + jl) * p.Di + c0 + cl] = s;
+    if (j0 + jl == p.J) p.part_b[pc * p.Di + c0 + cl] = s;
+    else if (JMajor) part[static_cast<int64_t>(j0 + jl) * p.Di + c0 + cl] = s;
     else part[(c0 + cl) * p.J + j0 + jl] = s;
   }
 }
@@ -173,7 +182,7 @@ bool skinny_wgrad_supported(Act act, int64_t N, int64_t Di, int64_t J, int64_t l
 
 int64_t skinny_wgrad_chunks(int64_t N, int64_t Di, int64_t J, int64_t* chunk) {
   // (the launch rounds the tiles up to a multiple of 8 per column group)
-  const int64_t KS = (N + 31) / 32, tiles = (Di / 64) * ((J + 63) / 64);
+  const int64_t KS = (N + 31) / 32, tiles = (Di / 64) * ((J + 64) / 64);
   int64_t P = (512 + tiles - 1) / tiles;
   const int64_t by_steps = KS / 8;   // at least 8 token steps (2 per wave) per chunk
   P = P < by_steps ? P : by_steps;
@@ -184,8 +193,8 @@ int64_t skinny_wgrad_chunks(int64_t N, int64_t Di, int64_t J, int64_t* chunk) {
 }
 
 hipError_t launch_skinny_wgrad(const SkinnyWgradArgs& p, Act act, bool j_major, hipStream_t st) {
-  const int64_t T = (p.Di / 64) * p.P;
-  const dim3 grid(static_cast<unsigned>((T + 7) / 8 * 8 * ((p.J + 63) / 64))), blk(kTw);
+  const int64_t T = (p.Di / 64) * p.P, Jt = p.J + (p.part_b ? 1 : 0);
+  const dim3 grid(static_cast<unsigned>((T + 7) / 8 * 8 * ((Jt + 63) / 64))), blk(kTw);
   if (act == Act::BF16) {
     if (j_major) hipLaunchKernelGGL((skinny_wgrad_kernel<Act::BF16, true>), grid, blk, 0, st, p);
     else hipLaunchKernelGGL((skinny_wgrad_kernel<Act::BF16, false>), grid, blk, 0, st, p);

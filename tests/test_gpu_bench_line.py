@@ -77,7 +77,8 @@ def test_layer_mode_line():
     (d,) = _run(["--layer", "layer_130m_bf16", "--steps", "3", "--warmup", "1", "--no-cpu-baseline"])
     _contract(d, 3, 1)
     assert d["config"]["workload"] == "layer_130m_bf16" and d["dtype"] == "bf16"
-    assert d["fwd_ms"] > 0 and d["bwd_ms"] > 0 and d["fwd_ms"] + d["bwd_ms"] <= d["ms_per_step"] * 1.05
+    assert d["fwd_ms"] > 0 and d["bwd_ms"] > 0 and d["fwd_ms"] + d["bwd_ms"] <= d["ms_per_step_eager"] * 1.05
+    assert 0 < d["ms_per_step"] <= d["ms_per_step_eager"] * 1.05 and d["config"]["step"] == "HIP graph replay"
     assert d["projection_flops_per_step"] == bench.layer_flops(bench.workloads.LAYER_CONFIGS["layer_130m_bf16"])
     r = d["roofline"]
     assert r["bound"] == "mfma" and r["peak"] == 2500.0

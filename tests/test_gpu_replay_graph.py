@@ -130,3 +130,36 @@ def test_decode_chain_replays(mscan):
     assert torch.equal(h[steps], core.h_last)
     g = _capture(chain)
     _replay_and_compare(g, tensors, ref)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_layer_step_replays(mscan, act):
+    """zero_grads + mamba_layer_fwd + mamba_layer_bwd captured as one graph:
+    the library products, the weight-gradient products forked onto the
+    second stream and joined back, the column sums and (bf16) the
+    matrix-core projection and weight-gradient kernels.  1041 token rows, so
+    the wide weight products take their K split with a 1-row tail."""
+    w = workloads.LayerWorkload("graph_layer_" + act, 3, 347, 96, 192, 16, 8, 4, act)
+    inp = workloads.make_layer_inputs(w, 13)
+    at = {"f32": torch.float32, "bf16": torch.bfloat16}[act]
+    weights = {n: torch.from_numpy(np.ascontiguousarray(inp[n])).to("cuda", at if n in mscan.LAYER_TYPED else
+                                                                      torch.float32) for n in mscan.LAYER_PARAMS}
+    dims = mscan.LayerDims.make(w.batch, w.seqlen, w.d_model, w.d_inner, w.d_state, w.dt_rank, w.d_conv, 16, w.act)
+    layer = mscan.MambaLayer(dims, weights)
+    resid = torch.from_numpy(inp["resid"]).cuda()
+    d_out = torch.from_numpy(inp["d_resid_out"]).cuda()
+
+    def step():
+        layer.zero_grads()
+        layer.forward(resid)
+        layer.backward(resid, d_out)
+
+    step()
+    torch.cuda.synchronize()
+    outs = {"resid_out": layer.resid_out, "d_resid_in": layer.d_resid_in}
+    outs.update({"d_" + k: v for k, v in layer.grads.items()})
+    ref = {k: v.clone() for k, v in outs.items()}
+    for k, t in ref.items():
+        assert torch.isfinite(t).all(), k
+    g = _capture(step)
+    _replay_and_compare(g, outs, ref)
