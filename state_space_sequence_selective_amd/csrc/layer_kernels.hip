@@ -358,6 +358,8 @@ __global__ void __launch_bounds__(kThreads) colpart_kernel(const void* __restric
 // workgroup: wave w sums the w-th of four contiguous runs of blocks in
 // ascending order, then the four run sums are added in run order (a fixed
 // order, so the result does not vary between runs)
+constexpr int kFewBlocks = 8;   // colsum_few_kernel's most blocks
+
 __global__ void __launch_bounds__(kThreads) colsum_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                          int64_t nblk, int64_t cols) {
   constexpr int NW = kThreads / 64;
@@ -375,6 +377,34 @@ __global__ void __launch_bounds__(kThreads) colsum_kernel(const float* __restric
     for (int w = 1; w < NW; ++w) t += run[w][lane];
     out[j] += t;
   }
+}
+
+// The same sum for a few blocks over many columns (the K-split weight
+// products' partials): one thread per 4 columns adds the blocks in
+// ascending order, 16-byte accesses.
+__global__ void __launch_bounds__(kThreads) colsum_few_kernel(const float4* __restrict__ part, float4* __restrict__ out,
+                                                             int64_t nblk, int64_t cols4) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (j >= cols4) return;
+  float4 v[kFewBlocks];
+#pragma unroll
+  for (int b = 0; b < kFewBlocks; ++b)
+    if (b < nblk) v[b] = part[b * cols4 + j];
+  float4 t = v[0];
+#pragma unroll
+  for (int b = 1; b < kFewBlocks; ++b)
+    if (b < nblk) {
+      t.x += v[b].x;
+      t.y += v[b].y;
+      t.z += v[b].z;
+      t.w += v[b].w;
+    }
+  float4 o = out[j];
+  o.x += t.x;
+  o.y += t.y;
+  o.z += t.z;
+  o.w += t.w;
+  out[j] = o;
 }
 
 __global__ void __launch_bounds__(kThreads) zero_kernel(float* __restrict__ p, int64_t n) {
@@ -443,6 +473,12 @@ hipError_t launch(const Op& o, Act act, hipStream_t st) {
                          o.f0, o.f1, o.f2, o.f3, o.rows, o.cols, o.per_blk);
       return hipGetLastError();
     case OpKind::ColSum:
+      if (o.nblk >= 1 && o.nblk <= kFewBlocks && o.cols % 4 == 0 && reinterpret_cast<uintptr_t>(o.f0) % 16 == 0 &&
+          reinterpret_cast<uintptr_t>(o.f3) % 16 == 0) {
+        hipLaunchKernelGGL(colsum_few_kernel, grid1(o.cols / 4), blk, 0, st, reinterpret_cast<const float4*>(o.f0),
+                           reinterpret_cast<float4*>(o.f3), o.nblk, o.cols / 4);
+        return hipGetLastError();
+      }
       hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>((o.cols + 63) / 64)), blk, 0, st, o.f0, o.f3,
                          o.nblk, o.cols);
       return hipGetLastError();
