@@ -163,141 +163,214 @@ __global__ void __launch_bounds__(kThreads) rmsnorm_wgrad_part_kernel(const floa
   part[blk * dm + j] = acc;
 }
 
-// Tiles of the conv kernels: a workgroup walks kConvTT steps of one batch
-// row for 256 channels, the conv window in registers, so each input is read
-// once (plus a K-1 step halo).  Block id = (b * ntb + tb) * nchb + channel
-// block, ntb = ceil(T / kConvTT).
-constexpr int kConvTT = 64;
-constexpr int kConvU = 8;   // steps whose inputs are loaded together
-
-struct ConvTile {
-  int64_t b, t0, t1, i;
-};
-
-__device__ __forceinline__ bool conv_tile(int64_t T, int64_t Di, unsigned nchb, unsigned ntb, ConvTile* c) {
-  const unsigned cbk = blockIdx.x % nchb, rest = blockIdx.x / nchb;
-  c->i = static_cast<int64_t>(cbk) * kThreads + threadIdx.x;
-  if (c->i >= Di) return false;
-  c->b = rest / ntb;
-  c->t0 = static_cast<int64_t>(rest % ntb) * kConvTT;
-  c->t1 = c->t0 + kConvTT < T ? c->t0 + kConvTT : T;
-  return true;
+// Four consecutive elements e .. e+3 of an activation as f32 (e % 4 == 0;
+// the buffer 16-byte aligned, so the 8 or 16 bytes are aligned).
+template <Act A>
+__device__ __forceinline__ float4 ld4(const void* p, int64_t e);
+template <>
+__device__ __forceinline__ float4 ld4<Act::F32>(const void* p, int64_t e) {
+  return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + e);
+}
+template <>
+__device__ __forceinline__ float4 ld4<Act::BF16>(const void* p, int64_t e) {
+  const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + e);
+  return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                     __uint_as_float(r.y & 0xffff0000u));
+}
+template <>
+__device__ __forceinline__ float4 ld4<Act::F16>(const void* p, int64_t e) {
+  struct alignas(8) H4 {
+    _Float16 h[4];
+  };
+  const H4 q = *reinterpret_cast<const H4*>(static_cast<const _Float16*>(p) + e);
+  return make_float4(static_cast<float>(q.h[0]), static_cast<float>(q.h[1]), static_cast<float>(q.h[2]),
+                     static_cast<float>(q.h[3]));
 }
 
-// F4a: u_t = SiLU(b + sum_k w[i,k] x_{t-(K-1-k)}), zero history.  win[m] holds
-// x_{t-1-m}; tap k < K-1 reads win[K-2-k], tap K-1 reads x_t.
-template <Act A>
+__device__ __forceinline__ float4 f4zero() { return make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
+
+// Tiles of the conv kernels: the conv is a short stencil in time (K <= 4
+// taps), so every output is computed independently from global memory (the
+// K - 1 halo rows a neighbouring thread also reads come from the caches) and
+// the kernels have no loop over time.  A thread takes 4 channels (8- or
+// 16-byte accesses) x kConvS consecutive steps; a workgroup 64 channels x
+// kConvTT steps of one batch row.  Block id = (b * ntb + tb) * ncb + channel
+// block, ntb = ceil(T / kConvTT), ncb = ceil(d_inner / 64).
+constexpr int kConvS = 8;                                 // steps per thread
+constexpr int kConvCQ = 16;                               // channel quads per workgroup
+constexpr int kConvTT = (kThreads / kConvCQ) * kConvS;   // steps per workgroup: 128
+
+struct ConvTile {
+  int64_t b, tb, s0, i0;   // batch row, step block, first step, first channel
+  bool on;                 // the thread has channels and steps
+};
+
+__device__ __forceinline__ ConvTile conv_tile(int64_t T, int64_t Di, unsigned ncb, unsigned ntb) {
+  ConvTile c;
+  const unsigned cbk = blockIdx.x % ncb, rest = blockIdx.x / ncb;
+  c.b = rest / ntb;
+  c.tb = rest % ntb;
+  const int cq = threadIdx.x % kConvCQ, tg = threadIdx.x / kConvCQ;
+  c.i0 = static_cast<int64_t>(cbk) * (4 * kConvCQ) + 4 * cq;
+  c.s0 = c.tb * kConvTT + tg * kConvS;
+  c.on = c.i0 < Di && c.s0 < T;
+  return c;
+}
+
+// the conv weights of channels i0 .. i0+3 per tap and their bias
+template <int K>
+__device__ __forceinline__ void conv_weights(const float* cw, const float* cb, int64_t i0, float4 (&w)[K],
+                                             float4& bias) {
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    w[k] = make_float4(cw[i0 * K + k], cw[(i0 + 1) * K + k], cw[(i0 + 2) * K + k], cw[(i0 + 3) * K + k]);
+  bias = *reinterpret_cast<const float4*>(cb + i0);
+}
+
+// rows t0 .. t0 + R - 1 of 4 channels (zero before the sequence start; rows
+// past the end reload the last row: their values are not used)
+template <Act A, int R>
+__device__ __forceinline__ void conv_rows(const void* p, int64_t rb, int64_t t0, int64_t T, int64_t Di, int64_t i0,
+                                          float4 (&r)[R]) {
+#pragma unroll
+  for (int m = 0; m < R; ++m) {
+    const int64_t t = t0 + m;
+    const int64_t tc = t < 0 ? 0 : (t < T ? t : T - 1);
+    r[m] = ld4<A>(p, (rb + tc) * Di + i0);
+    if (t < 0) r[m] = f4zero();
+  }
+}
+
+// conv pre-activation b + sum_k w[k] x_{t-(K-1)+k} of 4 channels, xw[k] =
+// x_{t-(K-1)+k}
+template <int K>
+__device__ __forceinline__ float4 conv_pre(const float4 (&w)[K], const float4& bias, const float4* xw) {
+  float4 p = bias;
+#pragma unroll
+  for (int k = K - 1; k >= 0; --k) {
+    p.x = fmaf(w[k].x, xw[k].x, p.x);
+    p.y = fmaf(w[k].y, xw[k].y, p.y);
+    p.z = fmaf(w[k].z, xw[k].z, p.z);
+    p.w = fmaf(w[k].w, xw[k].w, p.w);
+  }
+  return p;
+}
+
+// F4a: u_t = SiLU(b + sum_k w[i,k] x_{t-(K-1-k)}), zero history.
+template <Act A, int K>
 __global__ void __launch_bounds__(kThreads) conv_silu_fwd_kernel(const void* __restrict__ x,
                                                                 const float* __restrict__ cw,
                                                                 const float* __restrict__ cb, void* __restrict__ u,
-                                                                int64_t T, int64_t Di, int K, unsigned nchb,
-                                                                unsigned ntb) {
-  ConvTile c;
-  if (!conv_tile(T, Di, nchb, ntb, &c)) return;
-  float w[4] = {0.0f, 0.0f, 0.0f, 0.0f}, win[3] = {0.0f, 0.0f, 0.0f};
-  for (int k = 0; k < K; ++k) w[k] = cw[c.i * K + k];
-  const float bias = cb[c.i];
-  const int64_t base = c.b * T * Di + c.i;
-  for (int m = 0; m < K - 1; ++m)
-    if (c.t0 - 1 - m >= 0) win[m] = IO<A>::ld(x, base + (c.t0 - 1 - m) * Di);
-  // kConvU steps' inputs are loaded before any is used (addresses clamped to
-  // the tile, so every load is unconditional): several loads in flight per
-  // thread instead of one round trip per step
-  for (int64_t t0 = c.t0; t0 < c.t1; t0 += kConvU) {
-    float xs[kConvU];
+                                                                int64_t T, int64_t Di, unsigned ncb, unsigned ntb) {
+  const ConvTile c = conv_tile(T, Di, ncb, ntb);
+  if (!c.on) return;
+  float4 w[K], bias;
+  conv_weights<K>(cw, cb, c.i0, w, bias);
+  const int64_t rb = c.b * T;
+  float4 xr[kConvS + K - 1];   // x_{s0-(K-1)} .. x_{s0+kConvS-1}
+  conv_rows<A>(x, rb, c.s0 - (K - 1), T, Di, c.i0, xr);
 #pragma unroll
-    for (int j = 0; j < kConvU; ++j) xs[j] = IO<A>::ld(x, base + (t0 + j < c.t1 ? t0 + j : c.t1 - 1) * Di);
-#pragma unroll
-    for (int j = 0; j < kConvU; ++j) {
-      if (t0 + j < c.t1) {
-        const float xt = xs[j];
-        float p = fmaf(w[K - 1], xt, bias);
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-          if (k < K - 1) p = fmaf(w[k], win[K - 2 - k], p);
-        IO<A>::st(u, base + (t0 + j) * Di, p * mscan::sigmoid(p));
-        win[2] = win[1];
-        win[1] = win[0];
-        win[0] = xt;
-      }
+  for (int j = 0; j < kConvS; ++j) {
+    const int64_t t = c.s0 + j;
+    if (t < T) {
+      const float4 p = conv_pre<K>(w, bias, xr + j);
+      st4<A>(u, (rb + t) * Di + c.i0,
+             make_float4(p.x * mscan::sigmoid(p.x), p.y * mscan::sigmoid(p.y), p.z * mscan::sigmoid(p.z),
+                         p.w * mscan::sigmoid(p.w)));
     }
   }
 }
 
-// Adjoint of F4a in one pass over a tile, forward in time:
-//   dp_t   = (d_u_t + d_u_extra_t) * silu'(p_t)          (p_t recomputed)
-//   d_x_s  = sum_k w[i,k] dp_{s+K-1-k}, emitted at t = s + K-1 as
-//            sum_k w[i,k] dp_{t-k} (dpw[k] holds dp_{t-k})
-//   part_w[blk, i, k] = sum_t dp_t x_{t-(K-1-k)},  part_b[blk, i] = sum_t dp_t
-// The K-1 steps after the tile are recomputed for the d_x of its last steps
-// (they enter no weight partial); past the sequence end dp is zero.
-template <Act A>
+__device__ __forceinline__ float dsilu(float p, float g) {
+  const float sg = mscan::sigmoid(p);
+  return g * (sg * (1.0f + p * (1.0f - sg)));
+}
+
+// Adjoint of F4a for a thread's 4 channels x kConvS steps s:
+//   dp_t  = (d_u_t + d_u_extra_t) * silu'(p_t)      (p_t recomputed; zero past T)
+//   d_x_s = sum_k w[i,k] dp_{s+K-1-k}               (dp for t in [s0, s0+kConvS+K-2])
+//   weight partials over the thread's own t = s: sum dp_t x_{t-(K-1-k)}, sum dp_t;
+// the 16 step groups of a workgroup are added in order through LDS, one
+// partial per (batch row, step block).
+template <Act A, int K>
 __global__ void __launch_bounds__(kThreads) conv_bwd_kernel(const void* __restrict__ x, const float* __restrict__ cw,
                                                            const float* __restrict__ cb, const void* __restrict__ du,
                                                            const float* __restrict__ du_extra,
                                                            void* __restrict__ dx, float* __restrict__ part_w,
-                                                           float* __restrict__ part_b, int64_t T, int64_t Di, int K,
-                                                           unsigned nchb, unsigned ntb) {
-  ConvTile c;
-  if (!conv_tile(T, Di, nchb, ntb, &c)) return;
-  float w[4] = {0.0f, 0.0f, 0.0f, 0.0f}, win[3] = {0.0f, 0.0f, 0.0f}, dpw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc_b = 0.0f;
-  for (int k = 0; k < K; ++k) w[k] = cw[c.i * K + k];
-  const float bias = cb[c.i];
-  const int64_t base = c.b * T * Di + c.i;
-  for (int m = 0; m < K - 1; ++m)
-    if (c.t0 - 1 - m >= 0) win[m] = IO<A>::ld(x, base + (c.t0 - 1 - m) * Di);
-  const int64_t t_stop = c.t1 + (K - 1);                  // last emitted d_x is step t1 - 1
-  const int64_t t_data = t_stop < T ? t_stop : T;          // steps with data
-  for (int64_t t0 = c.t0; t0 < t_stop; t0 += kConvU) {
-    // kConvU steps' inputs first (clamped to the data, so unconditional)
-    float xs[kConvU], gs[kConvU];
+                                                           float* __restrict__ part_b, int64_t T, int64_t Di,
+                                                           unsigned ncb, unsigned ntb) {
+  __shared__ float4 s_red[K + 1][kThreads];   // [tap k | bias][thread]: the thread's partials of its 4 channels
+  const ConvTile c = conv_tile(T, Di, ncb, ntb);
+  float4 acc[K + 1];   // taps, then the bias
 #pragma unroll
-    for (int j = 0; j < kConvU; ++j) {
-      const int64_t e = base + (t0 + j < t_data ? t0 + j : t_data - 1) * Di;
-      xs[j] = IO<A>::ld(x, e);
-      gs[j] = IO<A>::ld(du, e) + du_extra[e];
+  for (int k = 0; k <= K; ++k) acc[k] = f4zero();
+  if (c.on) {
+    float4 w[K], bias;
+    conv_weights<K>(cw, cb, c.i0, w, bias);
+    const int64_t rb = c.b * T;
+    constexpr int ND = kConvS + K - 1;   // dp_t for t = s0 .. s0 + ND - 1
+    float4 xr[ND + K - 1];                // x_{s0-(K-1)} .. x_{s0+ND-1}
+    conv_rows<A>(x, rb, c.s0 - (K - 1), T, Di, c.i0, xr);
+    float4 g0[ND];
+    conv_rows<A>(du, rb, c.s0, T, Di, c.i0, g0);
+    float4 dp[ND];
+#pragma unroll
+    for (int r = 0; r < ND; ++r) {
+      const int64_t t = c.s0 + r;
+      const int64_t tc = t < T ? t : T - 1;
+      const float4 g1 = *reinterpret_cast<const float4*>(du_extra + (rb + tc) * Di + c.i0);
+      const float4 p = conv_pre<K>(w, bias, xr + r);
+      dp[r] = make_float4(dsilu(p.x, g0[r].x + g1.x), dsilu(p.y, g0[r].y + g1.y), dsilu(p.z, g0[r].z + g1.z),
+                          dsilu(p.w, g0[r].w + g1.w));
+      if (t >= T) dp[r] = f4zero();
     }
 #pragma unroll
-    for (int j = 0; j < kConvU; ++j) {
-      const int64_t t = t0 + j;
-      if (t >= t_stop) break;
-      float g = 0.0f;
-      if (t < t_data) {
-        const float xt = xs[j];
-        float p = fmaf(w[K - 1], xt, bias);
+    for (int j = 0; j < kConvS; ++j) {
+      const int64_t s = c.s0 + j;
+      if (s < T) {
+        float4 gx = f4zero();
 #pragma unroll
-        for (int k = 0; k < 3; ++k)
-          if (k < K - 1) p = fmaf(w[k], win[K - 2 - k], p);
-        const float sg = mscan::sigmoid(p);
-        g = gs[j] * (sg * (1.0f + p * (1.0f - sg)));
-        if (t < c.t1) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            if (k < K) acc[k] = fmaf(g, k == K - 1 ? xt : win[K - 2 - k], acc[k]);
-          acc_b += g;
+        for (int k = 0; k < K; ++k) {
+          const float4 dk = dp[j + K - 1 - k];
+          gx.x = fmaf(w[k].x, dk.x, gx.x);
+          gx.y = fmaf(w[k].y, dk.y, gx.y);
+          gx.z = fmaf(w[k].z, dk.z, gx.z);
+          gx.w = fmaf(w[k].w, dk.w, gx.w);
         }
-        win[2] = win[1];
-        win[1] = win[0];
-        win[0] = xt;
-      }
-      dpw[3] = dpw[2];
-      dpw[2] = dpw[1];
-      dpw[1] = dpw[0];
-      dpw[0] = g;
-      const int64_t s = t - (K - 1);
-      if (s >= c.t0 && s < T) {
-        float gx = 0.0f;
+        st4<A>(dx, (rb + s) * Di + c.i0, gx);
+        // step t = s: tap k saw x_{t-(K-1)+k} = xr[j + k]
+        const float4 g = dp[j];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (k < K) gx = fmaf(w[k], dpw[k], gx);
-        IO<A>::st(dx, base + s * Di, gx);
+        for (int k = 0; k < K; ++k) {
+          acc[k].x = fmaf(g.x, xr[j + k].x, acc[k].x);
+          acc[k].y = fmaf(g.y, xr[j + k].y, acc[k].y);
+          acc[k].z = fmaf(g.z, xr[j + k].z, acc[k].z);
+          acc[k].w = fmaf(g.w, xr[j + k].w, acc[k].w);
+        }
+        acc[K].x += g.x;
+        acc[K].y += g.y;
+        acc[K].z += g.z;
+        acc[K].w += g.w;
       }
     }
   }
-  const int64_t blk = static_cast<int64_t>(blockIdx.x / nchb);   // b * ntb + tb
-  for (int k = 0; k < K; ++k) part_w[(blk * Di + c.i) * K + k] = acc[k];
-  part_b[blk * Di + c.i] = acc_b;
+#pragma unroll
+  for (int k = 0; k <= K; ++k) s_red[k][threadIdx.x] = acc[k];
+  __syncthreads();
+  // 64 channels x (K taps + bias): the 16 step groups added in order
+  const unsigned cbk = blockIdx.x % ncb;
+  const int64_t blk = c.b * ntb + c.tb;
+  const float* red = reinterpret_cast<const float*>(&s_red[0][0]);
+  for (int e = threadIdx.x; e < (K + 1) * 4 * kConvCQ; e += kThreads) {
+    const int k = e / (4 * kConvCQ), ch = e % (4 * kConvCQ);   // tap (K: bias), channel in the block
+    const int64_t i = static_cast<int64_t>(cbk) * (4 * kConvCQ) + ch;
+    if (i >= Di) continue;
+    // thread tg * kConvCQ + ch / 4 holds channel ch as component ch % 4
+    float t = 0.0f;
+    for (int tg = 0; tg < kThreads / kConvCQ; ++tg) t += red[(k * kThreads + tg * kConvCQ) * 4 + ch];
+    if (k < K) part_w[(blk * Di + i) * K + k] = t;
+    else part_b[blk * Di + i] = t;
+  }
 }
 
 // F4c tail: delta_raw = round(dt + b_dt[i]), four channels per thread
@@ -414,8 +487,8 @@ __global__ void __launch_bounds__(kThreads) zero_kernel(float* __restrict__ p, i
 
 dim3 grid1(int64_t n) { return dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)); }
 
-// channel blocks of 256 threads per row (conv kernels)
-unsigned nchb(const Op& o) { return static_cast<unsigned>((o.cols + kThreads - 1) / kThreads); }
+// channel blocks of 64 per row (conv kernels)
+unsigned nchb(const Op& o) { return static_cast<unsigned>((o.cols + 4 * kConvCQ - 1) / (4 * kConvCQ)); }
 // blocks of 256 four-channel groups per row (dt bias)
 unsigned nq4(const Op& o) { return static_cast<unsigned>((o.cols + 4 * kThreads - 1) / (4 * kThreads)); }
 // one wave per row (RMSNorm)
@@ -433,12 +506,30 @@ hipError_t dispatch(const Op& o, hipStream_t st) {
                          o.cols, o.eps);
       break;
     case OpKind::ConvSiluFwd:
-      hipLaunchKernelGGL(conv_silu_fwd_kernel<A>, grid_conv(o), blk, 0, st, o.c0, o.f0, o.f1, o.v0, o.T, o.cols, o.K,
-                         nchb(o), ntb(o));
+      switch (o.K) {
+#define CONV_FWD(KK)                                                                                                \
+  case KK:                                                                                                          \
+    hipLaunchKernelGGL((conv_silu_fwd_kernel<A, KK>), grid_conv(o), blk, 0, st, o.c0, o.f0, o.f1, o.v0, o.T, o.cols, \
+                       nchb(o), ntb(o));                                                                            \
+    break;
+        CONV_FWD(1) CONV_FWD(2) CONV_FWD(3) CONV_FWD(4)
+#undef CONV_FWD
+        default:
+          return hipErrorInvalidValue;
+      }
       break;
     case OpKind::ConvBwd:
-      hipLaunchKernelGGL(conv_bwd_kernel<A>, grid_conv(o), blk, 0, st, o.c0, o.f0, o.f1, o.c1, o.f2, o.v0, o.f3, o.f6,
-                         o.T, o.cols, o.K, nchb(o), ntb(o));
+      switch (o.K) {
+#define CONV_BWD(KK)                                                                                                \
+  case KK:                                                                                                          \
+    hipLaunchKernelGGL((conv_bwd_kernel<A, KK>), grid_conv(o), blk, 0, st, o.c0, o.f0, o.f1, o.c1, o.f2, o.v0, o.f3, \
+                       o.f6, o.T, o.cols, nchb(o), ntb(o));                                                          \
+    break;
+        CONV_BWD(1) CONV_BWD(2) CONV_BWD(3) CONV_BWD(4)
+#undef CONV_BWD
+        default:
+          return hipErrorInvalidValue;
+      }
       break;
     case OpKind::BiasRound:
       hipLaunchKernelGGL(bias_round_kernel<A>, dim3(static_cast<unsigned>(o.n / o.cols) * nq4(o)), blk, 0, st, o.f0,
