@@ -131,14 +131,28 @@ scan_fwd2_kernel(const Fwd2Args p) {
 #pragma unroll
     for (int n = 0; n < DS; ++n) h[n] = 0.0f;
   } else {
+    // h0 folded through the (sum of delta, end state) pairs of segments
+    // 0 .. seg-1 in order.  QU segments' loads are issued before their FMAs
+    // (indexes past seg-1 clamped, their values unused), so the fold waits
+    // about seg / QU memory round trips rather than one per segment and state.
+    constexpr int QU = DS <= 16 ? 64 / DS : (DS == 32 ? 2 : 1);
 #pragma unroll
-    for (int n = 0; n < DS; ++n) {
-      float hv = p.h0 ? p.h0[(b * Di + ic) * DS + n] : 0.0f;
-      for (int64_t q = 0; q < seg; ++q) {
-        const int64_t r = b * p.S + q;
-        hv = fmaf(exp2_fast(a2[n] * p.seg_sd[r * Di + ic]), hv, p.seg_h[(r * DS + n) * Di + ic]);
+    for (int n = 0; n < DS; ++n) h[n] = p.h0 ? p.h0[(b * Di + ic) * DS + n] : 0.0f;
+    for (int64_t q0 = 0; q0 < seg; q0 += QU) {
+      float sd[QU], hs[QU][DS];
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        const int64_t r = b * p.S + (q0 + u < seg ? q0 + u : seg - 1);
+        sd[u] = p.seg_sd[r * Di + ic];
+#pragma unroll
+        for (int n = 0; n < DS; ++n) hs[u][n] = p.seg_h[(r * DS + n) * Di + ic];
       }
-      h[n] = hv;
+#pragma unroll
+      for (int u = 0; u < QU; ++u)
+        if (q0 + u < seg) {
+#pragma unroll
+          for (int n = 0; n < DS; ++n) h[n] = fmaf(exp2_fast(a2[n] * sd[u]), h[n], hs[u][n]);
+        }
     }
   }
   const float Dv = (MODE == kFwdMain && p.D) ? p.D[ic] : 0.0f;

@@ -124,12 +124,17 @@ def _check_all(core, w, f, g, rep, nonfinite=False):
 
 
 def run_case(m, oracle_lib, w, seed=0, chunk=0, h0=False, conv_state0=False, d_u_extra=False, D=True,
-             segments=0, inp=None, nonfinite=False):
+             segments=0, inp=None, nonfinite=False, unaligned=()):
     if inp is None:
         inp = workloads.make_inputs(w, seed, h0=h0, conv_state0=conv_state0, d_u_extra=d_u_extra)
     if not D:
         inp["D"] = None
     dev = _device_inputs(w, inp)
+    for k in unaligned:   # the same values one element past an allocation's (256-byte aligned) start
+        t = dev[k]
+        buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+        dev[k] = buf[1:1 + t.numel()].view(t.shape)
+        dev[k].copy_(t)
     dims = _dims(m, w, chunk, segments)
     core = m.LayerCore(dims, gate=w.gate, keep_u=True)
     core.zero_grads()
@@ -169,6 +174,14 @@ def test_scan_gate_ragged(mscan, oracle_lib, act):
 def test_fused_ragged_states_and_extras(mscan, oracle_lib, act):
     w = workloads.Workload("fused_ragged_" + act, 2, 45, 68, 16, 5, 4, act, True)
     run_case(mscan, oracle_lib, w, chunk=16, h0=True, conv_state0=True, d_u_extra=True)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16", "f32"])
+def test_fused_unaligned_extra_gradient(mscan, oracle_lib, act):
+    """d_u_extra one element past an aligned start: the entry asks of it only
+    its element alignment, so the conv adjoint must read it element-wise."""
+    w = workloads.Workload("fused_unaligned_" + act, 2, 150, 68, 16, 5, 4, act, True)
+    run_case(mscan, oracle_lib, w, chunk=16, h0=True, conv_state0=True, d_u_extra=True, unaligned=("d_u_extra",))
 
 
 @pytest.mark.parametrize("ds,chunk", [(4, 32), (4, 16), (8, 32), (8, 16), (16, 16), (32, 16), (64, 16), (64, 64),
