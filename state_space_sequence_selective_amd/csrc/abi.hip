@@ -24,6 +24,7 @@ hipError_t launch_carry_f32(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_carry_bf16(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_carry_f16(const CarryArgs& p, int ds, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& p, hipStream_t st);
+hipError_t launch_carry_fold(const CarryFoldArgs& p, hipStream_t st);
 hipError_t launch_conv_bwd_f32(const ConvBwdArgs& p, hipStream_t st);
 hipError_t launch_conv_bwd_bf16(const ConvBwdArgs& p, hipStream_t st);
 hipError_t launch_conv_bwd_f16(const ConvBwdArgs& p, hipStream_t st);
@@ -117,9 +118,11 @@ struct Plan {
   int esize;      // bytes per activation element
   int bulk_align; // alignment of activation inputs staged with 4 / 16-byte granules
   int Sf, Sb;     // segments of the forward / backward schedule
+  int Fb;         // sub-segments per backward segment in the carry pass
   int64_t segf_steps;   // steps per forward segment (a multiple of 16)
   int64_t segb_tiles;   // Lb-step tiles per backward segment
   bool regen() const { return Lb != L; }
+  int Sc() const { return Sb * Fb; }   // carry sub-segments
 };
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;
@@ -172,6 +175,24 @@ void choose_segments_bwd(int hint, int64_t waves, int64_t resident, int64_t ntil
   s = s < 1 ? 1 : s;
   *per = (ntiles + s - 1) / s;
   *S = static_cast<int>((ntiles + *per - 1) / *per);
+}
+
+// Sub-segments per backward segment in the carry pass.  Its grid is one
+// workgroup per 32 channels of a batch row (`groups`) and sub-segment after
+// the first segment; with whole segments it can leave the CUs short of
+// waves (576 workgroups at batch 4, d_inner 1536, 4 segments: 0.40 ns per
+// element against 0.23 with a full grid).  Halve the sub-segments until
+// about 8 workgroups per CU are queued, keeping at least kCarryMinTiles
+// 16-step tiles each.
+constexpr int64_t kCarryWantWgs = 2048;
+constexpr int64_t kCarryMinTiles = 4;
+
+int carry_split(int64_t groups, int S, int64_t seg_steps) {
+  if (S < 2) return 1;
+  const int64_t tiles = seg_steps / 16;
+  int64_t f = 1;
+  while (groups * (S - 1) * f < kCarryWantWgs && tiles % (2 * f) == 0 && tiles / (2 * f) >= kCarryMinTiles) f *= 2;
+  return static_cast<int>(f);
 }
 
 // Forward segments (one single-wave workgroup per 64 channels of a batch
@@ -273,6 +294,7 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
     const int64_t resident =
         1024 * static_cast<int64_t>(mscan::bwd_waves_per_simd(static_cast<int>(d->d_state), pl->Lb, fused));
     choose_segments_bwd(d->segments, waves_b, resident, pl->nCb, &pl->Sb, &pl->segb_tiles);
+    pl->Fb = carry_split(pl->nG * d->batch, pl->Sb, pl->segb_tiles * pl->Lb);
   }
   // a launch holds at most 2^32 - 1 threads: the forward and backward (all
   // segments in one grid), the checkpoint regeneration and the reduction
@@ -314,9 +336,10 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace layouts.  Forward: [bc | seg_h | seg_sd], the last two when
 // segmented (nothing for the short-sequence step kernel).  Backward:
-// [part_bc | part_par | seg_q | seg_sd | bc | sub | du | part_conv], seg_q
-// and seg_sd when segmented, bc and sub when the checkpoints are
-// regenerated, du and part_conv for the fused entry.
+// [part_bc | part_par | seg_q | seg_sd | seg_c | bc | sub | du | part_conv],
+// seg_q, seg_sd (per carry sub-segment) and seg_c (per segment) when
+// segmented, bc and sub when the checkpoints are regenerated, du and
+// part_conv for the fused entry.
 size_t seg_state_bytes(const Plan& pl, int S) { return align256(sizeof(float) * pl.B * S * pl.Di * pl.Ds); }
 size_t seg_sum_bytes(const Plan& pl, int S) { return align256(sizeof(float) * pl.B * S * pl.Di); }
 size_t par_part_bytes(const Plan& pl) { return align256(sizeof(float) * pl.Sb * pl.B * pl.Di * param_width(pl)); }
@@ -336,7 +359,7 @@ size_t workspace_need_fwd(const Plan& pl) {
 
 size_t workspace_need_bwd(const Plan& pl) {
   return align256(bc_part_bytes(pl)) + par_part_bytes(pl) +
-         (pl.Sb > 1 ? seg_state_bytes(pl, pl.Sb) + seg_sum_bytes(pl, pl.Sb) : 0) +
+         (pl.Sb > 1 ? seg_state_bytes(pl, pl.Sc()) + seg_sum_bytes(pl, pl.Sc()) + seg_state_bytes(pl, pl.Sb) : 0) +
          (pl.regen() ? bc_f32_bytes(pl) + sub_ckpt_bytes(pl) : 0) + du_bytes(pl) + conv_part_bytes(pl);
 }
 
@@ -534,8 +557,11 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   float* part_par = reinterpret_cast<float*>(ws + align256(bc_part_bytes(pl)));
   char* after_par = ws + align256(bc_part_bytes(pl)) + par_part_bytes(pl);
   float* seg_q = reinterpret_cast<float*>(after_par);
-  float* seg_sd = reinterpret_cast<float*>(after_par + seg_state_bytes(pl, pl.Sb));
-  char* after_seg = after_par + (pl.Sb > 1 ? seg_state_bytes(pl, pl.Sb) + seg_sum_bytes(pl, pl.Sb) : 0);
+  float* seg_sd = reinterpret_cast<float*>(after_par + seg_state_bytes(pl, pl.Sc()));
+  float* seg_c = reinterpret_cast<float*>(after_par + seg_state_bytes(pl, pl.Sc()) + seg_sum_bytes(pl, pl.Sc()));
+  char* after_seg = after_par + (pl.Sb > 1 ? seg_state_bytes(pl, pl.Sc()) + seg_sum_bytes(pl, pl.Sc()) +
+                                                 seg_state_bytes(pl, pl.Sb)
+                                           : 0);
   const int PW = static_cast<int>(param_width(pl));
   hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -593,10 +619,23 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
     c.Di = pl.Di;
     c.R = pl.R;
     c.X = pl.X;
-    c.seg_steps = pl.segb_tiles * pl.Lb;
-    c.S = pl.Sb;
+    c.seg_steps = pl.segb_tiles * pl.Lb / pl.Fb;
+    c.S = pl.Sc();
+    c.first = pl.Fb;
     hipError_t err = mscan::launch_carry(c, pl.act, static_cast<int>(pl.Ds), st);
     if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("carry launch: ") + hipGetErrorString(err));
+    mscan::CarryFoldArgs fo{};
+    fo.a_log = a_log;
+    fo.seg_q = seg_q;
+    fo.seg_sd = seg_sd;
+    fo.seg_c = seg_c;
+    fo.B = pl.B;
+    fo.Di = pl.Di;
+    fo.Ds = pl.Ds;
+    fo.S = pl.Sb;
+    fo.F = pl.Fb;
+    err = mscan::launch_carry_fold(fo, st);
+    if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("carry fold launch: ") + hipGetErrorString(err));
   }
 
   mscan::BwdArgs a{};
@@ -629,10 +668,7 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   a.PW = PW;
   a.S = pl.Sb;
   a.seg_tiles = pl.segb_tiles;
-  if (pl.Sb > 1) {
-    a.seg_q = seg_q;
-    a.seg_sd = seg_sd;
-  }
+  if (pl.Sb > 1) a.seg_c = seg_c;
   hipError_t err = mscan::launch_bwd(a, pl.act, static_cast<int>(pl.Ds), pl.Lb, st);
   if (err != hipSuccess) return fail(MAMBA_ERR_HIP, fn, std::string("backward launch: ") + hipGetErrorString(err));
   if (pl.K > 0) {   // the conv + SiLU adjoint over the d_u just written

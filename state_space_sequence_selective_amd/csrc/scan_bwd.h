@@ -197,15 +197,12 @@ scan_bwd_kernel(const BwdArgs p) {
     const int n = g * SPL + s;
     an[s] = on ? -expf(p.a_log[i * DS + n]) : 0.0f;
     a2[s] = an[s] * kLog2e;
-    float cv = 0.0f;
-    if (on) {
-      for (int64_t q = p.S - 1; q > seg; --q) {   // carry handed back by the later segments
-        const int64_t r = b * p.S + q;
-        cv = fmaf(exp2_fast(a2[s] * p.seg_sd[r * Di + i]), cv, p.seg_q[(r * Di + i) * DS + n]);
-      }
-    }
-    carry[s] = cv;
+    carry[s] = 0.0f;
     dacc[s] = 0.0f;
+  }
+  if (on && p.S > 1) {   // the carry handed back by the later segments (mscan_carry_fold_kernel)
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) carry[s] = p.seg_c[((b * p.S + seg) * Di + i) * DS + g * SPL + s];
   }
   const float Dv = (on && p.D) ? p.D[i] : 0.0f;
   float cw[KMAX];

@@ -7,8 +7,11 @@
 //   Q + (prod_{t in [a,b)} dA_t) * (carry arriving at step b-1),
 // where Q is the segment's own sweep from a zero carry and the product is
 // exp(A * sum of delta).  This kernel computes Q and the sum of delta for
-// segments 1 .. S-1 (segment 0 hands nothing on); the main backward folds
-// the pairs of the later segments into its starting carry.
+// the sub-segments first .. S-1 (the main backward's segments cut into
+// equal sub-segments, so that this pass has workgroups enough to fill the
+// chip; those of the first segment hand nothing on); the main backward
+// folds the pairs of the sub-segments after its own segment into its
+// starting carry.
 //
 // Mapping as in the main backward: a workgroup owns CPW channels of one
 // batch row and one segment; thread (g, c) runs states [g*SPL, (g+1)*SPL)
@@ -49,7 +52,7 @@ scan_bwd_carry_kernel(const CarryArgs p) {
   constexpr int NW = NT / 64;
   const int64_t ngrp = (p.Di + CPW - 1) / CPW;
   const int64_t nwg = ngrp * p.B;
-  const int64_t seg = 1 + blockIdx.x / nwg;
+  const int64_t seg = p.first + blockIdx.x / nwg;
   const int64_t wg = xcd_group_map<line_sharing_groups<ES, CPW>()>(blockIdx.x % nwg, nwg);
   const int64_t b = wg / ngrp;
   const int64_t i0 = (wg % ngrp) * CPW;
@@ -152,12 +155,12 @@ static hipError_t launch_carry_t(const CarryArgs& p, hipStream_t st) {
   constexpr int CPW = kBwdCpw;
   constexpr int G = DS / SPL;
   const int64_t nwg = (p.Di + CPW - 1) / CPW * p.B;
-  dim3 grid(static_cast<unsigned>(nwg * (p.S - 1)));
+  dim3 grid(static_cast<unsigned>(nwg * (p.S - p.first)));
   hipLaunchKernelGGL((scan_bwd_carry_kernel<A, DS, SPL, CPW>), grid, dim3(CPW * G), 0, st, p);
   return hipGetLastError();
 }
 
-// segments 1 .. S-1 (S > 1)
+// sub-segments first .. S-1 (first < S)
 template <Act A>
 hipError_t launch_carry_a(const CarryArgs& p, int ds, hipStream_t st) {
   if (ds == 4) return launch_carry_t<A, 4, 1>(p, st);

@@ -291,8 +291,7 @@ struct BwdArgs {
   float* part_bc;           // [nG, B*T, 2*Ds]: per channel-group sums of d_B | d_C
   float* part_par;          // [S, B, Di, PW]: per segment and batch row d_a_log | d_D
   // segmented schedule: segment s covers tiles [s * seg_tiles, ...) of L steps
-  const float* seg_q;       // [B,S,Di,Ds] carry each segment hands to earlier steps, from a zero start
-  const float* seg_sd;      // [B,S,Di] sum of delta over each segment
+  const float* seg_c;       // [B,S,Di,Ds] carry entering each segment's reverse sweep (S > 1)
   int64_t B, T, Di, R, X, nC;
   int64_t seg_tiles;        // tiles per segment
   int K;
@@ -311,8 +310,20 @@ struct CarryArgs {
   float* seg_q;             // [B,S,Di,Ds] out
   float* seg_sd;            // [B,S,Di] out
   int64_t B, T, Di, R, X;
-  int64_t seg_steps;        // steps per segment (a multiple of 16)
-  int S;
+  int64_t seg_steps;        // steps per (sub-)segment (a multiple of 16)
+  int S;                    // sub-segments
+  int first;                // the first sub-segment computed (those before it hand nothing on)
+};
+
+// the carry pass's sub-segment pairs folded into each segment's starting carry
+struct CarryFoldArgs {
+  const float* a_log;       // [Di,Ds]
+  const float* seg_q;       // [B,S*F,Di,Ds]
+  const float* seg_sd;      // [B,S*F,Di]
+  float* seg_c;             // [B,S,Di,Ds] out
+  int64_t B, Di, Ds;
+  int S;                    // segments
+  int F;                    // sub-segments per segment
 };
 
 struct ReduceArgs {

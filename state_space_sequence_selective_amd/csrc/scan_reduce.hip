@@ -2,7 +2,9 @@
 // row) / per-(batch row, conv tile) partials into the caller's accumulated
 // gradients (d_xdbl B/C columns, d_a_log, d_D, d_conv_w, d_conv_b).  No
 // atomics: every output element is summed by one thread in ascending
-// group / row order, so repeated runs give identical bits.
+// group / row order, so repeated runs give identical bits.  Also the fold
+// of the segmented backward's carry pairs into each segment's starting
+// carry, in a fixed order too.
 #include "scan_common.h"
 
 namespace mscan {
@@ -65,6 +67,48 @@ __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
   const float acc = ordered_sum(p.part_conv + i * CW + slot, p.conv_rows, p.Di * CW);
   if (slot < p.K) p.d_conv_w[i * p.K + slot] += acc;
   else p.d_conv_b[i] += acc;
+}
+
+// Starting carry of every backward segment from the carry pass's
+// sub-segment pairs (Q_q, sum of delta_q), folded from the last sub-segment
+// down as  c <- exp2(A log2(e) sum of delta_q) c + Q_q;  the value after
+// sub-segment s*F is what segment s-1 starts its reverse sweep from, and
+// the last segment starts from zero.  One thread per (batch row, channel,
+// state), states fastest; QU sub-segments' loads are issued before their
+// FMAs (indexes past the range clamped, their values unused).
+__global__ void __launch_bounds__(256) mscan_carry_fold_kernel(const CarryFoldArgs p) {
+  constexpr int QU = 8;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t DD = p.Di * p.Ds;
+  if (j >= p.B * DD) return;
+  const int64_t b = j / DD, in = j % DD, i = in / p.Ds;
+  const float a2 = -expf(p.a_log[in]) * kLog2e;
+  const int64_t SF = static_cast<int64_t>(p.S) * p.F;
+  p.seg_c[(b * p.S + p.S - 1) * DD + in] = 0.0f;
+  float c = 0.0f;
+  for (int64_t q0 = SF - 1; q0 >= p.F; q0 -= QU) {
+    float sd[QU], qv[QU];
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int64_t r = b * SF + (q0 - u >= p.F ? q0 - u : p.F);
+      sd[u] = p.seg_sd[r * p.Di + i];
+      qv[u] = p.seg_q[r * DD + in];
+    }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int64_t q = q0 - u;
+      if (q >= p.F) {
+        c = fmaf(exp2_fast(a2 * sd[u]), c, qv[u]);
+        if (q % p.F == 0) p.seg_c[(b * p.S + q / p.F - 1) * DD + in] = c;
+      }
+    }
+  }
+}
+
+hipError_t launch_carry_fold(const CarryFoldArgs& p, hipStream_t st) {
+  const int64_t n = p.B * p.Di * p.Ds;
+  hipLaunchKernelGGL(mscan_carry_fold_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce(const ReduceArgs& p, hipStream_t st) {

@@ -104,23 +104,28 @@ def test_segments_range(pkg, segments):
 
 def test_segmented_workspace_layout(pkg):
     # B=1, T=1024, Di=64, Ds=16, L=16: 64 checkpoint tiles, 64 forward tiles;
-    # four segments each way
+    # four segments each way.  The carry pass has 2 channel groups x 3 later
+    # segments = 6 workgroups, so it halves each 256-step segment down to
+    # 4 sub-segments of 64 steps (4 tiles, the least it cuts to): seg_q and
+    # seg_sd hold 16 sub-segments, seg_c (the folded carry) 4 segments.
     d = _dims(pkg, batch=1, seqlen=1024, chunk=16, segments=4)
     al = lambda x: (x + 255) // 256 * 256
     fwd = al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)                  # seg_h | seg_sd
     bwd = (al(2 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4)          # part_bc | part_par (4 segments)
-           + al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4))              # seg_q | seg_sd
+           + al(1 * 16 * 64 * 16 * 4) + al(1 * 16 * 64 * 4)             # seg_q | seg_sd (16 sub-segments)
+           + al(1 * 4 * 64 * 16 * 4))                                    # seg_c
     assert pkg.workspace_bytes(d) == max(fwd, bwd)
-    # a cap above the tile count gives one segment per tile
+    # a cap above the tile count gives one segment per tile (too short to split)
     d = _dims(pkg, batch=1, seqlen=64, chunk=16, segments=4096)
     fwd = al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
-    bwd = al(2 * 1 * 64 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
+    bwd = (al(2 * 1 * 64 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4) + al(1 * 4 * 64 * 4)
+           + al(1 * 4 * 64 * 16 * 4))
     assert pkg.workspace_bytes(d) == max(fwd, bwd)
     # the fused backward segments like the scan one and adds d_u (f32) and
     # the conv partials per (batch row, 64-step tile)
     d = _dims(pkg, batch=1, seqlen=1024, chunk=16, segments=4, d_conv=4)
-    bwd_fused = (al(2 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 4 * 64 * 16 * 4)
-                 + al(1 * 4 * 64 * 4) + al(1 * 1024 * 64 * 4) + al(1 * 16 * 64 * 5 * 4))
+    bwd_fused = (al(2 * 1 * 1024 * 32 * 4) + al(4 * 1 * 64 * 17 * 4) + al(1 * 16 * 64 * 16 * 4)
+                 + al(1 * 16 * 64 * 4) + al(1 * 4 * 64 * 16 * 4) + al(1 * 1024 * 64 * 4) + al(1 * 16 * 64 * 5 * 4))
     assert pkg.workspace_bytes(d) == bwd_fused
 
 

@@ -296,6 +296,16 @@ def test_segments_chosen_for_a_small_grid(mscan, oracle_lib):
     run_case(mscan, oracle_lib, w, chunk=16, h0=True)
 
 
+@pytest.mark.parametrize("act,segments,K", [("f32", 2, 0), ("bf16", 4, 0), ("f16", 4, 4)])
+def test_segments_carry_split(mscan, oracle_lib, act, segments, K):
+    """One batch row of 64 channels and long segments: the carry pass has
+    too few workgroups with whole segments and cuts each into sub-segments
+    (16 of 64 steps at 2 segments, 8 at 4), whose pairs the main backward
+    folds."""
+    w = workloads.Workload("seg_split_%s_%d" % (act, K), 1, 2048, 64, 16, 4, K, act, True)
+    run_case(mscan, oracle_lib, w, chunk=16, h0=True, conv_state0=K > 0, segments=segments)
+
+
 def test_segments_deterministic(mscan, oracle_lib):
     w = workloads.Workload("seg_det", 2, 300, 100, 16, 0, 0, "bf16", True)
     core, dev, inp, f, g = run_case(mscan, oracle_lib, w, chunk=16, segments=5)
