@@ -377,20 +377,22 @@ def m3_bench(torch, pkg, name: str, steps: int, warmup: int, no_cpu: bool, budge
     stream = torch.cuda.current_stream()
 
     def step(k, ev=None):
+        cur = torch.cuda.current_stream()   # the capture stream while a graph is captured
         dev = sets[k % len(sets)]
         core.zero_grads()
         if ev:
-            ev[0].record(stream)
-        core.forward(dev, stream=stream)
+            ev[0].record(cur)
+        core.forward(dev, stream=cur)
         if ev:
-            ev[1].record(stream)
-        core.backward(dev, dev["dy"], stream=stream)
+            ev[1].record(cur)
+        core.backward(dev, dev["dy"], stream=cur)
         if ev:
-            ev[2].record(stream)
+            ev[2].record(cur)
 
     for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
+    # eager calls: each step enqueues about 25 kernels from the host
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -398,9 +400,36 @@ def m3_bench(torch, pkg, name: str, steps: int, warmup: int, no_cpu: bool, budge
         step(warmup + k, evs[k])
     end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms_eager = start.elapsed_time(end) / steps
     fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # the same step captured as a HIP graph, one per input set, and the K
+    # steps replayed in the eager order: the identical kernels without the
+    # host's per-call launch work (the replay test checks replays bit for bit
+    # against the eager step)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for k in range(len(sets)):
+            step(k)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for k in range(len(sets)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(k)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for k in range(warmup):
+        graphs[k % len(graphs)].replay()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(steps):
+        graphs[(warmup + k) % len(graphs)].replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
     tokens = w.batch * w.seqlen
     ff, fb = m3_flops(w)
     bf, bb = m3_bytes(w)
@@ -417,8 +446,8 @@ def m3_bench(torch, pkg, name: str, steps: int, warmup: int, no_cpu: bool, budge
            "data": "synthetic (seeded; %d input sets rotated)" % len(sets),
            "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "heads": w.heads,
                       "headdim": w.headdim, "d_state": w.d_state, "groups": w.groups, "n_angles": w.n_angles,
-                      "chunk": 64, "parallelism": "single GPU"},
-           "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+                      "chunk": 64, "parallelism": "single GPU", "step": "HIP graph replay"},
+           "ms_per_step_eager": round(ms_eager, 4), "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
            "hbm_GBps": round((bf + bb) / (ms / 1e3) / 1e9, 1),
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,

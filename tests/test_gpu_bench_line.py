@@ -101,6 +101,8 @@ def test_m3_mode_line():
     w = bench.workloads.M3_CONFIGS["m3_small_bf16"]
     assert d["config"]["workload"] == "m3_small_bf16" and d["dtype"] == "bf16"
     assert abs(d["value"] - w.batch * w.seqlen / (d["ms_per_step"] / 1e3)) <= 1e-3 * d["value"] + 1
+    assert d["fwd_ms"] > 0 and d["bwd_ms"] > 0 and d["fwd_ms"] + d["bwd_ms"] <= d["ms_per_step_eager"] * 1.05
+    assert 0 < d["ms_per_step"] <= d["ms_per_step_eager"] * 1.05 and d["config"]["step"] == "HIP graph replay"
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0
     assert r["algorithmic_bytes_per_launch"] == bench.m3_bytes(w)[1]

@@ -163,3 +163,35 @@ def test_layer_step_replays(mscan, act):
         assert torch.isfinite(t).all(), k
     g = _capture(step)
     _replay_and_compare(g, outs, ref)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_m3_step_replays(mscan, act):
+    """zero_grads + the Mamba-3 SISO forward and backward (the chunked
+    passes, the angle scans, the fixed-order sums: about 25 kernels)
+    captured as one graph.  137 steps, so the last 64-step chunk is ragged;
+    two B/C groups of two heads."""
+    w = workloads.M3Workload("graph_m3_" + act, 2, 137, 4, 64, 64, 2, 16, act)
+    inp = workloads.make_m3_inputs(w, 21)
+    at = {"f32": torch.float32, "bf16": torch.bfloat16}[act]
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda", at if k in ("x", "b_in", "c_in", "dy") else
+                                                             torch.float32)
+           for k, v in inp.items() if v is not None}
+    dims = mscan.M3Dims.make(w.batch, w.seqlen, w.heads, w.headdim, w.d_state, w.groups, w.n_angles, w.act,
+                             w.a_floor)
+    core = mscan.Mamba3Core(dims)
+
+    def step():
+        core.zero_grads()
+        core.forward(dev)
+        core.backward(dev, dev["dy"])
+
+    step()
+    torch.cuda.synchronize()
+    outs = {"y": core.y, "states": core.states}
+    outs.update({"d_" + k: v for k, v in core.grads.items()})
+    ref = {k: v.clone() for k, v in outs.items()}
+    for k, t in ref.items():
+        assert torch.isfinite(t).all(), k
+    g = _capture(step)
+    _replay_and_compare(g, outs, ref)
