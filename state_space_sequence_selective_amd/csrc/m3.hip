@@ -118,7 +118,9 @@ __global__ void __launch_bounds__(256) m3_prep_kernel(const PrepArgs p) {
 // the backward g[b, h, t, a] = sum_{s>=t} dtheta[b, h, s, a], as two-level
 // scans over the 64-step chunks: each thread scans one (b, h, chunk, angle)
 // and leaves the chunk's total; a pass per (b, h, angle) turns the totals
-// into the sum of the chunks before (after) each one; the last pass adds it.
+// into the sum of the chunks before (after) each one, which the kernels
+// reading theta (the rotation and its adjoint) or g (the contribution pass)
+// add to the chunk-local sums.
 struct ScanArgs {
   const float *dt, *ang, *src;
   float *out, *ctot;
@@ -132,16 +134,39 @@ __global__ void __launch_bounds__(256) m3_scan_local_kernel(const ScanArgs p) {
   if (i >= d.B * d.H * d.nc * d.NA) return;
   const int64_t a = i % d.NA, c = (i / d.NA) % d.nc, bh = i / (d.NA * d.nc), b = bh / d.H;
   const int64_t t0 = c * kL, t1 = t0 + kL < d.T ? t0 + kL : d.T;
+  // U steps' loads are issued before their sums and stores (indexes past the
+  // chunk clamped, their values unused): the stores may alias the loads (the
+  // reverse scan runs in place), so the compiler would not move later loads
+  // ahead of them and every step would wait for its own load
+  constexpr int U = 16;
   float acc = 0.0f;
   if (!REV) {
-    for (int64_t t = t0; t < t1; ++t) {
-      acc = fmaf(p.dt[bh * d.T + t], p.ang[(b * d.T + t) * d.NA + a], acc);
-      p.out[(bh * d.T + t) * d.NA + a] = acc;
+    for (int64_t tb = t0; tb < t1; tb += U) {
+      float vd[U], va[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t t = tb + u < t1 ? tb + u : t1 - 1;
+        vd[u] = p.dt[bh * d.T + t];
+        va[u] = p.ang[(b * d.T + t) * d.NA + a];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (tb + u < t1) {
+          acc = fmaf(vd[u], va[u], acc);
+          p.out[(bh * d.T + tb + u) * d.NA + a] = acc;
+        }
     }
   } else {
-    for (int64_t t = t1 - 1; t >= t0; --t) {
-      acc += p.src[(bh * d.T + t) * d.NA + a];
-      p.out[(bh * d.T + t) * d.NA + a] = acc;
+    for (int64_t tb = t1 - 1; tb >= t0; tb -= U) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = p.src[(bh * d.T + (tb - u >= t0 ? tb - u : t0)) * d.NA + a];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (tb - u >= t0) {
+          acc += v[u];
+          p.out[(bh * d.T + tb - u) * d.NA + a] = acc;
+        }
     }
   }
   p.ctot[(bh * d.nc + c) * d.NA + a] = acc;
@@ -153,23 +178,30 @@ __global__ void __launch_bounds__(256) m3_scan_carry_kernel(const ScanArgs p) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= d.B * d.H * d.NA) return;
   const int64_t a = i % d.NA, bh = i / d.NA;
+  // in place: U chunks' totals read before they are overwritten (as above)
+  constexpr int U = 16;
   float run = 0.0f;
-  for (int64_t k = 0; k < d.nc; ++k) {
-    const int64_t c = REV ? d.nc - 1 - k : k;
-    float* q = p.ctot + (bh * d.nc + c) * d.NA + a;
-    const float v = *q;
-    *q = run;
-    run += v;
+  for (int64_t k0 = 0; k0 < d.nc; k0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = k0 + u < d.nc ? k0 + u : d.nc - 1;
+      v[u] = p.ctot[(bh * d.nc + (REV ? d.nc - 1 - k : k)) * d.NA + a];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (k0 + u < d.nc) {
+        p.ctot[(bh * d.nc + (REV ? d.nc - 1 - (k0 + u) : k0 + u)) * d.NA + a] = run;
+        run += v[u];
+      }
   }
 }
 
-// theta: the chunk-local sums plus the sum of the chunks before
-__global__ void __launch_bounds__(256) m3_scan_add_kernel(const ScanArgs p) {
-  const Dims d = p.d;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= d.B * d.H * d.T * d.NA) return;
-  const int64_t a = i % d.NA, bht = i / d.NA, t = bht % d.T, bh = bht / d.T;
-  p.out[i] += p.ctot[(bh * d.nc + t / kL) * d.NA + a];
+// theta[b, h, t, a]: the chunk-local sum plus the sum of the chunks before
+// (the scan's exclusive chunk totals), added where theta is read
+__device__ __forceinline__ float theta_at(const float* theta, const float* ctot, const Dims& d, int64_t bh,
+                                          int64_t t, int64_t a) {
+  return theta[(bh * d.T + t) * d.NA + a] + ctot[(bh * d.nc + t / kL) * d.NA + a];
 }
 
 // From g = the chunk-local suffix sum plus the chunks after, per (b, h, t,
@@ -198,8 +230,16 @@ __global__ void __launch_bounds__(256) m3_theta_dt_kernel(const ThetaBwdArgs p) 
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= d.B * d.H * d.T) return;
   const float* g = p.gl + i * d.NA;
+  constexpr int U = 16;   // loads issued before their adds; the adds keep the angle order
   float acc = 0.0f;
-  for (int64_t a = 0; a < d.NA; ++a) acc += g[a];
+  for (int64_t a0 = 0; a0 < d.NA; a0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = g[a0 + u < d.NA ? a0 + u : d.NA - 1];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (a0 + u < d.NA) acc += v[u];
+  }
   p.ddt_ang[i] = acc;
 }
 
@@ -209,7 +249,7 @@ __global__ void __launch_bounds__(256) m3_theta_dt_kernel(const ThetaBwdArgs p) 
 // j < N - NA: j < NA does the pair (j, j + NA), later j the dim j + NA.
 struct RotArgs {
   const void *b_in, *c_in;
-  const float *b_bias, *c_bias, *theta;
+  const float *b_bias, *c_bias, *theta, *ctot;   // theta chunk-local, ctot the chunks before
   void *Kr, *Qr;
   Dims d;
 };
@@ -227,7 +267,7 @@ __global__ void __launch_bounds__(256) m3_rotate_kernel(const RotArgs p) {
   const int64_t dst = bht * d.N;
   if (j < d.NA) {
     const int64_t n1 = j, n2 = j + d.NA;
-    const float th = p.theta[bht * d.NA + j];
+    const float th = theta_at(p.theta, p.ctot, d, bh, t, j);
     float s, c;
     __sincosf(th, &s, &c);
     const float k1 = io::ld(p.b_in, src + n1) + p.b_bias[h * d.N + n1];
@@ -287,7 +327,7 @@ __global__ void __launch_bounds__(256) m3_rotate8_kernel(const RotArgs p) {
       kp[k] += p.b_bias[h * d.N + pd + k];
       qp[k] += p.c_bias[h * d.N + pd + k];
       float sn, cs;
-      __sincosf(p.theta[bht * d.NA + a0 + k], &sn, &cs);
+      __sincosf(theta_at(p.theta, p.ctot, d, bh, t, a0 + k), &sn, &cs);
       // first half: x1 c - x2 s; second half: x1 s + x2 c (x1 = partner)
       ko[k] = first ? kv[k] * cs - kp[k] * sn : kp[k] * sn + kv[k] * cs;
       qo[k] = first ? qv[k] * cs - qp[k] * sn : qp[k] * sn + qv[k] * cs;
@@ -418,12 +458,27 @@ __global__ void __launch_bounds__(256) m3_state_pass_kernel(const PassArgs p) {
   const int64_t bh = blockIdx.x / per, e = (blockIdx.x % per) * 256 + threadIdx.x;
   float* st = p.st + bh * d.nc * PN + e;
   const float* tot = p.tot + bh * d.nc;
+  // in place: U chunks' states read before they are overwritten (the
+  // stores may alias the loads, so the compiler would not move later loads
+  // ahead of them)
+  constexpr int U = 8;
   float S = 0.0f;
-  for (int64_t k = 0; k < d.nc; ++k) {
-    const int64_t c = REV ? d.nc - 1 - k : k;
-    const float v = st[c * PN];
-    st[c * PN] = S;
-    S = fmaf(expf_fast(tot[c]), S, v);
+  for (int64_t k0 = 0; k0 < d.nc; k0 += U) {
+    float v[U], e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = k0 + u < d.nc ? k0 + u : d.nc - 1;
+      const int64_t c = REV ? d.nc - 1 - k : k;
+      v[u] = st[c * PN];
+      e[u] = tot[c];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (k0 + u < d.nc) {
+        const int64_t c = REV ? d.nc - 1 - (k0 + u) : k0 + u;
+        st[c * PN] = S;
+        S = fmaf(expf_fast(e[u]), S, v[u]);
+      }
   }
 }
 
@@ -861,7 +916,7 @@ __global__ void __launch_bounds__(kThreads) m3_chunk_bwd_kernel(const BwdArgs p)
 // over dK / dQ, and the angle gradient dtheta [B, H, T, NA].
 struct RotBwdArgs {
   const void *Qr, *Kr;
-  const float* theta;
+  const float *theta, *ctot;   // theta chunk-local, ctot the chunks before
   float *dQ, *dK, *dtheta;
   Dims d;
 };
@@ -875,7 +930,7 @@ __global__ void __launch_bounds__(256) m3_rot_bwd_kernel(const RotBwdArgs p) {
   const int64_t j = i % d.NA, bht = i / d.NA;
   const int64_t base = bht * d.N, n1 = j, n2 = j + d.NA;
   float s, c;
-  __sincosf(p.theta[bht * d.NA + j], &s, &c);
+  __sincosf(theta_at(p.theta, p.ctot, d, bht / d.T, bht % d.T, j), &s, &c);
   const float gq1 = p.dQ[base + n1], gq2 = p.dQ[base + n2];
   const float gk1 = p.dK[base + n1], gk2 = p.dK[base + n2];
   const float q1 = io::ld(p.Qr, base + n1), q2 = io::ld(p.Qr, base + n2);
@@ -935,11 +990,26 @@ __global__ void __launch_bounds__(256) m3_group_sum_kernel(const GroupArgs p) {
   if (i >= d.B * d.T * d.G * d.N) return;
   const int64_t n = i % d.N, btg = i / d.N, g = btg % d.G, bt = btg / d.G, t = bt % d.T, b = bt / d.T;
   const int64_t hpg = d.H / d.G;
+  // heads in batches of U, every load of a batch issued before its adds
+  // (heads past the group clamped, their values unused); the adds keep the
+  // head order
+  constexpr int U = 8;
   float sk = 0.0f, sq = 0.0f;
-  for (int64_t k = 0; k < hpg; ++k) {
-    const int64_t e = ((b * d.H + g * hpg + k) * d.T + t) * d.N + n;
-    sk += p.dK[e];
-    sq += p.dQ[e];
+  for (int64_t k0 = 0; k0 < hpg; k0 += U) {
+    float vk[U], vq[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = k0 + u < hpg ? k0 + u : hpg - 1;
+      const int64_t e = ((b * d.H + g * hpg + k) * d.T + t) * d.N + n;
+      vk[u] = p.dK[e];
+      vq[u] = p.dQ[e];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (k0 + u < hpg) {
+        sk += vk[u];
+        sq += vq[u];
+      }
   }
   io::st(p.d_b, i, sk);
   io::st(p.d_c, i, sq);
@@ -966,19 +1036,28 @@ __global__ void __launch_bounds__(256) m3_colpart_kernel(const ColArgs p) {
   const int64_t r0 = rb * per, r1 = r0 + per < rows ? r0 + per : rows;
   float acc = 0.0f;
   int64_t r = r0;
-  for (; r + 4 <= r1; r += 4) {
-    float v[4];
+  // row r = (b, t), stepped without a division per row
+  int64_t b = r0 / p.T, t = r0 % p.T;
+  constexpr int U = 16;   // rows whose loads are issued before their adds
+  for (; r + U <= r1; r += U) {
+    float v[U];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t b = (r + k) / p.T, t = (r + k) % p.T;
+    for (int k = 0; k < U; ++k) {
       v[k] = p.src[((b * p.H + h) * p.T + t) * p.W + w];
+      if (++t == p.T) {
+        t = 0;
+        ++b;
+      }
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc += v[k];
+    for (int k = 0; k < U; ++k) acc += v[k];
   }
   for (; r < r1; ++r) {
-    const int64_t b = r / p.T, t = r % p.T;
     acc += p.src[((b * p.H + h) * p.T + t) * p.W + w];
+    if (++t == p.T) {
+      t = 0;
+      ++b;
+    }
   }
   p.part[i] = acc;
 }
@@ -1005,8 +1084,16 @@ __global__ void __launch_bounds__(256) m3_angle_sum_kernel(const AngArgs p) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= d.B * d.T * d.NA) return;
   const int64_t a = i % d.NA, bt = i / d.NA, t = bt % d.T, b = bt / d.T;
+  constexpr int U = 8;   // heads' loads issued before their adds; the adds keep the head order
   float acc = 0.0f;
-  for (int64_t h = 0; h < d.H; ++h) acc += p.cang[((b * d.H + h) * d.T + t) * d.NA + a];
+  for (int64_t h0 = 0; h0 < d.H; h0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p.cang[((b * d.H + (h0 + u < d.H ? h0 + u : d.H - 1)) * d.T + t) * d.NA + a];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (h0 + u < d.H) acc += v[u];
+  }
   p.d_ang[i] = acc;
 }
 
@@ -1257,10 +1344,9 @@ int prep(const Dims& d, Act act, const Ws& w, const void* b_in, const void* c_in
     ScanArgs sa{w.dt, ang, nullptr, w.theta, w.atot, d};
     hipLaunchKernelGGL(m3_scan_local_kernel<false>, dim3(blocks(d.B * d.H * d.nc * d.NA)), dim3(256), 0, st, sa);
     hipLaunchKernelGGL(m3_scan_carry_kernel<false>, dim3(blocks(d.B * d.H * d.NA)), dim3(256), 0, st, sa);
-    hipLaunchKernelGGL(m3_scan_add_kernel, dim3(blocks(bht * d.NA)), dim3(256), 0, st, sa);
     M3_HIP(hipGetLastError());
   }
-  RotArgs ra{b_in, c_in, b_bias, c_bias, w.theta, w.Kr, w.Qr, d};
+  RotArgs ra{b_in, c_in, b_bias, c_bias, w.theta, w.atot, w.Kr, w.Qr, d};
   M3_HIP(launch_rotate(act, ra, blocks(bht * (d.N - d.NA)), st));
   return MAMBA_OK;
 }
@@ -1388,7 +1474,9 @@ int mamba3_siso_bwd(const mamba3_dims_t* dims, const void* x, const void* b_in, 
              w.dD_part, d};
   M3_HIP(chunk_bwd(d.N, act, nullptr, &ba, grid, st));
   if (d.NA > 0) {
-    RotBwdArgs rb{w.Qr, w.Kr, w.theta, w.dQ, w.dK, w.dtheta, d};
+    // theta is read as its chunk-local sums plus w.atot, the forward scan's
+    // chunk totals, before the reverse scan below reuses w.atot
+    RotBwdArgs rb{w.Qr, w.Kr, w.theta, w.atot, w.dQ, w.dK, w.dtheta, d};
     M3_HIP(launch_rot_bwd(act, rb, blocks(bht * d.NA), st));
     // g = suffix sums of dtheta (in place), then the per-step contributions
     ScanArgs sa{nullptr, nullptr, w.dtheta, w.dtheta, w.atot, d};
