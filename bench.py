@@ -58,13 +58,14 @@ SLOTS_BWD_ELEM = 16
 def kernel_source_hash():
     """sha256 over the sources the core's backward kernels are built from
     (file names and contents, sorted): every csrc file but the forward's
-    (scan_fwd.h, scan_step.h, inst_fwd_*) and the whole-layer kernels'
-    (layer_*), since the counters it guards are those of the backward."""
+    (scan_fwd.h, scan_step.h, inst_fwd_*), the whole-layer kernels' (layer_*)
+    and the Mamba-3 core's (m3*), since the counters it guards are those of
+    the backward."""
     import hashlib
     csrc = os.path.join(ROOT, "state_space_sequence_selective_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")) and not f.startswith(("layer_", "scan_fwd", "scan_step", "inst_fwd_")):
+        if f.endswith((".hip", ".h")) and not f.startswith(("layer_", "scan_fwd", "scan_step", "inst_fwd_", "m3")):
             h.update(f.encode())
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()

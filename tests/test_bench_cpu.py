@@ -85,8 +85,8 @@ def tree(tmp_path, monkeypatch):
 def test_traffic_guard_follows_the_backward_sources(tree):
     csrc = tree / "state_space_sequence_selective_amd" / "csrc"
     h0 = bench.kernel_source_hash()
-    # the forward's and the layer's sources are not part of it
-    for name in ("scan_fwd.h", "scan_step.h", "inst_fwd_bf16.hip", "layer_kernels.hip"):
+    # the forward's, the layer's and the Mamba-3 core's sources are not part of it
+    for name in ("scan_fwd.h", "scan_step.h", "inst_fwd_bf16.hip", "layer_kernels.hip", "m3.hip"):
         with open(csrc / name, "a") as f:
             f.write("\n// edited\n")
         assert bench.kernel_source_hash() == h0, name
