@@ -285,17 +285,18 @@ __global__ void __launch_bounds__(256) m3_rotate_kernel(const RotArgs p) {
   }
 }
 
-// The same for 16-bit activations and n_angles a multiple of 8: a thread
-// makes 8 consecutive dims of one (b, h, t) row of both Qr and Kr, which lie
-// wholly in the first halves of the pairs, the second halves, or past them.
+// The same for 16-bit activations and n_angles a multiple of 8.  A row of
+// (b, h, t) has (N - NA) / 8 threads: the first NA / 8 each turn 8 pairs
+// (dims a0 .. a0+7 with a0 + NA .. a0 + NA + 7), so each angle's sine and
+// cosine is computed once; the rest copy 8 unturned dims past 2 NA.
 template <Act A>
 __global__ void __launch_bounds__(256) m3_rotate8_kernel(const RotArgs p) {
   using io = IO<A>;
   const Dims d = p.d;
-  const int64_t W = d.N / 8;
+  const int64_t W = (d.N - d.NA) / 8, WP = d.NA / 8;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= d.B * d.H * d.T * W) return;
-  const int64_t d0 = (i % W) * 8, bht = i / W, t = bht % d.T, bh = bht / d.T, h = bh % d.H, b = bh / d.H;
+  const int64_t j = i % W, bht = i / W, t = bht % d.T, bh = bht / d.T, h = bh % d.H, b = bh / d.H;
   const int64_t g = h / (d.H / d.G);
   const int64_t src = ((b * d.T + t) * d.G + g) * d.N;
   auto row = [&](const void* base, int64_t off, float* v) {
@@ -307,40 +308,7 @@ __global__ void __launch_bounds__(256) m3_rotate8_kernel(const RotArgs p) {
       v[2 * k + 1] = io::cvt(wv[k] >> 16);
     }
   };
-  float kv[8], qv[8], ko[8], qo[8];
-  row(p.b_in, d0, kv);
-  row(p.c_in, d0, qv);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    kv[k] += p.b_bias[h * d.N + d0 + k];
-    qv[k] += p.c_bias[h * d.N + d0 + k];
-  }
-  if (d0 < 2 * d.NA) {
-    const bool first = d0 < d.NA;
-    const int64_t pd = first ? d0 + d.NA : d0 - d.NA;   // partner dims
-    const int64_t a0 = first ? d0 : d0 - d.NA;
-    float kp[8], qp[8];
-    row(p.b_in, pd, kp);
-    row(p.c_in, pd, qp);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      kp[k] += p.b_bias[h * d.N + pd + k];
-      qp[k] += p.c_bias[h * d.N + pd + k];
-      float sn, cs;
-      __sincosf(theta_at(p.theta, p.ctot, d, bh, t, a0 + k), &sn, &cs);
-      // first half: x1 c - x2 s; second half: x1 s + x2 c (x1 = partner)
-      ko[k] = first ? kv[k] * cs - kp[k] * sn : kp[k] * sn + kv[k] * cs;
-      qo[k] = first ? qv[k] * cs - qp[k] * sn : qp[k] * sn + qv[k] * cs;
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      ko[k] = kv[k];
-      qo[k] = qv[k];
-    }
-  }
-  const int64_t dst = bht * d.N + d0;
-  auto put = [&](void* base, const float* v) {   // 8 values as one 16-byte store
+  auto put = [&](void* base, int64_t d0, const float* v) {   // 8 values as one 16-byte store
     uint16_t hv[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -352,10 +320,42 @@ __global__ void __launch_bounds__(256) m3_rotate8_kernel(const RotArgs p) {
     o.y = hv[2] | (uint32_t(hv[3]) << 16);
     o.z = hv[4] | (uint32_t(hv[5]) << 16);
     o.w = hv[6] | (uint32_t(hv[7]) << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + dst) = o;
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + bht * d.N + d0) = o;
   };
-  put(p.Kr, ko);
-  put(p.Qr, qo);
+  float k1[8], q1[8];
+  const int64_t d1 = j < WP ? 8 * j : 2 * d.NA + 8 * (j - WP);   // first (or only) dims
+  row(p.b_in, d1, k1);
+  row(p.c_in, d1, q1);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    k1[k] += p.b_bias[h * d.N + d1 + k];
+    q1[k] += p.c_bias[h * d.N + d1 + k];
+  }
+  if (j < WP) {
+    const int64_t d2 = d1 + d.NA;   // the second halves of the pairs
+    float k2[8], q2[8], ko1[8], qo1[8], ko2[8], qo2[8];
+    row(p.b_in, d2, k2);
+    row(p.c_in, d2, q2);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      k2[k] += p.b_bias[h * d.N + d2 + k];
+      q2[k] += p.c_bias[h * d.N + d2 + k];
+      float sn, cs;
+      __sincosf(theta_at(p.theta, p.ctot, d, bh, t, d1 + k), &sn, &cs);
+      // first half: x1 c - x2 s; second half: x1 s + x2 c
+      ko1[k] = k1[k] * cs - k2[k] * sn;
+      qo1[k] = q1[k] * cs - q2[k] * sn;
+      ko2[k] = k1[k] * sn + k2[k] * cs;
+      qo2[k] = q1[k] * sn + q2[k] * cs;
+    }
+    put(p.Kr, d1, ko1);
+    put(p.Qr, d1, qo1);
+    put(p.Kr, d2, ko2);
+    put(p.Qr, d2, qo2);
+  } else {
+    put(p.Kr, d1, k1);
+    put(p.Qr, d1, q1);
+  }
 }
 
 // ------------------------------------------------------- chunk state
@@ -1188,7 +1188,7 @@ hipError_t chunk_bwd(int64_t N, Act act, const ChunkStateArgs* cs, const BwdArgs
 hipError_t launch_rotate(Act act, const RotArgs& a, unsigned grid, hipStream_t st) {
   const Dims& d = a.d;
   if (act != Act::F32 && d.NA % 8 == 0) {
-    const unsigned g8 = blocks(d.B * d.H * d.T * (d.N / 8));
+    const unsigned g8 = blocks(d.B * d.H * d.T * ((d.N - d.NA) / 8));
     if (act == Act::BF16) hipLaunchKernelGGL(m3_rotate8_kernel<Act::BF16>, dim3(g8), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(m3_rotate8_kernel<Act::F16>, dim3(g8), dim3(256), 0, st, a);
     return hipGetLastError();
