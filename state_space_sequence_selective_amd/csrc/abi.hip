@@ -121,6 +121,7 @@ struct Plan {
   int Fb;         // sub-segments per backward segment in the carry pass
   int64_t segf_steps;   // steps per forward segment (a multiple of 16)
   int64_t segb_tiles;   // Lb-step tiles per backward segment
+  int64_t ldz = 0;      // elements between rows of z and d_z: d_inner, or the stride the layer keeps x | z in
   bool regen() const { return Lb != L; }
   int Sc() const { return Sb * Fb; }   // carry sub-segments
 };
@@ -272,6 +273,7 @@ int plan_dims(const mamba_dims_t* d, bool fused, const char* fn, Plan* pl) {
   pl->T = d->seqlen;
   pl->Di = d->d_inner;
   pl->Ds = d->d_state;
+  pl->ldz = d->d_inner;
   pl->R = d->dt_rank;
   pl->X = X;
   pl->L = L;
@@ -456,6 +458,7 @@ int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_
   a.R = pl.R;
   a.X = pl.X;
   a.nC = pl.nC;
+  a.ldz = pl.ldz;
   a.K = pl.K;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
@@ -494,6 +497,7 @@ int do_forward(const char* fn, const Plan& pl, const void* x, const float* conv_
       f.T = pl.T;
       f.Di = pl.Di;
       f.nC = pl.nC;
+      f.ldz = pl.ldz;
       f.seg_steps = pl.segf_steps;
       f.K = pl.K;
       f.L = pl.L;
@@ -595,6 +599,7 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
     f.T = pl.T;
     f.Di = pl.Di;
     f.nC = pl.nC;
+    f.ldz = pl.ldz;
     f.seg_steps = pl.L;
     f.K = pl.K;
     f.L = pl.L;
@@ -619,6 +624,7 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
     c.Di = pl.Di;
     c.R = pl.R;
     c.X = pl.X;
+    c.ldz = pl.ldz;
     c.seg_steps = pl.segb_tiles * pl.Lb / pl.Fb;
     c.S = pl.Sc();
     c.first = pl.Fb;
@@ -663,6 +669,7 @@ int do_backward(const char* fn, const Plan& pl, const void* x, const float* conv
   a.R = pl.R;
   a.X = pl.X;
   a.nC = pl.nCb;
+  a.ldz = pl.ldz;
   a.K = pl.K;
   a.L = pl.Lb;
   a.PW = PW;
@@ -815,3 +822,35 @@ int mamba_conv_scan_gate_bwd(const mamba_dims_t* dims, const void* x, const floa
 }
 
 }  // extern "C"
+
+namespace mscan {
+
+// mamba_scan_fwd / mamba_scan_bwd with the rows of z (and d_z) ldz elements
+// apart, for the layer, which keeps x | z and d_x | d_z interleaved.
+int scan_fwd_ldz(const mamba_dims_t* dims, const void* u, const void* delta_raw, const float* a_log,
+                 const void* xdbl, const float* D, const void* z, int64_t ldz, const float* h0, void* out,
+                 void* y_save, float* h_last, float* ckpt, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "mamba_scan_fwd";
+  Plan pl;
+  MSCAN_TRY(plan_dims(dims, false, fn, &pl));
+  if (ldz < pl.Di || ldz % 4 != 0) return fail(MAMBA_ERR_INVALID, fn, "z rows: stride below d_inner or not a multiple of 4");
+  pl.ldz = ldz;
+  return do_forward(fn, pl, u, nullptr, nullptr, nullptr, delta_raw, a_log, xdbl, D, z, h0, out, nullptr,
+                    y_save, h_last, nullptr, ckpt, workspace, workspace_bytes, stream);
+}
+
+int scan_bwd_ldz(const mamba_dims_t* dims, const void* u, const void* delta_raw, const float* a_log,
+                 const void* xdbl, const float* D, const void* z, int64_t ldz, const void* y_saved,
+                 const float* ckpt, const void* dout, void* d_u, void* d_delta_raw, void* d_z, float* d_xdbl,
+                 float* d_a_log, float* d_D, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "mamba_scan_bwd";
+  Plan pl;
+  MSCAN_TRY(plan_dims(dims, false, fn, &pl));
+  if (ldz < pl.Di || ldz % 4 != 0) return fail(MAMBA_ERR_INVALID, fn, "z rows: stride below d_inner or not a multiple of 4");
+  pl.ldz = ldz;
+  return do_backward(fn, pl, u, nullptr, nullptr, nullptr, delta_raw, a_log, xdbl, D, z, y_saved, ckpt, dout,
+                     nullptr, d_u, d_delta_raw, d_z, d_xdbl, d_a_log, d_D, nullptr, nullptr, workspace,
+                     workspace_bytes, stream);
+}
+
+}  // namespace mscan

@@ -15,6 +15,7 @@
 #include "layer_kernels.h"
 #include "mamba_layer.h"
 #include "mamba_scan.h"
+#include "scan_strided.h"
 
 namespace mscan {
 void set_last_error(const std::string& msg);   // abi.hip
@@ -137,8 +138,9 @@ int plan_layer(const mamba_layer_dims_t* d, const char* fn, LPlan* pl) {
   Layout s;
   pl->s_xn = s.take(N * dm * es);
   pl->s_rstd = s.take(N * f);
-  pl->s_x = s.take(N * Di * es);
-  pl->s_z = s.take(N * Di * es);
+  // x | z interleaved, rows of 2 d_inner: the one in_proj product's output
+  pl->s_x = s.take(2 * N * Di * es);
+  pl->s_z = pl->s_x + Di * es;
   pl->s_u = s.take(N * Di * es);
   pl->s_xdbl = s.take(N * X * es);
   pl->s_dr = s.take(N * Di * es);
@@ -179,11 +181,12 @@ int plan_layer(const mamba_layer_dims_t* d, const char* fn, LPlan* pl) {
   pl->w_dgated = wb.take(N * Di * es);
   pl->w_du = wb.take(N * Di * es);
   pl->w_ddr = wb.take(N * Di * es);
-  pl->w_dz = wb.take(N * Di * es);
+  // d_x | d_z interleaved like x | z: the one in_proj input-gradient product's operand
+  pl->w_dx = wb.take(2 * N * Di * es);
+  pl->w_dz = pl->w_dx + Di * es;
   pl->w_dxdbl = wb.take(N * X * f);
   pl->w_dxdbl_a = wb.take(N * X * es);
   pl->w_duex = wb.take(N * Di * f);
-  pl->w_dx = wb.take(N * Di * es);
   pl->w_dxn = wb.take(N * dm * f);
   pl->w_pnorm = wb.take(static_cast<size_t>(pl->norm_nblk) * dm * f);
   pl->w_pbdt = wb.take(static_cast<size_t>(pl->bdt_nblk) * Di * f);
@@ -479,7 +482,6 @@ int mamba_layer_fwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
   float* ckpt = reinterpret_cast<float*>(S + pl.s_ckpt);
   float* dt = reinterpret_cast<float*>(W + pl.w_dt);
   const int64_t N = pl.N, Di = pl.Di, dm = pl.dm, X = pl.X, R = pl.R;
-  const char* w_in_z = static_cast<const char*>(w->w_in) + Di * dm * pl.es;
 
   Op o{OpKind::RmsnormFwd};   // F1
   o.f0 = resid_in;
@@ -490,11 +492,13 @@ int mamba_layer_fwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
   o.cols = dm;
   o.eps = kNormEps;
   LAYER_TRY(run(fn, "rmsnorm", o, act, st));
-  // F2: x = xn W_in[:Di]^T, z = xn W_in[Di:]^T
-  LAYER_TRY(gemm(fn, "in_proj x", h, false, true, N, Di, dm, xn, at, dm, w->w_in, at, dm, 0.0f, x, x, at, Di));
-  LAYER_TRY(gemm(fn, "in_proj z", h, false, true, N, Di, dm, xn, at, dm, w_in_z, at, dm, 0.0f, z, z, at, Di));
+  // F2: x = xn W_in[:Di]^T, z = xn W_in[Di:]^T into the halves of rows of 2 d_inner
+  const char* w_in_z = static_cast<const char*>(w->w_in) + Di * dm * pl.es;
+  LAYER_TRY(gemm(fn, "in_proj x", h, false, true, N, Di, dm, xn, at, dm, w->w_in, at, dm, 0.0f, x, x, at, 2 * Di));
+  LAYER_TRY(gemm(fn, "in_proj z", h, false, true, N, Di, dm, xn, at, dm, w_in_z, at, dm, 0.0f, z, z, at, 2 * Di));
   o = Op{OpKind::ConvSiluFwd};   // F4a
   o.c0 = x;
+  o.ld = 2 * Di;
   o.f0 = w->conv_w;
   o.f1 = w->conv_b;
   o.v0 = u;
@@ -533,8 +537,9 @@ int mamba_layer_fwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     LAYER_TRY(run(fn, "dt bias", o, act, st));
   }
   // F4d/e
-  LAYER_TRY(core_call(fn, "scan", mamba_scan_fwd(&pl.core, u, dr, w->a_log, xdbl, w->D, z, nullptr, gated, y,
-                                                 nullptr, ckpt, W + pl.w_core_f, pl.core_ws, stream)));
+  LAYER_TRY(core_call(fn, "scan", mscan::scan_fwd_ldz(&pl.core, u, dr, w->a_log, xdbl, w->D, z, 2 * Di, nullptr,
+                                                      gated, y, nullptr, ckpt, W + pl.w_core_f, pl.core_ws,
+                                                      stream)));
   // F5 + F6: resid_out = resid_in + gated W_out^T
   LAYER_TRY(gemm(fn, "out_proj", h, false, true, N, dm, Di, gated, at, Di, w->w_out, at, Di, 1.0f, resid_in, resid_out,
                  f32, dm));
@@ -607,7 +612,6 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     float* pcb = reinterpret_cast<float*>(W + pl.w_pconv_b);
     float* pwg = reinterpret_cast<float*>(W + pl.w_pwg);
     const int64_t N = pl.N, Di = pl.Di, dm = pl.dm, X = pl.X, R = pl.R;
-    const char* w_in_z = static_cast<const char*>(w->w_in) + Di * dm * pl.es;
     mlayer::XdtArgs xa;
     xa.w_x = w->w_x;
     xa.w_dt = w->w_dt;
@@ -651,15 +655,16 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     o.n = N * X;
     LAYER_TRY(run(fn, "zero d_xdbl", o, act, st));
     LAYER_TRY(core_call(fn, "scan backward",
-                        mamba_scan_bwd(&pl.core, u, dr, w->a_log, xdbl, w->D, z, y, ckpt, d_gated, d_u, d_dr, d_z,
-                                       d_xdbl, g->a_log, g->D, W + pl.w_core_b, pl.core_ws, stream)));
+                        mscan::scan_bwd_ldz(&pl.core, u, dr, w->a_log, xdbl, w->D, z, 2 * Di, y, ckpt, d_gated,
+                                            d_u, d_dr, d_z, d_xdbl, g->a_log, g->D, W + pl.w_core_b, pl.core_ws,
+                                            stream)));
     // the out_proj weight product, and d_z being final, its in_proj one,
     // start beside the rest of the adjoint
     float* gw_in_z = g->w_in + Di * dm;
     LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[0]));
     LAYER_TRY(wgrad(fn, "out_proj wgrad", hw, sd->s, act, dm, Di, N, dy, at, dm, gated, at, Di, pl.es, g->w_out, pwg,
                     pl.P_wide));
-    LAYER_TRY(wgrad(fn, "in_proj wgrad z", hw, sd->s, act, Di, dm, N, d_z, at, Di, xn, at, dm, pl.es, gw_in_z, pwg,
+    LAYER_TRY(wgrad(fn, "in_proj wgrad z", hw, sd->s, act, Di, dm, N, d_z, at, 2 * Di, xn, at, dm, pl.es, gw_in_z, pwg,
                     pl.P_wide));
     // dt_proj adjoint: W_dt and b_dt here; the dt columns of d_xdbl with the
     // x_proj adjoint below
@@ -744,12 +749,13 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     o.f6 = pcb;
     o.T = pl.T;
     o.cols = Di;
+    o.ld = 2 * Di;   // x and d_x: rows of x | z and of d_x | d_z
     o.K = static_cast<int>(pl.K);
     o.n = N * Di;
     LAYER_TRY(run(fn, "conv adjoint", o, act, st));
     // d_x is final here: its in_proj weight product starts beside the rest
     LAYER_TRY(fork_wait(fn, st, sd->s, sd->ev[3]));
-    LAYER_TRY(wgrad(fn, "in_proj wgrad x", hw, sd->s, act, Di, dm, N, d_x, at, Di, xn, at, dm, pl.es, g->w_in, pwg,
+    LAYER_TRY(wgrad(fn, "in_proj wgrad x", hw, sd->s, act, Di, dm, N, d_x, at, 2 * Di, xn, at, dm, pl.es, g->w_in, pwg,
                     pl.P_wide));
     o = Op{OpKind::ColSum};
     o.f0 = pcw;
@@ -761,11 +767,9 @@ int mamba_layer_bwd(const mamba_layer_dims_t* dims, const mamba_layer_weights_t*
     o.f3 = g->conv_b;
     o.cols = Di;
     LAYER_TRY(run(fn, "conv_b sum", o, act, st));
-    // in_proj adjoint: d_xn = d_x W_in[:Di] + d_z W_in[Di:]
-    LAYER_TRY(gemm(fn, "in_proj dgrad x", h, false, false, N, dm, Di, d_x, at, Di, w->w_in, at, dm, 0.0f, d_xn, d_xn, f32,
-                   dm));
-    LAYER_TRY(gemm(fn, "in_proj dgrad z", h, false, false, N, dm, Di, d_z, at, Di, w_in_z, at, dm, 1.0f, d_xn, d_xn, f32,
-                   dm));
+    // in_proj adjoint: d_xn = [d_x | d_z] W_in, one product over K = 2 d_inner
+    LAYER_TRY(gemm(fn, "in_proj dgrad", h, false, false, N, dm, 2 * Di, d_x, at, 2 * Di, w->w_in, at, dm, 0.0f, d_xn,
+                   d_xn, f32, dm));
     // RMSNorm adjoint and the residual
     o = Op{OpKind::RmsnormBwd};
     o.f0 = d_xn;

@@ -14,8 +14,9 @@ enum class OpKind {
   RmsnormFwd,        // x f0, w f1 -> y v0 (act), rstd f3; rows, cols = d_model, eps
   RmsnormBwd,        // dy f0, x f1, w f2, rstd f4, d_out f5 -> d_in f3; rows, cols
   RmsnormWgradPart,  // dy f0, x f1, rstd f2 -> part f3 [nblk, cols]; rows, cols, per_blk, nblk
-  ConvSiluFwd,       // x c0, conv_w f0, conv_b f1 -> u v0; T, cols = d_inner, K, n
-  ConvBwd,           // x c0, conv_w f0, conv_b f1, d_u c1 (act), d_u_extra f2 -> d_x v0 (act),
+  ConvSiluFwd,       // x c0 (rows ld apart), conv_w f0, conv_b f1 -> u v0; T, cols = d_inner, ld, K, n
+  ConvBwd,           // x c0 (rows ld apart), conv_w f0, conv_b f1, d_u c1 (act), d_u_extra f2 -> d_x v0 (act,
+                     // rows ld apart),
                      // part_w f3 [batch * ntiles, cols, K], part_b f6 [batch * ntiles, cols]; T, cols, K, n
                      // (ntiles = conv_step_tiles(T))
   BiasRound,         // dt f0, b f1 -> out v0 (act); cols = d_inner (% 4 == 0), n
@@ -38,6 +39,7 @@ struct Op {
   const void* c1 = nullptr;
   void* v0 = nullptr;
   int64_t rows = 0, cols = 0, n = 0, T = 0, nblk = 0, per_blk = 0, nblk_t = 0;
+  int64_t ld = 0;   // elements between rows of the conv kernels' x and d_x (0: cols)
   int K = 0;
   float eps = 0.0f;
 };

@@ -227,16 +227,17 @@ __device__ __forceinline__ void conv_weights(const float* cw, const float* cb, i
   bias = *reinterpret_cast<const float4*>(cb + i0);
 }
 
-// rows t0 .. t0 + R - 1 of 4 channels (zero before the sequence start; rows
-// past the end reload the last row: their values are not used)
+// rows t0 .. t0 + R - 1 of 4 channels, rows `ld` elements apart (zero
+// before the sequence start; rows past the end reload the last row: their
+// values are not used)
 template <Act A, int R>
-__device__ __forceinline__ void conv_rows(const void* p, int64_t rb, int64_t t0, int64_t T, int64_t Di, int64_t i0,
+__device__ __forceinline__ void conv_rows(const void* p, int64_t rb, int64_t t0, int64_t T, int64_t ld, int64_t i0,
                                           float4 (&r)[R]) {
 #pragma unroll
   for (int m = 0; m < R; ++m) {
     const int64_t t = t0 + m;
     const int64_t tc = t < 0 ? 0 : (t < T ? t : T - 1);
-    r[m] = ld4<A>(p, (rb + tc) * Di + i0);
+    r[m] = ld4<A>(p, (rb + tc) * ld + i0);
     if (t < 0) r[m] = f4zero();
   }
 }
@@ -256,19 +257,21 @@ __device__ __forceinline__ float4 conv_pre(const float4 (&w)[K], const float4& b
   return p;
 }
 
-// F4a: u_t = SiLU(b + sum_k w[i,k] x_{t-(K-1-k)}), zero history.
+// F4a: u_t = SiLU(b + sum_k w[i,k] x_{t-(K-1-k)}), zero history; x rows ldx
+// elements apart, u rows Di.
 template <Act A, int K>
 __global__ void __launch_bounds__(kThreads) conv_silu_fwd_kernel(const void* __restrict__ x,
                                                                 const float* __restrict__ cw,
                                                                 const float* __restrict__ cb, void* __restrict__ u,
-                                                                int64_t T, int64_t Di, unsigned ncb, unsigned ntb) {
+                                                                int64_t T, int64_t Di, int64_t ldx, unsigned ncb,
+                                                                unsigned ntb) {
   const ConvTile c = conv_tile(T, Di, ncb, ntb);
   if (!c.on) return;
   float4 w[K], bias;
   conv_weights<K>(cw, cb, c.i0, w, bias);
   const int64_t rb = c.b * T;
   float4 xr[kConvS + K - 1];   // x_{s0-(K-1)} .. x_{s0+kConvS-1}
-  conv_rows<A>(x, rb, c.s0 - (K - 1), T, Di, c.i0, xr);
+  conv_rows<A>(x, rb, c.s0 - (K - 1), T, ldx, c.i0, xr);
 #pragma unroll
   for (int j = 0; j < kConvS; ++j) {
     const int64_t t = c.s0 + j;
@@ -291,14 +294,15 @@ __device__ __forceinline__ float dsilu(float p, float g) {
 //   d_x_s = sum_k w[i,k] dp_{s+K-1-k}               (dp for t in [s0, s0+kConvS+K-2])
 //   weight partials over the thread's own t = s: sum dp_t x_{t-(K-1-k)}, sum dp_t;
 // the 16 step groups of a workgroup are added in order through LDS, one
-// partial per (batch row, step block).
+// partial per (batch row, step block).  x and d_x rows ldx elements apart,
+// d_u and d_u_extra rows Di.
 template <Act A, int K>
 __global__ void __launch_bounds__(kThreads) conv_bwd_kernel(const void* __restrict__ x, const float* __restrict__ cw,
                                                            const float* __restrict__ cb, const void* __restrict__ du,
                                                            const float* __restrict__ du_extra,
                                                            void* __restrict__ dx, float* __restrict__ part_w,
                                                            float* __restrict__ part_b, int64_t T, int64_t Di,
-                                                           unsigned ncb, unsigned ntb) {
+                                                           int64_t ldx, unsigned ncb, unsigned ntb) {
   __shared__ float4 s_red[K + 1][kThreads];   // [tap k | bias][thread]: the thread's partials of its 4 channels
   const ConvTile c = conv_tile(T, Di, ncb, ntb);
   float4 acc[K + 1];   // taps, then the bias
@@ -310,7 +314,7 @@ __global__ void __launch_bounds__(kThreads) conv_bwd_kernel(const void* __restri
     const int64_t rb = c.b * T;
     constexpr int ND = kConvS + K - 1;   // dp_t for t = s0 .. s0 + ND - 1
     float4 xr[ND + K - 1];                // x_{s0-(K-1)} .. x_{s0+ND-1}
-    conv_rows<A>(x, rb, c.s0 - (K - 1), T, Di, c.i0, xr);
+    conv_rows<A>(x, rb, c.s0 - (K - 1), T, ldx, c.i0, xr);
     float4 g0[ND];
     conv_rows<A>(du, rb, c.s0, T, Di, c.i0, g0);
     float4 dp[ND];
@@ -337,7 +341,7 @@ __global__ void __launch_bounds__(kThreads) conv_bwd_kernel(const void* __restri
           gx.z = fmaf(w[k].z, dk.z, gx.z);
           gx.w = fmaf(w[k].w, dk.w, gx.w);
         }
-        st4<A>(dx, (rb + s) * Di + c.i0, gx);
+        st4<A>(dx, (rb + s) * ldx + c.i0, gx);
         // step t = s: tap k saw x_{t-(K-1)+k} = xr[j + k]
         const float4 g = dp[j];
 #pragma unroll
@@ -510,7 +514,7 @@ hipError_t dispatch(const Op& o, hipStream_t st) {
 #define CONV_FWD(KK)                                                                                                \
   case KK:                                                                                                          \
     hipLaunchKernelGGL((conv_silu_fwd_kernel<A, KK>), grid_conv(o), blk, 0, st, o.c0, o.f0, o.f1, o.v0, o.T, o.cols, \
-                       nchb(o), ntb(o));                                                                            \
+                       o.ld ? o.ld : o.cols, nchb(o), ntb(o));                                                      \
     break;
         CONV_FWD(1) CONV_FWD(2) CONV_FWD(3) CONV_FWD(4)
 #undef CONV_FWD
@@ -523,7 +527,7 @@ hipError_t dispatch(const Op& o, hipStream_t st) {
 #define CONV_BWD(KK)                                                                                                \
   case KK:                                                                                                          \
     hipLaunchKernelGGL((conv_bwd_kernel<A, KK>), grid_conv(o), blk, 0, st, o.c0, o.f0, o.f1, o.c1, o.f2, o.v0, o.f3, \
-                       o.f6, o.T, o.cols, nchb(o), ntb(o));                                                          \
+                       o.f6, o.T, o.cols, o.ld ? o.ld : o.cols, nchb(o), ntb(o));                                    \
     break;
         CONV_BWD(1) CONV_BWD(2) CONV_BWD(3) CONV_BWD(4)
 #undef CONV_BWD

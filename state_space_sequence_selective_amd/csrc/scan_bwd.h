@@ -219,12 +219,12 @@ scan_bwd_kernel(const BwdArgs p) {
   float hn[SPL];
   auto prefetch = [&](int64_t kt) {
     const int64_t t0 = kt * L;
-    async_rows<ES, CPW>(raw_l, p.x, row0, t0 - (KMAX - 1), T, Di, i0, XR, wave, NW, lane);
-    async_rows<ES, CPW>(raw_l + XR * RB, p.delta_raw, row0, t0, T, Di, i0, TR, wave, NW, lane);
-    async_rows<ES, CPW>(raw_l + (XR + TR) * RB, p.dout, row0, t0, T, Di, i0, TR, wave, NW, lane);
+    async_rows<ES, CPW>(raw_l, p.x, row0, t0 - (KMAX - 1), T, Di, i0, XR, wave, NW, lane, Di);
+    async_rows<ES, CPW>(raw_l + XR * RB, p.delta_raw, row0, t0, T, Di, i0, TR, wave, NW, lane, Di);
+    async_rows<ES, CPW>(raw_l + (XR + TR) * RB, p.dout, row0, t0, T, Di, i0, TR, wave, NW, lane, Di);
     if (gate) {
-      async_rows<ES, CPW>(raw_l + (XR + 2 * TR) * RB, p.z, row0, t0, T, Di, i0, TR, wave, NW, lane);
-      async_rows<ES, CPW>(raw_l + (XR + 3 * TR) * RB, p.y_saved, row0, t0, T, Di, i0, TR, wave, NW, lane);
+      async_rows<ES, CPW>(raw_l + (XR + 2 * TR) * RB, p.z, row0, t0, T, Di, i0, TR, wave, NW, lane, p.ldz);
+      async_rows<ES, CPW>(raw_l + (XR + 3 * TR) * RB, p.y_saved, row0, t0, T, Di, i0, TR, wave, NW, lane, Di);
     }
 #pragma unroll
     for (int q = 0; q < BCPT; ++q) {
@@ -298,7 +298,7 @@ scan_bwd_kernel(const BwdArgs p) {
           const float sz = sigmoid(zv);
           dy = go * zv * sz;
           const float yv = raw_ld<A>(raw_y, tt * CPW + c);
-          io::st(p.d_z, e, go * yv * (sz * (1.0f + zv * (1.0f - sz))));
+          io::st(p.d_z, (row0 + t0 + tt) * p.ldz + i, go * yv * (sz * (1.0f + zv * (1.0f - sz))));
         } else {
           dy = go;
         }

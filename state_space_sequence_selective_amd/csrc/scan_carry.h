@@ -81,9 +81,9 @@ scan_bwd_carry_kernel(const CarryArgs p) {
   uint32_t cbits[CPT];
   auto prefetch = [&](int64_t kt) {
     const int64_t t0 = kt * TT;
-    async_rows<ES, CPW>(raw_l, p.delta_raw, row0, t0, T, Di, i0, TR, wave, NW, lane);
-    async_rows<ES, CPW>(raw_l + TR * RB, p.dout, row0, t0, T, Di, i0, TR, wave, NW, lane);
-    if (gate) async_rows<ES, CPW>(raw_l + 2 * TR * RB, p.z, row0, t0, T, Di, i0, TR, wave, NW, lane);
+    async_rows<ES, CPW>(raw_l, p.delta_raw, row0, t0, T, Di, i0, TR, wave, NW, lane, Di);
+    async_rows<ES, CPW>(raw_l + TR * RB, p.dout, row0, t0, T, Di, i0, TR, wave, NW, lane, Di);
+    if (gate) async_rows<ES, CPW>(raw_l + 2 * TR * RB, p.z, row0, t0, T, Di, i0, TR, wave, NW, lane, p.ldz);
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int j = tid + q * NT;

@@ -201,16 +201,17 @@ constexpr int rows_per_inst() {
 }
 
 // Asynchronous copy (global_load_lds, no registers) of `nrows` time rows of
-// one CPW-channel group of an activation tensor [B, T, Di] into LDS, one row
-// of CPW * ES bytes after another starting at `dst`.  Time rows are clamped
-// to [0, T) and granules past Di re-read the last granule of the row, so no
-// load leaves the tensor (Di % 4 == 0).  nrows must be a multiple of
+// one CPW-channel group of an activation tensor [B, T, Di] (rows `ld`
+// elements apart, ld >= Di) into LDS, one row of CPW * ES bytes after another
+// starting at `dst`.  Time rows are clamped to [0, T) and granules past Di
+// re-read the last granule of the row, so no load leaves the tensor
+// (Di % 4 == 0).  nrows must be a multiple of
 // rows_per_inst; instructions are spread over the waves.  The caller ends
 // the copy with a full s_waitcnt and a workgroup barrier.
 template <int ES, int CPW>
 __device__ __forceinline__ void async_rows(lds_char_t* dst, const void* src, int64_t row0, int64_t t_lo,
                                            int64_t T, int64_t Di, int64_t i0, int nrows, int wave,
-                                           int nwaves, int lane) {
+                                           int nwaves, int lane, int64_t ld) {
   constexpr int GB = ES == 4 ? 16 : 4;   // bytes per lane
   constexpr int GC = GB / ES;            // channels per lane
   constexpr int LPR = CPW / GC;          // lanes per row
@@ -219,8 +220,8 @@ __device__ __forceinline__ void async_rows(lds_char_t* dst, const void* src, int
   const int ninst = nrows / RPI;
   int64_t ch = i0 + (lane % LPR) * GC;
   if (ch > Di - GC) ch = Di - GC;
-  const char* base = static_cast<const char*>(src) + (row0 * Di + ch) * ES;
-  const int64_t rstride = Di * ES;
+  const char* base = static_cast<const char*>(src) + (row0 * ld + ch) * ES;
+  const int64_t rstride = ld * ES;
   for (int j = wave; j < ninst; j += nwaves) {
     int64_t t = t_lo + j * RPI + lane / LPR;
     t = t < 0 ? 0 : (t >= T ? T - 1 : t);
@@ -268,6 +269,7 @@ struct FwdArgs {
   float* conv_state_last;   // [B,Di,K] or null
   float* ckpt;              // [B,nC,Ds,Di] or null
   int64_t B, T, Di, R, X, nC;
+  int64_t ldz;              // elements between rows of z (>= Di)
   int K;                    // conv taps, 0 = no conv
 };
 
@@ -277,7 +279,7 @@ struct BwdArgs {
   const float* a_log;
   const void* xdbl;
   const float* D;
-  const void* z;
+  const void* z;            // [B,T,Di], rows ldz elements apart (gate only)
   const void* y_saved;      // [B,T,Di] (gate only)
   const float* conv_w;
   const float* conv_b;
@@ -287,12 +289,13 @@ struct BwdArgs {
   void* d_x;                // d_u [B,T,Di] (scan entry)
   float* du_out;            // d_u [B,T,Di] f32 (fused entry: the conv adjoint pass reads it)
   void* d_delta_raw;        // [B,T,Di]
-  void* d_z;                // [B,T,Di] (gate only)
+  void* d_z;                // [B,T,Di], rows ldz elements apart (gate only)
   float* part_bc;           // [nG, B*T, 2*Ds]: per channel-group sums of d_B | d_C
   float* part_par;          // [S, B, Di, PW]: per segment and batch row d_a_log | d_D
   // segmented schedule: segment s covers tiles [s * seg_tiles, ...) of L steps
   const float* seg_c;       // [B,S,Di,Ds] carry entering each segment's reverse sweep (S > 1)
   int64_t B, T, Di, R, X, nC;
+  int64_t ldz;              // elements between rows of z and d_z (>= Di)
   int64_t seg_tiles;        // tiles per segment
   int K;
   int L;
@@ -305,11 +308,12 @@ struct CarryArgs {
   const void* delta_raw;    // [B,T,Di]
   const float* a_log;       // [Di,Ds]
   const void* xdbl;         // [B,T,X]
-  const void* z;            // [B,T,Di] or null
+  const void* z;            // [B,T,Di], rows ldz elements apart, or null
   const void* dout;         // [B,T,Di]
   float* seg_q;             // [B,S,Di,Ds] out
   float* seg_sd;            // [B,S,Di] out
   int64_t B, T, Di, R, X;
+  int64_t ldz;              // elements between rows of z (>= Di)
   int64_t seg_steps;        // steps per (sub-)segment (a multiple of 16)
   int S;                    // sub-segments
   int first;                // the first sub-segment computed (those before it hand nothing on)

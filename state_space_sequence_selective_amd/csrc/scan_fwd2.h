@@ -48,7 +48,7 @@ struct Fwd2Args {
   const float* a_log;       // [Di,Ds]
   const float* bc;          // [B*T, 2*Ds] f32: B_t then C_t
   const float* D;           // [Di] or null
-  const void* z;            // [B,T,Di] or null
+  const void* z;            // [B,T,Di] (rows ldz elements apart) or null
   const float* h0;          // [B,Di,Ds] or null
   const float* conv_w;      // [Di,K] (K > 0)
   const float* conv_b;      // [Di] or null
@@ -63,6 +63,7 @@ struct Fwd2Args {
   float* seg_h;             // [B,S,Ds,Di] end state of each segment scanned from zero
   float* seg_sd;            // [B,S,Di] sum of delta over each segment
   int64_t B, T, Di, nC;
+  int64_t ldz;              // elements between rows of z (>= Di)
   int64_t seg_steps;        // steps per segment (a multiple of 16); REGEN: L
   int K;                    // conv taps, 0 = no conv
   int L;                    // checkpoint interval (a multiple of 16)
@@ -222,13 +223,14 @@ scan_fwd2_kernel(const Fwd2Args p) {
       else __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(dst + q * 64 * BCG), 4, 0, 0);
     }
     const void* srcs[3] = {p.x, p.delta_raw, zsrc};
+    const int64_t lds_[3] = {Di, Di, gate ? p.ldz : Di};   // row strides
 #pragma unroll
     for (int a = 0; a < (MODE == kFwdMain ? 3 : 2); ++a) {
 #pragma unroll
       for (int q = 0; q < U / RPI; ++q) {
         int64_t t = t0 + q * RPI + lrow;
         t = t < T ? t : T - 1;
-        const char* g = static_cast<const char*>(srcs[a]) + ((row0 + t) * Di + cch) * ES;
+        const char* g = static_cast<const char*>(srcs[a]) + ((row0 + t) * lds_[a] + cch) * ES;
         __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(dst + ACT0 + (a * U + q * RPI) * RB), 4, 0, 0);
       }
     }

@@ -54,12 +54,13 @@ __global__ void __launch_bounds__(256) scan_step_kernel(const FwdArgs p) {
   // load under a branch makes the compiler wait for it before the branches
   // join, one memory round trip per optional input.
   const void* zsrc = gate ? p.z : p.x;   // same shape; unused without the gate
+  const int64_t lz = gate ? p.ldz : Di;   // its row stride
   auto fetch = [&](int64_t t) {
     In s;
     const int64_t e = (b * T + t) * Di + i;
     s.x = io::ldraw(p.x, e);
     s.dr = io::ldraw(p.delta_raw, e);
-    s.z = io::ldraw(zsrc, e);
+    s.z = io::ldraw(zsrc, (b * T + t) * lz + i);
     // the row is contiguous; its start need not be 4-byte aligned, which
     // global loads allow
     const char* row = static_cast<const char*>(p.xdbl) + ((b * T + t) * p.X + p.R) * ES;
