@@ -435,7 +435,7 @@ __global__ void __launch_bounds__(kThreads) colpart_kernel(const void* __restric
 // workgroup: wave w sums the w-th of four contiguous runs of blocks in
 // ascending order, then the four run sums are added in run order (a fixed
 // order, so the result does not vary between runs)
-constexpr int kFewBlocks = 8;   // colsum_few_kernel's most blocks
+constexpr int kFewBlocks = 16;   // colsum_few_kernel's most blocks
 
 __global__ void __launch_bounds__(kThreads) colsum_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                          int64_t nblk, int64_t cols) {
