@@ -171,12 +171,13 @@ def test_errors(mscan):
     assert e.value.status == 3
 
 
-def test_full_size_sampled_heads(mscan):
+def test_full_size_every_output(mscan):
     """The measured shape (B=4, T=2048, 24 heads of 64, d_state 128, 32
-    angles, bf16) as the bench launches it; the per-head outputs of three
-    heads of batch row 0 against the oracle run on those heads alone (they
-    share the single B/C group, so their outputs do not depend on the
-    others)."""
+    angles, bf16) as the bench launches it, every element of every output
+    against the oracle.  The oracle runs each batch row on its own (rows
+    are independent), four at a time in threads; the parameter gradients
+    are the sums of the rows' ones."""
+    from concurrent.futures import ThreadPoolExecutor
     w = workloads.M3_CONFIGS["m3_siso_bf16"]
     inp = workloads.make_m3_inputs(w, 0)
     dims = mscan.M3Dims.make(w.batch, w.seqlen, w.heads, w.headdim, w.d_state, w.groups, w.n_angles, w.act,
@@ -187,18 +188,20 @@ def test_full_size_sampled_heads(mscan):
     core.forward(dev)
     core.backward(dev, dev["dy"])
     torch.cuda.synchronize()
-    heads = [0, 11, 23]
-    P = w.headdim
-    cols = np.concatenate([np.arange(h * P, (h + 1) * P) for h in heads])
-    sub = dict(x=inp["x"][:1, :, cols], b_in=inp["b_in"][:1], c_in=inp["c_in"][:1],
-               dd_dt_raw=inp["dd_dt_raw"][:1, :, heads], dd_a_raw=inp["dd_a_raw"][:1, :, heads],
-               trap_raw=inp["trap_raw"][:1, :, heads], angles_raw=inp["angles_raw"][:1], b_bias=inp["b_bias"][heads],
-               c_bias=inp["c_bias"][heads], dt_bias=inp["dt_bias"][heads], D=inp["D"][heads], a_floor=w.a_floor,
-               heads=len(heads), headdim=P)
-    y = m3o.forward(**sub)
-    g = m3o.backward(inp["dy"][:1, :, cols], **sub)
-    rep = {"y": err(core.y[:1, :, cols], y, True), "x": err(core.grads["x"][:1, :, cols], g["x"], True)}
-    for k in ("dd_dt_raw", "dd_a_raw", "trap_raw"):
-        rep[k] = err(core.grads[k][:1, :, heads], g[k], True)
+    per_row = ("x", "dy", "b_in", "c_in", "dd_dt_raw", "dd_a_raw", "trap_raw", "angles_raw")
+
+    def row(bi):
+        one = {k: (v[bi:bi + 1] if k in per_row else v) for k, v in inp.items()}
+        args = oracle_args(w, one)
+        return m3o.forward(**args), m3o.backward(one["dy"], **args)
+
+    with ThreadPoolExecutor(4) as ex:
+        res = list(ex.map(row, range(w.batch)))
+    y = np.concatenate([r[0] for r in res])
+    rep = {"y": err(core.y, y, True)}
+    for k in KEYS:
+        parts = [r[1][k] for r in res]
+        ora = np.concatenate(parts) if k in per_row else np.sum(parts, axis=0)
+        rep[k] = err(core.grads[k], ora, True)
     bad = {k: v for k, v in rep.items() if not v <= TOL_HALF}
     assert not bad, {k: "%.1e" % v for k, v in rep.items()}
