@@ -16,9 +16,10 @@
 // token), and packs them into 4 operands, one per channel of the 4.  Operand
 // q of the A side then holds channels c0 + 4 i + q (i = lane % 16) and of the
 // B side columns j0 + 4 i + q; the 16 products of the 4 x 4 operands cover
-// the 64 x 64 tile.  The 4 waves' tiles meet in LDS and are added in wave
-// order, and each chunk writes its own partial (f32, in the gradient's
-// layout); a column sum adds the chunks in order onto the gradient, so no
+// the 64 x 64 tile.  The 4 waves' tiles meet in LDS and are added in a
+// fixed order, (w0 + w2) + (w1 + w3), through a buffer of two tiles (so
+// three workgroups fit a CU), and each chunk writes its own partial (f32, in
+// the gradient's layout); a column sum adds the chunks in order onto the gradient, so no
 // result depends on timing.  With part_b, column J of SMALL is taken as all
 // ones: its products are the column sums of BIG (the dt bias gradient beside
 // the dt_proj weight gradient), written to part_b[P][Di].
@@ -85,7 +86,7 @@ __global__ void __launch_bounds__(kTw) skinny_wgrad_kernel(const SkinnyWgradArgs
   using M = Mma<A>;
   typedef typename M::v8 v8;
   typedef typename M::f4 f4;
-  __shared__ float red[kWw][64 * kLs];
+  __shared__ float red[kWw / 2][64 * kLs];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int i = lane & 15, g = lane >> 4;
   const int64_t Jt = p.J + (p.part_b ? 1 : 0);   // columns computed
@@ -151,22 +152,36 @@ __global__ void __launch_bounds__(kTw) skinny_wgrad_kernel(const SkinnyWgradArgs
   }
   // accumulator lane (i, g), element e of product (qa, qb): channel
   // c0 + 4 (4 g + e) + qa, column j0 + 4 i + qb; kept at LDS row
-  // 16 g + 4 e + qa, word 16 qb + i
+  // 16 g + 4 e + qa, word 16 qb + i.  Waves 2 and 3 store their tiles,
+  // waves 0 and 1 add theirs to them (each lane to the words it stored).
+  float* mine = red[w & 1];
+  if (w >= 2) {
 #pragma unroll
-  for (int qa = 0; qa < 4; ++qa)
+    for (int qa = 0; qa < 4; ++qa)
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+      for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[w][(16 * g + 4 * e + qa) * kLs + 16 * qb + i] = acc[qa][qb][e];
+        for (int e = 0; e < 4; ++e) mine[(16 * g + 4 * e + qa) * kLs + 16 * qb + i] = acc[qa][qb][e];
+  }
+  __syncthreads();
+  if (w < 2) {
+#pragma unroll
+    for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float& r = mine[(16 * g + 4 * e + qa) * kLs + 16 * qb + i];
+          r = acc[qa][qb][e] + r;
+        }
+  }
   __syncthreads();
   float* part = p.part + pc * p.Di * p.J;
   for (int e = threadIdx.x; e < 64 * 64; e += kTw) {
     const int cl = JMajor ? e % 64 : e / 64, jl = JMajor ? e / 64 : e % 64;
     if (j0 + jl >= Jt) continue;
     const int at = cl * kLs + 16 * (jl & 3) + (jl >> 2);
-    float s = red[0][at];
-#pragma unroll
-    for (int ww = 1; ww < kWw; ++ww) s += red[ww][at];
+    const float s = red[0][at] + red[1][at];
     if (j0 + jl == p.J) p.part_b[pc * p.Di + c0 + cl] = s;
     else if (JMajor) part[static_cast<int64_t>(j0 + jl) * p.Di + c0 + cl] = s;
     else part[(c0 + cl) * p.J + j0 + jl] = s;
@@ -183,7 +198,7 @@ bool skinny_wgrad_supported(Act act, int64_t N, int64_t Di, int64_t J, int64_t l
 int64_t skinny_wgrad_chunks(int64_t N, int64_t Di, int64_t J, int64_t* chunk) {
   // (the launch rounds the tiles up to a multiple of 8 per column group)
   const int64_t KS = (N + 31) / 32, tiles = (Di / 64) * ((J + 64) / 64);
-  int64_t P = (512 + tiles - 1) / tiles;
+  int64_t P = (768 + tiles - 1) / tiles;   // about three workgroups per CU
   const int64_t by_steps = KS / 8;   // at least 8 token steps (2 per wave) per chunk
   P = P < by_steps ? P : by_steps;
   P = P < 1 ? 1 : P;
