@@ -243,6 +243,56 @@ __global__ void __launch_bounds__(256) m3_theta_dt_kernel(const ThetaBwdArgs p) 
   p.ddt_ang[i] = acc;
 }
 
+// Both of the above in one pass when NA is a power of two: the grid is (row
+// tiles, B * H), so a (b, h, t) row's NA angles are NA aligned lanes of one
+// wave, whose sum of g angles_raw_t[a] is a butterfly over those lanes (every
+// lane of the row ends with the same bits; the first stores it).  g angles_raw
+// itself is then not stored: nothing reads it after this sum.  A thread takes
+// kThetaU elements 256 apart, all loads issued first, so that the
+// butterflies of its rows overlap.
+constexpr int kThetaU = 4;
+
+__global__ void __launch_bounds__(256) m3_theta_grad_kernel(const ThetaBwdArgs p) {
+  const Dims d = p.d;
+  const uint32_t NA = static_cast<uint32_t>(d.NA), H = static_cast<uint32_t>(d.H), bh32 = blockIdx.y;
+  const uint32_t n = static_cast<uint32_t>(d.T) * NA, sh = __builtin_ctz(NA);
+  const int64_t bh = bh32, b = bh32 / H;
+  // this (b, h)'s blocks; offsets within them are 32-bit (T * NA < 2^31)
+  const float* gl = p.gl + bh * n;              // [T, NA]
+  const float* ctot = p.ctot + bh * d.nc * NA;  // [nc, NA]
+  const float* dtv = p.dt + bh * d.T;           // [T]
+  const float* ang = p.ang + b * n;             // [T, NA] of batch row b
+  float* cang = p.cang + bh * n;
+  float vg[kThetaU], vc[kThetaU], vd[kThetaU], va[kThetaU];
+#pragma unroll
+  for (int u = 0; u < kThetaU; ++u) {
+    // lanes past the last row (whole rows of them) re-read element 0, unused
+    const uint32_t li = (blockIdx.x * kThetaU + u) * 256u + threadIdx.x;
+    const uint32_t e = li < n ? li : 0, t = e >> sh;
+    vg[u] = gl[e];
+    vc[u] = ctot[((t / kL) << sh) + (e & (NA - 1))];
+    vd[u] = dtv[t];
+    va[u] = ang[e];
+  }
+  float v[kThetaU];
+#pragma unroll
+  for (int u = 0; u < kThetaU; ++u) {
+    const uint32_t li = (blockIdx.x * kThetaU + u) * 256u + threadIdx.x;
+    const float g = vg[u] + vc[u];
+    if (li < n) cang[li] = g * vd[u];
+    v[u] = li < n ? g * va[u] : 0.0f;
+  }
+  for (uint32_t off = NA >> 1; off > 0; off >>= 1) {
+#pragma unroll
+    for (int u = 0; u < kThetaU; ++u) v[u] += __shfl_xor(v[u], static_cast<int>(off), 64);
+  }
+#pragma unroll
+  for (int u = 0; u < kThetaU; ++u) {
+    const uint32_t li = (blockIdx.x * kThetaU + u) * 256u + threadIdx.x;
+    if (li < n && (li & (NA - 1)) == 0) p.ddt_ang[bh * d.T + (li >> sh)] = v[u];
+  }
+}
+
 // ---------------------------------------------------------------- rotate
 // Qr / Kr [B, H, T, N] (activation dtype) = the biased C / B of the head's
 // group, pairs (a, a + NA) turned by theta[a].  Thread per (b, h, t, j),
@@ -285,30 +335,49 @@ __global__ void __launch_bounds__(256) m3_rotate_kernel(const RotArgs p) {
   }
 }
 
-// The same for 16-bit activations and n_angles a multiple of 8.  A row of
-// (b, h, t) has (N - NA) / 8 threads: the first NA / 8 each turn 8 pairs
-// (dims a0 .. a0+7 with a0 + NA .. a0 + NA + 7), so each angle's sine and
-// cosine is computed once; the rest copy 8 unturned dims past 2 NA.
+// The same for 16-bit activations and n_angles a multiple of 8.  The grid
+// is (row tiles, B * H, 2): z = 0 turns pairs, NA / 8 threads per (b, h, t)
+// row, each 8 pairs (dims a0 .. a0+7 with a0 + NA .. a0 + NA + 7), so each
+// angle's sine and cosine is computed once; z = 1 copies the unturned dims
+// past 2 NA, (N - 2 NA) / 8 threads per row, 8 dims each.  Every wave takes
+// one branch, and (b, h) comes from the workgroup, so a thread's only
+// division is the one that splits its row from its dims (32-bit).
 template <Act A>
 __global__ void __launch_bounds__(256) m3_rotate8_kernel(const RotArgs p) {
   using io = IO<A>;
   const Dims d = p.d;
-  const int64_t W = (d.N - d.NA) / 8, WP = d.NA / 8;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= d.B * d.H * d.T * W) return;
-  const int64_t j = i % W, bht = i / W, t = bht % d.T, bh = bht / d.T, h = bh % d.H, b = bh / d.H;
-  const int64_t g = h / (d.H / d.G);
-  const int64_t src = ((b * d.T + t) * d.G + g) * d.N;
-  auto row = [&](const void* base, int64_t off, float* v) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + src + off);
+  const bool turn = blockIdx.z == 0;   // uniform
+  const uint32_t per = static_cast<uint32_t>(turn ? d.NA / 8 : (d.N - 2 * d.NA) / 8);
+  const uint32_t li = blockIdx.x * 256u + threadIdx.x;
+  if (li >= static_cast<uint32_t>(d.T) * per) return;
+  const uint32_t H = static_cast<uint32_t>(d.H), bh32 = blockIdx.y;   // B * H < 2^16
+  const uint32_t h = bh32 % H, g = h / (H / static_cast<uint32_t>(d.G));
+  const int64_t bh = bh32, b = bh32 / H;
+  const uint32_t t = li / per, j = li - t * per;
+  const int64_t bht = bh * d.T + t;
+  // this row's unturned B / C (16-bit), the head's biases, the output rows
+  const uint16_t* bsrc = static_cast<const uint16_t*>(p.b_in) + ((b * d.T + t) * d.G + g) * d.N;
+  const uint16_t* csrc = static_cast<const uint16_t*>(p.c_in) + ((b * d.T + t) * d.G + g) * d.N;
+  const float* bb = p.b_bias + static_cast<int64_t>(h) * d.N;
+  const float* cb = p.c_bias + static_cast<int64_t>(h) * d.N;
+  uint16_t* kdst = static_cast<uint16_t*>(p.Kr) + bht * d.N;
+  uint16_t* qdst = static_cast<uint16_t*>(p.Qr) + bht * d.N;
+  auto ld8 = [](const uint16_t* q) { return *reinterpret_cast<const uint4*>(q); };
+  auto ldf8 = [](const float* q, float4& lo, float4& hi) {
+    lo = *reinterpret_cast<const float4*>(q);
+    hi = *reinterpret_cast<const float4*>(q + 4);
+  };
+  // 8 raw 16-bit values (lower address in the low half) plus 8 biases
+  auto unpack = [](const uint4& raw, const float4& lo, const float4& hi, float* v) {
     const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+    const float bv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      v[2 * k] = io::cvt(wv[k] & 0xffffu);
-      v[2 * k + 1] = io::cvt(wv[k] >> 16);
+      v[2 * k] = io::cvt(wv[k] & 0xffffu) + bv[2 * k];
+      v[2 * k + 1] = io::cvt(wv[k] >> 16) + bv[2 * k + 1];
     }
   };
-  auto put = [&](void* base, int64_t d0, const float* v) {   // 8 values as one 16-byte store
+  auto put = [](uint16_t* q, const float* v) {   // 8 values as one 16-byte store
     uint16_t hv[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -320,41 +389,52 @@ __global__ void __launch_bounds__(256) m3_rotate8_kernel(const RotArgs p) {
     o.y = hv[2] | (uint32_t(hv[3]) << 16);
     o.z = hv[4] | (uint32_t(hv[5]) << 16);
     o.w = hv[6] | (uint32_t(hv[7]) << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + bht * d.N + d0) = o;
+    *reinterpret_cast<uint4*>(q) = o;
   };
   float k1[8], q1[8];
-  const int64_t d1 = j < WP ? 8 * j : 2 * d.NA + 8 * (j - WP);   // first (or only) dims
-  row(p.b_in, d1, k1);
-  row(p.c_in, d1, q1);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    k1[k] += p.b_bias[h * d.N + d1 + k];
-    q1[k] += p.c_bias[h * d.N + d1 + k];
-  }
-  if (j < WP) {
-    const int64_t d2 = d1 + d.NA;   // the second halves of the pairs
+  if (turn) {
+    const int64_t d1 = 8 * static_cast<int64_t>(j), d2 = d1 + d.NA;   // the pairs' two halves
+    // every load first: rows, biases, the chunk-local angles and the chunks before
+    const uint4 rk1 = ld8(bsrc + d1), rq1 = ld8(csrc + d1), rk2 = ld8(bsrc + d2), rq2 = ld8(csrc + d2);
+    float4 bk1l, bk1h, bq1l, bq1h, bk2l, bk2h, bq2l, bq2h, thl, thh, tcl, tch;
+    ldf8(bb + d1, bk1l, bk1h);
+    ldf8(cb + d1, bq1l, bq1h);
+    ldf8(bb + d2, bk2l, bk2h);
+    ldf8(cb + d2, bq2l, bq2h);
+    ldf8(p.theta + bht * d.NA + d1, thl, thh);
+    ldf8(p.ctot + (bh * d.nc + t / kL) * d.NA + d1, tcl, tch);
+    __builtin_amdgcn_sched_barrier(0);
     float k2[8], q2[8], ko1[8], qo1[8], ko2[8], qo2[8];
-    row(p.b_in, d2, k2);
-    row(p.c_in, d2, q2);
+    unpack(rk1, bk1l, bk1h, k1);
+    unpack(rq1, bq1l, bq1h, q1);
+    unpack(rk2, bk2l, bk2h, k2);
+    unpack(rq2, bq2l, bq2h, q2);
+    const float th[8] = {thl.x + tcl.x, thl.y + tcl.y, thl.z + tcl.z, thl.w + tcl.w,
+                         thh.x + tch.x, thh.y + tch.y, thh.z + tch.z, thh.w + tch.w};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      k2[k] += p.b_bias[h * d.N + d2 + k];
-      q2[k] += p.c_bias[h * d.N + d2 + k];
       float sn, cs;
-      __sincosf(theta_at(p.theta, p.ctot, d, bh, t, d1 + k), &sn, &cs);
+      __sincosf(th[k], &sn, &cs);
       // first half: x1 c - x2 s; second half: x1 s + x2 c
       ko1[k] = k1[k] * cs - k2[k] * sn;
       qo1[k] = q1[k] * cs - q2[k] * sn;
       ko2[k] = k1[k] * sn + k2[k] * cs;
       qo2[k] = q1[k] * sn + q2[k] * cs;
     }
-    put(p.Kr, d1, ko1);
-    put(p.Qr, d1, qo1);
-    put(p.Kr, d2, ko2);
-    put(p.Qr, d2, qo2);
+    put(kdst + d1, ko1);
+    put(qdst + d1, qo1);
+    put(kdst + d2, ko2);
+    put(qdst + d2, qo2);
   } else {
-    put(p.Kr, d1, k1);
-    put(p.Qr, d1, q1);
+    const int64_t d1 = 2 * d.NA + 8 * static_cast<int64_t>(j);   // unturned dims
+    const uint4 rk1 = ld8(bsrc + d1), rq1 = ld8(csrc + d1);
+    float4 bk1l, bk1h, bq1l, bq1h;
+    ldf8(bb + d1, bk1l, bk1h);
+    ldf8(cb + d1, bq1l, bq1h);
+    unpack(rk1, bk1l, bk1h, k1);
+    unpack(rq1, bq1l, bq1h, q1);
+    put(kdst + d1, k1);
+    put(qdst + d1, q1);
   }
 }
 
@@ -1187,10 +1267,12 @@ hipError_t chunk_bwd(int64_t N, Act act, const ChunkStateArgs* cs, const BwdArgs
 
 hipError_t launch_rotate(Act act, const RotArgs& a, unsigned grid, hipStream_t st) {
   const Dims& d = a.d;
-  if (act != Act::F32 && d.NA % 8 == 0) {
-    const unsigned g8 = blocks(d.B * d.H * d.T * ((d.N - d.NA) / 8));
-    if (act == Act::BF16) hipLaunchKernelGGL(m3_rotate8_kernel<Act::BF16>, dim3(g8), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(m3_rotate8_kernel<Act::F16>, dim3(g8), dim3(256), 0, st, a);
+  // the 8-wide kernel: (b, h) on the grid's y, a row's dims in 32-bit indexes
+  const int64_t per = d.NA / 8 > (d.N - 2 * d.NA) / 8 ? d.NA / 8 : (d.N - 2 * d.NA) / 8;
+  if (act != Act::F32 && d.NA % 8 == 0 && d.B * d.H <= 65535 && d.T * per < (int64_t(1) << 31)) {
+    const dim3 g8(blocks(d.T * per), static_cast<unsigned>(d.B * d.H), 2);
+    if (act == Act::BF16) hipLaunchKernelGGL(m3_rotate8_kernel<Act::BF16>, g8, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(m3_rotate8_kernel<Act::F16>, g8, dim3(256), 0, st, a);
     return hipGetLastError();
   }
   switch (act) {
@@ -1483,8 +1565,13 @@ int mamba3_siso_bwd(const mamba3_dims_t* dims, const void* x, const void* b_in, 
     hipLaunchKernelGGL(m3_scan_local_kernel<true>, dim3(blocks(d.B * d.H * d.nc * d.NA)), dim3(256), 0, st, sa);
     hipLaunchKernelGGL(m3_scan_carry_kernel<true>, dim3(blocks(d.B * d.H * d.NA)), dim3(256), 0, st, sa);
     ThetaBwdArgs tb{w.dtheta, w.atot, w.dt, angles_raw, w.cang, w.ddt_ang, d};
-    hipLaunchKernelGGL(m3_theta_contrib_kernel, dim3(blocks(bht * d.NA)), dim3(256), 0, st, tb);
-    hipLaunchKernelGGL(m3_theta_dt_kernel, dim3(blocks(bht)), dim3(256), 0, st, tb);
+    if ((d.NA & (d.NA - 1)) == 0 && d.B * d.H <= 65535 && d.T * d.NA < (int64_t(1) << 31)) {
+      const dim3 tg(blocks(d.T * d.NA, 256 * kThetaU), static_cast<unsigned>(d.B * d.H));
+      hipLaunchKernelGGL(m3_theta_grad_kernel, tg, dim3(256), 0, st, tb);
+    } else {
+      hipLaunchKernelGGL(m3_theta_contrib_kernel, dim3(blocks(bht * d.NA)), dim3(256), 0, st, tb);
+      hipLaunchKernelGGL(m3_theta_dt_kernel, dim3(blocks(bht)), dim3(256), 0, st, tb);
+    }
     M3_HIP(hipGetLastError());
     AngArgs aa{w.cang, d_angles_raw, d};
     hipLaunchKernelGGL(m3_angle_sum_kernel, dim3(blocks(d.B * d.T * d.NA)), dim3(256), 0, st, aa);

@@ -112,6 +112,14 @@ def test_ragged_lengths(mscan, T):
     run(mscan, w, seed=T)
 
 
+@pytest.mark.parametrize("N,NA,act", [(32, 12, "f32"), (64, 24, "bf16"), (128, 40, "f16")])
+def test_angle_counts_not_powers_of_two(mscan, N, NA, act):
+    """The angle gradient's two-pass form (n_angles not a power of two) and
+    the 8-wide rotation with unequal pair and copy thread counts per row."""
+    w = workloads.M3Workload("m3_na", 2, 130, 3, 64, N, 1, NA, act)
+    run(mscan, w, seed=NA)
+
+
 def test_no_D(mscan):
     w = workloads.M3Workload("m3_nod", 1, 90, 2, 64, 32, 2, 4, "f32")
     run(mscan, w, D=False)
