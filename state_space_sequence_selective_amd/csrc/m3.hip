@@ -1107,7 +1107,16 @@ struct ColArgs {
   int64_t B, H, T, W;
 };
 
-__global__ void __launch_bounds__(256) m3_colpart_kernel(const ColArgs p) {
+// The four bias sums (B, C, dt, D) are independent, so each pass runs them
+// as one launch: grid y = the job.
+constexpr int kColJobs = 4;
+
+struct ColJobs {
+  ColArgs job[kColJobs];
+};
+
+__global__ void __launch_bounds__(256) m3_colpart_kernel(const ColJobs jobs) {
+  const ColArgs& p = jobs.job[blockIdx.y];
   const int64_t HW = p.H * p.W;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= kRowBlocks * HW) return;
@@ -1142,12 +1151,21 @@ __global__ void __launch_bounds__(256) m3_colpart_kernel(const ColArgs p) {
   p.part[i] = acc;
 }
 
-__global__ void __launch_bounds__(256) m3_colsum_kernel(const ColArgs p) {
+__global__ void __launch_bounds__(256) m3_colsum_kernel(const ColJobs jobs) {
+  const ColArgs& p = jobs.job[blockIdx.y];
   const int64_t HW = p.H * p.W;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= HW) return;
+  constexpr int U = 16;   // partials whose loads are issued before their adds (in order)
+  static_assert(kRowBlocks % U == 0, "partial batches");
   float acc = 0.0f;
-  for (int rb = 0; rb < kRowBlocks; ++rb) acc += p.part[rb * HW + i];
+  for (int r0 = 0; r0 < kRowBlocks; r0 += U) {
+    float v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = p.part[(r0 + k) * HW + i];
+#pragma unroll
+    for (int k = 0; k < U; ++k) acc += v[k];
+  }
   p.out[i] += acc;
 }
 
@@ -1350,7 +1368,7 @@ size_t al(size_t v) { return (v + 255) / 256 * 256; }
 // workspace: [dt | da | gam | sc : B*H*T f32 each] [tot : B*H*nc] [theta : B*H*T*NA] [atot : B*H*nc*NA]
 //            [Qr | Kr : B*H*T*N act]   -- forward and backward
 //            [dst : B*H*nc*P*N] [dQ | dK : B*H*T*N f32] [d_da | d_sc | d_gam | ddt_ang | dt_bht : B*H*T]
-//            [dtheta | cang : B*H*T*NA] [dD_part : B*H*nc] [colpart : kRowBlocks*H*N]   -- backward
+//            [dtheta | cang : B*H*T*NA] [dD_part : B*H*nc] [colpart : kRowBlocks*H*(2N+2)]   -- backward
 struct Ws {
   float *dt, *da, *gam, *sc, *tot, *theta, *atot;
   void *Qr, *Kr;
@@ -1389,7 +1407,7 @@ Ws layout(const Dims& d, Act act, char* base) {
   w.dtheta = reinterpret_cast<float*>(take(bht * d.NA * f + f));
   w.cang = reinterpret_cast<float*>(take(bht * d.NA * f + f));
   w.dD_part = reinterpret_cast<float*>(take(bhc * f));
-  w.colpart = reinterpret_cast<float*>(take(size_t(kRowBlocks) * d.H * d.N * f));
+  w.colpart = reinterpret_cast<float*>(take(size_t(kRowBlocks) * d.H * (2 * d.N + 2) * f));
   w.bwd_bytes = off;
   return w;
 }
@@ -1586,22 +1604,20 @@ int mamba3_siso_bwd(const mamba3_dims_t* dims, const void* x, const void* b_in, 
   M3_HIP(hipGetLastError());
   GroupArgs ga{w.dK, w.dQ, d_b_in, d_c_in, d};
   M3_HIP(launch_group_sum(act, ga, blocks(d.B * d.T * d.G * d.N), st));
-  // bias gradients: column sums of dK / dQ over (b, t)
-  ColArgs cb{w.dK, w.colpart, d_b_bias, d.B, d.H, d.T, d.N};
-  hipLaunchKernelGGL(m3_colpart_kernel, dim3(blocks(kRowBlocks * d.H * d.N)), dim3(256), 0, st, cb);
-  hipLaunchKernelGGL(m3_colsum_kernel, dim3(blocks(d.H * d.N)), dim3(256), 0, st, cb);
-  ColArgs cc{w.dQ, w.colpart, d_c_bias, d.B, d.H, d.T, d.N};
-  hipLaunchKernelGGL(m3_colpart_kernel, dim3(blocks(kRowBlocks * d.H * d.N)), dim3(256), 0, st, cc);
-  hipLaunchKernelGGL(m3_colsum_kernel, dim3(blocks(d.H * d.N)), dim3(256), 0, st, cc);
   TransArgs tr{d_dd_dt_raw, w.dt_bht, d};
   hipLaunchKernelGGL(m3_bth_to_bht_kernel, dim3(blocks(bht)), dim3(256), 0, st, tr);
-  ColArgs cd{w.dt_bht, w.colpart, d_dt_bias, d.B, d.H, d.T, 1};
-  hipLaunchKernelGGL(m3_colpart_kernel, dim3(blocks(kRowBlocks * d.H)), dim3(256), 0, st, cd);
-  hipLaunchKernelGGL(m3_colsum_kernel, dim3(blocks(d.H)), dim3(256), 0, st, cd);
-  if (D) {
-    ColArgs cD{w.dD_part, w.colpart, d_D, d.B, d.H, d.nc, 1};
-    hipLaunchKernelGGL(m3_colpart_kernel, dim3(blocks(kRowBlocks * d.H)), dim3(256), 0, st, cD);
-    hipLaunchKernelGGL(m3_colsum_kernel, dim3(blocks(d.H)), dim3(256), 0, st, cD);
+  // bias gradients: column sums over (b, t) of dK / dQ (B / C biases) and of
+  // dt_bht (dt bias); the D gradient sums the per-chunk partials
+  {
+    const int64_t pbc = int64_t(kRowBlocks) * d.H * d.N, pdt = int64_t(kRowBlocks) * d.H;
+    ColJobs cj{};
+    cj.job[0] = ColArgs{w.dK, w.colpart, d_b_bias, d.B, d.H, d.T, d.N};
+    cj.job[1] = ColArgs{w.dQ, w.colpart + pbc, d_c_bias, d.B, d.H, d.T, d.N};
+    cj.job[2] = ColArgs{w.dt_bht, w.colpart + 2 * pbc, d_dt_bias, d.B, d.H, d.T, 1};
+    cj.job[3] = ColArgs{w.dD_part, w.colpart + 2 * pbc + pdt, d_D, d.B, d.H, d.nc, 1};
+    const unsigned nj = D ? 4 : 3;
+    hipLaunchKernelGGL(m3_colpart_kernel, dim3(blocks(kRowBlocks * d.H * d.N), nj), dim3(256), 0, st, cj);
+    hipLaunchKernelGGL(m3_colsum_kernel, dim3(blocks(d.H * d.N), nj), dim3(256), 0, st, cj);
   }
   M3_HIP(hipGetLastError());
   mscan::set_last_error("");

@@ -25,13 +25,21 @@ class Mamba3Core:
         shp = dict(x=(s["x"], at), b_in=(s["bc"], at), c_in=(s["bc"], at), dd_dt_raw=(s["bth"], f),
                    dd_a_raw=(s["bth"], f), trap_raw=(s["bth"], f), angles_raw=(s["ang"], f), b_bias=(s["hn"], f),
                    c_bias=(s["hn"], f), dt_bias=(s["h"], f), D=(s["h"], f))
-        self.grads = {k: torch.empty(shp[k][0], dtype=shp[k][1], **kw) for k in GRADS}
+        self.grads = {k: torch.empty(shp[k][0], dtype=shp[k][1], **kw) for k in GRADS if k not in PARAMS}
+        # the accumulating parameter gradients are views of one f32 block (each
+        # at a 256-byte boundary), so clearing them is one fill
+        sizes = [int(torch.Size(shp[k][0]).numel()) for k in PARAMS]
+        padded = [(n + 63) // 64 * 64 for n in sizes]
+        self._param_grads = torch.empty(sum(padded), dtype=f, **kw)
+        off = 0
+        for k, n, pn in zip(PARAMS, sizes, padded):
+            self.grads[k] = self._param_grads[off:off + n].view(shp[k][0])
+            off += pn
         self.workspace = torch.empty(_lib.m3_workspace_bytes(d), dtype=torch.uint8, **kw)
 
     def zero_grads(self):
         """The parameter gradients accumulate; clear them once per step."""
-        for k in PARAMS:
-            self.grads[k].zero_()
+        self._param_grads.zero_()
 
     def _inputs(self, inp):
         return (inp["x"], inp["b_in"], inp["c_in"], inp["dd_dt_raw"], inp["dd_a_raw"], inp["trap_raw"],
