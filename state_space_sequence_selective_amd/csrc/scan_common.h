@@ -81,8 +81,8 @@ struct IO<Act::F16> {
 // sum_{r < n} src[r * stride] in ascending r.  Eight loads are issued before
 // their adds so each thread keeps several in flight; the adds keep the order
 // (the result is that of the plain sequential loop, bit for bit).
+template <int U = 8>   // loads issued before their adds
 __device__ __forceinline__ float ordered_sum(const float* src, int64_t n, int64_t stride) {
-  constexpr int U = 8;
   float acc = 0.0f;
   int64_t r = 0;
   for (; r + U <= n; r += U) {

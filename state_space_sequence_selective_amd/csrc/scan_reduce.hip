@@ -37,13 +37,27 @@ __device__ __forceinline__ float4 ordered_sum4(const float* src, int64_t n, int6
   return acc;
 }
 
+// The grid puts the conv weight / bias sums (fused entry) first: each is a
+// chain of strided loads over the batch rows and conv tiles on few threads,
+// so they start at once and run beside the bandwidth-bound B/C sums that
+// follow; the a_log / D sums over the segments and batch rows come last.
 __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t CW = p.K + 1;
+  const int64_t nconv = p.K > 0 ? p.Di * CW : 0;
+  if (j < nconv) {   // conv weight and bias partials
+    const int64_t i = j / CW, slot = j % CW;
+    const float acc = ordered_sum<16>(p.part_conv + i * CW + slot, p.conv_rows, p.Di * CW);
+    if (slot < p.K) p.d_conv_w[i * p.K + slot] += acc;
+    else p.d_conv_b[i] += acc;
+    return;
+  }
+  const int64_t jb = j - nconv;   // B/C columns, four per thread
   const int64_t BT = p.B * p.T;
   const int64_t W = 2 * p.Ds;
   const int64_t nbc4 = BT * W / 4;
-  if (j < nbc4) {
-    const int64_t row = j / (W / 4), m = (j % (W / 4)) * 4;
+  if (jb < nbc4) {
+    const int64_t row = jb / (W / 4), m = (jb % (W / 4)) * 4;
     const float4 s = ordered_sum4(p.part_bc + row * W + m, p.nG, BT * W);
     float* o = p.d_xdbl + row * p.X + p.R + m;
     o[0] += s.x;
@@ -52,21 +66,12 @@ __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
     o[3] += s.w;
     return;
   }
-  const int64_t jp = j - nbc4;
-  if (jp < p.Di * p.PW) {
-    const int64_t i = jp / p.PW, slot = jp % p.PW;
-    const float acc = ordered_sum(p.part_par + i * p.PW + slot, p.par_rows, p.Di * p.PW);
-    if (slot < p.Ds) p.d_a_log[i * p.Ds + slot] += acc;
-    else p.d_D[i] += acc;
-    return;
-  }
-  const int64_t jc = jp - p.Di * p.PW;   // conv weight and bias partials
-  const int64_t CW = p.K + 1;
-  if (p.K == 0 || jc >= p.Di * CW) return;
-  const int64_t i = jc / CW, slot = jc % CW;
-  const float acc = ordered_sum(p.part_conv + i * CW + slot, p.conv_rows, p.Di * CW);
-  if (slot < p.K) p.d_conv_w[i * p.K + slot] += acc;
-  else p.d_conv_b[i] += acc;
+  const int64_t jp = jb - nbc4;
+  if (jp >= p.Di * p.PW) return;
+  const int64_t i = jp / p.PW, slot = jp % p.PW;
+  const float acc = ordered_sum<16>(p.part_par + i * p.PW + slot, p.par_rows, p.Di * p.PW);
+  if (slot < p.Ds) p.d_a_log[i * p.Ds + slot] += acc;
+  else p.d_D[i] += acc;
 }
 
 // Starting carry of every backward segment from the carry pass's
