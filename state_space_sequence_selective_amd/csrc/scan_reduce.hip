@@ -38,18 +38,31 @@ __device__ __forceinline__ float4 ordered_sum4(const float* src, int64_t n, int6
 }
 
 // The grid puts the conv weight / bias sums (fused entry) first: each is a
-// chain of strided loads over the batch rows and conv tiles on few threads,
-// so they start at once and run beside the bandwidth-bound B/C sums that
-// follow; the a_log / D sums over the segments and batch rows come last.
+// chain of strided loads over the batch rows and conv tiles, so they start at
+// once and run beside the bandwidth-bound B/C sums that follow; four
+// adjacent lanes share one, each summing a quarter of the rows, and the
+// quarters are added in order.  The a_log / D sums over the segments and
+// batch rows come last.
+constexpr int kConvQuarters = 4;
+
 __global__ void __launch_bounds__(256) mscan_reduce_kernel(const ReduceArgs p) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t CW = p.K + 1;
-  const int64_t nconv = p.K > 0 ? p.Di * CW : 0;
+  constexpr int CQ = kConvQuarters;
+  static_assert(CQ == 4, "the quarters are added as ((q0 + q1) + q2) + q3");
+  const int64_t nconv = p.K > 0 ? p.Di * CW * CQ : 0;   // whole quads of lanes
   if (j < nconv) {   // conv weight and bias partials
-    const int64_t i = j / CW, slot = j % CW;
-    const float acc = ordered_sum<16>(p.part_conv + i * CW + slot, p.conv_rows, p.Di * CW);
-    if (slot < p.K) p.d_conv_w[i * p.K + slot] += acc;
-    else p.d_conv_b[i] += acc;
+    const int64_t c = j / CQ, i = c / CW, slot = c % CW;
+    const int q = static_cast<int>(j % CQ);
+    const int64_t per = (p.conv_rows + CQ - 1) / CQ, r0 = q * per;
+    const int64_t r1 = r0 + per < p.conv_rows ? r0 + per : p.conv_rows;
+    const float v = r1 > r0 ? ordered_sum<16>(p.part_conv + r0 * p.Di * CW + c, r1 - r0, p.Di * CW) : 0.0f;
+    const float v1 = __shfl_down(v, 1, CQ), v2 = __shfl_down(v, 2, CQ), v3 = __shfl_down(v, 3, CQ);
+    if (q == 0) {
+      const float acc = ((v + v1) + v2) + v3;
+      if (slot < p.K) p.d_conv_w[i * p.K + slot] += acc;
+      else p.d_conv_b[i] += acc;
+    }
     return;
   }
   const int64_t jb = j - nconv;   // B/C columns, four per thread
@@ -117,7 +130,7 @@ hipError_t launch_carry_fold(const CarryFoldArgs& p, hipStream_t st) {
 }
 
 hipError_t launch_reduce(const ReduceArgs& p, hipStream_t st) {
-  const int64_t n = p.B * p.T * 2 * p.Ds / 4 + p.Di * p.PW + (p.K > 0 ? p.Di * (p.K + 1) : 0);
+  const int64_t n = p.B * p.T * 2 * p.Ds / 4 + p.Di * p.PW + (p.K > 0 ? p.Di * (p.K + 1) * kConvQuarters : 0);
   dim3 grid(static_cast<unsigned>((n + 255) / 256));
   hipLaunchKernelGGL(mscan_reduce_kernel, grid, dim3(256), 0, st, p);
   return hipGetLastError();
