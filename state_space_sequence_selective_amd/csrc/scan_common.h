@@ -101,13 +101,19 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// log(1 + e) for e in [0, 1], with the correction that keeps the relative
-// error small when 1 + e rounds (Goldberg, "What every computer scientist
-// should know about floating-point arithmetic", Theorem 4).
+// log(1 + e) for e in [0, 1].  w = 1 + e is rounded; c = (w - 1) - e is
+// that rounding error exactly (w - 1 is exact for w in [1, 2], and so is the
+// difference of two numbers this close), so log(1 + e) = log(w - c), which
+// is log(w) - c / w to first order.  Taking c for c / w leaves an error of
+// about c e, i.e. a relative error of about |c| <= 2^-24 whatever e is; for
+// w = 1 (e below half an ulp of 1) it returns e exactly.  The same accuracy
+// as the classic correction log(w) e / (w - 1) (Goldberg, "What every
+// computer scientist should know about floating-point arithmetic",
+// Theorem 4) without its reciprocal and select.
 __device__ __forceinline__ float log1p_small(float e) {
   const float w = 1.0f + e;
-  if (w == 1.0f) return e;
-  return __builtin_amdgcn_logf(w) * 0.6931471805599453f * (e * rcp_fast(w - 1.0f));
+  const float c = (w - 1.0f) - e;
+  return fmaf(__builtin_amdgcn_logf(w), 0.6931471805599453f, -c);
 }
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|)
