@@ -1096,7 +1096,8 @@ __global__ void __launch_bounds__(256) m3_group_sum_kernel(const GroupArgs p) {
 }
 
 // Column sums over the (b, t) rows of [B, H, T, W] arrays (W = N for the
-// B / C bias gradients, 1 for the dt-bias gradient laid out [B, H, T]):
+// B / C bias gradients; the dt-bias gradient [B, T, H] is read as one head
+// of B * T rows and W = H columns):
 // partial sums over RB row blocks, then a fixed-order sum += into out[h, w].
 constexpr int kRowBlocks = 128;
 
@@ -1198,21 +1199,6 @@ __global__ void __launch_bounds__(256) m3_angle_sum_kernel(const AngArgs p) {
 __global__ void __launch_bounds__(256) m3_zero_kernel(float* p, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < n) p[i] = 0.0f;
-}
-
-// the dt gradient rearranged [B, T, H] -> [B, H, T] for the column sums
-struct TransArgs {
-  const float* src;
-  float* dst;
-  Dims d;
-};
-
-__global__ void __launch_bounds__(256) m3_bth_to_bht_kernel(const TransArgs p) {
-  const Dims d = p.d;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= d.B * d.H * d.T) return;
-  const int64_t t = i % d.T, bh = i / d.T, h = bh % d.H, b = bh / d.H;
-  p.dst[i] = p.src[(b * d.T + t) * d.H + h];
 }
 
 }  // namespace m3
@@ -1367,12 +1353,12 @@ size_t al(size_t v) { return (v + 255) / 256 * 256; }
 
 // workspace: [dt | da | gam | sc : B*H*T f32 each] [tot : B*H*nc] [theta : B*H*T*NA] [atot : B*H*nc*NA]
 //            [Qr | Kr : B*H*T*N act]   -- forward and backward
-//            [dst : B*H*nc*P*N] [dQ | dK : B*H*T*N f32] [d_da | d_sc | d_gam | ddt_ang | dt_bht : B*H*T]
+//            [dst : B*H*nc*P*N] [dQ | dK : B*H*T*N f32] [d_da | d_sc | d_gam | ddt_ang : B*H*T]
 //            [dtheta | cang : B*H*T*NA] [dD_part : B*H*nc] [colpart : kRowBlocks*H*(2N+2)]   -- backward
 struct Ws {
   float *dt, *da, *gam, *sc, *tot, *theta, *atot;
   void *Qr, *Kr;
-  float *dst, *dQ, *dK, *d_da, *d_sc, *d_gam, *ddt_ang, *dt_bht, *dtheta, *cang, *dD_part, *colpart;
+  float *dst, *dQ, *dK, *d_da, *d_sc, *d_gam, *ddt_ang, *dtheta, *cang, *dD_part, *colpart;
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -1403,7 +1389,6 @@ Ws layout(const Dims& d, Act act, char* base) {
   w.d_sc = reinterpret_cast<float*>(take(bht * f));
   w.d_gam = reinterpret_cast<float*>(take(bht * f));
   w.ddt_ang = reinterpret_cast<float*>(take(bht * f));
-  w.dt_bht = reinterpret_cast<float*>(take(bht * f));
   w.dtheta = reinterpret_cast<float*>(take(bht * d.NA * f + f));
   w.cang = reinterpret_cast<float*>(take(bht * d.NA * f + f));
   w.dD_part = reinterpret_cast<float*>(take(bhc * f));
@@ -1604,16 +1589,14 @@ int mamba3_siso_bwd(const mamba3_dims_t* dims, const void* x, const void* b_in, 
   M3_HIP(hipGetLastError());
   GroupArgs ga{w.dK, w.dQ, d_b_in, d_c_in, d};
   M3_HIP(launch_group_sum(act, ga, blocks(d.B * d.T * d.G * d.N), st));
-  TransArgs tr{d_dd_dt_raw, w.dt_bht, d};
-  hipLaunchKernelGGL(m3_bth_to_bht_kernel, dim3(blocks(bht)), dim3(256), 0, st, tr);
   // bias gradients: column sums over (b, t) of dK / dQ (B / C biases) and of
-  // dt_bht (dt bias); the D gradient sums the per-chunk partials
+  // d_dd_dt_raw (dt bias, [B * T rows, H]); the D gradient sums the per-chunk partials
   {
     const int64_t pbc = int64_t(kRowBlocks) * d.H * d.N, pdt = int64_t(kRowBlocks) * d.H;
     ColJobs cj{};
     cj.job[0] = ColArgs{w.dK, w.colpart, d_b_bias, d.B, d.H, d.T, d.N};
     cj.job[1] = ColArgs{w.dQ, w.colpart + pbc, d_c_bias, d.B, d.H, d.T, d.N};
-    cj.job[2] = ColArgs{w.dt_bht, w.colpart + 2 * pbc, d_dt_bias, d.B, d.H, d.T, 1};
+    cj.job[2] = ColArgs{d_dd_dt_raw, w.colpart + 2 * pbc, d_dt_bias, 1, 1, d.B * d.T, d.H};
     cj.job[3] = ColArgs{w.dD_part, w.colpart + 2 * pbc + pdt, d_D, d.B, d.H, d.nc, 1};
     const unsigned nj = D ? 4 : 3;
     hipLaunchKernelGGL(m3_colpart_kernel, dim3(blocks(kRowBlocks * d.H * d.N), nj), dim3(256), 0, st, cj);
