@@ -34,6 +34,8 @@
 //           the state entering every 16th step of each L-step chunk (one
 //           wave per chunk), written as 16-step checkpoints.
 #pragma once
+#include <type_traits>
+
 #include "scan_common.h"
 
 namespace mscan {
@@ -274,9 +276,11 @@ scan_fwd2_kernel(const Fwd2Args p) {
     o.u = rsrc(p.u_out ? p.u_out : p.out, t0);
     return o;
   };
-  // one step: per-lane work, then the states
-  auto step = [&](int64_t t, const char* buf, int k, const Outs& o) {
-    const bool live = t < t_end;   // wave-uniform
+  // one step: per-lane work, then the states.  Only the last tile of a
+  // segment can reach past its end (CHECK): the others skip the test.
+  auto step = [&](auto check, int64_t t, const char* buf, int k, const Outs& o) {
+    constexpr bool CHECK = decltype(check)::value;
+    const bool live = !CHECK || t < t_end;   // wave-uniform
     float dl = softplus(io::cvt(raw_act(buf, 1, k)));
     float u;
     if constexpr (FUSED) {
@@ -363,13 +367,21 @@ scan_fwd2_kernel(const Fwd2Args p) {
     boundary(t0);
     const Outs o = outs_at(t0);
     __builtin_amdgcn_s_setprio(1);
+    // without the stores of the main pass to pace it, the compiler would
+    // hoist the reads and per-step work of all U steps (twice the
+    // registers): a compiler-only memory barrier keeps them per step
+    if (t0 + U <= t_end) {
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      step(t0 + k, buf, k, o);
-      // without the stores of the main pass to pace it, the compiler would
-      // hoist the reads and per-step work of all U steps (twice the
-      // registers): a compiler-only memory barrier keeps them per step
-      if constexpr (MODE != kFwdMain) __asm__ __volatile__("" ::: "memory");
+      for (int k = 0; k < U; ++k) {
+        step(std::false_type{}, t0 + k, buf, k, o);
+        if constexpr (MODE != kFwdMain) __asm__ __volatile__("" ::: "memory");
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        step(std::true_type{}, t0 + k, buf, k, o);
+        if constexpr (MODE != kFwdMain) __asm__ __volatile__("" ::: "memory");
+      }
     }
     __builtin_amdgcn_s_setprio(0);
     // the LDS reads of the tile before this one are complete before copies
