@@ -19,6 +19,8 @@
 // copied to LDS asynchronously during the previous tile, turned into
 // {delta, dy} per (step, channel), and C_t into f32, both in LDS.
 #pragma once
+#include <type_traits>
+
 #include "scan_common.h"
 
 namespace mscan {
@@ -79,7 +81,10 @@ scan_bwd_carry_kernel(const CarryArgs p) {
   const int64_t ke = kb + tps < ntiles ? kb + tps : ntiles;
 
   uint32_t cbits[CPT];
-  auto prefetch = [&](int64_t kt) {
+  // Only the sequence's last tile can reach past its end (FULL false): the
+  // other tiles skip the end tests in the row clamps and the stage.
+  auto prefetch = [&](auto fullc, int64_t kt) {
+    constexpr bool FULL = decltype(fullc)::value;
     const int64_t t0 = kt * TT;
     async_rows<ES, CPW>(raw_l, p.delta_raw, row0, t0, T, Di, i0, TR, wave, NW, lane, Di);
     async_rows<ES, CPW>(raw_l + TR * RB, p.dout, row0, t0, T, Di, i0, TR, wave, NW, lane, Di);
@@ -88,27 +93,23 @@ scan_bwd_carry_kernel(const CarryArgs p) {
     for (int q = 0; q < CPT; ++q) {
       const int j = tid + q * NT;
       const int tt = (j < NCV ? j : NCV - 1) / DS, n = j % DS;
-      const int64_t t = t0 + tt < T ? t0 + tt : T - 1;   // rows past the end: zeroed in the stage
+      const int64_t t = FULL || t0 + tt < T ? t0 + tt : T - 1;   // rows past the end: zeroed in the stage
       cbits[q] = io::ldraw(p.xdbl, (row0 + t) * p.X + p.R + DS + n);
     }
   };
 
-  prefetch(ke - 1);
-  for (int64_t kt = ke - 1; kt >= kb; --kt) {
-    const int64_t t0 = kt * TT;
-    const int len = static_cast<int>(T - t0 < TT ? T - t0 : TT);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  auto stage = [&](auto fullc, int len) {
+    constexpr bool FULL = decltype(fullc)::value;
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int j = tid + q * NT;
-      if (NCV % NT == 0 || j < NCV) (&s_c[0][0])[j] = j / DS < len ? io::cvt(cbits[q]) : 0.0f;
+      if (NCV % NT == 0 || j < NCV) (&s_c[0][0])[j] = FULL || j / DS < len ? io::cvt(cbits[q]) : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       const int tt = g + G * k;
       float dl = 0.0f, dy = 0.0f;
-      if (tt < len && on) {
+      if ((FULL || tt < len) && on) {
         dl = softplus(raw_ld<A>(raw_dr, tt * CPW + c));
         const float go = raw_ld<A>(raw_go, tt * CPW + c);
         if (gate) {
@@ -121,8 +122,19 @@ scan_bwd_carry_kernel(const CarryArgs p) {
       s_q[tt][c] = make_float2(dl, dy);
       sd_acc += dl;
     }
+  };
+
+  if ((ke - 1) * TT + TT <= T) prefetch(std::true_type{}, ke - 1);
+  else prefetch(std::false_type{}, ke - 1);
+  for (int64_t kt = ke - 1; kt >= kb; --kt) {
+    const int64_t t0 = kt * TT;
+    const int len = static_cast<int>(T - t0 < TT ? T - t0 : TT);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt > kb) prefetch(kt - 1);
+    if (len == TT) stage(std::true_type{}, len);
+    else stage(std::false_type{}, len);
+    __syncthreads();
+    if (kt > kb) prefetch(std::true_type{}, kt - 1);   // tiles before the last are whole
     // past the end of the sequence delta = dy = C = 0: the steps are identities
 #pragma unroll
     for (int tt = TT - 1; tt >= 0; --tt) {
