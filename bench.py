@@ -672,13 +672,15 @@ def main():
     step_bytes = (fb + bb) * w.layers
     hbm_gbps = step_bytes / (ms_step / 1e3) / 1e9
     # dominant launch: the backward entry point of one layer (its segment
-    # carry pass when segmented, scan_bwd_kernel and the fixed-order reduce),
+    # carry pass and fold when segmented, scan_bwd_kernel, the fused entry's
+    # conv adjoint and the fixed-order reduce),
     # event-timed on the stream its kernels run on
     bwd_gbps = bb / (bwd_ms / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(bwd_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name, L),
-                "kernel": "mamba_scan_bwd entry point (scan_bwd_carry_kernel + scan_bwd_kernel + "
-                          "mscan_reduce_kernel), layer 0",
+                "kernel": ("mamba_conv_scan_gate_bwd" if w.d_conv else "mamba_scan_bwd")
+                          + " entry point (scan_bwd_carry_kernel + mscan_carry_fold_kernel + scan_bwd_kernel + "
+                          + ("conv_bwd_kernel + " if w.d_conv else "") + "mscan_reduce_kernel), layer 0",
                 "launch_ms": round(bwd_ms, 4), "algorithmic_bytes_per_launch": bb,
                 "overhead_bytes_per_launch": over["bwd"]}
     bwd_slots = elems * SLOTS_BWD_ELEM / (bwd_ms / 1e3)
