@@ -118,6 +118,7 @@ scan_bwd_kernel(const BwdArgs p) {
   constexpr int G = DS / SPL;          // state groups
   constexpr int NT = CPW * G;          // threads: (state group, channel)
   static_assert(NT % 64 == 0, "whole waves");
+  static_assert(CPW == 32, "a wave holds two state groups of the same channels (lanes l and l + 32)");
   // SUB steps per sub-tile (the unit of the channel sums and the epilogue).
   // Item (step tt of the tile, channel c) is staged, and finished in the
   // epilogue, by thread (tt % G, c) as its item number tt / G; SUB divides G
@@ -404,7 +405,12 @@ scan_bwd_kernel(const BwdArgs p) {
           sd = fmaf(qv, an[s], sd);
           red[c * (NO + 1) + q * SPL + s] = dh * cur.y;
         }
-        s_part[bi][g][q * CPW + c] = make_float2(su, sd);
+        // the wave's two state groups (lanes l and l + 32, one channel)
+        // added in registers: after the swap the lower half holds both
+        // groups' su, the upper half both groups' sd, for its channel
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(su), __float_as_uint(sd), false, false);
+        reinterpret_cast<float*>(&s_part[bi][wave][q * CPW + c])[lane >> 5] =
+            __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         __builtin_amdgcn_sched_barrier(0);
       }
       wave_lds_sync();
@@ -433,7 +439,7 @@ scan_bwd_kernel(const BwdArgs p) {
         const float4 st = s_st[tt][c];   // delta, delta*u, dy, u
         float su = 0.0f, sd = 0.0f;
 #pragma unroll
-        for (int w = 0; w < G; ++w) {
+        for (int w = 0; w < NW; ++w) {   // the waves' pair sums, in wave order
           const float2 pv = s_part[bi][w][q * CPW + c];
           su += pv.x;
           sd += pv.y;
