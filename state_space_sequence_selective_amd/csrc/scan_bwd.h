@@ -98,6 +98,32 @@ __device__ __forceinline__ void group_channel_sum(const float* red, int c,
   }
 }
 
+// The same sum when channels c and c + 16 of the group were already added
+// in registers (a v_permlane16_swap of two values, see the step loops): the
+// block holds 16 channel-pair rows, red[cp][o] (row stride NO + 1), and LPO
+// = 32 / NO lanes share an output, each adding NO / 2 rows before a
+// butterfly over them.  Lane c < NO ends with output c.
+template <int NO>
+__device__ __forceinline__ float group_pair_sum(const float* red, int c) {
+  static_assert(NO >= 2 && NO <= 16 && 32 % NO == 0, "outputs per block");
+  constexpr int LPO = 32 / NO, RPL = 16 / LPO;
+  const int o = c % NO, part = c / NO;
+  float acc = 0.0f;
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) acc += red[(part * RPL + m) * (NO + 1) + o];
+#pragma unroll
+  for (int off = NO; off < 32; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  return acc;
+}
+
+// Adds value a of channel c + 16 into lane c and value b of channel c into
+// lane c + 16 (per 16-lane row pair); lane c then holds a(c) + a(c + 16),
+// lane c + 16 holds b(c) + b(c + 16).
+__device__ __forceinline__ float pair16(float a, float b) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // Bytes of the raw tile: x (with the conv halo) | delta_raw | dout | z | y.
 // It lives in dynamic LDS: the compiler then sees it as an object of its own
 // and does not hold LDS accesses to the other arrays until the tile's
@@ -129,6 +155,10 @@ scan_bwd_kernel(const BwdArgs p) {
   constexpr int NO = SUB * SPL;        // channel sums per group per sub-tile
   static_assert(PD >= 1 && PD <= L, "operand look-ahead");
   constexpr int NOL = group_sum_outputs_per_lane<NO, CPW>();
+  // channel sums pre-added over channel pairs (c, c + 16) in registers when
+  // the thread's states come in pairs (d_B / d_C: half the LDS traffic)
+  constexpr bool PAIR = SPL % 2 == 0 && NO <= 16;
+  static_assert(!PAIR || NOL == 1, "one output per lane");
   constexpr int KMAX = FUSED ? 4 : 1;  // conv taps supported: 1..4
   constexpr int ES = A == Act::F32 ? 4 : 2;
   constexpr int RB = CPW * ES;         // bytes per raw row
@@ -354,13 +384,19 @@ scan_bwd_kernel(const BwdArgs p) {
           h[s] = fmaf(dA, h[s], cur.y * cB[s]);
           hs[tt][s] = h[s];
           das[tt][s] = dA;
-          red[c * (NO + 1) + q * SPL + s] = cur.z * h[s];
+          if constexpr (!PAIR) red[c * (NO + 1) + q * SPL + s] = cur.z * h[s];
+        }
+        if constexpr (PAIR) {   // states s, s+1: channels c and c + 16 added first
+#pragma unroll
+          for (int s = 0; s < SPL; s += 2)
+            red[(c & 15) * (NO + 1) + q * SPL + s + (c >> 4)] = pair16(cur.z * h[s], cur.z * h[s + 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       wave_lds_sync();
       float v[NOL];
-      group_channel_sum<NO, CPW>(red, c, v);
+      if constexpr (PAIR) v[0] = group_pair_sum<NO>(red, c);
+      else group_channel_sum<NO, CPW>(red, c, v);
 #pragma unroll
       for (int k = 0; k < NOL; ++k) {
         const int o = group_sum_output<NO, CPW>(c, k);   // o = step-in-sub-tile * SPL + state
@@ -391,6 +427,7 @@ scan_bwd_kernel(const BwdArgs p) {
         }
         if (tt - PD >= 0) operands(tt - PD, sl);
         float su = 0.0f, sd = 0.0f;
+        float du_[SPL];
 #pragma unroll
         for (int s = 0; s < SPL; ++s) {
           const float dh = fmaf(cur.z, cC[s], carry[s]);
@@ -403,7 +440,12 @@ scan_bwd_kernel(const BwdArgs p) {
           carry[s] = dh * das[tt][s];
           su = fmaf(dh, cB[s], su);
           sd = fmaf(qv, an[s], sd);
-          red[c * (NO + 1) + q * SPL + s] = dh * cur.y;
+          if constexpr (PAIR) du_[s] = dh * cur.y;
+          else red[c * (NO + 1) + q * SPL + s] = dh * cur.y;
+        }
+        if constexpr (PAIR) {
+#pragma unroll
+          for (int s = 0; s < SPL; s += 2) red[(c & 15) * (NO + 1) + q * SPL + s + (c >> 4)] = pair16(du_[s], du_[s + 1]);
         }
         // the wave's two state groups (lanes l and l + 32, one channel)
         // added in registers: after the swap the lower half holds both
@@ -416,7 +458,8 @@ scan_bwd_kernel(const BwdArgs p) {
       wave_lds_sync();
       {
         float v[NOL];
-        group_channel_sum<NO, CPW>(red, c, v);
+        if constexpr (PAIR) v[0] = group_pair_sum<NO>(red, c);
+        else group_channel_sum<NO, CPW>(red, c, v);
 #pragma unroll
         for (int k = 0; k < NOL; ++k) {
           const int o = group_sum_output<NO, CPW>(c, k);
