@@ -116,9 +116,9 @@ __device__ __forceinline__ float group_pair_sum(const float* red, int c) {
   return acc;
 }
 
-// Adds value a of channel c + 16 into lane c and value b of channel c into
-// lane c + 16 (per 16-lane row pair); lane c then holds a(c) + a(c + 16),
-// lane c + 16 holds b(c) + b(c + 16).
+// Two values a, b per lane, lanes c and c + 16 (c < 16, in each 32-lane half)
+// holding one channel pair: one v_permlane16_swap and one add leave lane c
+// with a(c) + a(c + 16) and lane c + 16 with b(c) + b(c + 16).
 __device__ __forceinline__ float pair16(float a, float b) {
   const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
@@ -427,7 +427,7 @@ scan_bwd_kernel(const BwdArgs p) {
         }
         if (tt - PD >= 0) operands(tt - PD, sl);
         float su = 0.0f, sd = 0.0f;
-        float du_[SPL];
+        float dbv[SPL];   // the d_B channel-sum terms dh * delta * u
 #pragma unroll
         for (int s = 0; s < SPL; ++s) {
           const float dh = fmaf(cur.z, cC[s], carry[s]);
@@ -440,12 +440,12 @@ scan_bwd_kernel(const BwdArgs p) {
           carry[s] = dh * das[tt][s];
           su = fmaf(dh, cB[s], su);
           sd = fmaf(qv, an[s], sd);
-          if constexpr (PAIR) du_[s] = dh * cur.y;
+          if constexpr (PAIR) dbv[s] = dh * cur.y;
           else red[c * (NO + 1) + q * SPL + s] = dh * cur.y;
         }
         if constexpr (PAIR) {
 #pragma unroll
-          for (int s = 0; s < SPL; s += 2) red[(c & 15) * (NO + 1) + q * SPL + s + (c >> 4)] = pair16(du_[s], du_[s + 1]);
+          for (int s = 0; s < SPL; s += 2) red[(c & 15) * (NO + 1) + q * SPL + s + (c >> 4)] = pair16(dbv[s], dbv[s + 1]);
         }
         // the wave's two state groups (lanes l and l + 32, one channel)
         // added in registers: after the swap the lower half holds both
